@@ -1,0 +1,414 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid compressed-attention hot path on one MI355X.
+
+The timed step is one decode step of a CSA + HCA layer pair at 1M context
+(8 sequences of 2^20 raw tokens, one query each at position L-1, 64 heads x
+128, window 128, HISA B=128 m=64 k=2048 on a 16 x 128 indexer over 262,143
+CSA entries, 8,192 HCA entries):
+
+  CSA: compress the window the new token completes -> refresh the last HISA
+       block mean -> visible counts -> HISA (block scores, block top-m, token
+       scores in the chosen blocks, token top-k) -> sparse attention
+  HCA: compress the completed 128-token window -> dense attention
+
+Every step runs as a replay of a HIP graph captured from the library calls.
+Caches are replicated R times (R graphs) and steps rotate through them, so
+the working set (about 70 MB a step) is not served by the 256 MB last-level
+cache.  Inputs are seeded synthetic tensors drawn on the device.
+
+Per-kernel durations come from the library's event timer (events recorded on
+the launch stream around every kernel) over a second, eager pass of the same
+steps.  Extras: HCA dense decode at batch 32, the 128K indexer chunk (flat
+and HISA), compression of 1M-token sequences.  The CPU baseline is the fp64
+oracle on a bounded sample of the same decode step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MiB = 1 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# Algorithmic traffic / work models (what the method must move or compute).
+# ----------------------------------------------------------------------------
+
+def attn_bytes(n_keys, H=64, d=128):
+    """One query: every key row (K|V bf16) once, q in, fp32 out and lse."""
+    return n_keys * 2 * d * 2 + H * d * 2 + H * d * 4 + H * 4
+
+
+def attn_flops(n_keys, H=64, d=128):
+    return 4.0 * H * d * n_keys
+
+
+def hisa_stage1_bytes(nb, d_i=128, h_i=16):
+    return nb * d_i * 4 + h_i * d_i * 2 + h_i * 4 + nb * 4
+
+
+def hisa_stage2_bytes(ncand, d_i=128, h_i=16):
+    return ncand * d_i * 2 + h_i * d_i * 2 + h_i * 4 + ncand * 4
+
+
+# ----------------------------------------------------------------------------
+
+def timed_graphs(graphs, steps, warmup):
+    import torch
+
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per step
+
+
+def capture(fn, reps):
+    import torch
+
+    graphs = []
+    for r in reps:
+        fn(r)  # eager warm-up on the current stream (workspaces, LDS limits)
+    torch.cuda.synchronize()
+    for r in reps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def kernel_times(fn, reps, steps):
+    """Eager pass with the library's event timer: {kernel: avg ms}."""
+    import torch
+    from compressed_attention_amd import ops
+
+    for r in reps:
+        fn(r)
+    torch.cuda.synchronize()
+    ops.timer_enable(True)
+    for i in range(steps):
+        fn(reps[i % len(reps)])
+    tot = ops.timer_collect()
+    ops.timer_enable(False)
+    return {k: (v[0] / v[1], v[1] // steps) for k, v in tot.items()}
+
+
+# ----------------------------------------------------------------------------
+# main workload: hybrid layer pair decode at 1M
+# ----------------------------------------------------------------------------
+
+def hybrid_pair(args):
+    import torch
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    bt, L, k = 8, 1 << 20, args.k
+    N, Nh, B, m = 262143, 8192, 128, 64
+    t0 = time.time()
+    W = synth.hybrid_pair_decode(0, device=dev, bt=bt, L=L, N_csa=N)
+    t = W.tensors
+    ckv = ops.compress(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4)
+    hkv = ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128)
+    reps = ops.hisa_pool(t["k_i"], B)
+    torch.cuda.synchronize()
+    assert ckv.shape[1] == N and hkv.shape[1] == Nh
+    nb = reps.shape[1]
+    R = args.replicas
+    caches = [dict(ckv=ckv, hkv=hkv, k_i=t["k_i"], reps=reps)]
+    for _ in range(R - 1):
+        caches.append(dict(ckv=ckv.clone(), hkv=hkv.clone(), k_i=t["k_i"].clone(), reps=reps.clone()))
+    torch.cuda.synchronize()
+    log(f"[bench] hybrid pair inputs + {R} cache replicas ready in {time.time() - t0:.1f}s")
+
+    def step(c):
+        ops.compress(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, N - 1, N, out=c["ckv"])
+        ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, Nh - 1, Nh, out=c["hkv"])
+        ops.hisa_pool(c["k_i"], B, nb - 1, nb, out=c["reps"])
+        nv = ops.visible_count(t["q_pos"], 8, 4, N)
+        nvh = ops.visible_count(t["q_pos"], 128, 128, Nh)
+        idx = ops.hisa_topk(t["q_i"], c["k_i"], t["w_i"], nv, c["reps"], B, m, k)
+        o1 = ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128)
+        o2 = ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128)
+        return o1, o2
+
+    graphs = capture(step, caches)
+    ms = timed_graphs(graphs, args.steps, args.warmup)
+    kt = kernel_times(step, caches, args.steps)
+    o1, o2 = step(caches[0])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all() and torch.isfinite(o2).all()
+
+    # per-kernel algorithmic bytes for this step (one launch each)
+    win = 128
+    kb = {
+        "attn_dense_mfma": bt * attn_bytes(Nh + win),
+        "attn_sparse_mfma": bt * attn_bytes(k + win),
+        "score_stage1_mfma": bt * hisa_stage1_bytes(nb),
+        "score_stage2_mfma": bt * hisa_stage2_bytes(m * B),
+    }
+    step_bytes = sum(kb.values())
+    info = dict(ms=ms, kernels=kt, kernel_bytes=kb, step_bytes=step_bytes, bt=bt, N=N, Nh=Nh, k=k, L=L)
+    del graphs
+    return info
+
+
+# ----------------------------------------------------------------------------
+# extras
+# ----------------------------------------------------------------------------
+
+def hca_decode_b32(args):
+    import torch
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    bt, L, Nh = 32, 1 << 20, 8192
+    W = synth.hca_decode(0, device=dev, bt=bt, L=L)
+    t = W.tensors
+    # compression of 32 x 1M tokens (HCA, disjoint 128)
+    hkv = ops.compress(t["raw_kv"], t["z"], t["b"], 128, 128)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        ops.compress(t["raw_kv"], t["z"], t["b"], 128, 128, out=hkv)
+    e1.record()
+    torch.cuda.synchronize()
+    comp_ms = e0.elapsed_time(e1) / 3
+    comp_bytes = bt * (L * 512 + L * 4 + Nh * 512)
+    nvh = ops.visible_count(t["q_pos"], 128, 128, Nh)
+    reps = [hkv] + [hkv.clone() for _ in range(3)]
+
+    def step(c):
+        return ops.dense_compressed_attn(t["q"], c, nvh, t["raw_kv"], t["q_pos"], 128)
+
+    graphs = capture(step, reps)
+    ms = timed_graphs(graphs, args.steps, args.warmup)
+    kt = kernel_times(step, reps, args.steps)
+    byt = bt * attn_bytes(Nh + 128)
+    del graphs
+    return dict(ms=ms, kernels=kt, step_bytes=byt, compress_ms=comp_ms, compress_bytes=comp_bytes, bt=bt)
+
+
+def indexer_128k(args):
+    import torch
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    W = synth.indexer_128k(0, device=dev)
+    t = W.tensors
+    N, nq, k, B, m = 131072, 1024, 2048, 128, 64
+    pos = torch.arange(N - nq, N, dtype=torch.int32, device=dev).reshape(1, nq)
+    nv = ops.visible_count(pos, 1, 1, N)
+    reps = ops.hisa_pool(t["k_i"], B)
+
+    def flat(_):
+        return ops.index_topk(t["q_i"], t["k_i"], t["w_i"], nv, k)
+
+    def hisa(_):
+        r = ops.hisa_pool(t["k_i"], B, out=reps)
+        return ops.hisa_topk(t["q_i"], t["k_i"], t["w_i"], nv, r, B, m, k)
+
+    out = {}
+    for name, fn in (("flat", flat), ("hisa", hisa)):
+        graphs = capture(fn, [None])
+        ms = timed_graphs(graphs, max(5, args.steps // 5), 2)
+        kt = kernel_times(fn, [None], max(5, args.steps // 5))
+        out[name] = dict(ms=ms, kernels=kt)
+        del graphs
+    i_f = flat(None).cpu().numpy()[0]
+    i_h = hisa(None).cpu().numpy()[0]
+    ious, rec_f, rec_h = [], [], []
+    needles = set(t["needles"].tolist())
+    nvh = nv.cpu().numpy()[0]
+    for q in range(nq):
+        a, b = set(i_f[q][i_f[q] >= 0].tolist()), set(i_h[q][i_h[q] >= 0].tolist())
+        ious.append(len(a & b) / max(1, len(a | b)))
+        vis = {x for x in needles if x < nvh[q]}
+        if vis:
+            rec_f.append(len(vis & a) / len(vis))
+            rec_h.append(len(vis & b) / len(vis))
+    flops = 2.0 * 16 * 128 * float(nvh.sum())
+    out.update(iou_mean=float(sum(ious) / len(ious)), iou_min=float(min(ious)),
+               needle_recall_flat=float(sum(rec_f) / len(rec_f)), needle_recall_hisa=float(sum(rec_h) / len(rec_h)),
+               flat_flops=flops)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the same decode step
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(args, k):
+    import numpy as np
+    import torch
+
+    import oracle
+    from compressed_attention_amd import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    N, Nh, B, m, L, W = 262143, 8192, 128, 64, 1 << 20, 128
+    # One sequence's caches, drawn on the host (values do not affect timing).
+    ckv = synth.normal((N, 256), 901, dtype=torch.bfloat16).double().numpy()
+    hkv = synth.normal((Nh, 256), 902, dtype=torch.bfloat16).double().numpy()
+    k_i = synth.normal((N, 128), 903, dtype=torch.bfloat16).double().numpy()
+    tail = synth.normal((256, 256), 904, dtype=torch.bfloat16).double().numpy()  # last raw rows
+    z = synth.normal((256,), 905).double().numpy()
+    b8 = synth.tiled_bias(4, 8, 906).double().numpy()
+    b128 = synth.tiled_bias(128, 128, 907).double().numpy()
+    reps = oracle.hisa_pool(k_i, B)  # the static block-mean cache, kept outside the timing
+    p_local = 255  # the query is the last of the 256 tail rows (position L-1)
+    done, el = 0, 0.0
+    while True:
+        q = synth.normal((1, 64, 128), 1000 + done, dtype=torch.bfloat16).double().numpy()
+        qh = synth.normal((1, 64, 128), 2000 + done, dtype=torch.bfloat16).double().numpy()
+        q_i = synth.normal((1, 16, 128), 3000 + done, dtype=torch.bfloat16).double().numpy()
+        w_i = synth.uniform((1, 16), 4000 + done).double().numpy()
+        s = time.perf_counter()
+        ckv[N - 1] = oracle.compress(tail[-8:], z[-8:], b8, 8, 4)[0]
+        hkv[Nh - 1] = oracle.compress(tail[-128:], z[-128:], b128, 128, 128)[0]
+        reps[-1] = oracle.hisa_pool(k_i[(N // B) * B:], B)[0]
+        idx, _ = oracle.hisa_topk(q_i, k_i, w_i, np.array([N]), B, m, k, reps=reps)
+        oracle.sparse_attention(q, ckv, idx, tail, np.array([p_local]), W, 1 / math.sqrt(128))
+        oracle.dense_compressed_attention(qh, hkv, np.array([Nh]), tail, np.array([p_local]), W, 1 / math.sqrt(128))
+        done += 1
+        el += time.perf_counter() - s
+        if el >= args.cpu_seconds or done >= 2000:
+            break
+    return dict(value=done / el, unit="decode queries/s", cores=int(threads), kind="oracle",
+                sample=f"{done} decode queries of one 2^20-token sequence (both layers, k={k}), "
+                       f"{el:.1f} s of host time; block means precomputed as in the GPU step")
+
+
+# ----------------------------------------------------------------------------
+
+def roofline_entry(kern_ms, nbytes):
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    return gbs
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--k", type=int, default=2048, choices=[512, 2048])
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(decode batches shard by sequence with no communication; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from compressed_attention_amd import _lib
+
+    _lib.lib()  # fail loudly if the HIP library is missing
+
+    main_k = args.k
+    res = hybrid_pair(args)
+    log(f"[bench] hybrid pair k={main_k}: {res['ms'] * 1e3:.1f} us/step")
+    extras = {}
+    if not args.no_extras:
+        a2 = argparse.Namespace(**vars(args))
+        a2.k = 512 if main_k == 2048 else 2048
+        r2 = hybrid_pair(a2)
+        extras[f"hybrid_pair_k{a2.k}"] = dict(us_per_step=r2["ms"] * 1e3, queries_per_s=r2["bt"] / (r2["ms"] * 1e-3),
+                                             step_GBps=r2["step_bytes"] / (r2["ms"] * 1e-3) / 1e9,
+                                             hbm_frac=r2["step_bytes"] / (r2["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        torch.cuda.empty_cache()
+        h = hca_decode_b32(args)
+        dk = h["kernels"].get("attn_dense_mfma", (float("nan"), 1))[0]
+        extras["hca_decode_b32"] = dict(
+            us_per_step=h["ms"] * 1e3, queries_per_s=h["bt"] / (h["ms"] * 1e-3),
+            step_MiB=h["step_bytes"] / MiB, step_GBps=h["step_bytes"] / (h["ms"] * 1e-3) / 1e9,
+            hbm_frac_step=h["step_bytes"] / (h["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            attn_kernel_us=dk * 1e3, hbm_frac_attn_kernel=h["step_bytes"] / (dk * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            kernels_us={kk: v[0] * 1e3 for kk, v in h["kernels"].items()})
+        extras["compress_1M_hca_b32"] = dict(ms=h["compress_ms"], GBps=h["compress_bytes"] / (h["compress_ms"] * 1e-3) / 1e9,
+                                             hbm_frac=h["compress_bytes"] / (h["compress_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        torch.cuda.empty_cache()
+        ix = indexer_128k(args)
+        fk = ix["flat"]["kernels"].get("score_flat_mfma", (float("nan"), 1))[0]
+        extras["indexer_128k"] = dict(
+            flat_ms=ix["flat"]["ms"], hisa_ms=ix["hisa"]["ms"], hisa_speedup=ix["flat"]["ms"] / ix["hisa"]["ms"],
+            flat_score_kernel_ms=fk, flat_score_TFLOPs=ix["flat_flops"] / (fk * 1e-3) / 1e12,
+            flat_score_mfma_frac=ix["flat_flops"] / (fk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            flat_total_mfma_frac=ix["flat_flops"] / (ix["flat"]["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            hisa_vs_flat_iou_mean=ix["iou_mean"], hisa_vs_flat_iou_min=ix["iou_min"],
+            needle_recall_flat=ix["needle_recall_flat"], needle_recall_hisa=ix["needle_recall_hisa"],
+            flat_kernels_ms={kk: v[0] for kk, v in ix["flat"]["kernels"].items()},
+            hisa_kernels_ms={kk: v[0] for kk, v in ix["hisa"]["kernels"].items()},
+            pages_context="HISA about 2x (32K) / 4x (128K) faster than the flat indexer, hardware not stated")
+        torch.cuda.empty_cache()
+
+    ms = res["ms"]
+    kt = res["kernels"]
+    # dominant kernel of the step: the one with the largest time per step
+    dom = max(kt.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
+    dom_ms = kt[dom][0]
+    dom_bytes = res["kernel_bytes"].get(dom)
+    roof = dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None, traffic=None, kernel=dom,
+                kernel_us=dom_ms * 1e3)
+    if dom_bytes:
+        a = dom_bytes / (dom_ms * 1e-3) / 1e9
+        roof.update(achieved=round(a, 1), frac=round(a / HBM_PEAK_GBS, 4), algorithmic_bytes=dom_bytes)
+    line = {
+        "metric": "decode queries/s at 1M context (CSA+HCA hybrid layer pair, HISA top-k)",
+        "value": round(res["bt"] / (ms * 1e-3), 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded device draws; N(0,1) K/V/q, logits N(0,1), bias N(0,0.1))",
+        "config": {"workload": "hybrid_pair_decode_1M", "batch": res["bt"], "context": res["L"], "heads": 64,
+                   "head_dim": 128, "window": 128, "csa_entries": res["N"], "hca_entries": res["Nh"],
+                   "indexer": "16x128", "hisa_B": 128, "hisa_m": 64, "k": res["k"], "cache_replicas": args.replicas,
+                   "launch": "hip graph replay"},
+        "step_GBps": round(res["step_bytes"] / (ms * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(res["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": roof,
+        "kernels_us": {kk: round(v[0] * 1e3, 2) for kk, v in kt.items()},
+        "extras": extras,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, main_k)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,30 @@
+"""Hybrid compressed attention (CSA + HCA + HISA) for MI355X (gfx950).
+
+The compute path is libhattn.so: hand-written HIP kernels behind a C ABI
+(include/hattn.h).  This package is its thin binding (``ops``) plus the
+seeded synthetic-input recipes (``synth``).  The library is loaded on first
+use; without it every op raises (there is no CPU fallback).
+"""
+from .ops import (  # noqa: F401
+    compress,
+    dense_compressed_attn,
+    hisa_pool,
+    hisa_topk,
+    index_topk,
+    sparse_attn,
+    timer_collect,
+    timer_enable,
+    visible_count,
+)
+
+__all__ = [
+    "compress",
+    "visible_count",
+    "index_topk",
+    "hisa_pool",
+    "hisa_topk",
+    "sparse_attn",
+    "dense_compressed_attn",
+    "timer_enable",
+    "timer_collect",
+]

@@ -1,0 +1,64 @@
+"""ctypes loader for libhattn.so (the HIP library).  No fallback: if the
+library is missing the first call raises, naming the build step."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhattn.so")
+
+_i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+_psz = ctypes.POINTER(ctypes.c_size_t)
+
+# name -> argument types, in the order of include/hattn.h
+SIGNATURES = {
+    "hattn_compress": [_i32, _p, _i64, _i64, _i32, _p, _p, _i32, _i32, _i64, _i64, _p, _p],
+    "hattn_visible_count": [_p, _i64, _i32, _i32, _i64, _p, _p],
+    "hattn_index_topk": [_i32, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _i32, _p, _p, _p, _psz, _p],
+    "hattn_hisa_pool": [_i32, _p, _i64, _i64, _i32, _i32, _i64, _i64, _p, _p],
+    "hattn_hisa_topk": [_i32, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i32, _i32, _i32, _p, _p, _p, _psz,
+                        _p],
+    "hattn_sparse_attn": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p, _p,
+                          _psz, _p],
+    "hattn_dense_compressed_attn": [_i32, _p, _p, _i64, _p, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p,
+                                    _p, _psz, _p],
+    "hattn_timer_enable": [_i32],
+    "hattn_timer_collect": [],
+    "hattn_timer_query": [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
+    "hattn_timer_names": [ctypes.c_char_p, _i64],
+    "hattn_status_string": [ctypes.c_int],
+    "hattn_last_error": [],
+    "hattn_abi_version": [],
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run __graft_entry__.build() (there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.hattn_status_string.restype = ctypes.c_char_p
+        L.hattn_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+class HattnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        L = lib()
+        msg = L.hattn_last_error().decode(errors="replace")
+        super().__init__(f"{fn}: {L.hattn_status_string(status).decode()} ({msg})")
+        self.status = status
+
+
+def check(fn: str, status: int) -> None:
+    if status != 0:
+        raise HattnError(fn, status)

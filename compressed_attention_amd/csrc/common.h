@@ -1,0 +1,90 @@
+// Device helpers shared by the hattn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define HATTN_DEV __device__ __forceinline__
+
+namespace hattn {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 is carried as raw 16-bit patterns (uint16_t) everywhere.
+HATTN_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+HATTN_DEV float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+HATTN_DEV float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+HATTN_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+HATTN_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// Order-preserving map fp32 -> uint32: a < b (as reals) <=> key(a) < key(b).
+// -0.0 is folded onto +0.0 (equal scores).  Key 0 is never produced by a
+// non-NaN value and is used as the "no candidate" sentinel.
+HATTN_DEV uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+HATTN_DEV float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+template <typename T>
+HATTN_DEV T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+template <typename T>
+HATTN_DEV T wave_max(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
+  return v;
+}
+
+HATTN_DEV int lane_id() { return __lane_id(); }
+
+// Number of lanes below this one whose bit is set in mask.
+HATTN_DEV int mbcnt(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
+}
+
+HATTN_DEV uint64_t ballot(bool p) { return __ballot(p); }
+
+// 16-byte global load/store helpers.
+HATTN_DEV u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+HATTN_DEV void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+HATTN_DEV u32x4_t ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+HATTN_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// MFMA 16x16x32 bf16 -> fp32 (gfx950).  Lane l holds A[l%16][8*(l/16)..+7],
+// B[8*(l/16)..+7][l%16]; D[4*(l/16)+i][l%16] in element i.
+HATTN_DEV f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+HATTN_DEV float to_float(float x) { return x; }
+HATTN_DEV float to_float(uint16_t x) { return bf16_to_f32(x); }
+
+HATTN_DEV int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+HATTN_DEV int64_t imax64(int64_t a, int64_t b) { return a > b ? a : b; }
+
+}  // namespace hattn

@@ -1,0 +1,281 @@
+// Sequence-dimension KV compression, window visibility and HISA block pooling.
+//
+// Compression ([HCA] daiw.net "前代 · HCA：128 倍压缩后再做稠密注意力", section 怎么压):
+// entry i of a sequence is the softmax(logit + position bias)-weighted sum of
+// raw rows [i*s, i*s + w).  The kernel is a pure HBM stream: each thread owns
+// 16 bytes of channels (8 bf16 or 4 fp32) of a run of consecutive entries and
+// walks the window rows with fp32 accumulation; the window weights are
+// recomputed per thread from the (cache-resident) logits, which costs w exps
+// per w 16-byte loads.  When windows overlap (s < w) the rows shared with the
+// previous entry of the run are kept in registers instead of being re-read.
+#include "common.h"
+#include "internal.h"
+
+namespace hattn {
+
+template <typename T>
+struct Vec16;
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  static HATTN_DEV void unpack(u32x4_t v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+  static HATTN_DEV u32x4_t pack(const float* f) {
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
+    return v;
+  }
+};
+template <>
+struct Vec16<uint16_t> {
+  static constexpr int N = 8;
+  static HATTN_DEV void unpack(u32x4_t v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16lo(v[i]);
+      f[2 * i + 1] = bf16hi(v[i]);
+    }
+  }
+  static HATTN_DEV u32x4_t pack(const float* f) {
+    u32x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return v;
+  }
+};
+
+// Generic window: any w, s.  Thread = (sequence, run of entries, 16-byte slot).
+template <typename T>
+__global__ __launch_bounds__(256) void compress_generic_kernel(const T* __restrict__ x, const float* __restrict__ z,
+                                                               const float* __restrict__ bias, T* __restrict__ y,
+                                                               int64_t L, int C, int w, int s, int64_t N, int64_t e0,
+                                                               int64_t runs_per_seq, int run, int64_t total) {
+  constexpr int V = Vec16<T>::N;
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int slots = C / V;
+  const int cs = int(t % slots);
+  const int64_t rest = t / slots;
+  const int64_t b = rest / runs_per_seq;
+  const int64_t r = rest % runs_per_seq;
+  const int64_t ebeg = e0 + r * run;
+  const T* xb = x + b * L * C + cs * V;
+  const float* zb = z ? z + b * L : nullptr;
+  for (int j = 0; j < run; ++j) {
+    const int64_t e = ebeg + j;
+    if (e >= N) break;
+    const int64_t t0 = e * s;
+    float mx = -INFINITY;
+    for (int u = 0; u < w; ++u) {
+      const float a = (zb ? zb[t0 + u] : 0.f) + (bias ? bias[u] : 0.f);
+      mx = fmaxf(mx, a);
+    }
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    float den = 0.f;
+    for (int u = 0; u < w; ++u) {
+      const float a = (zb ? zb[t0 + u] : 0.f) + (bias ? bias[u] : 0.f);
+      const float p = __expf(a - mx);
+      den += p;
+      float f[V];
+      Vec16<T>::unpack(ld16(xb + (t0 + u) * C), f);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(p, f[i], acc[i]);
+    }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] *= inv;
+    st16(y + (b * N + e) * C + cs * V, Vec16<T>::pack(acc));
+  }
+}
+
+// Overlapping windows with w = 2*s (CSA: 8 at stride 4): a thread walks a run
+// of consecutive entries; the second half of entry e's window is the first
+// half of entry e+1's, so each raw row is loaded once per run.
+template <typename T, int S>
+__global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restrict__ x, const float* __restrict__ z,
+                                                                const float* __restrict__ bias, T* __restrict__ y,
+                                                                int64_t L, int C, int64_t N, int64_t e0, int64_t e1,
+                                                                int64_t runs_per_seq, int run, int64_t total) {
+  constexpr int V = Vec16<T>::N;
+  constexpr int W = 2 * S;
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int slots = C / V;
+  const int cs = int(t % slots);
+  const int64_t rest = t / slots;
+  const int64_t b = rest / runs_per_seq;
+  const int64_t r = rest % runs_per_seq;
+  const int64_t ebeg = e0 + r * run;
+  const int64_t eend = imin64(e1, ebeg + run);
+  if (ebeg >= eend) return;
+  const T* xb = x + b * L * C + cs * V;
+  const float* zb = z ? z + b * L : nullptr;
+  float bs[W];
+#pragma unroll
+  for (int u = 0; u < W; ++u) bs[u] = bias ? bias[u] : 0.f;
+
+  // prev[] holds rows ebeg*S .. ebeg*S + S-1 (first half of the first window).
+  float prev[S][V];
+  float zprev[S];
+#pragma unroll
+  for (int u = 0; u < S; ++u) {
+    Vec16<T>::unpack(ld16(xb + (ebeg * S + u) * C), prev[u]);
+    zprev[u] = zb ? zb[ebeg * S + u] : 0.f;
+  }
+  for (int64_t e = ebeg; e < eend; ++e) {
+    float cur[S][V];
+    float zcur[S];
+    const int64_t t1 = e * S + S;
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      Vec16<T>::unpack(ld16(xb + (t1 + u) * C), cur[u]);
+      zcur[u] = zb ? zb[t1 + u] : 0.f;
+    }
+    float a[W];
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      a[u] = zprev[u] + bs[u];
+      a[S + u] = zcur[u] + bs[S + u];
+    }
+    float mx = a[0];
+#pragma unroll
+    for (int u = 1; u < W; ++u) mx = fmaxf(mx, a[u]);
+    float den = 0.f;
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      const float p = __expf(a[u] - mx);
+      den += p;
+      const float* row = u < S ? prev[u] : cur[u - S];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(p, row[i], acc[i]);
+    }
+    const float inv = 1.f / den;
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] *= inv;
+    st16(y + (b * N + e) * C + cs * V, Vec16<T>::pack(acc));
+#pragma unroll
+    for (int u = 0; u < S; ++u) {
+      zprev[u] = zcur[u];
+#pragma unroll
+      for (int i = 0; i < V; ++i) prev[u][i] = cur[u][i];
+    }
+  }
+}
+
+template <typename T>
+static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
+                                    int w, int s, int64_t N, int64_t e0, int64_t e1, void* y, hipStream_t st) {
+  constexpr int V = Vec16<T>::N;
+  const int slots = C / V;
+  const int64_t ne = e1 - e0;
+  if (ne <= 0 || bt <= 0) return hipSuccess;
+  if (w == 2 * s && s == 4) {
+    // Runs long enough to amortise the re-read first half, short enough to
+    // keep many waves in flight.
+    const int run = ne >= 16 * 1024 ? 16 : 1;
+    const int64_t runs = (ne + run - 1) / run;
+    const int64_t total = bt * runs * slots;
+    LaunchScope ls("compress_overlap2", st);
+    hipLaunchKernelGGL((compress_overlap2_kernel<T, 4>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                       (const T*)x, z, bias, (T*)y, L, C, N, e0, e1, runs, run, total);
+    return hipGetLastError();
+  }
+  const int run = 1;
+  const int64_t runs = ne;
+  const int64_t total = bt * runs * slots;
+  LaunchScope ls("compress", st);
+  hipLaunchKernelGGL((compress_generic_kernel<T>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                     (const T*)x, z, bias, (T*)y, L, C, w, s, N, e0, runs, run, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z,
+                           const float* bias, int w, int s, int64_t N, int64_t e0, int64_t e1, void* y,
+                           hipStream_t st) {
+  if (dtype == 0) return launch_compress_t<float>(x, bt, L, C, z, bias, w, s, N, e0, e1, y, st);
+  return launch_compress_t<uint16_t>(x, bt, L, C, z, bias, w, s, N, e0, e1, y, st);
+}
+
+// ---------------------------------------------------------------------------
+// Visibility: entry i is visible at raw position p iff i*s + w - 1 <= p.
+// ---------------------------------------------------------------------------
+__global__ void visible_count_kernel(const int32_t* __restrict__ pos, int64_t count, int w, int s, int64_t n_entries,
+                                     int32_t* __restrict__ n_vis) {
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= count) return;
+  const int64_t p = pos[t];
+  int64_t v = p < w - 1 ? 0 : (p - w + 1) / s + 1;
+  if (v > n_entries) v = n_entries;
+  n_vis[t] = int32_t(v);
+}
+
+hipError_t launch_visible_count(const int32_t* pos, int64_t count, int w, int s, int64_t n_entries, int32_t* n_vis,
+                                hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  LaunchScope ls("visible_count", st);
+  hipLaunchKernelGGL(visible_count_kernel, dim3(unsigned((count + 255) / 256)), dim3(256), 0, st, pos, count, w, s,
+                     n_entries, n_vis);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// HISA pooling ([HISA] my.qihongyi.cn/?p=787, section 第一阶段): block mean
+// with a zero-padded short tail.  Thread = (sequence, block, 16-byte slot);
+// rows are summed in index order in fp32.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k_i, int64_t n, int d, int B, int64_t nb,
+                                                   int64_t j0, int64_t nj, float* __restrict__ reps, int64_t total) {
+  constexpr int V = Vec16<T>::N;
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int slots = d / V;
+  const int cs = int(t % slots);
+  const int64_t rest = t / slots;
+  const int64_t b = rest / nj;
+  const int64_t j = j0 + rest % nj;
+  const int64_t i0 = j * B;
+  const int64_t i1 = imin64(n, i0 + B);
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  const T* base = k_i + b * n * d + cs * V;
+  for (int64_t i = i0; i < i1; ++i) {
+    float f[V];
+    Vec16<T>::unpack(ld16(base + i * d), f);
+#pragma unroll
+    for (int u = 0; u < V; ++u) acc[u] += f[u];
+  }
+  const float inv = 1.f / float(B);
+  float* out = reps + (b * nb + j) * d + cs * V;
+#pragma unroll
+  for (int u = 0; u < V; ++u) out[u] = acc[u] * inv;
+}
+
+hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_i, int B, int64_t j0, int64_t j1,
+                       float* reps, hipStream_t st) {
+  const int64_t nb = (n + B - 1) / B;
+  const int64_t nj = j1 - j0;
+  if (nj <= 0 || bt <= 0) return hipSuccess;
+  LaunchScope ls("hisa_pool", st);
+  if (dtype == 0) {
+    const int64_t total = bt * nj * (d_i / 4);
+    hipLaunchKernelGGL(pool_kernel<float>, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                       (const float*)k_i, n, d_i, B, nb, j0, nj, reps, total);
+  } else {
+    const int64_t total = bt * nj * (d_i / 8);
+    hipLaunchKernelGGL(pool_kernel<uint16_t>, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                       (const uint16_t*)k_i, n, d_i, B, nb, j0, nj, reps, total);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hattn

@@ -1,0 +1,309 @@
+// C ABI of libhattn: argument validation, workspace sizing, dispatch, timer.
+// Every check happens before anything is enqueued; see include/hattn.h.
+#include "hattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hattn_status_t fail(hattn_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+hattn_status_t ok() {
+  g_err[0] = 0;
+  return HATTN_OK;
+}
+
+hattn_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int dt) { return dt == HATTN_F32 || dt == HATTN_BF16; }
+int elem_bytes(int dt) { return dt == HATTN_F32 ? 4 : 2; }
+
+// Workspace protocol shared by every entry point that takes one.  Returns
+// true when the call must end here: a size query (HATTN_OK) or a missing /
+// too small workspace.  ws_bytes == NULL means "no workspace given", which
+// is fine exactly when the call needs none.
+bool ws_query(void* ws, size_t* ws_bytes, size_t need, hattn_status_t* st) {
+  if (!ws_bytes) {
+    if (need == 0) {
+      *st = HATTN_OK;
+      return false;
+    }
+    *st = fail(HATTN_ERR_WORKSPACE, "a workspace of %zu bytes is required", need);
+    return true;
+  }
+  if (!ws) {
+    *ws_bytes = need;
+    *st = ok();
+    return true;
+  }
+  if (*ws_bytes < need) {
+    *st = fail(HATTN_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", *ws_bytes, need);
+    return true;
+  }
+  *st = HATTN_OK;
+  return false;
+}
+
+// ---- kernel timer ----------------------------------------------------------
+struct Pending {
+  std::string name;
+  hipEvent_t e0, e1;
+};
+bool g_timer_on = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_free;
+std::map<std::string, std::pair<double, int64_t>> g_totals;
+
+hipEvent_t take_event() {
+  if (!g_free.empty()) {
+    hipEvent_t e = g_free.back();
+    g_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace hattn {
+
+LaunchScope::LaunchScope(const char* name, hipStream_t s) : name_(name), stream_(s), ev0_(nullptr) {
+  if (!g_timer_on) return;
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, s) == hipSuccess) ev0_ = e;
+}
+
+LaunchScope::~LaunchScope() {
+  if (!ev0_) return;
+  hipEvent_t e1 = take_event();
+  if (e1 && hipEventRecord(e1, stream_) == hipSuccess) {
+    g_pending.push_back({name_, (hipEvent_t)ev0_, e1});
+  } else {
+    g_free.push_back((hipEvent_t)ev0_);
+    if (e1) g_free.push_back(e1);
+  }
+}
+
+}  // namespace hattn
+
+extern "C" {
+
+const char* hattn_status_string(int status) {
+  switch (status) {
+    case HATTN_OK: return "HATTN_OK";
+    case HATTN_ERR_ARG: return "HATTN_ERR_ARG: invalid argument";
+    case HATTN_ERR_UNSUPPORTED: return "HATTN_ERR_UNSUPPORTED: no kernel for this configuration";
+    case HATTN_ERR_WORKSPACE: return "HATTN_ERR_WORKSPACE: workspace too small";
+    case HATTN_ERR_HIP: return "HATTN_ERR_HIP: HIP runtime error";
+    default: return "unknown hattn status";
+  }
+}
+
+const char* hattn_last_error(void) { return g_err; }
+
+int hattn_abi_version(void) { return 1; }
+
+hattn_status_t hattn_compress(int dtype, const void* x, int64_t bt, int64_t L, int32_t C, const float* logits,
+                              const float* pos_bias, int32_t w, int32_t stride, int64_t e_begin, int64_t e_end,
+                              void* y, void* stream) {
+  if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "compress: bad dtype %d", dtype);
+  if (bt < 0 || L < 0) return fail(HATTN_ERR_ARG, "compress: negative size");
+  if (w < 1 || w > 4096 || stride < 1) return fail(HATTN_ERR_ARG, "compress: need 1 <= w <= 4096 and stride >= 1");
+  const int vec = 16 / elem_bytes(dtype);
+  if (C <= 0 || C % vec) return fail(HATTN_ERR_ARG, "compress: C=%d must be a positive multiple of %d", C, vec);
+  if (L < w) return fail(HATTN_ERR_ARG, "compress: L=%lld shorter than the window %d", (long long)L, w);
+  const int64_t N = (L - w) / stride + 1;
+  if (e_begin < 0 || e_end < e_begin || e_end > N)
+    return fail(HATTN_ERR_ARG, "compress: entry range [%lld, %lld) outside [0, %lld]", (long long)e_begin,
+                (long long)e_end, (long long)N);
+  if (bt == 0 || e_end == e_begin) return ok();
+  if (!x || !y) return fail(HATTN_ERR_ARG, "compress: NULL x or y");
+  return hip_status(hattn::launch_compress(dtype, x, bt, L, C, logits, pos_bias, w, stride, N, e_begin, e_end, y,
+                                           (hipStream_t)stream),
+                    "compress");
+}
+
+hattn_status_t hattn_visible_count(const int32_t* pos, int64_t count, int32_t w, int32_t stride, int64_t n_entries,
+                                   int32_t* n_vis, void* stream) {
+  if (count < 0 || w < 1 || stride < 1 || n_entries < 0 || n_entries > INT32_MAX)
+    return fail(HATTN_ERR_ARG, "visible_count: bad sizes");
+  if (count == 0) return ok();
+  if (!pos || !n_vis) return fail(HATTN_ERR_ARG, "visible_count: NULL pointer");
+  return hip_status(hattn::launch_visible_count(pos, count, w, stride, n_entries, n_vis, (hipStream_t)stream),
+                    "visible_count");
+}
+
+static hattn_status_t check_index_args(const char* fn, int dtype, const void* q_i, const void* k_i, const float* w_i,
+                                       const int32_t* n_vis, int64_t bt, int64_t nq, int32_t h_i, int32_t d_i,
+                                       int64_t n, int32_t k, const int32_t* idx) {
+  if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "%s: bad dtype %d", fn, dtype);
+  if (bt < 0 || nq < 0 || n < 0 || n > INT32_MAX) return fail(HATTN_ERR_ARG, "%s: bad sizes", fn);
+  if (k < 1 || k > 8192) return fail(HATTN_ERR_ARG, "%s: need 1 <= k <= 8192 (k=%d)", fn, k);
+  if (h_i < 1 || h_i > 64) return fail(HATTN_ERR_ARG, "%s: need 1 <= h_i <= 64", fn);
+  if (d_i < 1 || d_i > 256) return fail(HATTN_ERR_ARG, "%s: need 1 <= d_i <= 256", fn);
+  if (h_i * d_i > 8192) return fail(HATTN_ERR_UNSUPPORTED, "%s: h_i*d_i > 8192", fn);
+  if (bt * nq > 0 && (!q_i || !w_i || !n_vis || !idx || (n > 0 && !k_i)))
+    return fail(HATTN_ERR_ARG, "%s: NULL required pointer", fn);
+  return HATTN_OK;
+}
+
+hattn_status_t hattn_index_topk(int dtype, const void* q_i, const void* k_i, const float* w_i, const int32_t* n_vis,
+                                int64_t bt, int64_t nq, int32_t h_i, int32_t d_i, int64_t n, int32_t k, int32_t* idx,
+                                float* score, void* ws, size_t* ws_bytes, void* stream) {
+  hattn_status_t st = check_index_args("index_topk", dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n, k, idx);
+  if (st != HATTN_OK) return st;
+  hattn::IndexArgs a{dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n};
+  const size_t need = bt * nq > 0 ? hattn::flat_topk_ws_bytes(a, k) : 0;
+  if (ws_query(ws, ws_bytes, need, &st)) return st;
+  if (bt * nq == 0) return ok();
+  return hip_status(hattn::launch_flat_topk(a, k, idx, score, ws, (hipStream_t)stream), "index_topk");
+}
+
+hattn_status_t hattn_hisa_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int32_t d_i, int32_t B,
+                               int64_t j_begin, int64_t j_end, float* reps, void* stream) {
+  if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "hisa_pool: bad dtype %d", dtype);
+  if (bt < 0 || n < 0 || B < 1 || d_i < 1) return fail(HATTN_ERR_ARG, "hisa_pool: bad sizes");
+  const int vec = 16 / elem_bytes(dtype);
+  if (d_i % vec) return fail(HATTN_ERR_ARG, "hisa_pool: d_i=%d must be a multiple of %d", d_i, vec);
+  const int64_t nb = (n + B - 1) / B;
+  if (j_begin < 0 || j_end < j_begin || j_end > nb) return fail(HATTN_ERR_ARG, "hisa_pool: block range outside [0, %lld]", (long long)nb);
+  if (bt == 0 || j_end == j_begin) return ok();
+  if (!k_i || !reps) return fail(HATTN_ERR_ARG, "hisa_pool: NULL pointer");
+  return hip_status(hattn::launch_pool(dtype, k_i, bt, n, d_i, B, j_begin, j_end, reps, (hipStream_t)stream),
+                    "hisa_pool");
+}
+
+hattn_status_t hattn_hisa_topk(int dtype, const void* q_i, const void* k_i, const float* w_i, const int32_t* n_vis,
+                               int64_t bt, int64_t nq, int32_t h_i, int32_t d_i, int64_t n, const float* reps,
+                               int32_t B, int32_t m, int32_t k, int32_t* idx, int32_t* blk, void* ws,
+                               size_t* ws_bytes, void* stream) {
+  hattn_status_t st = check_index_args("hisa_topk", dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n, k, idx);
+  if (st != HATTN_OK) return st;
+  if (B < 1 || B > 1024 || m < 1 || int64_t(m) * B > 16384)
+    return fail(HATTN_ERR_ARG, "hisa_topk: need 1 <= B <= 1024, m >= 1, m*B <= 16384");
+  if ((n + B - 1) / B > 16384) return fail(HATTN_ERR_UNSUPPORTED, "hisa_topk: more than 16384 blocks");
+  if (bt * nq > 0 && n > 0 && !reps) return fail(HATTN_ERR_ARG, "hisa_topk: NULL reps");
+  hattn::IndexArgs a{dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n};
+  const size_t need = bt * nq > 0 ? hattn::hisa_topk_ws_bytes(a, B, m, k) : 0;
+  if (ws_query(ws, ws_bytes, need, &st)) return st;
+  if (bt * nq == 0) return ok();
+  return hip_status(hattn::launch_hisa_topk(a, reps, B, m, k, idx, blk, ws, (hipStream_t)stream), "hisa_topk");
+}
+
+static hattn_status_t attn_common(const char* fn, hattn::AttnArgs& a, void* ws, size_t* ws_bytes, void* stream) {
+  if (!dtype_ok(a.dtype)) return fail(HATTN_ERR_ARG, "%s: bad dtype %d", fn, a.dtype);
+  if (a.bt < 0 || a.nq < 0 || a.n < 0 || a.L < 1 || a.window < 1)
+    return fail(HATTN_ERR_ARG, "%s: bad sizes (need L >= 1, window >= 1)", fn);
+  if (a.h < 1 || a.d < 1 || a.d % 8) return fail(HATTN_ERR_ARG, "%s: bad head shape h=%d d=%d", fn, a.h, a.d);
+  if (!(a.scale > 0.f) || a.scale != a.scale) return fail(HATTN_ERR_ARG, "%s: scale must be > 0", fn);
+  if (!hattn::attn_supported(a)) return fail(HATTN_ERR_UNSUPPORTED, "%s: h=%d d=%d has no kernel", fn, a.h, a.d);
+  const int64_t rows = a.bt * a.nq;
+  if (rows > 0 && (!a.q || !a.raw_kv || !a.q_pos || !a.out || (a.n > 0 && !a.ckv)))
+    return fail(HATTN_ERR_ARG, "%s: NULL required pointer", fn);
+  const size_t need = rows > 0 ? hattn::attn_ws_bytes(a) : 0;
+  hattn_status_t st;
+  if (ws_query(ws, ws_bytes, need, &st)) return st;
+  if (rows == 0) return ok();
+  return hip_status(hattn::launch_attn(a, ws, (hipStream_t)stream), fn);
+}
+
+hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx, int32_t k,
+                                 const void* raw_kv, int64_t L, const int32_t* q_pos, int32_t window, float scale,
+                                 int64_t bt, int64_t nq, int32_t h, int32_t d, float* out, float* lse, void* ws,
+                                 size_t* ws_bytes, void* stream) {
+  if (k < 0) return fail(HATTN_ERR_ARG, "sparse_attn: k < 0");
+  if (bt * nq > 0 && k > 0 && !idx) return fail(HATTN_ERR_ARG, "sparse_attn: NULL idx");
+  static const int32_t dummy = -1;
+  hattn::AttnArgs a{dtype, q, ckv, n, idx ? idx : &dummy, k, nullptr, raw_kv, L, q_pos, window, scale,
+                    bt, nq, h, d, out, lse};
+  return attn_common("sparse_attn", a, ws, ws_bytes, stream);
+}
+
+hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* n_vis,
+                                           const void* raw_kv, int64_t L, const int32_t* q_pos, int32_t window,
+                                           float scale, int64_t bt, int64_t nq, int32_t h, int32_t d, float* out,
+                                           float* lse, void* ws, size_t* ws_bytes, void* stream) {
+  if (bt * nq > 0 && !n_vis) return fail(HATTN_ERR_ARG, "dense_compressed_attn: NULL n_vis");
+  hattn::AttnArgs a{dtype, q, ckv, n, nullptr, 0, n_vis, raw_kv, L, q_pos, window, scale, bt, nq, h, d, out, lse};
+  return attn_common("dense_compressed_attn", a, ws, ws_bytes, stream);
+}
+
+hattn_status_t hattn_timer_enable(int on) {
+  if (on) {
+    g_totals.clear();
+    for (auto& p : g_pending) {
+      g_free.push_back(p.e0);
+      g_free.push_back(p.e1);
+    }
+    g_pending.clear();
+  }
+  g_timer_on = on != 0;
+  return ok();
+}
+
+hattn_status_t hattn_timer_collect(void) {
+  hipError_t err = hipSuccess;
+  for (auto& p : g_pending) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(p.e1);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.e0, p.e1);
+    if (e == hipSuccess) {
+      auto& t = g_totals[p.name];
+      t.first += ms;
+      t.second += 1;
+    } else {
+      err = e;
+    }
+    g_free.push_back(p.e0);
+    g_free.push_back(p.e1);
+  }
+  g_pending.clear();
+  return hip_status(err, "timer_collect");
+}
+
+hattn_status_t hattn_timer_query(const char* name, double* total_ms, int64_t* count) {
+  if (!name || !total_ms || !count) return fail(HATTN_ERR_ARG, "timer_query: NULL pointer");
+  auto it = g_totals.find(name);
+  if (it == g_totals.end()) return fail(HATTN_ERR_ARG, "timer_query: no kernel named %s was recorded", name);
+  *total_ms = it->second.first;
+  *count = it->second.second;
+  return ok();
+}
+
+hattn_status_t hattn_timer_names(char* buf, int64_t len) {
+  if (!buf || len < 1) return fail(HATTN_ERR_ARG, "timer_names: bad buffer");
+  std::string s;
+  for (auto& kv : g_totals) {
+    if (!s.empty()) s += '\n';
+    s += kv.first;
+  }
+  const size_t n = std::min<size_t>(s.size(), size_t(len - 1));
+  std::memcpy(buf, s.data(), n);
+  buf[n] = 0;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,713 @@
+// Lightning-indexer scores and top-k selection, flat and two-stage (HISA).
+//
+// [HISA] my.qihongyi.cn/?p=787, "DeepSeek速度狂飙4倍还不丢精度": section 01
+// (flat token indexer over the whole prefix), sections 第一阶段 / 第二阶段
+// (block-level filter on pooled representatives, then the token indexer
+// inside the chosen blocks) and section 05, Step 3 (same output form).
+//
+// Score of query q (h_i heads) against key row x:
+//     S = sum_h w[q][h] * max(0, q_i[q][h] . x)
+// The per-head dot products are a dense contraction and run on MFMA:
+//   - flat, bf16, 16 heads: 16 queries x 16 heads = 256 rows per workgroup,
+//     entries stream through LDS in tiles of 64 (16x16x32 bf16 MFMA); the
+//     ReLU, head weights and head sum happen in the accumulator epilogue;
+//   - HISA stage 1 on fp32 block means: 16x16x4 fp32 MFMA (keeps the
+//     representatives exact; they are not bf16 values);
+//   - HISA stage 2: one wave per (query, chosen block), keys gathered straight
+//     from HBM into MFMA operands.
+// Other shapes take a plain vector kernel.  Scores are written to a
+// workspace and reduced by the LDS radix select of select.h.
+#include <algorithm>
+
+#include "common.h"
+#include "internal.h"
+#include "select.h"
+
+namespace hattn {
+
+constexpr int kSelCap = 16384;  // keys per LDS-resident selection
+constexpr int kSelNT = 1024;    // threads per selection workgroup
+
+HATTN_DEV float to_f(float x) { return x; }
+HATTN_DEV float to_f(uint16_t x) { return bf16_to_f32(x); }
+
+// Decodes a linear block id so that the 8 XCDs each sweep whole key chunks:
+// the workgroups resident on one XCD share a chunk and re-read it from L2.
+HATTN_DEV bool xcd_decode(int id, int ngroups, int nchunks, int* group, int* chunk) {
+  const int xcd = id & 7;
+  const int slot = id >> 3;
+  *group = slot % ngroups;
+  *chunk = (slot / ngroups) * 8 + xcd;
+  return *chunk < nchunks;
+}
+static unsigned xcd_grid(int ngroups, int nchunks) { return unsigned(ngroups * ((nchunks + 7) / 8) * 8); }
+
+// ---------------------------------------------------------------------------
+// Flat score, bf16, 16 heads, d_i = 32*KS.
+// ---------------------------------------------------------------------------
+template <int KS>
+__global__ __launch_bounds__(256, 2) void score_flat_mfma_kernel(const uint16_t* __restrict__ q_i,
+                                                                 const uint16_t* __restrict__ k_i,
+                                                                 const float* __restrict__ w_i,
+                                                                 const int32_t* __restrict__ n_vis, int64_t nq,
+                                                                 int64_t n, int64_t ld, float* __restrict__ S,
+                                                                 int nqb, int nch, int chunk) {
+  constexpr int D = 32 * KS;
+  constexpr int TN = 64;
+  constexpr int PITCH = D + 8;
+  constexpr int PIECES = TN * D / 8 / 256;  // 16-byte pieces per thread per tile
+  __shared__ __align__(16) uint16_t kt[2][TN * PITCH];
+  __shared__ int s_nv[16];
+
+  int qb, ch;
+  if (!xcd_decode(blockIdx.x, nqb, nch, &qb, &ch)) return;
+  const int64_t b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t q0 = int64_t(qb) * 16;
+  if (threadIdx.x < 16) {
+    const int64_t q = q0 + threadIdx.x;
+    int v = 0;
+    if (q < nq) v = int(imin64(n, imax64(0, n_vis[b * nq + q])));
+    s_nv[threadIdx.x] = v;
+  }
+  __syncthreads();
+  int maxv = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) maxv = max(maxv, s_nv[i]);
+  const int64_t e_begin = int64_t(ch) * chunk;
+  const int64_t e_end = imin64(e_begin + chunk, maxv);
+  if (e_begin >= e_end) return;
+
+  u32x4_t a[4][KS];
+  float wv[4][4];
+  int nv[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t q = q0 + 4 * wave + mt;
+    const bool ok = q < nq;
+    const uint16_t* qp = q_i + ((b * nq + (ok ? q : 0)) * 16 + r16) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[mt][ks] = ok ? ld16(qp + 32 * ks) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[mt][i] = ok ? w_i[(b * nq + q) * 16 + 4 * g + i] : 0.f;
+    nv[mt] = s_nv[4 * wave + mt];
+  }
+
+  const uint16_t* kb = k_i + b * n * D;
+  u32x4_t pre[PIECES];
+  auto load = [&](int64_t e0) {
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+      const int p = threadIdx.x + 256 * j;
+      const int row = p / (D / 8), col = p % (D / 8);
+      const int64_t e = e0 + row;
+      pre[j] = e < n ? ld16(kb + e * D + col * 8) : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  load(e_begin);
+  int buf = 0;
+  for (int64_t e0 = e_begin; e0 < e_end; e0 += TN, buf ^= 1) {
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+      const int p = threadIdx.x + 256 * j;
+      const int row = p / (D / 8), col = p % (D / 8);
+      *reinterpret_cast<u32x4_t*>(&kt[buf][row * PITCH + col * 8]) = pre[j];
+    }
+    __syncthreads();
+    if (e0 + TN < e_end) load(e0 + TN);
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t bf[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+        bf[nt] = *reinterpret_cast<const u32x4_t*>(&kt[buf][(16 * nt + r16) * PITCH + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma16x16x32(a[mt][ks], bf[nt], acc[mt][nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float v[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = fmaf(wv[mt][i], fmaxf(acc[mt][nt][i], 0.f), s);
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        v[mt] = s;
+      }
+      // lane group g stores the row of query 4*wave + g
+      const float mine = g == 0 ? v[0] : g == 1 ? v[1] : g == 2 ? v[2] : v[3];
+      const int64_t e = e0 + 16 * nt + r16;
+      const int64_t q = q0 + 4 * wave + g;
+      const int nvg = g == 0 ? nv[0] : g == 1 ? nv[1] : g == 2 ? nv[2] : nv[3];
+      if (q < nq && e < nvg) S[(b * nq + q) * ld + e] = mine;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// HISA stage 1 score on fp32 block representatives, 16 heads, d_i = 16*KQ.
+// One wave per query (4 queries per workgroup), blocks in LDS tiles of 64.
+// ---------------------------------------------------------------------------
+template <typename TQ, int KQ>
+__global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restrict__ q_i,
+                                                              const float* __restrict__ reps,
+                                                              const float* __restrict__ w_i,
+                                                              const int32_t* __restrict__ n_vis, int64_t nq,
+                                                              int64_t n, int B, int64_t nb, int64_t ld,
+                                                              float* __restrict__ S1, int nqg, int nch, int chunk) {
+  constexpr int D = 16 * KQ;
+  constexpr int TB = 64;
+  constexpr int PITCH = D + 4;
+  constexpr int PIECES = TB * D / 4 / 256;
+  __shared__ __align__(16) float rt[TB * PITCH];
+  __shared__ int s_nb[4];
+
+  int qg, ch;
+  if (!xcd_decode(blockIdx.x, nqg, nch, &qg, &ch)) return;
+  const int64_t b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t q = int64_t(qg) * 4 + wave;
+  if (threadIdx.x < 4) {
+    const int64_t qq = int64_t(qg) * 4 + threadIdx.x;
+    int v = 0;
+    if (qq < nq) {
+      const int64_t nvq = imin64(n, imax64(0, n_vis[b * nq + qq]));
+      v = int((nvq + B - 1) / B);
+    }
+    s_nb[threadIdx.x] = v;
+  }
+  __syncthreads();
+  const int maxb = max(max(s_nb[0], s_nb[1]), max(s_nb[2], s_nb[3]));
+  const int64_t j_begin = int64_t(ch) * chunk;
+  const int64_t j_end = imin64(j_begin + chunk, maxb);
+  if (j_begin >= j_end) return;
+  const bool ok = q < nq;
+  const int my_nb = s_nb[wave];
+
+  f32x4_t a[KQ];
+  float wv[4];
+  {
+    const TQ* qp = q_i + ((b * nq + (ok ? q : 0)) * 16 + r16) * D + 4 * g;
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[kq][j] = ok ? to_f(qp[16 * kq + j]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wv[i] = ok ? w_i[(b * nq + q) * 16 + 4 * g + i] : 0.f;
+  }
+  const float* rb = reps + b * nb * D;
+  for (int64_t j0 = j_begin; j0 < j_end; j0 += TB) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int p = threadIdx.x + 256 * u;
+      const int row = p / (D / 4), col = p % (D / 4);
+      const int64_t j = j0 + row;
+      const u32x4_t v = j < nb ? ld16(rb + j * D + col * 4) : u32x4_t{0, 0, 0, 0};
+      *reinterpret_cast<u32x4_t*>(&rt[row * PITCH + col * 4]) = v;
+    }
+    __syncthreads();
+    if (!ok || j0 >= my_nb) continue;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&rt[(16 * nt + r16) * PITCH + 16 * kq + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kq][j], bv[j], acc[nt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = fmaf(wv[i], fmaxf(acc[nt][i], 0.f), s);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      const int64_t j = j0 + 16 * nt + r16;
+      if (g == 0 && j < my_nb) S1[(b * nq + q) * ld + j] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// HISA stage 2 score, bf16, 16 heads: one wave per (query, chosen block).
+// Candidate position j = slot*B + offset; visible candidates form a prefix.
+// ---------------------------------------------------------------------------
+template <int KS>
+__global__ __launch_bounds__(64) void score_stage2_mfma_kernel(const uint16_t* __restrict__ q_i,
+                                                               const uint16_t* __restrict__ k_i,
+                                                               const float* __restrict__ w_i,
+                                                               const int32_t* __restrict__ n_vis,
+                                                               const int32_t* __restrict__ blk, int64_t nq, int64_t n,
+                                                               int B, int m, int64_t ld, float* __restrict__ S2) {
+  constexpr int D = 32 * KS;
+  const int64_t row = blockIdx.y;
+  const int slot = blockIdx.x;
+  const int64_t b = row / nq;
+  const int bid = blk[row * m + slot];
+  if (bid < 0) return;
+  const int64_t nv = imin64(n, imax64(0, n_vis[row]));
+  const int64_t e_begin = int64_t(bid) * B;
+  const int64_t e_end = imin64(e_begin + B, nv);
+  if (e_begin >= e_end) return;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, r16 = lane & 15;
+  u32x4_t a[KS];
+  const uint16_t* qp = q_i + (row * 16 + r16) * D + 8 * g;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) a[ks] = ld16(qp + 32 * ks);
+  float wv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wv[i] = w_i[row * 16 + 4 * g + i];
+  const uint16_t* kb = k_i + b * n * D + 8 * g;
+  float* out = S2 + row * ld + int64_t(slot) * B;
+  for (int64_t e0 = e_begin; e0 < e_end; e0 += 64) {
+    u32x4_t bf[4][KS];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int64_t e = e0 + 16 * nt + r16;
+      const bool ok = e < e_end;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bf[nt][ks] = ok ? ld16(kb + e * D + 32 * ks) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ks], bf[nt][ks], acc);
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = fmaf(wv[i], fmaxf(acc[i], 0.f), s);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      const int64_t e = e0 + 16 * nt + r16;
+      if (g == 0 && e < e_end) out[e - e_begin] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Vector fallback for any dtype / head count / dim.  MODE 0: flat entries;
+// MODE 1: stage-1 block representatives (fp32 keys); MODE 2: stage-2
+// entries inside the chosen blocks.  One query per workgroup row of the grid.
+// ---------------------------------------------------------------------------
+template <typename TQ, typename TK, int MODE>
+__global__ __launch_bounds__(256) void score_valu_kernel(const TQ* __restrict__ q_i, const TK* __restrict__ keys,
+                                                         const float* __restrict__ w_i,
+                                                         const int32_t* __restrict__ n_vis,
+                                                         const int32_t* __restrict__ blk, int64_t nq, int h_i,
+                                                         int d_i, int64_t n, int64_t keys_per_seq, int B, int m,
+                                                         int64_t ld, float* __restrict__ S) {
+  extern __shared__ float qs[];  // [h_i][d_i] then [h_i] weights
+  const int64_t row = blockIdx.y;
+  const int64_t b = row / nq;
+  for (int i = threadIdx.x; i < h_i * d_i; i += blockDim.x) qs[i] = to_f(q_i[row * h_i * d_i + i]);
+  for (int i = threadIdx.x; i < h_i; i += blockDim.x) qs[h_i * d_i + i] = w_i[row * h_i + i];
+  __syncthreads();
+  const int64_t nv = imin64(n, imax64(0, n_vis[row]));
+  const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  int64_t krow;
+  if (MODE == 0) {
+    if (j >= nv) return;
+    krow = j;
+  } else if (MODE == 1) {
+    if (j >= (nv + B - 1) / B) return;
+    krow = j;
+  } else {
+    const int64_t slot = j / B;
+    if (slot >= m) return;
+    const int bid = blk[row * m + slot];
+    const int64_t e = int64_t(bid) * B + (j % B);
+    if (bid < 0 || e >= nv) return;
+    krow = e;
+  }
+  const TK* kp = keys + (b * keys_per_seq + krow) * d_i;
+  float s = 0.f;
+  for (int h = 0; h < h_i; ++h) {
+    float dot = 0.f;
+    for (int c = 0; c < d_i; ++c) dot = fmaf(qs[h * d_i + c], to_f(kp[c]), dot);
+    s = fmaf(qs[h_i * d_i + h], fmaxf(dot, 0.f), s);
+  }
+  S[row * ld + j] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Selection kernels.
+// ---------------------------------------------------------------------------
+// Number of valid candidates of a row.  MODE 0: visible entries; MODE 1:
+// blocks whose first entry is visible; MODE 2: visible entries inside the
+// chosen blocks (a prefix of slot space, see the stage-2 kernel).
+template <int MODE>
+HATTN_DEV int row_valid_count(const int32_t* n_vis, const int32_t* blk, int64_t row, int64_t n, int B, int m, int* red) {
+  const int64_t nv = imin64(n, imax64(0, n_vis[row]));
+  if (MODE == 0) return int(nv);
+  if (MODE == 1) return int((nv + B - 1) / B);
+  int c = 0;
+  for (int s = threadIdx.x; s < m; s += blockDim.x) {
+    const int bid = blk[row * m + s];
+    if (bid >= 0) c += int(imax64(0, imin64(B, nv - int64_t(bid) * B)));
+  }
+  c = wave_sum(c);
+  if ((threadIdx.x & 63) == 0) atomicAdd(red, c);
+  __syncthreads();
+  return *red;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __restrict__ S, int64_t ld,
+                                                             const int32_t* __restrict__ n_vis,
+                                                             const int32_t* __restrict__ blk, int64_t n, int B, int m,
+                                                             int k, int32_t* __restrict__ idx,
+                                                             float* __restrict__ score_out) {
+  extern __shared__ uint32_t keys[];
+  __shared__ SelectShared<kSelNT> sh;
+  __shared__ int cnt;
+  const int64_t row = blockIdx.x;
+  if (threadIdx.x == 0) cnt = 0;
+  __syncthreads();
+  const int nvalid = min(kSelCap, row_valid_count<MODE>(n_vis, blk, row, n, B, m, &cnt));
+  const float* srow = S + row * ld;
+  for (int i = threadIdx.x; i < nvalid; i += kSelNT) keys[i] = order_key(srow[i]);
+  __syncthreads();
+  radix_threshold<kSelNT>(keys, nvalid, k, sh);
+  int32_t* orow = idx + row * k;
+  float* scrow = score_out ? score_out + row * k : nullptr;
+  const int32_t* brow = blk + row * m;
+  const int chosen = emit_selected<kSelNT>(keys, nvalid, sh, [&](int slot, int i) {
+    int32_t v = i;
+    if (MODE == 2) v = brow[i / B] * B + (i % B);
+    orow[slot] = v;
+    if (scrow) scrow[slot] = key_to_float(keys[i]);
+  });
+  for (int s = chosen + threadIdx.x; s < k; s += kSelNT) {
+    orow[s] = -1;
+    if (scrow) scrow[s] = -INFINITY;
+  }
+}
+
+// Level 1 for long flat rows: exact top-k of each segment (an element outside
+// its segment's top-k has k larger elements and cannot be chosen overall).
+__global__ __launch_bounds__(kSelNT) void select_segment_kernel(const float* __restrict__ S, int64_t ld,
+                                                                const int32_t* __restrict__ n_vis, int64_t n, int seg,
+                                                                int nseg, int k, uint32_t* __restrict__ ckey,
+                                                                int32_t* __restrict__ cpos) {
+  extern __shared__ uint32_t keys[];
+  __shared__ SelectShared<kSelNT> sh;
+  const int64_t row = blockIdx.y;
+  const int s = blockIdx.x;
+  const int64_t nv = imin64(n, imax64(0, n_vis[row]));
+  const int64_t p0 = int64_t(s) * seg;
+  const int cnt = int(imax64(0, imin64(seg, nv - p0)));
+  const float* srow = S + row * ld + p0;
+  for (int i = threadIdx.x; i < cnt; i += kSelNT) keys[i] = order_key(srow[i]);
+  __syncthreads();
+  radix_threshold<kSelNT>(keys, cnt, k, sh);
+  uint32_t* ok = ckey + (row * nseg + s) * int64_t(k);
+  int32_t* op = cpos + (row * nseg + s) * int64_t(k);
+  const int chosen = emit_selected<kSelNT>(keys, cnt, sh, [&](int slot, int i) {
+    ok[slot] = keys[i];
+    op[slot] = int32_t(p0 + i);
+  });
+  for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+    ok[t] = 0u;
+    op[t] = -1;
+  }
+}
+
+// Level >= 2: merges groups of G candidate lists (ascending positions, key 0
+// = empty slot).  With one group left it writes the final indices.
+__global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __restrict__ ikey,
+                                                              const int32_t* __restrict__ ipos, int nin, int G, int k,
+                                                              uint32_t* __restrict__ okey, int32_t* __restrict__ opos,
+                                                              int32_t* __restrict__ idx, float* __restrict__ score_out) {
+  extern __shared__ uint32_t keys[];
+  __shared__ SelectShared<kSelNT> sh;
+  int32_t* pos = reinterpret_cast<int32_t*>(keys + kSelCap);
+  const int64_t row = blockIdx.y;
+  const int grp = blockIdx.x;
+  const int nout = (nin + G - 1) / G;
+  const int l0 = grp * G, l1 = min(nin, l0 + G);
+  const int cnt = (l1 - l0) * k;
+  const uint32_t* ik = ikey + (row * nin + l0) * int64_t(k);
+  const int32_t* ip = ipos + (row * nin + l0) * int64_t(k);
+  for (int i = threadIdx.x; i < cnt; i += kSelNT) {
+    keys[i] = ik[i];
+    pos[i] = ip[i];
+  }
+  __syncthreads();
+  radix_threshold<kSelNT>(keys, cnt, k, sh);
+  if (nout == 1) {
+    int32_t* orow = idx + row * k;
+    float* scrow = score_out ? score_out + row * k : nullptr;
+    const int chosen = emit_selected<kSelNT>(keys, cnt, sh, [&](int slot, int i) {
+      orow[slot] = pos[i];
+      if (scrow) scrow[slot] = key_to_float(keys[i]);
+    });
+    for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+      orow[t] = -1;
+      if (scrow) scrow[t] = -INFINITY;
+    }
+  } else {
+    uint32_t* ok = okey + (row * nout + grp) * int64_t(k);
+    int32_t* op = opos + (row * nout + grp) * int64_t(k);
+    const int chosen = emit_selected<kSelNT>(keys, cnt, sh, [&](int slot, int i) {
+      ok[slot] = keys[i];
+      op[slot] = pos[i];
+    });
+    for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+      ok[t] = 0u;
+      op[t] = -1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+static int64_t round4(int64_t x) { return (x + 3) & ~int64_t(3); }
+
+static bool flat_mfma_ok(const IndexArgs& a) {
+  return a.dtype == 1 && a.h_i == 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128 || a.d_i == 256);
+}
+
+struct FlatPlan {
+  int64_t rows, ld;
+  bool multi;
+  int seg, nseg, G;
+  size_t s_bytes, cand_bytes, total;
+};
+
+static FlatPlan plan_flat(const IndexArgs& a, int k) {
+  FlatPlan p{};
+  p.rows = a.bt * a.nq;
+  p.ld = round4(std::max<int64_t>(a.n, 1));
+  p.multi = a.n > kSelCap;
+  p.s_bytes = align256(size_t(p.rows) * p.ld * 4);
+  if (p.multi) {
+    p.seg = kSelCap;
+    p.nseg = int((a.n + p.seg - 1) / p.seg);
+    p.G = kSelCap / k;
+    // ping-pong candidate buffers: level-1 lists, then merged lists
+    const size_t l1 = size_t(p.rows) * p.nseg * k * 8;
+    const size_t l2 = size_t(p.rows) * ((p.nseg + p.G - 1) / p.G) * k * 8;
+    p.cand_bytes = align256(l1) + align256(l2);
+  }
+  p.total = p.s_bytes + p.cand_bytes;
+  return p;
+}
+
+size_t flat_topk_ws_bytes(const IndexArgs& a, int k) { return plan_flat(a, k).total; }
+
+static void set_lds_limits() {
+  static bool done = false;
+  if (done) return;
+  done = true;
+  (void)hipFuncSetAttribute((const void*)select_rows_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
+  (void)hipFuncSetAttribute((const void*)select_rows_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
+  (void)hipFuncSetAttribute((const void*)select_rows_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
+  (void)hipFuncSetAttribute((const void*)select_segment_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
+  (void)hipFuncSetAttribute((const void*)select_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 8);
+}
+
+template <int MODE, typename TQ, typename TK>
+static void launch_valu_score(const IndexArgs& a, const TK* keys, int64_t keys_per_seq, int64_t ncand,
+                              const int32_t* blk, int B, int m, int64_t ld, float* S, hipStream_t st) {
+  const size_t smem = size_t(a.h_i) * a.d_i * 4 + size_t(a.h_i) * 4;
+  dim3 grid(unsigned((ncand + 255) / 256), unsigned(a.bt * a.nq));
+  LaunchScope ls(MODE == 0 ? "score_valu_flat" : MODE == 1 ? "score_valu_stage1" : "score_valu_stage2", st);
+  hipLaunchKernelGGL((score_valu_kernel<TQ, TK, MODE>), grid, dim3(256), smem, st, (const TQ*)a.q_i, keys, a.w_i,
+                     a.n_vis, blk, a.nq, a.h_i, a.d_i, a.n, keys_per_seq, B, m, ld, S);
+}
+
+static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, hipStream_t st) {
+  if (flat_mfma_ok(a)) {
+    const int nqb = int((a.nq + 15) / 16);
+    const int chunk = 2048;
+    const int nch = int((a.n + chunk - 1) / chunk);
+    dim3 grid(xcd_grid(nqb, nch), unsigned(a.bt));
+    LaunchScope ls("score_flat_mfma", st);
+#define HATTN_FLAT(KS)                                                                                       \
+  hipLaunchKernelGGL(score_flat_mfma_kernel<KS>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i,             \
+                     (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk)
+    switch (a.d_i) {
+      case 32: HATTN_FLAT(1); break;
+      case 64: HATTN_FLAT(2); break;
+      case 128: HATTN_FLAT(4); break;
+      default: HATTN_FLAT(8); break;
+    }
+#undef HATTN_FLAT
+  } else if (a.dtype == 0) {
+    launch_valu_score<0, float>(a, (const float*)a.k_i, a.n, a.n, nullptr, 1, 1, ld, S, st);
+  } else {
+    launch_valu_score<0, uint16_t>(a, (const uint16_t*)a.k_i, a.n, a.n, nullptr, 1, 1, ld, S, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* score, void* ws, hipStream_t st) {
+  set_lds_limits();
+  const FlatPlan p = plan_flat(a, k);
+  float* S = reinterpret_cast<float*>(ws);
+  hipError_t e = launch_flat_score(a, p.ld, S, st);
+  if (e != hipSuccess) return e;
+  if (!p.multi) {
+    LaunchScope ls("select_rows", st);
+    hipLaunchKernelGGL(select_rows_kernel<0>, dim3(unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st, S, p.ld, a.n_vis,
+                       nullptr, a.n, 1, 1, k, idx, score);
+    return hipGetLastError();
+  }
+  char* cb = reinterpret_cast<char*>(ws) + p.s_bytes;
+  const size_t l1 = align256(size_t(p.rows) * p.nseg * k * 8);
+  uint32_t* bufk[2];
+  int32_t* bufp[2];
+  bufk[0] = reinterpret_cast<uint32_t*>(cb);
+  bufp[0] = reinterpret_cast<int32_t*>(cb + size_t(p.rows) * p.nseg * k * 4);
+  bufk[1] = reinterpret_cast<uint32_t*>(cb + l1);
+  const int n2 = (p.nseg + p.G - 1) / p.G;
+  bufp[1] = reinterpret_cast<int32_t*>(cb + l1 + size_t(p.rows) * n2 * k * 4);
+  {
+    LaunchScope ls("select_segment", st);
+    hipLaunchKernelGGL(select_segment_kernel, dim3(unsigned(p.nseg), unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st,
+                       S, p.ld, a.n_vis, a.n, p.seg, p.nseg, k, bufk[0], bufp[0]);
+  }
+  int nin = p.nseg, cur = 0;
+  while (true) {
+    const int nout = (nin + p.G - 1) / p.G;
+    LaunchScope ls("select_merge", st);
+    // Lists of a row at level i+1 never outnumber those at level i, so the
+    // two buffers (sized for levels 1 and 2) alternate safely.
+    hipLaunchKernelGGL(select_merge_kernel, dim3(unsigned(nout), unsigned(p.rows)), dim3(kSelNT), kSelCap * 8, st,
+                       bufk[cur], bufp[cur], nin, p.G, k, bufk[cur ^ 1], bufp[cur ^ 1], idx, score);
+    e = hipGetLastError();
+    if (e != hipSuccess || nout == 1) return e;
+    nin = nout;
+    cur ^= 1;
+  }
+}
+
+// ---- HISA -------------------------------------------------------------------
+struct HisaPlan {
+  int64_t rows, nb, ld1, ld2;
+  size_t s1_bytes, blk_bytes, s2_bytes, total;
+};
+
+static HisaPlan plan_hisa(const IndexArgs& a, int B, int m) {
+  HisaPlan p{};
+  p.rows = a.bt * a.nq;
+  p.nb = (a.n + B - 1) / B;
+  p.ld1 = round4(std::max<int64_t>(p.nb, 1));
+  p.ld2 = round4(int64_t(m) * B);
+  p.s1_bytes = align256(size_t(p.rows) * p.ld1 * 4);
+  p.blk_bytes = align256(size_t(p.rows) * m * 4);
+  p.s2_bytes = align256(size_t(p.rows) * p.ld2 * 4);
+  p.total = p.s1_bytes + p.blk_bytes + p.s2_bytes;
+  return p;
+}
+
+size_t hisa_topk_ws_bytes(const IndexArgs& a, int B, int m, int k) {
+  (void)k;
+  return plan_hisa(a, B, m).total;
+}
+
+hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m, int k, int32_t* idx, int32_t* blk,
+                            void* ws, hipStream_t st) {
+  set_lds_limits();
+  const HisaPlan p = plan_hisa(a, B, m);
+  char* base = reinterpret_cast<char*>(ws);
+  float* S1 = reinterpret_cast<float*>(base);
+  int32_t* blk_ws = reinterpret_cast<int32_t*>(base + p.s1_bytes);
+  float* S2 = reinterpret_cast<float*>(base + p.s1_bytes + p.blk_bytes);
+  int32_t* blk_out = blk ? blk : blk_ws;
+
+  // Stage 1: block scores.
+  const bool mfma1 = a.h_i == 16 && a.d_i % 16 == 0 && a.d_i <= 256;
+  if (mfma1) {
+    const int nqg = int((a.nq + 3) / 4);
+    const int chunk = 256;
+    const int nch = int((p.nb + chunk - 1) / chunk);
+    dim3 grid(xcd_grid(nqg, nch), unsigned(a.bt));
+    LaunchScope ls("score_stage1_mfma", st);
+#define HATTN_S1(T, KQ)                                                                                      \
+  hipLaunchKernelGGL((score_stage1_kernel<T, KQ>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i,      \
+                     a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk)
+    if (a.dtype == 0) {
+      switch (a.d_i / 16) {
+        case 1: HATTN_S1(float, 1); break;
+        case 2: HATTN_S1(float, 2); break;
+        case 4: HATTN_S1(float, 4); break;
+        case 8: HATTN_S1(float, 8); break;
+        default: HATTN_S1(float, 16); break;
+      }
+    } else {
+      switch (a.d_i / 16) {
+        case 1: HATTN_S1(uint16_t, 1); break;
+        case 2: HATTN_S1(uint16_t, 2); break;
+        case 4: HATTN_S1(uint16_t, 4); break;
+        case 8: HATTN_S1(uint16_t, 8); break;
+        default: HATTN_S1(uint16_t, 16); break;
+      }
+    }
+#undef HATTN_S1
+  } else if (a.dtype == 0) {
+    launch_valu_score<1, float>(a, reps, p.nb, p.nb, nullptr, B, m, p.ld1, S1, st);
+  } else {
+    launch_valu_score<1, uint16_t>(a, reps, p.nb, p.nb, nullptr, B, m, p.ld1, S1, st);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    LaunchScope ls("select_blocks", st);
+    hipLaunchKernelGGL(select_rows_kernel<1>, dim3(unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st, S1, p.ld1,
+                       a.n_vis, nullptr, a.n, B, m, m, blk_out, nullptr);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // Stage 2: token scores inside the chosen blocks.
+  const bool mfma2 = a.dtype == 1 && a.h_i == 16 && B % 16 == 0 &&
+                     (a.d_i == 32 || a.d_i == 64 || a.d_i == 128 || a.d_i == 256);
+  if (mfma2) {
+    dim3 grid(unsigned(m), unsigned(p.rows));
+    LaunchScope ls("score_stage2_mfma", st);
+#define HATTN_S2(KS)                                                                                         \
+  hipLaunchKernelGGL(score_stage2_mfma_kernel<KS>, grid, dim3(64), 0, st, (const uint16_t*)a.q_i,           \
+                     (const uint16_t*)a.k_i, a.w_i, a.n_vis, blk_out, a.nq, a.n, B, m, p.ld2, S2)
+    switch (a.d_i) {
+      case 32: HATTN_S2(1); break;
+      case 64: HATTN_S2(2); break;
+      case 128: HATTN_S2(4); break;
+      default: HATTN_S2(8); break;
+    }
+#undef HATTN_S2
+  } else if (a.dtype == 0) {
+    launch_valu_score<2, float>(a, (const float*)a.k_i, a.n, int64_t(m) * B, blk_out, B, m, p.ld2, S2, st);
+  } else {
+    launch_valu_score<2, uint16_t>(a, (const uint16_t*)a.k_i, a.n, int64_t(m) * B, blk_out, B, m, p.ld2, S2, st);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    LaunchScope ls("select_tokens", st);
+    hipLaunchKernelGGL(select_rows_kernel<2>, dim3(unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st, S2, p.ld2,
+                       a.n_vis, blk_out, a.n, B, m, k, idx, nullptr);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hattn

@@ -1,0 +1,71 @@
+// Internal host-side interface between the C ABI (hattn.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hattn {
+
+// Brackets one kernel launch with timer events when the kernel timer is on.
+struct LaunchScope {
+  LaunchScope(const char* name, hipStream_t s);
+  ~LaunchScope();
+  const char* name_;
+  hipStream_t stream_;
+  void* ev0_;
+};
+
+// ---- compression / geometry / pooling -------------------------------------
+hipError_t launch_compress(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z,
+                           const float* bias, int w, int s, int64_t N, int64_t e0, int64_t e1, void* y,
+                           hipStream_t st);
+hipError_t launch_visible_count(const int32_t* pos, int64_t count, int w, int s, int64_t n_entries,
+                                int32_t* n_vis, hipStream_t st);
+hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_i, int B, int64_t j0,
+                       int64_t j1, float* reps, hipStream_t st);
+
+// ---- indexer ---------------------------------------------------------------
+struct IndexArgs {
+  int dtype;
+  const void* q_i;
+  const void* k_i;
+  const float* w_i;
+  const int32_t* n_vis;
+  int64_t bt, nq;
+  int h_i, d_i;
+  int64_t n;
+};
+
+size_t flat_topk_ws_bytes(const IndexArgs& a, int k);
+hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* score, void* ws, hipStream_t st);
+
+size_t hisa_topk_ws_bytes(const IndexArgs& a, int B, int m, int k);
+hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m, int k, int32_t* idx,
+                            int32_t* blk, void* ws, hipStream_t st);
+
+// ---- attention -------------------------------------------------------------
+struct AttnArgs {
+  int dtype;
+  const void* q;
+  const void* ckv;
+  int64_t n;
+  const int32_t* idx;    // sparse: [bt][nq][k]
+  int k;                 // sparse list length
+  const int32_t* n_vis;  // dense: [bt][nq]
+  const void* raw_kv;
+  int64_t L;
+  const int32_t* q_pos;
+  int window;
+  float scale;
+  int64_t bt, nq;
+  int h, d;
+  float* out;
+  float* lse;
+};
+
+size_t attn_ws_bytes(const AttnArgs& a);
+hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st);
+bool attn_supported(const AttnArgs& a);
+
+}  // namespace hattn

@@ -1,0 +1,247 @@
+"""Torch-facing wrappers of the libhattn C ABI.
+
+Argument marshalling only: every step runs in the HIP kernels of
+libhattn.so, on the caller's current stream.  Tensors must be contiguous
+CUDA tensors; floating inputs are all fp32 or all bf16 (indexer head weights
+and compression logits are always fp32).  See include/hattn.h for the exact
+definition of each operation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import check, lib
+
+_DT = {torch.float32: 0, torch.bfloat16: 1}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a CUDA (HIP) device; there is no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _fdt(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"{name} must be float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+# One workspace per (device, stream, purpose), grown on demand.  Calls on one
+# stream are ordered, so they may share it; the torch caching allocator keeps
+# a replaced buffer alive until the stream has passed its last use.
+_WS: dict = {}
+
+
+def _workspace(key, nbytes: int, device) -> torch.Tensor:
+    t = _WS.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = t
+    return t
+
+
+def _ws_call(fn_name: str, key, device, call):
+    """Runs a C call twice: size query (ws=NULL), then with the workspace."""
+    sz = ctypes.c_size_t(0)
+    check(fn_name, call(None, ctypes.byref(sz)))
+    if sz.value == 0:
+        check(fn_name, call(None, None))
+        return
+    ws = _workspace(key, sz.value, device)
+    have = ctypes.c_size_t(ws.numel())
+    check(fn_name, call(_ptr(ws), ctypes.byref(have)))
+
+
+def compress(x, logits, pos_bias, w: int, stride: int, e_begin: int = 0, e_end: int | None = None, out=None):
+    """Softmax-weighted window merge: x [bt][L][C] -> [bt][N][C] (x's dtype)."""
+    _need(x, "x", ndim=3)
+    dt = _fdt(x, "x")
+    bt, L, C = x.shape
+    N = (L - w) // stride + 1 if L >= w else 0
+    if logits is not None:
+        _need(logits, "logits", torch.float32, 2)
+        if tuple(logits.shape) != (bt, L):
+            raise ValueError("logits must be [bt][L]")
+    if pos_bias is not None:
+        _need(pos_bias, "pos_bias", torch.float32, 1)
+        if pos_bias.numel() != w:
+            raise ValueError("pos_bias must have w elements")
+    if e_end is None:
+        e_end = N
+    if out is None:
+        out = torch.empty((bt, N, C), dtype=x.dtype, device=x.device)
+    else:
+        _need(out, "out", x.dtype, 3)
+        if tuple(out.shape) != (bt, N, C):
+            raise ValueError(f"out must be [{bt}][{N}][{C}]")
+    check("hattn_compress", lib().hattn_compress(dt, _ptr(x), bt, L, C, _ptr(logits), _ptr(pos_bias), w, stride,
+                                                 e_begin, e_end, _ptr(out), _stream(x.device)))
+    return out
+
+
+def visible_count(pos, w: int, stride: int, n_entries: int, out=None):
+    """Entries visible at each raw position: int32 tensor shaped like pos."""
+    _need(pos, "pos", torch.int32)
+    if out is None:
+        out = torch.empty_like(pos)
+    check("hattn_visible_count", lib().hattn_visible_count(_ptr(pos), pos.numel(), w, stride, n_entries, _ptr(out),
+                                                           _stream(pos.device)))
+    return out
+
+
+def _index_common(q_i, k_i, w_i, n_vis):
+    _need(q_i, "q_i", ndim=4)
+    dt = _fdt(q_i, "q_i")
+    _need(k_i, "k_i", q_i.dtype, 3)
+    _need(w_i, "w_i", torch.float32, 3)
+    _need(n_vis, "n_vis", torch.int32, 2)
+    bt, nq, h_i, d_i = q_i.shape
+    if k_i.shape[0] != bt or k_i.shape[2] != d_i or tuple(w_i.shape) != (bt, nq, h_i) or tuple(n_vis.shape) != (bt, nq):
+        raise ValueError("indexer shapes disagree")
+    return dt, bt, nq, h_i, d_i, k_i.shape[1]
+
+
+def index_topk(q_i, k_i, w_i, n_vis, k: int, return_scores: bool = False):
+    """Flat indexer: idx [bt][nq][k] int32 (ascending, -1 padded)."""
+    dt, bt, nq, h_i, d_i, n = _index_common(q_i, k_i, w_i, n_vis)
+    idx = torch.empty((bt, nq, k), dtype=torch.int32, device=q_i.device)
+    sc = torch.empty((bt, nq, k), dtype=torch.float32, device=q_i.device) if return_scores else None
+    L = lib()
+    st = _stream(q_i.device)
+
+    def call(ws, szp):
+        return L.hattn_index_topk(dt, _ptr(q_i), _ptr(k_i), _ptr(w_i), _ptr(n_vis), bt, nq, h_i, d_i, n, k,
+                                  _ptr(idx), _ptr(sc), ws, szp, st)
+
+    _ws_call("hattn_index_topk", ("index", q_i.device, st.value), q_i.device, call)
+    return (idx, sc) if return_scores else idx
+
+
+def hisa_pool(k_i, B: int, j_begin: int = 0, j_end: int | None = None, out=None):
+    """Block means of k_i [bt][n][d_i] -> fp32 [bt][ceil(n/B)][d_i]."""
+    _need(k_i, "k_i", ndim=3)
+    dt = _fdt(k_i, "k_i")
+    bt, n, d_i = k_i.shape
+    nb = -(-n // B)
+    if j_end is None:
+        j_end = nb
+    if out is None:
+        out = torch.empty((bt, nb, d_i), dtype=torch.float32, device=k_i.device)
+    else:
+        _need(out, "out", torch.float32, 3)
+    check("hattn_hisa_pool", lib().hattn_hisa_pool(dt, _ptr(k_i), bt, n, d_i, B, j_begin, j_end, _ptr(out),
+                                                   _stream(k_i.device)))
+    return out
+
+
+def hisa_topk(q_i, k_i, w_i, n_vis, reps, B: int, m: int, k: int, return_blocks: bool = False):
+    """Two-stage HISA selection: idx [bt][nq][k] (and blocks [bt][nq][m])."""
+    dt, bt, nq, h_i, d_i, n = _index_common(q_i, k_i, w_i, n_vis)
+    _need(reps, "reps", torch.float32, 3)
+    if tuple(reps.shape) != (bt, -(-n // B), d_i):
+        raise ValueError("reps must be [bt][ceil(n/B)][d_i]")
+    idx = torch.empty((bt, nq, k), dtype=torch.int32, device=q_i.device)
+    blk = torch.empty((bt, nq, m), dtype=torch.int32, device=q_i.device) if return_blocks else None
+    L = lib()
+    st = _stream(q_i.device)
+
+    def call(ws, szp):
+        return L.hattn_hisa_topk(dt, _ptr(q_i), _ptr(k_i), _ptr(w_i), _ptr(n_vis), bt, nq, h_i, d_i, n, _ptr(reps),
+                                 B, m, k, _ptr(idx), _ptr(blk), ws, szp, st)
+
+    _ws_call("hattn_hisa_topk", ("hisa", q_i.device, st.value), q_i.device, call)
+    return (idx, blk) if return_blocks else idx
+
+
+def _attn_common(q, ckv, raw_kv, q_pos):
+    _need(q, "q", ndim=4)
+    dt = _fdt(q, "q")
+    _need(ckv, "ckv", q.dtype, 3)
+    _need(raw_kv, "raw_kv", q.dtype, 3)
+    _need(q_pos, "q_pos", torch.int32, 2)
+    bt, nq, h, d = q.shape
+    if ckv.shape[0] != bt or ckv.shape[2] != 2 * d or raw_kv.shape[0] != bt or raw_kv.shape[2] != 2 * d:
+        raise ValueError("K|V rows must be [.., 2*d]")
+    if tuple(q_pos.shape) != (bt, nq):
+        raise ValueError("q_pos must be [bt][nq]")
+    return dt, bt, nq, h, d
+
+
+def sparse_attn(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = None, return_lse: bool = False):
+    """Attention over ckv[idx] plus the raw window: out [bt][nq][h][d] fp32."""
+    dt, bt, nq, h, d = _attn_common(q, ckv, raw_kv, q_pos)
+    _need(idx, "idx", torch.int32, 3)
+    if idx.shape[:2] != (bt, nq):
+        raise ValueError("idx must be [bt][nq][k]")
+    k = idx.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = torch.empty((bt, nq, h, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((bt, nq, h), dtype=torch.float32, device=q.device) if return_lse else None
+    L = lib()
+    st = _stream(q.device)
+
+    def call(ws, szp):
+        return L.hattn_sparse_attn(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(idx), k, _ptr(raw_kv), raw_kv.shape[1],
+                                   _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out), _ptr(lse), ws, szp, st)
+
+    _ws_call("hattn_sparse_attn", ("attn", q.device, st.value), q.device, call)
+    return (out, lse) if return_lse else out
+
+
+def dense_compressed_attn(q, ckv, n_vis, raw_kv, q_pos, window: int, scale: float | None = None,
+                          return_lse: bool = False):
+    """Attention over ckv[0 .. n_vis) plus the raw window: out [bt][nq][h][d] fp32."""
+    dt, bt, nq, h, d = _attn_common(q, ckv, raw_kv, q_pos)
+    _need(n_vis, "n_vis", torch.int32, 2)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = torch.empty((bt, nq, h, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((bt, nq, h), dtype=torch.float32, device=q.device) if return_lse else None
+    L = lib()
+    st = _stream(q.device)
+
+    def call(ws, szp):
+        return L.hattn_dense_compressed_attn(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(n_vis), _ptr(raw_kv),
+                                             raw_kv.shape[1], _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out),
+                                             _ptr(lse), ws, szp, st)
+
+    _ws_call("hattn_dense_compressed_attn", ("attn", q.device, st.value), q.device, call)
+    return (out, lse) if return_lse else out
+
+
+# ---- kernel timer -----------------------------------------------------------
+
+def timer_enable(on: bool) -> None:
+    check("hattn_timer_enable", lib().hattn_timer_enable(1 if on else 0))
+
+
+def timer_collect() -> dict:
+    """Waits for recorded launches; returns {kernel: (total_ms, count)}."""
+    L = lib()
+    check("hattn_timer_collect", L.hattn_timer_collect())
+    buf = ctypes.create_string_buffer(1 << 16)
+    check("hattn_timer_names", L.hattn_timer_names(buf, len(buf)))
+    out = {}
+    for name in filter(None, buf.value.decode().split("\n")):
+        ms, cnt = ctypes.c_double(), ctypes.c_int64()
+        check("hattn_timer_query", L.hattn_timer_query(name.encode(), ctypes.byref(ms), ctypes.byref(cnt)))
+        out[name] = (ms.value, cnt.value)
+    return out

@@ -56,9 +56,10 @@ def uniform(shape, seed: int, device="cpu") -> torch.Tensor:
     return torch.rand(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
 
 
-def dyadic_uniform(shape, seed: int, device="cpu") -> torch.Tensor:
-    """U[0,1) snapped down to a multiple of 1/256 (exact in fp32 products)."""
-    return torch.floor(uniform(shape, seed, device) * 256.0) / 256.0
+def dyadic_uniform(shape, seed: int, device="cpu", bits: int = 8) -> torch.Tensor:
+    """U[0,1) snapped down to a multiple of 2^-bits (exact in fp32 products)."""
+    scale = float(1 << bits)
+    return torch.floor(uniform(shape, seed, device) * scale) / scale
 
 
 def int_grid(shape, seed: int, lo: int, hi: int, dtype=torch.float32, device="cpu") -> torch.Tensor:
@@ -195,14 +196,15 @@ def hca_decode(seed: int = 0, device="cpu", bt: int = 32, L: int = 1 << 20) -> W
 
 
 def indexer_128k(seed: int = 0, device="cpu", N: int = 131072, nq: int = 1024, n_needles: int = 64,
-                 integer_grid: bool = False) -> Workload:
+                 integer_grid: bool = False, weight_bits: int = 8) -> Workload:
     """Indexer chunk over 131072 entries, 1024 queries at the end, 16 x 128 heads.
 
     Keys N(0,1) bf16 with ``n_needles`` rows at distinct random positions
     scaled by 4 (their own draw times 4); queries N(0,1) bf16; head weights
     U(0,1).  Query j of the chunk sits at entry position N - nq + j.  HISA:
     B=128, m=64, k=2048.  ``integer_grid`` swaps in grid values in [-4, 4]
-    (dyadic weights) so that every fp32 score is exact.
+    (dyadic weights on a 2^-weight_bits grid) so that fp32 scores are exact;
+    4-bit weights also keep the block-mean (HISA stage 1) scores exact.
     """
     HI, DI = 16, 128
     names = ["q_i", "k_i", "w_i", "needles"]
@@ -211,7 +213,7 @@ def indexer_128k(seed: int = 0, device="cpu", N: int = 131072, nq: int = 1024, n
     if integer_grid:
         k_i = int_grid((1, N, DI), s["k_i"], -4, 4, device=device)
         q_i = int_grid((1, nq, HI, DI), s["q_i"], -4, 4, dtype=bf, device=device)
-        w_i = dyadic_uniform((1, nq, HI), s["w_i"], device=device)
+        w_i = dyadic_uniform((1, nq, HI), s["w_i"], device=device, bits=weight_bits)
     else:
         k_i = normal((1, N, DI), s["k_i"], device=device)
         q_i = normal((1, nq, HI, DI), s["q_i"], dtype=bf, device=device)

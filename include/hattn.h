@@ -1,0 +1,213 @@
+/*
+ * hattn.h -- C ABI of the hybrid compressed-attention library (libhattn.so).
+ *
+ * The library computes, on one gfx950 GPU, the steps of hybrid compressed
+ * attention: sequence-dimension KV compression, lightning-indexer top-k
+ * selection (flat and two-stage HISA), sparse MQA attention over the
+ * selected entries plus a sliding window, and dense MQA attention over the
+ * heavily compressed sequence plus the same window.
+ *
+ * Sources (cited by page title and section):
+ *   [HYB]  process-cxr.github.io, "Hybrid Attention" (ai-library/architecture/attention)
+ *   [HCA]  daiw.net, "前代 · HCA：128 倍压缩后再做稠密注意力" (deepseek-v4-flash/hca)
+ *   [HISA] my.qihongyi.cn/?p=787, "DeepSeek速度狂飙4倍还不丢精度"
+ *   [TRDM] trdm.cn/news/749237, section 2.1
+ *
+ * Conventions for every entry point:
+ *   - Every array argument is a DEVICE pointer (memory from hipMalloc or a
+ *     torch CUDA tensor), row-major and contiguous.  Sizes are element counts.
+ *   - The caller owns and allocates all inputs, outputs and workspaces.  The
+ *     library allocates nothing and keeps no state between calls (except the
+ *     optional kernel timer below).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on that stream and never synchronise; buffers
+ *     must stay alive until the stream has passed the call.
+ *   - Validation happens before anything is enqueued: on any status other
+ *     than HATTN_OK nothing has been launched and no output was written.
+ *     hattn_last_error() returns a thread-local message for the last failure.
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Floating inputs are either all fp32 (HATTN_F32) or bf16 (HATTN_BF16,
+ *     stored as raw 16-bit patterns) as stated per argument; accumulation is
+ *     always fp32.  Non-finite inputs are not supported.
+ *   - Workspaces (device scratch for intermediate scores and partial
+ *     results; contents need no initialisation and are meaningless after
+ *     the call): with ws == NULL and ws_bytes != NULL the call stores the
+ *     required byte count in *ws_bytes and returns HATTN_OK without
+ *     launching anything.  With ws != NULL, *ws_bytes must hold the size of
+ *     ws; a smaller size than required gives HATTN_ERR_WORKSPACE.
+ *     ws_bytes == NULL means no workspace is given, which is accepted when
+ *     the call needs none (required size 0) and gives HATTN_ERR_WORKSPACE
+ *     otherwise.  Calls that overlap in time must not share a workspace.
+ *   - Index lists are int32, ascending, padded with -1 at the end.
+ */
+#ifndef HATTN_H
+#define HATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HATTN_OK = 0,
+  HATTN_ERR_ARG = 1,         /* bad size, NULL required pointer, inconsistent arguments */
+  HATTN_ERR_UNSUPPORTED = 2, /* valid arguments with no kernel (e.g. a head size) */
+  HATTN_ERR_WORKSPACE = 3,   /* workspace smaller than required */
+  HATTN_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} hattn_status_t;
+
+typedef enum { HATTN_F32 = 0, HATTN_BF16 = 1 } hattn_dtype_t;
+
+/* Text for a status code (static storage). */
+const char* hattn_status_string(int status);
+/* Detail for the calling thread's last failing call (static thread storage). */
+const char* hattn_last_error(void);
+/* Version of this ABI (bumped on incompatible changes). */
+int hattn_abi_version(void);
+
+/*
+ * hattn_compress -- sequence-dimension KV compression.
+ * [HCA] section 怎么压: each compressed entry is the sum of a run of raw rows
+ * weighted by a softmax over (per-token compression logit + learnable
+ * position bias).  CSA uses runs of 8 at stride 4 (rate 4, [HCA] section
+ * 它补的正是 CSA 的短板, [TRDM] 2.1); HCA uses disjoint runs of 128.
+ *
+ *   entry i of sequence b covers raw rows [i*stride, i*stride + w):
+ *     a_j   = logits[b][i*stride + j] + pos_bias[j]          (j < w)
+ *     y[b][i][c] = sum_j softmax(a)_j * x[b][i*stride + j][c]
+ *
+ *   x        [bt][L][C]  dtype (K and V of a row side by side: C = 2*d)
+ *   logits   [bt][L]     fp32, or NULL for all-zero logits
+ *   pos_bias [w]         fp32, or NULL for zero bias
+ *   y        [bt][N][C]  dtype, N = (L - w)/stride + 1 complete windows
+ *   Only entries e_begin <= i < e_end are (re)written, so a decode step can
+ *   compress just the windows its new token completed.
+ * Requires 1 <= w <= 4096, 1 <= stride, L >= w, C a multiple of 16 bytes'
+ * worth of elements (8 for bf16, 4 for fp32), 0 <= e_begin <= e_end <= N.
+ */
+hattn_status_t hattn_compress(int dtype, const void* x, int64_t bt, int64_t L, int32_t C,
+                              const float* logits, const float* pos_bias, int32_t w, int32_t stride,
+                              int64_t e_begin, int64_t e_end, void* y, void* stream);
+
+/*
+ * hattn_visible_count -- how many compressed entries each query may see.
+ * Causal reading of [HYB] section 为什么长上下文需要新的 Attention (decode
+ * reads only history): entry i is visible to a query at raw position p iff
+ * its last raw row i*stride + w - 1 <= p, so
+ *   n_vis = 0 if p < w - 1, else min(n_entries, (p - w + 1)/stride + 1).
+ *   pos [count] int32 raw positions (>= 0) -> n_vis [count] int32.
+ */
+hattn_status_t hattn_visible_count(const int32_t* pos, int64_t count, int32_t w, int32_t stride,
+                                   int64_t n_entries, int32_t* n_vis, void* stream);
+
+/*
+ * hattn_index_topk -- flat lightning-indexer selection.
+ * [HISA] section 01: score every visible candidate of a query, keep the top k.
+ * Score (the pages print no formula; ReLU-weighted head sum):
+ *   S[q][i] = sum_h w_i[q][h] * max(0, q_i[q][h] . k_i[i])     for i < n_vis[q]
+ * Selection: the k largest S (ties to the lower i), emitted in ascending i,
+ * padded with -1 when n_vis[q] < k.  -0.0 and +0.0 are equal scores.
+ *
+ *   q_i   [bt][nq][h_i][d_i]  dtype       k_i [bt][n][d_i] dtype
+ *   w_i   [bt][nq][h_i]       fp32        n_vis [bt][nq] int32 (clamped to [0, n])
+ *   idx   [bt][nq][k]         int32 out   score [bt][nq][k] fp32 out or NULL
+ *         (the selected scores; -inf where idx is -1)
+ *   ws    workspace (size by query, see conventions)
+ * Requires 1 <= k <= 8192, 1 <= h_i <= 64, d_i in {32, 64, 128, 256} for
+ * bf16 (any d_i <= 256 for fp32).
+ */
+hattn_status_t hattn_index_topk(int dtype, const void* q_i, const void* k_i, const float* w_i,
+                                const int32_t* n_vis, int64_t bt, int64_t nq, int32_t h_i, int32_t d_i,
+                                int64_t n, int32_t k, int32_t* idx, float* score, void* ws,
+                                size_t* ws_bytes, void* stream);
+
+/*
+ * hattn_hisa_pool -- HISA block representatives.
+ * [HISA] section 第一阶段: the prefix is cut into blocks of B entries, each
+ * summarised by one pooled vector; here the mean, with a short last block
+ * zero-padded (divided by B, not by its own count).
+ *   reps[b][j][c] = (1/B) * sum_{i in [jB, min(n, jB+B))} k_i[b][i][c]
+ *   k_i [bt][n][d_i] dtype  ->  reps [bt][ceil(n/B)][d_i] fp32.
+ * Only blocks j_begin <= j < j_end are written (a decode step refreshes the
+ * last block alone).
+ */
+hattn_status_t hattn_hisa_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int32_t d_i, int32_t B,
+                               int64_t j_begin, int64_t j_end, float* reps, void* stream);
+
+/*
+ * hattn_hisa_topk -- two-stage HISA selection.
+ * [HISA] section 第一阶段: score every block representative whose first entry
+ * is visible with the same score form as above and keep the top m blocks
+ * (ties to the lower block).  Section 第二阶段: run the token indexer only on
+ * the visible entries of those blocks and keep the top k.  Section 05,
+ * Step 3: the output has the flat indexer's form (ascending, -1 padded).
+ *
+ *   q_i, k_i, w_i, n_vis as for hattn_index_topk; reps from hattn_hisa_pool.
+ *   idx [bt][nq][k] int32 out;  blk [bt][nq][m] int32 out (chosen blocks,
+ *   ascending, -1 padded) or NULL.
+ * Requires 1 <= B <= 1024, 1 <= m, m*B <= 16384, 1 <= k <= 8192.
+ */
+hattn_status_t hattn_hisa_topk(int dtype, const void* q_i, const void* k_i, const float* w_i,
+                               const int32_t* n_vis, int64_t bt, int64_t nq, int32_t h_i, int32_t d_i,
+                               int64_t n, const float* reps, int32_t B, int32_t m, int32_t k,
+                               int32_t* idx, int32_t* blk, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * hattn_sparse_attn -- CSA attention: selected entries plus sliding window.
+ * [HYB] section Compressed Sparse Attention; [HCA] section 怎么压 (MQA: all
+ * query heads share one K/V; a branch over the latest 128 raw tokens).
+ * One softmax runs over the union U of {ckv[idx[q][j]] : idx != -1} and the
+ * raw rows max(0, p - window + 1) .. p (no de-duplication):
+ *   out[q][h] = sum_{u in U} softmax_u(scale * q[q][h] . K_u) * V_u
+ *   lse[q][h] = log sum_{u in U} exp(scale * q[q][h] . K_u)
+ *
+ *   q      [bt][nq][h][d] dtype      ckv [bt][n][2d] dtype (K | V per entry)
+ *   idx    [bt][nq][k] int32; entries < 0 or >= n are skipped
+ *   raw_kv [bt][L][2d] dtype         q_pos [bt][nq] int32, 0 <= p < L
+ *   out    [bt][nq][h][d] fp32 out   lse [bt][nq][h] fp32 out or NULL
+ * Requires window >= 1 and d a multiple of 8.  bf16 with d in {64, 128}
+ * and h in {16, 32, 64} runs on MFMA; any other shape with h*d <= 8192 and
+ * d <= 256 takes the vector path.
+ */
+hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx,
+                                 int32_t k, const void* raw_kv, int64_t L, const int32_t* q_pos,
+                                 int32_t window, float scale, int64_t bt, int64_t nq, int32_t h, int32_t d,
+                                 float* out, float* lse, void* ws, size_t* ws_bytes, void* stream);
+
+/*
+ * hattn_dense_compressed_attn -- HCA attention: every visible entry plus window.
+ * [HCA] sections 128 倍是什么概念 and 怎么压: no selection; each query attends
+ * to all compressed entries it may see (ckv[0 .. n_vis[q]-1]) and to the
+ * same window branch, in one softmax.  Arguments as for hattn_sparse_attn
+ * with n_vis [bt][nq] int32 (clamped to [0, n]) in place of idx and k.
+ */
+hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void* ckv, int64_t n,
+                                           const int32_t* n_vis, const void* raw_kv, int64_t L,
+                                           const int32_t* q_pos, int32_t window, float scale, int64_t bt,
+                                           int64_t nq, int32_t h, int32_t d, float* out, float* lse, void* ws,
+                                           size_t* ws_bytes, void* stream);
+
+/*
+ * Kernel timer (profiling aid).  When enabled, every kernel the library
+ * launches is bracketed by HIP events recorded on the same stream, and its
+ * duration is accumulated per kernel name when hattn_timer_collect() is
+ * called (which synchronises on those events).  Disabled by default; not
+ * thread-safe; do not enable it while a HIP graph is being captured.
+ *   hattn_timer_enable(1|0)     start / stop recording (start clears totals)
+ *   hattn_timer_collect()       wait for recorded events, fold them into totals
+ *   hattn_timer_query(name, &total_ms, &count) -> HATTN_OK or HATTN_ERR_ARG if
+ *                               no kernel of that name was recorded
+ *   hattn_timer_names(buf, len) writes the recorded kernel names, '\n'-separated
+ */
+hattn_status_t hattn_timer_enable(int on);
+hattn_status_t hattn_timer_collect(void);
+hattn_status_t hattn_timer_query(const char* name, double* total_ms, int64_t* count);
+hattn_status_t hattn_timer_names(char* buf, int64_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HATTN_H */

@@ -1,0 +1,105 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/hattn.h declares, and rejects bad arguments before launching."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hattn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libhattn.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def test_exports_match_header(L):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no binding signature"
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.hattn_status_string(s).startswith(b"HATTN_")
+    assert L.hattn_abi_version() == 1
+
+
+def test_compress_validation(L):
+    f = L.hattn_compress
+    assert f(7, None, 1, 100, 256, None, None, 8, 4, 0, 1, None, None) == 1
+    assert f(1, None, 1, 100, 250, None, None, 8, 4, 0, 1, None, None) == 1  # C not multiple of 8
+    assert f(0, None, 1, 100, 6, None, None, 8, 4, 0, 1, None, None) == 1    # fp32 C not multiple of 4
+    assert f(1, None, 1, 5, 256, None, None, 8, 4, 0, 1, None, None) == 1    # L < w
+    assert f(1, None, 1, 100, 256, None, None, 8, 4, 0, 30, None, None) == 1  # e_end > N = 24
+    assert f(1, None, 1, 100, 256, None, None, 0, 4, 0, 1, None, None) == 1  # w = 0
+    assert f(1, None, 1, 100, 256, None, None, 8, 4, 0, 1, None, None) == 1  # NULL x
+    assert b"NULL" in L.hattn_last_error()
+    assert f(1, None, 0, 100, 256, None, None, 8, 4, 0, 24, None, None) == 0  # bt = 0: nothing to do
+
+
+def _sz():
+    return ctypes.c_size_t(0)
+
+
+def test_index_topk_validation_and_size_query(L):
+    p = ctypes.c_void_p(16)  # never dereferenced: every call below returns before launching
+    sz = _sz()
+    # bad k, bad heads, NULL pointer
+    assert L.hattn_index_topk(1, p, p, p, p, 1, 4, 16, 128, 1000, 0, p, None, None, ctypes.byref(sz), None) == 1
+    assert L.hattn_index_topk(1, p, p, p, p, 1, 4, 16, 128, 1000, 9000, p, None, None, ctypes.byref(sz), None) == 1
+    assert L.hattn_index_topk(1, p, p, p, p, 1, 4, 65, 128, 1000, 8, p, None, None, ctypes.byref(sz), None) == 1
+    assert L.hattn_index_topk(1, None, p, p, p, 1, 4, 16, 128, 1000, 8, p, None, None, ctypes.byref(sz), None) == 1
+    # size query: rows * round4(n) * 4 bytes of scores (n below the LDS cap)
+    assert L.hattn_index_topk(1, p, p, p, p, 2, 8, 16, 128, 1000, 8, p, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value >= 16 * 1000 * 4
+    # a long row needs candidate lists too
+    big = _sz()
+    assert L.hattn_index_topk(1, p, p, p, p, 1, 1, 16, 128, 131072, 2048, p, None, None, ctypes.byref(big), None) == 0
+    assert big.value > 131072 * 4
+    # too small a workspace, or none at all
+    small = ctypes.c_size_t(sz.value - 1)
+    assert L.hattn_index_topk(1, p, p, p, p, 2, 8, 16, 128, 1000, 8, p, None, p, ctypes.byref(small), None) == 3
+    assert L.hattn_index_topk(1, p, p, p, p, 2, 8, 16, 128, 1000, 8, p, None, None, None, None) == 3
+
+
+def test_hisa_validation(L):
+    p = ctypes.c_void_p(16)
+    sz = _sz()
+    assert L.hattn_hisa_topk(1, p, p, p, p, 1, 4, 16, 128, 4096, p, 128, 200, 64, p, None, None,
+                             ctypes.byref(sz), None) == 1  # m*B > 16384
+    assert L.hattn_hisa_topk(1, p, p, p, p, 1, 4, 16, 128, 4096, None, 128, 8, 64, p, None, None,
+                             ctypes.byref(sz), None) == 1  # NULL reps
+    assert L.hattn_hisa_topk(1, p, p, p, p, 1, 4, 16, 128, 4096, p, 128, 8, 64, p, None, None,
+                             ctypes.byref(sz), None) == 0 and sz.value > 0
+    assert L.hattn_hisa_pool(1, p, 1, 100, 12, 16, 0, 7, p, None) == 1  # d_i not multiple of 8
+    assert L.hattn_hisa_pool(1, p, 1, 100, 16, 16, 0, 8, p, None) == 1  # block range past ceil(100/16) = 7
+
+
+def test_attention_validation(L):
+    p = ctypes.c_void_p(16)
+    sz = _sz()
+    f = L.hattn_dense_compressed_attn
+    assert f(1, p, p, 100, p, p, 1000, p, 0, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1  # window
+    assert f(1, p, p, 100, p, p, 1000, p, 128, -1.0, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert f(1, p, p, 100, p, p, 1000, p, 128, 0.1, 1, 1, 64, 12, p, None, None, ctypes.byref(sz), None) == 1
+    assert f(1, p, p, 100, None, p, 1000, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert f(1, p, p, 100, p, p, 1000, p, 128, 0.1, 1, 1, 512, 128, p, None, None, ctypes.byref(sz), None) == 2
+    # long key lists are split: the partials need a workspace
+    assert f(1, p, p, 8192, p, p, 1 << 20, p, 128, 0.1, 32, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 0
+    assert sz.value > 0
+    g = L.hattn_sparse_attn
+    assert g(1, p, p, 100, None, 8, p, 1000, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1

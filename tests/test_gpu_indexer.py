@@ -1,0 +1,190 @@
+"""GPU parity: flat indexer top-k and HISA two-stage selection vs the oracle.
+
+Integer-grid inputs make every fp32 score exact, so indices must be
+bit-identical; float inputs are held to mean IoU >= 0.999 plus the check
+that every disagreement sits at the selection boundary."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_attention_amd import ops, synth
+from helpers import check_near_ties, f64, iou_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _nvis_entry_space(nq, N):
+    # queries at the end of the entry sequence: query j sits at entry N - nq + j
+    pos = torch.arange(N - nq, N, dtype=torch.int32).reshape(1, nq)
+    return ops.visible_count(pos.to(DEV), 1, 1, N)
+
+
+def _rows(nq, count, seed=0):
+    rng = np.random.default_rng(seed)
+    return sorted(set(rng.choice(nq, min(nq, count), replace=False).tolist()) | {0, nq - 1})
+
+
+def test_tiny_layer_fp32_flat_exact():
+    t = synth.tiny_hybrid_layer(0).tensors
+    nv = ops.visible_count(t["q_pos"].to(DEV), 8, 4, 1023)
+    idx, sc = ops.index_topk(t["q_i"].to(DEV), t["k_i"].to(DEV), t["w_i"].to(DEV), nv, 64, return_scores=True)
+    torch.cuda.synchronize()
+    nv_o = np.array([oracle.n_visible(int(p), 8, 4, 1023) for p in t["q_pos"][0]])
+    assert np.array_equal(nv.cpu().numpy()[0], nv_o)
+    ref, ref_sc = oracle.flat_topk(f64(t["q_i"][0]), f64(t["k_i"][0]), f64(t["w_i"][0]), nv_o, 64, return_scores=True)
+    assert np.array_equal(idx.cpu().numpy()[0], ref)
+    got_sc = f64(sc[0])
+    assert np.array_equal(np.where(ref >= 0, got_sc, 0), np.where(ref >= 0, ref_sc, 0))
+
+
+@pytest.mark.parametrize("nq,N,k,hi", [(1024, 8191, 512, 8), (37, 1000, 64, 8), (16, 70000, 700, 4)])
+def test_bf16_mfma_integer_grid_exact(nq, N, k, hi):
+    # 16 heads x 64 dims on the grid [-8, 8] (16 x 128 on [-4, 4]) keep every
+    # fp32 partial sum an exact multiple of 2^-8 below 2^24.
+    d = 64 if hi == 8 else 128
+    q_i = synth.int_grid((1, nq, 16, d), 41, -hi, hi, dtype=torch.bfloat16)
+    k_i = synth.int_grid((1, N, d), 42, -hi, hi, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((1, nq, 16), 43)
+    nv = _nvis_entry_space(nq, N)
+    idx = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv, k)
+    torch.cuda.synchronize()
+    rows = _rows(nq, 48)
+    nvh = nv.cpu().numpy()[0]
+    ref = oracle.flat_topk(f64(q_i[0, rows]), f64(k_i[0]), f64(w_i[0, rows]), nvh[rows], k)
+    assert np.array_equal(idx.cpu().numpy()[0, rows], ref)
+
+
+def test_indexer_128k_integer_grid_exact_sampled():
+    # The 128K-entry chunk at full size (multi-level selection), grid [-4, 4].
+    w = synth.indexer_128k(0, integer_grid=True)
+    t = w.tensors
+    N, nq, k = 131072, 1024, 2048
+    nv = _nvis_entry_space(nq, N)
+    idx = ops.index_topk(t["q_i"].to(DEV), t["k_i"].to(DEV), t["w_i"].to(DEV), nv, k)
+    torch.cuda.synchronize()
+    rows = _rows(nq, 10)
+    ref = oracle.flat_topk(f64(t["q_i"][0, rows]), f64(t["k_i"][0]), f64(t["w_i"][0, rows]),
+                           nv.cpu().numpy()[0][rows], k)
+    assert np.array_equal(idx.cpu().numpy()[0, rows], ref)
+
+
+def test_float_inputs_iou_and_boundary():
+    t = synth.csa_prefill_chunk(0).tensors
+    N, nq, k = 8191, 1024, 512
+    nv = ops.visible_count(t["q_pos"].to(DEV), 8, 4, N)
+    idx = ops.index_topk(t["q_i"].to(DEV), t["k_i"].to(DEV), t["w_i"].to(DEV), nv, k)
+    torch.cuda.synchronize()
+    rows = _rows(nq, 96)
+    nvh = nv.cpu().numpy()[0]
+    q, kk, ww = f64(t["q_i"][0]), f64(t["k_i"][0]), f64(t["w_i"][0])
+    ref = oracle.flat_topk(q[rows], kk, ww[rows], nvh[rows], k)
+    got = idx.cpu().numpy()[0, rows]
+    mean, mn = iou_rows(got, ref)
+    assert mean >= 0.999, (mean, mn)
+
+    def scores(r):
+        return oracle.index_scores(q[rows[r]], kk[: nvh[rows[r]]], ww[rows[r]])
+
+    def tol(r):  # fp32 accumulation bound: d * 2^-23 * sum_h w |q||k|
+        qa = np.abs(q[rows[r]])
+        return 64 * 2.0**-23 * float((ww[rows[r]][:, None] * (qa @ np.abs(kk).T)).max()) * 4
+
+    check_near_ties(got, ref, scores, tol)
+
+
+def test_edge_cases():
+    d, N, nq = 64, 300, 20
+    q_i = synth.int_grid((2, nq, 16, d), 51, -8, 8, dtype=torch.bfloat16)
+    k_i = synth.int_grid((2, N, d), 52, -8, 8, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((2, nq, 16), 53)
+    nv = torch.tensor([[0, 1, 2, 5, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 200, 255, 256, 299, 300, 300]] * 2,
+                      dtype=torch.int32)
+    nv[1] = nv[1].flip(0)
+    for k in (1, 7, 64, 299, 300, 512):
+        idx = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), k).cpu().numpy()
+        for b in range(2):
+            ref = oracle.flat_topk(f64(q_i[b]), f64(k_i[b]), f64(w_i[b]), nv[b].numpy(), k)
+            assert np.array_equal(idx[b], ref), (b, k)
+    # an all-zero query: every visible score is 0, the lowest indices win
+    qz = torch.zeros_like(q_i)
+    idx = ops.index_topk(qz.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), 10).cpu().numpy()
+    assert list(idx[0, 19]) == list(range(10)) and list(idx[0, 0]) == [-1] * 10
+
+
+# ---- HISA -------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,m", [(16, 1), (16, 2), (16, 8), (128, 1), (128, 2), (128, 8)])
+def test_tiny_layer_fp32_hisa_exact(B, m):
+    t = synth.tiny_hybrid_layer(0).tensors
+    N = 1023
+    nv = ops.visible_count(t["q_pos"].to(DEV), 8, 4, N)
+    k_i = t["k_i"].to(DEV)
+    reps = ops.hisa_pool(k_i, B)
+    idx, blk = ops.hisa_topk(t["q_i"].to(DEV), k_i, t["w_i"].to(DEV), nv, reps, B, m, 64, return_blocks=True)
+    torch.cuda.synchronize()
+    ref, ref_blk = oracle.hisa_topk(f64(t["q_i"][0]), f64(t["k_i"][0]), f64(t["w_i"][0]), nv.cpu().numpy()[0], B, m, 64)
+    assert np.array_equal(blk.cpu().numpy()[0], ref_blk)
+    assert np.array_equal(idx.cpu().numpy()[0], ref)
+
+
+def _stage1_exact_bound(q, k_i, w, B, weight_bits):
+    # With block sums S_b (integers), representatives S_b / B (B a power of 2)
+    # and head weights v / 2^bits, every partial sum of a stage-1 score is a
+    # multiple of 2^-(log2 B + bits); it is exact in fp32 when
+    #     max_v * sum_h sum_c |q_hc S_bc| < 2^24      (asserted here).
+    nb = -(-k_i.shape[0] // B)
+    S = np.stack([k_i[j * B:(j + 1) * B].sum(0) for j in range(nb)])
+    worst = (np.abs(q).reshape(-1, q.shape[-1]) @ np.abs(S).T).reshape(q.shape[0], q.shape[1], nb).sum(1).max()
+    assert worst * ((1 << weight_bits) - 1) < 2**24, worst
+
+
+def test_hisa_128k_bf16_integer_grid_exact_sampled():
+    w = synth.indexer_128k(0, integer_grid=True, weight_bits=4)
+    t = w.tensors
+    N, nq, B, m, k = 131072, 1024, 128, 64, 2048
+    nv = _nvis_entry_space(nq, N)
+    k_i = t["k_i"].to(DEV)
+    reps = ops.hisa_pool(k_i, B)
+    idx, blk = ops.hisa_topk(t["q_i"].to(DEV), k_i, t["w_i"].to(DEV), nv, reps, B, m, k, return_blocks=True)
+    torch.cuda.synchronize()
+    rows = _rows(nq, 10)
+    q, kk, ww = f64(t["q_i"][0]), f64(t["k_i"][0]), f64(t["w_i"][0])
+    _stage1_exact_bound(q[rows], kk, ww, B, 4)
+    ref, ref_blk = oracle.hisa_topk(q[rows], kk, ww[rows], nv.cpu().numpy()[0][rows], B, m, k)
+    assert np.array_equal(blk.cpu().numpy()[0, rows], ref_blk)
+    assert np.array_equal(idx.cpu().numpy()[0, rows], ref)
+
+
+@pytest.mark.parametrize("N,B,m", [(4096, 128, 32), (1000, 64, 16), (8191, 128, 64)])
+def test_hisa_keeping_every_block_equals_flat(N, B, m):
+    nq, k = 64, 256
+    q_i = synth.normal((1, nq, 16, 128), 61, dtype=torch.bfloat16).to(DEV)
+    k_i = synth.normal((1, N, 128), 62, dtype=torch.bfloat16).to(DEV)
+    w_i = synth.uniform((1, nq, 16), 63).to(DEV)
+    nv = _nvis_entry_space(nq, N)
+    reps = ops.hisa_pool(k_i, B)
+    a = ops.hisa_topk(q_i, k_i, w_i, nv, reps, B, m, k)
+    f = ops.index_topk(q_i, k_i, w_i, nv, k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, f)
+
+
+def test_hisa_float_inputs_vs_oracle():
+    # N(0,1) indexer at the 128K chunk with needles: IoU of GPU HISA vs oracle
+    # HISA on sampled rows (the selection itself is a heuristic, so it is the
+    # oracle's HISA, not flat, that the GPU must match).
+    w = synth.indexer_128k(0)
+    t = w.tensors
+    N, nq, B, m, k = 131072, 1024, 128, 64, 2048
+    nv = _nvis_entry_space(nq, N)
+    k_i = t["k_i"].to(DEV)
+    reps = ops.hisa_pool(k_i, B)
+    idx = ops.hisa_topk(t["q_i"].to(DEV), k_i, t["w_i"].to(DEV), nv, reps, B, m, k)
+    torch.cuda.synchronize()
+    rows = _rows(nq, 8)
+    ref, _ = oracle.hisa_topk(f64(t["q_i"][0, rows]), f64(t["k_i"][0]), f64(t["w_i"][0, rows]),
+                              nv.cpu().numpy()[0][rows], B, m, k)
+    mean, mn = iou_rows(idx.cpu().numpy()[0, rows], ref)
+    assert mean >= 0.999, (mean, mn)
