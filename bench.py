@@ -11,7 +11,9 @@ CSA entries, 8,192 HCA entries):
        scores in the chosen blocks, token top-k) -> sparse attention
   HCA: compress the completed 128-token window -> dense attention
 
-Every step runs as a replay of a HIP graph captured from the library calls.
+Every step replays two HIP graphs captured from the library calls, one per
+layer, on two streams that join at the end of the step, so the HCA layer's
+kernels overlap the CSA chain.
 Caches are replicated R times (R graphs) and steps rotate through them, so
 the working set (about 70 MB a step) is not served by the 256 MB last-level
 cache.  Inputs are seeded synthetic tensors drawn on the device.
@@ -82,7 +84,10 @@ def timed_graphs(graphs, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per step
 
 
-def capture(fn, reps):
+def capture(fn, reps, stream=None):
+    """One graph per replica.  Graphs that will replay concurrently must be
+    captured on different streams: the binding keys its scratch workspaces by
+    stream, so they then own separate workspaces."""
     import torch
 
     graphs = []
@@ -91,7 +96,7 @@ def capture(fn, reps):
     torch.cuda.synchronize()
     for r in reps:
         g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
+        with torch.cuda.graph(g, stream=stream):
             fn(r)
         graphs.append(g)
     torch.cuda.synchronize()
@@ -141,19 +146,46 @@ def hybrid_pair(args):
     torch.cuda.synchronize()
     log(f"[bench] hybrid pair inputs + {R} cache replicas ready in {time.time() - t0:.1f}s")
 
-    def step(c):
+    def csa_step(c):
         ops.compress(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, N - 1, N, out=c["ckv"])
-        ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, Nh - 1, Nh, out=c["hkv"])
         ops.hisa_pool(c["k_i"], B, nb - 1, nb, out=c["reps"])
         nv = ops.visible_count(t["q_pos"], 8, 4, N)
-        nvh = ops.visible_count(t["q_pos"], 128, 128, Nh)
         idx = ops.hisa_topk(t["q_i"], c["k_i"], t["w_i"], nv, c["reps"], B, m, k)
-        o1 = ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128)
-        o2 = ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128)
-        return o1, o2
+        return ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128)
 
-    graphs = capture(step, caches)
-    ms = timed_graphs(graphs, args.steps, args.warmup)
+    def hca_step(c):
+        ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, Nh - 1, Nh, out=c["hkv"])
+        nvh = ops.visible_count(t["q_pos"], 128, 128, Nh)
+        return ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128)
+
+    def step(c):  # eager, one stream
+        return csa_step(c), hca_step(c)
+
+    # The two layers' inputs are independent: each is captured as its own
+    # graph and the pair is replayed on two streams (default priority both)
+    # that join at the end of every step.
+    side = torch.cuda.Stream()
+    g_csa = capture(csa_step, caches, stream=torch.cuda.Stream())
+    g_hca = capture(hca_step, caches, stream=torch.cuda.Stream())
+    main = torch.cuda.current_stream()
+
+    def replay(i):
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            g_hca[i % R].replay()
+        g_csa[i % R].replay()
+        main.wait_stream(side)
+
+    for i in range(args.warmup):
+        replay(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(args.steps):
+        replay(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
     kt = kernel_times(step, caches, args.steps)
     o1, o2 = step(caches[0])
     torch.cuda.synchronize()
@@ -169,7 +201,7 @@ def hybrid_pair(args):
     }
     step_bytes = sum(kb.values())
     info = dict(ms=ms, kernels=kt, kernel_bytes=kb, step_bytes=step_bytes, bt=bt, N=N, Nh=Nh, k=k, L=L)
-    del graphs
+    del g_csa, g_hca
     return info
 
 
@@ -373,8 +405,9 @@ def main():
 
     ms = res["ms"]
     kt = res["kernels"]
-    # dominant kernel of the step: the one with the largest time per step
-    dom = max(kt.items(), key=lambda kv: kv[1][0] * kv[1][1])[0]
+    # dominant kernel of the step: the modelled kernel with the largest time
+    # per step (kernel times come from the sequential eager pass)
+    dom = max((kk for kk in kt if kk in res["kernel_bytes"]), key=lambda kk: kt[kk][0] * kt[kk][1])
     dom_ms = kt[dom][0]
     dom_bytes = res["kernel_bytes"].get(dom)
     roof = dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None, traffic=None, kernel=dom,

@@ -42,28 +42,67 @@ HATTN_DEV const T* key_row(int64_t j, int64_t nc, const int32_t* idx_row, const 
   return raw_b + r * C;
 }
 
+// Source row of virtual key j (0 <= j < 2^31) for the MFMA kernel, computed
+// branch-free in 32-bit arithmetic (each sequence's cache holds fewer than
+// 2^31 elements, checked on the host).  `ok` says whether the key exists;
+// when it does not, the row is row 0 of the raw sequence (always valid,
+// L >= 1) and its data is never used.  Sparse lists are read at a clamped
+// index so the load is always in bounds.
+template <bool SPARSE>
+HATTN_DEV const uint16_t* key_src32(int j, int j_end, int nc, const int32_t* idx_row, const uint16_t* ckv_b,
+                                    int n, const uint16_t* raw_b, int L, int rbase, int C, bool* ok) {
+  const bool in_c = j < nc;
+  int e;
+  if (SPARSE) e = idx_row[in_c ? j : 0];
+  else e = j;
+  const int r = rbase + j;  // rbase = p - nw + 1 - nc
+  const bool okc = in_c && unsigned(e) < unsigned(n);
+  const bool okr = !in_c && unsigned(r) < unsigned(L);
+  const bool v = j < j_end && (okc || okr);
+  *ok = v;
+  const unsigned off = v ? unsigned(okc ? e : r) * unsigned(C) : 0u;
+  return (v && okc ? ckv_b : raw_b) + off;
+}
+
+// MFMA attention workgroup: one query, one chunk of its key list, 16 heads
+// per wave (H = 16*NW), head dim D.  Tiles of 64 keys are shared by the
+// waves through LDS (small enough that the prefetch registers leave room for
+// the compiler to keep several LDS operand reads in flight per MFMA chain):
+//   load    the next tile's K|V rows into registers (16-byte loads) while
+//           the current tile is computed
+//   S^T     = K . Q^T   (A = K rows via ds_read_b128, B = Q in VGPRs)
+//   softmax per head in the log2 domain; the reference maximum moves only
+//           when a tile maximum exceeds it by more than 8, so O and l are
+//           rescaled rarely and P stays below 2^8
+//   O^T    += V^T . P^T (A = V columns via the gfx950 LDS transpose read,
+//           B = P straight from the S^T accumulators, no re-layout)
+// The workgroup writes the normalised output, or an unnormalised partial
+// (O, max, sum) when the key list is split over several workgroups.
 template <int D, int NW, bool SPARSE>
-__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ ckv, int64_t n,
-                                                            const int32_t* __restrict__ idx, int k,
-                                                            const int32_t* __restrict__ n_vis,
-                                                            const uint16_t* __restrict__ raw, int64_t L,
-                                                            const int32_t* __restrict__ q_pos, int window,
-                                                            float scale_log2, int64_t nq, int chunk, int nsplit,
-                                                            float* __restrict__ out, float* __restrict__ lse,
-                                                            float* __restrict__ part_o, float* __restrict__ part_ml) {
+__global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ ckv, int64_t n,
+                                                               const int32_t* __restrict__ idx, int k,
+                                                               const int32_t* __restrict__ n_vis,
+                                                               const uint16_t* __restrict__ raw, int64_t L,
+                                                               const int32_t* __restrict__ q_pos, int window,
+                                                               float scale_log2, int64_t nq, int chunk, int nsplit,
+                                                               float* __restrict__ out, float* __restrict__ lse,
+                                                               float* __restrict__ part_o, float* __restrict__ part_ml) {
   constexpr int H = 16 * NW;
   constexpr int C = 2 * D;
-  constexpr int TK = 64;
-  constexpr int PITCH = C + 8;
+  constexpr int TK = 64;      // keys per tile (32 KiB of K|V at d = 128)
+  constexpr int MT = TK / 16;
+  constexpr int KP = D + 8;   // K rows 4 banks apart: conflict-free b128 operand reads
+  constexpr int VP = D + 16;  // V rows 8 banks apart: conflict-free transpose reads
   constexpr int NT = 64 * NW;
-  constexpr int PPR = C / 8;                // 16-byte pieces per row
-  constexpr int PIECES = TK * PPR / NT;     // per thread per tile
+  constexpr int PPR = C / 8;             // 16-byte pieces per row
+  constexpr int PIECES = TK * PPR / NT;  // per thread per tile
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   static_assert(TK * PPR % NT == 0, "tile split");
-  __shared__ __align__(16) uint16_t tile[TK * PITCH];
-  __shared__ uint64_t vmask;
+  __shared__ __align__(16) uint16_t kt[TK * KP];
+  __shared__ __align__(16) uint16_t vt[TK * VP];
+  __shared__ uint64_t vmask[TK / 64];
 
   const int64_t qrow = blockIdx.y;
   const int split = blockIdx.x;
@@ -71,12 +110,14 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(const uint16_t* __re
   const int64_t p = q_pos[qrow];
   const int nw = int(imax64(0, imin64(window, p + 1)));
   const int64_t nc = SPARSE ? int64_t(k) : imin64(n, imax64(0, n_vis[qrow]));
-  const int64_t total = nc + nw;
-  const int64_t j_begin = int64_t(split) * chunk;
-  const int64_t j_end = imin64(total, j_begin + chunk);
+  const int total = int(nc) + nw;
+  const int j_begin = split * chunk;
+  const int j_end = min(total, j_begin + chunk);
   const int32_t* idx_row = SPARSE ? idx + qrow * k : nullptr;
   const uint16_t* ckv_b = ckv + b * n * C;
   const uint16_t* raw_b = raw + b * L * C;
+  const int rbase = int(p) - nw + 1 - int(nc);
+  const int n32 = int(n), L32 = int(L), nc32 = int(nc);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -84,106 +125,138 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(const uint16_t* __re
   const int head = 16 * wave + r16;
 
   u32x4_t qf[KS];
-  {
-    const uint16_t* qp = q + (qrow * H + head) * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(qp + 32 * ks);
-  }
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(q + (qrow * H + head) * D + 32 * ks + 8 * g);
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
   u32x4_t pre[PIECES];
-  auto prefetch = [&](int64_t j0) {
+  // A tile is "plain" when all its TK keys exist and sit in one contiguous
+  // run of rows (dense entries, or window rows): then row r is base + r*C
+  // and every key is valid.  Other tiles take the general per-row path.
+  auto plain_base = [&](int j0) -> const uint16_t* {
+    if (SPARSE || j0 + TK > j_end) return nullptr;
+    if (j0 + TK <= nc32) return ckv_b + size_t(j0) * C;
+    if (j0 >= nc32) return raw_b + size_t(rbase + j0) * C;
+    return nullptr;
+  };
+  auto fetch = [&](int j0) {
+    const uint16_t* base = plain_base(j0);
+    if (base) {
 #pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-      const int pidx = tid + NT * u;
-      const int row = pidx / PPR, col = pidx % PPR;
-      const int64_t j = j0 + row;
-      const uint16_t* src =
-          j < j_end ? key_row<uint16_t, SPARSE>(j, nc, idx_row, ckv_b, n, raw_b, L, p, nw, C) : nullptr;
-      pre[u] = src ? ld16(src + col * 8) : u32x4_t{0, 0, 0, 0};
+      for (int u = 0; u < PIECES; ++u) {
+        const int pidx = tid + NT * u;
+        pre[u] = ld16_nt(base + (pidx / PPR) * C + (pidx % PPR) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < PIECES; ++u) {
+        const int pidx = tid + NT * u;
+        bool ok;
+        // Skipped keys read raw row 0 (finite data); their logits are masked.
+        const uint16_t* src = key_src32<SPARSE>(j0 + pidx / PPR, j_end, nc32, idx_row, ckv_b, n32, raw_b, L32,
+                                                rbase, C, &ok);
+        pre[u] = ld16_nt(src + (pidx % PPR) * 8);
+      }
     }
   };
-  if (j_begin < j_end) prefetch(j_begin);
-  for (int64_t j0 = j_begin; j0 < j_end; j0 += TK) {
+  if (j_begin < j_end) fetch(j_begin);
+  for (int j0 = j_begin; j0 < j_end; j0 += TK) {
 #pragma unroll
     for (int u = 0; u < PIECES; ++u) {
       const int pidx = tid + NT * u;
       const int row = pidx / PPR, col = pidx % PPR;
-      *reinterpret_cast<u32x4_t*>(&tile[row * PITCH + col * 8]) = pre[u];
+      uint16_t* dst = col < PPR / 2 ? kt + row * KP + col * 8 : vt + row * VP + (col - PPR / 2) * 8;
+      *reinterpret_cast<u32x4_t*>(dst) = pre[u];
     }
-    if (wave == 0) {
-      const int64_t j = j0 + lane;
-      const bool ok =
-          j < j_end && key_row<uint16_t, SPARSE>(j, nc, idx_row, ckv_b, n, raw_b, L, p, nw, C) != nullptr;
-      const uint64_t mk = ballot(ok);
-      if (lane == 0) vmask = mk;
+    const bool plain = plain_base(j0) != nullptr;  // uniform: every key valid
+    if (!plain && wave == 0) {
+#pragma unroll
+      for (int h = 0; h < TK / 64; ++h) {
+        bool ok;
+        key_src32<SPARSE>(j0 + 64 * h + lane, j_end, nc32, idx_row, ckv_b, n32, raw_b, L32, rbase, C, &ok);
+        const uint64_t mk = ballot(ok);
+        if (lane == 0) vmask[h] = mk;
+      }
     }
     __syncthreads();
-    if (j0 + TK < j_end) prefetch(j0 + TK);
-    const uint64_t mk = vmask;
+    if (j0 + TK < j_end) fetch(j0 + TK);
 
-    // S^T = K . Q^T for 64 keys x 16 heads (this wave's heads).
-    f32x4_t s[4];
+    f32x4_t s[MT];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt) s[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&tile[(16 * mt + r16) * PITCH + 32 * ks + 8 * g]);
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kt + (16 * mt + r16) * KP + 32 * ks + 8 * g);
         s[mt] = mfma16x16x32(a, qf[ks], s[mt]);
       }
-    }
-    // Online softmax (log2 domain) for head r16 of this wave.
+
     float mx = -INFINITY;
+    if (plain) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 16 * mt + 4 * g + i;
-        const bool ok = (mk >> kk) & 1ull;
-        const float x = ok ? s[mt][i] * scale_log2 : -INFINITY;
-        s[mt][i] = x;
-        mx = fmaxf(mx, x);
+        for (int i = 0; i < 4; ++i) {
+          s[mt][i] *= scale_log2;
+          mx = fmaxf(mx, s[mt][i]);
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint64_t mk = vmask[mt >> 2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = (16 * mt + 4 * g + i) & 63;
+          const float x = ((mk >> kk) & 1ull) ? s[mt][i] * scale_log2 : -INFINITY;
+          s[mt][i] = x;
+          mx = fmaxf(mx, x);
+        }
       }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+    const bool up = mx > m_run + 8.f;  // false while mx is -inf
+    if (__any(up)) {
+      const float m_new = up ? mx : m_run;
+      // o and l are still zero while the reference is -inf
+      const float a = (up && m_run != -INFINITY) ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= a;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= a;
+      m_run = m_new;
+    }
+    // exp2 of -inf (masked key) is +0; a reference that is still -inf means
+    // every key so far was masked, and then all weights are 0.
+    const float mref = m_run == -INFINITY ? INFINITY : m_run;
     float psum = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = m_new == -INFINITY ? 0.f : exp2f(s[mt][i] - m_new);
+        const float e = fast_exp2(s[mt][i] - mref);
         s[mt][i] = e;
         psum += e;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    l_run += psum;
 
-    // O^T += V^T . P^T, two steps of 32 keys.
+    // k-slots of lane group g in step k2: keys 32k2+4g..+3, then 32k2+16+4g..+3.
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
+    for (int k2 = 0; k2 < TK / 32; ++k2) {
       u32x4_t pb;
-      pb[0] = pack_bf16x2(s[2 * k2][0], s[2 * k2][1]);
-      pb[1] = pack_bf16x2(s[2 * k2][2], s[2 * k2][3]);
-      pb[2] = pack_bf16x2(s[2 * k2 + 1][0], s[2 * k2 + 1][1]);
-      pb[3] = pack_bf16x2(s[2 * k2 + 1][2], s[2 * k2 + 1][3]);
-      const int key0 = 32 * k2 + 4 * g;
+      pb[0] = pack_bf16x2_hw(s[2 * k2][0], s[2 * k2][1]);
+      pb[1] = pack_bf16x2_hw(s[2 * k2][2], s[2 * k2][3]);
+      pb[2] = pack_bf16x2_hw(s[2 * k2 + 1][0], s[2 * k2 + 1][1]);
+      pb[3] = pack_bf16x2_hw(s[2 * k2 + 1][2], s[2 * k2 + 1][3]);
+      const uint16_t* vb = vt + (32 * k2 + 4 * g + (r16 >> 2)) * VP + 4 * (r16 & 3);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t* vcol = &tile[D + 16 * dt + r16];
-        u32x4_t va;
-        va[0] = uint32_t(vcol[(key0 + 0) * PITCH]) | (uint32_t(vcol[(key0 + 1) * PITCH]) << 16);
-        va[1] = uint32_t(vcol[(key0 + 2) * PITCH]) | (uint32_t(vcol[(key0 + 3) * PITCH]) << 16);
-        va[2] = uint32_t(vcol[(key0 + 16) * PITCH]) | (uint32_t(vcol[(key0 + 17) * PITCH]) << 16);
-        va[3] = uint32_t(vcol[(key0 + 18) * PITCH]) | (uint32_t(vcol[(key0 + 19) * PITCH]) << 16);
+        const u32x2_t lo = lds_read_tr16(vb + 16 * dt);
+        const u32x2_t hi = lds_read_tr16(vb + 16 * VP + 16 * dt);
+        const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
         o[dt] = mfma16x16x32(va, pb, o[dt]);
       }
     }
@@ -197,10 +270,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(const uint16_t* __re
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* op = out + (qrow * H + head) * D + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      f32x4_t v = o[dt] * inv;
-      *reinterpret_cast<f32x4_t*>(op + 16 * dt) = v;
-    }
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t*>(op + 16 * dt) = o[dt] * inv;
     if (lse && g == 0) lse[qrow * H + head] = (m_run + __log2f(l_tot)) * kLn2;
   } else {
     const int64_t pr = qrow * nsplit + split;
@@ -332,22 +402,31 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
 }
 
 // Combines per-chunk partials: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-__global__ void attn_merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml, int nsplit,
-                                  int H, int D, float* __restrict__ out, float* __restrict__ lse) {
+// One workgroup per (query, 256 consecutive outputs); the loops over chunks
+// issue independent loads.
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_ml, int nsplit, int H, int D,
+                                                         float* __restrict__ out, float* __restrict__ lse) {
   const int64_t qrow = blockIdx.y;
-  const int h = blockIdx.x;
-  const int c = threadIdx.x;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= H * D) return;
+  const int h = e / D, c = e % D;
+  const float* ml = part_ml + (qrow * nsplit * H + h) * 2;
+  const int64_t mls = int64_t(H) * 2;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, part_ml[((qrow * nsplit + s) * H + h) * 2]);
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[s * mls]);
   float num = 0.f, den = 0.f;
+  const float* po = part_o + qrow * nsplit * H * D + e;
+  const int64_t pos = int64_t(H) * D;
+#pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
-    const int64_t pr = (qrow * nsplit + s) * H + h;
-    const float ms = part_ml[pr * 2];
+    const float ms = ml[s * mls];
     const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    den = fmaf(w, part_ml[pr * 2 + 1], den);
-    if (c < D) num = fmaf(w, part_o[pr * D + c], num);
+    den = fmaf(w, ml[s * mls + 1], den);
+    num = fmaf(w, po[s * pos], num);
   }
-  if (c < D) out[(qrow * H + h) * D + c] = den > 0.f ? num / den : 0.f;
+  out[qrow * H * D + e] = den > 0.f ? num / den : 0.f;
   if (c == 0 && lse) lse[qrow * H + h] = (M + __log2f(den)) * kLn2;
 }
 
@@ -355,7 +434,9 @@ __global__ void attn_merge_kernel(const float* __restrict__ part_o, const float*
 // Host side.
 // ---------------------------------------------------------------------------
 static bool mfma_shape(const AttnArgs& a) {
-  return a.dtype == 1 && (a.d == 64 || a.d == 128) && (a.h == 16 || a.h == 32 || a.h == 64);
+  const int64_t lim = int64_t(1) << 31;
+  return a.dtype == 1 && (a.d == 64 || a.d == 128) && (a.h == 16 || a.h == 32 || a.h == 64) &&
+         a.n * 2 * a.d < lim && a.L * 2 * a.d < lim && (a.idx ? int64_t(a.k) : a.n) + a.window < lim;
 }
 
 bool attn_supported(const AttnArgs& a) {
@@ -372,14 +453,15 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 static AttnPlan plan_attn(const AttnArgs& a) {
   AttnPlan p{};
-  const int tk = mfma_shape(a) ? 64 : 32;
+  const int tk = mfma_shape(a) ? 64 : 32;  // keys per tile
   const int64_t rows = a.bt * a.nq;
   const int64_t maxkeys = (a.idx ? int64_t(a.k) : a.n) + a.window;
-  // Aim for about four workgroups per compute unit overall, never a chunk
-  // under 256 keys (partials cost 32 KiB per chunk and query).
+  // Aim for about two resident workgroups per compute unit (256 CUs; each
+  // keeps two 32 KiB tiles in flight), never a chunk under 128 keys (a
+  // partial costs h*d*4 bytes per chunk and query).
   const int64_t target_wg = 1024;
   int64_t chunk = (rows * maxkeys + target_wg - 1) / target_wg;
-  chunk = std::max<int64_t>(chunk, 256);
+  chunk = std::max<int64_t>(chunk, 128);
   chunk = (chunk + tk - 1) / tk * tk;
   if (chunk >= maxkeys) chunk = (maxkeys + tk - 1) / tk * tk;
   p.chunk = int(chunk);
@@ -397,8 +479,8 @@ template <bool SPARSE>
 static void launch_attn_mfma(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml, hipStream_t st) {
   const float sl2 = a.scale * kLog2e;
   dim3 grid(unsigned(pl.nsplit), unsigned(a.bt * a.nq));
-#define HATTN_ATTN(D, NW)                                                                                      \
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NW, SPARSE>), grid, dim3(64 * NW), 0, st, (const uint16_t*)a.q,      \
+#define HATTN_ATTN(D, NH)                                                                                      \
+  hipLaunchKernelGGL((attn_mfma_kernel<D, NH, SPARSE>), grid, dim3(64 * NH), 0, st, (const uint16_t*)a.q,      \
                      (const uint16_t*)a.ckv, a.n, a.idx, a.k, a.n_vis, (const uint16_t*)a.raw_kv, a.L, a.q_pos, \
                      a.window, sl2, a.nq, pl.chunk, pl.nsplit, a.out, a.lse, po, pml)
   const int nw = a.h / 16;
@@ -455,8 +537,8 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   LaunchScope ls("attn_merge", st);
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned(a.h), unsigned(a.bt * a.nq)), dim3(unsigned(a.d)), 0, st, po,
-                     pml, pl.nsplit, a.h, a.d, a.out, a.lse);
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256), 0,
+                     st, po, pml, pl.nsplit, a.h, a.d, a.out, a.lse);
   return hipGetLastError();
 }
 

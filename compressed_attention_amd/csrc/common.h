@@ -30,6 +30,16 @@ HATTN_DEV uint16_t f32_to_bf16(float f) {
 HATTN_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
+// Same rounding with the gfx950 packed conversion instruction (one VALU op).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+HATTN_DEV uint32_t pack_bf16x2_hw(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+// 2^x without the denormal-range fixups of exp2f (results below 2^-126
+// flush to zero, which only ever meets softmax weights that are negligible).
+HATTN_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Order-preserving map fp32 -> uint32: a < b (as reals) <=> key(a) < key(b).
 // -0.0 is folded onto +0.0 (equal scores).  Key 0 is never produced by a
@@ -79,6 +89,18 @@ HATTN_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v)
 // B[8*(l/16)..+7][l%16]; D[4*(l/16)+i][l%16] in element i.
 HATTN_DEV f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// gfx950 LDS transpose read: within each group of 16 lanes, lane i receives
+// element i of each of the four 16-element rows formed by concatenating the
+// group's 8-byte chunks (lane j's chunk holds elements 4(j%4)..4(j%4)+3 of
+// row j/4).  Pointing lane j at row (kb + j/4), column (c0 + 4(j%4)) of a
+// row-major bf16 tile yields rows kb..kb+3 of column c0 + i in lane i.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+HATTN_DEV u32x2_t lds_read_tr16(const uint16_t* p) {
+  const i16x4_t v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 HATTN_DEV float to_float(float x) { return x; }

@@ -170,6 +170,93 @@ __global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restr
   }
 }
 
+// Long windows (w >= 32, e.g. HCA's 128): one workgroup per (sequence,
+// entry).  The window's softmax weights go through LDS; thread (row group
+// rg, slot cs) sums rows rg, rg+RG, ... of its 16-byte slot, issuing all its
+// loads before using any; the RG partial sums are then added through LDS
+// in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(256) void compress_window_kernel(const T* __restrict__ x, const float* __restrict__ z,
+                                                              const float* __restrict__ bias, T* __restrict__ y,
+                                                              int64_t L, int C, int w, int s, int64_t N, int64_t e0,
+                                                              int64_t ne) {
+  constexpr int V = Vec16<T>::N;
+  extern __shared__ float wsm[];  // [w] weights, then [RG][C] partial sums
+  __shared__ float red[8];
+  const int64_t e = e0 + blockIdx.x % ne;
+  const int64_t b = blockIdx.x / ne;
+  const int64_t t0 = e * s;
+  const int slots = C / V;
+  const int RG = 256 / slots;
+  const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
+  float mx = -INFINITY;
+  for (int u = threadIdx.x; u < w; u += 256) {
+    const float a = (z ? z[b * L + t0 + u] : 0.f) + (bias ? bias[u] : 0.f);
+    wsm[u] = a;
+    mx = fmaxf(mx, a);
+  }
+  mx = wave_max(mx);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float den = 0.f;
+  for (int u = threadIdx.x; u < w; u += 256) {
+    const float p = __expf(wsm[u] - mx);
+    wsm[u] = p;
+    den += p;
+  }
+  den = wave_sum(den);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[4 + (threadIdx.x >> 6)] = den;
+  __syncthreads();
+  den = red[4] + red[5] + red[6] + red[7];
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.f;
+  const T* xb = x + (b * L + t0) * C + cs * V;
+  if (rg < RG) {
+    int u = rg;
+    for (; u + 3 * RG < w; u += 4 * RG) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = ld16(xb + int64_t(u + j * RG) * C);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float f[V];
+        Vec16<T>::unpack(v[j], f);
+        const float p = wsm[u + j * RG];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = fmaf(p, f[i], acc[i]);
+      }
+    }
+    for (; u < w; u += RG) {
+      float f[V];
+      Vec16<T>::unpack(ld16(xb + int64_t(u) * C), f);
+      const float p = wsm[u];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = fmaf(p, f[i], acc[i]);
+    }
+  }
+  float* part = wsm + w;  // [RG][C]
+  if (rg < RG) {
+#pragma unroll
+    for (int i = 0; i < V; ++i) part[rg * C + cs * V + i] = acc[i];
+  }
+  __syncthreads();
+  const float inv = 1.f / den;
+  for (int c = threadIdx.x; c < C / V; c += 256) {
+    float r[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) r[i] = 0.f;
+    for (int g2 = 0; g2 < RG; ++g2)
+#pragma unroll
+      for (int i = 0; i < V; ++i) r[i] += part[g2 * C + c * V + i];
+#pragma unroll
+    for (int i = 0; i < V; ++i) r[i] *= inv;
+    st16(y + (b * N + e) * C + c * V, Vec16<T>::pack(r));
+  }
+}
+
 template <typename T>
 static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
                                     int w, int s, int64_t N, int64_t e0, int64_t e1, void* y, hipStream_t st) {
@@ -186,6 +273,14 @@ static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C,
     LaunchScope ls("compress_overlap2", st);
     hipLaunchKernelGGL((compress_overlap2_kernel<T, 4>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
                        (const T*)x, z, bias, (T*)y, L, C, N, e0, e1, runs, run, total);
+    return hipGetLastError();
+  }
+  if (w >= 32 && slots <= 256) {
+    const int RG = 256 / slots;
+    const size_t smem = (size_t(w) + size_t(RG) * C) * 4;
+    LaunchScope ls("compress_window", st);
+    hipLaunchKernelGGL((compress_window_kernel<T>), dim3(unsigned(bt * ne)), dim3(256), smem, st, (const T*)x, z, bias,
+                       (T*)y, L, C, w, s, N, e0, ne);
     return hipGetLastError();
   }
   const int run = 1;
@@ -228,36 +323,56 @@ hipError_t launch_visible_count(const int32_t* pos, int64_t count, int w, int s,
 
 // ---------------------------------------------------------------------------
 // HISA pooling ([HISA] my.qihongyi.cn/?p=787, section 第一阶段): block mean
-// with a zero-padded short tail.  Thread = (sequence, block, 16-byte slot);
-// rows are summed in index order in fp32.
+// with a zero-padded short tail.  One workgroup per (sequence, block):
+// thread (row group rg, 16-byte slot cs) sums rows rg, rg+RG, ... in fp32,
+// then the RG partial sums are added through LDS in a fixed order.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k_i, int64_t n, int d, int B, int64_t nb,
-                                                   int64_t j0, int64_t nj, float* __restrict__ reps, int64_t total) {
+                                                   int64_t j0, int64_t nj, float* __restrict__ reps) {
   constexpr int V = Vec16<T>::N;
-  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (t >= total) return;
+  extern __shared__ float part[];  // [RG][d]
+  const int64_t b = blockIdx.x / nj;
+  const int64_t j = j0 + blockIdx.x % nj;
   const int slots = d / V;
-  const int cs = int(t % slots);
-  const int64_t rest = t / slots;
-  const int64_t b = rest / nj;
-  const int64_t j = j0 + rest % nj;
+  const int RG = 256 / slots;
+  const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
   const int64_t i0 = j * B;
-  const int64_t i1 = imin64(n, i0 + B);
+  const int cnt = int(imin64(n, i0 + B) - i0);
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  const T* base = k_i + b * n * d + cs * V;
-  for (int64_t i = i0; i < i1; ++i) {
-    float f[V];
-    Vec16<T>::unpack(ld16(base + i * d), f);
+  if (rg < RG) {
+    const T* base = k_i + (b * n + i0) * d + cs * V;
+    int u = rg;
+    for (; u + 3 * RG < cnt; u += 4 * RG) {
+      u32x4_t v[4];
 #pragma unroll
-    for (int u = 0; u < V; ++u) acc[u] += f[u];
+      for (int q = 0; q < 4; ++q) v[q] = ld16(base + int64_t(u + q * RG) * d);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[V];
+        Vec16<T>::unpack(v[q], f);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += f[i];
+      }
+    }
+    for (; u < cnt; u += RG) {
+      float f[V];
+      Vec16<T>::unpack(ld16(base + int64_t(u) * d), f);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] += f[i];
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) part[rg * d + cs * V + i] = acc[i];
   }
+  __syncthreads();
   const float inv = 1.f / float(B);
-  float* out = reps + (b * nb + j) * d + cs * V;
-#pragma unroll
-  for (int u = 0; u < V; ++u) out[u] = acc[u] * inv;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float r = 0.f;
+    for (int g2 = 0; g2 < RG; ++g2) r += part[g2 * d + c];
+    reps[(b * nb + j) * d + c] = r * inv;
+  }
 }
 
 hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_i, int B, int64_t j0, int64_t j1,
@@ -266,14 +381,15 @@ hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_
   const int64_t nj = j1 - j0;
   if (nj <= 0 || bt <= 0) return hipSuccess;
   LaunchScope ls("hisa_pool", st);
+  const int V = dtype == 0 ? 4 : 8;
+  const int RG = 256 / (d_i / V);
+  const size_t smem = size_t(RG) * d_i * 4;
   if (dtype == 0) {
-    const int64_t total = bt * nj * (d_i / 4);
-    hipLaunchKernelGGL(pool_kernel<float>, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
-                       (const float*)k_i, n, d_i, B, nb, j0, nj, reps, total);
+    hipLaunchKernelGGL(pool_kernel<float>, dim3(unsigned(bt * nj)), dim3(256), smem, st, (const float*)k_i, n, d_i, B,
+                       nb, j0, nj, reps);
   } else {
-    const int64_t total = bt * nj * (d_i / 8);
-    hipLaunchKernelGGL(pool_kernel<uint16_t>, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
-                       (const uint16_t*)k_i, n, d_i, B, nb, j0, nj, reps, total);
+    hipLaunchKernelGGL(pool_kernel<uint16_t>, dim3(unsigned(bt * nj)), dim3(256), smem, st, (const uint16_t*)k_i, n,
+                       d_i, B, nb, j0, nj, reps);
   }
   return hipGetLastError();
 }

@@ -185,7 +185,7 @@ hattn_status_t hattn_index_topk(int dtype, const void* q_i, const void* k_i, con
 hattn_status_t hattn_hisa_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int32_t d_i, int32_t B,
                                int64_t j_begin, int64_t j_end, float* reps, void* stream) {
   if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "hisa_pool: bad dtype %d", dtype);
-  if (bt < 0 || n < 0 || B < 1 || d_i < 1) return fail(HATTN_ERR_ARG, "hisa_pool: bad sizes");
+  if (bt < 0 || n < 0 || B < 1 || d_i < 1 || d_i > 1024) return fail(HATTN_ERR_ARG, "hisa_pool: bad sizes");
   const int vec = 16 / elem_bytes(dtype);
   if (d_i % vec) return fail(HATTN_ERR_ARG, "hisa_pool: d_i=%d must be a multiple of %d", d_i, vec);
   const int64_t nb = (n + B - 1) / B;
@@ -236,8 +236,9 @@ hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int6
                                  size_t* ws_bytes, void* stream) {
   if (k < 0) return fail(HATTN_ERR_ARG, "sparse_attn: k < 0");
   if (bt * nq > 0 && k > 0 && !idx) return fail(HATTN_ERR_ARG, "sparse_attn: NULL idx");
-  static const int32_t dummy = -1;
-  hattn::AttnArgs a{dtype, q, ckv, n, idx ? idx : &dummy, k, nullptr, raw_kv, L, q_pos, window, scale,
+  // With k == 0 no index is ever used; the kernels still read a clamped
+  // slot, so hand them a valid device int32 array (q_pos has >= 1 entry).
+  hattn::AttnArgs a{dtype, q, ckv, n, k > 0 ? idx : q_pos, k, nullptr, raw_kv, L, q_pos, window, scale,
                     bt, nq, h, d, out, lse};
   return attn_common("sparse_attn", a, ws, ws_bytes, stream);
 }

@@ -156,9 +156,12 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma_kernel(const uint16_t*
 
 // ---------------------------------------------------------------------------
 // HISA stage 1 score on fp32 block representatives, 16 heads, d_i = 16*KQ.
-// One wave per query (4 queries per workgroup), blocks in LDS tiles of 64.
+// A workgroup owns QPW queries (1 or 4) and one LDS tile of 64 block means;
+// its 4 waves cover the (query, 16-block subtile) pairs: with 4 queries each
+// wave takes one query and all four subtiles, with one query (decode) each
+// wave takes one subtile.
 // ---------------------------------------------------------------------------
-template <typename TQ, int KQ>
+template <typename TQ, int KQ, int QPW>
 __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restrict__ q_i,
                                                               const float* __restrict__ reps,
                                                               const float* __restrict__ w_i,
@@ -169,17 +172,20 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
   constexpr int TB = 64;
   constexpr int PITCH = D + 4;
   constexpr int PIECES = TB * D / 4 / 256;
+  constexpr int NTW = 4 / (4 / QPW);  // subtiles per wave: 4 (QPW=4) or 1 (QPW=1)
   __shared__ __align__(16) float rt[TB * PITCH];
-  __shared__ int s_nb[4];
+  __shared__ int s_nb[QPW];
 
   int qg, ch;
   if (!xcd_decode(blockIdx.x, nqg, nch, &qg, &ch)) return;
   const int64_t b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int64_t q = int64_t(qg) * 4 + wave;
-  if (threadIdx.x < 4) {
-    const int64_t qq = int64_t(qg) * 4 + threadIdx.x;
+  const int qw = QPW == 4 ? wave : 0;           // this wave's query within the group
+  const int nt0 = QPW == 4 ? 0 : wave;          // first subtile of this wave
+  const int64_t q = int64_t(qg) * QPW + qw;
+  if (threadIdx.x < QPW) {
+    const int64_t qq = int64_t(qg) * QPW + threadIdx.x;
     int v = 0;
     if (qq < nq) {
       const int64_t nvq = imin64(n, imax64(0, n_vis[b * nq + qq]));
@@ -188,12 +194,14 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
     s_nb[threadIdx.x] = v;
   }
   __syncthreads();
-  const int maxb = max(max(s_nb[0], s_nb[1]), max(s_nb[2], s_nb[3]));
+  int maxb = 0;
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) maxb = max(maxb, s_nb[i]);
   const int64_t j_begin = int64_t(ch) * chunk;
   const int64_t j_end = imin64(j_begin + chunk, maxb);
   if (j_begin >= j_end) return;
   const bool ok = q < nq;
-  const int my_nb = s_nb[wave];
+  const int my_nb = s_nb[qw];
 
   f32x4_t a[KQ];
   float wv[4];
@@ -209,36 +217,41 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
   const float* rb = reps + b * nb * D;
   for (int64_t j0 = j_begin; j0 < j_end; j0 += TB) {
     __syncthreads();
+    u32x4_t v[PIECES];
 #pragma unroll
     for (int u = 0; u < PIECES; ++u) {
       const int p = threadIdx.x + 256 * u;
-      const int row = p / (D / 4), col = p % (D / 4);
-      const int64_t j = j0 + row;
-      const u32x4_t v = j < nb ? ld16(rb + j * D + col * 4) : u32x4_t{0, 0, 0, 0};
-      *reinterpret_cast<u32x4_t*>(&rt[row * PITCH + col * 4]) = v;
+      const int64_t j = j0 + p / (D / 4);
+      v[u] = j < nb ? ld16(rb + j * D + (p % (D / 4)) * 4) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int p = threadIdx.x + 256 * u;
+      *reinterpret_cast<u32x4_t*>(&rt[(p / (D / 4)) * PITCH + (p % (D / 4)) * 4]) = v[u];
     }
     __syncthreads();
     if (!ok || j0 >= my_nb) continue;
-    f32x4_t acc[4];
+    f32x4_t acc[NTW];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NTW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int t = 0; t < NTW; ++t) {
+        const int nt = nt0 + t;
         const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&rt[(16 * nt + r16) * PITCH + 16 * kq + 4 * g]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kq][j], bv[j], acc[nt], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kq][j], bv[j], acc[t], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int t = 0; t < NTW; ++t) {
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(wv[i], fmaxf(acc[nt][i], 0.f), s);
+      for (int i = 0; i < 4; ++i) s = fmaf(wv[i], fmaxf(acc[t][i], 0.f), s);
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
-      const int64_t j = j0 + 16 * nt + r16;
+      const int64_t j = j0 + 16 * (nt0 + t) + r16;
       if (g == 0 && j < my_nb) S1[(b * nq + q) * ld + j] = s;
     }
   }
@@ -381,8 +394,7 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
   if (threadIdx.x == 0) cnt = 0;
   __syncthreads();
   const int nvalid = min(kSelCap, row_valid_count<MODE>(n_vis, blk, row, n, B, m, &cnt));
-  const float* srow = S + row * ld;
-  for (int i = threadIdx.x; i < nvalid; i += kSelNT) keys[i] = order_key(srow[i]);
+  load_score_keys<kSelNT>(S + row * ld, nvalid, keys);
   __syncthreads();
   radix_threshold<kSelNT>(keys, nvalid, k, sh);
   int32_t* orow = idx + row * k;
@@ -400,30 +412,181 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
   }
 }
 
+// Long flat rows (more than kSelCap candidates), one workgroup per row:
+//  1. threshold: tau = the key of rank r in an evenly spaced sample of 8192
+//     scores, with r about 1.5 * k * 8192 / n (expected ~1.5 k keys >= tau);
+//  2. collect: each wave streams its contiguous part of the row once with
+//     16-byte loads and appends the keys >= tau, with their positions, to its
+//     own LDS region in position order (ballot prefix sums);
+//  3. exact top-k over the collected candidates (empty region slots hold the
+//     key 0, which is never chosen), emitted in position order.
+// The result is exact whatever the sample says: if fewer than k keys were
+// collected the threshold was too high, if a region overflowed it was too
+// low; both retry with a rank 2x lower / higher, and a row that still fails
+// is flagged and finished by the exact segment + merge kernels below.
+constexpr int kSampleN = 8192;
+constexpr int kRegion = 512;  // candidate slots per wave (16 waves -> 8192)
+
+__global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __restrict__ S, int64_t ld,
+                                                                const int32_t* __restrict__ n_vis, int64_t n, int k,
+                                                                int32_t* __restrict__ idx,
+                                                                float* __restrict__ score_out,
+                                                                int32_t* __restrict__ flags) {
+  constexpr int NW = kSelNT / kWave;
+  static_assert(NW * kRegion == kSampleN, "region layout");
+  extern __shared__ uint32_t dyn[];
+  uint32_t* rkey = dyn;                               // [NW][kRegion]
+  int32_t* rpos = reinterpret_cast<int32_t*>(dyn + kSampleN);  // [NW][kRegion]
+  uint32_t* samp = dyn + 2 * kSampleN;                // [kSampleN]
+  __shared__ SelectShared<kSelNT> sh;
+  __shared__ int wcnt[NW];
+  __shared__ int verdict;
+  const int64_t row = blockIdx.x;
+  const int nv = int(imin64(n, imax64(0, n_vis[row])));
+  const float* srow = S + row * ld;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t* orow = idx + row * k;
+  float* scrow = score_out ? score_out + row * k : nullptr;
+
+  if (nv <= kSelCap) {  // short row: plain LDS selection over all of it
+    load_score_keys<kSelNT>(srow, nv, dyn);
+    __syncthreads();
+    radix_threshold<kSelNT>(dyn, nv, k, sh);
+    const int chosen = emit_selected<kSelNT>(dyn, nv, sh, [&](int slot, int i) {
+      orow[slot] = i;
+      if (scrow) scrow[slot] = key_to_float(dyn[i]);
+    });
+    for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+      orow[t] = -1;
+      if (scrow) scrow[t] = -INFINITY;
+    }
+    if (threadIdx.x == 0) flags[row] = 0;
+    return;
+  }
+  // 1. sample: 16 evenly spaced runs of 512 scores (16-byte aligned)
+  {
+    const int stride = (nv / 16) & ~3;
+    for (int c = 0; c < 16; ++c) load_score_keys<kSelNT>(srow + c * stride, 512, samp + c * 512);
+  }
+  __syncthreads();
+  int r = min(kSampleN, int((3LL * k * kSampleN) / (2LL * nv)) + 32);
+  const int segw = ((nv + NW - 1) / NW + 255) & ~255;
+  const int p0 = wave * segw, p1 = min(nv, p0 + segw);
+  bool done = false;
+  for (int attempt = 0; attempt < 4 && !done; ++attempt) {
+    radix_threshold<kSelNT>(samp, kSampleN, r, sh);
+    const uint32_t tau = sh.thr;  // key of the r-th largest sample (0: all)
+    // 2. collect keys >= tau of this wave's segment, in position order
+    uint32_t* rk = rkey + wave * kRegion;
+    int32_t* rp = rpos + wave * kRegion;
+    int cnt = 0;
+    for (int base = p0; base < p1; base += 256 * 2) {
+      f32x4_t v[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = base + u * 256 + lane * 4;
+        if (i + 3 < p1) {
+          v[u] = *reinterpret_cast<const f32x4_t*>(srow + i);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[u][e] = i + e < p1 ? srow[i + e] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = base + u * 256 + lane * 4;
+        uint32_t key[4];
+        bool sel[4];
+        uint64_t bal[4];
+        int below = 0, total = 0;
+        const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          key[e] = i + e < p1 ? order_key(v[u][e]) : 0u;
+          sel[e] = key[e] != 0u && key[e] >= tau;
+          bal[e] = ballot(sel[e]);
+          below += __popcll(bal[e] & lt);
+          total += __popcll(bal[e]);
+        }
+        int slot = cnt + below;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (sel[e]) {
+            if (slot < kRegion) {
+              rk[slot] = key[e];
+              rp[slot] = i + e;
+            }
+            ++slot;
+          }
+        }
+        cnt += total;
+      }
+    }
+    if (lane == 0) wcnt[wave] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0, ovf = 0;
+      for (int w = 0; w < NW; ++w) {
+        tot += wcnt[w];
+        ovf |= wcnt[w] > kRegion;
+      }
+      verdict = ovf ? 1 : (tot < k ? 2 : 0);  // 1: tau too low, 2: tau too high
+    }
+    __syncthreads();
+    const int vd = verdict;
+    if (vd == 0) {
+      for (int t = min(cnt, kRegion) + lane; t < kRegion; t += 64) rk[t] = 0u;
+      done = true;
+    } else {
+      const int r2 = vd == 1 ? max(1, r / 2) : min(kSampleN, r * 2);
+      if (r2 == r) break;
+      r = r2;
+    }
+    __syncthreads();
+  }
+  if (!done) {
+    if (threadIdx.x == 0) flags[row] = 1;  // finished by the segment + merge kernels
+    return;
+  }
+  // 3. exact selection over the candidates (key 0 = empty slot)
+  radix_threshold<kSelNT>(rkey, kSampleN, k, sh);
+  const int chosen = emit_selected<kSelNT>(rkey, kSampleN, sh, [&](int slot, int i) {
+    orow[slot] = rpos[i];
+    if (scrow) scrow[slot] = key_to_float(rkey[i]);
+  });
+  for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+    orow[t] = -1;
+    if (scrow) scrow[t] = -INFINITY;
+  }
+  if (threadIdx.x == 0) flags[row] = 0;
+}
+
 // Level 1 for long flat rows: exact top-k of each segment (an element outside
 // its segment's top-k has k larger elements and cannot be chosen overall).
+// Candidate lists are stored with a stride of kp = k rounded up to 4 entries.
 __global__ __launch_bounds__(kSelNT) void select_segment_kernel(const float* __restrict__ S, int64_t ld,
                                                                 const int32_t* __restrict__ n_vis, int64_t n, int seg,
-                                                                int nseg, int k, uint32_t* __restrict__ ckey,
-                                                                int32_t* __restrict__ cpos) {
+                                                                int nseg, int k, int kp, uint32_t* __restrict__ ckey,
+                                                                int32_t* __restrict__ cpos,
+                                                                const int32_t* __restrict__ flags) {
   extern __shared__ uint32_t keys[];
   __shared__ SelectShared<kSelNT> sh;
   const int64_t row = blockIdx.y;
+  if (flags[row] == 0) return;  // already selected by select_sampled_kernel
   const int s = blockIdx.x;
   const int64_t nv = imin64(n, imax64(0, n_vis[row]));
   const int64_t p0 = int64_t(s) * seg;
   const int cnt = int(imax64(0, imin64(seg, nv - p0)));
-  const float* srow = S + row * ld + p0;
-  for (int i = threadIdx.x; i < cnt; i += kSelNT) keys[i] = order_key(srow[i]);
+  load_score_keys<kSelNT>(S + row * ld + p0, cnt, keys);
   __syncthreads();
   radix_threshold<kSelNT>(keys, cnt, k, sh);
-  uint32_t* ok = ckey + (row * nseg + s) * int64_t(k);
-  int32_t* op = cpos + (row * nseg + s) * int64_t(k);
+  uint32_t* ok = ckey + (row * nseg + s) * int64_t(kp);
+  int32_t* op = cpos + (row * nseg + s) * int64_t(kp);
   const int chosen = emit_selected<kSelNT>(keys, cnt, sh, [&](int slot, int i) {
     ok[slot] = keys[i];
     op[slot] = int32_t(p0 + i);
   });
-  for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+  for (int t = chosen + threadIdx.x; t < kp; t += kSelNT) {
     ok[t] = 0u;
     op[t] = -1;
   }
@@ -433,22 +596,22 @@ __global__ __launch_bounds__(kSelNT) void select_segment_kernel(const float* __r
 // = empty slot).  With one group left it writes the final indices.
 __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __restrict__ ikey,
                                                               const int32_t* __restrict__ ipos, int nin, int G, int k,
-                                                              uint32_t* __restrict__ okey, int32_t* __restrict__ opos,
-                                                              int32_t* __restrict__ idx, float* __restrict__ score_out) {
+                                                              int kp, uint32_t* __restrict__ okey,
+                                                              int32_t* __restrict__ opos,
+                                                              int32_t* __restrict__ idx, float* __restrict__ score_out,
+                                                              const int32_t* __restrict__ flags) {
   extern __shared__ uint32_t keys[];
   __shared__ SelectShared<kSelNT> sh;
   int32_t* pos = reinterpret_cast<int32_t*>(keys + kSelCap);
   const int64_t row = blockIdx.y;
+  if (flags[row] == 0) return;  // already selected by select_sampled_kernel
   const int grp = blockIdx.x;
   const int nout = (nin + G - 1) / G;
   const int l0 = grp * G, l1 = min(nin, l0 + G);
-  const int cnt = (l1 - l0) * k;
-  const uint32_t* ik = ikey + (row * nin + l0) * int64_t(k);
-  const int32_t* ip = ipos + (row * nin + l0) * int64_t(k);
-  for (int i = threadIdx.x; i < cnt; i += kSelNT) {
-    keys[i] = ik[i];
-    pos[i] = ip[i];
-  }
+  const int cnt = (l1 - l0) * kp;
+  const uint32_t* ik = ikey + (row * nin + l0) * int64_t(kp);
+  const int32_t* ip = ipos + (row * nin + l0) * int64_t(kp);
+  load_candidates<kSelNT>(ik, ip, cnt, keys, pos);
   __syncthreads();
   radix_threshold<kSelNT>(keys, cnt, k, sh);
   if (nout == 1) {
@@ -463,13 +626,13 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
       if (scrow) scrow[t] = -INFINITY;
     }
   } else {
-    uint32_t* ok = okey + (row * nout + grp) * int64_t(k);
-    int32_t* op = opos + (row * nout + grp) * int64_t(k);
+    uint32_t* ok = okey + (row * nout + grp) * int64_t(kp);
+    int32_t* op = opos + (row * nout + grp) * int64_t(kp);
     const int chosen = emit_selected<kSelNT>(keys, cnt, sh, [&](int slot, int i) {
       ok[slot] = keys[i];
       op[slot] = pos[i];
     });
-    for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+    for (int t = chosen + threadIdx.x; t < kp; t += kSelNT) {
       ok[t] = 0u;
       op[t] = -1;
     }
@@ -489,8 +652,8 @@ static bool flat_mfma_ok(const IndexArgs& a) {
 struct FlatPlan {
   int64_t rows, ld;
   bool multi;
-  int seg, nseg, G;
-  size_t s_bytes, cand_bytes, total;
+  int seg, nseg, G, kp;
+  size_t s_bytes, cand_bytes, flag_bytes, total;
 };
 
 static FlatPlan plan_flat(const IndexArgs& a, int k) {
@@ -502,13 +665,15 @@ static FlatPlan plan_flat(const IndexArgs& a, int k) {
   if (p.multi) {
     p.seg = kSelCap;
     p.nseg = int((a.n + p.seg - 1) / p.seg);
-    p.G = kSelCap / k;
+    p.kp = (k + 3) & ~3;
+    p.G = kSelCap / p.kp;
     // ping-pong candidate buffers: level-1 lists, then merged lists
-    const size_t l1 = size_t(p.rows) * p.nseg * k * 8;
-    const size_t l2 = size_t(p.rows) * ((p.nseg + p.G - 1) / p.G) * k * 8;
+    const size_t l1 = size_t(p.rows) * p.nseg * p.kp * 8;
+    const size_t l2 = size_t(p.rows) * ((p.nseg + p.G - 1) / p.G) * p.kp * 8;
     p.cand_bytes = align256(l1) + align256(l2);
+    p.flag_bytes = align256(size_t(p.rows) * 4);
   }
-  p.total = p.s_bytes + p.cand_bytes;
+  p.total = p.s_bytes + p.cand_bytes + p.flag_bytes;
   return p;
 }
 
@@ -523,6 +688,8 @@ static void set_lds_limits() {
   (void)hipFuncSetAttribute((const void*)select_rows_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
   (void)hipFuncSetAttribute((const void*)select_segment_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
   (void)hipFuncSetAttribute((const void*)select_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 8);
+  (void)hipFuncSetAttribute((const void*)select_sampled_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kSampleN * 12);
 }
 
 template <int MODE, typename TQ, typename TK>
@@ -573,18 +740,26 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
     return hipGetLastError();
   }
   char* cb = reinterpret_cast<char*>(ws) + p.s_bytes;
-  const size_t l1 = align256(size_t(p.rows) * p.nseg * k * 8);
+  const size_t l1 = align256(size_t(p.rows) * p.nseg * p.kp * 8);
   uint32_t* bufk[2];
   int32_t* bufp[2];
   bufk[0] = reinterpret_cast<uint32_t*>(cb);
-  bufp[0] = reinterpret_cast<int32_t*>(cb + size_t(p.rows) * p.nseg * k * 4);
+  bufp[0] = reinterpret_cast<int32_t*>(cb + size_t(p.rows) * p.nseg * p.kp * 4);
   bufk[1] = reinterpret_cast<uint32_t*>(cb + l1);
   const int n2 = (p.nseg + p.G - 1) / p.G;
-  bufp[1] = reinterpret_cast<int32_t*>(cb + l1 + size_t(p.rows) * n2 * k * 4);
+  bufp[1] = reinterpret_cast<int32_t*>(cb + l1 + size_t(p.rows) * n2 * p.kp * 4);
+  int32_t* flags = reinterpret_cast<int32_t*>(cb + p.cand_bytes);
+  {
+    LaunchScope ls("select_sampled", st);
+    hipLaunchKernelGGL(select_sampled_kernel, dim3(unsigned(p.rows)), dim3(kSelNT), kSampleN * 12, st, S, p.ld,
+                       a.n_vis, a.n, k, idx, score, flags);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   {
     LaunchScope ls("select_segment", st);
     hipLaunchKernelGGL(select_segment_kernel, dim3(unsigned(p.nseg), unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st,
-                       S, p.ld, a.n_vis, a.n, p.seg, p.nseg, k, bufk[0], bufp[0]);
+                       S, p.ld, a.n_vis, a.n, p.seg, p.nseg, k, p.kp, bufk[0], bufp[0], flags);
   }
   int nin = p.nseg, cur = 0;
   while (true) {
@@ -593,7 +768,7 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
     // Lists of a row at level i+1 never outnumber those at level i, so the
     // two buffers (sized for levels 1 and 2) alternate safely.
     hipLaunchKernelGGL(select_merge_kernel, dim3(unsigned(nout), unsigned(p.rows)), dim3(kSelNT), kSelCap * 8, st,
-                       bufk[cur], bufp[cur], nin, p.G, k, bufk[cur ^ 1], bufp[cur ^ 1], idx, score);
+                       bufk[cur], bufp[cur], nin, p.G, k, p.kp, bufk[cur ^ 1], bufp[cur ^ 1], idx, score, flags);
     e = hipGetLastError();
     if (e != hipSuccess || nout == 1) return e;
     nin = nout;
@@ -638,14 +813,19 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   // Stage 1: block scores.
   const bool mfma1 = a.h_i == 16 && a.d_i % 16 == 0 && a.d_i <= 256;
   if (mfma1) {
-    const int nqg = int((a.nq + 3) / 4);
-    const int chunk = 256;
+    const int qpw = a.nq >= 4 ? 4 : 1;  // queries per workgroup
+    const int nqg = int((a.nq + qpw - 1) / qpw);
+    const int chunk = 64;  // one LDS tile of block means per workgroup
     const int nch = int((p.nb + chunk - 1) / chunk);
     dim3 grid(xcd_grid(nqg, nch), unsigned(a.bt));
     LaunchScope ls("score_stage1_mfma", st);
 #define HATTN_S1(T, KQ)                                                                                      \
-  hipLaunchKernelGGL((score_stage1_kernel<T, KQ>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i,      \
-                     a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk)
+  if (qpw == 4)                                                                                              \
+    hipLaunchKernelGGL((score_stage1_kernel<T, KQ, 4>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
+                       a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk);                            \
+  else                                                                                                       \
+    hipLaunchKernelGGL((score_stage1_kernel<T, KQ, 1>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
+                       a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk)
     if (a.dtype == 0) {
       switch (a.d_i / 16) {
         case 1: HATTN_S1(float, 1); break;

@@ -28,6 +28,63 @@ struct SelectShared {
   int digit;
 };
 
+// Loads n fp32 scores (16-byte aligned row) into LDS as order-preserving
+// keys.  Every thread issues all its 16-byte loads before converting any, so
+// a row costs one memory round trip instead of one per element.
+template <int NT>
+HATTN_DEV void load_score_keys(const float* __restrict__ src, int n, uint32_t* keys) {
+  constexpr int UNR = 4;
+  const int n4 = n & ~3;
+  for (int base = threadIdx.x * 4; base < n4; base += NT * 4 * UNR) {
+    f32x4_t v[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + u * NT * 4;
+      v[u] = i < n4 ? *reinterpret_cast<const f32x4_t*>(src + i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + u * NT * 4;
+      if (i < n4) {
+        u32x4_t kv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[e] = order_key(v[u][e]);
+        *reinterpret_cast<u32x4_t*>(keys + i) = kv;
+      }
+    }
+  }
+  for (int i = n4 + threadIdx.x; i < n; i += NT) keys[i] = order_key(src[i]);
+}
+
+// Same for (key, position) candidate lists of n entries (16-byte aligned).
+template <int NT>
+HATTN_DEV void load_candidates(const uint32_t* __restrict__ ik, const int32_t* __restrict__ ip, int n, uint32_t* keys,
+                               int32_t* pos) {
+  constexpr int UNR = 2;
+  const int n4 = n & ~3;
+  for (int base = threadIdx.x * 4; base < n4; base += NT * 4 * UNR) {
+    u32x4_t kv[UNR], pv[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + u * NT * 4;
+      kv[u] = i < n4 ? *reinterpret_cast<const u32x4_t*>(ik + i) : u32x4_t{0, 0, 0, 0};
+      pv[u] = i < n4 ? *reinterpret_cast<const u32x4_t*>(ip + i) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int i = base + u * NT * 4;
+      if (i < n4) {
+        *reinterpret_cast<u32x4_t*>(keys + i) = kv[u];
+        *reinterpret_cast<u32x4_t*>(pos + i) = pv[u];
+      }
+    }
+  }
+  for (int i = n4 + threadIdx.x; i < n; i += NT) {
+    keys[i] = ik[i];
+    pos[i] = ip[i];
+  }
+}
+
 // Block-wide exclusive prefix sum of v (thread order); *total gets the sum.
 template <int NT>
 HATTN_DEV int block_exclusive_scan(int v, int* red, int* total) {

@@ -46,3 +46,54 @@ def test_tiny_hybrid_layer_chain():
     r_nvh = np.array([oracle.n_visible(int(p), 128, 128, r_hkv.shape[0]) for p in pos])
     r_oh, _ = oracle.dense_compressed_attention(f64(t["q"][0]), r_hkv, r_nvh, raw, pos, P["window"], sc)
     assert np.abs(f64(o_hca[0]) - r_oh).max() < 1e-4
+
+
+def test_decode_step_hybrid_pair_reduced():
+    # The decode step that bench.py times, at 2 sequences of 65536 tokens:
+    # compress the windows the last token completes, refresh the last HISA
+    # block mean, HISA selection, sparse (CSA) and dense (HCA) attention.
+    # Oracle: the same step on the host from the same inputs.
+    bt, L = 2, 65536
+    N = oracle.n_entries(L, 8, 4)
+    Nh = oracle.n_entries(L, 128, 128)
+    w = synth.hybrid_pair_decode(0, device="cpu", bt=bt, L=L, N_csa=N)
+    t = w.tensors
+    # integer-grid indexer (4-bit weights): exact selection on both sides
+    t["q_i"] = synth.int_grid((bt, 1, 16, 128), 301, -4, 4, dtype=torch.bfloat16)
+    t["k_i"] = synth.int_grid((bt, N, 128), 302, -4, 4, dtype=torch.bfloat16)
+    t["w_i"] = synth.dyadic_uniform((bt, 1, 16), 303, bits=4)
+    g = {k_: v.to(DEV) for k_, v in t.items()}
+    B, m, k = 128, 64, 512
+    # caches built from all but the last token's windows (as before the step)
+    ckv = ops.compress(g["csa_raw_kv"], g["csa_z"], g["csa_b"], 8, 4)
+    hkv = ops.compress(g["hca_raw_kv"], g["hca_z"], g["hca_b"], 128, 128)
+    ckv[:, N - 1] = 0
+    hkv[:, Nh - 1] = 0
+    reps = ops.hisa_pool(g["k_i"], B)
+    reps[:, -1] = 0
+    # the step
+    ops.compress(g["csa_raw_kv"], g["csa_z"], g["csa_b"], 8, 4, N - 1, N, out=ckv)
+    ops.compress(g["hca_raw_kv"], g["hca_z"], g["hca_b"], 128, 128, Nh - 1, Nh, out=hkv)
+    nb = reps.shape[1]
+    ops.hisa_pool(g["k_i"], B, nb - 1, nb, out=reps)
+    nv = ops.visible_count(g["q_pos"], 8, 4, N)
+    nvh = ops.visible_count(g["q_pos"], 128, 128, Nh)
+    idx = ops.hisa_topk(g["q_i"], g["k_i"], g["w_i"], nv, reps, B, m, k)
+    o1 = ops.sparse_attn(g["csa_q"], ckv, idx, g["csa_raw_kv"], g["q_pos"], 128)
+    o2 = ops.dense_compressed_attn(g["hca_q"], hkv, nvh, g["hca_raw_kv"], g["q_pos"], 128)
+    torch.cuda.synchronize()
+    sc = 1 / math.sqrt(128)
+    for b in range(bt):
+        raw_c, raw_h = f64(t["csa_raw_kv"][b]), f64(t["hca_raw_kv"][b])
+        r_ckv = oracle.compress(raw_c, f64(t["csa_z"][b]), f64(t["csa_b"]), 8, 4)
+        r_hkv = oracle.compress(raw_h, f64(t["hca_z"][b]), f64(t["hca_b"]), 128, 128)
+        p = int(t["q_pos"][b, 0])
+        assert int(nv[b, 0]) == oracle.n_visible(p, 8, 4, N) == N
+        assert int(nvh[b, 0]) == oracle.n_visible(p, 128, 128, Nh) == Nh
+        r_idx, _ = oracle.hisa_topk(f64(t["q_i"][b]), f64(t["k_i"][b]), f64(t["w_i"][b]), np.array([N]), B, m, k)
+        assert np.array_equal(idx[b].cpu().numpy(), r_idx)
+        # GPU caches are bf16 roundings of the oracle's fp64 entries
+        r_o1, _ = oracle.sparse_attention(f64(t["csa_q"][b]), r_ckv, r_idx, raw_c, np.array([p]), 128, sc)
+        r_o2, _ = oracle.dense_compressed_attention(f64(t["hca_q"][b]), r_hkv, [Nh], raw_h, np.array([p]), 128, sc)
+        assert np.abs(f64(o1[b]) - r_o1).max() < 1e-2
+        assert np.abs(f64(o2[b]) - r_o2).max() < 1e-2

@@ -188,3 +188,45 @@ def test_hisa_float_inputs_vs_oracle():
                               nv.cpu().numpy()[0][rows], B, m, k)
     mean, mn = iou_rows(idx.cpu().numpy()[0, rows], ref)
     assert mean >= 0.999, (mean, mn)
+
+
+@pytest.mark.parametrize("N,B,m,k", [(20000, 128, 64, 2048), (262143, 128, 64, 512), (5000, 64, 8, 300)])
+def test_hisa_decode_shape_exact(N, B, m, k):
+    # One query per sequence (the decode launch shape), ragged last block,
+    # integer grid with 4-bit weights (stage-1 scores exact, bound asserted).
+    bt = 3
+    q_i = synth.int_grid((bt, 1, 16, 128), 201, -4, 4, dtype=torch.bfloat16)
+    k_i = synth.int_grid((bt, N, 128), 202, -4, 4, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((bt, 1, 16), 203, bits=4)
+    nv = torch.tensor([[N], [N - 77], [B * 3 + 5]], dtype=torch.int32)
+    kd = k_i.to(DEV)
+    reps = ops.hisa_pool(kd, B)
+    idx, blk = ops.hisa_topk(q_i.to(DEV), kd, w_i.to(DEV), nv.to(DEV), reps, B, m, k, return_blocks=True)
+    torch.cuda.synchronize()
+    for b in range(bt):
+        q, kk, ww = f64(q_i[b]), f64(k_i[b]), f64(w_i[b])
+        _stage1_exact_bound(q, kk, ww, B, 4)
+        ref, ref_blk = oracle.hisa_topk(q, kk, ww, nv[b].numpy(), B, m, k)
+        assert np.array_equal(blk.cpu().numpy()[b], ref_blk), b
+        assert np.array_equal(idx.cpu().numpy()[b], ref), b
+
+
+def test_long_rows_ties_take_the_fallback_path():
+    # All-zero queries: every visible score is exactly 0, so the sampled
+    # threshold can never isolate k candidates; the exact segment + merge
+    # kernels must finish those rows (lowest indices win the ties).  Row 1 is
+    # ordinary float data on the fast path, row 2 a short row.
+    N, k = 40000, 1000
+    q_i = synth.normal((1, 3, 16, 128), 211, dtype=torch.bfloat16)
+    q_i[0, 0] = 0
+    k_i = synth.normal((1, N, 128), 212, dtype=torch.bfloat16)
+    w_i = synth.uniform((1, 3, 16), 213)
+    nv = torch.tensor([[N, N - 5, 9000]], dtype=torch.int32)
+    idx, sc = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), k, return_scores=True)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()[0]
+    assert list(got[0]) == list(range(k))
+    assert float(sc[0, 0].abs().max()) == 0.0
+    ref = oracle.flat_topk(f64(q_i[0, 1:]), f64(k_i[0]), f64(w_i[0, 1:]), nv[0, 1:].numpy(), k)
+    mean, mn = iou_rows(got[1:], ref)
+    assert mean >= 0.999, (mean, mn)
