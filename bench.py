@@ -336,6 +336,72 @@ def cpu_baseline(args, k):
                        f"{el:.1f} s of host time; block means precomputed as in the GPU step")
 
 
+
+# ----------------------------------------------------------------------------
+# counter probe: the dominant kernel alone, in the launch configuration the
+# step uses, plus a plain copy of known size that calibrates the counters
+# ----------------------------------------------------------------------------
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_dense_hybrid_pair_b8_traffic.txt")
+ATTN_SOURCES = ["compressed_attention_amd/csrc/attention.hip", "compressed_attention_amd/csrc/common.h",
+                "compressed_attention_amd/csrc/internal.h"]
+COPY_BYTES = 256 * MiB
+
+
+def attn_sources_sha():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def probe_attn_dense(args):
+    """Launches the layer pair's HCA dense attention (8 sequences, 8,192
+    entries + window) ``args.steps`` times over rotating cache replicas, then
+    copies a 256 MiB buffer 3 times.  Run under rocprofv3 --pmc."""
+    import torch
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    bt, L, Nh = 8, 1 << 20, 8192
+    W = synth.hybrid_pair_decode(0, device=dev, bt=bt, L=L, N_csa=262143)
+    t = W.tensors
+    hkv = ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128)
+    nvh = ops.visible_count(t["q_pos"], 128, 128, Nh)
+    caches = [hkv] + [hkv.clone() for _ in range(args.replicas - 1)]
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    log(f"[probe] sources {attn_sources_sha()}: {args.steps} dense attention launches, then 3 copies of {COPY_BYTES} B")
+    for i in range(args.steps):
+        ops.dense_compressed_attn(t["hca_q"], caches[i % len(caches)], nvh, t["hca_raw_kv"], t["q_pos"], 128)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)  # one elementwise kernel: reads and writes COPY_BYTES
+    torch.cuda.synchronize()
+    log("[probe] done")
+
+
+def load_traffic():
+    """Calibrated HBM bytes per launch of the dominant kernel, from the
+    committed counter summary; None when it is missing or was taken on other
+    attention sources than the ones here."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith(("#", " ")):
+                    a, b = line.split(":", 1)
+                    kv[a.strip()] = b.strip()
+        if kv.get("sources_sha256_16") != attn_sources_sha():
+            return None
+        return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
 # ----------------------------------------------------------------------------
 
 def roofline_entry(kern_ms, nbytes):
@@ -353,6 +419,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", choices=["attn_dense"], default=None,
+                    help="run only the dominant kernel and a calibration copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -365,6 +433,9 @@ def main():
     from compressed_attention_amd import _lib
 
     _lib.lib()  # fail loudly if the HIP library is missing
+    if args.probe == "attn_dense":
+        probe_attn_dense(args)
+        return
 
     main_k = args.k
     res = hybrid_pair(args)
@@ -410,8 +481,9 @@ def main():
     dom = max((kk for kk in kt if kk in res["kernel_bytes"]), key=lambda kk: kt[kk][0] * kt[kk][1])
     dom_ms = kt[dom][0]
     dom_bytes = res["kernel_bytes"].get(dom)
-    roof = dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None, traffic=None, kernel=dom,
-                kernel_us=dom_ms * 1e3)
+    traffic = load_traffic() if dom == "attn_dense_mfma" else None
+    roof = dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None,
+                traffic=None if traffic is None else round(traffic), kernel=dom, kernel_us=dom_ms * 1e3)
     if dom_bytes:
         a = dom_bytes / (dom_ms * 1e-3) / 1e9
         roof.update(achieved=round(a, 1), frac=round(a / HBM_PEAK_GBS, 4), algorithmic_bytes=dom_bytes)

@@ -402,11 +402,78 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
 }
 
 // Combines per-chunk partials: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per (query, 256 consecutive outputs); the loops over chunks
-// issue independent loads.
+// One workgroup per (query, 64 consecutive outputs of one head); four groups
+// of 64 threads take every fourth split.  Every thread first issues the loads
+// of its (up to kMergeRegs) partial outputs, then the head's (m_s, l_s) pairs
+// go to LDS and become weights w_s = 2^(m_s - M) / sum_t 2^(m_t - M) l_t, so
+// the whole merge costs about one memory round trip; the four groups are
+// added through LDS.  Needs d % 64 == 0 and nsplit <= 4 * kMergeRegs.
+constexpr int kMergeRegs = 16;
+constexpr int kMergeMaxSplit = 4 * kMergeRegs;
+
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float* __restrict__ part_ml, int nsplit, int H, int D,
                                                          float* __restrict__ out, float* __restrict__ lse) {
+  __shared__ float wsh[kMergeMaxSplit];
+  __shared__ float lsh[kMergeMaxSplit];
+  __shared__ float red[4][64];
+  __shared__ float stat[2];
+  const int64_t qrow = blockIdx.y;
+  const int e0 = blockIdx.x * 64;
+  const int h = e0 / D;
+  const int tid = threadIdx.x, lane = tid & 63, sg = tid >> 6;
+  const float* po = part_o + qrow * nsplit * H * D + e0 + lane;
+  const int64_t pos = int64_t(H) * D;
+  float ov[kMergeRegs];
+#pragma unroll
+  for (int i = 0; i < kMergeRegs; ++i) {
+    const int s = sg + 4 * i;
+    ov[i] = s < nsplit ? po[s * pos] : 0.f;
+  }
+  const float* ml = part_ml + (qrow * nsplit * H + h) * 2;
+  const int64_t mls = int64_t(H) * 2;
+  if (tid < nsplit) {
+    const float2 v = *reinterpret_cast<const float2*>(ml + tid * mls);
+    wsh[tid] = v.x;
+    lsh[tid] = v.y;
+  }
+  __syncthreads();
+  if (sg == 0) {
+    float M = lane < nsplit ? wsh[lane] : -INFINITY;
+    M = wave_max(M);
+    float den = 0.f;
+    if (lane < nsplit && wsh[lane] != -INFINITY) den = exp2f(wsh[lane] - M) * lsh[lane];
+    den = wave_sum(den);
+    if (lane == 0) {
+      stat[0] = M;
+      stat[1] = den;
+    }
+  }
+  __syncthreads();
+  const float M = stat[0], den = stat[1];
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  float num = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMergeRegs; ++i) {
+    const int s = sg + 4 * i;
+    if (s < nsplit) {
+      const float ms = wsh[s];
+      num = fmaf(ms == -INFINITY ? 0.f : exp2f(ms - M) * inv, ov[i], num);
+    }
+  }
+  red[sg][lane] = num;
+  __syncthreads();
+  if (sg == 0) {
+    out[qrow * H * D + e0 + lane] = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+    if (lane == 0 && (e0 % D) == 0 && lse) lse[qrow * H + h] = (M + __log2f(den)) * kLn2;
+  }
+}
+
+// Same combination for any head size or split count: one thread per output,
+// each looping over all splits.
+__global__ __launch_bounds__(256) void attn_merge_any_kernel(const float* __restrict__ part_o,
+                                                             const float* __restrict__ part_ml, int nsplit, int H,
+                                                             int D, float* __restrict__ out, float* __restrict__ lse) {
   const int64_t qrow = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= H * D) return;
@@ -456,10 +523,11 @@ static AttnPlan plan_attn(const AttnArgs& a) {
   const int tk = mfma_shape(a) ? 64 : 32;  // keys per tile
   const int64_t rows = a.bt * a.nq;
   const int64_t maxkeys = (a.idx ? int64_t(a.k) : a.n) + a.window;
-  // Aim for about two resident workgroups per compute unit (256 CUs; each
-  // keeps two 32 KiB tiles in flight), never a chunk under 128 keys (a
-  // partial costs h*d*4 bytes per chunk and query).
-  const int64_t target_wg = 1024;
+  // MFMA kernel (two resident workgroups per CU): about 1.4 workgroups per
+  // CU of the 256 balances filling the chip against the h*d*4 bytes that
+  // every extra chunk writes as a partial and the merge reads back.  Never
+  // a chunk under 128 keys.
+  const int64_t target_wg = mfma_shape(a) ? 352 : 1024;
   int64_t chunk = (rows * maxkeys + target_wg - 1) / target_wg;
   chunk = std::max<int64_t>(chunk, 128);
   chunk = (chunk + tk - 1) / tk * tk;
@@ -480,7 +548,7 @@ static void launch_attn_mfma(const AttnArgs& a, const AttnPlan& pl, float* po, f
   const float sl2 = a.scale * kLog2e;
   dim3 grid(unsigned(pl.nsplit), unsigned(a.bt * a.nq));
 #define HATTN_ATTN(D, NH)                                                                                      \
-  hipLaunchKernelGGL((attn_mfma_kernel<D, NH, SPARSE>), grid, dim3(64 * NH), 0, st, (const uint16_t*)a.q,      \
+  HATTN_LAUNCH((attn_mfma_kernel<D, NH, SPARSE>), grid, dim3(64 * NH), 0, st, (const uint16_t*)a.q,      \
                      (const uint16_t*)a.ckv, a.n, a.idx, a.k, a.n_vis, (const uint16_t*)a.raw_kv, a.L, a.q_pos, \
                      a.window, sl2, a.nq, pl.chunk, pl.nsplit, a.out, a.lse, po, pml)
   const int nw = a.h / 16;
@@ -505,7 +573,7 @@ static void launch_attn_valu(const AttnArgs& a, const AttnPlan& pl, float* po, f
   const float sl2 = a.scale * kLog2e;
   dim3 grid(unsigned(pl.nsplit), unsigned(a.bt * a.nq));
   const size_t smem = size_t(a.h) * a.d * 4 + 2 * 32 * size_t(a.d) * 4 + size_t(a.h) * 32 * 4 + 3 * size_t(a.h) * 4;
-  hipLaunchKernelGGL((attn_valu_kernel<T, SPARSE>), grid, dim3(256), smem, st, (const T*)a.q, (const T*)a.ckv, a.n,
+  HATTN_LAUNCH((attn_valu_kernel<T, SPARSE>), grid, dim3(256), smem, st, (const T*)a.q, (const T*)a.ckv, a.n,
                      a.idx, a.k, a.n_vis, (const T*)a.raw_kv, a.L, a.q_pos, a.window, sl2, a.nq, a.h, a.d, pl.chunk,
                      pl.nsplit, a.out, a.lse, po, pml);
 }
@@ -537,8 +605,12 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   LaunchScope ls("attn_merge", st);
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256), 0,
-                     st, po, pml, pl.nsplit, a.h, a.d, a.out, a.lse);
+  if (a.d % 64 == 0 && pl.nsplit <= kMergeMaxSplit)
+    HATTN_LAUNCH(attn_merge_kernel, dim3(unsigned(a.h * a.d / 64), unsigned(a.bt * a.nq)), dim3(256), 0, st, po, pml,
+                 pl.nsplit, a.h, a.d, a.out, a.lse);
+  else
+    HATTN_LAUNCH(attn_merge_any_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256), 0,
+                 st, po, pml, pl.nsplit, a.h, a.d, a.out, a.lse);
   return hipGetLastError();
 }
 

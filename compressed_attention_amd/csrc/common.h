@@ -67,6 +67,13 @@ HATTN_DEV T wave_max(T v) {
   return v;
 }
 
+template <typename T>
+HATTN_DEV T wave_min(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  return v;
+}
+
 HATTN_DEV int lane_id() { return __lane_id(); }
 
 // Number of lanes below this one whose bit is set in mask.

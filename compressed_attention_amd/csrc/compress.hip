@@ -271,7 +271,7 @@ static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C,
     const int64_t runs = (ne + run - 1) / run;
     const int64_t total = bt * runs * slots;
     LaunchScope ls("compress_overlap2", st);
-    hipLaunchKernelGGL((compress_overlap2_kernel<T, 4>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+    HATTN_LAUNCH((compress_overlap2_kernel<T, 4>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
                        (const T*)x, z, bias, (T*)y, L, C, N, e0, e1, runs, run, total);
     return hipGetLastError();
   }
@@ -279,7 +279,7 @@ static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C,
     const int RG = 256 / slots;
     const size_t smem = (size_t(w) + size_t(RG) * C) * 4;
     LaunchScope ls("compress_window", st);
-    hipLaunchKernelGGL((compress_window_kernel<T>), dim3(unsigned(bt * ne)), dim3(256), smem, st, (const T*)x, z, bias,
+    HATTN_LAUNCH((compress_window_kernel<T>), dim3(unsigned(bt * ne)), dim3(256), smem, st, (const T*)x, z, bias,
                        (T*)y, L, C, w, s, N, e0, ne);
     return hipGetLastError();
   }
@@ -287,7 +287,7 @@ static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C,
   const int64_t runs = ne;
   const int64_t total = bt * runs * slots;
   LaunchScope ls("compress", st);
-  hipLaunchKernelGGL((compress_generic_kernel<T>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+  HATTN_LAUNCH((compress_generic_kernel<T>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
                      (const T*)x, z, bias, (T*)y, L, C, w, s, N, e0, runs, run, total);
   return hipGetLastError();
 }
@@ -316,7 +316,7 @@ hipError_t launch_visible_count(const int32_t* pos, int64_t count, int w, int s,
                                 hipStream_t st) {
   if (count <= 0) return hipSuccess;
   LaunchScope ls("visible_count", st);
-  hipLaunchKernelGGL(visible_count_kernel, dim3(unsigned((count + 255) / 256)), dim3(256), 0, st, pos, count, w, s,
+  HATTN_LAUNCH(visible_count_kernel, dim3(unsigned((count + 255) / 256)), dim3(256), 0, st, pos, count, w, s,
                      n_entries, n_vis);
   return hipGetLastError();
 }
@@ -385,10 +385,10 @@ hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_
   const int RG = 256 / (d_i / V);
   const size_t smem = size_t(RG) * d_i * 4;
   if (dtype == 0) {
-    hipLaunchKernelGGL(pool_kernel<float>, dim3(unsigned(bt * nj)), dim3(256), smem, st, (const float*)k_i, n, d_i, B,
+    HATTN_LAUNCH(pool_kernel<float>, dim3(unsigned(bt * nj)), dim3(256), smem, st, (const float*)k_i, n, d_i, B,
                        nb, j0, nj, reps);
   } else {
-    hipLaunchKernelGGL(pool_kernel<uint16_t>, dim3(unsigned(bt * nj)), dim3(256), smem, st, (const uint16_t*)k_i, n,
+    HATTN_LAUNCH(pool_kernel<uint16_t>, dim3(unsigned(bt * nj)), dim3(256), smem, st, (const uint16_t*)k_i, n,
                        d_i, B, nb, j0, nj, reps);
   }
   return hipGetLastError();

@@ -90,21 +90,33 @@ hipEvent_t take_event() {
 
 namespace hattn {
 
-LaunchScope::LaunchScope(const char* name, hipStream_t s) : name_(name), stream_(s), ev0_(nullptr) {
+thread_local LaunchScope* t_scope = nullptr;
+
+LaunchScope::LaunchScope(const char* name, hipStream_t s)
+    : name_(name), stream_(s), ev0_(nullptr), ev1_(nullptr), used_(false), outer_(t_scope) {
+  t_scope = this;
   if (!g_timer_on) return;
-  hipEvent_t e = take_event();
-  if (e && hipEventRecord(e, s) == hipSuccess) ev0_ = e;
+  ev0_ = take_event();
+  ev1_ = take_event();
 }
 
 LaunchScope::~LaunchScope() {
-  if (!ev0_) return;
-  hipEvent_t e1 = take_event();
-  if (e1 && hipEventRecord(e1, stream_) == hipSuccess) {
-    g_pending.push_back({name_, (hipEvent_t)ev0_, e1});
+  t_scope = outer_;
+  if (used_ && ev0_ && ev1_) {
+    g_pending.push_back({name_, ev0_, ev1_});
   } else {
-    g_free.push_back((hipEvent_t)ev0_);
-    if (e1) g_free.push_back(e1);
+    if (ev0_) g_free.push_back(ev0_);
+    if (ev1_) g_free.push_back(ev1_);
   }
+}
+
+bool timer_events(hipEvent_t* e0, hipEvent_t* e1) {
+  LaunchScope* sc = t_scope;
+  if (!sc || sc->used_ || !sc->ev0_ || !sc->ev1_) return false;
+  sc->used_ = true;
+  *e0 = sc->ev0_;
+  *e1 = sc->ev1_;
+  return true;
 }
 
 }  // namespace hattn

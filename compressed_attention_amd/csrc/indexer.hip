@@ -387,24 +387,28 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
                                                              const int32_t* __restrict__ blk, int64_t n, int B, int m,
                                                              int k, int32_t* __restrict__ idx,
                                                              float* __restrict__ score_out) {
-  extern __shared__ uint32_t keys[];
   __shared__ SelectShared<kSelNT> sh;
   __shared__ int cnt;
+  __shared__ int32_t bsh[MODE == 2 ? kSelNT : 1];  // chosen block ids, for the emission
   const int64_t row = blockIdx.x;
   if (threadIdx.x == 0) cnt = 0;
+  const int32_t* brow = blk + row * m;
+  if (MODE == 2 && m <= kSelNT)
+    for (int s = threadIdx.x; s < m; s += kSelNT) bsh[s] = brow[s];
   __syncthreads();
   const int nvalid = min(kSelCap, row_valid_count<MODE>(n_vis, blk, row, n, B, m, &cnt));
-  load_score_keys<kSelNT>(S + row * ld, nvalid, keys);
-  __syncthreads();
-  radix_threshold<kSelNT>(keys, nvalid, k, sh);
+  const SelSeg sg = wave_segment<kSelNT>(nvalid);
+  uint32_t kc[kSelIT];
+  seg_keys_from_scores(S + row * ld, sg, kc);
+  radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
   int32_t* orow = idx + row * k;
   float* scrow = score_out ? score_out + row * k : nullptr;
-  const int32_t* brow = blk + row * m;
-  const int chosen = emit_selected<kSelNT>(keys, nvalid, sh, [&](int slot, int i) {
+  const bool blk_lds = m <= kSelNT;
+  const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int i, uint32_t key, int) {
     int32_t v = i;
-    if (MODE == 2) v = brow[i / B] * B + (i % B);
+    if (MODE == 2) v = (blk_lds ? bsh[i / B] : brow[i / B]) * B + (i % B);
     orow[slot] = v;
-    if (scrow) scrow[slot] = key_to_float(keys[i]);
+    if (scrow) scrow[slot] = key_to_float(key);
   });
   for (int s = chosen + threadIdx.x; s < k; s += kSelNT) {
     orow[s] = -1;
@@ -448,13 +452,14 @@ __global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __r
   int32_t* orow = idx + row * k;
   float* scrow = score_out ? score_out + row * k : nullptr;
 
-  if (nv <= kSelCap) {  // short row: plain LDS selection over all of it
-    load_score_keys<kSelNT>(srow, nv, dyn);
-    __syncthreads();
-    radix_threshold<kSelNT>(dyn, nv, k, sh);
-    const int chosen = emit_selected<kSelNT>(dyn, nv, sh, [&](int slot, int i) {
+  if (nv <= kSelCap) {  // short row: plain selection over all of it
+    const SelSeg sg = wave_segment<kSelNT>(nv);
+    uint32_t kc[kSelIT];
+    seg_keys_from_scores(srow, sg, kc);
+    radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
+    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int i, uint32_t key, int) {
       orow[slot] = i;
-      if (scrow) scrow[slot] = key_to_float(dyn[i]);
+      if (scrow) scrow[slot] = key_to_float(key);
     });
     for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
       orow[t] = -1;
@@ -469,12 +474,15 @@ __global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __r
     for (int c = 0; c < 16; ++c) load_score_keys<kSelNT>(srow + c * stride, 512, samp + c * 512);
   }
   __syncthreads();
+  const SelSeg ssg = wave_segment<kSelNT>(kSampleN);
+  uint32_t skc[kSelIT];
+  seg_keys_from_u32(samp, ssg, skc);
   int r = min(kSampleN, int((3LL * k * kSampleN) / (2LL * nv)) + 32);
   const int segw = ((nv + NW - 1) / NW + 255) & ~255;
   const int p0 = wave * segw, p1 = min(nv, p0 + segw);
   bool done = false;
   for (int attempt = 0; attempt < 4 && !done; ++attempt) {
-    radix_threshold<kSelNT>(samp, kSampleN, r, sh);
+    radix_threshold<kSelNT, kSelIT>(skc, ssg.iters, r, sh);
     const uint32_t tau = sh.thr;  // key of the r-th largest sample (0: all)
     // 2. collect keys >= tau of this wave's segment, in position order
     uint32_t* rk = rkey + wave * kRegion;
@@ -548,11 +556,15 @@ __global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __r
     if (threadIdx.x == 0) flags[row] = 1;  // finished by the segment + merge kernels
     return;
   }
-  // 3. exact selection over the candidates (key 0 = empty slot)
-  radix_threshold<kSelNT>(rkey, kSampleN, k, sh);
-  const int chosen = emit_selected<kSelNT>(rkey, kSampleN, sh, [&](int slot, int i) {
+  // 3. exact selection over the candidates (key 0 = empty slot); the wave
+  // segments of kSampleN keys are exactly the waves' regions
+  const SelSeg csg = wave_segment<kSelNT>(kSampleN);
+  uint32_t ckc[kSelIT];
+  seg_keys_from_u32(rkey, csg, ckc);
+  radix_threshold<kSelNT, kSelIT>(ckc, csg.iters, k, sh);
+  const int chosen = emit_selected<kSelNT, kSelIT>(ckc, csg, sh, [&](int slot, int i, uint32_t key, int) {
     orow[slot] = rpos[i];
-    if (scrow) scrow[slot] = key_to_float(rkey[i]);
+    if (scrow) scrow[slot] = key_to_float(key);
   });
   for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
     orow[t] = -1;
@@ -569,7 +581,6 @@ __global__ __launch_bounds__(kSelNT) void select_segment_kernel(const float* __r
                                                                 int nseg, int k, int kp, uint32_t* __restrict__ ckey,
                                                                 int32_t* __restrict__ cpos,
                                                                 const int32_t* __restrict__ flags) {
-  extern __shared__ uint32_t keys[];
   __shared__ SelectShared<kSelNT> sh;
   const int64_t row = blockIdx.y;
   if (flags[row] == 0) return;  // already selected by select_sampled_kernel
@@ -577,13 +588,14 @@ __global__ __launch_bounds__(kSelNT) void select_segment_kernel(const float* __r
   const int64_t nv = imin64(n, imax64(0, n_vis[row]));
   const int64_t p0 = int64_t(s) * seg;
   const int cnt = int(imax64(0, imin64(seg, nv - p0)));
-  load_score_keys<kSelNT>(S + row * ld + p0, cnt, keys);
-  __syncthreads();
-  radix_threshold<kSelNT>(keys, cnt, k, sh);
+  const SelSeg sg = wave_segment<kSelNT>(cnt);
+  uint32_t kc[kSelIT];
+  seg_keys_from_scores(S + row * ld + p0, sg, kc);
+  radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
   uint32_t* ok = ckey + (row * nseg + s) * int64_t(kp);
   int32_t* op = cpos + (row * nseg + s) * int64_t(kp);
-  const int chosen = emit_selected<kSelNT>(keys, cnt, sh, [&](int slot, int i) {
-    ok[slot] = keys[i];
+  const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int i, uint32_t key, int) {
+    ok[slot] = key;
     op[slot] = int32_t(p0 + i);
   });
   for (int t = chosen + threadIdx.x; t < kp; t += kSelNT) {
@@ -600,9 +612,7 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
                                                               int32_t* __restrict__ opos,
                                                               int32_t* __restrict__ idx, float* __restrict__ score_out,
                                                               const int32_t* __restrict__ flags) {
-  extern __shared__ uint32_t keys[];
   __shared__ SelectShared<kSelNT> sh;
-  int32_t* pos = reinterpret_cast<int32_t*>(keys + kSelCap);
   const int64_t row = blockIdx.y;
   if (flags[row] == 0) return;  // already selected by select_sampled_kernel
   const int grp = blockIdx.x;
@@ -611,15 +621,26 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
   const int cnt = (l1 - l0) * kp;
   const uint32_t* ik = ikey + (row * nin + l0) * int64_t(kp);
   const int32_t* ip = ipos + (row * nin + l0) * int64_t(kp);
-  load_candidates<kSelNT>(ik, ip, cnt, keys, pos);
-  __syncthreads();
-  radix_threshold<kSelNT>(keys, cnt, k, sh);
+  const SelSeg sg = wave_segment<kSelNT>(cnt);
+  uint32_t kc[kSelIT];
+  int32_t pc[kSelIT];
+  {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int it = 0; it < kSelIT; ++it) {
+      const int i = sg.p0 + it * kWave + lane;
+      const bool in = it < sg.iters && i < sg.p1;
+      kc[it] = in ? ik[i] : 0u;
+      pc[it] = in ? ip[i] : -1;
+    }
+  }
+  radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
   if (nout == 1) {
     int32_t* orow = idx + row * k;
     float* scrow = score_out ? score_out + row * k : nullptr;
-    const int chosen = emit_selected<kSelNT>(keys, cnt, sh, [&](int slot, int i) {
-      orow[slot] = pos[i];
-      if (scrow) scrow[slot] = key_to_float(keys[i]);
+    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int, uint32_t key, int it) {
+      orow[slot] = pc[it];
+      if (scrow) scrow[slot] = key_to_float(key);
     });
     for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
       orow[t] = -1;
@@ -628,9 +649,9 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
   } else {
     uint32_t* ok = okey + (row * nout + grp) * int64_t(kp);
     int32_t* op = opos + (row * nout + grp) * int64_t(kp);
-    const int chosen = emit_selected<kSelNT>(keys, cnt, sh, [&](int slot, int i) {
-      ok[slot] = keys[i];
-      op[slot] = pos[i];
+    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int, uint32_t key, int it) {
+      ok[slot] = key;
+      op[slot] = pc[it];
     });
     for (int t = chosen + threadIdx.x; t < kp; t += kSelNT) {
       ok[t] = 0u;
@@ -683,11 +704,6 @@ static void set_lds_limits() {
   static bool done = false;
   if (done) return;
   done = true;
-  (void)hipFuncSetAttribute((const void*)select_rows_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
-  (void)hipFuncSetAttribute((const void*)select_rows_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
-  (void)hipFuncSetAttribute((const void*)select_rows_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
-  (void)hipFuncSetAttribute((const void*)select_segment_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 4);
-  (void)hipFuncSetAttribute((const void*)select_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kSelCap * 8);
   (void)hipFuncSetAttribute((const void*)select_sampled_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             kSampleN * 12);
 }
@@ -698,7 +714,7 @@ static void launch_valu_score(const IndexArgs& a, const TK* keys, int64_t keys_p
   const size_t smem = size_t(a.h_i) * a.d_i * 4 + size_t(a.h_i) * 4;
   dim3 grid(unsigned((ncand + 255) / 256), unsigned(a.bt * a.nq));
   LaunchScope ls(MODE == 0 ? "score_valu_flat" : MODE == 1 ? "score_valu_stage1" : "score_valu_stage2", st);
-  hipLaunchKernelGGL((score_valu_kernel<TQ, TK, MODE>), grid, dim3(256), smem, st, (const TQ*)a.q_i, keys, a.w_i,
+  HATTN_LAUNCH((score_valu_kernel<TQ, TK, MODE>), grid, dim3(256), smem, st, (const TQ*)a.q_i, keys, a.w_i,
                      a.n_vis, blk, a.nq, a.h_i, a.d_i, a.n, keys_per_seq, B, m, ld, S);
 }
 
@@ -710,7 +726,7 @@ static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, hi
     dim3 grid(xcd_grid(nqb, nch), unsigned(a.bt));
     LaunchScope ls("score_flat_mfma", st);
 #define HATTN_FLAT(KS)                                                                                       \
-  hipLaunchKernelGGL(score_flat_mfma_kernel<KS>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i,             \
+  HATTN_LAUNCH(score_flat_mfma_kernel<KS>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i,             \
                      (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk)
     switch (a.d_i) {
       case 32: HATTN_FLAT(1); break;
@@ -735,7 +751,7 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
   if (e != hipSuccess) return e;
   if (!p.multi) {
     LaunchScope ls("select_rows", st);
-    hipLaunchKernelGGL(select_rows_kernel<0>, dim3(unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st, S, p.ld, a.n_vis,
+    HATTN_LAUNCH(select_rows_kernel<0>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S, p.ld, a.n_vis,
                        nullptr, a.n, 1, 1, k, idx, score);
     return hipGetLastError();
   }
@@ -751,14 +767,14 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
   int32_t* flags = reinterpret_cast<int32_t*>(cb + p.cand_bytes);
   {
     LaunchScope ls("select_sampled", st);
-    hipLaunchKernelGGL(select_sampled_kernel, dim3(unsigned(p.rows)), dim3(kSelNT), kSampleN * 12, st, S, p.ld,
+    HATTN_LAUNCH(select_sampled_kernel, dim3(unsigned(p.rows)), dim3(kSelNT), kSampleN * 12, st, S, p.ld,
                        a.n_vis, a.n, k, idx, score, flags);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     LaunchScope ls("select_segment", st);
-    hipLaunchKernelGGL(select_segment_kernel, dim3(unsigned(p.nseg), unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st,
+    HATTN_LAUNCH(select_segment_kernel, dim3(unsigned(p.nseg), unsigned(p.rows)), dim3(kSelNT), 0, st,
                        S, p.ld, a.n_vis, a.n, p.seg, p.nseg, k, p.kp, bufk[0], bufp[0], flags);
   }
   int nin = p.nseg, cur = 0;
@@ -767,7 +783,7 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
     LaunchScope ls("select_merge", st);
     // Lists of a row at level i+1 never outnumber those at level i, so the
     // two buffers (sized for levels 1 and 2) alternate safely.
-    hipLaunchKernelGGL(select_merge_kernel, dim3(unsigned(nout), unsigned(p.rows)), dim3(kSelNT), kSelCap * 8, st,
+    HATTN_LAUNCH(select_merge_kernel, dim3(unsigned(nout), unsigned(p.rows)), dim3(kSelNT), 0, st,
                        bufk[cur], bufp[cur], nin, p.G, k, p.kp, bufk[cur ^ 1], bufp[cur ^ 1], idx, score, flags);
     e = hipGetLastError();
     if (e != hipSuccess || nout == 1) return e;
@@ -821,10 +837,10 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     LaunchScope ls("score_stage1_mfma", st);
 #define HATTN_S1(T, KQ)                                                                                      \
   if (qpw == 4)                                                                                              \
-    hipLaunchKernelGGL((score_stage1_kernel<T, KQ, 4>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
+    HATTN_LAUNCH((score_stage1_kernel<T, KQ, 4>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
                        a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk);                            \
   else                                                                                                       \
-    hipLaunchKernelGGL((score_stage1_kernel<T, KQ, 1>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
+    HATTN_LAUNCH((score_stage1_kernel<T, KQ, 1>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
                        a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk)
     if (a.dtype == 0) {
       switch (a.d_i / 16) {
@@ -853,7 +869,7 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   if (e != hipSuccess) return e;
   {
     LaunchScope ls("select_blocks", st);
-    hipLaunchKernelGGL(select_rows_kernel<1>, dim3(unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st, S1, p.ld1,
+    HATTN_LAUNCH(select_rows_kernel<1>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S1, p.ld1,
                        a.n_vis, nullptr, a.n, B, m, m, blk_out, nullptr);
   }
   e = hipGetLastError();
@@ -866,7 +882,7 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     dim3 grid(unsigned(m), unsigned(p.rows));
     LaunchScope ls("score_stage2_mfma", st);
 #define HATTN_S2(KS)                                                                                         \
-  hipLaunchKernelGGL(score_stage2_mfma_kernel<KS>, grid, dim3(64), 0, st, (const uint16_t*)a.q_i,           \
+  HATTN_LAUNCH(score_stage2_mfma_kernel<KS>, grid, dim3(64), 0, st, (const uint16_t*)a.q_i,           \
                      (const uint16_t*)a.k_i, a.w_i, a.n_vis, blk_out, a.nq, a.n, B, m, p.ld2, S2)
     switch (a.d_i) {
       case 32: HATTN_S2(1); break;
@@ -884,7 +900,7 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   if (e != hipSuccess) return e;
   {
     LaunchScope ls("select_tokens", st);
-    hipLaunchKernelGGL(select_rows_kernel<2>, dim3(unsigned(p.rows)), dim3(kSelNT), kSelCap * 4, st, S2, p.ld2,
+    HATTN_LAUNCH(select_rows_kernel<2>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
                        a.n_vis, blk_out, a.n, B, m, k, idx, nullptr);
   }
   return hipGetLastError();

@@ -1,20 +1,40 @@
 // Internal host-side interface between the C ABI (hattn.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace hattn {
 
-// Brackets one kernel launch with timer events when the kernel timer is on.
+// Names the kernel launched inside its lifetime.  When the kernel timer is
+// on, the scope owns a start/stop event pair that HATTN_LAUNCH hands to
+// hipExtLaunchKernelGGL, so the events carry the dispatch's own start and end
+// times (no marker packets around the kernel); the destructor queues the pair
+// for hattn_timer_collect().  One timed launch per scope.
 struct LaunchScope {
   LaunchScope(const char* name, hipStream_t s);
   ~LaunchScope();
   const char* name_;
   hipStream_t stream_;
-  void* ev0_;
+  hipEvent_t ev0_, ev1_;
+  bool used_;
+  LaunchScope* outer_;
 };
+
+// Events of the innermost live scope if the timer is on and the scope has
+// not timed a launch yet (then the scope counts as used); false otherwise.
+bool timer_events(hipEvent_t* e0, hipEvent_t* e1);
+
+#define HATTN_LAUNCH(kernel, grid, block, shm, st, ...)                                             \
+  do {                                                                                               \
+    hipEvent_t hattn_e0_, hattn_e1_;                                                                 \
+    if (::hattn::timer_events(&hattn_e0_, &hattn_e1_))                                               \
+      hipExtLaunchKernelGGL(kernel, grid, block, shm, st, hattn_e0_, hattn_e1_, 0u, __VA_ARGS__);    \
+    else                                                                                             \
+      hipLaunchKernelGGL(kernel, grid, block, shm, st, __VA_ARGS__);                                 \
+  } while (0)
 
 // ---- compression / geometry / pooling -------------------------------------
 hipError_t launch_compress(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z,
