@@ -76,6 +76,31 @@ HATTN_DEV T wave_min(T v) {
 
 HATTN_DEV int lane_id() { return __lane_id(); }
 
+// max(x, 0) as one integer max: every negative float and -0.0 compares below
+// +0.0 as a signed integer.  (fmaxf would first canonicalise x, an extra
+// instruction per element.)
+HATTN_DEV float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Lane groups g = lane / 16 of a wave.  sum4_transpose: every lane holds
+// four partial sums v0..v3; group g receives the sum of value g over the
+// four groups (at the same position inside the group).  Three lane-swap
+// VALU ops (gfx950 v_permlane32_swap / v_permlane16_swap), no LDS traffic.
+HATTN_DEV float sum4_transpose(float v0, float v1, float v2, float v3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+  const float A = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows 0,1: v0 pairs; rows 2,3: v2 pairs
+  const float B = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // rows 0,1: v1 pairs; rows 2,3: v3 pairs
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(A), __float_as_uint(B), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+// Sum of v over the four lane groups, in every lane.
+HATTN_DEV float sum_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float A = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(A), __float_as_uint(A), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Number of lanes below this one whose bit is set in mask.
 HATTN_DEV int mbcnt(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));

@@ -45,8 +45,8 @@ static unsigned xcd_grid(int ngroups, int nchunks) { return unsigned(ngroups * (
 // ---------------------------------------------------------------------------
 // Flat score, bf16, 16 heads, d_i = 32*KS.
 // ---------------------------------------------------------------------------
-template <int KS>
-__global__ __launch_bounds__(256, 2) void score_flat_mfma_kernel(const uint16_t* __restrict__ q_i,
+template <int KS, int NWQ>
+__global__ __launch_bounds__(64 * NWQ, KS >= 8 ? 1 : 8 / NWQ) void score_flat_mfma_kernel(const uint16_t* __restrict__ q_i,
                                                                  const uint16_t* __restrict__ k_i,
                                                                  const float* __restrict__ w_i,
                                                                  const int32_t* __restrict__ n_vis, int64_t nq,
@@ -55,17 +55,20 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma_kernel(const uint16_t*
   constexpr int D = 32 * KS;
   constexpr int TN = 64;
   constexpr int PITCH = D + 8;
-  constexpr int PIECES = TN * D / 8 / 256;  // 16-byte pieces per thread per tile
+  constexpr int NT = 64 * NWQ;
+  constexpr int QB = 4 * NWQ;                // queries per workgroup (4 per wave)
+  constexpr int PIECES = TN * D / 8 / NT;    // 16-byte pieces per thread per tile
+  static_assert(TN * D / 8 % NT == 0, "tile split");
   __shared__ __align__(16) uint16_t kt[2][TN * PITCH];
-  __shared__ int s_nv[16];
+  __shared__ int s_nv[QB];
 
   int qb, ch;
   if (!xcd_decode(blockIdx.x, nqb, nch, &qb, &ch)) return;
   const int64_t b = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int64_t q0 = int64_t(qb) * 16;
-  if (threadIdx.x < 16) {
+  const int64_t q0 = int64_t(qb) * QB;
+  if (threadIdx.x < QB) {
     const int64_t q = q0 + threadIdx.x;
     int v = 0;
     if (q < nq) v = int(imin64(n, imax64(0, n_vis[b * nq + q])));
@@ -74,14 +77,13 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma_kernel(const uint16_t*
   __syncthreads();
   int maxv = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) maxv = max(maxv, s_nv[i]);
+  for (int i = 0; i < QB; ++i) maxv = max(maxv, s_nv[i]);
   const int64_t e_begin = int64_t(ch) * chunk;
   const int64_t e_end = imin64(e_begin + chunk, maxv);
   if (e_begin >= e_end) return;
 
   u32x4_t a[4][KS];
   float wv[4][4];
-  int nv[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int64_t q = q0 + 4 * wave + mt;
@@ -91,31 +93,40 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma_kernel(const uint16_t*
     for (int ks = 0; ks < KS; ++ks) a[mt][ks] = ok ? ld16(qp + 32 * ks) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[mt][i] = ok ? w_i[(b * nq + q) * 16 + 4 * g + i] : 0.f;
-    nv[mt] = s_nv[4 * wave + mt];
   }
+  // Lane group g stores the scores of query 4*wave + g: its visible count
+  // (0 for a query beyond nq) and row pointer, fixed for the whole chunk.
+  const int64_t my_q = q0 + 4 * wave + g;
+  const int my_nv = my_q < nq ? s_nv[4 * wave + g] : 0;
+  float* srow = S + (b * nq + (my_q < nq ? my_q : 0)) * ld;
 
+  // Keys: 32-bit row indices (n < 2^31 is checked on the host).  Rows past
+  // the end of the cache are read clamped to the last row; their scores are
+  // never stored (every stored key is below n_vis <= n).
   const uint16_t* kb = k_i + b * n * D;
+  const int n32 = int(n);
   u32x4_t pre[PIECES];
-  auto load = [&](int64_t e0) {
+  auto load = [&](int e0) {
 #pragma unroll
     for (int j = 0; j < PIECES; ++j) {
-      const int p = threadIdx.x + 256 * j;
+      const int p = threadIdx.x + NT * j;
       const int row = p / (D / 8), col = p % (D / 8);
-      const int64_t e = e0 + row;
-      pre[j] = e < n ? ld16(kb + e * D + col * 8) : u32x4_t{0, 0, 0, 0};
+      const int e = min(e0 + row, n32 - 1);
+      pre[j] = ld16(kb + size_t(e) * D + col * 8);
     }
   };
-  load(e_begin);
+  const int eb = int(e_begin), ee = int(e_end);
+  load(eb);
   int buf = 0;
-  for (int64_t e0 = e_begin; e0 < e_end; e0 += TN, buf ^= 1) {
+  for (int e0 = eb; e0 < ee; e0 += TN, buf ^= 1) {
 #pragma unroll
     for (int j = 0; j < PIECES; ++j) {
-      const int p = threadIdx.x + 256 * j;
+      const int p = threadIdx.x + NT * j;
       const int row = p / (D / 8), col = p % (D / 8);
       *reinterpret_cast<u32x4_t*>(&kt[buf][row * PITCH + col * 8]) = pre[j];
     }
     __syncthreads();
-    if (e0 + TN < e_end) load(e0 + TN);
+    if (e0 + TN < ee) load(e0 + TN);
     f32x4_t acc[4][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
@@ -139,17 +150,13 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma_kernel(const uint16_t*
       for (int mt = 0; mt < 4; ++mt) {
         float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s = fmaf(wv[mt][i], fmaxf(acc[mt][nt][i], 0.f), s);
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        v[mt] = s;
+        for (int i = 0; i < 4; ++i) s = fmaf(wv[mt][i], relu_bits(acc[mt][nt][i]), s);
+        v[mt] = s;  // this lane group's 4 heads
       }
-      // lane group g stores the row of query 4*wave + g
-      const float mine = g == 0 ? v[0] : g == 1 ? v[1] : g == 2 ? v[2] : v[3];
-      const int64_t e = e0 + 16 * nt + r16;
-      const int64_t q = q0 + 4 * wave + g;
-      const int nvg = g == 0 ? nv[0] : g == 1 ? nv[1] : g == 2 ? nv[2] : nv[3];
-      if (q < nq && e < nvg) S[(b * nq + q) * ld + e] = mine;
+      // lane group g receives (and stores) the row of query 4*wave + g
+      const float mine = sum4_transpose(v[0], v[1], v[2], v[3]);
+      const int e = e0 + 16 * nt + r16;
+      if (e < my_nv) srow[e] = mine;
     }
   }
 }
@@ -244,15 +251,26 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
         for (int j = 0; j < 4; ++j) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kq][j], bv[j], acc[t], 0, 0, 0);
       }
     }
+    float hs[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(wv[i], fmaxf(acc[t][i], 0.f), s);
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      const int64_t j = j0 + 16 * (nt0 + t) + r16;
-      if (g == 0 && j < my_nb) S1[(b * nq + q) * ld + j] = s;
+      for (int i = 0; i < 4; ++i) s = fmaf(wv[i], relu_bits(acc[t][i]), s);
+      hs[t] = s;  // this lane group's 4 heads
+    }
+    if constexpr (NTW == 4) {
+      // lane group g receives (and stores) subtile nt0 + g
+      const float s = sum4_transpose(hs[0], hs[1], hs[2], hs[3]);
+      const int64_t j = j0 + 16 * (nt0 + g) + r16;
+      if (j < my_nb) S1[(b * nq + q) * ld + j] = s;
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const float s = sum_groups(hs[t]);
+        const int64_t j = j0 + 16 * (nt0 + t) + r16;
+        if (g == 0 && j < my_nb) S1[(b * nq + q) * ld + j] = s;
+      }
     }
   }
 }
@@ -298,6 +316,7 @@ __global__ __launch_bounds__(64) void score_stage2_mfma_kernel(const uint16_t* _
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) bf[nt][ks] = ok ? ld16(kb + e * D + 32 * ks) : u32x4_t{0, 0, 0, 0};
     }
+    float v[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -305,11 +324,14 @@ __global__ __launch_bounds__(64) void score_stage2_mfma_kernel(const uint16_t* _
       for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ks], bf[nt][ks], acc);
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s = fmaf(wv[i], fmaxf(acc[i], 0.f), s);
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      const int64_t e = e0 + 16 * nt + r16;
-      if (g == 0 && e < e_end) out[e - e_begin] = s;
+      for (int i = 0; i < 4; ++i) s = fmaf(wv[i], relu_bits(acc[i]), s);
+      v[nt] = s;  // this lane group's 4 heads
+    }
+    {
+      // lane group g receives (and stores) key tile g
+      const float s = sum4_transpose(v[0], v[1], v[2], v[3]);
+      const int64_t e = e0 + 16 * g + r16;
+      if (e < e_end) out[e - e_begin] = s;
     }
   }
 }
@@ -667,7 +689,8 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static int64_t round4(int64_t x) { return (x + 3) & ~int64_t(3); }
 
 static bool flat_mfma_ok(const IndexArgs& a) {
-  return a.dtype == 1 && a.h_i == 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128 || a.d_i == 256);
+  return a.dtype == 1 && a.h_i == 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128 || a.d_i == 256) &&
+         a.n < (int64_t(1) << 31);
 }
 
 struct FlatPlan {
@@ -720,14 +743,16 @@ static void launch_valu_score(const IndexArgs& a, const TK* keys, int64_t keys_p
 
 static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, hipStream_t st) {
   if (flat_mfma_ok(a)) {
+    // 16 queries per workgroup.  (32, with 8 waves sharing each key tile,
+    // measured slower: one resident workgroup per CU and longer barriers.)
     const int nqb = int((a.nq + 15) / 16);
     const int chunk = 2048;
     const int nch = int((a.n + chunk - 1) / chunk);
     dim3 grid(xcd_grid(nqb, nch), unsigned(a.bt));
     LaunchScope ls("score_flat_mfma", st);
 #define HATTN_FLAT(KS)                                                                                       \
-  HATTN_LAUNCH(score_flat_mfma_kernel<KS>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i,             \
-                     (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk)
+  HATTN_LAUNCH((score_flat_mfma_kernel<KS, 4>), grid, dim3(256), 0, st, (const uint16_t*)a.q_i,             \
+               (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk)
     switch (a.d_i) {
       case 32: HATTN_FLAT(1); break;
       case 64: HATTN_FLAT(2); break;
