@@ -20,8 +20,9 @@ cache.  Inputs are seeded synthetic tensors drawn on the device.
 
 Per-kernel durations come from the library's event timer (events recorded on
 the launch stream around every kernel) over a second, eager pass of the same
-steps.  Extras: HCA dense decode at batch 32, the 128K indexer chunk (flat
-and HISA), compression of 1M-token sequences.  The CPU baseline is the fp64
+steps.  Extras: HCA dense decode at batch 32, the CSA prefill chunk (1,024
+queries of a 32K sequence), the 128K indexer chunk (flat and HISA),
+compression of 1M-token sequences.  The CPU baseline is the fp64
 oracle on a bounded sample of the same decode step.
 """
 from __future__ import annotations
@@ -146,12 +147,20 @@ def hybrid_pair(args):
     torch.cuda.synchronize()
     log(f"[bench] hybrid pair inputs + {R} cache replicas ready in {time.time() - t0:.1f}s")
 
-    def csa_step(c):
+    def csa_compress(c):
         ops.compress(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, N - 1, N, out=c["ckv"])
+
+    def csa_select(c):
         ops.hisa_pool(c["k_i"], B, nb - 1, nb, out=c["reps"])
         nv = ops.visible_count(t["q_pos"], 8, 4, N)
-        idx = ops.hisa_topk(t["q_i"], c["k_i"], t["w_i"], nv, c["reps"], B, m, k)
+        return ops.hisa_topk(t["q_i"], c["k_i"], t["w_i"], nv, c["reps"], B, m, k)
+
+    def csa_attend(c, idx):
         return ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128)
+
+    def csa_step(c):
+        csa_compress(c)
+        return csa_attend(c, csa_select(c))
 
     def hca_step(c):
         ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, Nh - 1, Nh, out=c["hkv"])
@@ -163,7 +172,9 @@ def hybrid_pair(args):
 
     # The two layers' inputs are independent: each is captured as its own
     # graph and the pair is replayed on two streams (default priority both)
-    # that join at the end of every step.
+    # that join at the end of every step.  (Splitting the CSA layer further,
+    # so that its tail compression runs beside its selection, measured
+    # slower: every extra dependent graph launch costs more than it hides.)
     side = torch.cuda.Stream()
     g_csa = capture(csa_step, caches, stream=torch.cuda.Stream())
     g_hca = capture(hca_step, caches, stream=torch.cuda.Stream())
@@ -240,6 +251,39 @@ def hca_decode_b32(args):
     byt = bt * attn_bytes(Nh + 128)
     del graphs
     return dict(ms=ms, kernels=kt, step_bytes=byt, compress_ms=comp_ms, compress_bytes=comp_bytes, bt=bt)
+
+
+def csa_prefill(args):
+    """CSA prefill chunk: 1,024 query tokens at the end of a 32K sequence
+    (H=64, d=128; 8,191 entries; 16 x 64 indexer; k=512 + window 128).  The
+    step is compress (whole sequence) -> visible counts -> flat top-k ->
+    sparse attention, replayed as one graph."""
+    import torch
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    W = synth.csa_prefill_chunk(0, device=dev)
+    t = W.tensors
+    N, nq, k = 8191, 1024, 512
+    ckv = ops.compress(t["raw_kv"], t["z"], t["b"], 8, 4)
+
+    def step(_):
+        ops.compress(t["raw_kv"], t["z"], t["b"], 8, 4, out=ckv)
+        nv = ops.visible_count(t["q_pos"], 8, 4, N)
+        idx = ops.index_topk(t["q_i"], t["k_i"], t["w_i"], nv, k)
+        return ops.sparse_attn(t["q"], ckv, idx, t["raw_kv"], t["q_pos"], 128), nv
+
+    graphs = capture(step, [None])
+    ms = timed_graphs(graphs, max(10, args.steps // 2), 3)
+    kt = kernel_times(step, [None], max(10, args.steps // 2))
+    _, nv = step(None)
+    torch.cuda.synchronize()
+    nvh = nv.cpu().numpy()[0].astype(float)
+    idx_flops = 2.0 * 16 * 64 * float(nvh.sum())
+    attn_flops = 4.0 * 64 * 128 * nq * (k + 128)
+    del graphs
+    return dict(ms=ms, kernels=kt, idx_flops=idx_flops, attn_flops=attn_flops, nq=nq,
+                compress_bytes=32768 * 512 + 32768 * 4 + N * 512)
 
 
 def indexer_128k(args):
@@ -459,6 +503,18 @@ def main():
             kernels_us={kk: v[0] * 1e3 for kk, v in h["kernels"].items()})
         extras["compress_1M_hca_b32"] = dict(ms=h["compress_ms"], GBps=h["compress_bytes"] / (h["compress_ms"] * 1e-3) / 1e9,
                                              hbm_frac=h["compress_bytes"] / (h["compress_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        torch.cuda.empty_cache()
+        cp = csa_prefill(args)
+        ck = {kk: v[0] for kk, v in cp["kernels"].items()}
+        sk = ck.get("score_flat_mfma", float("nan"))
+        ak = ck.get("attn_sparse_mfma", float("nan"))
+        extras["csa_prefill_32k_chunk1024"] = dict(
+            ms=cp["ms"], tokens_per_s=cp["nq"] / (cp["ms"] * 1e-3),
+            step_TFLOPs=(cp["idx_flops"] + cp["attn_flops"]) / (cp["ms"] * 1e-3) / 1e12,
+            step_mfma_frac=(cp["idx_flops"] + cp["attn_flops"]) / (cp["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            index_score_mfma_frac=cp["idx_flops"] / (sk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            sparse_attn_mfma_frac=cp["attn_flops"] / (ak * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            kernels_us={kk: v * 1e3 for kk, v in ck.items()})
         torch.cuda.empty_cache()
         ix = indexer_128k(args)
         fk = ix["flat"]["kernels"].get("score_flat_mfma", (float("nan"), 1))[0]

@@ -123,6 +123,13 @@ HATTN_DEV f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// MFMA 32x32x16 bf16 -> fp32 (on gfx950 twice the rate per FLOP of the
+// 16x16x32 form).  Lane l holds A[l%32][8*(l/32)..+7], B[8*(l/32)..+7][l%32];
+// element v of the result is D[8*(v/4) + 4*(l/32) + v%4][l%32].
+HATTN_DEV f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
 // gfx950 LDS transpose read: within each group of 16 lanes, lane i receives
 // element i of each of the four 16-element rows formed by concatenating the
 // group's 8-byte chunks (lane j's chunk holds elements 4(j%4)..4(j%4)+3 of

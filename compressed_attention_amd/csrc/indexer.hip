@@ -162,6 +162,146 @@ __global__ __launch_bounds__(64 * NWQ, KS >= 8 ? 1 : 8 / NWQ) void score_flat_mf
 }
 
 // ---------------------------------------------------------------------------
+// Flat score, bf16, 16 heads, d_i = 16*KS in {32, 64, 128}, on the 32x32x16
+// MFMA.  Same workgroup tiling as above (16 queries, 64-key LDS tiles,
+// double-buffered), but each wave covers two query pairs: an MFMA row is
+// (query of the pair, head), a column a key of a 32-key half tile, so a wave
+// issues 32 MFMAs per tile.  Lane l holds, for key l%32, heads
+// {4h..4h+3, 8+4h..8+4h+3} (h = l/32) of both queries of the pair: it sums
+// its 8 heads per query and one lane swap between the wave halves finishes
+// both queries' head sums (lanes < 32: first query, lanes >= 32: second).
+// ---------------------------------------------------------------------------
+template <int KS>
+__global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_t* __restrict__ q_i,
+                                                                   const uint16_t* __restrict__ k_i,
+                                                                   const float* __restrict__ w_i,
+                                                                   const int32_t* __restrict__ n_vis, int64_t nq,
+                                                                   int64_t n, int64_t ld, float* __restrict__ S,
+                                                                   int nqb, int nch, int chunk) {
+  constexpr int D = 16 * KS;
+  constexpr int TN = 64;
+  constexpr int PITCH = D + 8;
+  constexpr int PIECES = TN * D / 8 / 256;  // 16-byte pieces per thread per tile
+  static_assert(TN * D / 8 % 256 == 0, "tile split");
+  __shared__ __align__(16) uint16_t kt[2][TN * PITCH];
+  __shared__ int s_nv[16];
+
+  int qb, ch;
+  if (!xcd_decode(blockIdx.x, nqb, nch, &qb, &ch)) return;
+  const int64_t b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, c32 = lane & 31;
+  const int64_t q0 = int64_t(qb) * 16;
+  if (threadIdx.x < 16) {
+    const int64_t q = q0 + threadIdx.x;
+    int v = 0;
+    if (q < nq) v = int(imin64(n, imax64(0, n_vis[b * nq + q])));
+    s_nv[threadIdx.x] = v;
+  }
+  __syncthreads();
+  int maxv = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) maxv = max(maxv, s_nv[i]);
+  const int64_t e_begin = int64_t(ch) * chunk;
+  const int64_t e_end = imin64(e_begin + chunk, maxv);
+  if (e_begin >= e_end) return;
+
+  // A operand: row c32 of pair p = (query 4*wave + 2p + c32/16, head c32%16)
+  u32x4_t a[2][KS];
+  // weights of this lane's 8 heads, for both queries of each pair
+  float wv[2][2][8];
+  int my_nv[2];
+  float* srow[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    {
+      const int64_t q = q0 + 4 * wave + 2 * p + (c32 >> 4);
+      const bool ok = q < nq;
+      const uint16_t* qp = q_i + ((b * nq + (ok ? q : 0)) * 16 + (c32 & 15)) * D + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a[p][ks] = ok ? ld16(qp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t q = q0 + 4 * wave + 2 * p + j;
+      const bool ok = q < nq;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int head = 8 * (v >> 2) + 4 * half + (v & 3);
+        wv[p][j][v] = ok ? w_i[(b * nq + q) * 16 + head] : 0.f;
+      }
+    }
+    // this lane stores query 4*wave + 2p + half
+    const int64_t mq = q0 + 4 * wave + 2 * p + half;
+    my_nv[p] = mq < nq ? s_nv[4 * wave + 2 * p + half] : 0;
+    srow[p] = S + (b * nq + (mq < nq ? mq : 0)) * ld;
+  }
+
+  // Keys: 32-bit row indices (n < 2^31 is checked on the host).  Rows past
+  // the end of the cache are read clamped to the last row; their scores are
+  // never stored (every stored key is below n_vis <= n).
+  const uint16_t* kb = k_i + b * n * D;
+  const int n32 = int(n);
+  u32x4_t pre[PIECES];
+  auto load = [&](int e0) {
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+      const int pc = threadIdx.x + 256 * j;
+      const int row = pc / (D / 8), col = pc % (D / 8);
+      const int e = min(e0 + row, n32 - 1);
+      pre[j] = ld16(kb + size_t(e) * D + col * 8);
+    }
+  };
+  const int eb = int(e_begin), ee = int(e_end);
+  load(eb);
+  int buf = 0;
+  for (int e0 = eb; e0 < ee; e0 += TN, buf ^= 1) {
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+      const int pc = threadIdx.x + 256 * j;
+      const int row = pc / (D / 8), col = pc % (D / 8);
+      *reinterpret_cast<u32x4_t*>(&kt[buf][row * PITCH + col * 8]) = pre[j];
+    }
+    __syncthreads();
+    if (e0 + TN < ee) load(e0 + TN);
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[p][kh][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t bf[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+        bf[kh] = *reinterpret_cast<const u32x4_t*>(&kt[buf][(32 * kh + c32) * PITCH + 16 * ks + 8 * half]);
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) acc[p][kh] = mfma32x32x16(a[p][ks], bf[kh], acc[p][kh]);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        float s0 = 0.f, s1 = 0.f;  // this lane's 8 heads of the pair's first / second query
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          s0 = fmaf(wv[p][0][v], relu_bits(acc[p][kh][v]), s0);
+          s1 = fmaf(wv[p][1][v], relu_bits(acc[p][kh][8 + v]), s1);
+        }
+        // lanes < 32 receive the first query's total, lanes >= 32 the second's
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+        const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int e = e0 + 32 * kh + c32;
+        if (e < my_nv[p]) srow[p][e] = tot;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // HISA stage 1 score on fp32 block representatives, 16 heads, d_i = 16*KQ.
 // A workgroup owns QPW queries (1 or 4) and one LDS tile of 64 block means;
 // its 4 waves cover the (query, 16-block subtile) pairs: with 4 queries each
@@ -510,10 +650,12 @@ __global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __r
     uint32_t* rk = rkey + wave * kRegion;
     int32_t* rp = rpos + wave * kRegion;
     int cnt = 0;
-    for (int base = p0; base < p1; base += 256 * 2) {
-      f32x4_t v[2];
+    // kCollectU 16-byte loads per lane in flight per sweep step
+    constexpr int kCollectU = 8;
+    for (int base = p0; base < p1; base += 256 * kCollectU) {
+      f32x4_t v[kCollectU];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kCollectU; ++u) {
         const int i = base + u * 256 + lane * 4;
         if (i + 3 < p1) {
           v[u] = *reinterpret_cast<const f32x4_t*>(srow + i);
@@ -523,7 +665,7 @@ __global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __r
         }
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kCollectU; ++u) {
         const int i = base + u * 256 + lane * 4;
         uint32_t key[4];
         bool sel[4];
@@ -750,15 +892,19 @@ static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, hi
     const int nch = int((a.n + chunk - 1) / chunk);
     dim3 grid(xcd_grid(nqb, nch), unsigned(a.bt));
     LaunchScope ls("score_flat_mfma", st);
+#define HATTN_FLAT32(KS)                                                                                     \
+  HATTN_LAUNCH((score_flat_mfma32_kernel<KS>), grid, dim3(256), 0, st, (const uint16_t*)a.q_i,              \
+               (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk)
 #define HATTN_FLAT(KS)                                                                                       \
   HATTN_LAUNCH((score_flat_mfma_kernel<KS, 4>), grid, dim3(256), 0, st, (const uint16_t*)a.q_i,             \
                (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk)
     switch (a.d_i) {
-      case 32: HATTN_FLAT(1); break;
-      case 64: HATTN_FLAT(2); break;
-      case 128: HATTN_FLAT(4); break;
+      case 32: HATTN_FLAT32(2); break;
+      case 64: HATTN_FLAT32(4); break;
+      case 128: HATTN_FLAT32(8); break;
       default: HATTN_FLAT(8); break;
     }
+#undef HATTN_FLAT32
 #undef HATTN_FLAT
   } else if (a.dtype == 0) {
     launch_valu_score<0, float>(a, (const float*)a.k_i, a.n, a.n, nullptr, 1, 1, ld, S, st);

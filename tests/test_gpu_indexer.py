@@ -94,6 +94,24 @@ def test_float_inputs_iou_and_boundary():
     check_near_ties(got, ref, scores, tol)
 
 
+@pytest.mark.parametrize("d,lo,hi", [(32, -8, 8), (64, -8, 8), (128, -4, 4), (256, -4, 4)])
+def test_flat_mfma_head_dims_exact(d, lo, hi):
+    # Every bf16 MFMA flat-score head size, bit-exact on an integer grid whose
+    # weighted sums stay below 2^24 units of 2^-8 (16 heads * d * hi^2 * 255):
+    # ragged query count, key count off the 64-key tile, mixed visibility.
+    N, nq = 3001, 37
+    q_i = synth.int_grid((2, nq, 16, d), 61 + d, lo, hi, dtype=torch.bfloat16)
+    k_i = synth.int_grid((2, N, d), 62 + d, lo, hi, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((2, nq, 16), 63 + d)
+    nv = synth.int_grid((2, nq), 64 + d, 0, N, dtype=torch.int32)
+    nv[0, :3] = torch.tensor([0, 1, N], dtype=torch.int32)
+    for k in (1, 100, 700, 4000):
+        idx = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), k).cpu().numpy()
+        for b in range(2):
+            ref = oracle.flat_topk(f64(q_i[b]), f64(k_i[b]), f64(w_i[b]), nv[b].numpy(), k)
+            assert np.array_equal(idx[b], ref), (d, b, k)
+
+
 def test_edge_cases():
     d, N, nq = 64, 300, 20
     q_i = synth.int_grid((2, nq, 16, d), 51, -8, 8, dtype=torch.bfloat16)
