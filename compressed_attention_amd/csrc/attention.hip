@@ -25,6 +25,7 @@
 namespace hattn {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSparseChunkMax = 2048;  // keys per sparse MFMA workgroup (their indices are staged in LDS)
 constexpr float kLn2 = 0.6931471805599453f;
 
 // Source row of virtual key j of a query: compressed keys first, then the
@@ -46,14 +47,16 @@ HATTN_DEV const T* key_row(int64_t j, int64_t nc, const int32_t* idx_row, const 
 // branch-free in 32-bit arithmetic (each sequence's cache holds fewer than
 // 2^31 elements, checked on the host).  `ok` says whether the key exists;
 // when it does not, the row is row 0 of the raw sequence (always valid,
-// L >= 1) and its data is never used.  Sparse lists are read at a clamped
-// index so the load is always in bounds.
+// L >= 1) and its data is never used.  Sparse indices come from the
+// workgroup's LDS copy of its chunk (sidx[t] = index of key j_base + t, for
+// the chunk's compressed keys), read at a clamped slot.
 template <bool SPARSE>
-HATTN_DEV const uint16_t* key_src32(int j, int j_end, int nc, const int32_t* idx_row, const uint16_t* ckv_b,
-                                    int n, const uint16_t* raw_b, int L, int rbase, int C, bool* ok) {
+HATTN_DEV const uint16_t* key_src32(int j, int j_end, int nc, const int32_t* sidx, int j_base,
+                                    const uint16_t* ckv_b, int n, const uint16_t* raw_b, int L, int rbase, int C,
+                                    bool* ok) {
   const bool in_c = j < nc;
   int e;
-  if (SPARSE) e = idx_row[in_c ? j : 0];
+  if (SPARSE) e = sidx[in_c && j < j_end ? j - j_base : 0];
   else e = j;
   const int r = rbase + j;  // rbase = p - nw + 1 - nc
   const bool okc = in_c && unsigned(e) < unsigned(n);
@@ -103,6 +106,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* _
   __shared__ __align__(16) uint16_t kt[TK * KP];
   __shared__ __align__(16) uint16_t vt[TK * VP];
   __shared__ uint64_t vmask[TK / 64];
+  __shared__ int32_t sidx[SPARSE ? kSparseChunkMax : 1];  // this chunk's compressed indices
 
   const int64_t qrow = blockIdx.y;
   const int split = blockIdx.x;
@@ -156,12 +160,19 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* _
         const int pidx = tid + NT * u;
         bool ok;
         // Skipped keys read raw row 0 (finite data); their logits are masked.
-        const uint16_t* src = key_src32<SPARSE>(j0 + pidx / PPR, j_end, nc32, idx_row, ckv_b, n32, raw_b, L32,
-                                                rbase, C, &ok);
+        const uint16_t* src = key_src32<SPARSE>(j0 + pidx / PPR, j_end, nc32, sidx, j_begin, ckv_b, n32, raw_b,
+                                                L32, rbase, C, &ok);
         pre[u] = ld16_nt(src + (pidx % PPR) * 8);
       }
     }
   };
+  if (SPARSE) {
+    // Stage the chunk's indices once: every tile then computes its row
+    // addresses from LDS instead of a dependent global load.
+    const int cend = min(j_end, nc32);
+    for (int t = tid; j_begin + t < cend; t += NT) sidx[t] = idx_row[j_begin + t];
+    __syncthreads();
+  }
   if (j_begin < j_end) fetch(j_begin);
   for (int j0 = j_begin; j0 < j_end; j0 += TK) {
 #pragma unroll
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* _
 #pragma unroll
       for (int h = 0; h < TK / 64; ++h) {
         bool ok;
-        key_src32<SPARSE>(j0 + 64 * h + lane, j_end, nc32, idx_row, ckv_b, n32, raw_b, L32, rbase, C, &ok);
+        key_src32<SPARSE>(j0 + 64 * h + lane, j_end, nc32, sidx, j_begin, ckv_b, n32, raw_b, L32, rbase, C, &ok);
         const uint64_t mk = ballot(ok);
         if (lane == 0) vmask[h] = mk;
       }
@@ -532,6 +543,7 @@ static AttnPlan plan_attn(const AttnArgs& a) {
   chunk = std::max<int64_t>(chunk, 128);
   chunk = (chunk + tk - 1) / tk * tk;
   if (chunk >= maxkeys) chunk = (maxkeys + tk - 1) / tk * tk;
+  if (mfma_shape(a) && a.idx) chunk = std::min<int64_t>(chunk, kSparseChunkMax);
   p.chunk = int(chunk);
   p.nsplit = int((maxkeys + chunk - 1) / chunk);
   if (p.nsplit > 1) {

@@ -590,21 +590,24 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
 // collected the threshold was too high, if a region overflowed it was too
 // low; both retry with a rank 2x lower / higher, and a row that still fails
 // is flagged and finished by the exact segment + merge kernels below.
-constexpr int kSampleN = 8192;
-constexpr int kRegion = 512;  // candidate slots per wave (16 waves -> 8192)
+constexpr int kSampNT = 512;                 // threads per workgroup (two resident per CU: 4 waves/SIMD)
+constexpr int kSampleN = 8192;               // sample size, and candidate slots per row
+constexpr int kSampW = kSampNT / kWave;      // waves per workgroup
+constexpr int kRegion = kSampleN / kSampW;   // candidate slots per wave
+constexpr size_t kSampLds = kSampleN * 6;    // u32 keys + u16 positions
 
-__global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __restrict__ S, int64_t ld,
+__global__ __launch_bounds__(kSampNT, 4) void select_sampled_kernel(const float* __restrict__ S, int64_t ld,
                                                                 const int32_t* __restrict__ n_vis, int64_t n, int k,
                                                                 int32_t* __restrict__ idx,
                                                                 float* __restrict__ score_out,
                                                                 int32_t* __restrict__ flags) {
-  constexpr int NW = kSelNT / kWave;
-  static_assert(NW * kRegion == kSampleN, "region layout");
+  constexpr int NW = kSampW;
+  static_assert(NW * kRegion == kSampleN && kRegion % kWave == 0, "region layout");
   extern __shared__ uint32_t dyn[];
-  uint32_t* rkey = dyn;                               // [NW][kRegion]
-  int32_t* rpos = reinterpret_cast<int32_t*>(dyn + kSampleN);  // [NW][kRegion]
-  uint32_t* samp = dyn + 2 * kSampleN;                // [kSampleN]
-  __shared__ SelectShared<kSelNT> sh;
+  uint32_t* rkey = dyn;  // [NW][kRegion] candidate keys; first holds the sample
+  uint16_t* rpos = reinterpret_cast<uint16_t*>(dyn + kSampleN);  // [NW][kRegion] offsets in the wave's segment
+  uint32_t* samp = rkey;
+  __shared__ SelectShared<kSampNT> sh;
   __shared__ int wcnt[NW];
   __shared__ int verdict;
   const int64_t row = blockIdx.x;
@@ -614,44 +617,51 @@ __global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __r
   int32_t* orow = idx + row * k;
   float* scrow = score_out ? score_out + row * k : nullptr;
 
-  if (nv <= kSelCap) {  // short row: plain selection over all of it
-    const SelSeg sg = wave_segment<kSelNT>(nv);
+  if (nv <= kSampleN) {  // short row: plain selection over all of it
+    const SelSeg sg = wave_segment<kSampNT>(nv);
     uint32_t kc[kSelIT];
     seg_keys_from_scores(srow, sg, kc);
-    radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
-    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int i, uint32_t key, int) {
+    radix_threshold<kSampNT, kSelIT>(kc, sg.iters, k, sh);
+    const int chosen = emit_selected<kSampNT, kSelIT>(kc, sg, sh, [&](int slot, int i, uint32_t key, int) {
       orow[slot] = i;
       if (scrow) scrow[slot] = key_to_float(key);
     });
-    for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+    for (int t = chosen + threadIdx.x; t < k; t += kSampNT) {
       orow[t] = -1;
       if (scrow) scrow[t] = -INFINITY;
     }
     if (threadIdx.x == 0) flags[row] = 0;
     return;
   }
+  // Candidate positions are kept as 16-bit offsets inside each wave's
+  // segment; a row too long for that goes to the exact fallback.
+  const int segw = ((nv + NW - 1) / NW + 255) & ~255;
+  if (segw > 65536) {
+    if (threadIdx.x == 0) flags[row] = 1;
+    return;
+  }
   // 1. sample: 16 evenly spaced runs of 512 scores (16-byte aligned)
   {
     const int stride = (nv / 16) & ~3;
-    for (int c = 0; c < 16; ++c) load_score_keys<kSelNT>(srow + c * stride, 512, samp + c * 512);
+    for (int c = 0; c < 16; ++c) load_score_keys<kSampNT>(srow + c * stride, 512, samp + c * 512);
   }
   __syncthreads();
-  const SelSeg ssg = wave_segment<kSelNT>(kSampleN);
+  const SelSeg ssg = wave_segment<kSampNT>(kSampleN);
   uint32_t skc[kSelIT];
   seg_keys_from_u32(samp, ssg, skc);
+  __syncthreads();  // the sample's LDS becomes the candidate area
   int r = min(kSampleN, int((3LL * k * kSampleN) / (2LL * nv)) + 32);
-  const int segw = ((nv + NW - 1) / NW + 255) & ~255;
   const int p0 = wave * segw, p1 = min(nv, p0 + segw);
   bool done = false;
   for (int attempt = 0; attempt < 4 && !done; ++attempt) {
-    radix_threshold<kSelNT, kSelIT>(skc, ssg.iters, r, sh);
+    radix_threshold<kSampNT, kSelIT>(skc, ssg.iters, r, sh);
     const uint32_t tau = sh.thr;  // key of the r-th largest sample (0: all)
     // 2. collect keys >= tau of this wave's segment, in position order
     uint32_t* rk = rkey + wave * kRegion;
-    int32_t* rp = rpos + wave * kRegion;
+    uint16_t* rp = rpos + wave * kRegion;
     int cnt = 0;
     // kCollectU 16-byte loads per lane in flight per sweep step
-    constexpr int kCollectU = 8;
+    constexpr int kCollectU = 4;
     for (int base = p0; base < p1; base += 256 * kCollectU) {
       f32x4_t v[kCollectU];
 #pragma unroll
@@ -686,7 +696,7 @@ __global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __r
           if (sel[e]) {
             if (slot < kRegion) {
               rk[slot] = key[e];
-              rp[slot] = i + e;
+              rp[slot] = uint16_t(i + e - p0);
             }
             ++slot;
           }
@@ -722,15 +732,16 @@ __global__ __launch_bounds__(kSelNT) void select_sampled_kernel(const float* __r
   }
   // 3. exact selection over the candidates (key 0 = empty slot); the wave
   // segments of kSampleN keys are exactly the waves' regions
-  const SelSeg csg = wave_segment<kSelNT>(kSampleN);
+  const SelSeg csg = wave_segment<kSampNT>(kSampleN);
   uint32_t ckc[kSelIT];
   seg_keys_from_u32(rkey, csg, ckc);
-  radix_threshold<kSelNT, kSelIT>(ckc, csg.iters, k, sh);
-  const int chosen = emit_selected<kSelNT, kSelIT>(ckc, csg, sh, [&](int slot, int i, uint32_t key, int) {
-    orow[slot] = rpos[i];
+  radix_threshold<kSampNT, kSelIT>(ckc, csg.iters, k, sh);
+  // candidate i lies in the region (and segment) of the wave that emits it
+  const int chosen = emit_selected<kSampNT, kSelIT>(ckc, csg, sh, [&](int slot, int i, uint32_t key, int) {
+    orow[slot] = p0 + int(rpos[i]);
     if (scrow) scrow[slot] = key_to_float(key);
   });
-  for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+  for (int t = chosen + threadIdx.x; t < k; t += kSampNT) {
     orow[t] = -1;
     if (scrow) scrow[t] = -INFINITY;
   }
@@ -870,7 +881,7 @@ static void set_lds_limits() {
   if (done) return;
   done = true;
   (void)hipFuncSetAttribute((const void*)select_sampled_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            kSampleN * 12);
+                            kSampLds);
 }
 
 template <int MODE, typename TQ, typename TK>
@@ -888,7 +899,10 @@ static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, hi
     // 16 queries per workgroup.  (32, with 8 waves sharing each key tile,
     // measured slower: one resident workgroup per CU and longer barriers.)
     const int nqb = int((a.nq + 15) / 16);
-    const int chunk = 2048;
+    // Key chunks of 2048 keys, halved (down to 256) until the grid has about
+    // four workgroups per CU (two resident, 256 CUs).
+    int chunk = 2048;
+    while (chunk > 256 && int64_t(nqb) * a.bt * ((a.n + chunk - 1) / chunk) < 1024) chunk /= 2;
     const int nch = int((a.n + chunk - 1) / chunk);
     dim3 grid(xcd_grid(nqb, nch), unsigned(a.bt));
     LaunchScope ls("score_flat_mfma", st);
@@ -938,7 +952,7 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
   int32_t* flags = reinterpret_cast<int32_t*>(cb + p.cand_bytes);
   {
     LaunchScope ls("select_sampled", st);
-    HATTN_LAUNCH(select_sampled_kernel, dim3(unsigned(p.rows)), dim3(kSelNT), kSampleN * 12, st, S, p.ld,
+    HATTN_LAUNCH(select_sampled_kernel, dim3(unsigned(p.rows)), dim3(kSampNT), kSampLds, st, S, p.ld,
                        a.n_vis, a.n, k, idx, score, flags);
   }
   e = hipGetLastError();

@@ -112,6 +112,21 @@ def test_flat_mfma_head_dims_exact(d, lo, hi):
             assert np.array_equal(idx[b], ref), (d, b, k)
 
 
+def test_long_row_selection_boundaries_exact():
+    # A flat launch with n above the LDS-resident limit: rows whose visible
+    # counts straddle the in-register limit (8192), the LDS limit (16384) and
+    # the full row take every selection path; bit-exact on the integer grid.
+    d, N, nq = 64, 40000, 12
+    q_i = synth.int_grid((1, nq, 16, d), 71, -8, 8, dtype=torch.bfloat16)
+    k_i = synth.int_grid((1, N, d), 72, -8, 8, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((1, nq, 16), 73)
+    nv = torch.tensor([[0, 1, 5000, 8192, 8193, 12000, 16384, 16385, 20000, 33333, 39999, 40000]], dtype=torch.int32)
+    for k in (64, 2048):
+        idx = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), k).cpu().numpy()
+        ref = oracle.flat_topk(f64(q_i[0]), f64(k_i[0]), f64(w_i[0]), nv[0].numpy(), k)
+        assert np.array_equal(idx[0], ref), k
+
+
 def test_edge_cases():
     d, N, nq = 64, 300, 20
     q_i = synth.int_grid((2, nq, 16, d), 51, -8, 8, dtype=torch.bfloat16)
