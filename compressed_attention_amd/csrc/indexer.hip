@@ -314,7 +314,12 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
                                                               const float* __restrict__ w_i,
                                                               const int32_t* __restrict__ n_vis, int64_t nq,
                                                               int64_t n, int B, int64_t nb, int64_t ld,
-                                                              float* __restrict__ S1, int nqg, int nch, int chunk) {
+                                                              float* __restrict__ S1, int nqg, int nch, int chunk,
+                                                              int32_t* __restrict__ zero, int64_t zero_n) {
+  // Clears the block-major stage-2 counters (the kernels after this one in
+  // the same call fill them).
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int64_t i = threadIdx.x; i < zero_n; i += 256) zero[i] = 0;
   constexpr int D = 16 * KQ;
   constexpr int TB = 64;
   constexpr int PITCH = D + 4;
@@ -416,6 +421,169 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
 }
 
 // ---------------------------------------------------------------------------
+// HISA stage 1 on the bf16 MFMA for many queries (bf16 queries, 16 heads,
+// d_i = 16*KS in {32, 64, 128}).  Every fp32 block mean is split exactly into
+// three bf16 parts, hi + mid + lo (each captures the next 8 significant bits
+// of the remaining value), while its tile is staged in LDS; each MFMA step
+// then accumulates q.hi + q.mid + q.lo.  Each product of two bf16 values is
+// exact in fp32, so the scores carry the fp32 block means in full; the
+// tiling, head reduction and layout are those of the 32x32x16 flat score
+// kernel (16 queries per workgroup, 64 blocks per tile).  Candidate blocks of
+// a query are those whose first entry is visible.
+// ---------------------------------------------------------------------------
+HATTN_DEV void split3_bf16(float x, uint16_t* hi, uint16_t* mid, uint16_t* lo) {
+  const uint16_t h = f32_to_bf16(x);
+  const float r1 = x - bf16_to_f32(h);
+  const uint16_t m = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(m);
+  *hi = h;
+  *mid = m;
+  *lo = f32_to_bf16(r2);
+}
+
+template <int KS>
+__global__ __launch_bounds__(256, 2) void score_stage1_x3_kernel(const uint16_t* __restrict__ q_i,
+                                                                 const float* __restrict__ reps,
+                                                                 const float* __restrict__ w_i,
+                                                                 const int32_t* __restrict__ n_vis, int64_t nq,
+                                                                 int64_t n, int B, int64_t nb, int64_t ld,
+                                                                 float* __restrict__ S1, int nqb, int nch, int chunk,
+                                                                 int32_t* __restrict__ zero, int64_t zero_n) {
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int64_t i = threadIdx.x; i < zero_n; i += 256) zero[i] = 0;
+  constexpr int D = 16 * KS;
+  constexpr int TN = 64;
+  constexpr int PITCH = D + 8;
+  constexpr int PIECES = TN * D / 4 / 256;  // 16-byte (4 x fp32) pieces per thread per tile
+  static_assert(TN * D / 4 % 256 == 0, "tile split");
+  __shared__ __align__(16) uint16_t kt[3][TN * PITCH];
+  __shared__ int s_nb[16];
+
+  int qb, ch;
+  if (!xcd_decode(blockIdx.x, nqb, nch, &qb, &ch)) return;
+  const int64_t b = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, c32 = lane & 31;
+  const int64_t q0 = int64_t(qb) * 16;
+  if (threadIdx.x < 16) {
+    const int64_t q = q0 + threadIdx.x;
+    int v = 0;
+    if (q < nq) {
+      const int64_t nvq = imin64(n, imax64(0, n_vis[b * nq + q]));
+      v = int((nvq + B - 1) / B);
+    }
+    s_nb[threadIdx.x] = v;
+  }
+  __syncthreads();
+  int maxb = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) maxb = max(maxb, s_nb[i]);
+  const int jb = ch * chunk;
+  const int je = min(jb + chunk, maxb);
+  if (jb >= je) return;
+
+  u32x4_t a[2][KS];
+  float wv[2][2][8];
+  int my_nb[2];
+  float* srow[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    {
+      const int64_t q = q0 + 4 * wave + 2 * p + (c32 >> 4);
+      const bool ok = q < nq;
+      const uint16_t* qp = q_i + ((b * nq + (ok ? q : 0)) * 16 + (c32 & 15)) * D + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) a[p][ks] = ok ? ld16(qp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t q = q0 + 4 * wave + 2 * p + j;
+      const bool ok = q < nq;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int head = 8 * (v >> 2) + 4 * half + (v & 3);
+        wv[p][j][v] = ok ? w_i[(b * nq + q) * 16 + head] : 0.f;
+      }
+    }
+    const int64_t mq = q0 + 4 * wave + 2 * p + half;
+    my_nb[p] = mq < nq ? s_nb[4 * wave + 2 * p + half] : 0;
+    srow[p] = S1 + (b * nq + (mq < nq ? mq : 0)) * ld;
+  }
+
+  // Block means: 32-bit row indices; rows past nb are read clamped (their
+  // scores are never stored: every stored block is below its query's count).
+  const float* rb = reps + b * nb * D;
+  const int nb32 = int(nb);
+  u32x4_t pre[PIECES];
+  auto load = [&](int j0) {
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int pc = threadIdx.x + 256 * u;
+      const int row = pc / (D / 4), col = pc % (D / 4);
+      const int j = min(j0 + row, nb32 - 1);
+      pre[u] = ld16(rb + size_t(j) * D + col * 4);
+    }
+  };
+  load(jb);
+  for (int j0 = jb; j0 < je; j0 += TN) {
+    __syncthreads();  // the previous tile's readers are done
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int pc = threadIdx.x + 256 * u;
+      const int row = pc / (D / 4), col = pc % (D / 4);
+      uint16_t hv[4], mv[4], lv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split3_bf16(__uint_as_float(pre[u][e]), &hv[e], &mv[e], &lv[e]);
+      const int off = row * PITCH + col * 4;
+      *reinterpret_cast<u32x2_t*>(&kt[0][off]) = u32x2_t{uint32_t(hv[0]) | (uint32_t(hv[1]) << 16),
+                                                         uint32_t(hv[2]) | (uint32_t(hv[3]) << 16)};
+      *reinterpret_cast<u32x2_t*>(&kt[1][off]) = u32x2_t{uint32_t(mv[0]) | (uint32_t(mv[1]) << 16),
+                                                         uint32_t(mv[2]) | (uint32_t(mv[3]) << 16)};
+      *reinterpret_cast<u32x2_t*>(&kt[2][off]) = u32x2_t{uint32_t(lv[0]) | (uint32_t(lv[1]) << 16),
+                                                         uint32_t(lv[2]) | (uint32_t(lv[3]) << 16)};
+    }
+    __syncthreads();
+    if (j0 + TN < je) load(j0 + TN);
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[p][kh][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int part = 0; part < 3; ++part) {
+        u32x4_t bf[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          bf[kh] = *reinterpret_cast<const u32x4_t*>(&kt[part][(32 * kh + c32) * PITCH + 16 * ks + 8 * half]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) acc[p][kh] = mfma32x32x16(a[p][ks], bf[kh], acc[p][kh]);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          s0 = fmaf(wv[p][0][v], relu_bits(acc[p][kh][v]), s0);
+          s1 = fmaf(wv[p][1][v], relu_bits(acc[p][kh][8 + v]), s1);
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+        const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int j = j0 + 32 * kh + c32;
+        if (j < my_nb[p]) srow[p][j] = tot;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // HISA stage 2 score, bf16, 16 heads: one wave per (query, chosen block).
 // Candidate position j = slot*B + offset; visible candidates form a prefix.
 // ---------------------------------------------------------------------------
@@ -472,6 +640,128 @@ __global__ __launch_bounds__(64) void score_stage2_mfma_kernel(const uint16_t* _
       const float s = sum4_transpose(v[0], v[1], v[2], v[3]);
       const int64_t e = e0 + 16 * g + r16;
       if (e < e_end) out[e - e_begin] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// HISA stage 2, block-major (bf16, 16 heads, d_i = 16*KS, B <= 128): used
+// when many queries choose each block.  The block-select kernel appended
+// every (row, slot) that chose block b to list[b]; a workgroup loads block
+// b's keys into LDS once and scores them for groups of 16 of its choosers
+// (32x32x16 MFMA, the flat kernel's per-wave layout: two query pairs per
+// wave, 32-key column tiles).  Workgroups of one block take every nslice-th
+// group, so a block chosen by many queries is spread over nslice of them.
+// Scores land where the per-slot kernel puts them: S2[row][slot*B + j] for
+// the visible entries j of the block.
+// ---------------------------------------------------------------------------
+template <int KS>
+__global__ __launch_bounds__(256, 2) void score_stage2_bm_kernel(const uint16_t* __restrict__ q_i,
+                                                                 const uint16_t* __restrict__ k_i,
+                                                                 const float* __restrict__ w_i,
+                                                                 const int32_t* __restrict__ n_vis,
+                                                                 const int32_t* __restrict__ cnt,
+                                                                 const int32_t* __restrict__ list, int64_t nq,
+                                                                 int64_t n, int B, int m, int64_t nb, int64_t ld2,
+                                                                 float* __restrict__ S2, int nslice) {
+  constexpr int D = 16 * KS;
+  constexpr int BMAX = 128;
+  constexpr int PITCH = D + 8;
+  __shared__ __align__(16) uint16_t kt[BMAX * PITCH];
+  const int slice = blockIdx.x;
+  const int64_t blkid = blockIdx.y, b = blockIdx.z;
+  const int64_t bucket = b * nb + blkid;
+  const int c = cnt[bucket];
+  const int ngroups = (c + 15) / 16;
+  if (slice >= ngroups) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, c32 = lane & 31;
+
+  // the block's keys (rows past the cache end read clamped; never stored)
+  const uint16_t* kb = k_i + b * n * D;
+  const int64_t e_blk = blkid * B;
+  for (int pc = threadIdx.x; pc < B * (D / 8); pc += 256) {
+    const int row = pc / (D / 8), col = pc % (D / 8);
+    const int64_t e = imin64(e_blk + row, n - 1);
+    *reinterpret_cast<u32x4_t*>(&kt[row * PITCH + col * 8]) = ld16(kb + e * D + col * 8);
+  }
+  __syncthreads();
+  const int32_t* lst = list + bucket * nq;
+
+  for (int gi = slice; gi < ngroups; gi += nslice) {
+    // entries 16*gi + 4*wave + {0..3}: pair p holds entries 2p, 2p+1
+    int rowq[2][2];
+    int slotq[2][2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ent = 16 * gi + 4 * wave + 2 * p + j;
+        const int packed = ent < c ? lst[ent] : -1;
+        rowq[p][j] = packed < 0 ? -1 : packed / m;
+        slotq[p][j] = packed < 0 ? 0 : packed % m;
+      }
+    u32x4_t a[2][KS];
+    float wv[2][2][8];
+    int my_nv[2];
+    float* srow[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      {
+        const int r = rowq[p][c32 >> 4];
+        const uint16_t* qp = q_i + (int64_t(r < 0 ? 0 : r) * 16 + (c32 & 15)) * D + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) a[p][ks] = r >= 0 ? ld16(qp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = rowq[p][j];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int head = 8 * (v >> 2) + 4 * half + (v & 3);
+          wv[p][j][v] = r >= 0 ? w_i[int64_t(r) * 16 + head] : 0.f;
+        }
+      }
+      // this lane stores entry 2p + half of the pair
+      const int r = rowq[p][half];
+      const int64_t nvr = r >= 0 ? imin64(n, imax64(0, n_vis[r])) : 0;
+      my_nv[p] = int(imax64(0, imin64(int64_t(B), nvr - e_blk)));  // visible entries of this block
+      srow[p] = S2 + int64_t(r < 0 ? 0 : r) * ld2 + int64_t(slotq[p][half]) * B;
+    }
+    for (int t0 = 0; t0 < B; t0 += 64) {
+      f32x16_t acc[2][2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[p][kh][v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t bf[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+          bf[kh] = *reinterpret_cast<const u32x4_t*>(&kt[(t0 + 32 * kh + c32) * PITCH + 16 * ks + 8 * half]);
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) acc[p][kh] = mfma32x32x16(a[p][ks], bf[kh], acc[p][kh]);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+          float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            s0 = fmaf(wv[p][0][v], relu_bits(acc[p][kh][v]), s0);
+            s1 = fmaf(wv[p][1][v], relu_bits(acc[p][kh][8 + v]), s1);
+          }
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
+          const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+          const int jloc = t0 + 32 * kh + c32;
+          if (jloc < my_nv[p]) srow[p][jloc] = tot;
+        }
     }
   }
 }
@@ -548,7 +838,10 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
                                                              const int32_t* __restrict__ n_vis,
                                                              const int32_t* __restrict__ blk, int64_t n, int B, int m,
                                                              int k, int32_t* __restrict__ idx,
-                                                             float* __restrict__ score_out) {
+                                                             float* __restrict__ score_out,
+                                                             int32_t* __restrict__ inv_cnt,
+                                                             int32_t* __restrict__ inv_list, int64_t nq,
+                                                             int64_t nb) {
   __shared__ SelectShared<kSelNT> sh;
   __shared__ int cnt;
   __shared__ int32_t bsh[MODE == 2 ? kSelNT : 1];  // chosen block ids, for the emission
@@ -571,6 +864,12 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
     if (MODE == 2) v = (blk_lds ? bsh[i / B] : brow[i / B]) * B + (i % B);
     orow[slot] = v;
     if (scrow) scrow[slot] = key_to_float(key);
+    if (MODE == 1 && inv_cnt) {
+      // block-major stage 2: append (row, slot) to the chosen block's list
+      const int64_t bucket = (row / nq) * nb + i;
+      const int pos = atomicAdd(&inv_cnt[bucket], 1);
+      inv_list[bucket * nq + pos] = int32_t(row * m + slot);
+    }
   });
   for (int s = chosen + threadIdx.x; s < k; s += kSelNT) {
     orow[s] = -1;
@@ -937,7 +1236,7 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
   if (!p.multi) {
     LaunchScope ls("select_rows", st);
     HATTN_LAUNCH(select_rows_kernel<0>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S, p.ld, a.n_vis,
-                       nullptr, a.n, 1, 1, k, idx, score);
+                 nullptr, a.n, 1, 1, k, idx, score, nullptr, nullptr, int64_t(1), int64_t(1));
     return hipGetLastError();
   }
   char* cb = reinterpret_cast<char*>(ws) + p.s_bytes;
@@ -980,7 +1279,8 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
 // ---- HISA -------------------------------------------------------------------
 struct HisaPlan {
   int64_t rows, nb, ld1, ld2;
-  size_t s1_bytes, blk_bytes, s2_bytes, total;
+  bool bm;  // block-major stage 2
+  size_t s1_bytes, blk_bytes, s2_bytes, cnt_bytes, list_bytes, total;
 };
 
 static HisaPlan plan_hisa(const IndexArgs& a, int B, int m) {
@@ -992,7 +1292,17 @@ static HisaPlan plan_hisa(const IndexArgs& a, int B, int m) {
   p.s1_bytes = align256(size_t(p.rows) * p.ld1 * 4);
   p.blk_bytes = align256(size_t(p.rows) * m * 4);
   p.s2_bytes = align256(size_t(p.rows) * p.ld2 * 4);
-  p.total = p.s1_bytes + p.blk_bytes + p.s2_bytes;
+  // Block-major stage 2 pays off once each block has many choosers; its
+  // per-block lists hold up to nq entries each.
+  p.bm = a.dtype == 1 && a.h_i == 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128) && B <= 128 &&
+         B % 64 == 0 && a.nq >= 128 && int64_t(a.nq) * m >= 8 * p.nb && p.nb <= 65535 && a.bt <= 65535 &&
+         a.bt * p.nb * a.nq <= (int64_t(1) << 26) &&
+         p.rows * m < (int64_t(1) << 31);
+  if (p.bm) {
+    p.cnt_bytes = align256(size_t(a.bt) * p.nb * 4);
+    p.list_bytes = align256(size_t(a.bt) * p.nb * a.nq * 4);
+  }
+  p.total = p.s1_bytes + p.blk_bytes + p.s2_bytes + p.cnt_bytes + p.list_bytes;
   return p;
 }
 
@@ -1013,7 +1323,30 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
 
   // Stage 1: block scores.
   const bool mfma1 = a.h_i == 16 && a.d_i % 16 == 0 && a.d_i <= 256;
-  if (mfma1) {
+  const bool bm = p.bm && mfma1;  // the stage-1 MFMA kernel clears the counters
+  int32_t* bm_cnt = bm ? reinterpret_cast<int32_t*>(base + p.s1_bytes + p.blk_bytes + p.s2_bytes) : nullptr;
+  int32_t* bm_list = bm ? reinterpret_cast<int32_t*>(base + p.s1_bytes + p.blk_bytes + p.s2_bytes + p.cnt_bytes)
+                        : nullptr;
+  const int64_t bm_zero = bm ? a.bt * p.nb : 0;
+  const bool x3 = mfma1 && a.dtype == 1 && a.nq >= 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128) &&
+                  p.nb < (int64_t(1) << 31);
+  if (x3) {
+    const int nqb = int((a.nq + 15) / 16);
+    int chunk = 1024;  // blocks per workgroup, halved until ~4 workgroups per CU
+    while (chunk > 64 && int64_t(nqb) * a.bt * ((p.nb + chunk - 1) / chunk) < 1024) chunk /= 2;
+    const int nch = int((p.nb + chunk - 1) / chunk);
+    dim3 grid(xcd_grid(nqb, nch), unsigned(a.bt));
+    LaunchScope ls("score_stage1_mfma", st);
+#define HATTN_S1X3(KS)                                                                                       \
+  HATTN_LAUNCH(score_stage1_x3_kernel<KS>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i, reps, a.w_i,     \
+               a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqb, nch, chunk, bm_cnt, bm_zero)
+    switch (a.d_i) {
+      case 32: HATTN_S1X3(2); break;
+      case 64: HATTN_S1X3(4); break;
+      default: HATTN_S1X3(8); break;
+    }
+#undef HATTN_S1X3
+  } else if (mfma1) {
     const int qpw = a.nq >= 4 ? 4 : 1;  // queries per workgroup
     const int nqg = int((a.nq + qpw - 1) / qpw);
     const int chunk = 64;  // one LDS tile of block means per workgroup
@@ -1023,10 +1356,10 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
 #define HATTN_S1(T, KQ)                                                                                      \
   if (qpw == 4)                                                                                              \
     HATTN_LAUNCH((score_stage1_kernel<T, KQ, 4>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
-                       a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk);                            \
+                 a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk, bm_cnt, bm_zero);                 \
   else                                                                                                       \
     HATTN_LAUNCH((score_stage1_kernel<T, KQ, 1>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
-                       a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk)
+                 a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk, bm_cnt, bm_zero)
     if (a.dtype == 0) {
       switch (a.d_i / 16) {
         case 1: HATTN_S1(float, 1); break;
@@ -1055,7 +1388,7 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   {
     LaunchScope ls("select_blocks", st);
     HATTN_LAUNCH(select_rows_kernel<1>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S1, p.ld1,
-                       a.n_vis, nullptr, a.n, B, m, m, blk_out, nullptr);
+                 a.n_vis, nullptr, a.n, B, m, m, blk_out, nullptr, bm_cnt, bm_list, a.nq, p.nb);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1063,7 +1396,24 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   // Stage 2: token scores inside the chosen blocks.
   const bool mfma2 = a.dtype == 1 && a.h_i == 16 && B % 16 == 0 &&
                      (a.d_i == 32 || a.d_i == 64 || a.d_i == 128 || a.d_i == 256);
-  if (mfma2) {
+  if (bm) {
+    // Workgroups per block: about two groups of 16 choosers each on average
+    // (each workgroup first loads the block's keys and its first group's
+    // queries; fewer, longer workgroups amortise that).
+    const int64_t groups = (a.bt * a.nq * m + 16 * a.bt * p.nb - 1) / (16 * a.bt * p.nb);
+    const int nslice = int(std::max<int64_t>(1, std::min<int64_t>(16, (groups + 1) / 2)));
+    dim3 grid(unsigned(nslice), unsigned(p.nb), unsigned(a.bt));
+    LaunchScope ls("score_stage2_bm", st);
+#define HATTN_S2BM(KS)                                                                                       \
+  HATTN_LAUNCH(score_stage2_bm_kernel<KS>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i,                  \
+               (const uint16_t*)a.k_i, a.w_i, a.n_vis, bm_cnt, bm_list, a.nq, a.n, B, m, p.nb, p.ld2, S2, nslice)
+    switch (a.d_i) {
+      case 32: HATTN_S2BM(2); break;
+      case 64: HATTN_S2BM(4); break;
+      default: HATTN_S2BM(8); break;
+    }
+#undef HATTN_S2BM
+  } else if (mfma2) {
     dim3 grid(unsigned(m), unsigned(p.rows));
     LaunchScope ls("score_stage2_mfma", st);
 #define HATTN_S2(KS)                                                                                         \
@@ -1086,7 +1436,7 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   {
     LaunchScope ls("select_tokens", st);
     HATTN_LAUNCH(select_rows_kernel<2>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
-                       a.n_vis, blk_out, a.n, B, m, k, idx, nullptr);
+                 a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
   }
   return hipGetLastError();
 }

@@ -244,6 +244,29 @@ def test_hisa_decode_shape_exact(N, B, m, k):
         assert np.array_equal(idx.cpu().numpy()[b], ref), b
 
 
+@pytest.mark.parametrize("d,B", [(64, 64), (128, 128), (32, 128)])
+def test_hisa_block_major_stage2_exact(d, B):
+    # Many queries per sequence (the block-major stage-2 path: each chosen
+    # block scored once for all its choosers), two sequences, ragged key
+    # count, mixed visibility; integer grid, 4-bit weights, bound asserted.
+    bt, nq, N, m, k = 2, 200, 5001, 8, 300
+    q_i = synth.int_grid((bt, nq, 16, d), 221 + d, -4, 4, dtype=torch.bfloat16)
+    k_i = synth.int_grid((bt, N, d), 222 + d, -4, 4, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((bt, nq, 16), 223 + d, bits=4)
+    nv = synth.int_grid((bt, nq), 224 + d, 1, N, dtype=torch.int32)
+    nv[0, :4] = torch.tensor([1, B, B + 1, N], dtype=torch.int32)
+    kd = k_i.to(DEV)
+    reps = ops.hisa_pool(kd, B)
+    idx, blk = ops.hisa_topk(q_i.to(DEV), kd, w_i.to(DEV), nv.to(DEV), reps, B, m, k, return_blocks=True)
+    torch.cuda.synchronize()
+    for b in range(bt):
+        q, kk, ww = f64(q_i[b]), f64(k_i[b]), f64(w_i[b])
+        _stage1_exact_bound(q, kk, ww, B, 4)
+        ref, ref_blk = oracle.hisa_topk(q, kk, ww, nv[b].numpy(), B, m, k)
+        assert np.array_equal(blk.cpu().numpy()[b], ref_blk), b
+        assert np.array_equal(idx.cpu().numpy()[b], ref), b
+
+
 def test_long_rows_ties_take_the_fallback_path():
     # All-zero queries: every visible score is exactly 0, so the sampled
     # threshold can never isolate k candidates; the exact segment + merge
