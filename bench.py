@@ -6,10 +6,12 @@ The timed step is one decode step of a CSA + HCA layer pair at 1M context
 128, window 128, HISA B=128 m=64 k=2048 on a 16 x 128 indexer over 262,143
 CSA entries, 8,192 HCA entries):
 
-  CSA: compress the window the new token completes -> refresh the last HISA
-       block mean -> visible counts -> HISA (block scores, block top-m, token
-       scores in the chosen blocks, token top-k) -> sparse attention
-  HCA: compress the completed 128-token window -> dense attention
+  CSA: one launch compresses the window the new token completes, refreshes
+       the HISA block mean holding that entry and writes the visible count
+       -> HISA (block scores, block top-m, token scores in the chosen
+       blocks, token top-k) -> sparse attention
+  HCA: the same launch for the completed 128-token window (no block means)
+       -> dense attention
 
 Every step replays two HIP graphs captured from the library calls, one per
 layer, on two streams that join at the end of the step, so the HCA layer's
@@ -147,24 +149,20 @@ def hybrid_pair(args):
     torch.cuda.synchronize()
     log(f"[bench] hybrid pair inputs + {R} cache replicas ready in {time.time() - t0:.1f}s")
 
-    def csa_compress(c):
-        ops.compress(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, N - 1, N, out=c["ckv"])
-
     def csa_select(c):
-        ops.hisa_pool(c["k_i"], B, nb - 1, nb, out=c["reps"])
-        nv = ops.visible_count(t["q_pos"], 8, 4, N)
+        # compressed entry + block mean + visible count of the new token, one launch
+        nv = ops.decode_append(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, t["q_pos"], c["ckv"], c["k_i"],
+                               c["reps"], B)
         return ops.hisa_topk(t["q_i"], c["k_i"], t["w_i"], nv, c["reps"], B, m, k)
 
     def csa_attend(c, idx):
         return ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128)
 
     def csa_step(c):
-        csa_compress(c)
         return csa_attend(c, csa_select(c))
 
     def hca_step(c):
-        ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, Nh - 1, Nh, out=c["hkv"])
-        nvh = ops.visible_count(t["q_pos"], 128, 128, Nh)
+        nvh = ops.decode_append(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, t["q_pos"], c["hkv"])
         return ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128)
 
     def step(c):  # eager, one stream
@@ -172,9 +170,7 @@ def hybrid_pair(args):
 
     # The two layers' inputs are independent: each is captured as its own
     # graph and the pair is replayed on two streams (default priority both)
-    # that join at the end of every step.  (Splitting the CSA layer further,
-    # so that its tail compression runs beside its selection, measured
-    # slower: every extra dependent graph launch costs more than it hides.)
+    # that join at the end of every step.
     side = torch.cuda.Stream()
     g_csa = capture(csa_step, caches, stream=torch.cuda.Stream())
     g_hca = capture(hca_step, caches, stream=torch.cuda.Stream())

@@ -22,6 +22,7 @@ SIGNATURES = {
                           _psz, _p],
     "hattn_dense_compressed_attn": [_i32, _p, _p, _i64, _p, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p,
                                     _p, _psz, _p],
+    "hattn_decode_append": [_i32, _p, _i64, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p, _p, _i32, _i32, _p, _p],
     "hattn_timer_enable": [_i32],
     "hattn_timer_collect": [],
     "hattn_timer_query": [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],

@@ -168,8 +168,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* _
   };
   if (SPARSE) {
     // Stage the chunk's indices once: every tile then computes its row
-    // addresses from LDS instead of a dependent global load.
-    const int cend = min(j_end, nc32);
+    // addresses from LDS instead of a dependent global load.  (The chunk's
+    // compressed keys end at min(j_begin + chunk, k) whatever the window
+    // length, so these loads need not wait for the query position.)
+    const int cend = min(j_begin + chunk, nc32);
     for (int t = tid; j_begin + t < cend; t += NT) sidx[t] = idx_row[j_begin + t];
     __syncthreads();
   }

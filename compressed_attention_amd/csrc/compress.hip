@@ -8,6 +8,9 @@
 // recomputed per thread from the (cache-resident) logits, which costs w exps
 // per w 16-byte loads.  When windows overlap (s < w) the rows shared with the
 // previous entry of the run are kept in registers instead of being re-read.
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -392,6 +395,183 @@ hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_
                        d_i, B, nb, j0, nj, reps);
   }
   return hipGetLastError();
+}
+
+
+// ---------------------------------------------------------------------------
+// Per-token maintenance of one compressed layer in a decode step, one query
+// (the newest token, at position p) per sequence:
+//   workgroup 0: the visible count at p; if the token completes entry
+//                e = (p - w + 1) / s, the softmax-weighted compression of
+//                that window into ckv[e] (weights in LDS; row groups sum
+//                their rows, the groups are added in a fixed order);
+//   workgroup 1: if it does and block means are kept, the mean of the HISA
+//                block holding e (entries past the last one count as zero).
+// The same arithmetic as hattn_compress / hattn_hisa_pool / the visible
+// count, in one launch instead of three.
+// ---------------------------------------------------------------------------
+constexpr int kAppNT = 512;  // threads per workgroup
+constexpr int kAppUNR = 8;   // rows each thread has in flight
+
+// Sums rows [0, n) of a [n][ld] matrix (16-byte slot cs, rows rg, rg + RG, ...)
+// with per-row weights wt(u) into acc.  The first batch of rows is already in
+// `first` (loaded before the weights were ready); later batches reuse it.
+// Loads of a batch are all issued before any is used.
+template <typename T, typename Wt>
+HATTN_DEV void append_rows(const T* __restrict__ base, int64_t ld, int n, int rg, int RG, u32x4_t (&first)[kAppUNR],
+                           Wt wt, float* acc) {
+  constexpr int V = Vec16<T>::N;
+  for (int u0 = rg; u0 < n; u0 += kAppUNR * RG) {
+    if (u0 != rg) {
+#pragma unroll
+      for (int k = 0; k < kAppUNR; ++k) {
+        const int u = u0 + k * RG;
+        first[k] = u < n ? ld16(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kAppUNR; ++k) {
+      const int u = u0 + k * RG;
+      if (u < n) {
+        float f[V];
+        Vec16<T>::unpack(first[k], f);
+        const float pu = wt(u);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = fmaf(pu, f[i], acc[i]);
+      }
+    }
+  }
+}
+
+template <typename T>
+HATTN_DEV void append_first(const T* __restrict__ base, int64_t ld, int n, int rg, u32x4_t (&first)[kAppUNR], int RG) {
+#pragma unroll
+  for (int k = 0; k < kAppUNR; ++k) {
+    const int u = rg + k * RG;
+    first[k] = u < n ? ld16(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kAppNT) void append_kernel(const T* __restrict__ x, int64_t L, int C,
+                                                        const float* __restrict__ z, const float* __restrict__ bias,
+                                                        int w, int s, const int32_t* __restrict__ q_pos,
+                                                        T* __restrict__ y, int64_t N, int32_t* __restrict__ n_vis,
+                                                        const T* __restrict__ k_i, int d_i, int B,
+                                                        float* __restrict__ reps) {
+  constexpr int V = Vec16<T>::N;
+  extern __shared__ float sm[];
+  __shared__ float red[2];
+  const int64_t b = blockIdx.y;
+  const int64_t p = q_pos[b];
+  int64_t nv = p < w - 1 ? 0 : (p - w + 1) / s + 1;
+  if (nv > N) nv = N;
+  const bool done = p >= w - 1 && (p - w + 1) % s == 0 && (p - w + 1) / s < N;
+  const int64_t e = done ? (p - w + 1) / s : -1;
+  if (blockIdx.x == 0) {
+    if (threadIdx.x == 0) n_vis[b] = int32_t(nv);
+    if (!done) return;
+    const int slots = C / V;
+    const int RG = kAppNT / slots;
+    const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
+    const int64_t t0 = e * s;
+    const T* xb = x + (b * L + t0) * C + cs * V;
+    // the window's first rows go out before the softmax weights are known
+    u32x4_t first[kAppUNR];
+    if (rg < RG) append_first(xb, C, w, rg, first, RG);
+    float* wt = sm;        // [w] logits, then softmax numerators
+    float* part = sm + w;  // [RG][C] row-group partial sums
+    for (int u = threadIdx.x; u < w; u += kAppNT) wt[u] = (z ? z[b * L + t0 + u] : 0.f) + (bias ? bias[u] : 0.f);
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+      float mx = -INFINITY;
+      for (int u = threadIdx.x; u < w; u += kWave) mx = fmaxf(mx, wt[u]);
+      mx = wave_max(mx);
+      float den = 0.f;
+      for (int u = threadIdx.x; u < w; u += kWave) den += __expf(wt[u] - mx);
+      den = wave_sum(den);
+      if (threadIdx.x == 0) {
+        red[0] = mx;
+        red[1] = den;
+      }
+    }
+    __syncthreads();
+    const float mx = red[0], inv = 1.f / red[1];
+    if (rg < RG) {
+      float acc[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      append_rows(xb, C, w, rg, RG, first, [&](int u) { return __expf(wt[u] - mx); }, acc);
+#pragma unroll
+      for (int i = 0; i < V; ++i) part[rg * C + cs * V + i] = acc[i];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < slots; c += kAppNT) {
+      float r[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) r[i] = 0.f;
+      for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int i = 0; i < V; ++i) r[i] += part[g * C + c * V + i];
+#pragma unroll
+      for (int i = 0; i < V; ++i) r[i] *= inv;
+      st16(y + (b * N + e) * C + c * V, Vec16<T>::pack(r));
+    }
+    return;
+  }
+  // workgroup 1: block mean of the block holding e
+  if (!done || !reps) return;
+  const int64_t nb = (N + B - 1) / B;
+  const int64_t j = e / B;
+  const int64_t i0 = j * B;
+  const int cnt = int(imin64(N, i0 + B) - i0);
+  const int slots = d_i / V;
+  const int RG = kAppNT / slots;
+  const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
+  float* part = sm;  // [RG][d_i]
+  if (rg < RG) {
+    const T* kb = k_i + (b * N + i0) * d_i + cs * V;
+    u32x4_t first[kAppUNR];
+    append_first(kb, d_i, cnt, rg, first, RG);
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    append_rows(kb, d_i, cnt, rg, RG, first, [](int) { return 1.f; }, acc);
+#pragma unroll
+    for (int i = 0; i < V; ++i) part[rg * d_i + cs * V + i] = acc[i];
+  }
+  __syncthreads();
+  const float invb = 1.f / float(B);
+  for (int c = threadIdx.x; c < d_i; c += kAppNT) {
+    float r = 0.f;
+    for (int g = 0; g < RG; ++g) r += part[g * d_i + c];
+    reps[(b * nb + j) * d_i + c] = r * invb;
+  }
+}
+
+template <typename T>
+static hipError_t launch_append_t(const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
+                                  int w, int s, const int32_t* q_pos, void* y, int64_t N, int32_t* n_vis,
+                                  const void* k_i, int d_i, int B, float* reps, hipStream_t st) {
+  const size_t smem = append_lds_bytes(std::is_same<T, float>::value ? 0 : 1, C, w, d_i, reps != nullptr);
+  LaunchScope ls("decode_append", st);
+  HATTN_LAUNCH((append_kernel<T>), dim3(reps ? 2u : 1u, unsigned(bt)), dim3(kAppNT), smem, st, (const T*)x, L, C, z,
+               bias, w, s, q_pos, (T*)y, N, n_vis, (const T*)k_i, d_i, B, reps);
+  return hipGetLastError();
+}
+
+size_t append_lds_bytes(int dtype, int C, int w, int d_i, bool with_reps) {
+  const int V = dtype == 0 ? 4 : 8;
+  const size_t sm_c = size_t(w + (kAppNT / (C / V)) * C) * 4;
+  const size_t sm_r = with_reps ? size_t(kAppNT / (d_i / V)) * d_i * 4 : 0;
+  return std::max(sm_c, sm_r);
+}
+
+hipError_t launch_append(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
+                         int w, int s, const int32_t* q_pos, void* y, int64_t N, int32_t* n_vis, const void* k_i,
+                         int d_i, int B, float* reps, hipStream_t st) {
+  if (dtype == 0) return launch_append_t<float>(x, bt, L, C, z, bias, w, s, q_pos, y, N, n_vis, k_i, d_i, B, reps, st);
+  return launch_append_t<uint16_t>(x, bt, L, C, z, bias, w, s, q_pos, y, N, n_vis, k_i, d_i, B, reps, st);
 }
 
 }  // namespace hattn

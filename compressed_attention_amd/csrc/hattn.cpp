@@ -264,6 +264,29 @@ hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void*
   return attn_common("dense_compressed_attn", a, ws, ws_bytes, stream);
 }
 
+hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, int64_t L, int32_t C,
+                                   const float* logits, const float* pos_bias, int32_t w, int32_t stride,
+                                   const int32_t* q_pos, void* ckv, int32_t* n_vis, const void* k_i, int32_t d_i,
+                                   int32_t B, float* reps, void* stream) {
+  if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "decode_append: bad dtype %d", dtype);
+  if (bt < 0 || L < 0) return fail(HATTN_ERR_ARG, "decode_append: negative size");
+  if (w < 1 || w > 4096 || stride < 1) return fail(HATTN_ERR_ARG, "decode_append: need 1 <= w <= 4096, stride >= 1");
+  if (L < w) return fail(HATTN_ERR_ARG, "decode_append: L=%lld shorter than the window %d", (long long)L, w);
+  const int vec = 16 / elem_bytes(dtype);
+  if (C <= 0 || C % vec || C / vec > 256)
+    return fail(HATTN_ERR_ARG, "decode_append: C=%d must be a positive multiple of %d, at most %d", C, vec, 256 * vec);
+  if ((k_i == nullptr) != (reps == nullptr)) return fail(HATTN_ERR_ARG, "decode_append: give both k_i and reps, or neither");
+  if (reps && (B < 1 || d_i <= 0 || d_i % vec || d_i / vec > 256))
+    return fail(HATTN_ERR_ARG, "decode_append: bad B=%d or d_i=%d", B, d_i);
+  if (bt == 0) return ok();
+  if (!raw_kv || !q_pos || !ckv || !n_vis) return fail(HATTN_ERR_ARG, "decode_append: NULL pointer");
+  const int64_t N = (L - w) / stride + 1;
+  if (N > INT32_MAX) return fail(HATTN_ERR_ARG, "decode_append: too many entries");
+  return hip_status(hattn::launch_append(dtype, raw_kv, bt, L, C, logits, pos_bias, w, stride, q_pos, ckv, N, n_vis,
+                                         k_i, d_i, B, reps, (hipStream_t)stream),
+                    "decode_append");
+}
+
 hattn_status_t hattn_timer_enable(int on) {
   if (on) {
     g_totals.clear();

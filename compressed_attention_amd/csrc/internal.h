@@ -44,6 +44,10 @@ hipError_t launch_visible_count(const int32_t* pos, int64_t count, int w, int s,
                                 int32_t* n_vis, hipStream_t st);
 hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_i, int B, int64_t j0,
                        int64_t j1, float* reps, hipStream_t st);
+size_t append_lds_bytes(int dtype, int C, int w, int d_i, bool with_reps);
+hipError_t launch_append(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
+                         int w, int s, const int32_t* q_pos, void* y, int64_t N, int32_t* n_vis, const void* k_i,
+                         int d_i, int B, float* reps, hipStream_t st);
 
 // ---- indexer ---------------------------------------------------------------
 struct IndexArgs {

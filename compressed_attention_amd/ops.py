@@ -108,6 +108,41 @@ def visible_count(pos, w: int, stride: int, n_entries: int, out=None):
     return out
 
 
+def decode_append(x, logits, pos_bias, w: int, stride: int, q_pos, ckv, k_i=None, reps=None, B: int = 1,
+                  n_vis=None):
+    """Per-token maintenance of one compressed layer for a decode step (one
+    query per sequence at q_pos [bt][1]): returns n_vis [bt][1]; rewrites the
+    entry of ckv that the token completes and, with k_i / reps, the mean of
+    the HISA block holding it."""
+    _need(x, "x", ndim=3)
+    dt = _fdt(x, "x")
+    bt, L, C = x.shape
+    _need(q_pos, "q_pos", torch.int32)
+    if q_pos.numel() != bt:
+        raise ValueError("q_pos must hold one position per sequence")
+    N = (L - w) // stride + 1 if L >= w else 0
+    _need(ckv, "ckv", x.dtype, 3)
+    if tuple(ckv.shape) != (bt, N, C):
+        raise ValueError(f"ckv must be [{bt}][{N}][{C}]")
+    if logits is not None:
+        _need(logits, "logits", torch.float32)
+    if pos_bias is not None:
+        _need(pos_bias, "pos_bias", torch.float32)
+    d_i = 0
+    if k_i is not None or reps is not None:
+        _need(k_i, "k_i", x.dtype, 3)
+        _need(reps, "reps", torch.float32, 3)
+        d_i = k_i.shape[2]
+        if k_i.shape[:2] != (bt, N) or tuple(reps.shape) != (bt, -(-N // B), d_i):
+            raise ValueError("k_i must be [bt][N][d_i] and reps [bt][ceil(N/B)][d_i]")
+    if n_vis is None:
+        n_vis = torch.empty(q_pos.shape, dtype=torch.int32, device=x.device)
+    check("hattn_decode_append", lib().hattn_decode_append(dt, _ptr(x), bt, L, C, _ptr(logits), _ptr(pos_bias), w,
+                                                           stride, _ptr(q_pos), _ptr(ckv), _ptr(n_vis), _ptr(k_i),
+                                                           d_i, B, _ptr(reps), _stream(x.device)))
+    return n_vis
+
+
 def _index_common(q_i, k_i, w_i, n_vis):
     _need(q_i, "q_i", ndim=4)
     dt = _fdt(q_i, "q_i")

@@ -190,6 +190,36 @@ hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void*
                                            size_t* ws_bytes, void* stream);
 
 /*
+ * hattn_decode_append -- per-token maintenance of one compressed layer in a
+ * decode step: one query per sequence, the sequence's newest token at
+ * position q_pos[b].  In one launch:
+ *   n_vis[b] = entries visible at q_pos[b] (exactly as hattn_visible_count);
+ *   if that token completes entry e = (q_pos[b] - w + 1) / stride (the token
+ *   is its window's last one and e < N), ckv[b][e] = the compression of
+ *   that window (as hattn_compress over entries [e, e+1));
+ *   if k_i and reps are given and an entry was completed, reps[b][e / B] =
+ *   the mean of the HISA block holding e (as hattn_hisa_pool over it).
+ * Sources: [HCA] section 怎么压 (each entry is a weighted merge of its run
+ * of raw entries), [HISA] section 02, first stage (one pooled representative
+ * per block), and the causal visibility of hattn_visible_count.
+ *   raw_kv   [bt][L][C]      dtype; K|V rows as in hattn_compress
+ *   logits   [bt][L] fp32 or NULL; pos_bias [w] fp32 or NULL
+ *   q_pos    [bt] int32      any values (positions that complete no entry
+ *                            only get their visible count)
+ *   ckv      [bt][N][C]      N = (L - w) / stride + 1; entry e rewritten
+ *   n_vis    [bt] int32      output
+ *   k_i      [bt][N][d_i]    dtype, or NULL (then reps must be NULL)
+ *   reps     [bt][ceil(N/B)][d_i] fp32; block e / B rewritten
+ * Limits: 1 <= w <= 4096, L >= w; C and d_i multiples of 16/elem_bytes with
+ * at most 256 16-byte pieces per row.  Errors: HATTN_ERR_ARG for bad sizes,
+ * NULL required pointers or an inconsistent k_i / reps pair.
+ */
+hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, int64_t L, int32_t C,
+                                   const float* logits, const float* pos_bias, int32_t w, int32_t stride,
+                                   const int32_t* q_pos, void* ckv, int32_t* n_vis, const void* k_i, int32_t d_i,
+                                   int32_t B, float* reps, void* stream);
+
+/*
  * Kernel timer (profiling aid).  When enabled, every kernel the library
  * launches is bracketed by HIP events recorded on the same stream, and its
  * duration is accumulated per kernel name when hattn_timer_collect() is

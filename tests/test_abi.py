@@ -51,6 +51,27 @@ def test_compress_validation(L):
     assert f(1, None, 0, 100, 256, None, None, 8, 4, 0, 24, None, None) == 0  # bt = 0: nothing to do
 
 
+def test_decode_append_validation(L):
+    f = L.hattn_decode_append
+    p = ctypes.c_void_p(16)
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("dt", 1), ("x", p), ("bt", 2), ("L", 100), ("C", 256), ("z", None), ("b", None), ("w", 8), ("s", 4),
+        ("qp", p), ("y", p), ("nv", p), ("ki", None), ("di", 0), ("B", 0), ("reps", None), ("st", None)]]
+    assert f(*args(dt=5)) == 1
+    assert f(*args(C=250)) == 1                      # not a multiple of 8 bf16 elements
+    assert f(*args(C=4096)) == 1                     # more than 256 16-byte slots
+    assert f(*args(w=0)) == 1
+    assert f(*args(w=5000, L=6000)) == 1             # window above 4096
+    assert f(*args(s=0)) == 1
+    assert f(*args(L=7)) == 1                        # shorter than the window
+    assert f(*args(ki=p)) == 1                       # k_i without reps
+    assert f(*args(ki=p, reps=p, di=128, B=0)) == 1  # B = 0
+    assert f(*args(ki=p, reps=p, di=12, B=16)) == 1  # d_i not a multiple of 8
+    assert f(*args(y=None)) == 1
+    assert b"NULL" in L.hattn_last_error()
+    assert f(*args(bt=0, x=None, qp=None, y=None, nv=None)) == 0  # nothing to do
+
+
 def _sz():
     return ctypes.c_size_t(0)
 

@@ -118,3 +118,61 @@ def test_hisa_pool(dtype, B, n):
     ops.hisa_pool(k_i.to(DEV), B, nb - 1, nb, out=part)
     torch.cuda.synchronize()
     assert torch.equal(part[:, nb - 1], reps[:, nb - 1]) and bool((part[:, : nb - 1] == 0).all())
+
+
+def _append_positions(L, w, s, N):
+    """Decode positions covering: an entry completed at the start, in the
+    middle and at the end; a position inside a window (no entry completed);
+    one before the first window closes; one past the last entry."""
+    return [w - 1, w - 1 + s * (N // 2), w - 1 + s * (N - 1), w - 1 + s * (N // 3) + (1 if s > 1 else 0),
+            max(0, w - 3), w - 1 + s * N + (s - 1)]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("w,s,L,C,pool", [(8, 4, 1001, 256, 16), (128, 128, 1000, 256, 0), (5, 3, 77, 64, 8),
+                                          (1, 1, 300, 32, 128), (12, 4, 259, 512, 0)])
+def test_decode_append(dtype, w, s, L, C, pool):
+    """The fused per-token step against the oracle's compression, block mean
+    and visible count: only the entry the token completes (and the block
+    holding it) is written; everything else keeps its previous value."""
+    N = (L - w) // s + 1
+    pos = _append_positions(L, w, s, N)
+    if s == 1:
+        pos[3] = w - 1 + (N // 3)  # every position past w - 2 completes an entry
+    bt = len(pos)
+    x = synth.normal((bt, L, C), seed=41 + w, dtype=dtype)
+    z = synth.normal((bt, L), seed=42 + w)
+    b = synth.normal((w,), seed=43 + w, std=0.1)
+    q_pos = torch.tensor(pos, dtype=torch.int32)
+    ckv = torch.full((bt, N, C), 7.0, dtype=dtype, device=DEV)
+    k_i = reps = None
+    if pool:
+        d_i = 128
+        k_i = synth.int_grid((bt, N, d_i), seed=44, lo=-4, hi=4, dtype=dtype)
+        reps = torch.full((bt, -(-N // pool), d_i), -3.0, dtype=torch.float32, device=DEV)
+    nv = ops.decode_append(x.to(DEV), z.to(DEV), b.to(DEV), w, s, q_pos.to(DEV), ckv,
+                           k_i.to(DEV) if pool else None, reps, pool or 1)
+    torch.cuda.synchronize()
+    nv = nv.cpu().numpy()
+    ckv = f64(ckv)
+    reps = f64(reps) if pool else None
+    for i, p in enumerate(pos):
+        assert nv[i] == oracle.n_visible(p, w, s, N), (i, p)
+        done = p >= w - 1 and (p - w + 1) % s == 0 and (p - w + 1) // s < N
+        e = (p - w + 1) // s if done else -1
+        for row in range(N):
+            if row != e:
+                assert (ckv[i, row] == 7.0).all(), (i, row)
+        if done:
+            ref = oracle.compress(f64(x[i, e * s : e * s + w]), f64(z[i, e * s : e * s + w]), f64(b), w, s)[0]
+            if dtype == torch.float32:
+                np.testing.assert_allclose(ckv[i, e], ref, rtol=2e-5, atol=2e-5)
+            else:
+                assert_bf16_close(ckv[i, e], ref)
+        if pool:
+            ref_reps = oracle.hisa_pool(f64(k_i[i]), pool)
+            for j in range(reps.shape[1]):
+                if done and j == e // pool:
+                    np.testing.assert_array_equal(reps[i, j], ref_reps[j])  # small integers / 2^k: exact
+                else:
+                    assert (reps[i, j] == -3.0).all(), (i, j)
