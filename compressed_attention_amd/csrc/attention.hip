@@ -110,7 +110,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* _
 
   const int64_t qrow = blockIdx.y;
   const int split = blockIdx.x;
-  const int64_t b = qrow / nq;
+  const int64_t b = idiv(qrow, nq);
   const int64_t p = q_pos[qrow];
   const int nw = int(imax64(0, imin64(window, p + 1)));
   const int64_t nc = SPARSE ? int64_t(k) : imin64(n, imax64(0, n_vis[qrow]));
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
 
   const int64_t qrow = blockIdx.y;
   const int split = blockIdx.x;
-  const int64_t b = qrow / nq;
+  const int64_t b = idiv(qrow, nq);
   const int64_t p = q_pos[qrow];
   const int nw = int(imax64(0, imin64(window, p + 1)));
   const int64_t nc = SPARSE ? int64_t(k) : imin64(n, imax64(0, n_vis[qrow]));

@@ -76,6 +76,30 @@ HATTN_DEV T wave_min(T v) {
 
 HATTN_DEV int lane_id() { return __lane_id(); }
 
+// a / b for 0 <= a and 0 < b: a 32-bit division when both fit (a row index
+// over a per-sequence count), the 64-bit expansion only otherwise.
+HATTN_DEV int64_t idiv(int64_t a, int64_t b) {
+  return ((uint64_t(a) | uint64_t(b)) >> 32) == 0 ? int64_t(uint32_t(a) / uint32_t(b)) : a / b;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts (1, 2, 4,
+// 8) scan each row of 16 lanes in registers, then the three lower row
+// totals are read out as scalars and added.  No LDS round trips (a
+// __shfl-based scan costs six ds_bpermute latencies).
+HATTN_DEV uint32_t wave_prefix_incl(uint32_t x) {
+  int v = int(x);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = __lane_id() >> 4;
+  v += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+  return uint32_t(v);
+}
+
 // max(x, 0) as one integer max: every negative float and -0.0 compares below
 // +0.0 as a signed integer.  (fmaxf would first canonicalise x, an extra
 // instruction per element.)

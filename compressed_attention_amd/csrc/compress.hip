@@ -464,10 +464,11 @@ __global__ __launch_bounds__(kAppNT) void append_kernel(const T* __restrict__ x,
   __shared__ float red[2];
   const int64_t b = blockIdx.y;
   const int64_t p = q_pos[b];
-  int64_t nv = p < w - 1 ? 0 : (p - w + 1) / s + 1;
+  const int64_t pe = p >= w - 1 ? idiv(p - w + 1, s) : -1;  // entry ending at or before p
+  int64_t nv = pe + 1;
   if (nv > N) nv = N;
-  const bool done = p >= w - 1 && (p - w + 1) % s == 0 && (p - w + 1) / s < N;
-  const int64_t e = done ? (p - w + 1) / s : -1;
+  const bool done = pe >= 0 && pe * s == p - w + 1 && pe < N;
+  const int64_t e = done ? pe : -1;
   if (blockIdx.x == 0) {
     if (threadIdx.x == 0) n_vis[b] = int32_t(nv);
     if (!done) return;
@@ -521,8 +522,8 @@ __global__ __launch_bounds__(kAppNT) void append_kernel(const T* __restrict__ x,
   }
   // workgroup 1: block mean of the block holding e
   if (!done || !reps) return;
-  const int64_t nb = (N + B - 1) / B;
-  const int64_t j = e / B;
+  const int64_t nb = idiv(N + B - 1, B);
+  const int64_t j = idiv(e, B);
   const int64_t i0 = j * B;
   const int cnt = int(imin64(N, i0 + B) - i0);
   const int slots = d_i / V;

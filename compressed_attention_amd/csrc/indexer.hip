@@ -336,25 +336,21 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
   const int qw = QPW == 4 ? wave : 0;           // this wave's query within the group
   const int nt0 = QPW == 4 ? 0 : wave;          // first subtile of this wave
   const int64_t q = int64_t(qg) * QPW + qw;
-  if (threadIdx.x < QPW) {
-    const int64_t qq = int64_t(qg) * QPW + threadIdx.x;
-    int v = 0;
-    if (qq < nq) {
-      const int64_t nvq = imin64(n, imax64(0, n_vis[b * nq + qq]));
-      v = int((nvq + B - 1) / B);
-    }
-    s_nb[threadIdx.x] = v;
-  }
-  __syncthreads();
-  int maxb = 0;
-#pragma unroll
-  for (int i = 0; i < QPW; ++i) maxb = max(maxb, s_nb[i]);
   const int64_t j_begin = int64_t(ch) * chunk;
-  const int64_t j_end = imin64(j_begin + chunk, maxb);
-  if (j_begin >= j_end) return;
+  const float* rb = reps + b * nb * D;
+  // The first tile of block means goes out before the visible counts are
+  // known (it is needed whenever this workgroup has any work).
+  auto load_tile = [&](int64_t j0, u32x4_t(&v)[PIECES]) {
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int p = threadIdx.x + 256 * u;
+      const int64_t j = j0 + p / (D / 4);
+      v[u] = j < nb ? ld16(rb + j * D + (p % (D / 4)) * 4) : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  u32x4_t v[PIECES];
+  load_tile(j_begin, v);
   const bool ok = q < nq;
-  const int my_nb = s_nb[qw];
-
   f32x4_t a[KQ];
   float wv[4];
   {
@@ -366,16 +362,25 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
 #pragma unroll
     for (int i = 0; i < 4; ++i) wv[i] = ok ? w_i[(b * nq + q) * 16 + 4 * g + i] : 0.f;
   }
-  const float* rb = reps + b * nb * D;
+  if (threadIdx.x < QPW) {
+    const int64_t qq = int64_t(qg) * QPW + threadIdx.x;
+    int nbq = 0;
+    if (qq < nq) {
+      const int64_t nvq = imin64(n, imax64(0, n_vis[b * nq + qq]));
+      nbq = int(idiv(nvq + B - 1, B));
+    }
+    s_nb[threadIdx.x] = nbq;
+  }
+  __syncthreads();
+  int maxb = 0;
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) maxb = max(maxb, s_nb[i]);
+  const int64_t j_end = imin64(j_begin + chunk, maxb);
+  if (j_begin >= j_end) return;
+  const int my_nb = s_nb[qw];
   for (int64_t j0 = j_begin; j0 < j_end; j0 += TB) {
     __syncthreads();
-    u32x4_t v[PIECES];
-#pragma unroll
-    for (int u = 0; u < PIECES; ++u) {
-      const int p = threadIdx.x + 256 * u;
-      const int64_t j = j0 + p / (D / 4);
-      v[u] = j < nb ? ld16(rb + j * D + (p % (D / 4)) * 4) : u32x4_t{0, 0, 0, 0};
-    }
+    if (j0 != j_begin) load_tile(j0, v);
 #pragma unroll
     for (int u = 0; u < PIECES; ++u) {
       const int p = threadIdx.x + 256 * u;
@@ -470,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void score_stage1_x3_kernel(const uint16_t*
     int v = 0;
     if (q < nq) {
       const int64_t nvq = imin64(n, imax64(0, n_vis[b * nq + q]));
-      v = int((nvq + B - 1) / B);
+      v = int(idiv(nvq + B - 1, B));
     }
     s_nb[threadIdx.x] = v;
   }
@@ -588,24 +593,21 @@ __global__ __launch_bounds__(256, 2) void score_stage1_x3_kernel(const uint16_t*
 // Candidate position j = slot*B + offset; visible candidates form a prefix.
 // ---------------------------------------------------------------------------
 template <int KS>
-__global__ __launch_bounds__(64) void score_stage2_mfma_kernel(const uint16_t* __restrict__ q_i,
-                                                               const uint16_t* __restrict__ k_i,
-                                                               const float* __restrict__ w_i,
-                                                               const int32_t* __restrict__ n_vis,
-                                                               const int32_t* __restrict__ blk, int64_t nq, int64_t n,
-                                                               int B, int m, int64_t ld, float* __restrict__ S2) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void score_stage2_mfma_kernel(
+    const uint16_t* __restrict__ q_i, const uint16_t* __restrict__ k_i, const float* __restrict__ w_i,
+    const int32_t* __restrict__ n_vis, const int32_t* __restrict__ blk, int64_t nq, int64_t n, int B, int m,
+    int64_t ld, float* __restrict__ S2) {
   constexpr int D = 32 * KS;
   const int64_t row = blockIdx.y;
   const int slot = blockIdx.x;
-  const int64_t b = row / nq;
-  const int bid = blk[row * m + slot];
-  if (bid < 0) return;
-  const int64_t nv = imin64(n, imax64(0, n_vis[row]));
-  const int64_t e_begin = int64_t(bid) * B;
-  const int64_t e_end = imin64(e_begin + B, nv);
-  if (e_begin >= e_end) return;
+  const int64_t b = idiv(row, nq);
   const int lane = threadIdx.x;
   const int g = lane >> 4, r16 = lane & 15;
+  // Every load is issued before any branch: query, weights, block id and
+  // visible count together, then the block's first 64 keys as soon as its
+  // id arrives (rows past the cache end, or of an empty slot, read a valid
+  // row and are never stored).  A wave at one block per SIMD needs no
+  // register economy, so the loads are not interleaved with the MFMAs.
   u32x4_t a[KS];
   const uint16_t* qp = q_i + (row * 16 + r16) * D + 8 * g;
 #pragma unroll
@@ -613,16 +615,27 @@ __global__ __launch_bounds__(64) void score_stage2_mfma_kernel(const uint16_t* _
   float wv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) wv[i] = w_i[row * 16 + 4 * g + i];
+  const int bid = blk[row * m + slot];
+  const int64_t nv = imin64(n, imax64(0, n_vis[row]));
+  const int64_t e_begin = int64_t(max(bid, 0)) * B;
+  const int64_t e_end = bid < 0 ? e_begin : imin64(e_begin + B, nv);
   const uint16_t* kb = k_i + b * n * D + 8 * g;
   float* out = S2 + row * ld + int64_t(slot) * B;
-  for (int64_t e0 = e_begin; e0 < e_end; e0 += 64) {
-    u32x4_t bf[4][KS];
+  u32x4_t bf[4][KS];
+  auto load_keys = [&](int64_t e0) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int64_t e = e0 + 16 * nt + r16;
-      const bool ok = e < e_end;
+      const int64_t e = imax64(0, imin64(e0 + 16 * nt + r16, n - 1));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bf[nt][ks] = ok ? ld16(kb + e * D + 32 * ks) : u32x4_t{0, 0, 0, 0};
+      for (int ks = 0; ks < KS; ++ks) bf[nt][ks] = ld16(kb + e * D + 32 * ks);
+    }
+  };
+  load_keys(e_begin);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int64_t e0 = e_begin; e0 < e_end; e0 += 64) {
+    if (e0 != e_begin) {
+      load_keys(e0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     float v[4];
 #pragma unroll
@@ -780,7 +793,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(const TQ* __restrict__ 
                                                          int64_t ld, float* __restrict__ S) {
   extern __shared__ float qs[];  // [h_i][d_i] then [h_i] weights
   const int64_t row = blockIdx.y;
-  const int64_t b = row / nq;
+  const int64_t b = idiv(row, nq);
   for (int i = threadIdx.x; i < h_i * d_i; i += blockDim.x) qs[i] = to_f(q_i[row * h_i * d_i + i]);
   for (int i = threadIdx.x; i < h_i; i += blockDim.x) qs[h_i * d_i + i] = w_i[row * h_i + i];
   __syncthreads();
@@ -791,7 +804,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(const TQ* __restrict__ 
     if (j >= nv) return;
     krow = j;
   } else if (MODE == 1) {
-    if (j >= (nv + B - 1) / B) return;
+    if (j >= idiv(nv + B - 1, B)) return;
     krow = j;
   } else {
     const int64_t slot = j / B;
@@ -816,21 +829,19 @@ __global__ __launch_bounds__(256) void score_valu_kernel(const TQ* __restrict__ 
 // ---------------------------------------------------------------------------
 // Number of valid candidates of a row.  MODE 0: visible entries; MODE 1:
 // blocks whose first entry is visible; MODE 2: visible entries inside the
-// chosen blocks (a prefix of slot space, see the stage-2 kernel).
+// chosen blocks (a prefix of slot space, see the stage-2 kernel), summed by
+// every wave on its own from the row's block ids (no barrier).
 template <int MODE>
-HATTN_DEV int row_valid_count(const int32_t* n_vis, const int32_t* blk, int64_t row, int64_t n, int B, int m, int* red) {
+HATTN_DEV int row_valid_count(const int32_t* n_vis, const int32_t* bids, int64_t row, int64_t n, int B, int m) {
   const int64_t nv = imin64(n, imax64(0, n_vis[row]));
   if (MODE == 0) return int(nv);
-  if (MODE == 1) return int((nv + B - 1) / B);
-  int c = 0;
-  for (int s = threadIdx.x; s < m; s += blockDim.x) {
-    const int bid = blk[row * m + s];
-    if (bid >= 0) c += int(imax64(0, imin64(B, nv - int64_t(bid) * B)));
+  if (MODE == 1) return int(idiv(nv + B - 1, B));
+  uint32_t c = 0;
+  for (int s = threadIdx.x & (kWave - 1); s < m; s += kWave) {
+    const int bid = bids[s];
+    if (bid >= 0) c += uint32_t(imax64(0, imin64(B, nv - int64_t(bid) * B)));
   }
-  c = wave_sum(c);
-  if ((threadIdx.x & 63) == 0) atomicAdd(red, c);
-  __syncthreads();
-  return *red;
+  return int(wave_total(c));
 }
 
 template <int MODE>
@@ -843,30 +854,48 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
                                                              int32_t* __restrict__ inv_list, int64_t nq,
                                                              int64_t nb) {
   __shared__ SelectShared<kSelNT> sh;
-  __shared__ int cnt;
-  __shared__ int32_t bsh[MODE == 2 ? kSelNT : 1];  // chosen block ids, for the emission
+  __shared__ int32_t bsh[MODE == 2 ? kSelNT : 1];  // chosen block ids
   const int64_t row = blockIdx.x;
-  if (threadIdx.x == 0) cnt = 0;
   const int32_t* brow = blk + row * m;
-  if (MODE == 2 && m <= kSelNT)
+  // Block and token rows: the scores of every slot a row can have are loaded
+  // at once, before the valid count is known (slots past it are masked
+  // below), so the two loads overlap.  Flat rows load only what is visible.
+  float v[kSelIT];
+  SelSeg sg;
+  if (MODE != 0) {
+    const int cap = MODE == 1 ? int(imin64(kSelCap, idiv(n + B - 1, B))) : min(kSelCap, m * B);
+    sg = wave_segment<kSelNT>(cap);
+    seg_load_scores(S + row * ld, sg, v);
+  }
+  const bool blk_lds = m <= kSelNT;
+  if (MODE == 2 && blk_lds)
     for (int s = threadIdx.x; s < m; s += kSelNT) bsh[s] = brow[s];
+  select_clear(sh);
   __syncthreads();
-  const int nvalid = min(kSelCap, row_valid_count<MODE>(n_vis, blk, row, n, B, m, &cnt));
-  const SelSeg sg = wave_segment<kSelNT>(nvalid);
+  const int nvalid = min(kSelCap, row_valid_count<MODE>(n_vis, blk_lds ? bsh : brow, row, n, B, m));
+  if (MODE == 0) {
+    sg = wave_segment<kSelNT>(nvalid);
+    seg_load_scores(S + row * ld, sg, v);
+  }
   uint32_t kc[kSelIT];
-  seg_keys_from_scores(S + row * ld, sg, kc);
-  radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
+  seg_keys_masked(v, sg, nvalid, kc);
+  const SelThr st = radix_threshold<kSelNT, kSelIT, true>(kc, sg.iters, k, sh);
   int32_t* orow = idx + row * k;
   float* scrow = score_out ? score_out + row * k : nullptr;
-  const bool blk_lds = m <= kSelNT;
-  const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int i, uint32_t key, int) {
-    int32_t v = i;
-    if (MODE == 2) v = (blk_lds ? bsh[i / B] : brow[i / B]) * B + (i % B);
-    orow[slot] = v;
+  const bool pow2 = (B & (B - 1)) == 0;
+  const int lgB = __builtin_ctz(unsigned(B));
+  const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
+    int32_t val = i;
+    if (MODE == 2) {
+      const int s = pow2 ? i >> lgB : i / B;
+      const int off = pow2 ? i & (B - 1) : i - s * B;
+      val = (blk_lds ? bsh[s] : brow[s]) * B + off;
+    }
+    orow[slot] = val;
     if (scrow) scrow[slot] = key_to_float(key);
     if (MODE == 1 && inv_cnt) {
       // block-major stage 2: append (row, slot) to the chosen block's list
-      const int64_t bucket = (row / nq) * nb + i;
+      const int64_t bucket = idiv(row, nq) * nb + i;
       const int pos = atomicAdd(&inv_cnt[bucket], 1);
       inv_list[bucket * nq + pos] = int32_t(row * m + slot);
     }
@@ -920,8 +949,8 @@ __global__ __launch_bounds__(kSampNT, 4) void select_sampled_kernel(const float*
     const SelSeg sg = wave_segment<kSampNT>(nv);
     uint32_t kc[kSelIT];
     seg_keys_from_scores(srow, sg, kc);
-    radix_threshold<kSampNT, kSelIT>(kc, sg.iters, k, sh);
-    const int chosen = emit_selected<kSampNT, kSelIT>(kc, sg, sh, [&](int slot, int i, uint32_t key, int) {
+    const SelThr st = radix_threshold<kSampNT, kSelIT>(kc, sg.iters, k, sh);
+    const int chosen = emit_selected<kSampNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
       orow[slot] = i;
       if (scrow) scrow[slot] = key_to_float(key);
     });
@@ -953,8 +982,8 @@ __global__ __launch_bounds__(kSampNT, 4) void select_sampled_kernel(const float*
   const int p0 = wave * segw, p1 = min(nv, p0 + segw);
   bool done = false;
   for (int attempt = 0; attempt < 4 && !done; ++attempt) {
-    radix_threshold<kSampNT, kSelIT>(skc, ssg.iters, r, sh);
-    const uint32_t tau = sh.thr;  // key of the r-th largest sample (0: all)
+    const SelThr st = radix_threshold<kSampNT, kSelIT>(skc, ssg.iters, r, sh);
+    const uint32_t tau = st.thr;  // key of the r-th largest sample (0: all)
     // 2. collect keys >= tau of this wave's segment, in position order
     uint32_t* rk = rkey + wave * kRegion;
     uint16_t* rp = rpos + wave * kRegion;
@@ -1034,9 +1063,9 @@ __global__ __launch_bounds__(kSampNT, 4) void select_sampled_kernel(const float*
   const SelSeg csg = wave_segment<kSampNT>(kSampleN);
   uint32_t ckc[kSelIT];
   seg_keys_from_u32(rkey, csg, ckc);
-  radix_threshold<kSampNT, kSelIT>(ckc, csg.iters, k, sh);
+  const SelThr st = radix_threshold<kSampNT, kSelIT>(ckc, csg.iters, k, sh);
   // candidate i lies in the region (and segment) of the wave that emits it
-  const int chosen = emit_selected<kSampNT, kSelIT>(ckc, csg, sh, [&](int slot, int i, uint32_t key, int) {
+  const int chosen = emit_selected<kSampNT, kSelIT>(ckc, csg, sh, st, [&](int slot, int i, uint32_t key, int) {
     orow[slot] = p0 + int(rpos[i]);
     if (scrow) scrow[slot] = key_to_float(key);
   });
@@ -1065,10 +1094,10 @@ __global__ __launch_bounds__(kSelNT) void select_segment_kernel(const float* __r
   const SelSeg sg = wave_segment<kSelNT>(cnt);
   uint32_t kc[kSelIT];
   seg_keys_from_scores(S + row * ld + p0, sg, kc);
-  radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
+  const SelThr st = radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
   uint32_t* ok = ckey + (row * nseg + s) * int64_t(kp);
   int32_t* op = cpos + (row * nseg + s) * int64_t(kp);
-  const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int i, uint32_t key, int) {
+  const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
     ok[slot] = key;
     op[slot] = int32_t(p0 + i);
   });
@@ -1108,11 +1137,11 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
       pc[it] = in ? ip[i] : -1;
     }
   }
-  radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
+  const SelThr st = radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
   if (nout == 1) {
     int32_t* orow = idx + row * k;
     float* scrow = score_out ? score_out + row * k : nullptr;
-    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int, uint32_t key, int it) {
+    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int, uint32_t key, int it) {
       orow[slot] = pc[it];
       if (scrow) scrow[slot] = key_to_float(key);
     });
@@ -1123,7 +1152,7 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
   } else {
     uint32_t* ok = okey + (row * nout + grp) * int64_t(kp);
     int32_t* op = opos + (row * nout + grp) * int64_t(kp);
-    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, [&](int slot, int, uint32_t key, int it) {
+    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int, uint32_t key, int it) {
       ok[slot] = key;
       op[slot] = pc[it];
     });

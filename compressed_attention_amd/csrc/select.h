@@ -13,13 +13,17 @@
 //
 // Method: an MSB radix search (12, 10, 10 bits) finds the threshold key T and
 // how many keys equal to T are still needed.  Each pass adds the key digits
-// into an LDS histogram; the threshold bin is then located in two levels (the
-// 4-bin sums are added into 64 coarse bins, wave 0 scans the coarse bins and
-// then the 64 fine bins of the chosen one, lanes reading adjacent words), so
-// a pass costs three barriers.  Emission: per-wave counts of keys above /
-// equal to T give every wave its output base; inside a wave, ballots give
-// each chosen key its slot, so the result is deterministic and needs no
-// sorting.
+// into an LDS histogram (pass 0 in words [0, 4096), pass 1 in [4096, 5120),
+// pass 2 in [0, 1024), which pass 1 clears, so no pass waits for a clear).
+// The threshold bin is then found without a further barrier: each thread
+// owns a run of adjacent bins and publishes its wave's count; every wave
+// reads the wave counts lane-parallel, picks the wave whose runs hold the
+// crossing, re-reads that wave's runs, and locates the bin with DPP prefix
+// sums and ballots.  Every thread thus knows the digit, and a pass costs two
+// barriers.  Emission: per-wave counts of keys above / equal to T give every
+// wave its output base (lane-parallel prefix sums over the waves); inside a
+// wave, ballots give each chosen key its slot, so the result is
+// deterministic and needs no sorting.
 #pragma once
 
 #include "common.h"
@@ -30,13 +34,16 @@ constexpr int kSelIT = 16;  // default keys per lane: rows of up to 16 * NT keys
 
 template <int NT>
 struct SelectShared {
-  __align__(16) uint32_t hist[4096];
-  uint32_t coarse[64];
+  __align__(16) uint32_t hist[4096 + 1024];
+  __align__(16) uint32_t wtot[NT / kWave];
   int wsum[2][NT / kWave];
+};
+
+// The selection's threshold: every key > thr, plus the first need_eq keys
+// equal to thr (in position order).
+struct SelThr {
   uint32_t thr;
   int need_eq;
-  int above;
-  int digit;
 };
 
 // This wave's contiguous segment of a row of n keys.
@@ -71,6 +78,29 @@ HATTN_DEV void seg_keys_from_scores(const float* __restrict__ src, const SelSeg&
   for (int it = 0; it < IT; ++it) {
     const int i = sg.p0 + it * kWave + lane;
     kc[it] = it < sg.iters && i < sg.p1 ? order_key(v[it]) : 0u;
+  }
+}
+
+// Raw fp32 scores of the segment (loads only; positions beyond the row read
+// 0).  seg_keys_masked turns them into keys once they have arrived.
+template <int IT>
+HATTN_DEV void seg_load_scores(const float* __restrict__ src, const SelSeg& sg, float (&v)[IT]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = sg.p0 + it * kWave + lane;
+    v[it] = it < sg.iters && i < sg.p1 ? src[i] : 0.f;
+  }
+}
+
+// Keys of positions below nvalid; 0 (no candidate) elsewhere.
+template <int IT>
+HATTN_DEV void seg_keys_masked(const float (&v)[IT], const SelSeg& sg, int nvalid, uint32_t (&kc)[IT]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = sg.p0 + it * kWave + lane;
+    kc[it] = it < sg.iters && i < sg.p1 && i < nvalid ? order_key(v[it]) : 0u;
   }
 }
 
@@ -113,104 +143,117 @@ HATTN_DEV void load_score_keys(const float* __restrict__ src, int n, uint32_t* k
   for (int i = n4 + threadIdx.x; i < n; i += NT) keys[i] = order_key(src[i]);
 }
 
-// Finds (thr, need_eq): select {key > thr} plus the first need_eq keys ==
-// thr, over the keys every thread holds in kc[0..iters).  If at most k keys
-// are valid, thr = 0 and need_eq = 0 (all valid keys); k <= 0 selects
-// nothing.  Ends with a barrier; sh.thr / sh.need_eq are then readable.
-template <int NT, int IT>
-HATTN_DEV void radix_threshold(const uint32_t (&kc)[IT], int iters, int k, SelectShared<NT>& sh) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  if (k <= 0) {
-    if (threadIdx.x == 0) {
-      sh.thr = 0xffffffffu;
-      sh.need_eq = 0;
-    }
-    __syncthreads();
-    return;
-  }
+// Zeroes the histogram.  A caller may do this early (e.g. while its key
+// loads are in flight) and then pass CLEARED = true to radix_threshold; a
+// barrier must separate the two.
+template <int NT>
+HATTN_DEV void select_clear(SelectShared<NT>& sh) {
   const u32x4_t z4 = {0u, 0u, 0u, 0u};
-  for (int i = threadIdx.x * 4; i < 4096; i += NT * 4) *reinterpret_cast<u32x4_t*>(sh.hist + i) = z4;
-  for (int i = threadIdx.x; i < 64; i += NT) sh.coarse[i] = 0u;
-  __syncthreads();
+  for (int i = threadIdx.x * 4; i < 4096 + 1024; i += NT * 4) *reinterpret_cast<u32x4_t*>(sh.hist + i) = z4;
+}
+
+// This wave's index as a scalar (uniform) value.
+HATTN_DEV int wave_index() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave); }
+
+// Sum over the wave of x, in every lane.
+HATTN_DEV uint32_t wave_total(uint32_t x) { return uint32_t(__builtin_amdgcn_readlane(int(wave_prefix_incl(x)), 63)); }
+
+// Lowest set lane of a nonzero ballot, as a scalar.
+HATTN_DEV int first_lane(uint64_t m) { return __builtin_amdgcn_readfirstlane(int(__builtin_ctzll(m))); }
+
+// Finds the threshold over the keys every thread holds in kc[0..iters): the
+// k largest valid keys are {key > thr} plus the first need_eq keys == thr.
+// If at most k keys are valid, thr = 0 and need_eq = 0 (all valid keys);
+// k <= 0 selects nothing.  Every thread returns the same value.  The
+// histogram must be zero on entry (CLEARED: the caller cleared it and
+// passed a barrier since; otherwise this clears it); it is left dirty.
+// sh.wtot is reused by the next call only after that call's first barrier.
+template <int NT, int IT, bool CLEARED = false>
+HATTN_DEV SelThr radix_threshold(const uint32_t (&kc)[IT], int iters, int k, SelectShared<NT>& sh) {
+  constexpr int NW = NT / kWave;
+  static_assert(NT >= 256 && NT <= 1024 && 4096 % NT == 0, "runs of whole bins per thread");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = wave_index();
+  if (k <= 0) return SelThr{0xffffffffu, 0};
+  if (!CLEARED) {
+    __syncthreads();  // a previous selection may still be reading the histogram
+    select_clear(sh);
+    __syncthreads();
+  }
   uint32_t prefix = 0, hmask = 0;
-  int remaining = k;
+  uint32_t remaining = uint32_t(k);
   constexpr int kShift[3] = {20, 10, 0};
   constexpr int kWidth[3] = {12, 10, 10};
+  constexpr int kBase[3] = {0, 4096, 0};
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = kShift[pass];
     const int nbins = 1 << kWidth[pass];
+    const int bpt = nbins / NT > 0 ? nbins / NT : 1;  // bins per owning thread
+    uint32_t* hist = sh.hist + kBase[pass];
     // 1. histogram of this pass's digit over the keys that match the prefix
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       if (it < iters) {
         const uint32_t key = kc[it];
-        if (key != 0u && (key & hmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nbins - 1)], 1u);
+        if (key != 0u && (key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & (nbins - 1)], 1u);
       }
     }
     __syncthreads();
-    // 2. coarse bins: each holds 64 fine bins (16 quads)
-    for (int q = threadIdx.x; q * 4 < nbins; q += NT) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sh.hist + 4 * q);
-      const uint32_t sum = v[0] + v[1] + v[2] + v[3];
-      if (sum) atomicAdd(&sh.coarse[q >> 4], sum);
+    // 2. thread t owns bins [bpt*t, bpt*(t+1)) of this pass; wave totals.
+    //    Pass 1 also clears pass 0's words, which pass 2 reuses.
+    {
+      uint32_t own = 0;
+      if (bpt * int(threadIdx.x) < nbins)
+        for (int j = 0; j < bpt; ++j) own += hist[bpt * threadIdx.x + j];
+      if (pass == 1) {
+        const u32x4_t z4 = {0u, 0u, 0u, 0u};
+        for (int i = threadIdx.x * 4; i < 4096; i += NT * 4) *reinterpret_cast<u32x4_t*>(sh.hist + i) = z4;
+      }
+      const uint32_t incl = wave_prefix_incl(own);
+      if (lane == kWave - 1) sh.wtot[wave] = incl;
     }
     __syncthreads();
-    // 3. wave 0: crossing coarse bin, then crossing fine bin inside it
-    if (wave == 0) {
-      const int c = int(sh.coarse[lane]);
-      int suf = c;  // keys in coarse bins >= lane
+    // 3. every wave: the crossing wave, then the crossing thread and bin
+    const uint32_t wt = lane < NW ? sh.wtot[lane] : 0u;
+    const uint32_t wincl = wave_prefix_incl(wt);
+    const uint32_t total = uint32_t(__builtin_amdgcn_readlane(int(wincl), NW - 1));
+    if (pass == 0 && total <= uint32_t(k)) return SelThr{0u, 0};  // every valid key is chosen
+    const uint32_t above_w = total - wincl;  // keys in waves above lane w's wave
+    const int wc = first_lane(ballot(lane < NW && above_w < remaining && above_w + wt >= remaining));
+    const uint32_t above_wave = uint32_t(__builtin_amdgcn_readlane(int(above_w), wc));
+    const int t = wc * kWave + lane;  // a thread of the crossing wave
+    uint32_t c[4096 / 256];
+    uint32_t own = 0;
 #pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int z = __shfl_down(suf, off);
-        if (lane + off < kWave) suf += z;
-      }
-      const int total = __shfl(suf, 0);
-      if (pass == 0 && total <= k) {
-        if (lane == 0) sh.digit = -1;  // every valid key is chosen
-      } else {
-        const uint64_t cross = ballot(suf >= remaining && suf - c < remaining);
-        const int cl = cross ? __ffsll((unsigned long long)cross) - 1 : 0;
-        const int above_c = __shfl(suf - c, cl);
-        const int f = int(sh.hist[cl * 64 + lane]);
-        int fs = f;  // keys in fine bins >= lane inside coarse bin cl
+    for (int j = 0; j < 4096 / 256; ++j) {
+      c[j] = j < bpt && bpt * t < nbins ? hist[bpt * t + j] : 0u;
+      own += c[j];
+    }
+    const uint32_t incl = wave_prefix_incl(own);
+    const uint32_t tot_w = uint32_t(__builtin_amdgcn_readlane(int(incl), kWave - 1));
+    const uint32_t above_run = above_wave + (tot_w - incl);
+    const int lc = first_lane(ballot(above_run < remaining && above_run + own >= remaining));
+    int digit = 0;
+    uint32_t above = 0;
+    {
+      uint32_t cum = above_run;
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-          const int z = __shfl_down(fs, off);
-          if (lane + off < kWave) fs += z;
+      for (int j = 4096 / 256 - 1; j >= 0; --j) {
+        if (j < bpt && cum < remaining && cum + c[j] >= remaining) {
+          digit = bpt * t + j;
+          above = cum;
         }
-        if (above_c + fs >= remaining && above_c + fs - f < remaining) {
-          sh.digit = cl * 64 + lane;
-          sh.above = above_c + fs - f;
-        }
-      }
-      // clear for the next pass (this wave has finished reading both arrays)
-      if (pass < 2) {
-        for (int i = lane * 4; i < nbins; i += 4 * kWave) *reinterpret_cast<u32x4_t*>(sh.hist + i) = z4;
-        sh.coarse[lane] = 0u;
+        cum += j < bpt ? c[j] : 0u;
       }
     }
-    __syncthreads();
-    const int digit = sh.digit;
-    if (digit < 0) {
-      __syncthreads();  // all threads have read sh.digit
-      if (threadIdx.x == 0) {
-        sh.thr = 0u;
-        sh.need_eq = 0;
-      }
-      __syncthreads();
-      return;
-    }
+    digit = __builtin_amdgcn_readlane(digit, lc);
+    above = uint32_t(__builtin_amdgcn_readlane(int(above), lc));
     prefix |= uint32_t(digit) << shift;
     hmask |= uint32_t(nbins - 1) << shift;
-    remaining -= sh.above;
+    remaining -= above;
   }
-  if (threadIdx.x == 0) {
-    sh.thr = prefix;
-    sh.need_eq = remaining;
-  }
-  __syncthreads();
+  return SelThr{prefix, int(remaining)};
 }
 
 // Emits the chosen positions in increasing order from the same register
@@ -218,12 +261,13 @@ HATTN_DEV void radix_threshold(const uint32_t (&kc)[IT], int iters, int k, Selec
 // in kc[it] of the calling lane) with its output slot; returns the number
 // chosen.  Does not end with a barrier.
 template <int NT, int IT, typename Emit>
-HATTN_DEV int emit_selected(const uint32_t (&kc)[IT], const SelSeg& sg, SelectShared<NT>& sh, Emit emit) {
+HATTN_DEV int emit_selected(const uint32_t (&kc)[IT], const SelSeg& sg, SelectShared<NT>& sh, SelThr st,
+                            Emit emit) {
   constexpr int NW = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const uint32_t thr = sh.thr;
-  const int need_eq = sh.need_eq;
+  const int wave = wave_index();
+  const uint32_t thr = st.thr;
+  const int need_eq = st.need_eq;
   int gt = 0, eq = 0;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -237,21 +281,17 @@ HATTN_DEV int emit_selected(const uint32_t (&kc)[IT], const SelSeg& sg, SelectSh
     sh.wsum[1][wave] = eq;
   }
   __syncthreads();
-  // Per-wave bases: equal keys and chosen elements in earlier waves.
-  int eqb = 0, outb = 0, my_eq_base = 0, my_out_base = 0;
-  for (int w = 0; w < NW; ++w) {
-    const int g = sh.wsum[0][w], e = sh.wsum[1][w];
-    const int take_eq = max(0, min(e, need_eq - eqb));
-    if (w == wave) {
-      my_eq_base = eqb;
-      my_out_base = outb;
-    }
-    outb += g + take_eq;
-    eqb += e;
-  }
-  const int chosen_total = outb;
-  int eq_seen = my_eq_base;
-  int out = my_out_base;
+  // Per-wave bases, lane w standing for wave w: equal keys in earlier waves
+  // (eqb), the equal keys wave w takes, and chosen keys in earlier waves.
+  const int g = lane < NW ? sh.wsum[0][lane] : 0;
+  const int e = lane < NW ? sh.wsum[1][lane] : 0;
+  const int e_incl = int(wave_prefix_incl(uint32_t(e)));
+  const int eqb = e_incl - e;
+  const int take_eq = max(0, min(e, need_eq - eqb));
+  const int out_incl = int(wave_prefix_incl(uint32_t(g + take_eq)));
+  const int chosen_total = __builtin_amdgcn_readlane(out_incl, NW - 1);
+  int eq_seen = wave > 0 ? __builtin_amdgcn_readlane(e_incl, wave - 1) : 0;
+  int out = wave > 0 ? __builtin_amdgcn_readlane(out_incl, wave - 1) : 0;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     if (it < sg.iters) {
