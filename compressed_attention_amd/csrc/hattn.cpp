@@ -4,6 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+#include <initializer_list>
+
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
@@ -138,6 +141,15 @@ const char* hattn_last_error(void) { return g_err; }
 
 int hattn_abi_version(void) { return 1; }
 
+// Arrays that kernels access with 16-byte vector loads or stores; NULL passes.
+static bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15u) return false;
+  return true;
+}
+#define HATTN_REQUIRE_ALIGNED(fn, ...) \
+  if (!aligned16({__VA_ARGS__})) return fail(HATTN_ERR_ARG, "%s: arrays must be 16-byte aligned", fn)
+
 hattn_status_t hattn_compress(int dtype, const void* x, int64_t bt, int64_t L, int32_t C, const float* logits,
                               const float* pos_bias, int32_t w, int32_t stride, int64_t e_begin, int64_t e_end,
                               void* y, void* stream) {
@@ -153,6 +165,7 @@ hattn_status_t hattn_compress(int dtype, const void* x, int64_t bt, int64_t L, i
                 (long long)e_end, (long long)N);
   if (bt == 0 || e_end == e_begin) return ok();
   if (!x || !y) return fail(HATTN_ERR_ARG, "compress: NULL x or y");
+  HATTN_REQUIRE_ALIGNED("compress", x, y);
   return hip_status(hattn::launch_compress(dtype, x, bt, L, C, logits, pos_bias, w, stride, N, e_begin, e_end, y,
                                            (hipStream_t)stream),
                     "compress");
@@ -179,6 +192,7 @@ static hattn_status_t check_index_args(const char* fn, int dtype, const void* q_
   if (h_i * d_i > 8192) return fail(HATTN_ERR_UNSUPPORTED, "%s: h_i*d_i > 8192", fn);
   if (bt * nq > 0 && (!q_i || !w_i || !n_vis || !idx || (n > 0 && !k_i)))
     return fail(HATTN_ERR_ARG, "%s: NULL required pointer", fn);
+  HATTN_REQUIRE_ALIGNED(fn, q_i, k_i, w_i);
   return HATTN_OK;
 }
 
@@ -189,6 +203,7 @@ hattn_status_t hattn_index_topk(int dtype, const void* q_i, const void* k_i, con
   if (st != HATTN_OK) return st;
   hattn::IndexArgs a{dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n};
   const size_t need = bt * nq > 0 ? hattn::flat_topk_ws_bytes(a, k) : 0;
+  HATTN_REQUIRE_ALIGNED("index_topk", ws);
   if (ws_query(ws, ws_bytes, need, &st)) return st;
   if (bt * nq == 0) return ok();
   return hip_status(hattn::launch_flat_topk(a, k, idx, score, ws, (hipStream_t)stream), "index_topk");
@@ -204,6 +219,7 @@ hattn_status_t hattn_hisa_pool(int dtype, const void* k_i, int64_t bt, int64_t n
   if (j_begin < 0 || j_end < j_begin || j_end > nb) return fail(HATTN_ERR_ARG, "hisa_pool: block range outside [0, %lld]", (long long)nb);
   if (bt == 0 || j_end == j_begin) return ok();
   if (!k_i || !reps) return fail(HATTN_ERR_ARG, "hisa_pool: NULL pointer");
+  HATTN_REQUIRE_ALIGNED("hisa_pool", k_i, reps);
   return hip_status(hattn::launch_pool(dtype, k_i, bt, n, d_i, B, j_begin, j_end, reps, (hipStream_t)stream),
                     "hisa_pool");
 }
@@ -220,6 +236,7 @@ hattn_status_t hattn_hisa_topk(int dtype, const void* q_i, const void* k_i, cons
   if (bt * nq > 0 && n > 0 && !reps) return fail(HATTN_ERR_ARG, "hisa_topk: NULL reps");
   hattn::IndexArgs a{dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n};
   const size_t need = bt * nq > 0 ? hattn::hisa_topk_ws_bytes(a, B, m, k) : 0;
+  HATTN_REQUIRE_ALIGNED("hisa_topk", reps, ws);
   if (ws_query(ws, ws_bytes, need, &st)) return st;
   if (bt * nq == 0) return ok();
   return hip_status(hattn::launch_hisa_topk(a, reps, B, m, k, idx, blk, ws, (hipStream_t)stream), "hisa_topk");
@@ -235,6 +252,7 @@ static hattn_status_t attn_common(const char* fn, hattn::AttnArgs& a, void* ws, 
   const int64_t rows = a.bt * a.nq;
   if (rows > 0 && (!a.q || !a.raw_kv || !a.q_pos || !a.out || (a.n > 0 && !a.ckv)))
     return fail(HATTN_ERR_ARG, "%s: NULL required pointer", fn);
+  HATTN_REQUIRE_ALIGNED(fn, a.q, a.ckv, a.raw_kv, a.out, ws);
   const size_t need = rows > 0 ? hattn::attn_ws_bytes(a) : 0;
   hattn_status_t st;
   if (ws_query(ws, ws_bytes, need, &st)) return st;
@@ -280,6 +298,7 @@ hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, in
     return fail(HATTN_ERR_ARG, "decode_append: bad B=%d or d_i=%d", B, d_i);
   if (bt == 0) return ok();
   if (!raw_kv || !q_pos || !ckv || !n_vis) return fail(HATTN_ERR_ARG, "decode_append: NULL pointer");
+  HATTN_REQUIRE_ALIGNED("decode_append", raw_kv, ckv, k_i);
   const int64_t N = (L - w) / stride + 1;
   if (N > INT32_MAX) return fail(HATTN_ERR_ARG, "decode_append: too many entries");
   return hip_status(hattn::launch_append(dtype, raw_kv, bt, L, C, logits, pos_bias, w, stride, q_pos, ckv, N, n_vis,

@@ -33,6 +33,14 @@ HATTN_DEV float to_f(uint16_t x) { return bf16_to_f32(x); }
 
 // Decodes a linear block id so that the 8 XCDs each sweep whole key chunks:
 // the workgroups resident on one XCD share a chunk and re-read it from L2.
+// Four consecutive elements as fp32 (8-byte aligned bf16 / 16-byte aligned
+// fp32 source).
+HATTN_DEV void load4_f32(const float* p, f32x4_t& v) { v = *reinterpret_cast<const f32x4_t*>(p); }
+HATTN_DEV void load4_f32(const uint16_t* p, f32x4_t& v) {
+  const uint2 r = *reinterpret_cast<const uint2*>(p);
+  v = f32x4_t{bf16lo(r.x), bf16hi(r.x), bf16lo(r.y), bf16hi(r.y)};
+}
+
 HATTN_DEV bool xcd_decode(int id, int ngroups, int nchunks, int* group, int* chunk) {
   const int xcd = id & 7;
   const int slot = id >> 3;
@@ -354,13 +362,21 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
   f32x4_t a[KQ];
   float wv[4];
   {
+    // 4 consecutive elements per (lane, kq): one 8-byte (bf16) or 16-byte
+    // (fp32) load each, not four scalar ones
     const TQ* qp = q_i + ((b * nq + (ok ? q : 0)) * 16 + r16) * D + 4 * g;
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq)
+    for (int kq = 0; kq < KQ; ++kq) load4_f32(qp + 16 * kq, a[kq]);
+    if (!ok)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a[kq][j] = ok ? to_f(qp[16 * kq + j]) : 0.f;
+      for (int kq = 0; kq < KQ; ++kq) a[kq] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[i] = ok ? w_i[(b * nq + q) * 16 + 4 * g + i] : 0.f;
+    for (int i = 0; i < 4; ++i) wv[i] = 0.f;
+    if (ok) {
+      const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(w_i + (b * nq + q) * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] = w4[i];
+    }
   }
   if (threadIdx.x < QPW) {
     const int64_t qq = int64_t(qg) * QPW + threadIdx.x;
@@ -612,9 +628,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const uint16_t* qp = q_i + (row * 16 + r16) * D + 8 * g;
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) a[ks] = ld16(qp + 32 * ks);
-  float wv[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) wv[i] = w_i[row * 16 + 4 * g + i];
+  const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(w_i + row * 16 + 4 * g);
   const int bid = blk[row * m + slot];
   const int64_t nv = imin64(n, imax64(0, n_vis[row]));
   const int64_t e_begin = int64_t(max(bid, 0)) * B;
@@ -828,9 +842,11 @@ __global__ __launch_bounds__(256) void score_valu_kernel(const TQ* __restrict__ 
 // Selection kernels.
 // ---------------------------------------------------------------------------
 // Number of valid candidates of a row.  MODE 0: visible entries; MODE 1:
-// blocks whose first entry is visible; MODE 2: visible entries inside the
-// chosen blocks (a prefix of slot space, see the stage-2 kernel), summed by
-// every wave on its own from the row's block ids (no barrier).
+// blocks whose first entry is visible; MODE 2 / 3: visible entries inside
+// the chosen blocks (a prefix of slot space, see the stage-2 kernel), summed
+// by every wave on its own from the row's block ids (no barrier).  MODE 2
+// keeps the block ids in LDS (m <= kSelNT), MODE 3 reads them from global
+// memory.
 template <int MODE>
 HATTN_DEV int row_valid_count(const int32_t* n_vis, const int32_t* bids, int64_t row, int64_t n, int B, int m) {
   const int64_t nv = imin64(n, imax64(0, n_vis[row]));
@@ -854,6 +870,7 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
                                                              int32_t* __restrict__ inv_list, int64_t nq,
                                                              int64_t nb) {
   __shared__ SelectShared<kSelNT> sh;
+  constexpr bool TOK = MODE >= 2;                 // token rows (stage 2)
   __shared__ int32_t bsh[MODE == 2 ? kSelNT : 1];  // chosen block ids
   const int64_t row = blockIdx.x;
   const int32_t* brow = blk + row * m;
@@ -863,16 +880,15 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
   float v[kSelIT];
   SelSeg sg;
   if (MODE != 0) {
-    const int cap = MODE == 1 ? int(imin64(kSelCap, idiv(n + B - 1, B))) : min(kSelCap, m * B);
+    const int cap = TOK ? min(kSelCap, m * B) : int(imin64(kSelCap, idiv(n + B - 1, B)));
     sg = wave_segment<kSelNT>(cap);
     seg_load_scores(S + row * ld, sg, v);
   }
-  const bool blk_lds = m <= kSelNT;
-  if (MODE == 2 && blk_lds)
+  if (MODE == 2)
     for (int s = threadIdx.x; s < m; s += kSelNT) bsh[s] = brow[s];
   select_clear(sh);
   __syncthreads();
-  const int nvalid = min(kSelCap, row_valid_count<MODE>(n_vis, blk_lds ? bsh : brow, row, n, B, m));
+  const int nvalid = min(kSelCap, row_valid_count<TOK ? 2 : MODE>(n_vis, MODE == 2 ? bsh : brow, row, n, B, m));
   if (MODE == 0) {
     sg = wave_segment<kSelNT>(nvalid);
     seg_load_scores(S + row * ld, sg, v);
@@ -886,10 +902,10 @@ __global__ __launch_bounds__(kSelNT) void select_rows_kernel(const float* __rest
   const int lgB = __builtin_ctz(unsigned(B));
   const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
     int32_t val = i;
-    if (MODE == 2) {
+    if (TOK) {
       const int s = pow2 ? i >> lgB : i / B;
       const int off = pow2 ? i & (B - 1) : i - s * B;
-      val = (blk_lds ? bsh[s] : brow[s]) * B + off;
+      val = (MODE == 2 ? bsh[s] : brow[s]) * B + off;
     }
     orow[slot] = val;
     if (scrow) scrow[slot] = key_to_float(key);
@@ -1464,8 +1480,12 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   if (e != hipSuccess) return e;
   {
     LaunchScope ls("select_tokens", st);
-    HATTN_LAUNCH(select_rows_kernel<2>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
-                 a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
+    if (m <= kSelNT)
+      HATTN_LAUNCH(select_rows_kernel<2>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
+                   a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
+    else
+      HATTN_LAUNCH(select_rows_kernel<3>, dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
+                   a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
   }
   return hipGetLastError();
 }

@@ -16,6 +16,10 @@
  * Conventions for every entry point:
  *   - Every array argument is a DEVICE pointer (memory from hipMalloc or a
  *     torch CUDA tensor), row-major and contiguous.  Sizes are element counts.
+ *     Activation, cache, query, output and workspace arrays (the bf16/fp32
+ *     data and the indexer head weights) must be 16-byte aligned: kernels
+ *     move them in 16-byte vectors.  A misaligned one gives HATTN_ERR_ARG.
+ *     Integer arrays (positions, counts, indices) need only 4-byte alignment.
  *   - The caller owns and allocates all inputs, outputs and workspaces.  The
  *     library allocates nothing and keeps no state between calls (except the
  *     optional kernel timer below).

@@ -49,6 +49,9 @@ def test_compress_validation(L):
     assert f(1, None, 1, 100, 256, None, None, 8, 4, 0, 1, None, None) == 1  # NULL x
     assert b"NULL" in L.hattn_last_error()
     assert f(1, None, 0, 100, 256, None, None, 8, 4, 0, 24, None, None) == 0  # bt = 0: nothing to do
+    # vector-accessed arrays must be 16-byte aligned (checked before any launch)
+    assert f(1, ctypes.c_void_p(20), 1, 100, 256, None, None, 8, 4, 0, 1, ctypes.c_void_p(32), None) == 1
+    assert b"aligned" in L.hattn_last_error()
 
 
 def test_decode_append_validation(L):
