@@ -23,6 +23,11 @@ SIGNATURES = {
     "hattn_dense_compressed_attn": [_i32, _p, _p, _i64, _p, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p,
                                     _p, _psz, _p],
     "hattn_decode_append": [_i32, _p, _i64, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p, _p, _i32, _i32, _p, _p],
+    "hattn_decode_desc_size": [],
+    "hattn_decode_plan_ws_bytes": [_p, _psz],
+    "hattn_decode_plan_create": [_p, ctypes.POINTER(_p)],
+    "hattn_decode_plan_run": [_p, _p],
+    "hattn_decode_plan_destroy": [_p],
     "hattn_timer_enable": [_i32],
     "hattn_timer_collect": [],
     "hattn_timer_query": [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)],
@@ -31,6 +36,26 @@ SIGNATURES = {
     "hattn_last_error": [],
     "hattn_abi_version": [],
 }
+
+
+
+class DecodeDesc(ctypes.Structure):
+    """Mirror of hattn_decode_desc (include/hattn.h), field for field."""
+    _fields_ = [
+        ("dtype", _i32), ("h", _i32), ("d", _i32), ("window", _i32),
+        ("bt", _i64), ("L", _i64),
+        ("scale", _f32),
+        ("h_i", _i32), ("d_i", _i32), ("B", _i32), ("m", _i32), ("k", _i32),
+        ("csa_w", _i32), ("csa_stride", _i32), ("hca_w", _i32), ("hca_stride", _i32),
+        ("q_pos", _p),
+        ("csa_raw_kv", _p), ("csa_logits", _p), ("csa_pos_bias", _p), ("csa_ckv", _p),
+        ("k_i", _p), ("reps", _p), ("q_i", _p), ("w_i", _p),
+        ("csa_q", _p), ("csa_out", _p), ("csa_lse", _p),
+        ("hca_raw_kv", _p), ("hca_logits", _p), ("hca_pos_bias", _p), ("hca_ckv", _p),
+        ("hca_q", _p), ("hca_out", _p), ("hca_lse", _p),
+        ("ws", _p), ("ws_bytes", ctypes.c_size_t),
+    ]
+
 
 _lib = None
 
@@ -48,6 +73,9 @@ def lib() -> ctypes.CDLL:
             f.restype = ctypes.c_int
         L.hattn_status_string.restype = ctypes.c_char_p
         L.hattn_last_error.restype = ctypes.c_char_p
+        L.hattn_decode_desc_size.restype = ctypes.c_int64
+        if L.hattn_decode_desc_size() != ctypes.sizeof(DecodeDesc):
+            raise RuntimeError("hattn_decode_desc layout differs between the library and the binding")
         _lib = L
     return _lib
 

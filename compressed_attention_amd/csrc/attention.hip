@@ -81,16 +81,54 @@ HATTN_DEV const uint16_t* key_src32(int j, int j_end, int nc, const int32_t* sid
 //           B = P straight from the S^T accumulators, no re-layout)
 // The workgroup writes the normalised output, or an unnormalised partial
 // (O, max, sum) when the key list is split over several workgroups.
+// Arguments of one MFMA attention launch (one query set).
+struct AttnK {
+  const uint16_t* q;
+  const uint16_t* ckv;
+  int64_t n;
+  const int32_t* idx;
+  int k;
+  const int32_t* n_vis;
+  const uint16_t* raw;
+  int64_t L;
+  const int32_t* q_pos;
+  int window;
+  float scale_log2;
+  int64_t nq;
+  int chunk, nsplit;
+  float* out;
+  float* lse;
+  float* part_o;
+  float* part_ml;
+};
+
+template <int D>
+struct AttnLds {
+  static constexpr int TK = 64, KP = D + 8, VP = D + 16;
+  __align__(16) uint16_t kt[TK * KP];
+  __align__(16) uint16_t vt[TK * VP];
+  uint64_t vmask[TK / 64];
+};
+
 template <int D, int NW, bool SPARSE>
-__global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ ckv, int64_t n,
-                                                               const int32_t* __restrict__ idx, int k,
-                                                               const int32_t* __restrict__ n_vis,
-                                                               const uint16_t* __restrict__ raw, int64_t L,
-                                                               const int32_t* __restrict__ q_pos, int window,
-                                                               float scale_log2, int64_t nq, int chunk, int nsplit,
-                                                               float* __restrict__ out, float* __restrict__ lse,
-                                                               float* __restrict__ part_o, float* __restrict__ part_ml) {
+HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D>& lds, int32_t* sidx) {
+  const uint16_t* __restrict__ q = a.q;
+  const uint16_t* __restrict__ ckv = a.ckv;
+  const int64_t n = a.n;
+  const int32_t* __restrict__ idx = a.idx;
+  const int k = a.k;
+  const int32_t* __restrict__ n_vis = a.n_vis;
+  const uint16_t* __restrict__ raw = a.raw;
+  const int64_t L = a.L;
+  const int32_t* __restrict__ q_pos = a.q_pos;
+  const int window = a.window;
+  const float scale_log2 = a.scale_log2;
+  const int64_t nq = a.nq;
+  const int chunk = a.chunk, nsplit = a.nsplit;
+  float* __restrict__ out = a.out;
+  float* __restrict__ lse = a.lse;
+  float* __restrict__ part_o = a.part_o;
+  float* __restrict__ part_ml = a.part_ml;
   constexpr int H = 16 * NW;
   constexpr int C = 2 * D;
   constexpr int TK = 64;      // keys per tile (32 KiB of K|V at d = 128)
@@ -103,13 +141,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* _
   constexpr int KS = D / 32;
   constexpr int DT = D / 16;
   static_assert(TK * PPR % NT == 0, "tile split");
-  __shared__ __align__(16) uint16_t kt[TK * KP];
-  __shared__ __align__(16) uint16_t vt[TK * VP];
-  __shared__ uint64_t vmask[TK / 64];
-  __shared__ int32_t sidx[SPARSE ? kSparseChunkMax : 1];  // this chunk's compressed indices
+  uint16_t* kt = lds.kt;
+  uint16_t* vt = lds.vt;
+  uint64_t* vmask = lds.vmask;
 
-  const int64_t qrow = blockIdx.y;
-  const int split = blockIdx.x;
   const int64_t b = idiv(qrow, nq);
   const int64_t p = q_pos[qrow];
   const int nw = int(imax64(0, imin64(window, p + 1)));
@@ -297,6 +332,32 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(const uint16_t* _
   }
 }
 
+template <int D, int NW, bool SPARSE>
+__global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnK a) {
+  __shared__ AttnLds<D> lds;
+  __shared__ int32_t sidx[SPARSE ? kSparseChunkMax : 1];  // this chunk's compressed indices
+  attn_mfma_body<D, NW, SPARSE>(a, blockIdx.x, blockIdx.y, lds, sidx);
+}
+
+// A sparse and a dense query set in one launch (e.g. the CSA and HCA
+// branches of one decode step): a 1-D grid whose first s.nsplit * rows_s
+// workgroups take the sparse (query, chunk) pairs and the rest the dense
+// ones.  Both roles share one set of LDS buffers.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_pair_kernel(AttnK s, int64_t rows_s, AttnK d) {
+  __shared__ AttnLds<D> lds;
+  __shared__ int32_t sidx[kSparseChunkMax];
+  const int64_t id = blockIdx.x;
+  const int64_t ns = int64_t(s.nsplit) * rows_s;
+  if (id < ns) {
+    const int64_t row = idiv(id, s.nsplit);
+    attn_mfma_body<D, NW, true>(s, int(id - row * s.nsplit), row, lds, sidx);
+  } else {
+    const int64_t row = idiv(id - ns, d.nsplit);
+    attn_mfma_body<D, NW, false>(d, int(id - ns - row * d.nsplit), row, lds, sidx);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Vector kernel for any dtype and shape (h*d <= 8192): same chunking and
 // partial protocol, fp32 throughout.
@@ -424,15 +485,32 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
 constexpr int kMergeRegs = 16;
 constexpr int kMergeMaxSplit = 4 * kMergeRegs;
 
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_ml, int nsplit, int H, int D,
-                                                         float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ float wsh[kMergeMaxSplit];
-  __shared__ float lsh[kMergeMaxSplit];
-  __shared__ float red[4][64];
-  __shared__ float stat[2];
-  const int64_t qrow = blockIdx.y;
-  const int e0 = blockIdx.x * 64;
+// Arguments of one merge (one query set's partials).
+struct MergeK {
+  const float* part_o;
+  const float* part_ml;
+  int nsplit;
+  float* out;
+  float* lse;
+};
+
+struct MergeLds {
+  float wsh[kMergeMaxSplit];
+  float lsh[kMergeMaxSplit];
+  float red[4][64];
+  float stat[2];
+};
+
+HATTN_DEV void attn_merge_body(const MergeK& mk, int H, int D, int64_t qrow, int e0, MergeLds& sm) {
+  const float* __restrict__ part_o = mk.part_o;
+  const float* __restrict__ part_ml = mk.part_ml;
+  const int nsplit = mk.nsplit;
+  float* __restrict__ out = mk.out;
+  float* __restrict__ lse = mk.lse;
+  float* wsh = sm.wsh;
+  float* lsh = sm.lsh;
+  float(*red)[64] = sm.red;
+  float* stat = sm.stat;
   const int h = e0 / D;
   const int tid = threadIdx.x, lane = tid & 63, sg = tid >> 6;
   const float* po = part_o + qrow * nsplit * H * D + e0 + lane;
@@ -480,6 +558,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     out[qrow * H * D + e0 + lane] = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
     if (lane == 0 && (e0 % D) == 0 && lse) lse[qrow * H + h] = (M + __log2f(den)) * kLn2;
   }
+}
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeK mk, int H, int D) {
+  __shared__ MergeLds sm;
+  attn_merge_body(mk, H, D, blockIdx.y, blockIdx.x * 64, sm);
+}
+
+// Two query sets' merges in one launch: rows [0, rows_a) of grid y are set
+// a, the rest set b (same head count and size).
+__global__ __launch_bounds__(256) void attn_merge_pair_kernel(MergeK a, int64_t rows_a, MergeK b, int H, int D) {
+  __shared__ MergeLds sm;
+  const int64_t y = blockIdx.y;
+  if (y < rows_a) attn_merge_body(a, H, D, y, blockIdx.x * 64, sm);
+  else attn_merge_body(b, H, D, y - rows_a, blockIdx.x * 64, sm);
 }
 
 // Same combination for any head size or split count: one thread per output,
@@ -557,14 +649,16 @@ static AttnPlan plan_attn(const AttnArgs& a) {
 
 size_t attn_ws_bytes(const AttnArgs& a) { return plan_attn(a).total; }
 
+static AttnK attn_k(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml) {
+  return AttnK{(const uint16_t*)a.q, (const uint16_t*)a.ckv, a.n, a.idx, a.k, a.n_vis, (const uint16_t*)a.raw_kv,
+               a.L, a.q_pos, a.window, a.scale * kLog2e, a.nq, pl.chunk, pl.nsplit, a.out, a.lse, po, pml};
+}
+
 template <bool SPARSE>
 static void launch_attn_mfma(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml, hipStream_t st) {
-  const float sl2 = a.scale * kLog2e;
+  const AttnK k = attn_k(a, pl, po, pml);
   dim3 grid(unsigned(pl.nsplit), unsigned(a.bt * a.nq));
-#define HATTN_ATTN(D, NH)                                                                                      \
-  HATTN_LAUNCH((attn_mfma_kernel<D, NH, SPARSE>), grid, dim3(64 * NH), 0, st, (const uint16_t*)a.q,      \
-                     (const uint16_t*)a.ckv, a.n, a.idx, a.k, a.n_vis, (const uint16_t*)a.raw_kv, a.L, a.q_pos, \
-                     a.window, sl2, a.nq, pl.chunk, pl.nsplit, a.out, a.lse, po, pml)
+#define HATTN_ATTN(D, NH) HATTN_LAUNCH((attn_mfma_kernel<D, NH, SPARSE>), grid, dim3(64 * NH), 0, st, k)
   const int nw = a.h / 16;
   if (a.d == 128) {
     switch (nw) {
@@ -620,12 +714,86 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   if (e != hipSuccess || pl.nsplit == 1) return e;
   LaunchScope ls("attn_merge", st);
   if (a.d % 64 == 0 && pl.nsplit <= kMergeMaxSplit)
-    HATTN_LAUNCH(attn_merge_kernel, dim3(unsigned(a.h * a.d / 64), unsigned(a.bt * a.nq)), dim3(256), 0, st, po, pml,
-                 pl.nsplit, a.h, a.d, a.out, a.lse);
+    HATTN_LAUNCH(attn_merge_kernel, dim3(unsigned(a.h * a.d / 64), unsigned(a.bt * a.nq)), dim3(256), 0, st,
+                 MergeK{po, pml, pl.nsplit, a.out, a.lse}, a.h, a.d);
   else
     HATTN_LAUNCH(attn_merge_any_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256), 0,
                  st, po, pml, pl.nsplit, a.h, a.d, a.out, a.lse);
   return hipGetLastError();
+}
+
+// Sparse set s and dense set d in one attention launch and one merge launch
+// (same bf16 MFMA head shape), each with its own workspace of
+// attn_ws_bytes; any other combination runs the two launches one after the
+// other.  Results equal launch_attn on each set.
+hipError_t launch_attn_pair(const AttnArgs& s, void* ws_s, const AttnArgs& d, void* ws_d, hipStream_t st) {
+  if (!(mfma_shape(s) && mfma_shape(d) && s.idx && !d.idx && s.h == d.h && s.d == d.d)) {
+    hipError_t e = launch_attn(s, ws_s, st);
+    return e != hipSuccess ? e : launch_attn(d, ws_d, st);
+  }
+  const AttnPlan ps = plan_attn(s), pd = plan_attn(d);
+  auto parts = [](const AttnPlan& pl, void* ws, float** po, float** pml) {
+    *po = nullptr;
+    *pml = nullptr;
+    if (pl.nsplit > 1) {
+      *po = reinterpret_cast<float*>(ws);
+      *pml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + pl.po_bytes);
+    }
+  };
+  float *po_s, *pml_s, *po_d, *pml_d;
+  parts(ps, ws_s, &po_s, &pml_s);
+  parts(pd, ws_d, &po_d, &pml_d);
+  const AttnK ks = attn_k(s, ps, po_s, pml_s), kd = attn_k(d, pd, po_d, pml_d);
+  const int64_t rows_s = s.bt * s.nq, rows_d = d.bt * d.nq;
+  const dim3 grid(unsigned(int64_t(ps.nsplit) * rows_s + int64_t(pd.nsplit) * rows_d));
+  {
+    LaunchScope ls("attn_pair_mfma", st);
+    const int nw = s.h / 16;
+#define HATTN_PAIR(D, NH) HATTN_LAUNCH((attn_pair_kernel<D, NH>), grid, dim3(64 * NH), 0, st, ks, rows_s, kd)
+    if (s.d == 128) {
+      switch (nw) {
+        case 1: HATTN_PAIR(128, 1); break;
+        case 2: HATTN_PAIR(128, 2); break;
+        default: HATTN_PAIR(128, 4); break;
+      }
+    } else {
+      switch (nw) {
+        case 1: HATTN_PAIR(64, 1); break;
+        case 2: HATTN_PAIR(64, 2); break;
+        default: HATTN_PAIR(64, 4); break;
+      }
+    }
+#undef HATTN_PAIR
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool ms = ps.nsplit > 1, md = pd.nsplit > 1;
+  const bool fast = s.d % 64 == 0 && ps.nsplit <= kMergeMaxSplit && pd.nsplit <= kMergeMaxSplit;
+  LaunchScope ls("attn_merge", st);
+  const MergeK mks{po_s, pml_s, ps.nsplit, s.out, s.lse}, mkd{po_d, pml_d, pd.nsplit, d.out, d.lse};
+  const unsigned gx = unsigned(s.h * s.d / 64);
+  if (ms && md && fast) {
+    HATTN_LAUNCH(attn_merge_pair_kernel, dim3(gx, unsigned(rows_s + rows_d)), dim3(256), 0, st, mks, rows_s, mkd,
+                 s.h, s.d);
+    return hipGetLastError();
+  }
+  for (int r = 0; r < 2; ++r) {
+    const bool need = r == 0 ? ms : md;
+    if (!need) continue;
+    const AttnPlan& pl = r == 0 ? ps : pd;
+    const AttnArgs& a = r == 0 ? s : d;
+    float* po = r == 0 ? po_s : po_d;
+    float* pml = r == 0 ? pml_s : pml_d;
+    if (a.d % 64 == 0 && pl.nsplit <= kMergeMaxSplit)
+      HATTN_LAUNCH(attn_merge_kernel, dim3(gx, unsigned(a.bt * a.nq)), dim3(256), 0, st,
+                   MergeK{po, pml, pl.nsplit, a.out, a.lse}, a.h, a.d);
+    else
+      HATTN_LAUNCH(attn_merge_any_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256),
+                   0, st, po, pml, pl.nsplit, a.h, a.d, a.out, a.lse);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace hattn

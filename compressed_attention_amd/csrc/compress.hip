@@ -452,86 +452,109 @@ HATTN_DEV void append_first(const T* __restrict__ base, int64_t ld, int n, int r
   }
 }
 
+// Per-token maintenance of one compressed layer: the launch arguments.
+struct AppendK {
+  const void* x;  // raw rows [bt][L][C]
+  int64_t L;
+  int C;
+  const float* z;
+  const float* bias;
+  int w, s;
+  void* y;  // entries [bt][N][C]
+  int64_t N;
+  int32_t* n_vis;
+  const void* k_i;  // [bt][N][d_i] or NULL
+  int d_i, B;
+  float* reps;  // [bt][ceil(N/B)][d_i] or NULL
+};
+
+// The entry the token at p completes (-1 if none) and the visible count.
+HATTN_DEV int64_t append_entry_of(const AppendK& a, int64_t p, int64_t* nv) {
+  const int64_t pe = p >= a.w - 1 ? idiv(p - a.w + 1, a.s) : -1;  // entry ending at or before p
+  *nv = pe + 1 > a.N ? a.N : pe + 1;
+  return pe >= 0 && pe * a.s == p - a.w + 1 && pe < a.N ? pe : -1;
+}
+
+// Workgroup role "entry": the visible count and, when the token completes
+// entry e, the softmax-weighted compression of its window into y[b][e].
 template <typename T>
-__global__ __launch_bounds__(kAppNT) void append_kernel(const T* __restrict__ x, int64_t L, int C,
-                                                        const float* __restrict__ z, const float* __restrict__ bias,
-                                                        int w, int s, const int32_t* __restrict__ q_pos,
-                                                        T* __restrict__ y, int64_t N, int32_t* __restrict__ n_vis,
-                                                        const T* __restrict__ k_i, int d_i, int B,
-                                                        float* __restrict__ reps) {
+HATTN_DEV void append_entry_body(const AppendK& a, int64_t b, int64_t p, float* sm, float* red) {
   constexpr int V = Vec16<T>::N;
-  extern __shared__ float sm[];
-  __shared__ float red[2];
-  const int64_t b = blockIdx.y;
-  const int64_t p = q_pos[b];
-  const int64_t pe = p >= w - 1 ? idiv(p - w + 1, s) : -1;  // entry ending at or before p
-  int64_t nv = pe + 1;
-  if (nv > N) nv = N;
-  const bool done = pe >= 0 && pe * s == p - w + 1 && pe < N;
-  const int64_t e = done ? pe : -1;
-  if (blockIdx.x == 0) {
-    if (threadIdx.x == 0) n_vis[b] = int32_t(nv);
-    if (!done) return;
-    const int slots = C / V;
-    const int RG = kAppNT / slots;
-    const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
-    const int64_t t0 = e * s;
-    const T* xb = x + (b * L + t0) * C + cs * V;
-    // the window's first rows go out before the softmax weights are known
-    u32x4_t first[kAppUNR];
-    if (rg < RG) append_first(xb, C, w, rg, first, RG);
-    float* wt = sm;        // [w] logits, then softmax numerators
-    float* part = sm + w;  // [RG][C] row-group partial sums
-    for (int u = threadIdx.x; u < w; u += kAppNT) wt[u] = (z ? z[b * L + t0 + u] : 0.f) + (bias ? bias[u] : 0.f);
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-      float mx = -INFINITY;
-      for (int u = threadIdx.x; u < w; u += kWave) mx = fmaxf(mx, wt[u]);
-      mx = wave_max(mx);
-      float den = 0.f;
-      for (int u = threadIdx.x; u < w; u += kWave) den += __expf(wt[u] - mx);
-      den = wave_sum(den);
-      if (threadIdx.x == 0) {
-        red[0] = mx;
-        red[1] = den;
-      }
+  const T* __restrict__ x = static_cast<const T*>(a.x);
+  const int C = a.C, w = a.w;
+  int64_t nv;
+  const int64_t e = append_entry_of(a, p, &nv);
+  if (threadIdx.x == 0) a.n_vis[b] = int32_t(nv);
+  if (e < 0) return;
+  const int slots = C / V;
+  const int RG = kAppNT / slots;
+  const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
+  const int64_t t0 = e * a.s;
+  const T* xb = x + (b * a.L + t0) * C + cs * V;
+  // the window's first rows go out before the softmax weights are known
+  u32x4_t first[kAppUNR];
+  if (rg < RG) append_first(xb, C, w, rg, first, RG);
+  float* wt = sm;        // [w] logits, then softmax numerators
+  float* part = sm + w;  // [RG][C] row-group partial sums
+  for (int u = threadIdx.x; u < w; u += kAppNT)
+    wt[u] = (a.z ? a.z[b * a.L + t0 + u] : 0.f) + (a.bias ? a.bias[u] : 0.f);
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    float mx = -INFINITY;
+    for (int u = threadIdx.x; u < w; u += kWave) mx = fmaxf(mx, wt[u]);
+    mx = wave_max(mx);
+    float den = 0.f;
+    for (int u = threadIdx.x; u < w; u += kWave) den += __expf(wt[u] - mx);
+    den = wave_sum(den);
+    if (threadIdx.x == 0) {
+      red[0] = mx;
+      red[1] = den;
     }
-    __syncthreads();
-    const float mx = red[0], inv = 1.f / red[1];
-    if (rg < RG) {
-      float acc[V];
-#pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = 0.f;
-      append_rows(xb, C, w, rg, RG, first, [&](int u) { return __expf(wt[u] - mx); }, acc);
-#pragma unroll
-      for (int i = 0; i < V; ++i) part[rg * C + cs * V + i] = acc[i];
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < slots; c += kAppNT) {
-      float r[V];
-#pragma unroll
-      for (int i = 0; i < V; ++i) r[i] = 0.f;
-      for (int g = 0; g < RG; ++g)
-#pragma unroll
-        for (int i = 0; i < V; ++i) r[i] += part[g * C + c * V + i];
-#pragma unroll
-      for (int i = 0; i < V; ++i) r[i] *= inv;
-      st16(y + (b * N + e) * C + c * V, Vec16<T>::pack(r));
-    }
-    return;
   }
-  // workgroup 1: block mean of the block holding e
-  if (!done || !reps) return;
-  const int64_t nb = idiv(N + B - 1, B);
+  __syncthreads();
+  const float mx = red[0], inv = 1.f / red[1];
+  if (rg < RG) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    append_rows(xb, C, w, rg, RG, first, [&](int u) { return __expf(wt[u] - mx); }, acc);
+#pragma unroll
+    for (int i = 0; i < V; ++i) part[rg * C + cs * V + i] = acc[i];
+  }
+  __syncthreads();
+  T* y = static_cast<T*>(a.y);
+  for (int c = threadIdx.x; c < slots; c += kAppNT) {
+    float r[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) r[i] = 0.f;
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+      for (int i = 0; i < V; ++i) r[i] += part[g * C + c * V + i];
+#pragma unroll
+    for (int i = 0; i < V; ++i) r[i] *= inv;
+    st16(y + (b * a.N + e) * C + c * V, Vec16<T>::pack(r));
+  }
+}
+
+// Workgroup role "block mean": the mean of the HISA block holding the
+// completed entry (entries past the last one count as zero).
+template <typename T>
+HATTN_DEV void append_mean_body(const AppendK& a, int64_t b, int64_t p, float* sm) {
+  constexpr int V = Vec16<T>::N;
+  int64_t nv;
+  const int64_t e = append_entry_of(a, p, &nv);
+  if (e < 0 || !a.reps) return;
+  const int B = a.B, d_i = a.d_i;
+  const int64_t nb = idiv(a.N + B - 1, B);
   const int64_t j = idiv(e, B);
   const int64_t i0 = j * B;
-  const int cnt = int(imin64(N, i0 + B) - i0);
+  const int cnt = int(imin64(a.N, i0 + B) - i0);
   const int slots = d_i / V;
   const int RG = kAppNT / slots;
   const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
   float* part = sm;  // [RG][d_i]
   if (rg < RG) {
-    const T* kb = k_i + (b * N + i0) * d_i + cs * V;
+    const T* kb = static_cast<const T*>(a.k_i) + (b * a.N + i0) * d_i + cs * V;
     u32x4_t first[kAppUNR];
     append_first(kb, d_i, cnt, rg, first, RG);
     float acc[V];
@@ -546,33 +569,74 @@ __global__ __launch_bounds__(kAppNT) void append_kernel(const T* __restrict__ x,
   for (int c = threadIdx.x; c < d_i; c += kAppNT) {
     float r = 0.f;
     for (int g = 0; g < RG; ++g) r += part[g * d_i + c];
-    reps[(b * nb + j) * d_i + c] = r * invb;
+    a.reps[(b * nb + j) * d_i + c] = r * invb;
   }
 }
 
+// One launch for one or two layers, grid (roles, bt): layer a's entry, then
+// (when a keeps block means) its block mean, then (when b_on) layer b's
+// entry.  Both layers serve the same sequences and token positions.
 template <typename T>
-static hipError_t launch_append_t(const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
-                                  int w, int s, const int32_t* q_pos, void* y, int64_t N, int32_t* n_vis,
-                                  const void* k_i, int d_i, int B, float* reps, hipStream_t st) {
-  const size_t smem = append_lds_bytes(std::is_same<T, float>::value ? 0 : 1, C, w, d_i, reps != nullptr);
+__global__ __launch_bounds__(kAppNT) void append_kernel(AppendK la, AppendK lb, int b_on,
+                                                        const int32_t* __restrict__ q_pos) {
+  extern __shared__ float sm[];
+  __shared__ float red[2];
+  const int64_t b = blockIdx.y;
+  const int64_t p = q_pos[b];
+  int role = blockIdx.x;
+  if (!la.reps && role >= 1) role += 1;
+  if (role == 0) append_entry_body<T>(la, b, p, sm, red);
+  else if (role == 1) append_mean_body<T>(la, b, p, sm);
+  else if (b_on) append_entry_body<T>(lb, b, p, sm, red);
+}
+
+static size_t append_lds_one(const AppendK& a, int V) {
+  const size_t sm_c = size_t(a.w + (kAppNT / (a.C / V)) * a.C) * 4;
+  const size_t sm_r = a.reps ? size_t(kAppNT / (a.d_i / V)) * a.d_i * 4 : 0;
+  return std::max(sm_c, sm_r);
+}
+
+static hipError_t launch_append_k(int dtype, const AppendK& la, const AppendK* lb, int64_t bt,
+                                  const int32_t* q_pos, hipStream_t st) {
+  const int V = dtype == 0 ? 4 : 8;
+  size_t smem = append_lds_one(la, V);
+  if (lb) smem = std::max(smem, append_lds_one(*lb, V));
+  const unsigned roles = 1u + (la.reps ? 1u : 0u) + (lb ? 1u : 0u);
+  const AppendK none{};
   LaunchScope ls("decode_append", st);
-  HATTN_LAUNCH((append_kernel<T>), dim3(reps ? 2u : 1u, unsigned(bt)), dim3(kAppNT), smem, st, (const T*)x, L, C, z,
-               bias, w, s, q_pos, (T*)y, N, n_vis, (const T*)k_i, d_i, B, reps);
+  if (dtype == 0)
+    HATTN_LAUNCH((append_kernel<float>), dim3(roles, unsigned(bt)), dim3(kAppNT), smem, st, la, lb ? *lb : none,
+                 lb ? 1 : 0, q_pos);
+  else
+    HATTN_LAUNCH((append_kernel<uint16_t>), dim3(roles, unsigned(bt)), dim3(kAppNT), smem, st, la, lb ? *lb : none,
+                 lb ? 1 : 0, q_pos);
   return hipGetLastError();
 }
 
 size_t append_lds_bytes(int dtype, int C, int w, int d_i, bool with_reps) {
-  const int V = dtype == 0 ? 4 : 8;
-  const size_t sm_c = size_t(w + (kAppNT / (C / V)) * C) * 4;
-  const size_t sm_r = with_reps ? size_t(kAppNT / (d_i / V)) * d_i * 4 : 0;
-  return std::max(sm_c, sm_r);
+  AppendK a{};
+  a.C = C;
+  a.w = w;
+  a.d_i = d_i;
+  a.reps = with_reps ? reinterpret_cast<float*>(16) : nullptr;
+  return append_lds_one(a, dtype == 0 ? 4 : 8);
 }
 
 hipError_t launch_append(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
                          int w, int s, const int32_t* q_pos, void* y, int64_t N, int32_t* n_vis, const void* k_i,
                          int d_i, int B, float* reps, hipStream_t st) {
-  if (dtype == 0) return launch_append_t<float>(x, bt, L, C, z, bias, w, s, q_pos, y, N, n_vis, k_i, d_i, B, reps, st);
-  return launch_append_t<uint16_t>(x, bt, L, C, z, bias, w, s, q_pos, y, N, n_vis, k_i, d_i, B, reps, st);
+  const AppendK la{x, L, C, z, bias, w, s, y, N, n_vis, k_i, d_i, B, reps};
+  return launch_append_k(dtype, la, nullptr, bt, q_pos, st);
+}
+
+hipError_t launch_append_pair(int dtype, int64_t bt, const int32_t* q_pos, const void* x1, const float* z1,
+                              const float* bias1, int w1, int s1, void* y1, int64_t N1, int32_t* n_vis1,
+                              const void* k_i, int d_i, int B, float* reps, const void* x2, const float* z2,
+                              const float* bias2, int w2, int s2, void* y2, int64_t N2, int32_t* n_vis2, int64_t L,
+                              int C, hipStream_t st) {
+  const AppendK la{x1, L, C, z1, bias1, w1, s1, y1, N1, n_vis1, k_i, d_i, B, reps};
+  const AppendK lb{x2, L, C, z2, bias2, w2, s2, y2, N2, n_vis2, nullptr, 0, 0, nullptr};
+  return launch_append_k(dtype, la, &lb, bt, q_pos, st);
 }
 
 }  // namespace hattn

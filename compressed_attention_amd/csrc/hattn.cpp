@@ -224,25 +224,33 @@ hattn_status_t hattn_hisa_pool(int dtype, const void* k_i, int64_t bt, int64_t n
                     "hisa_pool");
 }
 
-hattn_status_t hattn_hisa_topk(int dtype, const void* q_i, const void* k_i, const float* w_i, const int32_t* n_vis,
-                               int64_t bt, int64_t nq, int32_t h_i, int32_t d_i, int64_t n, const float* reps,
-                               int32_t B, int32_t m, int32_t k, int32_t* idx, int32_t* blk, void* ws,
-                               size_t* ws_bytes, void* stream) {
+static hattn_status_t hisa_check(int dtype, const void* q_i, const void* k_i, const float* w_i,
+                                 const int32_t* n_vis, int64_t bt, int64_t nq, int32_t h_i, int32_t d_i, int64_t n,
+                                 const float* reps, int32_t B, int32_t m, int32_t k, const int32_t* idx, void* ws) {
   hattn_status_t st = check_index_args("hisa_topk", dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n, k, idx);
   if (st != HATTN_OK) return st;
   if (B < 1 || B > 1024 || m < 1 || int64_t(m) * B > 16384)
     return fail(HATTN_ERR_ARG, "hisa_topk: need 1 <= B <= 1024, m >= 1, m*B <= 16384");
   if ((n + B - 1) / B > 16384) return fail(HATTN_ERR_UNSUPPORTED, "hisa_topk: more than 16384 blocks");
   if (bt * nq > 0 && n > 0 && !reps) return fail(HATTN_ERR_ARG, "hisa_topk: NULL reps");
+  HATTN_REQUIRE_ALIGNED("hisa_topk", reps, ws);
+  return HATTN_OK;
+}
+
+hattn_status_t hattn_hisa_topk(int dtype, const void* q_i, const void* k_i, const float* w_i, const int32_t* n_vis,
+                               int64_t bt, int64_t nq, int32_t h_i, int32_t d_i, int64_t n, const float* reps,
+                               int32_t B, int32_t m, int32_t k, int32_t* idx, int32_t* blk, void* ws,
+                               size_t* ws_bytes, void* stream) {
+  hattn_status_t st = hisa_check(dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n, reps, B, m, k, idx, ws);
+  if (st != HATTN_OK) return st;
   hattn::IndexArgs a{dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n};
   const size_t need = bt * nq > 0 ? hattn::hisa_topk_ws_bytes(a, B, m, k) : 0;
-  HATTN_REQUIRE_ALIGNED("hisa_topk", reps, ws);
   if (ws_query(ws, ws_bytes, need, &st)) return st;
   if (bt * nq == 0) return ok();
   return hip_status(hattn::launch_hisa_topk(a, reps, B, m, k, idx, blk, ws, (hipStream_t)stream), "hisa_topk");
 }
 
-static hattn_status_t attn_common(const char* fn, hattn::AttnArgs& a, void* ws, size_t* ws_bytes, void* stream) {
+static hattn_status_t attn_check(const char* fn, const hattn::AttnArgs& a, void* ws) {
   if (!dtype_ok(a.dtype)) return fail(HATTN_ERR_ARG, "%s: bad dtype %d", fn, a.dtype);
   if (a.bt < 0 || a.nq < 0 || a.n < 0 || a.L < 1 || a.window < 1)
     return fail(HATTN_ERR_ARG, "%s: bad sizes (need L >= 1, window >= 1)", fn);
@@ -253,8 +261,14 @@ static hattn_status_t attn_common(const char* fn, hattn::AttnArgs& a, void* ws, 
   if (rows > 0 && (!a.q || !a.raw_kv || !a.q_pos || !a.out || (a.n > 0 && !a.ckv)))
     return fail(HATTN_ERR_ARG, "%s: NULL required pointer", fn);
   HATTN_REQUIRE_ALIGNED(fn, a.q, a.ckv, a.raw_kv, a.out, ws);
+  return HATTN_OK;
+}
+
+static hattn_status_t attn_common(const char* fn, hattn::AttnArgs& a, void* ws, size_t* ws_bytes, void* stream) {
+  hattn_status_t st = attn_check(fn, a, ws);
+  if (st != HATTN_OK) return st;
+  const int64_t rows = a.bt * a.nq;
   const size_t need = rows > 0 ? hattn::attn_ws_bytes(a) : 0;
-  hattn_status_t st;
   if (ws_query(ws, ws_bytes, need, &st)) return st;
   if (rows == 0) return ok();
   return hip_status(hattn::launch_attn(a, ws, (hipStream_t)stream), fn);
@@ -282,10 +296,9 @@ hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void*
   return attn_common("dense_compressed_attn", a, ws, ws_bytes, stream);
 }
 
-hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, int64_t L, int32_t C,
-                                   const float* logits, const float* pos_bias, int32_t w, int32_t stride,
-                                   const int32_t* q_pos, void* ckv, int32_t* n_vis, const void* k_i, int32_t d_i,
-                                   int32_t B, float* reps, void* stream) {
+static hattn_status_t append_check(int dtype, const void* raw_kv, int64_t bt, int64_t L, int32_t C, int32_t w,
+                                   int32_t stride, const int32_t* q_pos, const void* ckv, const int32_t* n_vis,
+                                   const void* k_i, int32_t d_i, int32_t B, const float* reps, int64_t* N) {
   if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "decode_append: bad dtype %d", dtype);
   if (bt < 0 || L < 0) return fail(HATTN_ERR_ARG, "decode_append: negative size");
   if (w < 1 || w > 4096 || stride < 1) return fail(HATTN_ERR_ARG, "decode_append: need 1 <= w <= 4096, stride >= 1");
@@ -296,11 +309,23 @@ hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, in
   if ((k_i == nullptr) != (reps == nullptr)) return fail(HATTN_ERR_ARG, "decode_append: give both k_i and reps, or neither");
   if (reps && (B < 1 || d_i <= 0 || d_i % vec || d_i / vec > 256))
     return fail(HATTN_ERR_ARG, "decode_append: bad B=%d or d_i=%d", B, d_i);
-  if (bt == 0) return ok();
+  *N = (L - w) / stride + 1;
+  if (*N > INT32_MAX) return fail(HATTN_ERR_ARG, "decode_append: too many entries");
+  if (bt == 0) return HATTN_OK;
   if (!raw_kv || !q_pos || !ckv || !n_vis) return fail(HATTN_ERR_ARG, "decode_append: NULL pointer");
   HATTN_REQUIRE_ALIGNED("decode_append", raw_kv, ckv, k_i);
-  const int64_t N = (L - w) / stride + 1;
-  if (N > INT32_MAX) return fail(HATTN_ERR_ARG, "decode_append: too many entries");
+  return HATTN_OK;
+}
+
+hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, int64_t L, int32_t C,
+                                   const float* logits, const float* pos_bias, int32_t w, int32_t stride,
+                                   const int32_t* q_pos, void* ckv, int32_t* n_vis, const void* k_i, int32_t d_i,
+                                   int32_t B, float* reps, void* stream) {
+  int64_t N = 0;
+  const hattn_status_t st =
+      append_check(dtype, raw_kv, bt, L, C, w, stride, q_pos, ckv, n_vis, k_i, d_i, B, reps, &N);
+  if (st != HATTN_OK) return st;
+  if (bt == 0) return ok();
   return hip_status(hattn::launch_append(dtype, raw_kv, bt, L, C, logits, pos_bias, w, stride, q_pos, ckv, N, n_vis,
                                          k_i, d_i, B, reps, (hipStream_t)stream),
                     "decode_append");
@@ -358,6 +383,178 @@ hattn_status_t hattn_timer_names(char* buf, int64_t len) {
   const size_t n = std::min<size_t>(s.size(), size_t(len - 1));
   std::memcpy(buf, s.data(), n);
   buf[n] = 0;
+  return ok();
+}
+
+
+// ---- decode plan -----------------------------------------------------------
+}  // extern "C"
+
+struct hattn_decode_plan {
+  int device = -1;
+  int dtype = 0;
+  int64_t bt = 0, L = 0;
+  int C = 0;
+  const int32_t* q_pos = nullptr;
+  // CSA branch
+  const void* csa_raw_kv = nullptr;
+  const float *csa_logits = nullptr, *csa_pos_bias = nullptr;
+  int csa_w = 0, csa_stride = 0;
+  int64_t csa_N = 0;
+  void* csa_ckv = nullptr;
+  const void* k_i = nullptr;
+  float* reps = nullptr;
+  int d_i = 0, B = 0, m = 0, k = 0;
+  int32_t* nv_csa = nullptr;
+  int32_t* idx = nullptr;
+  hattn::IndexArgs ia{};
+  void* hisa_ws = nullptr;
+  hattn::AttnArgs sa{};
+  void* sa_ws = nullptr;
+  // HCA branch
+  const void* hca_raw_kv = nullptr;
+  const float *hca_logits = nullptr, *hca_pos_bias = nullptr;
+  int hca_w = 0, hca_stride = 0;
+  int64_t hca_N = 0;
+  void* hca_ckv = nullptr;
+  int32_t* nv_hca = nullptr;
+  hattn::AttnArgs da{};
+  void* da_ws = nullptr;
+};
+
+namespace {
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Validates the descriptor and lays the workspace out (offsets from ws);
+// fills `p` when it is given.
+hattn_status_t decode_layout(const hattn_decode_desc* d, size_t* total, hattn_decode_plan* p) {
+  if (!d) return fail(HATTN_ERR_ARG, "decode_plan: NULL descriptor");
+  if (d->bt < 1) return fail(HATTN_ERR_ARG, "decode_plan: need bt >= 1");
+  const int C = 2 * d->d;
+  int64_t Nc = 0, Nh = 0;
+  hattn_status_t st = append_check(d->dtype, d->csa_raw_kv, d->bt, d->L, C, d->csa_w, d->csa_stride, d->q_pos,
+                                   d->csa_ckv, d->q_pos, d->k_i, d->d_i, d->B, d->reps, &Nc);
+  if (st != HATTN_OK) return st;
+  if (!d->k_i) return fail(HATTN_ERR_ARG, "decode_plan: the CSA branch needs k_i and reps");
+  st = append_check(d->dtype, d->hca_raw_kv, d->bt, d->L, C, d->hca_w, d->hca_stride, d->q_pos, d->hca_ckv,
+                    d->q_pos, nullptr, 0, 0, nullptr, &Nh);
+  if (st != HATTN_OK) return st;
+  // Workspace: counts, selected indices, then each call's own workspace.
+  const size_t o_nvc = 0;
+  const size_t o_nvh = o_nvc + al256(size_t(d->bt) * 4);
+  const size_t o_idx = o_nvh + al256(size_t(d->bt) * 4);
+  const size_t o_hisa = o_idx + al256(size_t(d->bt) * std::max(d->k, 1) * 4);
+  char* base = reinterpret_cast<char*>(d->ws);
+  auto at = [&](size_t off) -> void* { return base ? base + off : reinterpret_cast<void*>(uintptr_t(256)); };
+  hattn::IndexArgs ia{d->dtype, d->q_i, d->k_i, d->w_i, (const int32_t*)at(o_nvc), d->bt, 1, d->h_i, d->d_i, Nc};
+  st = hisa_check(d->dtype, d->q_i, d->k_i, d->w_i, ia.n_vis, d->bt, 1, d->h_i, d->d_i, Nc, d->reps, d->B, d->m,
+                  d->k, (const int32_t*)at(o_idx), d->ws);
+  if (st != HATTN_OK) return st;
+  const size_t o_sa = o_hisa + al256(hattn::hisa_topk_ws_bytes(ia, d->B, d->m, d->k));
+  hattn::AttnArgs sa{d->dtype, d->csa_q, d->csa_ckv, Nc, (const int32_t*)at(o_idx), d->k, nullptr, d->csa_raw_kv,
+                     d->L, d->q_pos, d->window, d->scale, d->bt, 1, d->h, d->d, d->csa_out, d->csa_lse};
+  st = attn_check("decode_plan (CSA attention)", sa, d->ws);
+  if (st != HATTN_OK) return st;
+  const size_t o_da = o_sa + al256(hattn::attn_ws_bytes(sa));
+  hattn::AttnArgs da{d->dtype, d->hca_q, d->hca_ckv, Nh, nullptr, 0, (const int32_t*)at(o_nvh), d->hca_raw_kv,
+                     d->L, d->q_pos, d->window, d->scale, d->bt, 1, d->h, d->d, d->hca_out, d->hca_lse};
+  st = attn_check("decode_plan (HCA attention)", da, d->ws);
+  if (st != HATTN_OK) return st;
+  *total = o_da + al256(hattn::attn_ws_bytes(da));
+  if (!p) return HATTN_OK;
+  p->dtype = d->dtype;
+  p->bt = d->bt;
+  p->L = d->L;
+  p->C = C;
+  p->q_pos = d->q_pos;
+  p->csa_raw_kv = d->csa_raw_kv;
+  p->csa_logits = d->csa_logits;
+  p->csa_pos_bias = d->csa_pos_bias;
+  p->csa_w = d->csa_w;
+  p->csa_stride = d->csa_stride;
+  p->csa_N = Nc;
+  p->csa_ckv = d->csa_ckv;
+  p->k_i = d->k_i;
+  p->reps = d->reps;
+  p->d_i = d->d_i;
+  p->B = d->B;
+  p->m = d->m;
+  p->k = d->k;
+  p->nv_csa = reinterpret_cast<int32_t*>(at(o_nvc));
+  p->idx = reinterpret_cast<int32_t*>(at(o_idx));
+  p->ia = ia;
+  p->hisa_ws = at(o_hisa);
+  p->sa = sa;
+  p->sa_ws = at(o_sa);
+  p->hca_raw_kv = d->hca_raw_kv;
+  p->hca_logits = d->hca_logits;
+  p->hca_pos_bias = d->hca_pos_bias;
+  p->hca_w = d->hca_w;
+  p->hca_stride = d->hca_stride;
+  p->hca_N = Nh;
+  p->hca_ckv = d->hca_ckv;
+  p->nv_hca = reinterpret_cast<int32_t*>(at(o_nvh));
+  p->da = da;
+  p->da_ws = at(o_da);
+  return HATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hattn_decode_desc_size(void) { return int64_t(sizeof(hattn_decode_desc)); }
+
+hattn_status_t hattn_decode_plan_ws_bytes(const hattn_decode_desc* desc, size_t* ws_bytes) {
+  if (!ws_bytes) return fail(HATTN_ERR_ARG, "decode_plan_ws_bytes: NULL ws_bytes");
+  size_t total = 0;
+  hattn_status_t st = decode_layout(desc, &total, nullptr);
+  if (st != HATTN_OK) return st;
+  *ws_bytes = total;
+  return ok();
+}
+
+hattn_status_t hattn_decode_plan_create(const hattn_decode_desc* desc, hattn_decode_plan_t* plan) {
+  if (!plan) return fail(HATTN_ERR_ARG, "decode_plan_create: NULL plan");
+  *plan = nullptr;
+  size_t total = 0;
+  hattn_status_t st = decode_layout(desc, &total, nullptr);
+  if (st != HATTN_OK) return st;
+  if (!desc->ws || desc->ws_bytes < total)
+    return fail(HATTN_ERR_WORKSPACE, "decode_plan_create: workspace of %zu bytes is smaller than the %zu required",
+                desc->ws ? desc->ws_bytes : size_t(0), total);
+  hattn_decode_plan* p = new hattn_decode_plan();
+  decode_layout(desc, &total, p);
+  const hipError_t e = hipGetDevice(&p->device);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_status(e, "decode_plan_create");
+  }
+  *plan = p;
+  return ok();
+}
+
+hattn_status_t hattn_decode_plan_run(hattn_decode_plan_t p, void* stream) {
+  if (!p) return fail(HATTN_ERR_ARG, "decode_plan_run: NULL plan");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "decode_plan_run");
+  if (dev != p->device) return fail(HATTN_ERR_ARG, "decode_plan_run: plan made on device %d, current %d", p->device, dev);
+  const hipStream_t st = (hipStream_t)stream;
+  // Both branches on one stream: the HCA work rides in the CSA launches
+  // (one cache-maintenance launch, one attention launch, one merge launch).
+  e = hattn::launch_append_pair(p->dtype, p->bt, p->q_pos, p->csa_raw_kv, p->csa_logits, p->csa_pos_bias, p->csa_w,
+                                p->csa_stride, p->csa_ckv, p->csa_N, p->nv_csa, p->k_i, p->d_i, p->B, p->reps,
+                                p->hca_raw_kv, p->hca_logits, p->hca_pos_bias, p->hca_w, p->hca_stride, p->hca_ckv,
+                                p->hca_N, p->nv_hca, p->L, p->C, st);
+  if (e == hipSuccess) e = hattn::launch_hisa_topk(p->ia, p->reps, p->B, p->m, p->k, p->idx, nullptr, p->hisa_ws, st);
+  if (e == hipSuccess) e = hattn::launch_attn_pair(p->sa, p->sa_ws, p->da, p->da_ws, st);
+  return hip_status(e, "decode_plan_run");
+}
+
+hattn_status_t hattn_decode_plan_destroy(hattn_decode_plan_t p) {
+  delete p;
   return ok();
 }
 

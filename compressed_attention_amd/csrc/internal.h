@@ -45,6 +45,13 @@ hipError_t launch_visible_count(const int32_t* pos, int64_t count, int w, int s,
 hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_i, int B, int64_t j0,
                        int64_t j1, float* reps, hipStream_t st);
 size_t append_lds_bytes(int dtype, int C, int w, int d_i, bool with_reps);
+// Two layers of the same sequences in one launch: layer 1 (with block means
+// when k_i / reps are given) and layer 2 (entries only).
+hipError_t launch_append_pair(int dtype, int64_t bt, const int32_t* q_pos, const void* x1, const float* z1,
+                              const float* bias1, int w1, int s1, void* y1, int64_t N1, int32_t* n_vis1,
+                              const void* k_i, int d_i, int B, float* reps, const void* x2, const float* z2,
+                              const float* bias2, int w2, int s2, void* y2, int64_t N2, int32_t* n_vis2, int64_t L,
+                              int C, hipStream_t st);
 hipError_t launch_append(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
                          int w, int s, const int32_t* q_pos, void* y, int64_t N, int32_t* n_vis, const void* k_i,
                          int d_i, int B, float* reps, hipStream_t st);
@@ -90,6 +97,9 @@ struct AttnArgs {
 
 size_t attn_ws_bytes(const AttnArgs& a);
 hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st);
+// A sparse and a dense set (each with its own attn_ws_bytes workspace) in
+// shared launches; the same results as launch_attn on each.
+hipError_t launch_attn_pair(const AttnArgs& s, void* ws_s, const AttnArgs& d, void* ws_d, hipStream_t st);
 bool attn_supported(const AttnArgs& a);
 
 }  // namespace hattn

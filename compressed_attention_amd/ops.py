@@ -280,3 +280,91 @@ def timer_collect() -> dict:
         check("hattn_timer_query", L.hattn_timer_query(name.encode(), ctypes.byref(ms), ctypes.byref(cnt)))
         out[name] = (ms.value, cnt.value)
     return out
+
+
+class DecodePlan:
+    """One decode step of a hybrid layer pair (CSA branch: cache append ->
+    HISA -> sparse attention; HCA branch: cache append -> dense attention),
+    validated once and run with one host call per step (hattn_decode_plan_*).
+
+    Tensors are the per-step inputs of the separate ops with nq = 1: q_pos
+    [bt][1]; csa_q / hca_q [bt][1][h][d]; q_i [bt][1][h_i][d_i]; w_i
+    [bt][1][h_i].  csa_ckv, hca_ckv and reps are rewritten in place each run.
+    The plan holds references to every tensor; outputs live in .csa_out /
+    .hca_out ([bt][1][h][d] fp32) and, with return_lse, .csa_lse / .hca_lse.
+    """
+
+    def __init__(self, *, q_pos, csa_raw_kv, csa_logits, csa_pos_bias, csa_ckv, k_i, reps, q_i, w_i, csa_q,
+                 hca_raw_kv, hca_logits, hca_pos_bias, hca_ckv, hca_q, B: int, m: int, k: int, csa_w: int = 8,
+                 csa_stride: int = 4, hca_w: int = 128, hca_stride: int = 128, window: int = 128,
+                 scale: float | None = None, return_lse: bool = False):
+        from ._lib import DecodeDesc
+
+        self._plan = None
+        for name, t in [("csa_raw_kv", csa_raw_kv), ("csa_ckv", csa_ckv), ("k_i", k_i), ("q_i", q_i),
+                        ("csa_q", csa_q), ("hca_raw_kv", hca_raw_kv), ("hca_ckv", hca_ckv), ("hca_q", hca_q)]:
+            _need(t, name)
+        dt = _fdt(csa_raw_kv, "csa_raw_kv")
+        _need(q_pos, "q_pos", torch.int32)
+        _need(reps, "reps", torch.float32, 3)
+        _need(w_i, "w_i", torch.float32)
+        bt, L, C = csa_raw_kv.shape
+        h, d = csa_q.shape[-2], csa_q.shape[-1]
+        if q_pos.numel() != bt or csa_q.numel() != bt * h * d or hca_q.numel() != bt * h * d:
+            raise ValueError("one query per sequence: q_pos [bt][1], csa_q / hca_q [bt][1][h][d]")
+        if C != 2 * d or tuple(hca_raw_kv.shape) != (bt, L, C):
+            raise ValueError("raw K|V rows must be [bt][L][2d] for both branches")
+        h_i, d_i = q_i.shape[-2], q_i.shape[-1]
+        if q_i.numel() != bt * h_i * d_i or w_i.numel() != bt * h_i:
+            raise ValueError("q_i must be [bt][1][h_i][d_i] and w_i [bt][1][h_i]")
+        for name, t in [("csa_logits", csa_logits), ("csa_pos_bias", csa_pos_bias), ("hca_logits", hca_logits),
+                        ("hca_pos_bias", hca_pos_bias)]:
+            if t is not None:
+                _need(t, name, torch.float32)
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        dev = csa_raw_kv.device
+        self.csa_out = torch.empty((bt, 1, h, d), dtype=torch.float32, device=dev)
+        self.hca_out = torch.empty((bt, 1, h, d), dtype=torch.float32, device=dev)
+        self.csa_lse = torch.empty((bt, 1, h), dtype=torch.float32, device=dev) if return_lse else None
+        self.hca_lse = torch.empty((bt, 1, h), dtype=torch.float32, device=dev) if return_lse else None
+        self._keep = [q_pos, csa_raw_kv, csa_logits, csa_pos_bias, csa_ckv, k_i, reps, q_i, w_i, csa_q, hca_raw_kv,
+                      hca_logits, hca_pos_bias, hca_ckv, hca_q]
+        self.device = dev
+        desc = DecodeDesc(dtype=dt, h=h, d=d, window=window, bt=bt, L=L, scale=scale, h_i=h_i, d_i=d_i, B=B, m=m,
+                          k=k, csa_w=csa_w, csa_stride=csa_stride, hca_w=hca_w, hca_stride=hca_stride,
+                          q_pos=_ptr(q_pos), csa_raw_kv=_ptr(csa_raw_kv), csa_logits=_ptr(csa_logits),
+                          csa_pos_bias=_ptr(csa_pos_bias), csa_ckv=_ptr(csa_ckv), k_i=_ptr(k_i), reps=_ptr(reps),
+                          q_i=_ptr(q_i), w_i=_ptr(w_i), csa_q=_ptr(csa_q), csa_out=_ptr(self.csa_out),
+                          csa_lse=_ptr(self.csa_lse), hca_raw_kv=_ptr(hca_raw_kv), hca_logits=_ptr(hca_logits),
+                          hca_pos_bias=_ptr(hca_pos_bias), hca_ckv=_ptr(hca_ckv), hca_q=_ptr(hca_q),
+                          hca_out=_ptr(self.hca_out), hca_lse=_ptr(self.hca_lse), ws=None, ws_bytes=0)
+        Lb = lib()
+        sz = ctypes.c_size_t(0)
+        check("hattn_decode_plan_ws_bytes", Lb.hattn_decode_plan_ws_bytes(ctypes.byref(desc), ctypes.byref(sz)))
+        self._ws = torch.empty(max(sz.value, 256), dtype=torch.uint8, device=dev)
+        desc.ws = self._ws.data_ptr()
+        desc.ws_bytes = self._ws.numel()
+        plan = ctypes.c_void_p()
+        with torch.cuda.device(dev):
+            check("hattn_decode_plan_create", Lb.hattn_decode_plan_create(ctypes.byref(desc), ctypes.byref(plan)))
+        self._plan = plan
+        self._run = Lb.hattn_decode_plan_run
+
+    def run(self, stream=None):
+        """Enqueues one step on `stream` (default: the current stream)."""
+        st = ctypes.c_void_p((stream or torch.cuda.current_stream(self.device)).cuda_stream)
+        status = self._run(self._plan, st)
+        if status != 0:
+            check("hattn_decode_plan_run", status)
+        return self.csa_out, self.hca_out
+
+    def close(self):
+        if self._plan is not None:
+            check("hattn_decode_plan_destroy", lib().hattn_decode_plan_destroy(self._plan))
+            self._plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

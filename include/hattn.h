@@ -224,6 +224,88 @@ hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, in
                                    int32_t B, float* reps, void* stream);
 
 /*
+ * Decode step of a hybrid layer pair, as a reusable plan.
+ * [HYB] section Compressed Sparse Attention and [HCA] section 它补的正是 CSA
+ * 的短板 (a CSA branch and an HCA branch side by side); the steps are the
+ * entry points above, for one new token per sequence (nq = 1) at q_pos[b]:
+ *   CSA branch: hattn_decode_append (with block means) -> hattn_hisa_topk
+ *               -> hattn_sparse_attn
+ *   HCA branch: hattn_decode_append (no block means)
+ *               -> hattn_dense_compressed_attn
+ * A plan validates every argument once and keeps the launch parameters, so
+ * running a step costs one host call, and everything runs on the caller's
+ * stream: the HCA branch's work shares the CSA branch's launches (one
+ * cache-maintenance launch for both layers, one attention launch, one merge
+ * launch), so the two branches overlap on the GPU without any cross-stream
+ * synchronisation.  Results equal those of the separate calls on the same
+ * arguments.
+ *
+ * hattn_decode_desc (all arrays as documented for the calls above; the two
+ * branches share bt, L, h, d, window, scale and q_pos):
+ *   dtype, bt, L, h, d, window, scale, q_pos [bt] int32
+ *   csa_raw_kv, csa_logits, csa_pos_bias, csa_w, csa_stride, csa_ckv
+ *     ([bt][N][2d], N = (L - csa_w) / csa_stride + 1; rewritten in place)
+ *   k_i [bt][N][d_i], reps [bt][ceil(N/B)][d_i] fp32 (rewritten in place),
+ *   q_i [bt][h_i][d_i], w_i [bt][h_i] fp32, h_i, d_i, B, m, k
+ *   csa_q [bt][h][d], csa_out [bt][h][d] fp32, csa_lse [bt][h] fp32 or NULL
+ *   hca_raw_kv, hca_logits, hca_pos_bias, hca_w, hca_stride, hca_ckv,
+ *   hca_q, hca_out, hca_lse     (as the CSA fields, for the HCA branch)
+ *   ws, ws_bytes               workspace (size: hattn_decode_plan_ws_bytes);
+ *                              holds visible counts, the selected indices and
+ *                              the calls' own workspaces
+ *
+ *   hattn_decode_desc_size()        sizeof(hattn_decode_desc), for bindings
+ *   hattn_decode_plan_ws_bytes(desc, &bytes)
+ *   hattn_decode_plan_create(desc, &plan)  validates (HATTN_ERR_ARG /
+ *       HATTN_ERR_UNSUPPORTED / HATTN_ERR_WORKSPACE as the separate calls
+ *       would) and records the current device.  The plan keeps the
+ *       pointers, not the data: every buffer must stay valid while the plan
+ *       is used.
+ *   hattn_decode_plan_run(plan, stream)  enqueues one step on `stream` (the
+ *       current device must be the plan's).  Two runs of one plan must not
+ *       overlap in time (they share the workspace).
+ *   hattn_decode_plan_destroy(plan)  frees the plan (host memory only);
+ *       NULL is accepted.
+ */
+typedef struct hattn_decode_desc {
+  int32_t dtype;
+  int32_t h, d, window;
+  int64_t bt, L;
+  float scale;
+  int32_t h_i, d_i, B, m, k;
+  int32_t csa_w, csa_stride, hca_w, hca_stride;
+  const int32_t* q_pos;
+  const void* csa_raw_kv;
+  const float* csa_logits;
+  const float* csa_pos_bias;
+  void* csa_ckv;
+  const void* k_i;
+  float* reps;
+  const void* q_i;
+  const float* w_i;
+  const void* csa_q;
+  float* csa_out;
+  float* csa_lse;
+  const void* hca_raw_kv;
+  const float* hca_logits;
+  const float* hca_pos_bias;
+  void* hca_ckv;
+  const void* hca_q;
+  float* hca_out;
+  float* hca_lse;
+  void* ws;
+  size_t ws_bytes;
+} hattn_decode_desc;
+
+typedef struct hattn_decode_plan* hattn_decode_plan_t;
+
+int64_t hattn_decode_desc_size(void);
+hattn_status_t hattn_decode_plan_ws_bytes(const hattn_decode_desc* desc, size_t* ws_bytes);
+hattn_status_t hattn_decode_plan_create(const hattn_decode_desc* desc, hattn_decode_plan_t* plan);
+hattn_status_t hattn_decode_plan_run(hattn_decode_plan_t plan, void* stream);
+hattn_status_t hattn_decode_plan_destroy(hattn_decode_plan_t plan);
+
+/*
  * Kernel timer (profiling aid).  When enabled, every kernel the library
  * launches is bracketed by HIP events recorded on the same stream, and its
  * duration is accumulated per kernel name when hattn_timer_collect() is

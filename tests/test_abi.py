@@ -127,3 +127,34 @@ def test_attention_validation(L):
     assert sz.value > 0
     g = L.hattn_sparse_attn
     assert g(1, p, p, 100, None, 8, p, 1000, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+
+
+def test_decode_plan_validation(L):
+    from compressed_attention_amd._lib import DecodeDesc
+    assert L.hattn_decode_desc_size() == ctypes.sizeof(DecodeDesc)
+    plan = ctypes.c_void_p()
+    sz = ctypes.c_size_t(0)
+    assert L.hattn_decode_plan_create(None, ctypes.byref(plan)) == 1
+    assert L.hattn_decode_plan_ws_bytes(None, ctypes.byref(sz)) == 1
+    p = ctypes.c_void_p(256)
+    d = DecodeDesc(dtype=1, h=64, d=128, window=128, bt=2, L=4096, scale=0.088, h_i=16, d_i=128, B=128, m=8, k=64,
+                   csa_w=8, csa_stride=4, hca_w=128, hca_stride=128, q_pos=p, csa_raw_kv=p, csa_ckv=p, k_i=p,
+                   reps=p, q_i=p, w_i=p, csa_q=p, csa_out=p, hca_raw_kv=p, hca_ckv=p, hca_q=p, hca_out=p)
+    assert L.hattn_decode_plan_ws_bytes(ctypes.byref(d), ctypes.byref(sz)) == 0 and sz.value > 0
+    d.k_i = None  # the CSA branch needs the indexer keys and block means
+    d.reps = None
+    assert L.hattn_decode_plan_ws_bytes(ctypes.byref(d), ctypes.byref(sz)) == 1
+    d.k_i, d.reps = p, p
+    d.bt = 0
+    assert L.hattn_decode_plan_ws_bytes(ctypes.byref(d), ctypes.byref(sz)) == 1
+    d.bt = 2
+    d.csa_w = 0
+    assert L.hattn_decode_plan_ws_bytes(ctypes.byref(d), ctypes.byref(sz)) == 1
+    d.csa_w = 8
+    d.csa_q = ctypes.c_void_p(264)  # misaligned
+    assert L.hattn_decode_plan_ws_bytes(ctypes.byref(d), ctypes.byref(sz)) == 1
+    assert b"aligned" in L.hattn_last_error()
+    d.csa_q = p
+    d.ws, d.ws_bytes = p, 16  # too small: refused before any device work
+    assert L.hattn_decode_plan_create(ctypes.byref(d), ctypes.byref(plan)) == 3
+    assert L.hattn_decode_plan_destroy(None) == 0

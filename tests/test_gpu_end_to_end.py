@@ -97,3 +97,60 @@ def test_decode_step_hybrid_pair_reduced():
         r_o2, _ = oracle.dense_compressed_attention(f64(t["hca_q"][b]), r_hkv, [Nh], raw_h, np.array([p]), 128, sc)
         assert np.abs(f64(o1[b]) - r_o1).max() < 1e-2
         assert np.abs(f64(o2[b]) - r_o2).max() < 1e-2
+
+
+def test_decode_plan_matches_separate_calls_and_oracle():
+    # The native decode-step plan (both branches, one host call) against the
+    # separate entry points on copies of the same caches (identical kernels:
+    # bit-exact), and against the oracle's step; then a second run on another
+    # stream reproduces the first.
+    bt, L = 2, 65536
+    N = oracle.n_entries(L, 8, 4)
+    Nh = oracle.n_entries(L, 128, 128)
+    w = synth.hybrid_pair_decode(1, device="cpu", bt=bt, L=L, N_csa=N)
+    t = w.tensors
+    t["q_i"] = synth.int_grid((bt, 1, 16, 128), 311, -4, 4, dtype=torch.bfloat16)
+    t["k_i"] = synth.int_grid((bt, N, 128), 312, -4, 4, dtype=torch.bfloat16)
+    t["w_i"] = synth.dyadic_uniform((bt, 1, 16), 313, bits=4)
+    g = {k_: v.to(DEV) for k_, v in t.items()}
+    B, m, k = 128, 64, 512
+    ckv = ops.compress(g["csa_raw_kv"], g["csa_z"], g["csa_b"], 8, 4)
+    hkv = ops.compress(g["hca_raw_kv"], g["hca_z"], g["hca_b"], 128, 128)
+    ckv[:, N - 1] = 0
+    hkv[:, Nh - 1] = 0
+    reps = ops.hisa_pool(g["k_i"], B)
+    reps[:, -1] = 0
+    ckv2, hkv2, reps2 = ckv.clone(), hkv.clone(), reps.clone()
+    plan = ops.DecodePlan(q_pos=g["q_pos"], csa_raw_kv=g["csa_raw_kv"], csa_logits=g["csa_z"], csa_pos_bias=g["csa_b"],
+                          csa_ckv=ckv, k_i=g["k_i"], reps=reps, q_i=g["q_i"], w_i=g["w_i"], csa_q=g["csa_q"],
+                          hca_raw_kv=g["hca_raw_kv"], hca_logits=g["hca_z"], hca_pos_bias=g["hca_b"], hca_ckv=hkv,
+                          hca_q=g["hca_q"], B=B, m=m, k=k, return_lse=True)
+    o1, o2 = plan.run()
+    # the same step through the separate calls
+    nv = ops.decode_append(g["csa_raw_kv"], g["csa_z"], g["csa_b"], 8, 4, g["q_pos"], ckv2, g["k_i"], reps2, B)
+    idx = ops.hisa_topk(g["q_i"], g["k_i"], g["w_i"], nv, reps2, B, m, k)
+    s1, l1 = ops.sparse_attn(g["csa_q"], ckv2, idx, g["csa_raw_kv"], g["q_pos"], 128, return_lse=True)
+    nvh = ops.decode_append(g["hca_raw_kv"], g["hca_z"], g["hca_b"], 128, 128, g["q_pos"], hkv2)
+    s2, l2 = ops.dense_compressed_attn(g["hca_q"], hkv2, nvh, g["hca_raw_kv"], g["q_pos"], 128, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ckv, ckv2) and torch.equal(hkv, hkv2) and torch.equal(reps, reps2)
+    assert torch.equal(o1, s1) and torch.equal(o2, s2)
+    assert torch.equal(plan.csa_lse, l1) and torch.equal(plan.hca_lse, l2)
+    first = (o1.clone(), o2.clone())
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        plan.run()
+    torch.cuda.synchronize()
+    assert torch.equal(plan.csa_out, first[0]) and torch.equal(plan.hca_out, first[1])
+    sc = 1 / math.sqrt(128)
+    for b in range(bt):
+        raw_c, raw_h = f64(t["csa_raw_kv"][b]), f64(t["hca_raw_kv"][b])
+        r_ckv = oracle.compress(raw_c, f64(t["csa_z"][b]), f64(t["csa_b"]), 8, 4)
+        r_hkv = oracle.compress(raw_h, f64(t["hca_z"][b]), f64(t["hca_b"]), 128, 128)
+        p = int(t["q_pos"][b, 0])
+        r_idx, _ = oracle.hisa_topk(f64(t["q_i"][b]), f64(t["k_i"][b]), f64(t["w_i"][b]), np.array([N]), B, m, k)
+        r_o1, _ = oracle.sparse_attention(f64(t["csa_q"][b]), r_ckv, r_idx, raw_c, np.array([p]), 128, sc)
+        r_o2, _ = oracle.dense_compressed_attention(f64(t["hca_q"][b]), r_hkv, [Nh], raw_h, np.array([p]), 128, sc)
+        assert np.abs(f64(o1[b]) - r_o1).max() < 1e-2
+        assert np.abs(f64(o2[b]) - r_o2).max() < 1e-2
+    plan.close()
