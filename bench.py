@@ -221,7 +221,8 @@ def hybrid_pair(args):
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1) / args.steps
     del g_csa, g_hca
-    kt = kernel_times(step, caches, args.steps)
+    kt = kernel_times(lambda p_: p_.run(), plans, args.steps)  # the timed path
+    kt_calls = kernel_times(step, caches, args.steps)  # the same step through the separate calls
     o1, o2 = step(caches[0])
     torch.cuda.synchronize()
     assert torch.isfinite(o1).all() and torch.isfinite(o2).all()
@@ -229,14 +230,13 @@ def hybrid_pair(args):
     # per-kernel algorithmic bytes for this step (one launch each)
     win = 128
     kb = {
-        "attn_dense_mfma": bt * attn_bytes(Nh + win),
-        "attn_sparse_mfma": bt * attn_bytes(k + win),
+        "attn_pair_mfma": bt * (attn_bytes(Nh + win) + attn_bytes(k + win)),  # HCA dense + CSA sparse, one launch
         "score_stage1_mfma": bt * hisa_stage1_bytes(nb),
         "score_stage2_mfma": bt * hisa_stage2_bytes(m * B),
     }
     step_bytes = sum(kb.values())
-    info = dict(ms=ms, graph_ms=graph_ms, kernels=kt, kernel_bytes=kb, step_bytes=step_bytes, bt=bt, N=N, Nh=Nh,
-                k=k, L=L)
+    info = dict(ms=ms, graph_ms=graph_ms, kernels=kt, kernels_calls=kt_calls, kernel_bytes=kb, step_bytes=step_bytes,
+                bt=bt, N=N, Nh=Nh, k=k, L=L)
     for p_ in plans:
         p_.close()
     return info
@@ -408,11 +408,12 @@ def cpu_baseline(args, k):
 
 
 # ----------------------------------------------------------------------------
-# counter probe: the dominant kernel alone, in the launch configuration the
-# step uses, plus a plain copy of known size that calibrates the counters
+# counter probe: the decode step as timed (its dominant kernel is the paired
+# attention launch), plus a plain copy of known size that calibrates the
+# counters
 # ----------------------------------------------------------------------------
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_dense_hybrid_pair_b8_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_pair_decode_1M_b8_traffic.txt")
 ATTN_SOURCES = ["compressed_attention_amd/csrc/attention.hip", "compressed_attention_amd/csrc/common.h",
                 "compressed_attention_amd/csrc/internal.h"]
 COPY_BYTES = 256 * MiB
@@ -428,30 +429,39 @@ def attn_sources_sha():
     return h.hexdigest()[:16]
 
 
-def probe_attn_dense(args):
-    """Launches the layer pair's HCA dense attention (8 sequences, 8,192
-    entries + window) ``args.steps`` times over rotating cache replicas, then
-    copies a 256 MiB buffer 3 times.  Run under rocprofv3 --pmc."""
+def probe_decode_plan(args):
+    """Runs the layer-pair decode step (the native plan, 8 sequences at 1M)
+    ``args.steps`` times over rotating cache replicas, then copies a 256 MiB
+    buffer 3 times.  Run under rocprofv3 --pmc."""
     import torch
     from compressed_attention_amd import ops, synth
 
     dev = "cuda:0"
-    bt, L, Nh = 8, 1 << 20, 8192
-    W = synth.hybrid_pair_decode(0, device=dev, bt=bt, L=L, N_csa=262143)
+    bt, L, N, B, m = 8, 1 << 20, 262143, 128, 64
+    W = synth.hybrid_pair_decode(0, device=dev, bt=bt, L=L, N_csa=N)
     t = W.tensors
+    ckv = ops.compress(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4)
     hkv = ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128)
-    nvh = ops.visible_count(t["q_pos"], 128, 128, Nh)
-    caches = [hkv] + [hkv.clone() for _ in range(args.replicas - 1)]
+    reps = ops.hisa_pool(t["k_i"], B)
+    plans = []
+    for r in range(args.replicas):
+        c = (ckv, hkv, reps) if r == 0 else (ckv.clone(), hkv.clone(), reps.clone())
+        plans.append(ops.DecodePlan(q_pos=t["q_pos"], csa_raw_kv=t["csa_raw_kv"], csa_logits=t["csa_z"],
+                                    csa_pos_bias=t["csa_b"], csa_ckv=c[0], k_i=t["k_i"], reps=c[2], q_i=t["q_i"],
+                                    w_i=t["w_i"], csa_q=t["csa_q"], hca_raw_kv=t["hca_raw_kv"], hca_logits=t["hca_z"],
+                                    hca_pos_bias=t["hca_b"], hca_ckv=c[1], hca_q=t["hca_q"], B=B, m=m, k=args.k))
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    log(f"[probe] sources {attn_sources_sha()}: {args.steps} dense attention launches, then 3 copies of {COPY_BYTES} B")
+    log(f"[probe] sources {attn_sources_sha()}: {args.steps} decode steps, then 3 copies of {COPY_BYTES} B")
     for i in range(args.steps):
-        ops.dense_compressed_attn(t["hca_q"], caches[i % len(caches)], nvh, t["hca_raw_kv"], t["q_pos"], 128)
+        plans[i % len(plans)].run()
     torch.cuda.synchronize()
     for _ in range(3):
         torch.neg(src, out=dst)  # one elementwise kernel: reads and writes COPY_BYTES
     torch.cuda.synchronize()
+    for p_ in plans:
+        p_.close()
     log("[probe] done")
 
 
@@ -489,8 +499,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe", choices=["attn_dense"], default=None,
-                    help="run only the dominant kernel and a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--probe", choices=["decode_plan"], default=None,
+                    help="run only the decode step and a calibration copy (for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -503,8 +513,8 @@ def main():
     from compressed_attention_amd import _lib
 
     _lib.lib()  # fail loudly if the HIP library is missing
-    if args.probe == "attn_dense":
-        probe_attn_dense(args)
+    if args.probe == "decode_plan":
+        probe_decode_plan(args)
         return
 
     main_k = args.k
@@ -563,7 +573,7 @@ def main():
     dom = max((kk for kk in kt if kk in res["kernel_bytes"]), key=lambda kk: kt[kk][0] * kt[kk][1])
     dom_ms = kt[dom][0]
     dom_bytes = res["kernel_bytes"].get(dom)
-    traffic = load_traffic() if dom == "attn_dense_mfma" else None
+    traffic = load_traffic() if dom == "attn_pair_mfma" else None
     roof = dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None,
                 traffic=None if traffic is None else round(traffic), kernel=dom, kernel_us=dom_ms * 1e3)
     if dom_bytes:
@@ -590,6 +600,7 @@ def main():
         "step_hbm_frac": round(res["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,
         "kernels_us": {kk: round(v[0] * 1e3, 2) for kk, v in kt.items()},
+        "kernels_us_separate_calls": {kk: round(v[0] * 1e3, 2) for kk, v in res["kernels_calls"].items()},
         "step_us_two_graphs": round(res["graph_ms"] * 1e3, 1),
         "extras": extras,
     }
