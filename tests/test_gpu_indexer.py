@@ -224,7 +224,8 @@ def test_hisa_float_inputs_vs_oracle():
 
 
 @pytest.mark.parametrize("N,B,m,k", [(20000, 128, 64, 2048), (262143, 128, 64, 512), (5000, 64, 8, 300),
-                                     (20000, 8, 1100, 2048)])  # last: more chosen blocks than LDS slots
+                                     (20000, 8, 1100, 2048),  # more chosen blocks than LDS slots
+                                     (20000, 2, 64, 100)])  # over 8,192 blocks a row: the 1,024-thread block select
 def test_hisa_decode_shape_exact(N, B, m, k):
     # One query per sequence (the decode launch shape), ragged last block,
     # integer grid with 4-bit weights (stage-1 scores exact, bound asserted).
