@@ -11,44 +11,11 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "append.h"
 #include "common.h"
 #include "internal.h"
 
 namespace hattn {
-
-template <typename T>
-struct Vec16;
-template <>
-struct Vec16<float> {
-  static constexpr int N = 4;
-  static HATTN_DEV void unpack(u32x4_t v, float* f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
-  }
-  static HATTN_DEV u32x4_t pack(const float* f) {
-    u32x4_t v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(f[i]);
-    return v;
-  }
-};
-template <>
-struct Vec16<uint16_t> {
-  static constexpr int N = 8;
-  static HATTN_DEV void unpack(u32x4_t v, float* f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16lo(v[i]);
-      f[2 * i + 1] = bf16hi(v[i]);
-    }
-  }
-  static HATTN_DEV u32x4_t pack(const float* f) {
-    u32x4_t v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
-    return v;
-  }
-};
 
 // Generic window: any w, s.  Thread = (sequence, run of entries, 16-byte slot).
 template <typename T>
@@ -397,181 +364,6 @@ hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_
   return hipGetLastError();
 }
 
-
-// ---------------------------------------------------------------------------
-// Per-token maintenance of one compressed layer in a decode step, one query
-// (the newest token, at position p) per sequence:
-//   workgroup 0: the visible count at p; if the token completes entry
-//                e = (p - w + 1) / s, the softmax-weighted compression of
-//                that window into ckv[e] (weights in LDS; row groups sum
-//                their rows, the groups are added in a fixed order);
-//   workgroup 1: if it does and block means are kept, the mean of the HISA
-//                block holding e (entries past the last one count as zero).
-// The same arithmetic as hattn_compress / hattn_hisa_pool / the visible
-// count, in one launch instead of three.
-// ---------------------------------------------------------------------------
-constexpr int kAppNT = 512;  // threads per workgroup
-constexpr int kAppUNR = 8;   // rows each thread has in flight
-
-// Sums rows [0, n) of a [n][ld] matrix (16-byte slot cs, rows rg, rg + RG, ...)
-// with per-row weights wt(u) into acc.  The first batch of rows is already in
-// `first` (loaded before the weights were ready); later batches reuse it.
-// Loads of a batch are all issued before any is used.
-template <typename T, typename Wt>
-HATTN_DEV void append_rows(const T* __restrict__ base, int64_t ld, int n, int rg, int RG, u32x4_t (&first)[kAppUNR],
-                           Wt wt, float* acc) {
-  constexpr int V = Vec16<T>::N;
-  for (int u0 = rg; u0 < n; u0 += kAppUNR * RG) {
-    if (u0 != rg) {
-#pragma unroll
-      for (int k = 0; k < kAppUNR; ++k) {
-        const int u = u0 + k * RG;
-        first[k] = u < n ? ld16(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kAppUNR; ++k) {
-      const int u = u0 + k * RG;
-      if (u < n) {
-        float f[V];
-        Vec16<T>::unpack(first[k], f);
-        const float pu = wt(u);
-#pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(pu, f[i], acc[i]);
-      }
-    }
-  }
-}
-
-template <typename T>
-HATTN_DEV void append_first(const T* __restrict__ base, int64_t ld, int n, int rg, u32x4_t (&first)[kAppUNR], int RG) {
-#pragma unroll
-  for (int k = 0; k < kAppUNR; ++k) {
-    const int u = rg + k * RG;
-    first[k] = u < n ? ld16(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
-  }
-}
-
-// Per-token maintenance of one compressed layer: the launch arguments.
-struct AppendK {
-  const void* x;  // raw rows [bt][L][C]
-  int64_t L;
-  int C;
-  const float* z;
-  const float* bias;
-  int w, s;
-  void* y;  // entries [bt][N][C]
-  int64_t N;
-  int32_t* n_vis;
-  const void* k_i;  // [bt][N][d_i] or NULL
-  int d_i, B;
-  float* reps;  // [bt][ceil(N/B)][d_i] or NULL
-};
-
-// The entry the token at p completes (-1 if none) and the visible count.
-HATTN_DEV int64_t append_entry_of(const AppendK& a, int64_t p, int64_t* nv) {
-  const int64_t pe = p >= a.w - 1 ? idiv(p - a.w + 1, a.s) : -1;  // entry ending at or before p
-  *nv = pe + 1 > a.N ? a.N : pe + 1;
-  return pe >= 0 && pe * a.s == p - a.w + 1 && pe < a.N ? pe : -1;
-}
-
-// Workgroup role "entry": the visible count and, when the token completes
-// entry e, the softmax-weighted compression of its window into y[b][e].
-template <typename T>
-HATTN_DEV void append_entry_body(const AppendK& a, int64_t b, int64_t p, float* sm, float* red) {
-  constexpr int V = Vec16<T>::N;
-  const T* __restrict__ x = static_cast<const T*>(a.x);
-  const int C = a.C, w = a.w;
-  int64_t nv;
-  const int64_t e = append_entry_of(a, p, &nv);
-  if (threadIdx.x == 0) a.n_vis[b] = int32_t(nv);
-  if (e < 0) return;
-  const int slots = C / V;
-  const int RG = kAppNT / slots;
-  const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
-  const int64_t t0 = e * a.s;
-  const T* xb = x + (b * a.L + t0) * C + cs * V;
-  // the window's first rows go out before the softmax weights are known
-  u32x4_t first[kAppUNR];
-  if (rg < RG) append_first(xb, C, w, rg, first, RG);
-  float* wt = sm;        // [w] logits, then softmax numerators
-  float* part = sm + w;  // [RG][C] row-group partial sums
-  for (int u = threadIdx.x; u < w; u += kAppNT)
-    wt[u] = (a.z ? a.z[b * a.L + t0 + u] : 0.f) + (a.bias ? a.bias[u] : 0.f);
-  __syncthreads();
-  if (threadIdx.x < kWave) {
-    float mx = -INFINITY;
-    for (int u = threadIdx.x; u < w; u += kWave) mx = fmaxf(mx, wt[u]);
-    mx = wave_max(mx);
-    float den = 0.f;
-    for (int u = threadIdx.x; u < w; u += kWave) den += __expf(wt[u] - mx);
-    den = wave_sum(den);
-    if (threadIdx.x == 0) {
-      red[0] = mx;
-      red[1] = den;
-    }
-  }
-  __syncthreads();
-  const float mx = red[0], inv = 1.f / red[1];
-  if (rg < RG) {
-    float acc[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    append_rows(xb, C, w, rg, RG, first, [&](int u) { return __expf(wt[u] - mx); }, acc);
-#pragma unroll
-    for (int i = 0; i < V; ++i) part[rg * C + cs * V + i] = acc[i];
-  }
-  __syncthreads();
-  T* y = static_cast<T*>(a.y);
-  for (int c = threadIdx.x; c < slots; c += kAppNT) {
-    float r[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) r[i] = 0.f;
-    for (int g = 0; g < RG; ++g)
-#pragma unroll
-      for (int i = 0; i < V; ++i) r[i] += part[g * C + c * V + i];
-#pragma unroll
-    for (int i = 0; i < V; ++i) r[i] *= inv;
-    st16(y + (b * a.N + e) * C + c * V, Vec16<T>::pack(r));
-  }
-}
-
-// Workgroup role "block mean": the mean of the HISA block holding the
-// completed entry (entries past the last one count as zero).
-template <typename T>
-HATTN_DEV void append_mean_body(const AppendK& a, int64_t b, int64_t p, float* sm) {
-  constexpr int V = Vec16<T>::N;
-  int64_t nv;
-  const int64_t e = append_entry_of(a, p, &nv);
-  if (e < 0 || !a.reps) return;
-  const int B = a.B, d_i = a.d_i;
-  const int64_t nb = idiv(a.N + B - 1, B);
-  const int64_t j = idiv(e, B);
-  const int64_t i0 = j * B;
-  const int cnt = int(imin64(a.N, i0 + B) - i0);
-  const int slots = d_i / V;
-  const int RG = kAppNT / slots;
-  const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
-  float* part = sm;  // [RG][d_i]
-  if (rg < RG) {
-    const T* kb = static_cast<const T*>(a.k_i) + (b * a.N + i0) * d_i + cs * V;
-    u32x4_t first[kAppUNR];
-    append_first(kb, d_i, cnt, rg, first, RG);
-    float acc[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    append_rows(kb, d_i, cnt, rg, RG, first, [](int) { return 1.f; }, acc);
-#pragma unroll
-    for (int i = 0; i < V; ++i) part[rg * d_i + cs * V + i] = acc[i];
-  }
-  __syncthreads();
-  const float invb = 1.f / float(B);
-  for (int c = threadIdx.x; c < d_i; c += kAppNT) {
-    float r = 0.f;
-    for (int g = 0; g < RG; ++g) r += part[g * d_i + c];
-    a.reps[(b * nb + j) * d_i + c] = r * invb;
-  }
-}
 
 // One launch for one or two layers, grid (roles, bt): layer a's entry, then
 // (when a keeps block means) its block mean, then (when b_on) layer b's

@@ -392,6 +392,7 @@ hattn_status_t hattn_timer_names(char* buf, int64_t len) {
 
 struct hattn_decode_plan {
   int device = -1;
+  bool front = false;  // stage 1 and cache maintenance in one launch
   int dtype = 0;
   int64_t bt = 0, L = 0;
   int C = 0;
@@ -497,6 +498,7 @@ hattn_status_t decode_layout(const hattn_decode_desc* d, size_t* total, hattn_de
   p->nv_hca = reinterpret_cast<int32_t*>(at(o_nvh));
   p->da = da;
   p->da_ws = at(o_da);
+  p->front = hattn::decode_front_ok(ia, d->B, d->m);
   return HATTN_OK;
 }
 
@@ -544,11 +546,22 @@ hattn_status_t hattn_decode_plan_run(hattn_decode_plan_t p, void* stream) {
   const hipStream_t st = (hipStream_t)stream;
   // Both branches on one stream: the HCA work rides in the CSA launches
   // (one cache-maintenance launch, one attention launch, one merge launch).
-  e = hattn::launch_append_pair(p->dtype, p->bt, p->q_pos, p->csa_raw_kv, p->csa_logits, p->csa_pos_bias, p->csa_w,
-                                p->csa_stride, p->csa_ckv, p->csa_N, p->nv_csa, p->k_i, p->d_i, p->B, p->reps,
-                                p->hca_raw_kv, p->hca_logits, p->hca_pos_bias, p->hca_w, p->hca_stride, p->hca_ckv,
-                                p->hca_N, p->nv_hca, p->L, p->C, st);
-  if (e == hipSuccess) e = hattn::launch_hisa_topk(p->ia, p->reps, p->B, p->m, p->k, p->idx, nullptr, p->hisa_ws, st);
+  if (p->front) {
+    // cache maintenance of both layers + HISA stage 1 in one launch
+    e = hattn::launch_decode_front(p->ia, p->reps, p->B, p->m, p->hisa_ws, p->q_pos, p->csa_raw_kv, p->csa_logits,
+                                   p->csa_pos_bias, p->csa_w, p->csa_stride, p->csa_ckv, p->nv_csa, p->hca_raw_kv,
+                                   p->hca_logits, p->hca_pos_bias, p->hca_w, p->hca_stride, p->hca_ckv, p->hca_N,
+                                   p->nv_hca, p->L, p->C, st);
+    if (e == hipSuccess)
+      e = hattn::launch_hisa_topk(p->ia, p->reps, p->B, p->m, p->k, p->idx, nullptr, p->hisa_ws, st, true);
+  } else {
+    e = hattn::launch_append_pair(p->dtype, p->bt, p->q_pos, p->csa_raw_kv, p->csa_logits, p->csa_pos_bias,
+                                  p->csa_w, p->csa_stride, p->csa_ckv, p->csa_N, p->nv_csa, p->k_i, p->d_i, p->B,
+                                  p->reps, p->hca_raw_kv, p->hca_logits, p->hca_pos_bias, p->hca_w, p->hca_stride,
+                                  p->hca_ckv, p->hca_N, p->nv_hca, p->L, p->C, st);
+    if (e == hipSuccess)
+      e = hattn::launch_hisa_topk(p->ia, p->reps, p->B, p->m, p->k, p->idx, nullptr, p->hisa_ws, st);
+  }
   if (e == hipSuccess) e = hattn::launch_attn_pair(p->sa, p->sa_ws, p->da, p->da_ws, st);
   return hip_status(e, "decode_plan_run");
 }

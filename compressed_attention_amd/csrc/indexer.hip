@@ -19,6 +19,7 @@
 // workspace and reduced by the LDS radix select of select.h.
 #include <algorithm>
 
+#include "append.h"
 #include "common.h"
 #include "internal.h"
 #include "select.h"
@@ -602,6 +603,126 @@ __global__ __launch_bounds__(256, 2) void score_stage1_x3_kernel(const uint16_t*
         if (j < my_nb[p]) srow[p][j] = tot;
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Decode front: HISA stage 1 for one query per sequence (the CSA layer) in
+// the same launch as the step's cache maintenance (the cache-maintenance
+// roles of append_kernel).  Grid (nch_grid + nroles, bt), 256 threads:
+//   x < nch_grid  stage 1 over 64 block means, as score_stage1_kernel with
+//                 one query; the visible count comes from q_pos and the CSA
+//                 geometry.  When the new token completes entry e, the
+//                 workgroup holding block e / B recomputes that block's mean
+//                 from K_I (entries past the last one count as zero), scores
+//                 it and writes it back to reps.
+//   x >= nch_grid role 0: the CSA entry the token completes + its visible
+//                 count; role 1: the same for the HCA layer.
+// The same arithmetic as hattn_decode_append + the stage-1 kernel; one
+// kernel boundary less on the decode critical path.
+// ---------------------------------------------------------------------------
+template <int KQ>
+__global__ __launch_bounds__(256, 2) void decode_front_kernel(const uint16_t* __restrict__ q_i,
+                                                              float* __restrict__ reps,
+                                                              const float* __restrict__ w_i,
+                                                              const int32_t* __restrict__ q_pos, int B, int64_t nb,
+                                                              int64_t ld, float* __restrict__ S1, int nch,
+                                                              int nch_grid, AppendK la, AppendK lb, int nroles) {
+  constexpr int D = 16 * KQ;
+  constexpr int TB = 64;
+  constexpr int PITCH = D + 4;
+  constexpr int PIECES = TB * D / 4 / 256;
+  constexpr int V = 8;  // bf16 per 16-byte slot
+  __shared__ __align__(16) float rt[TB * PITCH];
+  __shared__ float red[2];
+  const int64_t b = blockIdx.y;
+  if (int(blockIdx.x) >= nch_grid) {
+    const int role = int(blockIdx.x) - nch_grid;
+    const int64_t p = q_pos[b];
+    if (role == 0) append_entry_body<uint16_t, 256>(la, b, p, rt, red);
+    else if (role == 1 && nroles > 1) append_entry_body<uint16_t, 256>(lb, b, p, rt, red);
+    return;
+  }
+  int qg, ch;
+  if (!xcd_decode(blockIdx.x, 1, nch, &qg, &ch)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int64_t n = la.N;
+  const int64_t j0 = int64_t(ch) * TB;
+  const float* rb = reps + b * nb * D;
+  u32x4_t v[PIECES];
+#pragma unroll
+  for (int u = 0; u < PIECES; ++u) {
+    const int pp = threadIdx.x + 256 * u;
+    const int64_t j = j0 + pp / (D / 4);
+    v[u] = j < nb ? ld16(rb + j * D + (pp % (D / 4)) * 4) : u32x4_t{0, 0, 0, 0};
+  }
+  f32x4_t a[KQ];
+  {
+    const uint16_t* qp = q_i + (b * 16 + r16) * D + 4 * g;
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) load4_f32(qp + 16 * kq, a[kq]);
+  }
+  const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(w_i + b * 16 + 4 * g);
+  const int64_t p = q_pos[b];
+  int64_t nv;
+  const int64_t e = append_entry_of(la, p, &nv);
+  const int my_nb = int(idiv(nv + B - 1, B));
+  if (j0 >= my_nb) return;
+  // The block holding a newly completed entry: its mean, from K_I.
+  const int64_t jl = e >= 0 ? idiv(e, B) : -1;
+  const bool fresh = jl >= j0 && jl < j0 + TB;  // uniform
+  float mean_c = 0.f;
+  if (fresh) {
+    const int slots = D / V;
+    const int RG = 256 / slots;
+    const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
+    const int64_t i0 = jl * B;
+    const int cnt = int(imin64(n, i0 + B) - i0);
+    float* part = rt;  // [RG][D], before the tile lands
+    if (rg < RG) {
+      const uint16_t* kb = static_cast<const uint16_t*>(la.k_i) + (b * n + i0) * D + cs * V;
+      u32x4_t first[kAppUNR];
+      append_first(kb, D, cnt, rg, first, RG);
+      float acc[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      append_rows(kb, D, cnt, rg, RG, first, [](int) { return 1.f; }, acc);
+#pragma unroll
+      for (int i = 0; i < V; ++i) part[rg * D + cs * V + i] = acc[i];
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+      float r = 0.f;
+      for (int gg = 0; gg < RG; ++gg) r += part[gg * D + threadIdx.x];
+      mean_c = r * (1.f / float(B));
+      reps[(b * nb + jl) * D + threadIdx.x] = mean_c;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < PIECES; ++u) {
+    const int pp = threadIdx.x + 256 * u;
+    *reinterpret_cast<u32x4_t*>(&rt[(pp / (D / 4)) * PITCH + (pp % (D / 4)) * 4]) = v[u];
+  }
+  if (fresh) {
+    __syncthreads();  // the stale row has landed; replace it
+    if (threadIdx.x < D) rt[(jl - j0) * PITCH + threadIdx.x] = mean_c;
+  }
+  __syncthreads();
+  // one 16-block subtile per wave (the one-query layout of stage 1)
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kq = 0; kq < KQ; ++kq) {
+    const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(&rt[(16 * wave + r16) * PITCH + 16 * kq + 4 * g]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kq][j], bv[j], acc, 0, 0, 0);
+  }
+  float hsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hsum = fmaf(wv[i], relu_bits(acc[i]), hsum);
+  const float sc = sum_groups(hsum);
+  const int64_t j = j0 + 16 * wave + r16;
+  if (g == 0 && j < my_nb) S1[b * ld + j] = sc;
 }
 
 // ---------------------------------------------------------------------------
@@ -1357,8 +1478,40 @@ size_t hisa_topk_ws_bytes(const IndexArgs& a, int B, int m, int k) {
   return plan_hisa(a, B, m).total;
 }
 
+bool decode_front_ok(const IndexArgs& a, int B, int m) {
+  return a.dtype == 1 && a.h_i == 16 && a.d_i % 16 == 0 && a.d_i <= 256 && a.nq == 1 && !plan_hisa(a, B, m).bm &&
+         a.n > 0;
+}
+
+hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, void* ws, const int32_t* q_pos,
+                               const void* x1, const float* z1, const float* bias1, int w1, int s1, void* y1,
+                               int32_t* n_vis1, const void* x2, const float* z2, const float* bias2, int w2, int s2,
+                               void* y2, int64_t N2, int32_t* n_vis2, int64_t L, int C, hipStream_t st) {
+  const HisaPlan p = plan_hisa(a, B, m);
+  float* S1 = reinterpret_cast<float*>(ws);
+  const AppendK la{x1, L, C, z1, bias1, w1, s1, y1, a.n, n_vis1, a.k_i, a.d_i, B, reps};
+  const AppendK lb{x2, L, C, z2, bias2, w2, s2, y2, N2, n_vis2, nullptr, 0, 0, nullptr};
+  const int nch = int((p.nb + 63) / 64);
+  const int nch_grid = int(xcd_grid(1, nch));
+  const int nroles = x2 ? 2 : 1;
+  dim3 grid(unsigned(nch_grid + nroles), unsigned(a.bt));
+  LaunchScope ls("decode_front", st);
+#define HATTN_FRONT(KQ)                                                                                      \
+  HATTN_LAUNCH(decode_front_kernel<KQ>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i, reps, a.w_i, q_pos, B, \
+               p.nb, p.ld1, S1, nch, nch_grid, la, lb, nroles)
+  switch (a.d_i / 16) {
+    case 1: HATTN_FRONT(1); break;
+    case 2: HATTN_FRONT(2); break;
+    case 4: HATTN_FRONT(4); break;
+    case 8: HATTN_FRONT(8); break;
+    default: HATTN_FRONT(16); break;
+  }
+#undef HATTN_FRONT
+  return hipGetLastError();
+}
+
 hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m, int k, int32_t* idx, int32_t* blk,
-                            void* ws, hipStream_t st) {
+                            void* ws, hipStream_t st, bool stage1_done) {
   set_lds_limits();
   const HisaPlan p = plan_hisa(a, B, m);
   char* base = reinterpret_cast<char*>(ws);
@@ -1376,7 +1529,9 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   const int64_t bm_zero = bm ? a.bt * p.nb : 0;
   const bool x3 = mfma1 && a.dtype == 1 && a.nq >= 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128) &&
                   p.nb < (int64_t(1) << 31);
-  if (x3) {
+  if (stage1_done) {
+    // S1 was written by the decode front kernel
+  } else if (x3) {
     const int nqb = int((a.nq + 15) / 16);
     int chunk = 1024;  // blocks per workgroup, halved until ~4 workgroups per CU
     while (chunk > 64 && int64_t(nqb) * a.bt * ((p.nb + chunk - 1) / chunk) < 1024) chunk /= 2;

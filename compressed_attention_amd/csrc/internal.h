@@ -73,7 +73,17 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
 
 size_t hisa_topk_ws_bytes(const IndexArgs& a, int B, int m, int k);
 hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m, int k, int32_t* idx,
-                            int32_t* blk, void* ws, hipStream_t st);
+                            int32_t* blk, void* ws, hipStream_t st, bool stage1_done = false);
+// Decode front: HISA stage 1 for one query per sequence (into ws's S1, as
+// launch_hisa_topk lays it out) fused with the cache maintenance of the
+// layer behind the indexer (layer 1: its entry, visible count and the block
+// mean holding the new entry) and optionally a second layer (layer 2: entry
+// and visible count).  Then launch_hisa_topk(..., stage1_done = true).
+bool decode_front_ok(const IndexArgs& a, int B, int m);
+hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, void* ws, const int32_t* q_pos,
+                               const void* x1, const float* z1, const float* bias1, int w1, int s1, void* y1,
+                               int32_t* n_vis1, const void* x2, const float* z2, const float* bias2, int w2, int s2,
+                               void* y2, int64_t N2, int32_t* n_vis2, int64_t L, int C, hipStream_t st);
 
 // ---- attention -------------------------------------------------------------
 struct AttnArgs {
