@@ -14,9 +14,10 @@ CSA entries, 8,192 HCA entries):
        -> dense attention
 
 Every step is one run of a native decode plan (hattn_decode_plan_run): one
-host call enqueues 7 kernels on the current stream, the HCA branch's work
-riding in the CSA branch's launches (a shared cache-maintenance launch, a
-shared attention launch, a shared merge launch), so the branches overlap on
+host call enqueues 6 kernels on the current stream, the HCA branch's work
+riding in the CSA branch's launches (a shared launch for both caches'
+maintenance and HISA's block scores, a shared attention launch, a shared
+merge launch), so the branches overlap on
 the GPU with no cross-stream synchronisation.  (The same step as two HIP
 graphs on two streams joined every step is reported beside it: torch's graph
 replays and stream joins cost more host time than the GPU needs.)
@@ -173,7 +174,7 @@ def hybrid_pair(args):
         return csa_step(c), hca_step(c)
 
     # The two branches' inputs are independent.  Each step is one native
-    # plan run (hattn_decode_plan_run): one host call, 7 kernels on the
+    # plan run (hattn_decode_plan_run): one host call, 6 kernels on the
     # current stream with the HCA work inside the CSA launches.  One plan per
     # cache replica.
     plans = [ops.DecodePlan(q_pos=t["q_pos"], csa_raw_kv=t["csa_raw_kv"], csa_logits=t["csa_z"],
@@ -595,7 +596,7 @@ def main():
         "config": {"workload": "hybrid_pair_decode_1M", "batch": res["bt"], "context": res["L"], "heads": 64,
                    "head_dim": 128, "window": 128, "csa_entries": res["N"], "hca_entries": res["Nh"],
                    "indexer": "16x128", "hisa_B": 128, "hisa_m": 64, "k": res["k"], "cache_replicas": args.replicas,
-                   "launch": "native decode plan (one host call, 7 kernels per step)"},
+                   "launch": "native decode plan (one host call, 6 kernels per step)"},
         "step_GBps": round(res["step_bytes"] / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(res["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,

@@ -237,8 +237,10 @@ hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, in
  * stream: the HCA branch's work shares the CSA branch's launches (one
  * cache-maintenance launch for both layers, one attention launch, one merge
  * launch), so the two branches overlap on the GPU without any cross-stream
- * synchronisation.  Results equal those of the separate calls on the same
- * arguments.
+ * synchronisation.  For bf16 with h_i = 16 the cache-maintenance launch also
+ * computes HISA's block scores (the first stage); the workgroup that scores
+ * the block holding the new entry recomputes that block's mean itself.
+ * Results equal those of the separate calls on the same arguments.
  *
  * hattn_decode_desc (all arrays as documented for the calls above; the two
  * branches share bt, L, h, d, window, scale and q_pos):
