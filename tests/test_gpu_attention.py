@@ -148,3 +148,32 @@ def test_deterministic():
     b = ops.dense_compressed_attn(q, ckv, nv, raw, pos, 128)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_long_chunks_ragged(d):
+    # 18 queries x ~6K keys, 64 heads: chunks of 320 keys (5 tiles, an odd
+    # count) over ragged visible counts, partial windows and sparse holes.
+    bt, nq, L, N, h = 2, 9, 6500, 6000, 64
+    dt = torch.bfloat16
+    raw = synth.normal((bt, L, 2 * d), 100 + d, dtype=dt).to(DEV)
+    ckv = synth.normal((bt, N, 2 * d), 101 + d, dtype=dt).to(DEV)
+    q = synth.normal((bt, nq, h, d), 102 + d, dtype=dt).to(DEV)
+    pos = torch.tensor([[0, 1, 63, 127, 128, 3000, 6497, 6498, 6499]] * bt, dtype=torch.int32)
+    nv = torch.tensor([[0, 1, 63, 64, 65, 4097, 5999, 6000, 6000], [6000, 0, 5937, 17, 6000, 4000, 2, 128, 5001]],
+                      dtype=torch.int32)
+    out, lse = ops.dense_compressed_attn(q, ckv, nv.to(DEV), raw, pos.to(DEV), 128, return_lse=True)
+    k = 5000
+    idx = synth.random_index_lists(nv.reshape(-1), k, seed=103 + d, n_pad_holes=7).reshape(bt, nq, k)
+    idx[1, 4, 100] = N + 9  # out of range: skipped
+    out_s, lse_s = ops.sparse_attn(q, ckv, idx.to(DEV), raw, pos.to(DEV), 128, return_lse=True)
+    torch.cuda.synchronize()
+    for b in range(bt):
+        ro, rl = oracle.dense_compressed_attention(f64(q[b]), f64(ckv[b]), nv[b].numpy(), f64(raw[b]),
+                                                   pos[b].numpy(), 128, 1 / math.sqrt(d))
+        _check(out[b], lse[b], ro, rl)
+        ii = idx[b].numpy().copy()
+        ii[ii >= N] = -1
+        ro, rl = oracle.sparse_attention(f64(q[b]), f64(ckv[b]), ii, f64(raw[b]), pos[b].numpy(), 128,
+                                         1 / math.sqrt(d))
+        _check(out_s[b], lse_s[b], ro, rl)
