@@ -130,7 +130,7 @@ HATTN_DEV int mbcnt(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
 }
 
-HATTN_DEV uint64_t ballot(bool p) { return __ballot(p); }
+HATTN_DEV uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
 // 16-byte global load/store helpers.
 HATTN_DEV u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }

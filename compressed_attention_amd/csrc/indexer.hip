@@ -179,14 +179,29 @@ __global__ __launch_bounds__(64 * NWQ, KS >= 8 ? 1 : 8 / NWQ) void score_flat_mf
 // {4h..4h+3, 8+4h..8+4h+3} (h = l/32) of both queries of the pair: it sums
 // its 8 heads per query and one lane swap between the wave halves finishes
 // both queries' head sums (lanes < 32: first query, lanes >= 32: second).
+//
+// The key axis may be virtual: key tile t of the launch is tile t * tstride
+// of the cache (tstride = 1: every key).  MODE 0 stores every score at its
+// launch position (with tstride > 1 that is a compact, evenly spread sample
+// of the row).  MODE 1 keeps only the scores >= the row's threshold thr[row]
+// (an order key): a wave owns its four queries for the whole chunk, so it
+// packs their candidates (score, key index) into the chunk's span of the
+// query's row of S, in increasing key order, with ballot ranks, and stores
+// the counts in ccnt[row][chunk] (a count above the span's capacity of
+// chunk/2 pairs means some were dropped).  A row whose threshold is key 0
+// (take every key) gets plain scores, as in MODE 0.  A nonzero gate skips
+// the workgroups none of whose queries has gate[row] != 0.
 // ---------------------------------------------------------------------------
-template <int KS>
+template <int KS, int MODE>
 __global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_t* __restrict__ q_i,
                                                                    const uint16_t* __restrict__ k_i,
                                                                    const float* __restrict__ w_i,
                                                                    const int32_t* __restrict__ n_vis, int64_t nq,
                                                                    int64_t n, int64_t ld, float* __restrict__ S,
-                                                                   int nqb, int nch, int chunk) {
+                                                                   int nqb, int nch, int chunk, int tstride,
+                                                                   const uint32_t* __restrict__ thr,
+                                                                   int32_t* __restrict__ ccnt,
+                                                                   const int32_t* __restrict__ gate) {
   constexpr int D = 16 * KS;
   constexpr int TN = 64;
   constexpr int PITCH = D + 8;
@@ -204,15 +219,18 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_
   if (threadIdx.x < 16) {
     const int64_t q = q0 + threadIdx.x;
     int v = 0;
-    if (q < nq) v = int(imin64(n, imax64(0, n_vis[b * nq + q])));
+    if (q < nq && (!gate || gate[b * nq + q] != 0)) v = int(imin64(n, imax64(0, n_vis[b * nq + q])));
     s_nv[threadIdx.x] = v;
   }
   __syncthreads();
   int maxv = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) maxv = max(maxv, s_nv[i]);
+  // launch keys [e_begin, e_end): launch tile t holds cache keys
+  // [64 t tstride, 64 t tstride + 64)
   const int64_t e_begin = int64_t(ch) * chunk;
-  const int64_t e_end = imin64(e_begin + chunk, maxv);
+  const int64_t tiles_vis = (int64_t(maxv) + 64LL * tstride - 1) / (64LL * tstride);
+  const int64_t e_end = imin64(e_begin + chunk, tiles_vis * 64);
   if (e_begin >= e_end) return;
 
   // A operand: row c32 of pair p = (query 4*wave + 2p + c32/16, head c32%16)
@@ -221,6 +239,13 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_
   float wv[2][2][8];
   int my_nv[2];
   float* srow[2];
+  float my_thr[2];     // MODE 1: the query's threshold as a score
+  bool my_all[2];      // MODE 1: the query takes every key (plain scores)
+  float* creg[2];      // MODE 1: the chunk's span of the query's row
+  int my_cap[2];       // MODE 1: candidate pairs the chunk's span holds
+  // MODE 1: candidates so far of each pair's first / second query (uniform;
+  // two arrays indexed by the unrolled pair only, so they stay in registers)
+  int cnt_a[2] = {0, 0}, cnt_b[2] = {0, 0};
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     {
@@ -244,20 +269,35 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_
     const int64_t mq = q0 + 4 * wave + 2 * p + half;
     my_nv[p] = mq < nq ? s_nv[4 * wave + 2 * p + half] : 0;
     srow[p] = S + (b * nq + (mq < nq ? mq : 0)) * ld;
+    if (MODE == 1) {
+      // key 0 (take all) maps to -inf; any other key to the score it encodes
+      const uint32_t t = mq < nq ? thr[b * nq + mq] : 0u;
+      my_all[p] = t == 0u;
+      my_thr[p] = t == 0u ? INFINITY : key_to_float(t);  // +inf: nothing packed
+      creg[p] = srow[p] + e_begin;
+      my_cap[p] = int(imin64(chunk, ld - e_begin)) / 2;
+    }
   }
+
+  // MODE 1: does any of the wave's queries take every key (uniform)?
+  const bool any_all = MODE == 1 && ballot(my_all[0] || my_all[1]) != 0ull;
+  // MODE 1: all-ones in the lanes of each pair's second query
+  const uint32_t hsel = half ? 0xffffffffu : 0u;
 
   // Keys: 32-bit row indices (n < 2^31 is checked on the host).  Rows past
   // the end of the cache are read clamped to the last row; their scores are
-  // never stored (every stored key is below n_vis <= n).
+  // never stored (every stored key is below n_vis <= n).  A launch tile
+  // starting at e0 starts at cache key e0 * tstride.
   const uint16_t* kb = k_i + b * n * D;
   const int n32 = int(n);
+  const int ts = MODE == 1 ? 1 : tstride;  // the collecting pass reads every key
   u32x4_t pre[PIECES];
   auto load = [&](int e0) {
 #pragma unroll
     for (int j = 0; j < PIECES; ++j) {
       const int pc = threadIdx.x + 256 * j;
       const int row = pc / (D / 8), col = pc % (D / 8);
-      const int e = min(e0 + row, n32 - 1);
+      const int e = min(e0 * ts + row, n32 - 1);
       pre[j] = ld16(kb + size_t(e) * D + col * 8);
     }
   };
@@ -304,9 +344,37 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_
         // lanes < 32 receive the first query's total, lanes >= 32 the second's
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
         const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        const int e = e0 + 32 * kh + c32;
-        if (e < my_nv[p]) srow[p][e] = tot;
+        const int el = e0 + 32 * kh + c32;   // launch position
+        if (MODE == 0) {
+          const int e = e0 * ts + 32 * kh + c32;  // cache key
+          if (e < my_nv[p]) srow[p][el] = tot;
+        } else {
+          if (any_all && my_all[p] && el < my_nv[p]) srow[p][el] = tot;
+          const bool ok = el < my_nv[p] && tot >= my_thr[p];
+          const uint64_t m = ballot(ok);
+          if (m != 0ull) {
+            const uint32_t mlo = uint32_t(m), mhi = uint32_t(m >> 32);
+            const int clo = __popc(mlo), chi = __popc(mhi);
+            // rank among the set lanes below this one over the whole wave,
+            // minus the first query's count in the second query's lanes, plus
+            // the lane's query's running count
+            const int delta = (cnt_b[p] - clo) - cnt_a[p];  // uniform
+            const int slot = int(__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u))) + cnt_a[p] +
+                             int(uint32_t(delta) & hsel);
+            if (ok && slot < my_cap[p])
+              *reinterpret_cast<float2*>(creg[p] + 2 * slot) = make_float2(tot, __int_as_float(el));
+            cnt_a[p] += clo;
+            cnt_b[p] += chi;
+          }
+        }
       }
+  }
+  if (MODE == 1 && c32 == 0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int64_t mq = q0 + 4 * wave + 2 * p + half;
+      if (mq < nq) ccnt[(b * nq + mq) * nch + ch] = half ? cnt_b[p] : cnt_a[p];
+    }
   }
 }
 
@@ -1062,11 +1130,13 @@ constexpr int kSampW = kSampNT / kWave;      // waves per workgroup
 constexpr int kRegion = kSampleN / kSampW;   // candidate slots per wave
 constexpr size_t kSampLds = kSampleN * 6;    // u32 keys + u16 positions
 
+// With gate_by_flags, only rows whose flag is already nonzero run.
 __global__ __launch_bounds__(kSampNT, 4) void select_sampled_kernel(const float* __restrict__ S, int64_t ld,
                                                                 const int32_t* __restrict__ n_vis, int64_t n, int k,
                                                                 int32_t* __restrict__ idx,
                                                                 float* __restrict__ score_out,
-                                                                int32_t* __restrict__ flags) {
+                                                                int32_t* __restrict__ flags, int gate_by_flags,
+                                                                int64_t rows) {
   constexpr int NW = kSampW;
   static_assert(NW * kRegion == kSampleN && kRegion % kWave == 0, "region layout");
   extern __shared__ uint32_t dyn[];
@@ -1076,142 +1146,150 @@ __global__ __launch_bounds__(kSampNT, 4) void select_sampled_kernel(const float*
   __shared__ SelectShared<kSampNT> sh;
   __shared__ int wcnt[NW];
   __shared__ int verdict;
-  const int64_t row = blockIdx.x;
-  const int nv = int(imin64(n, imax64(0, n_vis[row])));
-  const float* srow = S + row * ld;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t* orow = idx + row * k;
-  float* scrow = score_out ? score_out + row * k : nullptr;
+  // One row per trip (a gated launch uses a small grid and loops over the
+  // rows; each row's work ends with a return from the lambda).
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    if (gate_by_flags && flags[row] == 0) continue;
+    auto run_row = [&]() {
+      const int nv = int(imin64(n, imax64(0, n_vis[row])));
+      const float* srow = S + row * ld;
+      const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+      int32_t* orow = idx + row * k;
+      float* scrow = score_out ? score_out + row * k : nullptr;
 
-  if (nv <= kSampleN) {  // short row: plain selection over all of it
-    const SelSeg sg = wave_segment<kSampNT>(nv);
-    uint32_t kc[kSelIT];
-    seg_keys_from_scores(srow, sg, kc);
-    const SelThr st = radix_threshold<kSampNT, kSelIT>(kc, sg.iters, k, sh);
-    const int chosen = emit_selected<kSampNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
-      orow[slot] = i;
-      if (scrow) scrow[slot] = key_to_float(key);
-    });
-    for (int t = chosen + threadIdx.x; t < k; t += kSampNT) {
-      orow[t] = -1;
-      if (scrow) scrow[t] = -INFINITY;
-    }
-    if (threadIdx.x == 0) flags[row] = 0;
-    return;
-  }
-  // Candidate positions are kept as 16-bit offsets inside each wave's
-  // segment; a row too long for that goes to the exact fallback.
-  const int segw = ((nv + NW - 1) / NW + 255) & ~255;
-  if (segw > 65536) {
-    if (threadIdx.x == 0) flags[row] = 1;
-    return;
-  }
-  // 1. sample: 16 evenly spaced runs of 512 scores (16-byte aligned)
-  {
-    const int stride = (nv / 16) & ~3;
-    for (int c = 0; c < 16; ++c) load_score_keys<kSampNT>(srow + c * stride, 512, samp + c * 512);
-  }
-  __syncthreads();
-  const SelSeg ssg = wave_segment<kSampNT>(kSampleN);
-  uint32_t skc[kSelIT];
-  seg_keys_from_u32(samp, ssg, skc);
-  __syncthreads();  // the sample's LDS becomes the candidate area
-  int r = min(kSampleN, int((3LL * k * kSampleN) / (2LL * nv)) + 32);
-  const int p0 = wave * segw, p1 = min(nv, p0 + segw);
-  bool done = false;
-  for (int attempt = 0; attempt < 4 && !done; ++attempt) {
-    const SelThr st = radix_threshold<kSampNT, kSelIT>(skc, ssg.iters, r, sh);
-    const uint32_t tau = st.thr;  // key of the r-th largest sample (0: all)
-    // 2. collect keys >= tau of this wave's segment, in position order
-    uint32_t* rk = rkey + wave * kRegion;
-    uint16_t* rp = rpos + wave * kRegion;
-    int cnt = 0;
-    // kCollectU 16-byte loads per lane in flight per sweep step
-    constexpr int kCollectU = 4;
-    for (int base = p0; base < p1; base += 256 * kCollectU) {
-      f32x4_t v[kCollectU];
-#pragma unroll
-      for (int u = 0; u < kCollectU; ++u) {
-        const int i = base + u * 256 + lane * 4;
-        if (i + 3 < p1) {
-          v[u] = *reinterpret_cast<const f32x4_t*>(srow + i);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[u][e] = i + e < p1 ? srow[i + e] : 0.f;
+      if (nv <= kSampleN) {  // short row: plain selection over all of it
+        const SelSeg sg = wave_segment<kSampNT>(nv);
+        uint32_t kc[kSelIT];
+        seg_keys_from_scores(srow, sg, kc);
+        const SelThr st = radix_threshold<kSampNT, kSelIT>(kc, sg.iters, k, sh);
+        const int chosen = emit_selected<kSampNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
+          orow[slot] = i;
+          if (scrow) scrow[slot] = key_to_float(key);
+        });
+        for (int t = chosen + threadIdx.x; t < k; t += kSampNT) {
+          orow[t] = -1;
+          if (scrow) scrow[t] = -INFINITY;
         }
+        if (threadIdx.x == 0) flags[row] = 0;
+        return;
       }
-#pragma unroll
-      for (int u = 0; u < kCollectU; ++u) {
-        const int i = base + u * 256 + lane * 4;
-        uint32_t key[4];
-        bool sel[4];
-        uint64_t bal[4];
-        int below = 0, total = 0;
-        const uint64_t lt = (1ull << lane) - 1ull;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          key[e] = i + e < p1 ? order_key(v[u][e]) : 0u;
-          sel[e] = key[e] != 0u && key[e] >= tau;
-          bal[e] = ballot(sel[e]);
-          below += __popcll(bal[e] & lt);
-          total += __popcll(bal[e]);
-        }
-        int slot = cnt + below;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (sel[e]) {
-            if (slot < kRegion) {
-              rk[slot] = key[e];
-              rp[slot] = uint16_t(i + e - p0);
+      // Candidate positions are kept as 16-bit offsets inside each wave's
+      // segment; a row too long for that goes to the exact fallback.
+      const int segw = ((nv + NW - 1) / NW + 255) & ~255;
+      if (segw > 65536) {
+        if (threadIdx.x == 0) flags[row] = 1;
+        return;
+      }
+      // 1. sample: 16 evenly spaced runs of 512 scores (16-byte aligned)
+      {
+        const int stride = (nv / 16) & ~3;
+        for (int c = 0; c < 16; ++c) load_score_keys<kSampNT>(srow + c * stride, 512, samp + c * 512);
+      }
+      __syncthreads();
+      const SelSeg ssg = wave_segment<kSampNT>(kSampleN);
+      uint32_t skc[kSelIT];
+      seg_keys_from_u32(samp, ssg, skc);
+      __syncthreads();  // the sample's LDS becomes the candidate area
+      int r = min(kSampleN, int((3LL * k * kSampleN) / (2LL * nv)) + 32);
+      const int p0 = wave * segw, p1 = min(nv, p0 + segw);
+      bool done = false;
+      for (int attempt = 0; attempt < 4 && !done; ++attempt) {
+        const SelThr st = radix_threshold<kSampNT, kSelIT>(skc, ssg.iters, r, sh);
+        const uint32_t tau = st.thr;  // key of the r-th largest sample (0: all)
+        // 2. collect keys >= tau of this wave's segment, in position order
+        uint32_t* rk = rkey + wave * kRegion;
+        uint16_t* rp = rpos + wave * kRegion;
+        int cnt = 0;
+        // kCollectU 16-byte loads per lane in flight per sweep step
+        constexpr int kCollectU = 4;
+        for (int base = p0; base < p1; base += 256 * kCollectU) {
+          f32x4_t v[kCollectU];
+    #pragma unroll
+          for (int u = 0; u < kCollectU; ++u) {
+            const int i = base + u * 256 + lane * 4;
+            if (i + 3 < p1) {
+              v[u] = *reinterpret_cast<const f32x4_t*>(srow + i);
+            } else {
+    #pragma unroll
+              for (int e = 0; e < 4; ++e) v[u][e] = i + e < p1 ? srow[i + e] : 0.f;
             }
-            ++slot;
+          }
+    #pragma unroll
+          for (int u = 0; u < kCollectU; ++u) {
+            const int i = base + u * 256 + lane * 4;
+            uint32_t key[4];
+            bool sel[4];
+            uint64_t bal[4];
+            int below = 0, total = 0;
+            const uint64_t lt = (1ull << lane) - 1ull;
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              key[e] = i + e < p1 ? order_key(v[u][e]) : 0u;
+              sel[e] = key[e] != 0u && key[e] >= tau;
+              bal[e] = ballot(sel[e]);
+              below += __popcll(bal[e] & lt);
+              total += __popcll(bal[e]);
+            }
+            int slot = cnt + below;
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (sel[e]) {
+                if (slot < kRegion) {
+                  rk[slot] = key[e];
+                  rp[slot] = uint16_t(i + e - p0);
+                }
+                ++slot;
+              }
+            }
+            cnt += total;
           }
         }
-        cnt += total;
+        if (lane == 0) wcnt[wave] = cnt;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          int tot = 0, ovf = 0;
+          for (int w = 0; w < NW; ++w) {
+            tot += wcnt[w];
+            ovf |= wcnt[w] > kRegion;
+          }
+          verdict = ovf ? 1 : (tot < k ? 2 : 0);  // 1: tau too low, 2: tau too high
+        }
+        __syncthreads();
+        const int vd = verdict;
+        if (vd == 0) {
+          for (int t = min(cnt, kRegion) + lane; t < kRegion; t += 64) rk[t] = 0u;
+          done = true;
+        } else {
+          const int r2 = vd == 1 ? max(1, r / 2) : min(kSampleN, r * 2);
+          if (r2 == r) break;
+          r = r2;
+        }
+        __syncthreads();
       }
-    }
-    if (lane == 0) wcnt[wave] = cnt;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int tot = 0, ovf = 0;
-      for (int w = 0; w < NW; ++w) {
-        tot += wcnt[w];
-        ovf |= wcnt[w] > kRegion;
+      if (!done) {
+        if (threadIdx.x == 0) flags[row] = 1;  // finished by the segment + merge kernels
+        return;
       }
-      verdict = ovf ? 1 : (tot < k ? 2 : 0);  // 1: tau too low, 2: tau too high
-    }
+      // 3. exact selection over the candidates (key 0 = empty slot); the wave
+      // segments of kSampleN keys are exactly the waves' regions
+      const SelSeg csg = wave_segment<kSampNT>(kSampleN);
+      uint32_t ckc[kSelIT];
+      seg_keys_from_u32(rkey, csg, ckc);
+      const SelThr st = radix_threshold<kSampNT, kSelIT>(ckc, csg.iters, k, sh);
+      // candidate i lies in the region (and segment) of the wave that emits it
+      const int chosen = emit_selected<kSampNT, kSelIT>(ckc, csg, sh, st, [&](int slot, int i, uint32_t key, int) {
+        orow[slot] = p0 + int(rpos[i]);
+        if (scrow) scrow[slot] = key_to_float(key);
+      });
+      for (int t = chosen + threadIdx.x; t < k; t += kSampNT) {
+        orow[t] = -1;
+        if (scrow) scrow[t] = -INFINITY;
+      }
+      if (threadIdx.x == 0) flags[row] = 0;
+    };
+    run_row();
     __syncthreads();
-    const int vd = verdict;
-    if (vd == 0) {
-      for (int t = min(cnt, kRegion) + lane; t < kRegion; t += 64) rk[t] = 0u;
-      done = true;
-    } else {
-      const int r2 = vd == 1 ? max(1, r / 2) : min(kSampleN, r * 2);
-      if (r2 == r) break;
-      r = r2;
-    }
-    __syncthreads();
   }
-  if (!done) {
-    if (threadIdx.x == 0) flags[row] = 1;  // finished by the segment + merge kernels
-    return;
-  }
-  // 3. exact selection over the candidates (key 0 = empty slot); the wave
-  // segments of kSampleN keys are exactly the waves' regions
-  const SelSeg csg = wave_segment<kSampNT>(kSampleN);
-  uint32_t ckc[kSelIT];
-  seg_keys_from_u32(rkey, csg, ckc);
-  const SelThr st = radix_threshold<kSampNT, kSelIT>(ckc, csg.iters, k, sh);
-  // candidate i lies in the region (and segment) of the wave that emits it
-  const int chosen = emit_selected<kSampNT, kSelIT>(ckc, csg, sh, st, [&](int slot, int i, uint32_t key, int) {
-    orow[slot] = p0 + int(rpos[i]);
-    if (scrow) scrow[slot] = key_to_float(key);
-  });
-  for (int t = chosen + threadIdx.x; t < k; t += kSampNT) {
-    orow[t] = -1;
-    if (scrow) scrow[t] = -INFINITY;
-  }
-  if (threadIdx.x == 0) flags[row] = 0;
 }
 
 // Level 1 for long flat rows: exact top-k of each segment (an element outside
@@ -1221,27 +1299,30 @@ __global__ __launch_bounds__(kSelNT) void select_segment_kernel(const float* __r
                                                                 const int32_t* __restrict__ n_vis, int64_t n, int seg,
                                                                 int nseg, int k, int kp, uint32_t* __restrict__ ckey,
                                                                 int32_t* __restrict__ cpos,
-                                                                const int32_t* __restrict__ flags) {
+                                                                const int32_t* __restrict__ flags, int64_t rows) {
   __shared__ SelectShared<kSelNT> sh;
-  const int64_t row = blockIdx.y;
-  if (flags[row] == 0) return;  // already selected by select_sampled_kernel
-  const int s = blockIdx.x;
-  const int64_t nv = imin64(n, imax64(0, n_vis[row]));
-  const int64_t p0 = int64_t(s) * seg;
-  const int cnt = int(imax64(0, imin64(seg, nv - p0)));
-  const SelSeg sg = wave_segment<kSelNT>(cnt);
-  uint32_t kc[kSelIT];
-  seg_keys_from_scores(S + row * ld + p0, sg, kc);
-  const SelThr st = radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
-  uint32_t* ok = ckey + (row * nseg + s) * int64_t(kp);
-  int32_t* op = cpos + (row * nseg + s) * int64_t(kp);
-  const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
-    ok[slot] = key;
-    op[slot] = int32_t(p0 + i);
-  });
-  for (int t = chosen + threadIdx.x; t < kp; t += kSelNT) {
-    ok[t] = 0u;
-    op[t] = -1;
+  // One row per trip: a gated launch uses a small grid and loops over rows.
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+    if (flags[row] == 0) continue;  // already selected by select_sampled_kernel
+    const int s = blockIdx.x;
+    const int64_t nv = imin64(n, imax64(0, n_vis[row]));
+    const int64_t p0 = int64_t(s) * seg;
+    const int cnt = int(imax64(0, imin64(seg, nv - p0)));
+    const SelSeg sg = wave_segment<kSelNT>(cnt);
+    uint32_t kc[kSelIT];
+    seg_keys_from_scores(S + row * ld + p0, sg, kc);
+    const SelThr st = radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
+    uint32_t* ok = ckey + (row * nseg + s) * int64_t(kp);
+    int32_t* op = cpos + (row * nseg + s) * int64_t(kp);
+    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
+      ok[slot] = key;
+      op[slot] = int32_t(p0 + i);
+    });
+    for (int t = chosen + threadIdx.x; t < kp; t += kSelNT) {
+      ok[t] = 0u;
+      op[t] = -1;
+    }
+    __syncthreads();
   }
 }
 
@@ -1252,53 +1333,227 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
                                                               int kp, uint32_t* __restrict__ okey,
                                                               int32_t* __restrict__ opos,
                                                               int32_t* __restrict__ idx, float* __restrict__ score_out,
-                                                              const int32_t* __restrict__ flags) {
+                                                              const int32_t* __restrict__ flags, int64_t rows) {
   __shared__ SelectShared<kSelNT> sh;
-  const int64_t row = blockIdx.y;
-  if (flags[row] == 0) return;  // already selected by select_sampled_kernel
-  const int grp = blockIdx.x;
-  const int nout = (nin + G - 1) / G;
-  const int l0 = grp * G, l1 = min(nin, l0 + G);
-  const int cnt = (l1 - l0) * kp;
-  const uint32_t* ik = ikey + (row * nin + l0) * int64_t(kp);
-  const int32_t* ip = ipos + (row * nin + l0) * int64_t(kp);
-  const SelSeg sg = wave_segment<kSelNT>(cnt);
+  // One row per trip: a gated launch uses a small grid and loops over rows.
+  for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+    if (flags[row] == 0) continue;  // already selected by select_sampled_kernel
+    const int grp = blockIdx.x;
+    const int nout = (nin + G - 1) / G;
+    const int l0 = grp * G, l1 = min(nin, l0 + G);
+    const int cnt = (l1 - l0) * kp;
+    const uint32_t* ik = ikey + (row * nin + l0) * int64_t(kp);
+    const int32_t* ip = ipos + (row * nin + l0) * int64_t(kp);
+    const SelSeg sg = wave_segment<kSelNT>(cnt);
+    uint32_t kc[kSelIT];
+    int32_t pc[kSelIT];
+    {
+      const int lane = threadIdx.x & (kWave - 1);
+  #pragma unroll
+      for (int it = 0; it < kSelIT; ++it) {
+        const int i = sg.p0 + it * kWave + lane;
+        const bool in = it < sg.iters && i < sg.p1;
+        kc[it] = in ? ik[i] : 0u;
+        pc[it] = in ? ip[i] : -1;
+      }
+    }
+    const SelThr st = radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
+    if (nout == 1) {
+      int32_t* orow = idx + row * k;
+      float* scrow = score_out ? score_out + row * k : nullptr;
+      const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int, uint32_t key, int it) {
+        orow[slot] = pc[it];
+        if (scrow) scrow[slot] = key_to_float(key);
+      });
+      for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
+        orow[t] = -1;
+        if (scrow) scrow[t] = -INFINITY;
+      }
+    } else {
+      uint32_t* ok = okey + (row * nout + grp) * int64_t(kp);
+      int32_t* op = opos + (row * nout + grp) * int64_t(kp);
+      const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int, uint32_t key, int it) {
+        ok[slot] = key;
+        op[slot] = pc[it];
+      });
+      for (int t = chosen + threadIdx.x; t < kp; t += kSelNT) {
+        ok[t] = 0u;
+        op[t] = -1;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Fused long flat rows, step 1 of 2 (after the sample scores): the row's
+// candidate threshold.  The sample holds the scores of every tstride-th
+// 64-key tile, packed (sample position i is cache key
+// (i / 64) * 64 * tstride + i % 64).  With v visible keys of which the
+// sample holds s, the threshold is the sample key of rank
+// r = max(2 k s / v, 64) (at most s): about 2k keys of the whole row are
+// expected at or above it, and at least k with overwhelming probability for
+// any row whose scores do not depend on the key's position modulo the
+// stride.  Rows with v <= k, or a sample of at most r keys, take every key
+// (threshold key 0).  Also clears the row's chunk counts.
+constexpr int kThrNT = 512;
+__global__ __launch_bounds__(kThrNT) void flat_threshold_kernel(const float* __restrict__ Ssamp, int64_t lds,
+                                                                const int32_t* __restrict__ n_vis, int64_t n,
+                                                                int tstride, int k, uint32_t* __restrict__ thr,
+                                                                int32_t* __restrict__ ccnt, int nch) {
+  __shared__ SelectShared<kThrNT> sh;
+  const int64_t row = blockIdx.x;
+  for (int c = threadIdx.x; c < nch; c += kThrNT) ccnt[row * nch + c] = 0;
+  const int nv = int(imin64(n, imax64(0, n_vis[row])));
+  const int64_t span = 64LL * tstride;
+  // sample keys below nv: whole tiles, then the part of the tile holding nv
+  const int64_t full = nv / span;
+  const int ns = int(int64_t(full) * 64 + imin64(64, nv - full * span));
+  const int nsl = int(imin64(lds, ((nv + span - 1) / span) * 64));
+  const SelSeg sg = wave_segment<kThrNT>(nsl);
+  uint32_t kc[kSelIT];
+  {
+    const float* src = Ssamp + row * lds;
+    const int lane = threadIdx.x & (kWave - 1);
+    float v[kSelIT];
+#pragma unroll
+    for (int it = 0; it < kSelIT; ++it) {
+      const int i = sg.p0 + it * kWave + lane;
+      v[it] = it < sg.iters && i < sg.p1 ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int it = 0; it < kSelIT; ++it) {
+      const int i = sg.p0 + it * kWave + lane;
+      const int64_t e = int64_t(i / 64) * span + (i & 63);
+      kc[it] = it < sg.iters && i < sg.p1 && e < nv ? order_key(v[it]) : 0u;
+    }
+  }
+  int r = int(imin64(ns, imax64(64, (2LL * k * ns + nv - 1) / imax64(1, nv))));
+  if (nv <= k) r = ns;  // every key
+  const SelThr st = radix_threshold<kThrNT, kSelIT>(kc, sg.iters, r, sh);
+  if (threadIdx.x == 0) thr[row] = nv <= k ? 0u : st.thr;
+}
+
+// Fused long flat rows, step 2 of 2: exact top-k over the row's candidates
+// (every key at or above the threshold, packed per key chunk by the score
+// kernel in increasing key order, so the concatenated list is in key order
+// and the usual position-order emission gives ascending indices and the
+// lower-index tie rule).  The result equals the top-k of the whole row when
+// at least k candidates exist (or every visible key is one) and no chunk's
+// span overflowed; otherwise the row is flagged for the full path.
+constexpr int kCandNT = 512;
+constexpr int kCandMaxChunks = 2 * kCandNT;
+__global__ __launch_bounds__(kCandNT) void flat_cand_select_kernel(const float* __restrict__ S, int64_t ld,
+                                                                   const uint32_t* __restrict__ thr,
+                                                                   const int32_t* __restrict__ ccnt, int nch,
+                                                                   int chunk, const int32_t* __restrict__ n_vis,
+                                                                   int64_t n, int k, int32_t* __restrict__ idx,
+                                                                   float* __restrict__ score_out,
+                                                                   int32_t* __restrict__ flags) {
+  __shared__ SelectShared<kCandNT> sh;
+  __shared__ int pre[kCandMaxChunks + 1];
+  __shared__ int bad;
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nv = int(imin64(n, imax64(0, n_vis[row])));
+  int32_t* orow = idx + row * k;
+  float* scrow = score_out ? score_out + row * k : nullptr;
+  if (thr[row] == 0u) {  // every visible key: plain scores at their positions
+    if (nv > kSelIT * kCandNT) {
+      if (threadIdx.x == 0) flags[row] = 1;
+      return;
+    }
+    const SelSeg sg = wave_segment<kCandNT>(nv);
+    uint32_t kc[kSelIT];
+    seg_keys_from_scores(S + row * ld, sg, kc);
+    const SelThr st = radix_threshold<kCandNT, kSelIT>(kc, sg.iters, k, sh);
+    const int chosen = emit_selected<kCandNT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
+      orow[slot] = i;
+      if (scrow) scrow[slot] = key_to_float(key);
+    });
+    for (int t = chosen + threadIdx.x; t < k; t += kCandNT) {
+      orow[t] = -1;
+      if (scrow) scrow[t] = -INFINITY;
+    }
+    if (threadIdx.x == 0) flags[row] = 0;
+    return;
+  }
+  // chunk c's span holds min(chunk, ld - c*chunk) / 2 pairs
+  if (threadIdx.x == 0) bad = 0;
+  // thread t owns chunks 2t and 2t+1 (nch <= 2 * kCandNT)
+  int my[2] = {0, 0};
+  bool over = false;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = 2 * int(threadIdx.x) + j;
+    if (c < nch) {
+      const int cap = int(imin64(chunk, ld - int64_t(c) * chunk)) / 2;
+      my[j] = ccnt[row * nch + c];
+      over |= my[j] > cap;
+    }
+  }
+  __syncthreads();
+  if (over) bad = 1;
+  // exclusive prefix of the counts
+  {
+    const int wave = wave_index();
+    const uint32_t v = uint32_t(my[0] + my[1]);
+    const uint32_t incl = wave_prefix_incl(v);
+    if (lane == kWave - 1) sh.wtot[wave] = incl;
+    __syncthreads();
+    uint32_t base = 0;
+    for (int w = 0; w < wave; ++w) base += sh.wtot[w];
+    const int c = 2 * int(threadIdx.x);
+    const int ex = int(base + incl - v);
+    if (c < nch) pre[c] = ex;
+    if (c + 1 < nch) pre[c + 1] = ex + my[0];
+    if (c + 1 == nch) pre[nch] = ex + my[0];
+    if (c + 2 == nch) pre[nch] = ex + my[0] + my[1];
+  }
+  __syncthreads();
+  const int total = pre[nch];
+  if (bad || total > kSelIT * kCandNT || (total < k && total < nv)) {
+    if (threadIdx.x == 0) flags[row] = 1;  // finished by the full path
+    return;
+  }
+  const SelSeg sg = wave_segment<kCandNT>(total);
   uint32_t kc[kSelIT];
   int32_t pc[kSelIT];
   {
-    const int lane = threadIdx.x & (kWave - 1);
+    const float* srow = S + row * ld;
+    float2 v[kSelIT];
+#pragma unroll
+    for (int it = 0; it < kSelIT; ++it) {
+      const int i = sg.p0 + it * kWave + lane;
+      v[it] = make_float2(0.f, 0.f);
+      if (it < sg.iters && i < sg.p1) {
+        // chunk holding candidate i: the last c with pre[c] <= i
+        int lo = 0, hi = nch - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= i) lo = mid;
+          else hi = mid - 1;
+        }
+        v[it] = *reinterpret_cast<const float2*>(srow + int64_t(lo) * chunk + 2 * (i - pre[lo]));
+      }
+    }
 #pragma unroll
     for (int it = 0; it < kSelIT; ++it) {
       const int i = sg.p0 + it * kWave + lane;
       const bool in = it < sg.iters && i < sg.p1;
-      kc[it] = in ? ik[i] : 0u;
-      pc[it] = in ? ip[i] : -1;
+      kc[it] = in ? order_key(v[it].x) : 0u;
+      pc[it] = in ? __float_as_int(v[it].y) : -1;
     }
   }
-  const SelThr st = radix_threshold<kSelNT, kSelIT>(kc, sg.iters, k, sh);
-  if (nout == 1) {
-    int32_t* orow = idx + row * k;
-    float* scrow = score_out ? score_out + row * k : nullptr;
-    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int, uint32_t key, int it) {
-      orow[slot] = pc[it];
-      if (scrow) scrow[slot] = key_to_float(key);
-    });
-    for (int t = chosen + threadIdx.x; t < k; t += kSelNT) {
-      orow[t] = -1;
-      if (scrow) scrow[t] = -INFINITY;
-    }
-  } else {
-    uint32_t* ok = okey + (row * nout + grp) * int64_t(kp);
-    int32_t* op = opos + (row * nout + grp) * int64_t(kp);
-    const int chosen = emit_selected<kSelNT, kSelIT>(kc, sg, sh, st, [&](int slot, int, uint32_t key, int it) {
-      ok[slot] = key;
-      op[slot] = pc[it];
-    });
-    for (int t = chosen + threadIdx.x; t < kp; t += kSelNT) {
-      ok[t] = 0u;
-      op[t] = -1;
-    }
+  const SelThr st = radix_threshold<kCandNT, kSelIT>(kc, sg.iters, k, sh);
+  const int chosen = emit_selected<kCandNT, kSelIT>(kc, sg, sh, st, [&](int slot, int, uint32_t key, int it) {
+    orow[slot] = pc[it];
+    if (scrow) scrow[slot] = key_to_float(key);
+  });
+  for (int t = chosen + threadIdx.x; t < k; t += kCandNT) {
+    orow[t] = -1;
+    if (scrow) scrow[t] = -INFINITY;
   }
+  if (threadIdx.x == 0) flags[row] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1312,11 +1567,26 @@ static bool flat_mfma_ok(const IndexArgs& a) {
          a.n < (int64_t(1) << 31);
 }
 
+// Key chunk of the MFMA flat score over nkeys launch keys: 2048 keys, halved
+// (down to 256) until the grid has about four workgroups per CU (two
+// resident, 256 CUs).
+static int flat_chunk(const IndexArgs& a, int64_t nkeys) {
+  const int64_t nqb = (a.nq + 15) / 16;
+  int chunk = 2048;
+  while (chunk > 256 && nqb * a.bt * ((nkeys + chunk - 1) / chunk) < 1024) chunk /= 2;
+  return chunk;
+}
+
 struct FlatPlan {
   int64_t rows, ld;
   bool multi;
   int seg, nseg, G, kp;
-  size_t s_bytes, cand_bytes, flag_bytes, total;
+  // fused path (long rows on the 32x32 MFMA score kernel): sample stride and
+  // row length, key chunk of the collecting pass and its chunk count
+  bool fused;
+  int tstride, chunk, nch;
+  int64_t lds;
+  size_t s_bytes, cand_bytes, flag_bytes, samp_bytes, thr_bytes, ccnt_bytes, total;
 };
 
 static FlatPlan plan_flat(const IndexArgs& a, int k) {
@@ -1335,8 +1605,20 @@ static FlatPlan plan_flat(const IndexArgs& a, int k) {
     const size_t l2 = size_t(p.rows) * ((p.nseg + p.G - 1) / p.G) * p.kp * 8;
     p.cand_bytes = align256(l1) + align256(l2);
     p.flag_bytes = align256(size_t(p.rows) * 4);
+    const int64_t ntiles = (a.n + 63) / 64;
+    p.chunk = flat_chunk(a, a.n);
+    p.nch = int((a.n + p.chunk - 1) / p.chunk);
+    p.fused = flat_mfma_ok(a) && a.d_i <= 128 && p.nch <= kCandMaxChunks && ntiles >= 64;
+    if (p.fused) {
+      // 64 to 128 sample tiles (4,096 to 8,192 sample keys) spread evenly
+      p.tstride = int(ntiles / 64);
+      p.lds = (ntiles + p.tstride - 1) / p.tstride * 64;
+      p.samp_bytes = align256(size_t(p.rows) * p.lds * 4);
+      p.thr_bytes = align256(size_t(p.rows) * 4);
+      p.ccnt_bytes = align256(size_t(p.rows) * p.nch * 4);
+    }
   }
-  p.total = p.s_bytes + p.cand_bytes + p.flag_bytes;
+  p.total = p.s_bytes + p.cand_bytes + p.flag_bytes + p.samp_bytes + p.thr_bytes + p.ccnt_bytes;
   return p;
 }
 
@@ -1360,36 +1642,64 @@ static void launch_valu_score(const IndexArgs& a, const TK* keys, int64_t keys_p
                      a.n_vis, blk, a.nq, a.h_i, a.d_i, a.n, keys_per_seq, B, m, ld, S);
 }
 
-static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, hipStream_t st) {
+// Flat scores of every visible key into S (row stride ld).  On the 32x32
+// MFMA kernel the extra arguments select the sample (tstride > 1: launch key
+// e is cache key (e / 64) * 64 * tstride + e % 64, nkeys launch keys per
+// row), the candidate collection (thr, ccnt, with chunk fixed by the plan),
+// or a gated pass (rows with gate[row] != 0 only).
+struct FlatScoreMode {
+  int64_t nkeys;
+  int tstride = 1;
+  const uint32_t* thr = nullptr;
+  int32_t* ccnt = nullptr;
+  const int32_t* gate = nullptr;
+  int chunk = 0;  // 0: flat_chunk(nkeys)
+};
+
+static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, const FlatScoreMode& fm,
+                                    hipStream_t st) {
   if (flat_mfma_ok(a)) {
     // 16 queries per workgroup.  (32, with 8 waves sharing each key tile,
     // measured slower: one resident workgroup per CU and longer barriers.)
     const int nqb = int((a.nq + 15) / 16);
-    // Key chunks of 2048 keys, halved (down to 256) until the grid has about
-    // four workgroups per CU (two resident, 256 CUs).
-    int chunk = 2048;
-    while (chunk > 256 && int64_t(nqb) * a.bt * ((a.n + chunk - 1) / chunk) < 1024) chunk /= 2;
-    const int nch = int((a.n + chunk - 1) / chunk);
+    const int chunk = fm.chunk ? fm.chunk : flat_chunk(a, fm.nkeys);
+    const int nch = int((fm.nkeys + chunk - 1) / chunk);
     dim3 grid(xcd_grid(nqb, nch), unsigned(a.bt));
-    LaunchScope ls("score_flat_mfma", st);
-#define HATTN_FLAT32(KS)                                                                                     \
-  HATTN_LAUNCH((score_flat_mfma32_kernel<KS>), grid, dim3(256), 0, st, (const uint16_t*)a.q_i,              \
-               (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk)
+    const bool collect = fm.thr != nullptr;
+    LaunchScope ls(collect             ? "score_flat_collect"
+                   : fm.tstride > 1    ? "score_flat_sample"
+                   : fm.gate != nullptr ? "score_flat_fallback"
+                                        : "score_flat_mfma",
+                   st);
+#define HATTN_FLAT32(KS, MODE)                                                                               \
+  HATTN_LAUNCH((score_flat_mfma32_kernel<KS, MODE>), grid, dim3(256), 0, st, (const uint16_t*)a.q_i,        \
+               (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk, fm.tstride, fm.thr, \
+               fm.ccnt, fm.gate)
 #define HATTN_FLAT(KS)                                                                                       \
   HATTN_LAUNCH((score_flat_mfma_kernel<KS, 4>), grid, dim3(256), 0, st, (const uint16_t*)a.q_i,             \
                (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.nq, a.n, ld, S, nqb, nch, chunk)
+    if (a.d_i == 256 && (collect || fm.tstride != 1 || fm.gate)) return hipErrorInvalidValue;
     switch (a.d_i) {
-      case 32: HATTN_FLAT32(2); break;
-      case 64: HATTN_FLAT32(4); break;
-      case 128: HATTN_FLAT32(8); break;
+      case 32:
+        if (collect) HATTN_FLAT32(2, 1);
+        else HATTN_FLAT32(2, 0);
+        break;
+      case 64:
+        if (collect) HATTN_FLAT32(4, 1);
+        else HATTN_FLAT32(4, 0);
+        break;
+      case 128:
+        if (collect) HATTN_FLAT32(8, 1);
+        else HATTN_FLAT32(8, 0);
+        break;
       default: HATTN_FLAT(8); break;
     }
 #undef HATTN_FLAT32
 #undef HATTN_FLAT
-  } else if (a.dtype == 0) {
-    launch_valu_score<0, float>(a, (const float*)a.k_i, a.n, a.n, nullptr, 1, 1, ld, S, st);
   } else {
-    launch_valu_score<0, uint16_t>(a, (const uint16_t*)a.k_i, a.n, a.n, nullptr, 1, 1, ld, S, st);
+    if (fm.thr || fm.tstride != 1 || fm.gate) return hipErrorInvalidValue;
+    if (a.dtype == 0) launch_valu_score<0, float>(a, (const float*)a.k_i, a.n, a.n, nullptr, 1, 1, ld, S, st);
+    else launch_valu_score<0, uint16_t>(a, (const uint16_t*)a.k_i, a.n, a.n, nullptr, 1, 1, ld, S, st);
   }
   return hipGetLastError();
 }
@@ -1398,9 +1708,12 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
   set_lds_limits();
   const FlatPlan p = plan_flat(a, k);
   float* S = reinterpret_cast<float*>(ws);
-  hipError_t e = launch_flat_score(a, p.ld, S, st);
-  if (e != hipSuccess) return e;
+  FlatScoreMode full;
+  full.nkeys = a.n;
+  hipError_t e;
   if (!p.multi) {
+    e = launch_flat_score(a, p.ld, S, full, st);
+    if (e != hipSuccess) return e;
     LaunchScope ls("select_rows", st);
     HATTN_LAUNCH((select_rows_kernel<0, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S, p.ld, a.n_vis,
                  nullptr, a.n, 1, 1, k, idx, score, nullptr, nullptr, int64_t(1), int64_t(1));
@@ -1416,17 +1729,62 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
   const int n2 = (p.nseg + p.G - 1) / p.G;
   bufp[1] = reinterpret_cast<int32_t*>(cb + l1 + size_t(p.rows) * n2 * p.kp * 4);
   int32_t* flags = reinterpret_cast<int32_t*>(cb + p.cand_bytes);
+  if (p.fused) {
+    // sample scores -> per-row threshold -> scores >= threshold, packed per
+    // chunk -> exact top-k of the candidates; rows the candidates cannot
+    // decide are flagged and run the full path below, gated by their flag
+    char* fb = cb + p.cand_bytes + p.flag_bytes;
+    float* Ssamp = reinterpret_cast<float*>(fb);
+    uint32_t* thr = reinterpret_cast<uint32_t*>(fb + p.samp_bytes);
+    int32_t* ccnt = reinterpret_cast<int32_t*>(fb + p.samp_bytes + p.thr_bytes);
+    FlatScoreMode sm;
+    sm.nkeys = p.lds;
+    sm.tstride = p.tstride;
+    e = launch_flat_score(a, p.lds, Ssamp, sm, st);
+    if (e != hipSuccess) return e;
+    {
+      LaunchScope ls("flat_threshold", st);
+      HATTN_LAUNCH(flat_threshold_kernel, dim3(unsigned(p.rows)), dim3(kThrNT), 0, st, Ssamp, p.lds, a.n_vis, a.n,
+                   p.tstride, k, thr, ccnt, p.nch);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    FlatScoreMode cm;
+    cm.nkeys = a.n;
+    cm.thr = thr;
+    cm.ccnt = ccnt;
+    cm.chunk = p.chunk;
+    e = launch_flat_score(a, p.ld, S, cm, st);
+    if (e != hipSuccess) return e;
+    {
+      LaunchScope ls("flat_cand_select", st);
+      HATTN_LAUNCH(flat_cand_select_kernel, dim3(unsigned(p.rows)), dim3(kCandNT), 0, st, S, p.ld, thr, ccnt, p.nch,
+                   p.chunk, a.n_vis, a.n, k, idx, score, flags);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    FlatScoreMode gm;
+    gm.nkeys = a.n;
+    gm.gate = flags;
+    e = launch_flat_score(a, p.ld, S, gm, st);
+  } else {
+    e = launch_flat_score(a, p.ld, S, full, st);
+  }
+  if (e != hipSuccess) return e;
+  // After the fused path only flagged rows (normally none) remain: small
+  // grids whose workgroups loop over the rows keep these launches cheap.
+  const int64_t grows = p.fused ? std::min<int64_t>(p.rows, 64) : p.rows;
   {
     LaunchScope ls("select_sampled", st);
-    HATTN_LAUNCH(select_sampled_kernel, dim3(unsigned(p.rows)), dim3(kSampNT), kSampLds, st, S, p.ld,
-                       a.n_vis, a.n, k, idx, score, flags);
+    HATTN_LAUNCH(select_sampled_kernel, dim3(unsigned(p.fused ? std::min<int64_t>(p.rows, 256) : p.rows)),
+                 dim3(kSampNT), kSampLds, st, S, p.ld, a.n_vis, a.n, k, idx, score, flags, p.fused ? 1 : 0, p.rows);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
     LaunchScope ls("select_segment", st);
-    HATTN_LAUNCH(select_segment_kernel, dim3(unsigned(p.nseg), unsigned(p.rows)), dim3(kSelNT), 0, st,
-                       S, p.ld, a.n_vis, a.n, p.seg, p.nseg, k, p.kp, bufk[0], bufp[0], flags);
+    HATTN_LAUNCH(select_segment_kernel, dim3(unsigned(p.nseg), unsigned(grows)), dim3(kSelNT), 0, st,
+                       S, p.ld, a.n_vis, a.n, p.seg, p.nseg, k, p.kp, bufk[0], bufp[0], flags, p.rows);
   }
   int nin = p.nseg, cur = 0;
   while (true) {
@@ -1434,8 +1792,9 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
     LaunchScope ls("select_merge", st);
     // Lists of a row at level i+1 never outnumber those at level i, so the
     // two buffers (sized for levels 1 and 2) alternate safely.
-    HATTN_LAUNCH(select_merge_kernel, dim3(unsigned(nout), unsigned(p.rows)), dim3(kSelNT), 0, st,
-                       bufk[cur], bufp[cur], nin, p.G, k, p.kp, bufk[cur ^ 1], bufp[cur ^ 1], idx, score, flags);
+    HATTN_LAUNCH(select_merge_kernel, dim3(unsigned(nout), unsigned(grows)), dim3(kSelNT), 0, st,
+                       bufk[cur], bufp[cur], nin, p.G, k, p.kp, bufk[cur ^ 1], bufp[cur ^ 1], idx, score, flags,
+                       p.rows);
     e = hipGetLastError();
     if (e != hipSuccess || nout == 1) return e;
     nin = nout;

@@ -288,3 +288,80 @@ def test_long_rows_ties_take_the_fallback_path():
     ref = oracle.flat_topk(f64(q_i[0, 1:]), f64(k_i[0]), f64(w_i[0, 1:]), nv[0, 1:].numpy(), k)
     mean, mn = iou_rows(got[1:], ref)
     assert mean >= 0.999, (mean, mn)
+
+
+def _top_rows_case(seed, N, nq, top_rows):
+    # Non-negative queries; ordinary keys on [-4, 4], the listed rows all +4:
+    # those keys share the largest score of every query (ties everywhere).
+    d = 128
+    q_i = synth.int_grid((1, nq, 16, d), seed, 0, 4, dtype=torch.bfloat16)
+    k_i = synth.int_grid((1, N, d), seed + 1, -4, 4, dtype=torch.bfloat16)
+    k_i[0, top_rows] = 4
+    w_i = synth.dyadic_uniform((1, nq, 16), seed + 2)
+    return q_i, k_i, w_i
+
+
+def _flat_exact(q_i, k_i, w_i, nv, k, rows):
+    idx, sc = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), k, return_scores=True)
+    torch.cuda.synchronize()
+    ref, ref_sc = oracle.flat_topk(f64(q_i[0, rows]), f64(k_i[0]), f64(w_i[0, rows]), nv[0, rows].numpy(), k,
+                                   return_scores=True)
+    got = idx.cpu().numpy()[0, rows]
+    assert np.array_equal(got, ref)
+    got_sc = f64(sc[0, rows])
+    assert np.array_equal(np.where(ref >= 0, got_sc, 0), np.where(ref >= 0, ref_sc, 0))
+
+
+def test_fused_flat_threshold_too_high_falls_back():
+    # Long rows take the fused path: a threshold from an evenly spread sample
+    # of 64-key tiles (every 17th tile at N = 70,000), then only scores above
+    # it are kept.  Here the first 8 keys of every sampled tile tie for the
+    # top score, so the sample puts the threshold at that score although only
+    # 512 keys reach it, fewer than k: the rows must take the full path.
+    N, nq, k = 70000, 16, 700
+    ntiles = (N + 63) // 64
+    ts = ntiles // 64
+    top = [t * 64 * ts + j for t in range((ntiles + ts - 1) // ts) for j in range(8) if t * 64 * ts + j < N]
+    q_i, k_i, w_i = _top_rows_case(221, N, nq, top)
+    nv = torch.tensor([[N] * 8 + [N - 1000 * i for i in range(1, 9)]], dtype=torch.int32)
+    _flat_exact(q_i, k_i, w_i, nv, k, list(range(nq)))
+
+
+def test_fused_flat_chunk_overflow_falls_back():
+    # 2,000 consecutive keys tie for the top score: more candidates than a key
+    # chunk's span holds, so those rows take the full path; rows that do not
+    # see the cluster stay on the fused path.
+    N, nq, k = 70000, 16, 2048
+    q_i, k_i, w_i = _top_rows_case(231, N, nq, list(range(20000, 22000)))
+    nv = torch.tensor([[N] * 6 + [21000, 20500, 20001, 19999, 19000, 50000, 60000, 65536, 69999, 100]],
+                      dtype=torch.int32)
+    _flat_exact(q_i, k_i, w_i, nv, k, list(range(nq)))
+
+
+def test_fused_flat_float_inputs_vs_oracle():
+    # Float inputs on the fused path (sample, threshold, candidates) at
+    # N = 50,000: agreement with the fp64 oracle up to near ties.
+    N, nq, k = 50000, 24, 2048
+    q_i = synth.normal((1, nq, 16, 128), 241, dtype=torch.bfloat16)
+    k_i = synth.normal((1, N, 128), 242, dtype=torch.bfloat16)
+    w_i = synth.uniform((1, nq, 16), 243)
+    nv = torch.tensor([[N - 7 * i for i in range(nq)]], dtype=torch.int32)
+    nv[0, 5] = 3000   # between k and 2k: every key is a candidate
+    nv[0, 6] = 2048   # exactly k
+    idx = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), k)
+    torch.cuda.synchronize()
+    q, kk, ww = f64(q_i[0]), f64(k_i[0]), f64(w_i[0])
+    nvh = nv[0].numpy()
+    ref = oracle.flat_topk(q, kk, ww, nvh, k)
+    got = idx.cpu().numpy()[0]
+    mean, mn = iou_rows(got, ref)
+    assert mean >= 0.999, (mean, mn)
+
+    def scores(r):
+        return oracle.index_scores(q[r], kk[: nvh[r]], ww[r])
+
+    def tol(r):  # fp32 accumulation bound, as in the 8K test
+        qa = np.abs(q[r])
+        return 128 * 2.0**-23 * float((ww[r][:, None] * (qa @ np.abs(kk).T)).max()) * 4
+
+    check_near_ties(got, ref, scores, tol)
