@@ -628,11 +628,12 @@ static AttnPlan plan_attn(const AttnArgs& a) {
   const int tk = mfma_shape(a) ? 64 : 32;  // keys per tile
   const int64_t rows = a.bt * a.nq;
   const int64_t maxkeys = (a.idx ? int64_t(a.k) : a.n) + a.window;
-  // MFMA kernel (two resident workgroups per CU): about 1.4 workgroups per
-  // CU of the 256 balances filling the chip against the h*d*4 bytes that
-  // every extra chunk writes as a partial and the merge reads back.  Never
-  // a chunk under 128 keys.
-  const int64_t target_wg = mfma_shape(a) ? 352 : 1024;
+  // MFMA kernel (two resident workgroups per CU): up to about 512
+  // workgroups, one per resident slot, balances filling the chip against
+  // the h*d*4 bytes that every extra chunk writes as a partial and the merge
+  // reads back (measured: 480 beat 352 and 704 at batch 32).  Never a chunk
+  // under 128 keys.
+  const int64_t target_wg = mfma_shape(a) ? 512 : 1024;
   int64_t chunk = (rows * maxkeys + target_wg - 1) / target_wg;
   chunk = std::max<int64_t>(chunk, 128);
   chunk = (chunk + tk - 1) / tk * tk;
