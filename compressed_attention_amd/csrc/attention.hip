@@ -475,13 +475,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
   }
 }
 
-// Combines per-chunk partials: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-// One workgroup per (query, 64 consecutive outputs of one head); four groups
-// of 64 threads take every fourth split.  Every thread first issues the loads
-// of its (up to kMergeRegs) partial outputs, then the head's (m_s, l_s) pairs
-// go to LDS and become weights w_s = 2^(m_s - M) / sum_t 2^(m_t - M) l_t, so
-// the whole merge costs about one memory round trip; the four groups are
-// added through LDS.  Needs d % 64 == 0 and nsplit <= 4 * kMergeRegs.
+// Combines per-chunk partials: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
+// with weights w_s = 2^(m_s - M) / sum_t 2^(m_t - M) l_t.  Needs
+// nsplit <= 4 * kMergeRegs and a head shape merge_fast() accepts.
 constexpr int kMergeRegs = 16;
 constexpr int kMergeMaxSplit = 4 * kMergeRegs;
 
@@ -494,75 +490,81 @@ struct MergeK {
   float* lse;
 };
 
+static bool merge_fast(int h, int d, int nsplit) {
+  return d % 64 == 0 && d <= 256 && (h * d) % 256 == 0 && nsplit <= kMergeMaxSplit;
+}
+
 struct MergeLds {
-  float wsh[kMergeMaxSplit];
-  float lsh[kMergeMaxSplit];
-  float red[4][64];
-  float stat[2];
+  float w[4][kMergeMaxSplit];  // weight of split s for each head of the group
+  f32x4_t red[4][64];
 };
 
+// One workgroup merges 256 consecutive outputs [e0, e0 + 256) of row qrow
+// (256 / D heads; d % 4 == 0 and h * d % 256 == 0).  Lane l of every wave
+// holds outputs e0 + 4l .. 4l + 3 (one head), and wave g sums splits
+// g, g + 4, ...: all partial loads and, in wave 0, the heads' (m_s, l_s)
+// loads are issued before anything waits, so the merge is one memory round
+// trip.  Wave 0 turns (m_s, l_s) into per-split weights (exp2(m_s - M) / den
+// with M the heads' largest m_s), the waves weight their partials, and the
+// four group sums are added through LDS in group order.
 HATTN_DEV void attn_merge_body(const MergeK& mk, int H, int D, int64_t qrow, int e0, MergeLds& sm) {
-  const float* __restrict__ part_o = mk.part_o;
-  const float* __restrict__ part_ml = mk.part_ml;
   const int nsplit = mk.nsplit;
-  float* __restrict__ out = mk.out;
-  float* __restrict__ lse = mk.lse;
-  float* wsh = sm.wsh;
-  float* lsh = sm.lsh;
-  float(*red)[64] = sm.red;
-  float* stat = sm.stat;
-  const int h = e0 / D;
   const int tid = threadIdx.x, lane = tid & 63, sg = tid >> 6;
-  const float* po = part_o + qrow * nsplit * H * D + e0 + lane;
+  const int hpg = 256 / D;            // heads in the group
+  const int h0 = e0 / D;
+  const int hl = (4 * lane) / D;      // this lane's head within the group
   const int64_t pos = int64_t(H) * D;
-  float ov[kMergeRegs];
+  const float* __restrict__ po = mk.part_o + qrow * nsplit * pos + e0 + 4 * lane;
+  f32x4_t ov[kMergeRegs];
 #pragma unroll
   for (int i = 0; i < kMergeRegs; ++i) {
     const int s = sg + 4 * i;
-    ov[i] = s < nsplit ? po[s * pos] : 0.f;
+    ov[i] = s < nsplit ? *reinterpret_cast<const f32x4_t*>(po + s * pos) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const float* ml = part_ml + (qrow * nsplit * H + h) * 2;
-  const int64_t mls = int64_t(H) * 2;
-  if (tid < nsplit) {
-    const float2 v = *reinterpret_cast<const float2*>(ml + tid * mls);
-    wsh[tid] = v.x;
-    lsh[tid] = v.y;
-  }
-  __syncthreads();
   if (sg == 0) {
-    float M = lane < nsplit ? wsh[lane] : -INFINITY;
-    M = wave_max(M);
-    float den = 0.f;
-    if (lane < nsplit && wsh[lane] != -INFINITY) den = exp2f(wsh[lane] - M) * lsh[lane];
-    den = wave_sum(den);
-    if (lane == 0) {
-      stat[0] = M;
-      stat[1] = den;
+    const float* __restrict__ ml = mk.part_ml + (qrow * nsplit * H + h0) * 2;
+    const int64_t mls = int64_t(H) * 2;
+    float2 v[4];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh)
+      v[hh] = hh < hpg && lane < nsplit ? *reinterpret_cast<const float2*>(ml + lane * mls + 2 * hh)
+                                        : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      if (hh < hpg) {
+        const float M = wave_max(v[hh].x);
+        float den = v[hh].x != -INFINITY ? exp2f(v[hh].x - M) * v[hh].y : 0.f;
+        den = wave_sum(den);
+        const float inv = den > 0.f ? 1.f / den : 0.f;
+        if (lane < nsplit) sm.w[hh][lane] = v[hh].x == -INFINITY ? 0.f : exp2f(v[hh].x - M) * inv;
+        if (lane == 0 && mk.lse) mk.lse[qrow * H + h0 + hh] = (M + __log2f(den)) * kLn2;
+      }
     }
   }
   __syncthreads();
-  const float M = stat[0], den = stat[1];
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  float num = 0.f;
+  f32x4_t num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < kMergeRegs; ++i) {
     const int s = sg + 4 * i;
     if (s < nsplit) {
-      const float ms = wsh[s];
-      num = fmaf(ms == -INFINITY ? 0.f : exp2f(ms - M) * inv, ov[i], num);
+      const float w = sm.w[hl][s];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) num[c] = fmaf(w, ov[i][c], num[c]);
     }
   }
-  red[sg][lane] = num;
+  sm.red[sg][lane] = num;
   __syncthreads();
   if (sg == 0) {
-    out[qrow * H * D + e0 + lane] = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-    if (lane == 0 && (e0 % D) == 0 && lse) lse[qrow * H + h] = (M + __log2f(den)) * kLn2;
+    f32x4_t r;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r[c] = sm.red[0][lane][c] + sm.red[1][lane][c] + sm.red[2][lane][c] + sm.red[3][lane][c];
+    *reinterpret_cast<f32x4_t*>(mk.out + qrow * H * D + e0 + 4 * lane) = r;
   }
 }
 
 __global__ __launch_bounds__(256) void attn_merge_kernel(MergeK mk, int H, int D) {
   __shared__ MergeLds sm;
-  attn_merge_body(mk, H, D, blockIdx.y, blockIdx.x * 64, sm);
+  attn_merge_body(mk, H, D, blockIdx.y, blockIdx.x * 256, sm);
 }
 
 // Two query sets' merges in one launch: rows [0, rows_a) of grid y are set
@@ -570,8 +572,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeK mk, int H, int D
 __global__ __launch_bounds__(256) void attn_merge_pair_kernel(MergeK a, int64_t rows_a, MergeK b, int H, int D) {
   __shared__ MergeLds sm;
   const int64_t y = blockIdx.y;
-  if (y < rows_a) attn_merge_body(a, H, D, y, blockIdx.x * 64, sm);
-  else attn_merge_body(b, H, D, y - rows_a, blockIdx.x * 64, sm);
+  if (y < rows_a) attn_merge_body(a, H, D, y, blockIdx.x * 256, sm);
+  else attn_merge_body(b, H, D, y - rows_a, blockIdx.x * 256, sm);
 }
 
 // Same combination for any head size or split count: one thread per output,
@@ -714,8 +716,8 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   LaunchScope ls("attn_merge", st);
-  if (a.d % 64 == 0 && pl.nsplit <= kMergeMaxSplit)
-    HATTN_LAUNCH(attn_merge_kernel, dim3(unsigned(a.h * a.d / 64), unsigned(a.bt * a.nq)), dim3(256), 0, st,
+  if (merge_fast(a.h, a.d, pl.nsplit))
+    HATTN_LAUNCH(attn_merge_kernel, dim3(unsigned(a.h * a.d / 256), unsigned(a.bt * a.nq)), dim3(256), 0, st,
                  MergeK{po, pml, pl.nsplit, a.out, a.lse}, a.h, a.d);
   else
     HATTN_LAUNCH(attn_merge_any_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256), 0,
@@ -769,10 +771,10 @@ hipError_t launch_attn_pair(const AttnArgs& s, void* ws_s, const AttnArgs& d, vo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const bool ms = ps.nsplit > 1, md = pd.nsplit > 1;
-  const bool fast = s.d % 64 == 0 && ps.nsplit <= kMergeMaxSplit && pd.nsplit <= kMergeMaxSplit;
+  const bool fast = merge_fast(s.h, s.d, ps.nsplit) && merge_fast(d.h, d.d, pd.nsplit);
   LaunchScope ls("attn_merge", st);
   const MergeK mks{po_s, pml_s, ps.nsplit, s.out, s.lse}, mkd{po_d, pml_d, pd.nsplit, d.out, d.lse};
-  const unsigned gx = unsigned(s.h * s.d / 64);
+  const unsigned gx = unsigned(s.h * s.d / 256);
   if (ms && md && fast) {
     HATTN_LAUNCH(attn_merge_pair_kernel, dim3(gx, unsigned(rows_s + rows_d)), dim3(256), 0, st, mks, rows_s, mkd,
                  s.h, s.d);
@@ -785,8 +787,8 @@ hipError_t launch_attn_pair(const AttnArgs& s, void* ws_s, const AttnArgs& d, vo
     const AttnArgs& a = r == 0 ? s : d;
     float* po = r == 0 ? po_s : po_d;
     float* pml = r == 0 ? pml_s : pml_d;
-    if (a.d % 64 == 0 && pl.nsplit <= kMergeMaxSplit)
-      HATTN_LAUNCH(attn_merge_kernel, dim3(gx, unsigned(a.bt * a.nq)), dim3(256), 0, st,
+    if (merge_fast(a.h, a.d, pl.nsplit))
+      HATTN_LAUNCH(attn_merge_kernel, dim3(unsigned(a.h * a.d / 256), unsigned(a.bt * a.nq)), dim3(256), 0, st,
                    MergeK{po, pml, pl.nsplit, a.out, a.lse}, a.h, a.d);
     else
       HATTN_LAUNCH(attn_merge_any_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256),
