@@ -1715,8 +1715,14 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
     e = launch_flat_score(a, p.ld, S, full, st);
     if (e != hipSuccess) return e;
     LaunchScope ls("select_rows", st);
-    HATTN_LAUNCH((select_rows_kernel<0, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S, p.ld, a.n_vis,
-                 nullptr, a.n, 1, 1, k, idx, score, nullptr, nullptr, int64_t(1), int64_t(1));
+    // More rows than CUs: throughput counts, and 512-thread workgroups (rows
+    // of up to 8,192 keys) let four rows share a CU instead of two.
+    if (p.rows >= 256 && a.n <= kSelIT * 512)
+      HATTN_LAUNCH((select_rows_kernel<0, 512>), dim3(unsigned(p.rows)), dim3(512), 0, st, S, p.ld, a.n_vis,
+                   nullptr, a.n, 1, 1, k, idx, score, nullptr, nullptr, int64_t(1), int64_t(1));
+    else
+      HATTN_LAUNCH((select_rows_kernel<0, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S, p.ld, a.n_vis,
+                   nullptr, a.n, 1, 1, k, idx, score, nullptr, nullptr, int64_t(1), int64_t(1));
     return hipGetLastError();
   }
   char* cb = reinterpret_cast<char*>(ws) + p.s_bytes;
@@ -2001,7 +2007,11 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   if (e != hipSuccess) return e;
   {
     LaunchScope ls("select_tokens", st);
-    if (m <= kSelNT)
+    // as for flat rows: 512 threads when many rows share the chip
+    if (p.rows >= 256 && m <= 512 && int64_t(m) * B <= kSelIT * 512)
+      HATTN_LAUNCH((select_rows_kernel<2, 512>), dim3(unsigned(p.rows)), dim3(512), 0, st, S2, p.ld2, a.n_vis,
+                   blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
+    else if (m <= kSelNT)
       HATTN_LAUNCH((select_rows_kernel<2, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
                    a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
     else
