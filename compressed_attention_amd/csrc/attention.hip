@@ -265,8 +265,7 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
         }
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_groups(mx);  // over the four lane groups: lane swaps, no LDS
     const bool up = mx > m_run + 8.f;  // false while mx is -inf
     if (__any(up)) {
       const float m_new = up ? mx : m_run;
@@ -312,8 +311,7 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
   }
 
   // Lane partial sums cover this lane's keys only; sum over lane groups.
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_groups(l_run);
   if (nsplit == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* op = out + (qrow * H + head) * D + 4 * g;

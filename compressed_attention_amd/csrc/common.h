@@ -54,24 +54,31 @@ HATTN_DEV float key_to_float(uint32_t k) {
   return __uint_as_float(u);
 }
 
-template <typename T>
-HATTN_DEV T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+// Reduction of v over the wave, in every lane, without LDS: DPP moves inside
+// each 16-lane row (lane pairs, lane quads, row halves, rows), then the
+// gfx950 lane swaps across rows.  Every step combines two values in an
+// order that is the same in the two lanes, so every lane ends with the same
+// bits.
+template <int CTRL>
+HATTN_DEV float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
 }
-template <typename T>
-HATTN_DEV T wave_max(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
-  return v;
+template <typename Op>
+HATTN_DEV float wave_reduce(float v, Op op) {
+  v = op(v, dpp_move<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = op(v, dpp_move<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = op(v, dpp_move<0x141>(v));  // row_half_mirror: the other quad of the half row
+  v = op(v, dpp_move<0x140>(v));  // row_mirror: the other half of the row
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));  // row pairs
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));  // wave halves
 }
-
-template <typename T>
-HATTN_DEV T wave_min(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
-  return v;
+HATTN_DEV float wave_sum(float v) {
+  return wave_reduce(v, [](float x, float y) { return x + y; });
+}
+HATTN_DEV float wave_max(float v) {
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 HATTN_DEV int lane_id() { return __lane_id(); }
@@ -123,6 +130,14 @@ HATTN_DEV float sum_groups(float v) {
   const float A = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(A), __float_as_uint(A), false, false);
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Maximum of v over the four lane groups, in every lane (two lane swaps).
+HATTN_DEV float max_groups(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float A = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(A), __float_as_uint(A), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
 // Number of lanes below this one whose bit is set in mask.
