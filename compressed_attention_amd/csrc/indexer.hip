@@ -1570,12 +1570,13 @@ static bool flat_mfma_ok(const IndexArgs& a) {
 // Key chunk of the MFMA flat score over nkeys launch keys: 2048 keys, halved
 // (down to 256) until the grid has about four workgroups per CU (two
 // resident, 256 CUs).
-static int flat_chunk(const IndexArgs& a, int64_t nkeys) {
+static int flat_chunk(const IndexArgs& a, int64_t nkeys, int64_t target_wg = 1024) {
   const int64_t nqb = (a.nq + 15) / 16;
   int chunk = 2048;
-  while (chunk > 256 && nqb * a.bt * ((nkeys + chunk - 1) / chunk) < 1024) chunk /= 2;
+  while (chunk > 256 && nqb * a.bt * ((nkeys + chunk - 1) / chunk) < target_wg) chunk /= 2;
   return chunk;
 }
+
 
 struct FlatPlan {
   int64_t rows, ld;
@@ -1654,6 +1655,7 @@ struct FlatScoreMode {
   int32_t* ccnt = nullptr;
   const int32_t* gate = nullptr;
   int chunk = 0;  // 0: flat_chunk(nkeys)
+  int64_t target_wg = 1024;
 };
 
 static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, const FlatScoreMode& fm,
@@ -1662,7 +1664,7 @@ static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, co
     // 16 queries per workgroup.  (32, with 8 waves sharing each key tile,
     // measured slower: one resident workgroup per CU and longer barriers.)
     const int nqb = int((a.nq + 15) / 16);
-    const int chunk = fm.chunk ? fm.chunk : flat_chunk(a, fm.nkeys);
+    const int chunk = fm.chunk ? fm.chunk : flat_chunk(a, fm.nkeys, fm.target_wg);
     const int nch = int((fm.nkeys + chunk - 1) / chunk);
     dim3 grid(xcd_grid(nqb, nch), unsigned(a.bt));
     const bool collect = fm.thr != nullptr;
@@ -1746,6 +1748,7 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
     FlatScoreMode sm;
     sm.nkeys = p.lds;
     sm.tstride = p.tstride;
+    sm.target_wg = 512;  // twice as many tiles per workgroup as the full pass: half the query-fragment loads
     e = launch_flat_score(a, p.lds, Ssamp, sm, st);
     if (e != hipSuccess) return e;
     {
