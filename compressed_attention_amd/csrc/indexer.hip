@@ -1567,12 +1567,13 @@ static bool flat_mfma_ok(const IndexArgs& a) {
          a.n < (int64_t(1) << 31);
 }
 
-// Key chunk of the MFMA flat score over nkeys launch keys: 2048 keys, halved
+// Key chunk of the MFMA flat score over nkeys launch keys: 8192 keys, halved
 // (down to 256) until the grid has about four workgroups per CU (two
-// resident, 256 CUs).
+// resident, 256 CUs).  Long chunks spread each workgroup's query-fragment
+// loads over more tiles (measured at 128K: 8192-key chunks beat 2048).
 static int flat_chunk(const IndexArgs& a, int64_t nkeys, int64_t target_wg = 1024) {
   const int64_t nqb = (a.nq + 15) / 16;
-  int chunk = 2048;
+  int chunk = 8192;
   while (chunk > 256 && nqb * a.bt * ((nkeys + chunk - 1) / chunk) < target_wg) chunk /= 2;
   return chunk;
 }
