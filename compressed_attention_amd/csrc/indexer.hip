@@ -893,6 +893,20 @@ __global__ __launch_bounds__(256, 2) void score_stage2_bm_kernel(const uint16_t*
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, c32 = lane & 31;
 
+  const int32_t* lst = list + bucket * nq;
+  // this wave's four list entries of group gi (entries 16*gi + 4*wave + 0..3;
+  // pair p holds entries 2p, 2p+1), loaded one group ahead (the first group's
+  // before the block's keys)
+  auto load_entries = [&](int gi, int (&pk)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ent = 16 * gi + 4 * wave + i;
+      pk[i] = gi < ngroups && ent < c ? lst[ent] : -1;
+    }
+  };
+  int pk_next[4];
+  load_entries(slice, pk_next);
+
   // the block's keys (rows past the cache end read clamped; never stored)
   const uint16_t* kb = k_i + b * n * D;
   const int64_t e_blk = blkid * B;
@@ -902,21 +916,19 @@ __global__ __launch_bounds__(256, 2) void score_stage2_bm_kernel(const uint16_t*
     *reinterpret_cast<u32x4_t*>(&kt[row * PITCH + col * 8]) = ld16(kb + e * D + col * 8);
   }
   __syncthreads();
-  const int32_t* lst = list + bucket * nq;
 
   for (int gi = slice; gi < ngroups; gi += nslice) {
-    // entries 16*gi + 4*wave + {0..3}: pair p holds entries 2p, 2p+1
     int rowq[2][2];
     int slotq[2][2];
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int ent = 16 * gi + 4 * wave + 2 * p + j;
-        const int packed = ent < c ? lst[ent] : -1;
+        const int packed = pk_next[2 * p + j];
         rowq[p][j] = packed < 0 ? -1 : packed / m;
         slotq[p][j] = packed < 0 ? 0 : packed % m;
       }
+    load_entries(gi + nslice, pk_next);
     u32x4_t a[2][KS];
     float wv[2][2][8];
     int my_nv[2];
@@ -931,11 +943,17 @@ __global__ __launch_bounds__(256, 2) void score_stage2_bm_kernel(const uint16_t*
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        // heads 4*half..+3 and 8+4*half..+3: two 16-byte loads
         const int r = rowq[p][j];
+        f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+        if (r >= 0) {
+          load4_f32(w_i + int64_t(r) * 16 + 4 * half, lo);
+          load4_f32(w_i + int64_t(r) * 16 + 8 + 4 * half, hi);
+        }
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const int head = 8 * (v >> 2) + 4 * half + (v & 3);
-          wv[p][j][v] = r >= 0 ? w_i[int64_t(r) * 16 + head] : 0.f;
+        for (int v = 0; v < 4; ++v) {
+          wv[p][j][v] = lo[v];
+          wv[p][j][4 + v] = hi[v];
         }
       }
       // this lane stores entry 2p + half of the pair
