@@ -42,6 +42,22 @@ HATTN_DEV void load4_f32(const uint16_t* p, f32x4_t& v) {
   v = f32x4_t{bf16lo(r.x), bf16hi(r.x), bf16lo(r.y), bf16hi(r.y)};
 }
 
+// The 8 head weights a lane of the 32x32 score layout needs from one
+// query's 16 (16-byte aligned row): heads 4*half..+3 and 8+4*half..+3, in
+// that order, as two 16-byte loads; zeros when the query does not exist.
+HATTN_DEV void load_head_weights(const float* __restrict__ wrow, bool ok, int half, float (&wv)[8]) {
+  f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+    lo = *reinterpret_cast<const f32x4_t*>(wrow + 4 * half);
+    hi = *reinterpret_cast<const f32x4_t*>(wrow + 8 + 4 * half);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    wv[v] = lo[v];
+    wv[4 + v] = hi[v];
+  }
+}
+
 HATTN_DEV bool xcd_decode(int id, int ngroups, int nchunks, int* group, int* chunk) {
   const int xcd = id & 7;
   const int slot = id >> 3;
@@ -101,7 +117,12 @@ __global__ __launch_bounds__(64 * NWQ, KS >= 8 ? 1 : 8 / NWQ) void score_flat_mf
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a[mt][ks] = ok ? ld16(qp + 32 * ks) : u32x4_t{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wv[mt][i] = ok ? w_i[(b * nq + q) * 16 + 4 * g + i] : 0.f;
+    for (int i = 0; i < 4; ++i) wv[mt][i] = 0.f;
+    if (ok) {
+      const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(w_i + (b * nq + q) * 16 + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[mt][i] = w4[i];
+    }
   }
   // Lane group g stores the scores of query 4*wave + g: its visible count
   // (0 for a query beyond nq) and row pointer, fixed for the whole chunk.
@@ -258,12 +279,7 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t q = q0 + 4 * wave + 2 * p + j;
-      const bool ok = q < nq;
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int head = 8 * (v >> 2) + 4 * half + (v & 3);
-        wv[p][j][v] = ok ? w_i[(b * nq + q) * 16 + head] : 0.f;
-      }
+      load_head_weights(w_i + (b * nq + (q < nq ? q : 0)) * 16, q < nq, half, wv[p][j]);
     }
     // this lane stores query 4*wave + 2p + half
     const int64_t mq = q0 + 4 * wave + 2 * p + half;
@@ -588,12 +604,7 @@ __global__ __launch_bounds__(256, 2) void score_stage1_x3_kernel(const uint16_t*
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t q = q0 + 4 * wave + 2 * p + j;
-      const bool ok = q < nq;
-#pragma unroll
-      for (int v = 0; v < 8; ++v) {
-        const int head = 8 * (v >> 2) + 4 * half + (v & 3);
-        wv[p][j][v] = ok ? w_i[(b * nq + q) * 16 + head] : 0.f;
-      }
+      load_head_weights(w_i + (b * nq + (q < nq ? q : 0)) * 16, q < nq, half, wv[p][j]);
     }
     const int64_t mq = q0 + 4 * wave + 2 * p + half;
     my_nb[p] = mq < nq ? s_nb[4 * wave + 2 * p + half] : 0;
@@ -943,18 +954,8 @@ __global__ __launch_bounds__(256, 2) void score_stage2_bm_kernel(const uint16_t*
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        // heads 4*half..+3 and 8+4*half..+3: two 16-byte loads
         const int r = rowq[p][j];
-        f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-        if (r >= 0) {
-          load4_f32(w_i + int64_t(r) * 16 + 4 * half, lo);
-          load4_f32(w_i + int64_t(r) * 16 + 8 + 4 * half, hi);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          wv[p][j][v] = lo[v];
-          wv[p][j][4 + v] = hi[v];
-        }
+        load_head_weights(w_i + int64_t(r < 0 ? 0 : r) * 16, r >= 0, half, wv[p][j]);
       }
       // this lane stores entry 2p + half of the pair
       const int r = rowq[p][half];
