@@ -883,7 +883,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 // the visible entries j of the block.
 // ---------------------------------------------------------------------------
 template <int KS>
-__global__ __launch_bounds__(256, 2) void score_stage2_bm_kernel(const uint16_t* __restrict__ q_i,
+__global__ __launch_bounds__(256, 4) void score_stage2_bm_kernel(const uint16_t* __restrict__ q_i,
                                                                  const uint16_t* __restrict__ k_i,
                                                                  const float* __restrict__ w_i,
                                                                  const int32_t* __restrict__ n_vis,
@@ -918,85 +918,86 @@ __global__ __launch_bounds__(256, 2) void score_stage2_bm_kernel(const uint16_t*
   int pk_next[4];
   load_entries(slice, pk_next);
 
-  // the block's keys (rows past the cache end read clamped; never stored)
+  // the block's keys (rows past the cache end read clamped; never stored):
+  // every load is issued before the first LDS store (the trip count has a
+  // compile-time bound, so the loop unrolls)
   const uint16_t* kb = k_i + b * n * D;
   const int64_t e_blk = blkid * B;
-  for (int pc = threadIdx.x; pc < B * (D / 8); pc += 256) {
+  constexpr int KPT = BMAX * (D / 8) / 256;  // 16-byte pieces per thread
+  u32x4_t kp[KPT];
+#pragma unroll
+  for (int it = 0; it < KPT; ++it) {
+    const int pc = threadIdx.x + 256 * it;
     const int row = pc / (D / 8), col = pc % (D / 8);
-    const int64_t e = imin64(e_blk + row, n - 1);
-    *reinterpret_cast<u32x4_t*>(&kt[row * PITCH + col * 8]) = ld16(kb + e * D + col * 8);
+    const int64_t e = imin64(e_blk + imin64(row, B - 1), n - 1);
+    kp[it] = ld16(kb + e * D + col * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < KPT; ++it) {
+    const int pc = threadIdx.x + 256 * it;
+    const int row = pc / (D / 8), col = pc % (D / 8);
+    if (row < B) *reinterpret_cast<u32x4_t*>(&kt[row * PITCH + col * 8]) = kp[it];
   }
   __syncthreads();
 
   for (int gi = slice; gi < ngroups; gi += nslice) {
-    int rowq[2][2];
-    int slotq[2][2];
+    int pk[4];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int packed = pk_next[2 * p + j];
-        rowq[p][j] = packed < 0 ? -1 : packed / m;
-        slotq[p][j] = packed < 0 ? 0 : packed % m;
-      }
+    for (int i = 0; i < 4; ++i) pk[i] = pk_next[i];
     load_entries(gi + nslice, pk_next);
-    u32x4_t a[2][KS];
-    float wv[2][2][8];
-    int my_nv[2];
-    float* srow[2];
-#pragma unroll
+    // One query pair at a time: half the registers of both pairs at once
+    // (four resident workgroups instead of two), each pair reading the key
+    // tile from LDS on its own.
+#pragma unroll 1
     for (int p = 0; p < 2; ++p) {
+      const int pk0 = p ? pk[2] : pk[0], pk1 = p ? pk[3] : pk[1];
+      const int r0 = pk0 < 0 ? -1 : pk0 / m, r1 = pk1 < 0 ? -1 : pk1 / m;
+      u32x4_t a[KS];
       {
-        const int r = rowq[p][c32 >> 4];
+        const int r = (c32 >> 4) ? r1 : r0;
         const uint16_t* qp = q_i + (int64_t(r < 0 ? 0 : r) * 16 + (c32 & 15)) * D + 8 * half;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a[p][ks] = r >= 0 ? ld16(qp + 16 * ks) : u32x4_t{0, 0, 0, 0};
+        for (int ks = 0; ks < KS; ++ks) a[ks] = r >= 0 ? ld16(qp + 16 * ks) : u32x4_t{0, 0, 0, 0};
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = rowq[p][j];
-        load_head_weights(w_i + int64_t(r < 0 ? 0 : r) * 16, r >= 0, half, wv[p][j]);
-      }
+      float wv[2][8];
+      load_head_weights(w_i + int64_t(r0 < 0 ? 0 : r0) * 16, r0 >= 0, half, wv[0]);
+      load_head_weights(w_i + int64_t(r1 < 0 ? 0 : r1) * 16, r1 >= 0, half, wv[1]);
       // this lane stores entry 2p + half of the pair
-      const int r = rowq[p][half];
+      const int r = half ? r1 : r0;
+      const int pkh = half ? pk1 : pk0;
+      const int slot = pkh < 0 ? 0 : pkh % m;
       const int64_t nvr = r >= 0 ? imin64(n, imax64(0, n_vis[r])) : 0;
-      my_nv[p] = int(imax64(0, imin64(int64_t(B), nvr - e_blk)));  // visible entries of this block
-      srow[p] = S2 + int64_t(r < 0 ? 0 : r) * ld2 + int64_t(slotq[p][half]) * B;
-    }
-    for (int t0 = 0; t0 < B; t0 += 64) {
-      f32x16_t acc[2][2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
+      const int my_nv = int(imax64(0, imin64(int64_t(B), nvr - e_blk)));  // visible entries of this block
+      float* srow = S2 + int64_t(r < 0 ? 0 : r) * ld2 + int64_t(slot) * B;
+      for (int t0 = 0; t0 < B; t0 += 64) {
+        f32x16_t acc[2];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc[p][kh][v] = 0.f;
+          for (int v = 0; v < 16; ++v) acc[kh][v] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t bf[2];
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4_t bf[2];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-          bf[kh] = *reinterpret_cast<const u32x4_t*>(&kt[(t0 + 32 * kh + c32) * PITCH + 16 * ks + 8 * half]);
+          for (int kh = 0; kh < 2; ++kh)
+            bf[kh] = *reinterpret_cast<const u32x4_t*>(&kt[(t0 + 32 * kh + c32) * PITCH + 16 * ks + 8 * half]);
 #pragma unroll
-        for (int p = 0; p < 2; ++p)
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) acc[p][kh] = mfma32x32x16(a[p][ks], bf[kh], acc[p][kh]);
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
+          for (int kh = 0; kh < 2; ++kh) acc[kh] = mfma32x32x16(a[ks], bf[kh], acc[kh]);
+        }
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) {
           float s0 = 0.f, s1 = 0.f;
 #pragma unroll
           for (int v = 0; v < 8; ++v) {
-            s0 = fmaf(wv[p][0][v], relu_bits(acc[p][kh][v]), s0);
-            s1 = fmaf(wv[p][1][v], relu_bits(acc[p][kh][8 + v]), s1);
+            s0 = fmaf(wv[0][v], relu_bits(acc[kh][v]), s0);
+            s1 = fmaf(wv[1][v], relu_bits(acc[kh][8 + v]), s1);
           }
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s0), __float_as_uint(s1), false, false);
           const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
           const int jloc = t0 + 32 * kh + c32;
-          if (jloc < my_nv[p]) srow[p][jloc] = tot;
+          if (jloc < my_nv) srow[jloc] = tot;
         }
+      }
     }
   }
 }
