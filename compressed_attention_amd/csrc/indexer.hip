@@ -820,7 +820,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int lane = threadIdx.x;
   const int g = lane >> 4, r16 = lane & 15;
   // Every load is issued before any branch: query, weights, block id and
-  // visible count together, then the block's first 64 keys as soon as its
+  // visible count together, then the block's first 128 keys as soon as its
   // id arrives (rows past the cache end, or of an empty slot, read a valid
   // row and are never stored).  A wave at one block per SIMD needs no
   // register economy, so the loads are not interleaved with the MFMAs.
@@ -835,39 +835,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int64_t e_end = bid < 0 ? e_begin : imin64(e_begin + B, nv);
   const uint16_t* kb = k_i + b * n * D + 8 * g;
   float* out = S2 + row * ld + int64_t(slot) * B;
-  u32x4_t bf[4][KS];
+  // 128 keys (two 64-key tiles) per round: both tiles' loads go out together
+  u32x4_t bf[8][KS];
   auto load_keys = [&](int64_t e0) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 8; ++nt) {
       const int64_t e = imax64(0, imin64(e0 + 16 * nt + r16, n - 1));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) bf[nt][ks] = ld16(kb + e * D + 32 * ks);
     }
   };
-  load_keys(e_begin);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int64_t e0 = e_begin; e0 < e_end; e0 += 64) {
-    if (e0 != e_begin) {
-      load_keys(e0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  auto tile = [&](int64_t e0, int t) {
     float v[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ks], bf[nt][ks], acc);
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ks], bf[4 * t + nt][ks], acc);
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) s = fmaf(wv[i], relu_bits(acc[i]), s);
       v[nt] = s;  // this lane group's 4 heads
     }
-    {
-      // lane group g receives (and stores) key tile g
-      const float s = sum4_transpose(v[0], v[1], v[2], v[3]);
-      const int64_t e = e0 + 16 * g + r16;
-      if (e < e_end) out[e - e_begin] = s;
+    // lane group g receives (and stores) key tile g
+    const float s = sum4_transpose(v[0], v[1], v[2], v[3]);
+    const int64_t e = e0 + 16 * g + r16;
+    if (e < e_end) out[e - e_begin] = s;
+  };
+  load_keys(e_begin);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int64_t e0 = e_begin; e0 < e_end; e0 += 128) {
+    if (e0 != e_begin) {
+      load_keys(e0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    tile(e0, 0);
+    if (e0 + 64 < e_end) tile(e0 + 64, 1);
   }
 }
 
