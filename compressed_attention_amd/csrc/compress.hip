@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void compress_generic_kernel(const T* __restri
       const float p = __expf(a - mx);
       den += p;
       float f[V];
-      Vec16<T>::unpack(ld16(xb + (t0 + u) * C), f);
+      Vec16<T>::unpack(ld16_nt(xb + (t0 + u) * C), f);
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] = fmaf(p, f[i], acc[i]);
     }
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restr
   float zprev[S];
 #pragma unroll
   for (int u = 0; u < S; ++u) {
-    Vec16<T>::unpack(ld16(xb + (ebeg * S + u) * C), prev[u]);
+    Vec16<T>::unpack(ld16_nt(xb + (ebeg * S + u) * C), prev[u]);
     zprev[u] = zb ? zb[ebeg * S + u] : 0.f;
   }
   for (int64_t e = ebeg; e < eend; ++e) {
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restr
     const int64_t t1 = e * S + S;
 #pragma unroll
     for (int u = 0; u < S; ++u) {
-      Vec16<T>::unpack(ld16(xb + (t1 + u) * C), cur[u]);
+      Vec16<T>::unpack(ld16_nt(xb + (t1 + u) * C), cur[u]);
       zcur[u] = zb ? zb[t1 + u] : 0.f;
     }
     float a[W];
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void compress_window_kernel(const T* __restric
     for (; u + 3 * RG < w; u += 4 * RG) {
       u32x4_t v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = ld16(xb + int64_t(u + j * RG) * C);
+      for (int j = 0; j < 4; ++j) v[j] = ld16_nt(xb + int64_t(u + j * RG) * C);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float f[V];
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void compress_window_kernel(const T* __restric
     }
     for (; u < w; u += RG) {
       float f[V];
-      Vec16<T>::unpack(ld16(xb + int64_t(u) * C), f);
+      Vec16<T>::unpack(ld16_nt(xb + int64_t(u) * C), f);
       const float p = wsm[u];
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] = fmaf(p, f[i], acc[i]);
@@ -318,7 +318,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k_i, in
     for (; u + 3 * RG < cnt; u += 4 * RG) {
       u32x4_t v[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = ld16(base + int64_t(u + q * RG) * d);
+      for (int q = 0; q < 4; ++q) v[q] = ld16_nt(base + int64_t(u + q * RG) * d);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float f[V];
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k_i, in
     }
     for (; u < cnt; u += RG) {
       float f[V];
-      Vec16<T>::unpack(ld16(base + int64_t(u) * d), f);
+      Vec16<T>::unpack(ld16_nt(base + int64_t(u) * d), f);
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] += f[i];
     }
