@@ -517,7 +517,7 @@ HATTN_DEV void attn_merge_body(const MergeK& mk, int H, int D, int64_t qrow, int
 #pragma unroll
   for (int i = 0; i < kMergeRegs; ++i) {
     const int s = sg + 4 * i;
-    ov[i] = s < nsplit ? *reinterpret_cast<const f32x4_t*>(po + s * pos) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    ov[i] = s < nsplit ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(po + s * pos)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   if (sg == 0) {
     const float* __restrict__ ml = mk.part_ml + (qrow * nsplit * H + h0) * 2;

@@ -438,7 +438,7 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
     for (int u = 0; u < PIECES; ++u) {
       const int p = threadIdx.x + 256 * u;
       const int64_t j = j0 + p / (D / 4);
-      v[u] = j < nb ? ld16(rb + j * D + (p % (D / 4)) * 4) : u32x4_t{0, 0, 0, 0};
+      v[u] = j < nb ? ld16_nt(rb + j * D + (p % (D / 4)) * 4) : u32x4_t{0, 0, 0, 0};
     }
   };
   u32x4_t v[PIECES];
@@ -733,7 +733,7 @@ __global__ __launch_bounds__(256, 2) void decode_front_kernel(const uint16_t* __
   for (int u = 0; u < PIECES; ++u) {
     const int pp = threadIdx.x + 256 * u;
     const int64_t j = j0 + pp / (D / 4);
-    v[u] = j < nb ? ld16(rb + j * D + (pp % (D / 4)) * 4) : u32x4_t{0, 0, 0, 0};
+    v[u] = j < nb ? ld16_nt(rb + j * D + (pp % (D / 4)) * 4) : u32x4_t{0, 0, 0, 0};
   }
   f32x4_t a[KQ];
   {
@@ -842,7 +842,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int nt = 0; nt < 8; ++nt) {
       const int64_t e = imax64(0, imin64(e0 + 16 * nt + r16, n - 1));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bf[nt][ks] = ld16(kb + e * D + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks) bf[nt][ks] = ld16_nt(kb + e * D + 32 * ks);
     }
   };
   auto tile = [&](int64_t e0, int t) {
