@@ -72,7 +72,7 @@ HATTN_DEV void append_rows(const T* __restrict__ base, int64_t ld, int n, int rg
 #pragma unroll
       for (int k = 0; k < kAppUNR; ++k) {
         const int u = u0 + k * RG;
-        first[k] = u < n ? ld16(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
+        first[k] = u < n ? ld16_nt(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -94,7 +94,7 @@ HATTN_DEV void append_first(const T* __restrict__ base, int64_t ld, int n, int r
 #pragma unroll
   for (int k = 0; k < kAppUNR; ++k) {
     const int u = rg + k * RG;
-    first[k] = u < n ? ld16(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
+    first[k] = u < n ? ld16_nt(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
   }
 }
 
