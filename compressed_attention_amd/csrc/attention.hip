@@ -110,7 +110,11 @@ struct AttnLds {
   uint64_t vmask[TK / 64];
 };
 
-template <int D, int NW, bool SPARSE>
+// STREAM: K|V rows are read once by the launch (one query per sequence), so
+// they are loaded non-temporally; otherwise the queries of a sequence share
+// its cache and plain loads keep it in L2.  (A template parameter: the
+// compiler merges a runtime choice between the two loads into a plain one.)
+template <int D, int NW, bool SPARSE, bool STREAM>
 HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D>& lds, int32_t* sidx) {
   const uint16_t* __restrict__ q = a.q;
   const uint16_t* __restrict__ ckv = a.ckv;
@@ -187,7 +191,8 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
 #pragma unroll
       for (int u = 0; u < PIECES; ++u) {
         const int pidx = tid + NT * u;
-        pre[u] = ld16_nt(base + (pidx / PPR) * C + (pidx % PPR) * 8);
+        const uint16_t* src = base + (pidx / PPR) * C + (pidx % PPR) * 8;
+        pre[u] = STREAM ? ld16_nt(src) : ld16(src);
       }
     } else {
 #pragma unroll
@@ -197,7 +202,7 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
         // Skipped keys read raw row 0 (finite data); their logits are masked.
         const uint16_t* src = key_src32<SPARSE>(j0 + pidx / PPR, j_end, nc32, sidx, j_begin, ckv_b, n32, raw_b,
                                                 L32, rbase, C, &ok);
-        pre[u] = ld16_nt(src + (pidx % PPR) * 8);
+        pre[u] = STREAM ? ld16_nt(src + (pidx % PPR) * 8) : ld16(src + (pidx % PPR) * 8);
       }
     }
   };
@@ -330,11 +335,11 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
   }
 }
 
-template <int D, int NW, bool SPARSE>
+template <int D, int NW, bool SPARSE, bool STREAM>
 __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnK a) {
   __shared__ AttnLds<D> lds;
   __shared__ int32_t sidx[SPARSE ? kSparseChunkMax : 1];  // this chunk's compressed indices
-  attn_mfma_body<D, NW, SPARSE>(a, blockIdx.x, blockIdx.y, lds, sidx);
+  attn_mfma_body<D, NW, SPARSE, STREAM>(a, blockIdx.x, blockIdx.y, lds, sidx);
 }
 
 // A sparse and a dense query set in one launch (e.g. the CSA and HCA
@@ -349,10 +354,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_pair_kernel(AttnK s, int64_t 
   const int64_t ns = int64_t(s.nsplit) * rows_s;
   if (id < ns) {
     const int64_t row = idiv(id, s.nsplit);
-    attn_mfma_body<D, NW, true>(s, int(id - row * s.nsplit), row, lds, sidx);
+    attn_mfma_body<D, NW, true, true>(s, int(id - row * s.nsplit), row, lds, sidx);
   } else {
     const int64_t row = idiv(id - ns, d.nsplit);
-    attn_mfma_body<D, NW, false>(d, int(id - ns - row * d.nsplit), row, lds, sidx);
+    attn_mfma_body<D, NW, false, true>(d, int(id - ns - row * d.nsplit), row, lds, sidx);
   }
 }
 
@@ -659,7 +664,11 @@ template <bool SPARSE>
 static void launch_attn_mfma(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml, hipStream_t st) {
   const AttnK k = attn_k(a, pl, po, pml);
   dim3 grid(unsigned(pl.nsplit), unsigned(a.bt * a.nq));
-#define HATTN_ATTN(D, NH) HATTN_LAUNCH((attn_mfma_kernel<D, NH, SPARSE>), grid, dim3(64 * NH), 0, st, k)
+#define HATTN_ATTN(D, NH)                                                                     \
+  do {                                                                                        \
+    if (a.nq == 1) HATTN_LAUNCH((attn_mfma_kernel<D, NH, SPARSE, true>), grid, dim3(64 * NH), 0, st, k); \
+    else HATTN_LAUNCH((attn_mfma_kernel<D, NH, SPARSE, false>), grid, dim3(64 * NH), 0, st, k);        \
+  } while (0)
   const int nw = a.h / 16;
   if (a.d == 128) {
     switch (nw) {
@@ -728,7 +737,8 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
 // attn_ws_bytes; any other combination runs the two launches one after the
 // other.  Results equal launch_attn on each set.
 hipError_t launch_attn_pair(const AttnArgs& s, void* ws_s, const AttnArgs& d, void* ws_d, hipStream_t st) {
-  if (!(mfma_shape(s) && mfma_shape(d) && s.idx && !d.idx && s.h == d.h && s.d == d.d)) {
+  // (the paired launch streams K|V: one query per sequence, as in decode)
+  if (!(mfma_shape(s) && mfma_shape(d) && s.idx && !d.idx && s.h == d.h && s.d == d.d && s.nq == 1 && d.nq == 1)) {
     hipError_t e = launch_attn(s, ws_s, st);
     return e != hipSuccess ? e : launch_attn(d, ws_d, st);
   }
