@@ -58,6 +58,24 @@ HATTN_DEV void load_head_weights(const float* __restrict__ wrow, bool ok, int ha
   }
 }
 
+// Sets this workgroup's share of fill[0, fill_n) to -1: the grid's
+// workgroups split the array evenly (16-byte stores; the array is 16-byte
+// aligned).
+HATTN_DEV void fill_share(int32_t* __restrict__ fill, int64_t fill_n) {
+  const int64_t nwg = int64_t(gridDim.x) * gridDim.y * gridDim.z;
+  const int64_t wg = (int64_t(blockIdx.z) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+  const int64_t per = ((fill_n + nwg - 1) / nwg + 3) & ~int64_t(3);
+  const int64_t lo = wg * per, hi = imin64(fill_n, lo + per);
+  const u32x4_t m1 = {~0u, ~0u, ~0u, ~0u};
+  for (int64_t i = lo + 4 * int64_t(threadIdx.x); i < hi; i += 4 * int64_t(blockDim.x)) {
+    if (i + 3 < hi) {
+      *reinterpret_cast<u32x4_t*>(fill + i) = m1;
+    } else {
+      for (int64_t j = i; j < hi; ++j) fill[j] = -1;
+    }
+  }
+}
+
 HATTN_DEV bool xcd_decode(int id, int ngroups, int nchunks, int* group, int* chunk) {
   const int xcd = id & 7;
   const int slot = id >> 3;
@@ -408,11 +426,10 @@ __global__ __launch_bounds__(256, 2) void score_stage1_kernel(const TQ* __restri
                                                               const int32_t* __restrict__ n_vis, int64_t nq,
                                                               int64_t n, int B, int64_t nb, int64_t ld,
                                                               float* __restrict__ S1, int nqg, int nch, int chunk,
-                                                              int32_t* __restrict__ zero, int64_t zero_n) {
-  // Clears the block-major stage-2 counters (the kernels after this one in
-  // the same call fill them).
-  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int64_t i = threadIdx.x; i < zero_n; i += 256) zero[i] = 0;
+                                                              int32_t* __restrict__ fill, int64_t fill_n) {
+  // Clears the block-major chooser lists (the block select of the same call
+  // fills them), every workgroup its share.
+  if (fill) fill_share(fill, fill_n);
   constexpr int D = 16 * KQ;
   constexpr int TB = 64;
   constexpr int PITCH = D + 4;
@@ -554,9 +571,8 @@ __global__ __launch_bounds__(256, 2) void score_stage1_x3_kernel(const uint16_t*
                                                                  const int32_t* __restrict__ n_vis, int64_t nq,
                                                                  int64_t n, int B, int64_t nb, int64_t ld,
                                                                  float* __restrict__ S1, int nqb, int nch, int chunk,
-                                                                 int32_t* __restrict__ zero, int64_t zero_n) {
-  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int64_t i = threadIdx.x; i < zero_n; i += 256) zero[i] = 0;
+                                                                 int32_t* __restrict__ fill, int64_t fill_n) {
+  if (fill) fill_share(fill, fill_n);
   constexpr int D = 16 * KS;
   constexpr int TN = 64;
   constexpr int PITCH = D + 8;
@@ -876,54 +892,48 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
 // ---------------------------------------------------------------------------
 // HISA stage 2, block-major (bf16, 16 heads, d_i = 16*KS, B <= 128): used
-// when many queries choose each block.  The block-select kernel appended
-// every (row, slot) that chose block b to list[b]; a workgroup loads block
-// b's keys into LDS once and scores them for groups of 16 of its choosers
-// (32x32x16 MFMA, the flat kernel's per-wave layout: two query pairs per
-// wave, 32-key column tiles).  Workgroups of one block take every nslice-th
-// group, so a block chosen by many queries is spread over nslice of them.
-// Scores land where the per-slot kernel puts them: S2[row][slot*B + j] for
-// the visible entries j of the block.
+// when many queries choose each block.  The block-select kernel wrote, for
+// every query q of sequence b that chose block blk, the slot it chose into
+// list[b][blk][q] (-1 elsewhere).  A workgroup reads its block's column,
+// packs the choosers into an LDS list in query order, loads block blk's keys into LDS once and scores them for groups
+// of 16 choosers (32x32x16 MFMA, the flat kernel's per-wave layout: query
+// pairs, 32-key column tiles).  Workgroups of one block take every
+// nslice-th group, so a block chosen by many queries is spread over nslice
+// of them.  Scores land where the per-slot kernel puts them:
+// S2[row][slot*B + j] for the visible entries j of the block.
 // ---------------------------------------------------------------------------
 template <int KS>
 __global__ __launch_bounds__(256, 4) void score_stage2_bm_kernel(const uint16_t* __restrict__ q_i,
                                                                  const uint16_t* __restrict__ k_i,
                                                                  const float* __restrict__ w_i,
                                                                  const int32_t* __restrict__ n_vis,
-                                                                 const int32_t* __restrict__ cnt,
                                                                  const int32_t* __restrict__ list, int64_t nq,
                                                                  int64_t n, int B, int m, int64_t nb, int64_t ld2,
                                                                  float* __restrict__ S2, int nslice) {
   constexpr int D = 16 * KS;
   constexpr int BMAX = 128;
   constexpr int PITCH = D + 8;
+  constexpr int QMAX = 4096;  // queries per sequence (checked on the host)
   __shared__ __align__(16) uint16_t kt[BMAX * PITCH];
+  extern __shared__ int32_t lst[];  // [nq]: row * m + slot of the block's choosers
+  constexpr int CPT = QMAX / 256;   // column steps of 256 queries
+  static_assert(CPT * 4 == kWave, "one ballot mask per lane");
+  __shared__ uint64_t cmask[CPT * 4];  // chooser ballot of step j, wave w at [4 * j + w]
   const int slice = blockIdx.x;
   const int64_t blkid = blockIdx.y, b = blockIdx.z;
-  const int64_t bucket = b * nb + blkid;
-  const int c = cnt[bucket];
-  const int ngroups = (c + 15) / 16;
-  if (slice >= ngroups) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, c32 = lane & 31;
 
-  const int32_t* lst = list + bucket * nq;
-  // this wave's four list entries of group gi (entries 16*gi + 4*wave + 0..3;
-  // pair p holds entries 2p, 2p+1), loaded one group ahead (the first group's
-  // before the block's keys)
-  auto load_entries = [&](int gi, int (&pk)[4]) {
+  // The block's column of chooser slots and its keys: every load in flight
+  // at once (both loops have compile-time trip counts and unroll).
+  const int32_t* colp = list + (b * nb + blkid) * nq;
+  int cv[CPT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ent = 16 * gi + 4 * wave + i;
-      pk[i] = gi < ngroups && ent < c ? lst[ent] : -1;
-    }
-  };
-  int pk_next[4];
-  load_entries(slice, pk_next);
-
-  // the block's keys (rows past the cache end read clamped; never stored):
-  // every load is issued before the first LDS store (the trip count has a
-  // compile-time bound, so the loop unrolls)
+  for (int j = 0; j < CPT; ++j) {
+    const int q = threadIdx.x + 256 * j;
+    cv[j] = q < nq ? colp[q] : -1;
+  }
+  // (rows past the cache end read clamped; never stored)
   const uint16_t* kb = k_i + b * n * D;
   const int64_t e_blk = blkid * B;
   constexpr int KPT = BMAX * (D / 8) / 256;  // 16-byte pieces per thread
@@ -935,6 +945,16 @@ __global__ __launch_bounds__(256, 4) void score_stage2_bm_kernel(const uint16_t*
     const int64_t e = imin64(e_blk + imin64(row, B - 1), n - 1);
     kp[it] = ld16(kb + e * D + col * 8);
   }
+  // Pack the choosers in query order: every workgroup of the block builds
+  // the same list (its slices partition it by group), so the order must not
+  // depend on timing.  Ballot masks go to LDS; each wave scans the 64 counts
+  // (one per lane) for its bases.
+  uint64_t mks[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    mks[j] = ballot(cv[j] >= 0);
+    if (lane == 0) cmask[4 * j + wave] = mks[j];
+  }
 #pragma unroll
   for (int it = 0; it < KPT; ++it) {
     const int pc = threadIdx.x + 256 * it;
@@ -942,6 +962,32 @@ __global__ __launch_bounds__(256, 4) void score_stage2_bm_kernel(const uint16_t*
     if (row < B) *reinterpret_cast<u32x4_t*>(&kt[row * PITCH + col * 8]) = kp[it];
   }
   __syncthreads();
+  const uint32_t pcnt = uint32_t(__popcll(cmask[lane]));
+  const uint32_t pincl = wave_prefix_incl(pcnt);
+  const int c = __builtin_amdgcn_readlane(int(pincl), 63);
+  const int pexcl = int(pincl - pcnt);
+  const int wv4 = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    if (mks[j]) {
+      const int base = __builtin_amdgcn_readlane(pexcl, 4 * j + wv4);
+      if (cv[j] >= 0) lst[base + mbcnt(mks[j])] = int32_t((b * nq + threadIdx.x + 256 * j) * m + cv[j]);
+    }
+  }
+  __syncthreads();
+  const int ngroups = (c + 15) / 16;
+  if (slice >= ngroups) return;
+  // this wave's four entries of group gi (entries 16*gi + 4*wave + 0..3;
+  // pair p holds entries 2p, 2p+1), read one group ahead
+  auto load_entries = [&](int gi, int (&pk)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ent = 16 * gi + 4 * wave + i;
+      pk[i] = gi < ngroups && ent < c ? lst[ent] : -1;
+    }
+  };
+  int pk_next[4];
+  load_entries(slice, pk_next);
 
   for (int gi = slice; gi < ngroups; gi += nslice) {
     int pk[4];
@@ -1078,7 +1124,6 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(const float* __restrict
                                                              const int32_t* __restrict__ blk, int64_t n, int B, int m,
                                                              int k, int32_t* __restrict__ idx,
                                                              float* __restrict__ score_out,
-                                                             int32_t* __restrict__ inv_cnt,
                                                              int32_t* __restrict__ inv_list, int64_t nq,
                                                              int64_t nb) {
   __shared__ SelectShared<NT> sh;
@@ -1113,7 +1158,11 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(const float* __restrict
   float* scrow = score_out ? score_out + row * k : nullptr;
   const bool pow2 = (B & (B - 1)) == 0;
   const int lgB = __builtin_ctz(unsigned(B));
-  const int chosen = emit_selected<NT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int) {
+  // MODE 1, block-major stage 2: list[b][block][q] = slot of every block
+  // query q of sequence b chose (the lists were cleared to -1 by stage 1)
+  const int64_t bseq = MODE == 1 && inv_list ? idiv(row, nq) : 0;
+  int32_t* lrow = MODE == 1 && inv_list ? inv_list + bseq * nb * nq + (row - bseq * nq) : nullptr;
+  const int chosen = emit_selected<NT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int it) {
     int32_t val = i;
     if (TOK) {
       const int s = pow2 ? i >> lgB : i / B;
@@ -1122,12 +1171,7 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(const float* __restrict
     }
     orow[slot] = val;
     if (scrow) scrow[slot] = key_to_float(key);
-    if (MODE == 1 && inv_cnt) {
-      // block-major stage 2: append (row, slot) to the chosen block's list
-      const int64_t bucket = idiv(row, nq) * nb + i;
-      const int pos = atomicAdd(&inv_cnt[bucket], 1);
-      inv_list[bucket * nq + pos] = int32_t(row * m + slot);
-    }
+    if (MODE == 1 && lrow) lrow[int64_t(i) * nq] = slot;
   });
   for (int s = chosen + threadIdx.x; s < k; s += NT) {
     orow[s] = -1;
@@ -1745,10 +1789,10 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
     // of up to 8,192 keys) let four rows share a CU instead of two.
     if (p.rows >= 256 && a.n <= kSelIT * 512)
       HATTN_LAUNCH((select_rows_kernel<0, 512>), dim3(unsigned(p.rows)), dim3(512), 0, st, S, p.ld, a.n_vis,
-                   nullptr, a.n, 1, 1, k, idx, score, nullptr, nullptr, int64_t(1), int64_t(1));
+                   nullptr, a.n, 1, 1, k, idx, score, nullptr, int64_t(1), int64_t(1));
     else
       HATTN_LAUNCH((select_rows_kernel<0, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S, p.ld, a.n_vis,
-                   nullptr, a.n, 1, 1, k, idx, score, nullptr, nullptr, int64_t(1), int64_t(1));
+                   nullptr, a.n, 1, 1, k, idx, score, nullptr, int64_t(1), int64_t(1));
     return hipGetLastError();
   }
   char* cb = reinterpret_cast<char*>(ws) + p.s_bytes;
@@ -1839,7 +1883,7 @@ hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* scor
 struct HisaPlan {
   int64_t rows, nb, ld1, ld2;
   bool bm;  // block-major stage 2
-  size_t s1_bytes, blk_bytes, s2_bytes, cnt_bytes, list_bytes, total;
+  size_t s1_bytes, blk_bytes, s2_bytes, list_bytes, total;
 };
 
 static HisaPlan plan_hisa(const IndexArgs& a, int B, int m) {
@@ -1851,17 +1895,15 @@ static HisaPlan plan_hisa(const IndexArgs& a, int B, int m) {
   p.s1_bytes = align256(size_t(p.rows) * p.ld1 * 4);
   p.blk_bytes = align256(size_t(p.rows) * m * 4);
   p.s2_bytes = align256(size_t(p.rows) * p.ld2 * 4);
-  // Block-major stage 2 pays off once each block has many choosers; its
-  // per-block lists hold up to nq entries each.
+  // Block-major stage 2 pays off once each block has many choosers.  Its
+  // per-block chooser lists have one slot per query of the sequence (the
+  // chosen slot, or -1), cleared by stage 1 every call: at most 8M entries,
+  // and at most 4096 queries (a block's compacted list lives in LDS).
   p.bm = a.dtype == 1 && a.h_i == 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128) && B <= 128 &&
-         B % 64 == 0 && a.nq >= 128 && int64_t(a.nq) * m >= 8 * p.nb && p.nb <= 65535 && a.bt <= 65535 &&
-         a.bt * p.nb * a.nq <= (int64_t(1) << 26) &&
-         p.rows * m < (int64_t(1) << 31);
-  if (p.bm) {
-    p.cnt_bytes = align256(size_t(a.bt) * p.nb * 4);
-    p.list_bytes = align256(size_t(a.bt) * p.nb * a.nq * 4);
-  }
-  p.total = p.s1_bytes + p.blk_bytes + p.s2_bytes + p.cnt_bytes + p.list_bytes;
+         B % 64 == 0 && a.nq >= 128 && a.nq <= 4096 && int64_t(a.nq) * m >= 8 * p.nb && p.nb <= 65535 &&
+         a.bt <= 65535 && a.bt * p.nb * a.nq <= (int64_t(1) << 23) && p.rows * m < (int64_t(1) << 31);
+  if (p.bm) p.list_bytes = align256(size_t(a.bt) * p.nb * a.nq * 4);
+  p.total = p.s1_bytes + p.blk_bytes + p.s2_bytes + p.list_bytes;
   return p;
 }
 
@@ -1914,11 +1956,9 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
 
   // Stage 1: block scores.
   const bool mfma1 = a.h_i == 16 && a.d_i % 16 == 0 && a.d_i <= 256;
-  const bool bm = p.bm && mfma1;  // the stage-1 MFMA kernel clears the counters
-  int32_t* bm_cnt = bm ? reinterpret_cast<int32_t*>(base + p.s1_bytes + p.blk_bytes + p.s2_bytes) : nullptr;
-  int32_t* bm_list = bm ? reinterpret_cast<int32_t*>(base + p.s1_bytes + p.blk_bytes + p.s2_bytes + p.cnt_bytes)
-                        : nullptr;
-  const int64_t bm_zero = bm ? a.bt * p.nb : 0;
+  const bool bm = p.bm && mfma1;  // the stage-1 MFMA kernel clears the lists
+  int32_t* bm_list = bm ? reinterpret_cast<int32_t*>(base + p.s1_bytes + p.blk_bytes + p.s2_bytes) : nullptr;
+  const int64_t bm_fill = bm ? a.bt * p.nb * a.nq : 0;
   const bool x3 = mfma1 && a.dtype == 1 && a.nq >= 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128) &&
                   p.nb < (int64_t(1) << 31);
   if (stage1_done) {
@@ -1932,7 +1972,7 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     LaunchScope ls("score_stage1_mfma", st);
 #define HATTN_S1X3(KS)                                                                                       \
   HATTN_LAUNCH(score_stage1_x3_kernel<KS>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i, reps, a.w_i,     \
-               a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqb, nch, chunk, bm_cnt, bm_zero)
+               a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqb, nch, chunk, bm_list, bm_fill)
     switch (a.d_i) {
       case 32: HATTN_S1X3(2); break;
       case 64: HATTN_S1X3(4); break;
@@ -1949,10 +1989,10 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
 #define HATTN_S1(T, KQ)                                                                                      \
   if (qpw == 4)                                                                                              \
     HATTN_LAUNCH((score_stage1_kernel<T, KQ, 4>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
-                 a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk, bm_cnt, bm_zero);                 \
+                 a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk, bm_list, bm_fill);                 \
   else                                                                                                       \
     HATTN_LAUNCH((score_stage1_kernel<T, KQ, 1>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
-                 a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk, bm_cnt, bm_zero)
+                 a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk, bm_list, bm_fill)
     if (a.dtype == 0) {
       switch (a.d_i / 16) {
         case 1: HATTN_S1(float, 1); break;
@@ -1984,10 +2024,10 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     // these short rows: fewer waves meet at each barrier).
     if (p.nb <= kSelIT * 512)
       HATTN_LAUNCH((select_rows_kernel<1, 512>), dim3(unsigned(p.rows)), dim3(512), 0, st, S1, p.ld1, a.n_vis,
-                   nullptr, a.n, B, m, m, blk_out, nullptr, bm_cnt, bm_list, a.nq, p.nb);
+                   nullptr, a.n, B, m, m, blk_out, nullptr, bm_list, a.nq, p.nb);
     else
       HATTN_LAUNCH((select_rows_kernel<1, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S1, p.ld1,
-                   a.n_vis, nullptr, a.n, B, m, m, blk_out, nullptr, bm_cnt, bm_list, a.nq, p.nb);
+                   a.n_vis, nullptr, a.n, B, m, m, blk_out, nullptr, bm_list, a.nq, p.nb);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -2004,8 +2044,8 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     dim3 grid(unsigned(nslice), unsigned(p.nb), unsigned(a.bt));
     LaunchScope ls("score_stage2_bm", st);
 #define HATTN_S2BM(KS)                                                                                       \
-  HATTN_LAUNCH(score_stage2_bm_kernel<KS>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i,                  \
-               (const uint16_t*)a.k_i, a.w_i, a.n_vis, bm_cnt, bm_list, a.nq, a.n, B, m, p.nb, p.ld2, S2, nslice)
+  HATTN_LAUNCH(score_stage2_bm_kernel<KS>, grid, dim3(256), size_t(a.nq) * 4, st, (const uint16_t*)a.q_i,   \
+               (const uint16_t*)a.k_i, a.w_i, a.n_vis, bm_list, a.nq, a.n, B, m, p.nb, p.ld2, S2, nslice)
     switch (a.d_i) {
       case 32: HATTN_S2BM(2); break;
       case 64: HATTN_S2BM(4); break;
@@ -2037,13 +2077,13 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     // as for flat rows: 512 threads when many rows share the chip
     if (p.rows >= 256 && m <= 512 && int64_t(m) * B <= kSelIT * 512)
       HATTN_LAUNCH((select_rows_kernel<2, 512>), dim3(unsigned(p.rows)), dim3(512), 0, st, S2, p.ld2, a.n_vis,
-                   blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
+                   blk_out, a.n, B, m, k, idx, nullptr, nullptr, int64_t(1), int64_t(1));
     else if (m <= kSelNT)
       HATTN_LAUNCH((select_rows_kernel<2, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
-                   a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
+                   a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, int64_t(1), int64_t(1));
     else
       HATTN_LAUNCH((select_rows_kernel<3, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
-                   a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, nullptr, int64_t(1), int64_t(1));
+                   a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, int64_t(1), int64_t(1));
   }
   return hipGetLastError();
 }
