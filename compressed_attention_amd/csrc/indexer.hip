@@ -1179,6 +1179,41 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(const float* __restrict
   }
 }
 
+// HISA block selection for rows of at most 64 * IT blocks: one wave per
+// row (no cross-wave barriers), the same result as select_rows_kernel<1>.
+// Also fills the block-major chooser lists when inv_list is given.
+template <int IT>
+__global__ __launch_bounds__(64) void select_blocks_wave_kernel(const float* __restrict__ S, int64_t ld,
+                                                                const int32_t* __restrict__ n_vis, int64_t n, int B,
+                                                                int m, int32_t* __restrict__ blk,
+                                                                int32_t* __restrict__ inv_list, int64_t nq,
+                                                                int64_t nb) {
+  __shared__ __align__(16) uint32_t hist[256];
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int cap = int(imin64(kWave * IT, nb));
+  const float* srow = S + row * ld;
+  float v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int i = kWave * it + lane;
+    v[it] = i < cap ? srow[i] : 0.f;
+  }
+  const int nvalid = min(cap, row_valid_count<1>(n_vis, nullptr, row, n, B, m));
+  uint32_t kc[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) kc[it] = kWave * it + lane < nvalid ? order_key(v[it]) : 0u;
+  const SelThr st = wave_radix_threshold<IT>(kc, m, hist);
+  int32_t* orow = blk + row * m;
+  const int64_t bseq = inv_list ? idiv(row, nq) : 0;
+  int32_t* lrow = inv_list ? inv_list + bseq * nb * nq + (row - bseq * nq) : nullptr;
+  const int chosen = wave_emit_selected<IT>(kc, st, [&](int slot, int i) {
+    orow[slot] = i;
+    if (lrow) lrow[int64_t(i) * nq] = slot;
+  });
+  for (int s = chosen + lane; s < m; s += kWave) orow[s] = -1;
+}
+
 // Long flat rows (more than kSelCap candidates), one workgroup per row:
 //  1. threshold: tau = the key of rank r in an evenly spaced sample of 8192
 //     scores, with r about 1.5 * k * 8192 / n (expected ~1.5 k keys >= tau);
@@ -2020,9 +2055,16 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   if (e != hipSuccess) return e;
   {
     LaunchScope ls("select_blocks", st);
-    // Up to 8,192 blocks a row: 512 threads (measured faster than 1,024 on
-    // these short rows: fewer waves meet at each barrier).
-    if (p.nb <= kSelIT * 512)
+    // Many rows of up to 1,024 blocks: one wave per row (128K chunk, 1,024
+    // rows: 16.1 -> 10.3 us).  A few rows (decode) are latency-bound, and
+    // there the 512-thread workgroup is faster (8.0 against 12.2 us for
+    // 8 rows of 2,048 blocks).  Up to 8,192 blocks: 512 threads (measured
+    // faster than 1,024 on these short rows: fewer waves meet at each
+    // barrier).
+    if (p.nb <= 1024 && p.rows >= 256)
+      HATTN_LAUNCH((select_blocks_wave_kernel<16>), dim3(unsigned(p.rows)), dim3(kWave), 0, st, S1, p.ld1, a.n_vis,
+                   a.n, B, m, blk_out, bm_list, a.nq, p.nb);
+    else if (p.nb <= kSelIT * 512)
       HATTN_LAUNCH((select_rows_kernel<1, 512>), dim3(unsigned(p.rows)), dim3(512), 0, st, S1, p.ld1, a.n_vis,
                    nullptr, a.n, B, m, m, blk_out, nullptr, bm_list, a.nq, p.nb);
     else

@@ -256,6 +256,84 @@ HATTN_DEV SelThr radix_threshold(const uint32_t (&kc)[IT], int iters, int k, Sel
   return SelThr{prefix, int(remaining)};
 }
 
+// One-wave variant for short rows (up to 64 * IT keys; lane l holds
+// positions 64 * it + l): the same result as radix_threshold, found with
+// four 8-bit passes over a 256-bin LDS histogram.  With one wave per
+// workgroup a pass needs no cross-wave totals: lane l owns bins 4l..4l+3,
+// and one DPP scan over the lanes locates the crossing bin.  The single
+// wave's chain is longer than a workgroup's, so this pays off only when
+// many rows keep the chip busy.  hist is this wave's 256 words of LDS; the
+// workgroup must be this one wave (its barriers order the histogram's
+// clears, adds and reads).
+template <int IT>
+HATTN_DEV SelThr wave_radix_threshold(const uint32_t (&kc)[IT], int k, uint32_t* hist) {
+  const int lane = threadIdx.x & (kWave - 1);
+  if (k <= 0) return SelThr{0xffffffffu, 0};
+  uint32_t nval = 0;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) nval += uint32_t(__popcll(ballot(kc[it] != 0u)));
+  if (nval <= uint32_t(k)) return SelThr{0u, 0};  // every valid key is chosen
+  uint32_t prefix = 0, hmask = 0, remaining = uint32_t(k);
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    *reinterpret_cast<u32x4_t*>(hist + 4 * lane) = u32x4_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const uint32_t key = kc[it];
+      if (key != 0u && (key & hmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(hist + 4 * lane);
+    const uint32_t own = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_prefix_incl(own);
+    const uint32_t total = uint32_t(__builtin_amdgcn_readlane(int(incl), kWave - 1));
+    const uint32_t above_run = total - incl;  // keys in the bins of higher lanes
+    const int lc = first_lane(ballot(above_run < remaining && above_run + own >= remaining));
+    int digit = 0;
+    uint32_t above = 0;
+    {
+      uint32_t cum = above_run;
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        if (cum < remaining && cum + c[j] >= remaining) {
+          digit = 4 * lane + j;
+          above = cum;
+        }
+        cum += c[j];
+      }
+    }
+    digit = __builtin_amdgcn_readlane(digit, lc);
+    above = uint32_t(__builtin_amdgcn_readlane(int(above), lc));
+    prefix |= uint32_t(digit) << shift;
+    hmask |= 255u << shift;
+    remaining -= above;
+    __syncthreads();  // every lane has read its bins before the next clear
+  }
+  return SelThr{prefix, int(remaining)};
+}
+
+// One-wave emission (positions 64 * it + lane, increasing): emit(slot, i)
+// once per chosen position; returns the number chosen.
+template <int IT, typename Emit>
+HATTN_DEV int wave_emit_selected(const uint32_t (&kc)[IT], SelThr st, Emit emit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int out = 0, eq_seen = 0;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint32_t key = kc[it];
+    const bool is_eq = key == st.thr && key != 0u;
+    const uint64_t eqm = ballot(is_eq);
+    const bool sel = key > st.thr || (is_eq && eq_seen + int(mbcnt(eqm)) < st.need_eq);
+    const uint64_t sm = ballot(sel);
+    if (sel) emit(out + int(mbcnt(sm)), kWave * it + lane);
+    out += int(__popcll(sm));
+    eq_seen += int(__popcll(eqm));
+  }
+  return out;
+}
+
 // Emits the chosen positions in increasing order from the same register
 // keys.  emit(slot, i, key, it) is called once per chosen position i (held
 // in kc[it] of the calling lane) with its output slot; returns the number
