@@ -523,7 +523,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(decode batches shard by sequence with no communication; see DESIGN.md).", file=sys.stderr)
+              "(decode batches shard by sequence with no communication).", file=sys.stderr)
         sys.exit(2)
 
     import torch
