@@ -1179,19 +1179,29 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(const float* __restrict
   }
 }
 
-// HISA block selection for rows of at most 64 * IT blocks: one wave per
-// row (no cross-wave barriers), the same result as select_rows_kernel<1>.
-// Also fills the block-major chooser lists when inv_list is given.
-template <int IT>
-__global__ __launch_bounds__(64) void select_blocks_wave_kernel(const float* __restrict__ S, int64_t ld,
-                                                                const int32_t* __restrict__ n_vis, int64_t n, int B,
-                                                                int m, int32_t* __restrict__ blk,
-                                                                int32_t* __restrict__ inv_list, int64_t nq,
-                                                                int64_t nb) {
+// Row selection with one wave per row, for rows of at most 64 * IT
+// candidates: the same arguments and result as select_rows_kernel<MODE>
+// (MODE 2 for at most 512 chosen blocks), with no cross-wave barriers.
+// Lane l holds candidates 64 * it + l.  Launched for HISA block selection
+// (16 keys per lane).  For rows of 8,192 candidates (128 per lane) one
+// wave's serial work dominated: the 128K chunk's token selection took 65.8
+// against 27.5 us, the prefill chunk's flat selection 59 against 23.6 us.
+template <int MODE, int IT>
+__global__ __launch_bounds__(64) void select_rows_wave_kernel(const float* __restrict__ S, int64_t ld,
+                                                              const int32_t* __restrict__ n_vis,
+                                                              const int32_t* __restrict__ blk, int64_t n, int B,
+                                                              int m, int k, int32_t* __restrict__ idx,
+                                                              float* __restrict__ score_out,
+                                                              int32_t* __restrict__ inv_list, int64_t nq,
+                                                              int64_t nb) {
   __shared__ __align__(16) uint32_t hist[256];
+  __shared__ int32_t bsh[MODE == 2 ? 512 : 1];  // chosen block ids
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
-  const int cap = int(imin64(kWave * IT, nb));
+  const int32_t* brow = MODE == 2 ? blk + row * m : nullptr;
+  // every slot the row can have is loaded before the valid count is known
+  const int cap = MODE == 0 ? int(imin64(kWave * IT, n))
+                            : (MODE == 1 ? int(imin64(kWave * IT, idiv(n + B - 1, B))) : min(kWave * IT, m * B));
   const float* srow = S + row * ld;
   float v[IT];
 #pragma unroll
@@ -1199,19 +1209,34 @@ __global__ __launch_bounds__(64) void select_blocks_wave_kernel(const float* __r
     const int i = kWave * it + lane;
     v[it] = i < cap ? srow[i] : 0.f;
   }
-  const int nvalid = min(cap, row_valid_count<1>(n_vis, nullptr, row, n, B, m));
+  if (MODE == 2)
+    for (int s = lane; s < m; s += kWave) bsh[s] = brow[s];
+  const int nvalid = min(cap, row_valid_count<MODE == 2 ? 3 : MODE>(n_vis, brow, row, n, B, m));
   uint32_t kc[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) kc[it] = kWave * it + lane < nvalid ? order_key(v[it]) : 0u;
-  const SelThr st = wave_radix_threshold<IT>(kc, m, hist);
-  int32_t* orow = blk + row * m;
-  const int64_t bseq = inv_list ? idiv(row, nq) : 0;
-  int32_t* lrow = inv_list ? inv_list + bseq * nb * nq + (row - bseq * nq) : nullptr;
-  const int chosen = wave_emit_selected<IT>(kc, st, [&](int slot, int i) {
-    orow[slot] = i;
-    if (lrow) lrow[int64_t(i) * nq] = slot;
+  const SelThr st = wave_radix_threshold<IT>(kc, k, hist);  // its barriers also publish bsh
+  int32_t* orow = idx + row * k;
+  float* scrow = score_out ? score_out + row * k : nullptr;
+  const bool pow2 = (B & (B - 1)) == 0;
+  const int lgB = __builtin_ctz(unsigned(B));
+  const int64_t bseq = MODE == 1 && inv_list ? idiv(row, nq) : 0;
+  int32_t* lrow = MODE == 1 && inv_list ? inv_list + bseq * nb * nq + (row - bseq * nq) : nullptr;
+  const int chosen = wave_emit_selected<IT>(kc, st, [&](int slot, int i, uint32_t key) {
+    int32_t val = i;
+    if (MODE == 2) {
+      const int s = pow2 ? i >> lgB : i / B;
+      const int off = pow2 ? i & (B - 1) : i - s * B;
+      val = bsh[s] * B + off;
+    }
+    orow[slot] = val;
+    if (scrow) scrow[slot] = key_to_float(key);
+    if (MODE == 1 && lrow) lrow[int64_t(i) * nq] = slot;
   });
-  for (int s = chosen + lane; s < m; s += kWave) orow[s] = -1;
+  for (int s = chosen + lane; s < k; s += kWave) {
+    orow[s] = -1;
+    if (scrow) scrow[s] = -INFINITY;
+  }
 }
 
 // Long flat rows (more than kSelCap candidates), one workgroup per row:
@@ -2062,8 +2087,8 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     // faster than 1,024 on these short rows: fewer waves meet at each
     // barrier).
     if (p.nb <= 1024 && p.rows >= 256)
-      HATTN_LAUNCH((select_blocks_wave_kernel<16>), dim3(unsigned(p.rows)), dim3(kWave), 0, st, S1, p.ld1, a.n_vis,
-                   a.n, B, m, blk_out, bm_list, a.nq, p.nb);
+      HATTN_LAUNCH((select_rows_wave_kernel<1, 16>), dim3(unsigned(p.rows)), dim3(kWave), 0, st, S1, p.ld1,
+                   a.n_vis, nullptr, a.n, B, m, m, blk_out, nullptr, bm_list, a.nq, p.nb);
     else if (p.nb <= kSelIT * 512)
       HATTN_LAUNCH((select_rows_kernel<1, 512>), dim3(unsigned(p.rows)), dim3(512), 0, st, S1, p.ld1, a.n_vis,
                    nullptr, a.n, B, m, m, blk_out, nullptr, bm_list, a.nq, p.nb);

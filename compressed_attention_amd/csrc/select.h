@@ -314,8 +314,8 @@ HATTN_DEV SelThr wave_radix_threshold(const uint32_t (&kc)[IT], int k, uint32_t*
   return SelThr{prefix, int(remaining)};
 }
 
-// One-wave emission (positions 64 * it + lane, increasing): emit(slot, i)
-// once per chosen position; returns the number chosen.
+// One-wave emission (positions 64 * it + lane, increasing): emit(slot, i,
+// key) once per chosen position; returns the number chosen.
 template <int IT, typename Emit>
 HATTN_DEV int wave_emit_selected(const uint32_t (&kc)[IT], SelThr st, Emit emit) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -327,7 +327,7 @@ HATTN_DEV int wave_emit_selected(const uint32_t (&kc)[IT], SelThr st, Emit emit)
     const uint64_t eqm = ballot(is_eq);
     const bool sel = key > st.thr || (is_eq && eq_seen + int(mbcnt(eqm)) < st.need_eq);
     const uint64_t sm = ballot(sel);
-    if (sel) emit(out + int(mbcnt(sm)), kWave * it + lane);
+    if (sel) emit(out + int(mbcnt(sm)), kWave * it + lane, key);
     out += int(__popcll(sm));
     eq_seen += int(__popcll(eqm));
   }
