@@ -821,25 +821,27 @@ __global__ __launch_bounds__(256, 2) void decode_front_kernel(const uint16_t* __
 }
 
 // ---------------------------------------------------------------------------
-// HISA stage 2 score, bf16, 16 heads: one wave per (query, chosen block).
+// HISA stage 2 score, bf16, 16 heads: one wave per (query, chosen block,
+// 64-key tile group): workgroup x = slot * halves + h takes the block's
+// tiles h, h + halves, ...  (two workgroups per 128-key block: twice the
+// waves in flight of one wave per block, with half the registers each).
 // Candidate position j = slot*B + offset; visible candidates form a prefix.
 // ---------------------------------------------------------------------------
 template <int KS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void score_stage2_mfma_kernel(
+__global__ __launch_bounds__(64) void score_stage2_mfma_kernel(
     const uint16_t* __restrict__ q_i, const uint16_t* __restrict__ k_i, const float* __restrict__ w_i,
     const int32_t* __restrict__ n_vis, const int32_t* __restrict__ blk, int64_t nq, int64_t n, int B, int m,
-    int64_t ld, float* __restrict__ S2) {
+    int64_t ld, float* __restrict__ S2, int halves) {
   constexpr int D = 32 * KS;
   const int64_t row = blockIdx.y;
-  const int slot = blockIdx.x;
+  const int slot = int(blockIdx.x) / halves, h = int(blockIdx.x) - slot * halves;
   const int64_t b = idiv(row, nq);
   const int lane = threadIdx.x;
   const int g = lane >> 4, r16 = lane & 15;
   // Every load is issued before any branch: query, weights, block id and
-  // visible count together, then the block's first 128 keys as soon as its
+  // visible count together, then the first tile's keys as soon as the block
   // id arrives (rows past the cache end, or of an empty slot, read a valid
-  // row and are never stored).  A wave at one block per SIMD needs no
-  // register economy, so the loads are not interleaved with the MFMAs.
+  // row and are never stored).
   u32x4_t a[KS];
   const uint16_t* qp = q_i + (row * 16 + r16) * D + 8 * g;
 #pragma unroll
@@ -851,23 +853,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
   const int64_t e_end = bid < 0 ? e_begin : imin64(e_begin + B, nv);
   const uint16_t* kb = k_i + b * n * D + 8 * g;
   float* out = S2 + row * ld + int64_t(slot) * B;
-  // 128 keys (two 64-key tiles) per round: both tiles' loads go out together
-  u32x4_t bf[8][KS];
+  u32x4_t bf[4][KS];
   auto load_keys = [&](int64_t e0) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int nt = 0; nt < 4; ++nt) {
       const int64_t e = imax64(0, imin64(e0 + 16 * nt + r16, n - 1));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) bf[nt][ks] = ld16_nt(kb + e * D + 32 * ks);
     }
   };
-  auto tile = [&](int64_t e0, int t) {
+  auto tile = [&](int64_t e0) {
     float v[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ks], bf[4 * t + nt][ks], acc);
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ks], bf[nt][ks], acc);
       float s = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) s = fmaf(wv[i], relu_bits(acc[i]), s);
@@ -878,15 +879,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int64_t e = e0 + 16 * g + r16;
     if (e < e_end) out[e - e_begin] = s;
   };
-  load_keys(e_begin);
+  const int64_t first = e_begin + 64 * h;
+  load_keys(first);
   __builtin_amdgcn_sched_barrier(0);
-  for (int64_t e0 = e_begin; e0 < e_end; e0 += 128) {
-    if (e0 != e_begin) {
+  for (int64_t e0 = first; e0 < e_end; e0 += 64 * halves) {
+    if (e0 != first) {
       load_keys(e0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    tile(e0, 0);
-    if (e0 + 64 < e_end) tile(e0 + 64, 1);
+    tile(e0);
   }
 }
 
@@ -2120,11 +2121,12 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     }
 #undef HATTN_S2BM
   } else if (mfma2) {
-    dim3 grid(unsigned(m), unsigned(p.rows));
+    const int halves = B > 64 ? 2 : 1;  // 64-key tile groups per chosen block
+    dim3 grid(unsigned(m * halves), unsigned(p.rows));
     LaunchScope ls("score_stage2_mfma", st);
 #define HATTN_S2(KS)                                                                                         \
   HATTN_LAUNCH(score_stage2_mfma_kernel<KS>, grid, dim3(64), 0, st, (const uint16_t*)a.q_i,           \
-                     (const uint16_t*)a.k_i, a.w_i, a.n_vis, blk_out, a.nq, a.n, B, m, p.ld2, S2)
+                     (const uint16_t*)a.k_i, a.w_i, a.n_vis, blk_out, a.nq, a.n, B, m, p.ld2, S2, halves)
     switch (a.d_i) {
       case 32: HATTN_S2(1); break;
       case 64: HATTN_S2(2); break;
