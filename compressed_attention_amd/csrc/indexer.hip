@@ -1154,23 +1154,30 @@ __global__ __launch_bounds__(NT) void select_rows_kernel(const float* __restrict
   }
   uint32_t kc[kSelIT];
   seg_keys_masked(v, sg, nvalid, kc);
+  const bool pow2 = (B & (B - 1)) == 0;
+  const int lgB = __builtin_ctz(unsigned(B));
+  // Token rows: candidate i of slot s = i / B is entry blk[s] * B + i - s * B,
+  // i.e. i + dl[it].  The block ids are read here, so their LDS round trips
+  // overlap the threshold search instead of preceding each emitted store.
+  int dl[TOK ? kSelIT : 1];
+  if (TOK) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int it = 0; it < kSelIT; ++it) {
+      const int i = sg.p0 + it * kWave + lane;
+      const int sl = pow2 ? i >> lgB : i / B;
+      dl[it] = it < sg.iters && i < sg.p1 ? ((MODE == 2 ? bsh[sl] : brow[sl]) - sl) * B : 0;
+    }
+  }
   const SelThr st = radix_threshold<NT, kSelIT, true>(kc, sg.iters, k, sh);
   int32_t* orow = idx + row * k;
   float* scrow = score_out ? score_out + row * k : nullptr;
-  const bool pow2 = (B & (B - 1)) == 0;
-  const int lgB = __builtin_ctz(unsigned(B));
   // MODE 1, block-major stage 2: list[b][block][q] = slot of every block
   // query q of sequence b chose (the lists were cleared to -1 by stage 1)
   const int64_t bseq = MODE == 1 && inv_list ? idiv(row, nq) : 0;
   int32_t* lrow = MODE == 1 && inv_list ? inv_list + bseq * nb * nq + (row - bseq * nq) : nullptr;
   const int chosen = emit_selected<NT, kSelIT>(kc, sg, sh, st, [&](int slot, int i, uint32_t key, int it) {
-    int32_t val = i;
-    if (TOK) {
-      const int s = pow2 ? i >> lgB : i / B;
-      const int off = pow2 ? i & (B - 1) : i - s * B;
-      val = (MODE == 2 ? bsh[s] : brow[s]) * B + off;
-    }
-    orow[slot] = val;
+    orow[slot] = TOK ? i + dl[TOK ? it : 0] : i;
     if (scrow) scrow[slot] = key_to_float(key);
     if (MODE == 1 && lrow) lrow[int64_t(i) * nq] = slot;
   });
