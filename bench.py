@@ -484,6 +484,31 @@ def probe_decode_plan(args):
     log("[probe] done")
 
 
+def probe_indexer_128k(args):
+    """Runs the 128K flat indexer chunk (1,024 queries, 16 x 128, k = 2,048)
+    and then the HISA indexer on it, ``args.steps`` times each.  Run under
+    rocprofv3 --pmc for the score kernels' MFMA and VALU counters."""
+    import torch
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    W = synth.indexer_128k(0, device=dev)
+    t = W.tensors
+    N, nq, k, B, m = 131072, 1024, 2048, 128, 64
+    pos = torch.arange(N - nq, N, dtype=torch.int32, device=dev).reshape(1, nq)
+    nv = ops.visible_count(pos, 1, 1, N)
+    reps = ops.hisa_pool(t["k_i"], B)
+    torch.cuda.synchronize()
+    log(f"[probe] {args.steps} flat indexer chunks, then {args.steps} HISA chunks")
+    for _ in range(args.steps):
+        ops.index_topk(t["q_i"], t["k_i"], t["w_i"], nv, k)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        ops.hisa_topk(t["q_i"], t["k_i"], t["w_i"], nv, reps, B, m, k)
+    torch.cuda.synchronize()
+    log("[probe] done")
+
+
 def load_traffic():
     """Calibrated HBM bytes per launch of the dominant kernel, from the
     committed counter summary; None when it is missing or was taken on other
@@ -518,8 +543,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--probe", choices=["decode_plan"], default=None,
-                    help="run only the decode step and a calibration copy (for rocprofv3 --pmc)")
+    ap.add_argument("--probe", choices=["decode_plan", "indexer_128k"], default=None,
+                    help="run only the decode step and a calibration copy, or only the 128K indexer chunk "
+                         "(for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -534,6 +560,9 @@ def main():
     _lib.lib()  # fail loudly if the HIP library is missing
     if args.probe == "decode_plan":
         probe_decode_plan(args)
+        return
+    if args.probe == "indexer_128k":
+        probe_indexer_128k(args)
         return
 
     main_k = args.k
