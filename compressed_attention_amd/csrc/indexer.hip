@@ -1747,8 +1747,8 @@ static FlatPlan plan_flat(const IndexArgs& a, int k) {
     p.nch = int((a.n + p.chunk - 1) / p.chunk);
     p.fused = flat_mfma_ok(a) && a.d_i <= 128 && p.nch <= kCandMaxChunks && ntiles >= 64;
     if (p.fused) {
-      // 64 to 128 sample tiles (4,096 to 8,192 sample keys) spread evenly
-      p.tstride = int(ntiles / 64);
+      // 32 to 64 sample tiles (2,048 to 4,096 sample keys) spread evenly
+      p.tstride = int(ntiles / 32);
       p.lds = (ntiles + p.tstride - 1) / p.tstride * 64;
       p.samp_bytes = align256(size_t(p.rows) * p.lds * 4);
       p.thr_bytes = align256(size_t(p.rows) * 4);
