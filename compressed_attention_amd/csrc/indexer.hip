@@ -1530,7 +1530,7 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
 // any row whose scores do not depend on the key's position modulo the
 // stride.  Rows with v <= k, or a sample of at most r keys, take every key
 // (threshold key 0).  Also clears the row's chunk counts.
-constexpr int kThrNT = 512;
+constexpr int kThrNT = 256;
 __global__ __launch_bounds__(kThrNT) void flat_threshold_kernel(const float* __restrict__ Ssamp, int64_t lds,
                                                                 const int32_t* __restrict__ n_vis, int64_t n,
                                                                 int tstride, int k, uint32_t* __restrict__ thr,
