@@ -144,6 +144,46 @@ def kernel_times(fn, reps, steps):
     return {k: (v[0] / v[1], v[1] // steps) for k, v in tot.items()}
 
 
+def step_distribution(run_step, n):
+    """Per-step GPU time (us) of n consecutive steps: an event before each
+    step on the current stream (the same stream the steps are launched on),
+    so step i's time is the gap between its event and the next.  Returns
+    median / p10 / p90 / mean over the n steps."""
+    import numpy as np
+    import torch
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        evs[i].record()
+        run_step(i)
+    evs[n].record()
+    torch.cuda.synchronize()
+    us = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n)])
+    return dict(n=n, median=float(np.median(us)), p10=float(np.percentile(us, 10)),
+                p90=float(np.percentile(us, 90)), mean=float(us.mean()))
+
+
+def flat_decode_step(args, t, caches, k):
+    """The same decode step with the flat indexer in place of HISA (scores
+    every one of the 262,143 visible entries of each query), as one graph
+    per cache replica; returns ms per step."""
+    from compressed_attention_amd import ops
+
+    def step(c):
+        nv = ops.decode_append(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, t["q_pos"], c["ckv"])
+        idx = ops.index_topk(t["q_i"], c["k_i"], t["w_i"], nv, k)
+        o1 = ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128)
+        nvh = ops.decode_append(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, t["q_pos"], c["hkv"])
+        o2 = ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128)
+        return o1, o2
+
+    graphs = capture(step, caches)
+    ms = timed_graphs(graphs, max(10, args.steps), 3)
+    del graphs
+    return ms
+
+
 # ----------------------------------------------------------------------------
 # main workload: hybrid layer pair decode at 1M
 # ----------------------------------------------------------------------------
@@ -213,6 +253,7 @@ def hybrid_pair(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    dist = step_distribution(replay, max(30, args.steps))
 
     # For comparison: the same step as two HIP graphs (one per branch) on two
     # streams joined every step; torch's graph replays and stream joins cost
@@ -253,8 +294,9 @@ def hybrid_pair(args):
         "score_stage2_mfma": bt * hisa_stage2_bytes(m * B),
     }
     step_bytes = sum(kb.values())
+    flat_ms = flat_decode_step(args, t, caches, k) if args.flat_compare else None
     info = dict(ms=ms, graph_ms=graph_ms, kernels=kt, kernels_calls=kt_calls, kernel_bytes=kb, step_bytes=step_bytes,
-                bt=bt, N=N, Nh=Nh, k=k, L=L)
+                bt=bt, N=N, Nh=Nh, k=k, L=L, dist=dist, flat_ms=flat_ms)
     for p_ in plans:
         p_.close()
     return info
@@ -332,6 +374,7 @@ def csa_prefill(args):
 
 
 def indexer_128k(args):
+    import numpy as np
     import torch
     from compressed_attention_amd import ops, synth
 
@@ -370,6 +413,11 @@ def indexer_128k(args):
             rec_f.append(len(vis & a) / len(vis))
             rec_h.append(len(vis & b) / len(vis))
     flops = 2.0 * 16 * 128 * float(nvh.sum())
+    # HISA's own work: every candidate block of each query (stage 1) and the
+    # visible tokens of its m chosen blocks (stage 2, at most m * B)
+    nbq = (nvh.astype(float) + B - 1) // B
+    hisa_flops = 2.0 * 16 * 128 * float((nbq + np.minimum(m * B, nvh)).sum())
+    out.update(hisa_flops=hisa_flops)
     out.update(iou_mean=float(sum(ious) / len(ious)), iou_min=float(min(ious)),
                needle_recall_flat=float(sum(rec_f) / len(rec_f)), needle_recall_hisa=float(sum(rec_h) / len(rec_h)),
                flat_flops=flops)
@@ -380,19 +428,40 @@ def indexer_128k(args):
 # CPU baseline: the fp64 oracle on a bounded sample of the same decode step
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(args, k):
+def host_cpu_info():
+    """nproc (this process's CPU affinity), the CPU model and the BLAS pool."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        nproc = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        pass
+    return nproc, model, blas
+
+
+def _oracle_decode_rate(k, seconds):
+    """Decode queries/s of the fp64 oracle on one 2^20-token sequence per
+    query (both layers), for about `seconds` of host time."""
     import numpy as np
     import torch
 
     import oracle
     from compressed_attention_amd import synth
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    N, Nh, B, m, L, W = 262143, 8192, 128, 64, 1 << 20, 128
+    N, Nh, B, m, W = 262143, 8192, 128, 64, 128
     # One sequence's caches, drawn on the host (values do not affect timing).
     ckv = synth.normal((N, 256), 901, dtype=torch.bfloat16).double().numpy()
     hkv = synth.normal((Nh, 256), 902, dtype=torch.bfloat16).double().numpy()
@@ -418,12 +487,30 @@ def cpu_baseline(args, k):
         oracle.dense_compressed_attention(qh, hkv, np.array([Nh]), tail, np.array([p_local]), W, 1 / math.sqrt(128))
         done += 1
         el += time.perf_counter() - s
-        if el >= args.cpu_seconds or done >= 2000:
+        if el >= seconds or done >= 2000:
             break
-    return dict(value=done / el, unit="decode queries/s", cores=int(threads), kind="oracle",
-                sample=f"{done} decode queries of one 2^20-token sequence (both layers, k={k}), "
-                       f"{el:.1f} s of host time; block means precomputed as in the GPU step")
+    return done, el
 
+
+def cpu_baseline(args, k):
+    """The oracle timed twice on the host: with the BLAS pool as the process
+    starts it (all of the host share) and limited to one thread."""
+    nproc, model, blas = host_cpu_info()
+    half = max(1.0, args.cpu_seconds / 2)
+    done, el = _oracle_decode_rate(k, half)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            d1, e1 = _oracle_decode_rate(k, half)
+        one = d1 / e1
+    except Exception as exc:  # pragma: no cover
+        log(f"[bench] one-thread oracle run skipped: {exc}")
+    return dict(value=done / el, unit="decode queries/s", cores=int(blas), kind="oracle",
+                value_1core=one, nproc=nproc, cpu_model=model, blas_threads=int(blas),
+                sample=f"{done} decode queries of one 2^20-token sequence each (both layers, k={k}), "
+                       f"{el:.1f} s of host time with {blas} BLAS threads, then the same with 1 thread; "
+                       f"block means precomputed as in the GPU step")
 
 
 # ----------------------------------------------------------------------------
@@ -541,8 +628,10 @@ def main():
     ap.add_argument("--k", type=int, default=2048, choices=[512, 2048])
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flat-compare", dest="flat_compare", action="store_false",
+                    help="skip timing the decode step with the flat indexer in place of HISA")
     ap.add_argument("--probe", choices=["decode_plan", "indexer_128k"], default=None,
                     help="run only the decode step and a calibration copy, or only the 128K indexer chunk "
                          "(for rocprofv3 --pmc)")
@@ -574,6 +663,8 @@ def main():
         a2.k = 512 if main_k == 2048 else 2048
         r2 = hybrid_pair(a2)
         extras[f"hybrid_pair_k{a2.k}"] = dict(us_per_step=r2["ms"] * 1e3, queries_per_s=r2["bt"] / (r2["ms"] * 1e-3),
+                                             step_us=r2["dist"],
+                                             flat_indexer_step_us=None if r2["flat_ms"] is None else r2["flat_ms"] * 1e3,
                                              step_GBps=r2["step_bytes"] / (r2["ms"] * 1e-3) / 1e9,
                                              hbm_frac=r2["step_bytes"] / (r2["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
         torch.cuda.empty_cache()
@@ -610,6 +701,8 @@ def main():
             flat_score_kernel_ms=fk, flat_score_TFLOPs=ix["flat_flops"] / (fk * 1e-3) / 1e12,
             flat_score_mfma_frac=ix["flat_flops"] / (fk * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             flat_total_mfma_frac=ix["flat_flops"] / (ix["flat"]["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            hisa_TFLOPs=ix["hisa_flops"] / (ix["hisa"]["ms"] * 1e-3) / 1e12,
+            hisa_mfma_frac=ix["hisa_flops"] / (ix["hisa"]["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             hisa_vs_flat_iou_mean=ix["iou_mean"], hisa_vs_flat_iou_min=ix["iou_min"],
             needle_recall_flat=ix["needle_recall_flat"], needle_recall_hisa=ix["needle_recall_hisa"],
             flat_kernels_ms={kk: v[0] for kk, v in ix["flat"]["kernels"].items()},
@@ -647,6 +740,8 @@ def main():
                    "head_dim": 128, "window": 128, "csa_entries": res["N"], "hca_entries": res["Nh"],
                    "indexer": "16x128", "hisa_B": 128, "hisa_m": 64, "k": res["k"], "cache_replicas": args.replicas,
                    "launch": "native decode plan (one host call, 6 kernels per step)"},
+        "step_us": {kk: round(v, 2) for kk, v in res["dist"].items() if kk != "n"} | {"n": res["dist"]["n"]},
+        "flat_indexer_step_us": None if res["flat_ms"] is None else round(res["flat_ms"] * 1e3, 1),
         "step_GBps": round(res["step_bytes"] / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(res["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": roof,

@@ -6,6 +6,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhattn.so")
+ABI_VERSION = 2  # hattn_abi_version() of the library this binding matches
 
 _i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 _psz = ctypes.POINTER(ctypes.c_size_t)
@@ -50,7 +51,7 @@ class DecodeDesc(ctypes.Structure):
         ("q_pos", _p),
         ("csa_raw_kv", _p), ("csa_logits", _p), ("csa_pos_bias", _p), ("csa_ckv", _p),
         ("k_i", _p), ("reps", _p), ("q_i", _p), ("w_i", _p),
-        ("csa_q", _p), ("csa_out", _p), ("csa_lse", _p),
+        ("csa_q", _p), ("csa_out", _p), ("csa_lse", _p), ("csa_idx", _p),
         ("hca_raw_kv", _p), ("hca_logits", _p), ("hca_pos_bias", _p), ("hca_ckv", _p),
         ("hca_q", _p), ("hca_out", _p), ("hca_lse", _p),
         ("ws", _p), ("ws_bytes", ctypes.c_size_t),
@@ -74,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.hattn_status_string.restype = ctypes.c_char_p
         L.hattn_last_error.restype = ctypes.c_char_p
         L.hattn_decode_desc_size.restype = ctypes.c_int64
+        if L.hattn_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libhattn.so has ABI {L.hattn_abi_version()}, the binding expects {ABI_VERSION}; "
+                               "rebuild it with __graft_entry__.build()")
         if L.hattn_decode_desc_size() != ctypes.sizeof(DecodeDesc):
             raise RuntimeError("hattn_decode_desc layout differs between the library and the binding")
         _lib = L

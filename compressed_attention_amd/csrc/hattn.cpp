@@ -139,7 +139,7 @@ const char* hattn_status_string(int status) {
 
 const char* hattn_last_error(void) { return g_err; }
 
-int hattn_abi_version(void) { return 1; }
+int hattn_abi_version(void) { return 2; }
 
 // Arrays that kernels access with 16-byte vector loads or stores; NULL passes.
 static bool aligned16(std::initializer_list<const void*> ps) {
@@ -448,12 +448,14 @@ hattn_status_t decode_layout(const hattn_decode_desc* d, size_t* total, hattn_de
   const size_t o_hisa = o_idx + al256(size_t(d->bt) * std::max(d->k, 1) * 4);
   char* base = reinterpret_cast<char*>(d->ws);
   auto at = [&](size_t off) -> void* { return base ? base + off : reinterpret_cast<void*>(uintptr_t(256)); };
+  // the selected indices: the caller's array when given, else the workspace's
+  int32_t* idx = d->csa_idx ? d->csa_idx : reinterpret_cast<int32_t*>(at(o_idx));
   hattn::IndexArgs ia{d->dtype, d->q_i, d->k_i, d->w_i, (const int32_t*)at(o_nvc), d->bt, 1, d->h_i, d->d_i, Nc};
   st = hisa_check(d->dtype, d->q_i, d->k_i, d->w_i, ia.n_vis, d->bt, 1, d->h_i, d->d_i, Nc, d->reps, d->B, d->m,
-                  d->k, (const int32_t*)at(o_idx), d->ws);
+                  d->k, idx, d->ws);
   if (st != HATTN_OK) return st;
   const size_t o_sa = o_hisa + al256(hattn::hisa_topk_ws_bytes(ia, d->B, d->m, d->k));
-  hattn::AttnArgs sa{d->dtype, d->csa_q, d->csa_ckv, Nc, (const int32_t*)at(o_idx), d->k, nullptr, d->csa_raw_kv,
+  hattn::AttnArgs sa{d->dtype, d->csa_q, d->csa_ckv, Nc, idx, d->k, nullptr, d->csa_raw_kv,
                      d->L, d->q_pos, d->window, d->scale, d->bt, 1, d->h, d->d, d->csa_out, d->csa_lse};
   st = attn_check("decode_plan (CSA attention)", sa, d->ws);
   if (st != HATTN_OK) return st;
@@ -483,7 +485,7 @@ hattn_status_t decode_layout(const hattn_decode_desc* d, size_t* total, hattn_de
   p->m = d->m;
   p->k = d->k;
   p->nv_csa = reinterpret_cast<int32_t*>(at(o_nvc));
-  p->idx = reinterpret_cast<int32_t*>(at(o_idx));
+  p->idx = idx;
   p->ia = ia;
   p->hisa_ws = at(o_hisa);
   p->sa = sa;
@@ -498,7 +500,7 @@ hattn_status_t decode_layout(const hattn_decode_desc* d, size_t* total, hattn_de
   p->nv_hca = reinterpret_cast<int32_t*>(at(o_nvh));
   p->da = da;
   p->da_ws = at(o_da);
-  p->front = hattn::decode_front_ok(ia, d->B, d->m);
+  p->front = hattn::decode_front_ok(ia, d->B, d->m, std::max(d->csa_w, d->hca_w));
   return HATTN_OK;
 }
 

@@ -384,7 +384,9 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_
           if (e < my_nv[p]) srow[p][el] = tot;
         } else {
           if (any_all && my_all[p] && el < my_nv[p]) srow[p][el] = tot;
-          const bool ok = el < my_nv[p] && tot >= my_thr[p];
+          // rows that take every key store plain scores above and pack
+          // nothing (their threshold +inf would still admit a score of +inf)
+          const bool ok = !my_all[p] && el < my_nv[p] && tot >= my_thr[p];
           const uint64_t m = ballot(ok);
           if (m != 0ull) {
             const uint32_t mlo = uint32_t(m), mhi = uint32_t(m >> 32);
@@ -1745,7 +1747,10 @@ static FlatPlan plan_flat(const IndexArgs& a, int k) {
     const int64_t ntiles = (a.n + 63) / 64;
     p.chunk = flat_chunk(a, a.n);
     p.nch = int((a.n + p.chunk - 1) / p.chunk);
-    p.fused = flat_mfma_ok(a) && a.d_i <= 128 && p.nch <= kCandMaxChunks && ntiles >= 64;
+    // The threshold keeps about 2k candidates (+-12% at the smallest sample);
+    // the candidate select holds kSelIT * kCandNT = 8,192 of them, so larger
+    // k would flag most rows and rerun them on the full path.
+    p.fused = flat_mfma_ok(a) && a.d_i <= 128 && p.nch <= kCandMaxChunks && ntiles >= 64 && k <= 3072;
     if (p.fused) {
       // 32 to 64 sample tiles (2,048 to 4,096 sample keys) spread evenly
       p.tstride = int(ntiles / 32);
@@ -1980,9 +1985,21 @@ size_t hisa_topk_ws_bytes(const IndexArgs& a, int B, int m, int k) {
   return plan_hisa(a, B, m).total;
 }
 
-bool decode_front_ok(const IndexArgs& a, int B, int m) {
-  return a.dtype == 1 && a.h_i == 16 && a.d_i % 16 == 0 && a.d_i <= 256 && a.nq == 1 && !plan_hisa(a, B, m).bm &&
-         a.n > 0;
+// Head sizes with an MFMA stage-1 (and decode front) instantiation: the
+// kernels are compiled for d_i = 16 * KQ with KQ in {1, 2, 4, 8, 16} only, so
+// every other width must take the vector kernel.
+static bool stage1_mfma_dim(int d_i) {
+  return d_i == 16 || d_i == 32 || d_i == 64 || d_i == 128 || d_i == 256;
+}
+
+// The front kernel's static LDS tile (64 * (d_i + 4) floats) doubles as the
+// scratch of its cache-maintenance roles: an entry role needs w softmax
+// weights plus 2,048 floats of row-group sums (256 threads x 8 bf16 each),
+// and the fresh block mean needs 2,048 floats of row-group sums too.
+bool decode_front_ok(const IndexArgs& a, int B, int m, int max_w) {
+  const int64_t tile = 64LL * (a.d_i + 4);
+  return a.dtype == 1 && a.h_i == 16 && stage1_mfma_dim(a.d_i) && a.nq == 1 && !plan_hisa(a, B, m).bm &&
+         a.n > 0 && tile >= int64_t(max_w) + 2048;
 }
 
 hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, void* ws, const int32_t* q_pos,
@@ -2001,12 +2018,13 @@ hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, vo
 #define HATTN_FRONT(KQ)                                                                                      \
   HATTN_LAUNCH(decode_front_kernel<KQ>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i, reps, a.w_i, q_pos, B, \
                p.nb, p.ld1, S1, nch, nch_grid, la, lb, nroles)
-  switch (a.d_i / 16) {
-    case 1: HATTN_FRONT(1); break;
-    case 2: HATTN_FRONT(2); break;
-    case 4: HATTN_FRONT(4); break;
-    case 8: HATTN_FRONT(8); break;
-    default: HATTN_FRONT(16); break;
+  switch (a.d_i) {
+    case 16: HATTN_FRONT(1); break;
+    case 32: HATTN_FRONT(2); break;
+    case 64: HATTN_FRONT(4); break;
+    case 128: HATTN_FRONT(8); break;
+    case 256: HATTN_FRONT(16); break;
+    default: return hipErrorInvalidValue;  // decode_front_ok admits no other width
   }
 #undef HATTN_FRONT
   return hipGetLastError();
@@ -2023,7 +2041,7 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
   int32_t* blk_out = blk ? blk : blk_ws;
 
   // Stage 1: block scores.
-  const bool mfma1 = a.h_i == 16 && a.d_i % 16 == 0 && a.d_i <= 256;
+  const bool mfma1 = a.h_i == 16 && stage1_mfma_dim(a.d_i);
   const bool bm = p.bm && mfma1;  // the stage-1 MFMA kernel clears the lists
   int32_t* bm_list = bm ? reinterpret_cast<int32_t*>(base + p.s1_bytes + p.blk_bytes + p.s2_bytes) : nullptr;
   const int64_t bm_fill = bm ? a.bt * p.nb * a.nq : 0;
@@ -2062,20 +2080,20 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
     HATTN_LAUNCH((score_stage1_kernel<T, KQ, 1>), grid, dim3(256), 0, st, (const T*)a.q_i, reps, a.w_i, \
                  a.n_vis, a.nq, a.n, B, p.nb, p.ld1, S1, nqg, nch, chunk, bm_list, bm_fill)
     if (a.dtype == 0) {
-      switch (a.d_i / 16) {
-        case 1: HATTN_S1(float, 1); break;
-        case 2: HATTN_S1(float, 2); break;
-        case 4: HATTN_S1(float, 4); break;
-        case 8: HATTN_S1(float, 8); break;
-        default: HATTN_S1(float, 16); break;
+      switch (a.d_i) {
+        case 16: HATTN_S1(float, 1); break;
+        case 32: HATTN_S1(float, 2); break;
+        case 64: HATTN_S1(float, 4); break;
+        case 128: HATTN_S1(float, 8); break;
+        default: HATTN_S1(float, 16); break;  // 256 (stage1_mfma_dim)
       }
     } else {
-      switch (a.d_i / 16) {
-        case 1: HATTN_S1(uint16_t, 1); break;
-        case 2: HATTN_S1(uint16_t, 2); break;
-        case 4: HATTN_S1(uint16_t, 4); break;
-        case 8: HATTN_S1(uint16_t, 8); break;
-        default: HATTN_S1(uint16_t, 16); break;
+      switch (a.d_i) {
+        case 16: HATTN_S1(uint16_t, 1); break;
+        case 32: HATTN_S1(uint16_t, 2); break;
+        case 64: HATTN_S1(uint16_t, 4); break;
+        case 128: HATTN_S1(uint16_t, 8); break;
+        default: HATTN_S1(uint16_t, 16); break;  // 256 (stage1_mfma_dim)
       }
     }
 #undef HATTN_S1

@@ -79,7 +79,9 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
 // layer behind the indexer (layer 1: its entry, visible count and the block
 // mean holding the new entry) and optionally a second layer (layer 2: entry
 // and visible count).  Then launch_hisa_topk(..., stage1_done = true).
-bool decode_front_ok(const IndexArgs& a, int B, int m);
+// max_w: the longest compression window of the layers whose entries the
+// launch maintains (the roles reuse the kernel's LDS tile as scratch).
+bool decode_front_ok(const IndexArgs& a, int B, int m, int max_w);
 hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, void* ws, const int32_t* q_pos,
                                const void* x1, const float* z1, const float* bias1, int w1, int s1, void* y1,
                                int32_t* n_vis1, const void* x2, const float* z2, const float* bias2, int w2, int s2,

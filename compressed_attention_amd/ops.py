@@ -291,13 +291,14 @@ class DecodePlan:
     [bt][1]; csa_q / hca_q [bt][1][h][d]; q_i [bt][1][h_i][d_i]; w_i
     [bt][1][h_i].  csa_ckv, hca_ckv and reps are rewritten in place each run.
     The plan holds references to every tensor; outputs live in .csa_out /
-    .hca_out ([bt][1][h][d] fp32) and, with return_lse, .csa_lse / .hca_lse.
+    .hca_out ([bt][1][h][d] fp32), with return_lse in .csa_lse / .hca_lse,
+    and with return_idx the CSA selection in .csa_idx ([bt][1][k] int32).
     """
 
     def __init__(self, *, q_pos, csa_raw_kv, csa_logits, csa_pos_bias, csa_ckv, k_i, reps, q_i, w_i, csa_q,
                  hca_raw_kv, hca_logits, hca_pos_bias, hca_ckv, hca_q, B: int, m: int, k: int, csa_w: int = 8,
                  csa_stride: int = 4, hca_w: int = 128, hca_stride: int = 128, window: int = 128,
-                 scale: float | None = None, return_lse: bool = False):
+                 scale: float | None = None, return_lse: bool = False, return_idx: bool = False):
         from ._lib import DecodeDesc
 
         self._plan = None
@@ -327,6 +328,7 @@ class DecodePlan:
         self.hca_out = torch.empty((bt, 1, h, d), dtype=torch.float32, device=dev)
         self.csa_lse = torch.empty((bt, 1, h), dtype=torch.float32, device=dev) if return_lse else None
         self.hca_lse = torch.empty((bt, 1, h), dtype=torch.float32, device=dev) if return_lse else None
+        self.csa_idx = torch.empty((bt, 1, k), dtype=torch.int32, device=dev) if return_idx else None
         self._keep = [q_pos, csa_raw_kv, csa_logits, csa_pos_bias, csa_ckv, k_i, reps, q_i, w_i, csa_q, hca_raw_kv,
                       hca_logits, hca_pos_bias, hca_ckv, hca_q]
         self.device = dev
@@ -335,7 +337,7 @@ class DecodePlan:
                           q_pos=_ptr(q_pos), csa_raw_kv=_ptr(csa_raw_kv), csa_logits=_ptr(csa_logits),
                           csa_pos_bias=_ptr(csa_pos_bias), csa_ckv=_ptr(csa_ckv), k_i=_ptr(k_i), reps=_ptr(reps),
                           q_i=_ptr(q_i), w_i=_ptr(w_i), csa_q=_ptr(csa_q), csa_out=_ptr(self.csa_out),
-                          csa_lse=_ptr(self.csa_lse), hca_raw_kv=_ptr(hca_raw_kv), hca_logits=_ptr(hca_logits),
+                          csa_lse=_ptr(self.csa_lse), csa_idx=_ptr(self.csa_idx), hca_raw_kv=_ptr(hca_raw_kv), hca_logits=_ptr(hca_logits),
                           hca_pos_bias=_ptr(hca_pos_bias), hca_ckv=_ptr(hca_ckv), hca_q=_ptr(hca_q),
                           hca_out=_ptr(self.hca_out), hca_lse=_ptr(self.hca_lse), ws=None, ws_bytes=0)
         Lb = lib()

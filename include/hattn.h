@@ -68,7 +68,7 @@ typedef enum { HATTN_F32 = 0, HATTN_BF16 = 1 } hattn_dtype_t;
 const char* hattn_status_string(int status);
 /* Detail for the calling thread's last failing call (static thread storage). */
 const char* hattn_last_error(void);
-/* Version of this ABI (bumped on incompatible changes). */
+/* Version of this ABI (bumped on incompatible changes; 2: hattn_decode_desc gained csa_idx). */
 int hattn_abi_version(void);
 
 /*
@@ -119,8 +119,9 @@ hattn_status_t hattn_visible_count(const int32_t* pos, int64_t count, int32_t w,
  *   idx   [bt][nq][k]         int32 out   score [bt][nq][k] fp32 out or NULL
  *         (the selected scores; -inf where idx is -1)
  *   ws    workspace (size by query, see conventions)
- * Requires 1 <= k <= 8192, 1 <= h_i <= 64, d_i in {32, 64, 128, 256} for
- * bf16 (any d_i <= 256 for fp32).
+ * Requires 1 <= k <= 8192, 1 <= h_i <= 64, 1 <= d_i <= 256, h_i * d_i <=
+ * 8192 (HATTN_ERR_UNSUPPORTED above).  bf16 with h_i = 16 and d_i in
+ * {32, 64, 128, 256} runs on MFMA; every other shape on the vector kernel.
  */
 hattn_status_t hattn_index_topk(int dtype, const void* q_i, const void* k_i, const float* w_i,
                                 const int32_t* n_vis, int64_t bt, int64_t nq, int32_t h_i, int32_t d_i,
@@ -151,7 +152,15 @@ hattn_status_t hattn_hisa_pool(int dtype, const void* k_i, int64_t bt, int64_t n
  *   q_i, k_i, w_i, n_vis as for hattn_index_topk; reps from hattn_hisa_pool.
  *   idx [bt][nq][k] int32 out;  blk [bt][nq][m] int32 out (chosen blocks,
  *   ascending, -1 padded) or NULL.
- * Requires 1 <= B <= 1024, 1 <= m, m*B <= 16384, 1 <= k <= 8192.
+ * Requires 1 <= B <= 1024, 1 <= m, m*B <= 16384, 1 <= k <= 8192, and the
+ * indexer shape limits of hattn_index_topk.  With h_i = 16 the block scores
+ * run on MFMA for d_i in {16, 32, 64, 128, 256} (bf16 or fp32 queries);
+ * other shapes take the vector kernel.
+ *
+ * Departure from a compute-the-block-means mode: the block means are always
+ * an input here (hattn_hisa_pool builds them once per prefix, and
+ * hattn_decode_append keeps the last block current), so this call only reads
+ * them.
  */
 hattn_status_t hattn_hisa_topk(int dtype, const void* q_i, const void* k_i, const float* w_i,
                                const int32_t* n_vis, int64_t bt, int64_t nq, int32_t h_i, int32_t d_i,
@@ -250,6 +259,9 @@ hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, in
  *   k_i [bt][N][d_i], reps [bt][ceil(N/B)][d_i] fp32 (rewritten in place),
  *   q_i [bt][h_i][d_i], w_i [bt][h_i] fp32, h_i, d_i, B, m, k
  *   csa_q [bt][h][d], csa_out [bt][h][d] fp32, csa_lse [bt][h] fp32 or NULL
+ *   csa_idx [bt][k] int32 or NULL: where given, the step leaves the CSA
+ *     branch's selected entries there (hattn_hisa_topk's idx); otherwise
+ *     they live in the workspace
  *   hca_raw_kv, hca_logits, hca_pos_bias, hca_w, hca_stride, hca_ckv,
  *   hca_q, hca_out, hca_lse     (as the CSA fields, for the HCA branch)
  *   ws, ws_bytes               workspace (size: hattn_decode_plan_ws_bytes);
@@ -288,6 +300,7 @@ typedef struct hattn_decode_desc {
   const void* csa_q;
   float* csa_out;
   float* csa_lse;
+  int32_t* csa_idx;
   const void* hca_raw_kv;
   const float* hca_logits;
   const float* hca_pos_bias;

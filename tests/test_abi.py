@@ -35,7 +35,7 @@ def test_exports_match_header(L):
 def test_status_strings(L):
     for s in range(5):
         assert L.hattn_status_string(s).startswith(b"HATTN_")
-    assert L.hattn_abi_version() == 1
+    assert L.hattn_abi_version() == _lib.ABI_VERSION
 
 
 def test_compress_validation(L):

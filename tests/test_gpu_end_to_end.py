@@ -154,3 +154,52 @@ def test_decode_plan_matches_separate_calls_and_oracle():
         assert np.abs(f64(o1[b]) - r_o1).max() < 1e-2
         assert np.abs(f64(o2[b]) - r_o2).max() < 1e-2
     plan.close()
+
+
+@pytest.mark.parametrize("dtype,d_i", [(torch.bfloat16, 48), (torch.float32, 48), (torch.bfloat16, 16),
+                                       (torch.bfloat16, 32), (torch.float32, 128)])
+def test_decode_plan_indexer_widths(dtype, d_i):
+    # The decode plan at indexer widths that take each stage-1 path: 48 has no
+    # MFMA instantiation (vector kernels), 16 has one but its LDS tile is too
+    # small for the fused front kernel's cache-maintenance scratch, 32 runs
+    # the fused front kernel; fp32 runs every step on the vector kernels.
+    # Integer-grid indexer with 4-bit weights: the selection is exact.
+    bt, L = 2, 16384
+    N, Nh = oracle.n_entries(L, 8, 4), oracle.n_entries(L, 128, 128)
+    B, m, k = 128, 8, 256
+    t = dict(synth.hybrid_pair_decode(2, device="cpu", bt=bt, L=L, N_csa=N).tensors)
+    t["q_i"] = synth.int_grid((bt, 1, 16, d_i), 341 + d_i, -4, 4)
+    t["k_i"] = synth.int_grid((bt, N, d_i), 342 + d_i, -4, 4)
+    t["w_i"] = synth.dyadic_uniform((bt, 1, 16), 343 + d_i, bits=4)
+    for name in ("csa_raw_kv", "csa_q", "hca_raw_kv", "hca_q", "q_i", "k_i"):
+        t[name] = t[name].to(dtype)
+    g = {k_: v.to(DEV) for k_, v in t.items()}
+    ckv = ops.compress(g["csa_raw_kv"], g["csa_z"], g["csa_b"], 8, 4)
+    hkv = ops.compress(g["hca_raw_kv"], g["hca_z"], g["hca_b"], 128, 128)
+    ckv[:, N - 1] = 0
+    hkv[:, Nh - 1] = 0
+    reps = ops.hisa_pool(g["k_i"], B)
+    reps[:, -1] = 0
+    plan = ops.DecodePlan(q_pos=g["q_pos"], csa_raw_kv=g["csa_raw_kv"], csa_logits=g["csa_z"], csa_pos_bias=g["csa_b"],
+                          csa_ckv=ckv, k_i=g["k_i"], reps=reps, q_i=g["q_i"], w_i=g["w_i"], csa_q=g["csa_q"],
+                          hca_raw_kv=g["hca_raw_kv"], hca_logits=g["hca_z"], hca_pos_bias=g["hca_b"], hca_ckv=hkv,
+                          hca_q=g["hca_q"], B=B, m=m, k=k, return_idx=True)
+    o1, o2 = plan.run()
+    torch.cuda.synchronize()
+    tol = 1e-2 if dtype == torch.bfloat16 else 1e-4
+    sc = 1 / math.sqrt(128)
+    for b in range(bt):
+        raw_c, raw_h = f64(t["csa_raw_kv"][b]), f64(t["hca_raw_kv"][b])
+        r_ckv = oracle.compress(raw_c, f64(t["csa_z"][b]), f64(t["csa_b"]), 8, 4)
+        r_hkv = oracle.compress(raw_h, f64(t["hca_z"][b]), f64(t["hca_b"]), 128, 128)
+        p = int(t["q_pos"][b, 0])
+        r_idx, _ = oracle.hisa_topk(f64(t["q_i"][b]), f64(t["k_i"][b]), f64(t["w_i"][b]), np.array([N]), B, m, k)
+        assert np.array_equal(plan.csa_idx[b].cpu().numpy(), r_idx), b
+        r_o1, _ = oracle.sparse_attention(f64(t["csa_q"][b]), r_ckv, r_idx, raw_c, np.array([p]), 128, sc)
+        r_o2, _ = oracle.dense_compressed_attention(f64(t["hca_q"][b]), r_hkv, [Nh], raw_h, np.array([p]), 128, sc)
+        assert np.abs(f64(o1[b]) - r_o1).max() < tol, b
+        assert np.abs(f64(o2[b]) - r_o2).max() < tol, b
+    # the appended block mean is the oracle's mean of the last block
+    r_reps = oracle.hisa_pool(f64(t["k_i"][0]), B)
+    assert np.array_equal(f64(reps[0, -1]), r_reps[-1])
+    plan.close()

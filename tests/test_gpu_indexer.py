@@ -365,3 +365,29 @@ def test_fused_flat_float_inputs_vs_oracle():
         return 128 * 2.0**-23 * float((ww[r][:, None] * (qa @ np.abs(kk).T)).max()) * 4
 
     check_near_ties(got, ref, scores, tol)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d_i", [16, 48, 80, 256])
+def test_hisa_indexer_widths_exact(dtype, d_i):
+    # Block scores on MFMA exist for d_i in {16, 32, 64, 128, 256}; other
+    # widths (48, 80) must take the vector kernel.  Several queries per
+    # sequence and one query per sequence, ragged key count, mixed
+    # visibility; integer grid with 4-bit weights (bound asserted).
+    N, B, m, k = 3001, 64, 6, 200
+    for bt, nq in ((2, 40), (3, 1)):
+        q_i = synth.int_grid((bt, nq, 16, d_i), 401 + d_i, -4, 4, dtype=dtype)
+        k_i = synth.int_grid((bt, N, d_i), 402 + d_i, -4, 4, dtype=dtype)
+        w_i = synth.dyadic_uniform((bt, nq, 16), 403 + d_i, bits=4)
+        nv = synth.int_grid((bt, nq), 404 + d_i, 1, N, dtype=torch.int32)
+        nv[0, 0] = N
+        kd = k_i.to(DEV)
+        reps = ops.hisa_pool(kd, B)
+        idx, blk = ops.hisa_topk(q_i.to(DEV), kd, w_i.to(DEV), nv.to(DEV), reps, B, m, k, return_blocks=True)
+        torch.cuda.synchronize()
+        for b in range(bt):
+            q, kk, ww = f64(q_i[b]), f64(k_i[b]), f64(w_i[b])
+            _stage1_exact_bound(q, kk, ww, B, 4)
+            ref, ref_blk = oracle.hisa_topk(q, kk, ww, nv[b].numpy(), B, m, k)
+            assert np.array_equal(blk.cpu().numpy()[b], ref_blk), (d_i, bt, b)
+            assert np.array_equal(idx.cpu().numpy()[b], ref), (d_i, bt, b)
