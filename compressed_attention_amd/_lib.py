@@ -21,6 +21,8 @@ SIGNATURES = {
                         _p],
     "hattn_sparse_attn": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p, _p,
                           _psz, _p],
+    "hattn_sparse_attn_noalloc": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p,
+                                  _p, _p],
     "hattn_dense_compressed_attn": [_i32, _p, _p, _i64, _p, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p,
                                     _p, _psz, _p],
     "hattn_decode_append": [_i32, _p, _i64, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p, _p, _i32, _i32, _p, _p],

@@ -18,11 +18,39 @@
 // With more than one chunk per query the unnormalised (O, max, sum) partials
 // are combined by a second kernel with the log-sum-exp identity.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "internal.h"
 
 namespace hattn {
+
+// Device scratch for callers that cannot allocate (hattn_sparse_attn_noalloc):
+// the split-K partials of one attention call.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSparseChunkMax = 2048;  // keys per sparse MFMA workgroup (their indices are staged in LDS)

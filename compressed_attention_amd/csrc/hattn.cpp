@@ -287,6 +287,30 @@ hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int6
   return attn_common("sparse_attn", a, ws, ws_bytes, stream);
 }
 
+hattn_status_t hattn_sparse_attn_noalloc(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx,
+                                         int32_t k, const void* raw_kv, int64_t L, const int32_t* q_pos,
+                                         int32_t window, float scale, int64_t bt, int64_t nq, int32_t h, int32_t d,
+                                         float* out, float* lse, void* stream) {
+  if (k < 0) return fail(HATTN_ERR_ARG, "sparse_attn_noalloc: k < 0");
+  if (bt * nq > 0 && k > 0 && !idx) return fail(HATTN_ERR_ARG, "sparse_attn_noalloc: NULL idx");
+  hattn::AttnArgs a{dtype, q, ckv, n, k > 0 ? idx : q_pos, k, nullptr, raw_kv, L, q_pos, window, scale,
+                    bt, nq, h, d, out, lse};
+  hattn_status_t st = attn_check("sparse_attn_noalloc", a, nullptr);
+  if (st != HATTN_OK) return st;
+  const int64_t rows = bt * nq;
+  if (rows == 0) return ok();
+  const size_t need = hattn::attn_ws_bytes(a);
+  if (need > hattn::kStaticScratchBytes)
+    return fail(HATTN_ERR_WORKSPACE, "sparse_attn_noalloc: needs %zu bytes of scratch, the static limit is %zu",
+                need, hattn::kStaticScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = hattn::static_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "sparse_attn_noalloc (scratch address)");
+  }
+  return hip_status(hattn::launch_attn(a, ws, (hipStream_t)stream), "sparse_attn_noalloc");
+}
+
 hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* n_vis,
                                            const void* raw_kv, int64_t L, const int32_t* q_pos, int32_t window,
                                            float scale, int64_t bt, int64_t nq, int32_t h, int32_t d, float* out,

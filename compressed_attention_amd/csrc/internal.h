@@ -108,6 +108,11 @@ struct AttnArgs {
 };
 
 size_t attn_ws_bytes(const AttnArgs& a);
+// The library's static device scratch (used in place of a workspace by the
+// no-allocation entry point): its size, and its address on the current
+// device (resolved on the first call per device).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+hipError_t static_scratch(void** ptr);
 hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st);
 // A sparse and a dense set (each with its own attn_ws_bytes workspace) in
 // shared launches; the same results as launch_attn on each.

@@ -242,6 +242,27 @@ def sparse_attn(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = N
     return (out, lse) if return_lse else out
 
 
+def sparse_attn_noalloc(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = None, out=None, lse=None):
+    """sparse_attn through the entry point that allocates nothing (the
+    library's static scratch instead of a workspace).  Pass out (and lse) to
+    keep the call free of allocations on the torch side too."""
+    dt, bt, nq, h, d = _attn_common(q, ckv, raw_kv, q_pos)
+    _need(idx, "idx", torch.int32, 3)
+    if idx.shape[:2] != (bt, nq):
+        raise ValueError("idx must be [bt][nq][k]")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((bt, nq, h, d), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, 4)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    check("hattn_sparse_attn_noalloc",
+          lib().hattn_sparse_attn_noalloc(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(idx), idx.shape[2], _ptr(raw_kv),
+                                          raw_kv.shape[1], _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out),
+                                          _ptr(lse), _stream(q.device)))
+    return out
+
+
 def dense_compressed_attn(q, ckv, n_vis, raw_kv, q_pos, window: int, scale: float | None = None,
                           return_lse: bool = False):
     """Attention over ckv[0 .. n_vis) plus the raw window: out [bt][nq][h][d] fp32."""

@@ -190,6 +190,26 @@ hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int6
                                  float* out, float* lse, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * hattn_sparse_attn_noalloc -- hattn_sparse_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, result and errors as
+ * hattn_sparse_attn, without a workspace: the split-K partials go to a
+ * static device array of the library (32 MiB on each GPU it runs on, held
+ * until the process ends).  The call allocates nothing.
+ *   - A shape whose partials need more than 32 MiB (the size query of
+ *     hattn_sparse_attn returns more than 33,554,432 bytes) gives
+ *     HATTN_ERR_WORKSPACE and launches nothing.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (different streams, or graphs replayed concurrently)
+ *     race on it and give undefined results.  Nothing needs clearing
+ *     between calls (every partial is written before it is read).
+ */
+hattn_status_t hattn_sparse_attn_noalloc(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx,
+                                         int32_t k, const void* raw_kv, int64_t L, const int32_t* q_pos,
+                                         int32_t window, float scale, int64_t bt, int64_t nq, int32_t h, int32_t d,
+                                         float* out, float* lse, void* stream);
+
+/*
  * hattn_dense_compressed_attn -- HCA attention: every visible entry plus window.
  * [HCA] sections 128 倍是什么概念 and 怎么压: no selection; each query attends
  * to all compressed entries it may see (ckv[0 .. n_vis[q]-1]) and to the

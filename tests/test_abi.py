@@ -158,3 +158,19 @@ def test_decode_plan_validation(L):
     d.ws, d.ws_bytes = p, 16  # too small: refused before any device work
     assert L.hattn_decode_plan_create(ctypes.byref(d), ctypes.byref(plan)) == 3
     assert L.hattn_decode_plan_destroy(None) == 0
+
+
+def test_sparse_attn_noalloc_rejects_oversize(L):
+    # 600 fp32 queries with 2,048 + 128 keys split in two chunks need
+    # 600 * 2 * 64 * 128 * 4 bytes (39.3 MB) of partials, more than the
+    # 32 MiB static scratch: refused before any launch.
+    f = L.hattn_sparse_attn_noalloc
+    p = ctypes.c_void_p(256)
+    st = f(0, p, p, 4000, p, 2048, p, 9000, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p, None, None)
+    assert st == 3, L.hattn_last_error()
+    assert b"static" in L.hattn_last_error()
+    # the same call with a workspace would need more than 32 MiB
+    sz = ctypes.c_size_t(0)
+    assert L.hattn_sparse_attn(0, p, p, 4000, p, 2048, p, 9000, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p,
+                               None, None, ctypes.byref(sz), None) == 0
+    assert sz.value > 32 << 20
