@@ -255,6 +255,16 @@ def hybrid_pair(args):
     ms = e0.elapsed_time(e1) / args.steps
     dist = step_distribution(replay, max(30, args.steps))
 
+    # The same plan steps replayed from one HIP graph holding one step per
+    # cache replica (a decode loop captured once): kernel boundaries inside a
+    # graph cost less than stream launches, and one replay enqueues R steps.
+    chain = capture_chain(lambda p_: p_.run(), plans)
+    reps_graph = max(1, args.steps // R)
+    graph_plan_ms = timed_graphs([chain], reps_graph, max(1, args.warmup // R)) / R
+    graph_dist = step_distribution(lambda i: chain.replay(), max(30, args.steps // R))
+    graph_dist = {kk: (v / R if kk != "n" else v) for kk, v in graph_dist.items()}
+    del chain
+
     # For comparison: the same step as two HIP graphs (one per branch) on two
     # streams joined every step; torch's graph replays and stream joins cost
     # more host time than the GPU needs for the step.
@@ -290,13 +300,16 @@ def hybrid_pair(args):
     win = 128
     kb = {
         "attn_pair_mfma": bt * (attn_bytes(Nh + win) + attn_bytes(k + win)),  # HCA dense + CSA sparse, one launch
+        "attn_pair_fused": bt * (attn_bytes(Nh + win) + attn_bytes(k + win)),  # the same, token select fused in
         "score_stage1_mfma": bt * hisa_stage1_bytes(nb),
         "score_stage2_mfma": bt * hisa_stage2_bytes(m * B),
+        "stage2_fused": bt * hisa_stage2_bytes(m * B),
     }
     step_bytes = sum(kb.values())
     flat_ms = flat_decode_step(args, t, caches, k) if args.flat_compare else None
     info = dict(ms=ms, graph_ms=graph_ms, kernels=kt, kernels_calls=kt_calls, kernel_bytes=kb, step_bytes=step_bytes,
-                bt=bt, N=N, Nh=Nh, k=k, L=L, dist=dist, flat_ms=flat_ms)
+                bt=bt, N=N, Nh=Nh, k=k, L=L, dist=dist, flat_ms=flat_ms, graph_plan_ms=graph_plan_ms,
+                graph_dist=graph_dist)
     for p_ in plans:
         p_.close()
     return info
@@ -596,10 +609,11 @@ def probe_indexer_128k(args):
     log("[probe] done")
 
 
-def load_traffic():
-    """Calibrated HBM bytes per launch of the dominant kernel, from the
-    committed counter summary; None when it is missing or was taken on other
-    attention sources than the ones here."""
+def load_traffic(kernel):
+    """Calibrated HBM bytes per launch of the dominant kernel (its timer
+    name), from the committed counter summary; None when it is missing,
+    covers another kernel, or was taken on other sources than the ones
+    here."""
     try:
         kv = {}
         with open(TRAFFIC_FILE) as fh:
@@ -607,7 +621,7 @@ def load_traffic():
                 if ":" in line and not line.startswith(("#", " ")):
                     a, b = line.split(":", 1)
                     kv[a.strip()] = b.strip()
-        if kv.get("sources_sha256_16") != attn_sources_sha():
+        if kv.get("sources_sha256_16") != attn_sources_sha() or kv.get("timer_name") != kernel:
             return None
         return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -717,7 +731,7 @@ def main():
     dom = max((kk for kk in kt if kk in res["kernel_bytes"]), key=lambda kk: kt[kk][0] * kt[kk][1])
     dom_ms = kt[dom][0]
     dom_bytes = res["kernel_bytes"].get(dom)
-    traffic = load_traffic() if dom == "attn_pair_mfma" else None
+    traffic = load_traffic(dom)
     roof = dict(bound="hbm", achieved=None, peak=HBM_PEAK_GBS, unit="GB/s", frac=None,
                 traffic=None if traffic is None else round(traffic), kernel=dom, kernel_us=dom_ms * 1e3)
     if dom_bytes:
@@ -741,6 +755,8 @@ def main():
                    "indexer": "16x128", "hisa_B": 128, "hisa_m": 64, "k": res["k"], "cache_replicas": args.replicas,
                    "launch": "native decode plan (one host call, 6 kernels per step)"},
         "step_us": {kk: round(v, 2) for kk, v in res["dist"].items() if kk != "n"} | {"n": res["dist"]["n"]},
+        "step_us_plan_graph": round(res["graph_plan_ms"] * 1e3, 2),
+        "step_us_plan_graph_dist": {kk: round(v, 2) for kk, v in res["graph_dist"].items()},
         "flat_indexer_step_us": None if res["flat_ms"] is None else round(res["flat_ms"] * 1e3, 1),
         "step_GBps": round(res["step_bytes"] / (ms * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(res["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
