@@ -31,6 +31,7 @@ from .hattn_ref import (  # noqa: F401
     flat_topk,
     hisa_pool,
     hisa_topk,
+    block_sparse_topk,
     window_rows,
     attend,
     sparse_attention,

@@ -220,6 +220,36 @@ def hisa_topk(q_i, k_i, w_i, n_vis, B: int, m: int, k: int, reps=None):
     return idx, blk
 
 
+def block_sparse_topk(q_i, k_i, w_i, n_vis, B: int, m: int, reps=None):
+    """Block-sparse (MoBA/NSA-style) selection, the baseline HISA is compared with.
+
+    [HISA] section 04: block-sparse methods choose at block granularity, and
+    every token of a chosen block takes part in attention (HISA's block level
+    is only a first filter before its token-level top-k).  Here the blocks are
+    chosen exactly as HISA's first stage chooses them (same representatives,
+    same block score, candidates are the blocks whose first entry is
+    visible, ties to the lower block), and the selection is every visible
+    entry of the m chosen blocks, so the attention budget is m*B entries.
+
+    Returns (idx [nq][m*B], blk [nq][m]), both ascending and -1 padded.
+    """
+    k_i = np.asarray(k_i, dtype=np.float64)
+    reps = hisa_pool(k_i, B) if reps is None else np.asarray(reps, dtype=np.float64)
+    nq = q_i.shape[0]
+    idx = np.full((nq, m * B), -1, dtype=np.int64)
+    blk = np.full((nq, m), -1, dtype=np.int64)
+    for q in range(nq):
+        n = int(n_vis[q])
+        nbq = -(-n // B)
+        r = index_scores(q_i[q], reps[:nbq], w_i[q])
+        chosen = topk_select(r, nbq, m)
+        blk[q] = chosen
+        chosen = chosen[chosen >= 0]
+        ent = [e for c in chosen for e in range(c * B, min(n, c * B + B))]
+        idx[q, : len(ent)] = ent
+    return idx, blk
+
+
 # ----------------------------------------------------------------------------
 # 5. Attention
 # ----------------------------------------------------------------------------

@@ -163,3 +163,72 @@ def test_hisa_brute_force_enumeration():
         cand = [i for b in chosen for i in range(b * B, min(n, b * B + B))]
         ts = sorted(cand, key=lambda i: (-score(k_i[i]), i))[:k]
         assert list(idx[q]) == sorted(ts) + [-1] * (k - len(ts))
+
+
+# ---- block-sparse (MoBA/NSA-style) baseline --------------------------------
+
+def _brute_block_sparse(q, k_i, w, n, B, m):
+    """Loops only: block sums, the block score with explicit head and channel
+    loops, blocks ranked with Python sorted, chosen blocks expanded."""
+    N, d = k_i.shape
+    nb = (N + B - 1) // B
+    cand = (n + B - 1) // B
+    score = []
+    for b in range(cand):
+        rep = [sum(k_i[i][c] for i in range(b * B, min(N, b * B + B))) / B for c in range(d)]
+        s = 0.0
+        for h in range(q.shape[0]):
+            dot = sum(q[h][c] * rep[c] for c in range(d))
+            s += w[h] * max(0.0, dot)
+        score.append(s)
+    chosen = sorted(sorted(range(cand), key=lambda b: (-score[b], b))[:m])
+    ent = [e for b in chosen for e in range(b * B, min(n, b * B + B))]
+    return ent + [-1] * (m * B - len(ent)), chosen + [-1] * (m - len(chosen))
+
+
+@pytest.mark.parametrize("trial", range(12))
+def test_block_sparse_brute_force(trial):
+    N = int(rng.integers(1, 70))
+    B = int(rng.choice([1, 2, 4, 8]))
+    m = int(rng.integers(1, 6))
+    nq, H, d = 3, 2, 3
+    q = rng.integers(-2, 3, (nq, H, d)).astype(float)
+    k_i = rng.integers(-2, 3, (N, d)).astype(float)  # ties among block scores
+    w = rng.integers(0, 4, (nq, H)).astype(float) / 4
+    n_vis = rng.integers(0, N + 1, nq)
+    idx, blk = oracle.block_sparse_topk(q, k_i, w, n_vis, B, m)
+    for j in range(nq):
+        r_idx, r_blk = _brute_block_sparse(q[j], k_i, w[j], int(n_vis[j]), B, m)
+        assert list(idx[j]) == r_idx, (trial, j)
+        assert list(blk[j]) == r_blk, (trial, j)
+
+
+def test_block_sparse_every_block_and_unit_blocks():
+    N, nq, H, d = 50, 4, 3, 5
+    q = rng.standard_normal((nq, H, d))
+    k_i = rng.standard_normal((N, d))
+    w = rng.uniform(0, 1, (nq, H))
+    n_vis = np.array([50, 37, 8, 1])
+    # m * B >= N: every visible entry, in order, whatever the scores
+    idx, _ = oracle.block_sparse_topk(q, k_i, w, n_vis, 8, 7)
+    for j, n in enumerate(n_vis):
+        assert list(idx[j][:n]) == list(range(n)) and (idx[j][n:] == -1).all()
+    # B = 1: each block is one entry, so the selection is the flat top-m
+    idx1, _ = oracle.block_sparse_topk(q, k_i, w, n_vis, 1, 9)
+    np.testing.assert_array_equal(idx1, oracle.flat_topk(q, k_i, w, n_vis, 9))
+
+
+def test_block_sparse_planted_block_and_whole_blocks():
+    # one block of large keys aligned with the query: chosen, and taken whole
+    N, B, d = 64, 8, 4
+    k_i = rng.standard_normal((N, d)) * 0.1
+    k_i[24:32] = 5.0
+    q = np.ones((1, 1, d))
+    idx, blk = oracle.block_sparse_topk(q, k_i, np.ones((1, 1)), np.array([N]), B, 1)
+    assert list(blk[0]) == [3]
+    assert list(idx[0]) == list(range(24, 32))
+    # unlike the token-level top-k, a chosen block keeps its weak entries
+    k_i[28] = -5.0
+    idx, _ = oracle.block_sparse_topk(q, k_i, np.ones((1, 1)), np.array([N]), B, 1)
+    assert 28 in idx[0]
+    assert 28 not in oracle.flat_topk(q, k_i, np.ones((1, 1)), np.array([N]), 8)[0]
