@@ -406,8 +406,13 @@ def indexer_128k(args):
         r = ops.hisa_pool(t["k_i"], B, out=reps)
         return ops.hisa_topk(t["q_i"], t["k_i"], t["w_i"], nv, r, B, m, k)
 
+    # block-sparse baseline at the same attention budget: k / B whole blocks
+    def block_sparse(_):
+        r = ops.hisa_pool(t["k_i"], B, out=reps)
+        return ops.block_sparse_topk(t["q_i"], t["k_i"], t["w_i"], nv, r, B, k // B)
+
     out = {}
-    for name, fn in (("flat", flat), ("hisa", hisa)):
+    for name, fn in (("flat", flat), ("hisa", hisa), ("block_sparse", block_sparse)):
         graphs = capture(fn, [None])
         ms = timed_graphs(graphs, max(5, args.steps // 5), 2)
         kt = kernel_times(fn, [None], max(5, args.steps // 5))
@@ -415,16 +420,20 @@ def indexer_128k(args):
         del graphs
     i_f = flat(None).cpu().numpy()[0]
     i_h = hisa(None).cpu().numpy()[0]
-    ious, rec_f, rec_h = [], [], []
+    i_b = block_sparse(None).cpu().numpy()[0]
+    ious, ious_b, rec_f, rec_h, rec_b = [], [], [], [], []
     needles = set(t["needles"].tolist())
     nvh = nv.cpu().numpy()[0]
     for q in range(nq):
         a, b = set(i_f[q][i_f[q] >= 0].tolist()), set(i_h[q][i_h[q] >= 0].tolist())
+        c = set(i_b[q][i_b[q] >= 0].tolist())
         ious.append(len(a & b) / max(1, len(a | b)))
+        ious_b.append(len(a & c) / max(1, len(a | c)))
         vis = {x for x in needles if x < nvh[q]}
         if vis:
             rec_f.append(len(vis & a) / len(vis))
             rec_h.append(len(vis & b) / len(vis))
+            rec_b.append(len(vis & c) / len(vis))
     flops = 2.0 * 16 * 128 * float(nvh.sum())
     # HISA's own work: every candidate block of each query (stage 1) and the
     # visible tokens of its m chosen blocks (stage 2, at most m * B)
@@ -433,6 +442,8 @@ def indexer_128k(args):
     out.update(hisa_flops=hisa_flops)
     out.update(iou_mean=float(sum(ious) / len(ious)), iou_min=float(min(ious)),
                needle_recall_flat=float(sum(rec_f) / len(rec_f)), needle_recall_hisa=float(sum(rec_h) / len(rec_h)),
+               iou_block_sparse=float(sum(ious_b) / len(ious_b)),
+               needle_recall_block_sparse=float(sum(rec_b) / len(rec_b)),
                flat_flops=flops)
     return out
 
@@ -718,6 +729,10 @@ def main():
             hisa_TFLOPs=ix["hisa_flops"] / (ix["hisa"]["ms"] * 1e-3) / 1e12,
             hisa_mfma_frac=ix["hisa_flops"] / (ix["hisa"]["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             hisa_vs_flat_iou_mean=ix["iou_mean"], hisa_vs_flat_iou_min=ix["iou_min"],
+            block_sparse_ms=ix["block_sparse"]["ms"], block_sparse_blocks=16,
+            block_sparse_vs_flat_iou_mean=ix["iou_block_sparse"],
+            needle_recall_block_sparse=ix["needle_recall_block_sparse"],
+            block_sparse_kernels_ms={kk: v[0] for kk, v in ix["block_sparse"]["kernels"].items()},
             needle_recall_flat=ix["needle_recall_flat"], needle_recall_hisa=ix["needle_recall_hisa"],
             flat_kernels_ms={kk: v[0] for kk, v in ix["flat"]["kernels"].items()},
             hisa_kernels_ms={kk: v[0] for kk, v in ix["hisa"]["kernels"].items()},

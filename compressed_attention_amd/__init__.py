@@ -9,6 +9,7 @@ from .ops import (  # noqa: F401
     compress,
     dense_compressed_attn,
     hisa_pool,
+    block_sparse_topk,
     hisa_topk,
     index_topk,
     sparse_attn,
@@ -23,6 +24,7 @@ __all__ = [
     "index_topk",
     "hisa_pool",
     "hisa_topk",
+    "block_sparse_topk",
     "sparse_attn",
     "dense_compressed_attn",
     "timer_enable",

@@ -19,6 +19,8 @@ SIGNATURES = {
     "hattn_hisa_pool": [_i32, _p, _i64, _i64, _i32, _i32, _i64, _i64, _p, _p],
     "hattn_hisa_topk": [_i32, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i32, _i32, _i32, _p, _p, _p, _psz,
                         _p],
+    "hattn_block_sparse_topk": [_i32, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i32, _i32, _p, _p, _p, _psz,
+                               _p],
     "hattn_sparse_attn": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p, _p,
                           _psz, _p],
     "hattn_sparse_attn_noalloc": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p,

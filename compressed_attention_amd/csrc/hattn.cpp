@@ -250,6 +250,23 @@ hattn_status_t hattn_hisa_topk(int dtype, const void* q_i, const void* k_i, cons
   return hip_status(hattn::launch_hisa_topk(a, reps, B, m, k, idx, blk, ws, (hipStream_t)stream), "hisa_topk");
 }
 
+hattn_status_t hattn_block_sparse_topk(int dtype, const void* q_i, const void* k_i, const float* w_i,
+                                      const int32_t* n_vis, int64_t bt, int64_t nq, int32_t h_i, int32_t d_i,
+                                      int64_t n, const float* reps, int32_t B, int32_t m, int32_t* idx, int32_t* blk,
+                                      void* ws, size_t* ws_bytes, void* stream) {
+  if (m < 1 || B < 1 || int64_t(m) * B > 16384)
+    return fail(HATTN_ERR_ARG, "block_sparse_topk: need B >= 1, m >= 1, m*B <= 16384");
+  // the selection length m*B plays the part of k in the shared checks
+  hattn_status_t st = hisa_check(dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n, reps, B, m, std::min(m * B, 8192),
+                                 idx, ws);
+  if (st != HATTN_OK) return st;
+  hattn::IndexArgs a{dtype, q_i, k_i, w_i, n_vis, bt, nq, h_i, d_i, n};
+  const size_t need = bt * nq > 0 ? hattn::block_sparse_ws_bytes(a, B, m) : 0;
+  if (ws_query(ws, ws_bytes, need, &st)) return st;
+  if (bt * nq == 0) return ok();
+  return hip_status(hattn::launch_block_sparse(a, reps, B, m, idx, blk, ws, (hipStream_t)stream), "block_sparse_topk");
+}
+
 static hattn_status_t attn_check(const char* fn, const hattn::AttnArgs& a, void* ws) {
   if (!dtype_ok(a.dtype)) return fail(HATTN_ERR_ARG, "%s: bad dtype %d", fn, a.dtype);
   if (a.bt < 0 || a.nq < 0 || a.n < 0 || a.L < 1 || a.window < 1)

@@ -1694,6 +1694,26 @@ __global__ __launch_bounds__(kCandNT) void flat_cand_select_kernel(const float* 
 }
 
 // ---------------------------------------------------------------------------
+// Block-sparse selection: every visible entry of each chosen block.  Slot
+// s * B + j of a row is entry blk[s] * B + j when the block exists and the
+// entry is visible, else -1.  Chosen blocks are ascending and only the last
+// of them can be partly visible (it holds the row's last visible entry), so
+// the list is ascending with the -1s at its end.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void expand_blocks_kernel(const int32_t* __restrict__ blk,
+                                                            const int32_t* __restrict__ n_vis, int64_t n, int B,
+                                                            int m, int32_t* __restrict__ idx) {
+  const int64_t row = blockIdx.y;
+  const int t = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (t >= m * B) return;
+  const int s = t / B, j = t - s * B;
+  const int bid = blk[row * m + s];
+  const int64_t nv = imin64(n, imax64(0, n_vis[row]));
+  const int64_t e = int64_t(bid) * B + j;
+  idx[row * int64_t(m) * B + t] = bid >= 0 && e < nv ? int32_t(e) : -1;
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -1996,6 +2016,11 @@ static bool stage1_mfma_dim(int d_i) {
 // scratch of its cache-maintenance roles: an entry role needs w softmax
 // weights plus 2,048 floats of row-group sums (256 threads x 8 bf16 each),
 // and the fresh block mean needs 2,048 floats of row-group sums too.
+size_t block_sparse_ws_bytes(const IndexArgs& a, int B, int m) {
+  const HisaPlan p = plan_hisa(a, B, m);
+  return p.s1_bytes + p.blk_bytes;
+}
+
 bool decode_front_ok(const IndexArgs& a, int B, int m, int max_w) {
   const int64_t tile = 64LL * (a.d_i + 4);
   return a.dtype == 1 && a.h_i == 16 && stage1_mfma_dim(a.d_i) && a.nq == 1 && !plan_hisa(a, B, m).bm &&
@@ -2030,21 +2055,17 @@ hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, vo
   return hipGetLastError();
 }
 
-hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m, int k, int32_t* idx, int32_t* blk,
-                            void* ws, hipStream_t st, bool stage1_done) {
-  set_lds_limits();
-  const HisaPlan p = plan_hisa(a, B, m);
-  char* base = reinterpret_cast<char*>(ws);
-  float* S1 = reinterpret_cast<float*>(base);
-  int32_t* blk_ws = reinterpret_cast<int32_t*>(base + p.s1_bytes);
-  float* S2 = reinterpret_cast<float*>(base + p.s1_bytes + p.blk_bytes);
-  int32_t* blk_out = blk ? blk : blk_ws;
-
+// HISA's first stage for every row of a call: block scores of the blocks
+// whose first entry is visible into S1 (row stride ld1), then the top-m
+// blocks of each row into blk_out (ascending, -1 padded).  bm_list: the
+// block-major stage 2's chooser lists (cleared here, filled by the block
+// selection), or nullptr.  stage1_done: S1 already holds the scores (the
+// decode front kernel wrote them).
+static hipError_t launch_hisa_blocks(const IndexArgs& a, const float* reps, int B, int m, const HisaPlan& p, float* S1,
+                                     int32_t* blk_out, int32_t* bm_list, bool stage1_done, hipStream_t st) {
   // Stage 1: block scores.
   const bool mfma1 = a.h_i == 16 && stage1_mfma_dim(a.d_i);
-  const bool bm = p.bm && mfma1;  // the stage-1 MFMA kernel clears the lists
-  int32_t* bm_list = bm ? reinterpret_cast<int32_t*>(base + p.s1_bytes + p.blk_bytes + p.s2_bytes) : nullptr;
-  const int64_t bm_fill = bm ? a.bt * p.nb * a.nq : 0;
+  const int64_t bm_fill = bm_list ? a.bt * p.nb * a.nq : 0;
   const bool x3 = mfma1 && a.dtype == 1 && a.nq >= 16 && (a.d_i == 32 || a.d_i == 64 || a.d_i == 128) &&
                   p.nb < (int64_t(1) << 31);
   if (stage1_done) {
@@ -2122,7 +2143,24 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
       HATTN_LAUNCH((select_rows_kernel<1, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S1, p.ld1,
                    a.n_vis, nullptr, a.n, B, m, m, blk_out, nullptr, bm_list, a.nq, p.nb);
   }
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m, int k, int32_t* idx, int32_t* blk,
+                            void* ws, hipStream_t st, bool stage1_done) {
+  set_lds_limits();
+  const HisaPlan p = plan_hisa(a, B, m);
+  char* base = reinterpret_cast<char*>(ws);
+  float* S1 = reinterpret_cast<float*>(base);
+  int32_t* blk_ws = reinterpret_cast<int32_t*>(base + p.s1_bytes);
+  float* S2 = reinterpret_cast<float*>(base + p.s1_bytes + p.blk_bytes);
+  int32_t* blk_out = blk ? blk : blk_ws;
+
+  // Stage 1: block scores and the top-m blocks.  (The block-major stage 2
+  // needs the stage-1 MFMA kernel, which clears its chooser lists.)
+  const bool bm = p.bm && a.h_i == 16 && stage1_mfma_dim(a.d_i);
+  int32_t* bm_list = bm ? reinterpret_cast<int32_t*>(base + p.s1_bytes + p.blk_bytes + p.s2_bytes) : nullptr;
+  hipError_t e = launch_hisa_blocks(a, reps, B, m, p, S1, blk_out, bm_list, stage1_done, st);
   if (e != hipSuccess) return e;
 
   // Stage 2: token scores inside the chosen blocks.
@@ -2179,6 +2217,20 @@ hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m,
       HATTN_LAUNCH((select_rows_kernel<3, kSelNT>), dim3(unsigned(p.rows)), dim3(kSelNT), 0, st, S2, p.ld2,
                    a.n_vis, blk_out, a.n, B, m, k, idx, nullptr, nullptr, int64_t(1), int64_t(1));
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_block_sparse(const IndexArgs& a, const float* reps, int B, int m, int32_t* idx, int32_t* blk,
+                               void* ws, hipStream_t st) {
+  const HisaPlan p = plan_hisa(a, B, m);
+  char* base = reinterpret_cast<char*>(ws);
+  float* S1 = reinterpret_cast<float*>(base);
+  int32_t* blk_out = blk ? blk : reinterpret_cast<int32_t*>(base + p.s1_bytes);
+  hipError_t e = launch_hisa_blocks(a, reps, B, m, p, S1, blk_out, nullptr, false, st);
+  if (e != hipSuccess) return e;
+  LaunchScope ls("expand_blocks", st);
+  HATTN_LAUNCH(expand_blocks_kernel, dim3(unsigned((int64_t(m) * B + 255) / 256), unsigned(p.rows)), dim3(256), 0,
+               st, blk_out, a.n_vis, a.n, B, m, idx);
   return hipGetLastError();
 }
 

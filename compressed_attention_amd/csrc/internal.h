@@ -72,6 +72,11 @@ size_t flat_topk_ws_bytes(const IndexArgs& a, int k);
 hipError_t launch_flat_topk(const IndexArgs& a, int k, int32_t* idx, float* score, void* ws, hipStream_t st);
 
 size_t hisa_topk_ws_bytes(const IndexArgs& a, int B, int m, int k);
+// Block-sparse baseline: HISA's first stage (top-m blocks) and every visible
+// entry of the chosen blocks as the selection, idx [rows][m*B].
+size_t block_sparse_ws_bytes(const IndexArgs& a, int B, int m);
+hipError_t launch_block_sparse(const IndexArgs& a, const float* reps, int B, int m, int32_t* idx, int32_t* blk,
+                               void* ws, hipStream_t st);
 hipError_t launch_hisa_topk(const IndexArgs& a, const float* reps, int B, int m, int k, int32_t* idx,
                             int32_t* blk, void* ws, hipStream_t st, bool stage1_done = false);
 // Decode front: HISA stage 1 for one query per sequence (into ws's S1, as

@@ -207,6 +207,26 @@ def hisa_topk(q_i, k_i, w_i, n_vis, reps, B: int, m: int, k: int, return_blocks:
     return (idx, blk) if return_blocks else idx
 
 
+def block_sparse_topk(q_i, k_i, w_i, n_vis, reps, B: int, m: int, return_blocks: bool = False):
+    """Block-sparse baseline: every visible entry of the top-m blocks (HISA's
+    block choice): idx [bt][nq][m*B] (and blocks [bt][nq][m])."""
+    dt, bt, nq, h_i, d_i, n = _index_common(q_i, k_i, w_i, n_vis)
+    _need(reps, "reps", torch.float32, 3)
+    if tuple(reps.shape) != (bt, -(-n // B), d_i):
+        raise ValueError("reps must be [bt][ceil(n/B)][d_i]")
+    idx = torch.empty((bt, nq, m * B), dtype=torch.int32, device=q_i.device)
+    blk = torch.empty((bt, nq, m), dtype=torch.int32, device=q_i.device) if return_blocks else None
+    L = lib()
+    st = _stream(q_i.device)
+
+    def call(ws, szp):
+        return L.hattn_block_sparse_topk(dt, _ptr(q_i), _ptr(k_i), _ptr(w_i), _ptr(n_vis), bt, nq, h_i, d_i, n,
+                                         _ptr(reps), B, m, _ptr(idx), _ptr(blk), ws, szp, st)
+
+    _ws_call("hattn_block_sparse_topk", ("hisa", q_i.device, st.value), q_i.device, call)
+    return (idx, blk) if return_blocks else idx
+
+
 def _attn_common(q, ckv, raw_kv, q_pos):
     _need(q, "q", ndim=4)
     dt = _fdt(q, "q")

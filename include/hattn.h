@@ -168,6 +168,24 @@ hattn_status_t hattn_hisa_topk(int dtype, const void* q_i, const void* k_i, cons
                                int32_t* idx, int32_t* blk, void* ws, size_t* ws_bytes, void* stream);
 
 /*
+ * hattn_block_sparse_topk -- block-sparse (MoBA/NSA-style) selection, the
+ * baseline HISA is compared with.
+ * [HISA] section 04: block-sparse methods select at block granularity and
+ * every token of a chosen block takes part in attention; HISA's block level
+ * is only a first filter.  The blocks are chosen exactly as
+ * hattn_hisa_topk's first stage chooses them (same block means and score;
+ * candidates are the blocks whose first entry is visible; ties to the lower
+ * block), and the selection is every visible entry of the m chosen blocks:
+ *   idx [bt][nq][m*B] int32 out, ascending, -1 padded (the attention budget
+ *   of m blocks is m*B entries);  blk [bt][nq][m] int32 out or NULL.
+ * Other arguments and limits as for hattn_hisa_topk (1 <= m, m*B <= 16384).
+ */
+hattn_status_t hattn_block_sparse_topk(int dtype, const void* q_i, const void* k_i, const float* w_i,
+                                       const int32_t* n_vis, int64_t bt, int64_t nq, int32_t h_i, int32_t d_i,
+                                       int64_t n, const float* reps, int32_t B, int32_t m, int32_t* idx,
+                                       int32_t* blk, void* ws, size_t* ws_bytes, void* stream);
+
+/*
  * hattn_sparse_attn -- CSA attention: selected entries plus sliding window.
  * [HYB] section Compressed Sparse Attention; [HCA] section 怎么压 (MQA: all
  * query heads share one K/V; a branch over the latest 128 raw tokens).

@@ -391,3 +391,53 @@ def test_hisa_indexer_widths_exact(dtype, d_i):
             ref, ref_blk = oracle.hisa_topk(q, kk, ww, nv[b].numpy(), B, m, k)
             assert np.array_equal(blk.cpu().numpy()[b], ref_blk), (d_i, bt, b)
             assert np.array_equal(idx.cpu().numpy()[b], ref), (d_i, bt, b)
+
+
+@pytest.mark.parametrize("dtype,d_i", [(torch.bfloat16, 64), (torch.bfloat16, 128), (torch.float32, 64),
+                                       (torch.bfloat16, 48)])
+def test_block_sparse_exact(dtype, d_i):
+    # Block-sparse baseline: HISA's block choice, then every visible entry of
+    # the chosen blocks.  Many queries and one query per sequence, ragged
+    # key count, mixed visibility (partly visible last blocks, fewer
+    # candidate blocks than m); integer grid, 4-bit weights (bound asserted).
+    N, B, m = 3001, 64, 6
+    for bt, nq in ((2, 40), (3, 1)):
+        q_i = synth.int_grid((bt, nq, 16, d_i), 501 + d_i, -4, 4, dtype=dtype)
+        k_i = synth.int_grid((bt, N, d_i), 502 + d_i, -4, 4, dtype=dtype)
+        w_i = synth.dyadic_uniform((bt, nq, 16), 503 + d_i, bits=4)
+        nv = synth.int_grid((bt, nq), 504 + d_i, 0, N, dtype=torch.int32)
+        nv[0, 0] = N
+        if nq > 1:
+            nv[0, 1:4] = torch.tensor([1, B + 3, 3 * B], dtype=torch.int32)
+        kd = k_i.to(DEV)
+        reps = ops.hisa_pool(kd, B)
+        idx, blk = ops.block_sparse_topk(q_i.to(DEV), kd, w_i.to(DEV), nv.to(DEV), reps, B, m, return_blocks=True)
+        torch.cuda.synchronize()
+        for b in range(bt):
+            q, kk, ww = f64(q_i[b]), f64(k_i[b]), f64(w_i[b])
+            _stage1_exact_bound(q, kk, ww, B, 4)
+            ref, ref_blk = oracle.block_sparse_topk(q, kk, ww, nv[b].numpy(), B, m)
+            assert np.array_equal(blk.cpu().numpy()[b], ref_blk), (d_i, bt, b)
+            assert np.array_equal(idx.cpu().numpy()[b], ref), (d_i, bt, b)
+
+
+def test_block_sparse_128k_exact_sampled_and_same_blocks_as_hisa():
+    # The 128K chunk at the attention budget of HISA's k = 2,048: 16 blocks
+    # of 128.  Exact against the oracle on sampled queries; the chosen blocks
+    # are those of HISA's first stage with m = 16.
+    w = synth.indexer_128k(0, integer_grid=True, weight_bits=4)
+    t = w.tensors
+    N, nq, B, m = 131072, 1024, 128, 16
+    nv = _nvis_entry_space(nq, N)
+    k_i = t["k_i"].to(DEV)
+    reps = ops.hisa_pool(k_i, B)
+    idx, blk = ops.block_sparse_topk(t["q_i"].to(DEV), k_i, t["w_i"].to(DEV), nv, reps, B, m, return_blocks=True)
+    _, hblk = ops.hisa_topk(t["q_i"].to(DEV), k_i, t["w_i"].to(DEV), nv, reps, B, m, 2048, return_blocks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(blk, hblk)
+    rows = _rows(nq, 8)
+    q, kk, ww = f64(t["q_i"][0]), f64(t["k_i"][0]), f64(t["w_i"][0])
+    _stage1_exact_bound(q[rows], kk, ww, B, 4)
+    ref, ref_blk = oracle.block_sparse_topk(q[rows], kk, ww[rows], nv.cpu().numpy()[0][rows], B, m)
+    assert np.array_equal(blk.cpu().numpy()[0, rows], ref_blk)
+    assert np.array_equal(idx.cpu().numpy()[0, rows], ref)
