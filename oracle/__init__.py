@@ -26,6 +26,8 @@ from .hattn_ref import (  # noqa: F401
     entry_span,
     n_visible,
     compress,
+    compress_channel_logits,
+    compress_with_index,
     index_scores,
     topk_select,
     flat_topk,

@@ -102,6 +102,54 @@ def compress(x: np.ndarray, z: np.ndarray | None, b: np.ndarray | None, w: int, 
     return y
 
 
+def compress_channel_logits(x: np.ndarray, Z: np.ndarray, b: np.ndarray | None, w: int, s: int) -> np.ndarray:
+    """Compression with one logit per raw token and channel.
+
+    The variant of ``compress`` in which the compression weight is computed
+    per channel ([HCA] section 怎么压 computes a compression weight for each
+    raw entry and merges each window with a softmax over weight + position
+    bias; here that weight is a vector, one value per channel):
+
+        a_ijc  = Z[i*s + j][c] + b[j]
+        alpha  = softmax over j of a_i.c           (separately for each c)
+        y_ic   = sum_j alpha_ijc * x[i*s + j][c]
+
+    x [L][C], Z [L][C] -> y [N][C].  b=None means zero bias.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    Z = np.asarray(Z, dtype=np.float64)
+    L, C = x.shape
+    assert Z.shape == (L, C)
+    b = np.zeros(w) if b is None else np.asarray(b, dtype=np.float64)
+    N = n_entries(L, w, s)
+    y = np.empty((N, C), dtype=np.float64)
+    group = max(1, (1 << 22) // max(1, w * C))
+    offs = np.arange(w)
+    for e0 in range(0, N, group):
+        e1 = min(N, e0 + group)
+        tok = (np.arange(e0, e1) * s)[:, None] + offs[None, :]  # [g][w]
+        a = Z[tok] + b[None, :, None]  # [g][w][C]
+        a = a - a.max(axis=1, keepdims=True)
+        alpha = np.exp(a)
+        alpha /= alpha.sum(axis=1, keepdims=True)
+        y[e0:e1] = (alpha * x[tok]).sum(axis=1)
+    return y
+
+
+def compress_with_index(x, x_i, z, b, w: int, s: int):
+    """Compressed K|V entries and the indexer keys of the same entries.
+
+    The indexer keys K_I are not an independent input here: each entry's
+    indexer key is the merge of the raw indexer keys of its window with the
+    entry's own softmax weights ([TRDM] section 2.1: the indexer picks the
+    most important compressed KV blocks, so it scores the entries that
+    ``compress`` builds; [HCA] section 怎么压 for the weights).  x [L][C] K|V
+    rows, x_i [L][d_I] raw indexer keys, per-token logits z [L].
+    Returns (ckv [N][C], k_i [N][d_I]).
+    """
+    return compress(x, z, b, w, s), compress(x_i, z, b, w, s)
+
+
 # ----------------------------------------------------------------------------
 # 3. Lightning-indexer score and top-k
 # ----------------------------------------------------------------------------
