@@ -7,6 +7,8 @@ use; without it every op raises (there is no CPU fallback).
 """
 from .ops import (  # noqa: F401
     compress,
+    compress_channel_logits,
+    compress_with_index,
     dense_compressed_attn,
     hisa_pool,
     block_sparse_topk,
@@ -20,6 +22,8 @@ from .ops import (  # noqa: F401
 
 __all__ = [
     "compress",
+    "compress_with_index",
+    "compress_channel_logits",
     "visible_count",
     "index_topk",
     "hisa_pool",

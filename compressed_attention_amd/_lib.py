@@ -14,6 +14,8 @@ _psz = ctypes.POINTER(ctypes.c_size_t)
 # name -> argument types, in the order of include/hattn.h
 SIGNATURES = {
     "hattn_compress": [_i32, _p, _i64, _i64, _i32, _p, _p, _i32, _i32, _i64, _i64, _p, _p],
+    "hattn_compress_with_index": [_i32, _p, _p, _i64, _i64, _i32, _i32, _p, _p, _i32, _i32, _i64, _i64, _p, _p, _p],
+    "hattn_compress_channel_logits": [_i32, _p, _i64, _i64, _i32, _p, _p, _i32, _i32, _i64, _i64, _p, _p],
     "hattn_visible_count": [_p, _i64, _i32, _i32, _i64, _p, _p],
     "hattn_index_topk": [_i32, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _i32, _p, _p, _p, _psz, _p],
     "hattn_hisa_pool": [_i32, _p, _i64, _i64, _i32, _i32, _i64, _i64, _p, _p],

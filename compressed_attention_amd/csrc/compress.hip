@@ -18,21 +18,54 @@
 namespace hattn {
 
 // Generic window: any w, s.  Thread = (sequence, run of entries, 16-byte slot).
+// A second tensor compressed with the same weights as the first (the
+// indexer keys of the entries, [bt][L][C2] -> [bt][N][C2]), or none (x2 ==
+// nullptr, C2 == 0).  The kernels treat [x | x2] as one row of C + C2
+// channels: a 16-byte slot past x's C channels belongs to x2.
+template <typename T>
+struct Second {
+  const T* x2;
+  T* y2;
+  int C2;
+};
+
+// Source and destination of 16-byte slot cs of the virtual row, for
+// sequence b: raw row 0 and entry 0 of that slot, and the row stride.
+template <typename T>
+HATTN_DEV void slot_of(const T* x, T* y, int C, const Second<T>& sec, int64_t b, int64_t L, int64_t N, int cs,
+                       const T** xs, T** ys, int* ld) {
+  constexpr int V = Vec16<T>::N;
+  const int s1 = C / V;
+  if (cs < s1) {
+    *xs = x + b * L * C + cs * V;
+    *ys = y + b * N * C + cs * V;
+    *ld = C;
+  } else {
+    *xs = sec.x2 + b * L * sec.C2 + (cs - s1) * V;
+    *ys = sec.y2 + b * N * sec.C2 + (cs - s1) * V;
+    *ld = sec.C2;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void compress_generic_kernel(const T* __restrict__ x, const float* __restrict__ z,
                                                                const float* __restrict__ bias, T* __restrict__ y,
                                                                int64_t L, int C, int w, int s, int64_t N, int64_t e0,
-                                                               int64_t runs_per_seq, int run, int64_t total) {
+                                                               int64_t runs_per_seq, int run, int64_t total,
+                                                               Second<T> sec) {
   constexpr int V = Vec16<T>::N;
   const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (t >= total) return;
-  const int slots = C / V;
+  const int slots = (C + sec.C2) / V;
   const int cs = int(t % slots);
   const int64_t rest = t / slots;
   const int64_t b = rest / runs_per_seq;
   const int64_t r = rest % runs_per_seq;
   const int64_t ebeg = e0 + r * run;
-  const T* xb = x + b * L * C + cs * V;
+  const T* xb;
+  T* yb;
+  int ldc;
+  slot_of(x, y, C, sec, b, L, N, cs, &xb, &yb, &ldc);
   const float* zb = z ? z + b * L : nullptr;
   for (int j = 0; j < run; ++j) {
     const int64_t e = ebeg + j;
@@ -52,14 +85,14 @@ __global__ __launch_bounds__(256) void compress_generic_kernel(const T* __restri
       const float p = __expf(a - mx);
       den += p;
       float f[V];
-      Vec16<T>::unpack(ld16_nt(xb + (t0 + u) * C), f);
+      Vec16<T>::unpack(ld16_nt(xb + (t0 + u) * ldc), f);
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] = fmaf(p, f[i], acc[i]);
     }
     const float inv = 1.f / den;
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] *= inv;
-    st16(y + (b * N + e) * C + cs * V, Vec16<T>::pack(acc));
+    st16(yb + e * ldc, Vec16<T>::pack(acc));
   }
 }
 
@@ -70,12 +103,13 @@ template <typename T, int S>
 __global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restrict__ x, const float* __restrict__ z,
                                                                 const float* __restrict__ bias, T* __restrict__ y,
                                                                 int64_t L, int C, int64_t N, int64_t e0, int64_t e1,
-                                                                int64_t runs_per_seq, int run, int64_t total) {
+                                                                int64_t runs_per_seq, int run, int64_t total,
+                                                                Second<T> sec) {
   constexpr int V = Vec16<T>::N;
   constexpr int W = 2 * S;
   const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (t >= total) return;
-  const int slots = C / V;
+  const int slots = (C + sec.C2) / V;
   const int cs = int(t % slots);
   const int64_t rest = t / slots;
   const int64_t b = rest / runs_per_seq;
@@ -83,7 +117,10 @@ __global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restr
   const int64_t ebeg = e0 + r * run;
   const int64_t eend = imin64(e1, ebeg + run);
   if (ebeg >= eend) return;
-  const T* xb = x + b * L * C + cs * V;
+  const T* xb;
+  T* yb;
+  int ldc;
+  slot_of(x, y, C, sec, b, L, N, cs, &xb, &yb, &ldc);
   const float* zb = z ? z + b * L : nullptr;
   float bs[W];
 #pragma unroll
@@ -94,7 +131,7 @@ __global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restr
   float zprev[S];
 #pragma unroll
   for (int u = 0; u < S; ++u) {
-    Vec16<T>::unpack(ld16_nt(xb + (ebeg * S + u) * C), prev[u]);
+    Vec16<T>::unpack(ld16_nt(xb + (ebeg * S + u) * ldc), prev[u]);
     zprev[u] = zb ? zb[ebeg * S + u] : 0.f;
   }
   for (int64_t e = ebeg; e < eend; ++e) {
@@ -103,7 +140,7 @@ __global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restr
     const int64_t t1 = e * S + S;
 #pragma unroll
     for (int u = 0; u < S; ++u) {
-      Vec16<T>::unpack(ld16_nt(xb + (t1 + u) * C), cur[u]);
+      Vec16<T>::unpack(ld16_nt(xb + (t1 + u) * ldc), cur[u]);
       zcur[u] = zb ? zb[t1 + u] : 0.f;
     }
     float a[W];
@@ -130,7 +167,7 @@ __global__ __launch_bounds__(256) void compress_overlap2_kernel(const T* __restr
     const float inv = 1.f / den;
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] *= inv;
-    st16(y + (b * N + e) * C + cs * V, Vec16<T>::pack(acc));
+    st16(yb + e * ldc, Vec16<T>::pack(acc));
 #pragma unroll
     for (int u = 0; u < S; ++u) {
       zprev[u] = zcur[u];
@@ -149,14 +186,15 @@ template <typename T>
 __global__ __launch_bounds__(256) void compress_window_kernel(const T* __restrict__ x, const float* __restrict__ z,
                                                               const float* __restrict__ bias, T* __restrict__ y,
                                                               int64_t L, int C, int w, int s, int64_t N, int64_t e0,
-                                                              int64_t ne) {
+                                                              int64_t ne, Second<T> sec) {
   constexpr int V = Vec16<T>::N;
-  extern __shared__ float wsm[];  // [w] weights, then [RG][C] partial sums
+  extern __shared__ float wsm[];  // [w] weights, then [RG][C + C2] partial sums
   __shared__ float red[8];
   const int64_t e = e0 + blockIdx.x % ne;
   const int64_t b = blockIdx.x / ne;
   const int64_t t0 = e * s;
-  const int slots = C / V;
+  const int CT = C + sec.C2;  // channels of the virtual row
+  const int slots = CT / V;
   const int RG = 256 / slots;
   const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
   float mx = -INFINITY;
@@ -183,13 +221,17 @@ __global__ __launch_bounds__(256) void compress_window_kernel(const T* __restric
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  const T* xb = x + (b * L + t0) * C + cs * V;
+  const T* xs;
+  T* ys;
+  int ldc;
+  slot_of(x, y, C, sec, b, L, N, cs, &xs, &ys, &ldc);
+  const T* xb = xs + t0 * ldc;
   if (rg < RG) {
     int u = rg;
     for (; u + 3 * RG < w; u += 4 * RG) {
       u32x4_t v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = ld16_nt(xb + int64_t(u + j * RG) * C);
+      for (int j = 0; j < 4; ++j) v[j] = ld16_nt(xb + int64_t(u + j * RG) * ldc);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float f[V];
@@ -201,37 +243,43 @@ __global__ __launch_bounds__(256) void compress_window_kernel(const T* __restric
     }
     for (; u < w; u += RG) {
       float f[V];
-      Vec16<T>::unpack(ld16_nt(xb + int64_t(u) * C), f);
+      Vec16<T>::unpack(ld16_nt(xb + int64_t(u) * ldc), f);
       const float p = wsm[u];
 #pragma unroll
       for (int i = 0; i < V; ++i) acc[i] = fmaf(p, f[i], acc[i]);
     }
   }
-  float* part = wsm + w;  // [RG][C]
+  float* part = wsm + w;  // [RG][CT]
   if (rg < RG) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) part[rg * C + cs * V + i] = acc[i];
+    for (int i = 0; i < V; ++i) part[rg * CT + cs * V + i] = acc[i];
   }
   __syncthreads();
   const float inv = 1.f / den;
-  for (int c = threadIdx.x; c < C / V; c += 256) {
+  for (int c = threadIdx.x; c < slots; c += 256) {
     float r[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) r[i] = 0.f;
     for (int g2 = 0; g2 < RG; ++g2)
 #pragma unroll
-      for (int i = 0; i < V; ++i) r[i] += part[g2 * C + c * V + i];
+      for (int i = 0; i < V; ++i) r[i] += part[g2 * CT + c * V + i];
 #pragma unroll
     for (int i = 0; i < V; ++i) r[i] *= inv;
-    st16(y + (b * N + e) * C + c * V, Vec16<T>::pack(r));
+    const T* xo;
+    T* yo;
+    int ldo;
+    slot_of(x, y, C, sec, b, L, N, c, &xo, &yo, &ldo);
+    st16(yo + e * ldo, Vec16<T>::pack(r));
   }
 }
 
 template <typename T>
 static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
-                                    int w, int s, int64_t N, int64_t e0, int64_t e1, void* y, hipStream_t st) {
+                                    int w, int s, int64_t N, int64_t e0, int64_t e1, void* y, hipStream_t st,
+                                    const void* x2 = nullptr, void* y2 = nullptr, int C2 = 0) {
   constexpr int V = Vec16<T>::N;
-  const int slots = C / V;
+  const Second<T> sec{(const T*)x2, (T*)y2, x2 ? C2 : 0};
+  const int slots = (C + sec.C2) / V;
   const int64_t ne = e1 - e0;
   if (ne <= 0 || bt <= 0) return hipSuccess;
   if (w == 2 * s && s == 4) {
@@ -242,15 +290,15 @@ static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C,
     const int64_t total = bt * runs * slots;
     LaunchScope ls("compress_overlap2", st);
     HATTN_LAUNCH((compress_overlap2_kernel<T, 4>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
-                       (const T*)x, z, bias, (T*)y, L, C, N, e0, e1, runs, run, total);
+                       (const T*)x, z, bias, (T*)y, L, C, N, e0, e1, runs, run, total, sec);
     return hipGetLastError();
   }
   if (w >= 32 && slots <= 256) {
     const int RG = 256 / slots;
-    const size_t smem = (size_t(w) + size_t(RG) * C) * 4;
+    const size_t smem = (size_t(w) + size_t(RG) * (C + sec.C2)) * 4;
     LaunchScope ls("compress_window", st);
     HATTN_LAUNCH((compress_window_kernel<T>), dim3(unsigned(bt * ne)), dim3(256), smem, st, (const T*)x, z, bias,
-                       (T*)y, L, C, w, s, N, e0, ne);
+                       (T*)y, L, C, w, s, N, e0, ne, sec);
     return hipGetLastError();
   }
   const int run = 1;
@@ -258,15 +306,86 @@ static hipError_t launch_compress_t(const void* x, int64_t bt, int64_t L, int C,
   const int64_t total = bt * runs * slots;
   LaunchScope ls("compress", st);
   HATTN_LAUNCH((compress_generic_kernel<T>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
-                     (const T*)x, z, bias, (T*)y, L, C, w, s, N, e0, runs, run, total);
+                     (const T*)x, z, bias, (T*)y, L, C, w, s, N, e0, runs, run, total, sec);
   return hipGetLastError();
 }
 
 hipError_t launch_compress(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z,
                            const float* bias, int w, int s, int64_t N, int64_t e0, int64_t e1, void* y,
-                           hipStream_t st) {
-  if (dtype == 0) return launch_compress_t<float>(x, bt, L, C, z, bias, w, s, N, e0, e1, y, st);
-  return launch_compress_t<uint16_t>(x, bt, L, C, z, bias, w, s, N, e0, e1, y, st);
+                           hipStream_t st, const void* x2, void* y2, int C2) {
+  if (dtype == 0) return launch_compress_t<float>(x, bt, L, C, z, bias, w, s, N, e0, e1, y, st, x2, y2, C2);
+  return launch_compress_t<uint16_t>(x, bt, L, C, z, bias, w, s, N, e0, e1, y, st, x2, y2, C2);
+}
+
+// ---------------------------------------------------------------------------
+// Compression with one logit per raw token and channel: each channel has its
+// own softmax over the window.  Thread = (sequence, entry, 16-byte slot);
+// one pass over the window rows with an online softmax per channel (the
+// running maximum and sum are rescaled when the maximum grows).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void compress_channel_kernel(const T* __restrict__ x, const float* __restrict__ Z,
+                                                               const float* __restrict__ bias, T* __restrict__ y,
+                                                               int64_t L, int C, int w, int s, int64_t N, int64_t e0,
+                                                               int64_t ne, int64_t total) {
+  constexpr int V = Vec16<T>::N;
+  const int64_t t = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  const int slots = C / V;
+  const int cs = int(t % slots);
+  const int64_t rest = t / slots;
+  const int64_t b = rest / ne;
+  const int64_t e = e0 + rest % ne;
+  const int64_t t0 = e * s;
+  const T* xb = x + (b * L + t0) * C + cs * V;
+  const float* zb = Z + (b * L + t0) * C + cs * V;
+  float mx[V], den[V], acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    mx[i] = -INFINITY;
+    den[i] = 0.f;
+    acc[i] = 0.f;
+  }
+  for (int u = 0; u < w; ++u) {
+    float f[V], a[V];
+    Vec16<T>::unpack(ld16_nt(xb + int64_t(u) * C), f);
+    const float bu = bias ? bias[u] : 0.f;
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      const f32x4_t zz = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(zb + int64_t(u) * C + 4 * q));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[4 * q + i] = zz[i] + bu;
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const float m_new = fmaxf(mx[i], a[i]);
+      const float sc = __expf(mx[i] - m_new);  // 0 on the first row (mx = -inf)
+      const float p = __expf(a[i] - m_new);
+      den[i] = fmaf(den[i], sc, p);
+      acc[i] = fmaf(acc[i], sc, p * f[i]);
+      mx[i] = m_new;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] /= den[i];
+  st16(y + (b * N + e) * C + cs * V, Vec16<T>::pack(acc));
+}
+
+hipError_t launch_compress_channel(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* Z,
+                                   const float* bias, int w, int s, int64_t N, int64_t e0, int64_t e1, void* y,
+                                   hipStream_t st) {
+  const int V = dtype == 0 ? 4 : 8;
+  const int64_t ne = e1 - e0;
+  if (ne <= 0 || bt <= 0) return hipSuccess;
+  const int64_t total = bt * ne * (C / V);
+  LaunchScope ls("compress_channel", st);
+  if (dtype == 0)
+    HATTN_LAUNCH(compress_channel_kernel<float>, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                 (const float*)x, Z, bias, (float*)y, L, C, w, s, N, e0, ne, total);
+  else
+    HATTN_LAUNCH(compress_channel_kernel<uint16_t>, dim3(unsigned((total + 255) / 256)), dim3(256), 0, st,
+                 (const uint16_t*)x, Z, bias, (uint16_t*)y, L, C, w, s, N, e0, ne, total);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -171,6 +171,52 @@ hattn_status_t hattn_compress(int dtype, const void* x, int64_t bt, int64_t L, i
                     "compress");
 }
 
+hattn_status_t hattn_compress_with_index(int dtype, const void* x, const void* x_i, int64_t bt, int64_t L, int32_t C,
+                                        int32_t C_i, const float* logits, const float* pos_bias, int32_t w,
+                                        int32_t stride, int64_t e_begin, int64_t e_end, void* y, void* y_i,
+                                        void* stream) {
+  if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "compress_with_index: bad dtype %d", dtype);
+  if (bt < 0 || L < 0) return fail(HATTN_ERR_ARG, "compress_with_index: negative size");
+  if (w < 1 || w > 4096 || stride < 1)
+    return fail(HATTN_ERR_ARG, "compress_with_index: need 1 <= w <= 4096 and stride >= 1");
+  const int vec = 16 / elem_bytes(dtype);
+  if (C <= 0 || C % vec || C_i <= 0 || C_i % vec)
+    return fail(HATTN_ERR_ARG, "compress_with_index: C=%d and C_i=%d must be positive multiples of %d", C, C_i, vec);
+  if (L < w) return fail(HATTN_ERR_ARG, "compress_with_index: L=%lld shorter than the window %d", (long long)L, w);
+  const int64_t N = (L - w) / stride + 1;
+  if (e_begin < 0 || e_end < e_begin || e_end > N)
+    return fail(HATTN_ERR_ARG, "compress_with_index: entry range [%lld, %lld) outside [0, %lld]", (long long)e_begin,
+                (long long)e_end, (long long)N);
+  if (bt == 0 || e_end == e_begin) return ok();
+  if (!x || !y || !x_i || !y_i) return fail(HATTN_ERR_ARG, "compress_with_index: NULL x, x_i, y or y_i");
+  HATTN_REQUIRE_ALIGNED("compress_with_index", x, y, x_i, y_i);
+  return hip_status(hattn::launch_compress(dtype, x, bt, L, C, logits, pos_bias, w, stride, N, e_begin, e_end, y,
+                                           (hipStream_t)stream, x_i, y_i, C_i),
+                    "compress_with_index");
+}
+
+hattn_status_t hattn_compress_channel_logits(int dtype, const void* x, int64_t bt, int64_t L, int32_t C,
+                                            const float* logits, const float* pos_bias, int32_t w, int32_t stride,
+                                            int64_t e_begin, int64_t e_end, void* y, void* stream) {
+  if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "compress_channel_logits: bad dtype %d", dtype);
+  if (bt < 0 || L < 0) return fail(HATTN_ERR_ARG, "compress_channel_logits: negative size");
+  if (w < 1 || w > 4096 || stride < 1)
+    return fail(HATTN_ERR_ARG, "compress_channel_logits: need 1 <= w <= 4096 and stride >= 1");
+  const int vec = 16 / elem_bytes(dtype);
+  if (C <= 0 || C % vec)
+    return fail(HATTN_ERR_ARG, "compress_channel_logits: C=%d must be a positive multiple of %d", C, vec);
+  if (L < w) return fail(HATTN_ERR_ARG, "compress_channel_logits: L=%lld shorter than the window %d", (long long)L, w);
+  const int64_t N = (L - w) / stride + 1;
+  if (e_begin < 0 || e_end < e_begin || e_end > N)
+    return fail(HATTN_ERR_ARG, "compress_channel_logits: entry range outside [0, %lld]", (long long)N);
+  if (bt == 0 || e_end == e_begin) return ok();
+  if (!x || !y || !logits) return fail(HATTN_ERR_ARG, "compress_channel_logits: NULL x, logits or y");
+  HATTN_REQUIRE_ALIGNED("compress_channel_logits", x, y, logits);
+  return hip_status(hattn::launch_compress_channel(dtype, x, bt, L, C, logits, pos_bias, w, stride, N, e_begin,
+                                                   e_end, y, (hipStream_t)stream),
+                    "compress_channel_logits");
+}
+
 hattn_status_t hattn_visible_count(const int32_t* pos, int64_t count, int32_t w, int32_t stride, int64_t n_entries,
                                    int32_t* n_vis, void* stream) {
   if (count < 0 || w < 1 || stride < 1 || n_entries < 0 || n_entries > INT32_MAX)

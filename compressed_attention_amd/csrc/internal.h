@@ -37,9 +37,15 @@ bool timer_events(hipEvent_t* e0, hipEvent_t* e1);
   } while (0)
 
 // ---- compression / geometry / pooling -------------------------------------
+// With x2 (indexer keys [bt][L][C2]) the same weights also compress x2 into
+// y2 [bt][N][C2].
 hipError_t launch_compress(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z,
                            const float* bias, int w, int s, int64_t N, int64_t e0, int64_t e1, void* y,
-                           hipStream_t st);
+                           hipStream_t st, const void* x2 = nullptr, void* y2 = nullptr, int C2 = 0);
+// Per-channel logits Z [bt][L][C] fp32.
+hipError_t launch_compress_channel(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* Z,
+                                   const float* bias, int w, int s, int64_t N, int64_t e0, int64_t e1, void* y,
+                                   hipStream_t st);
 hipError_t launch_visible_count(const int32_t* pos, int64_t count, int w, int s, int64_t n_entries,
                                 int32_t* n_vis, hipStream_t st);
 hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_i, int B, int64_t j0,

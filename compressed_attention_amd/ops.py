@@ -98,6 +98,58 @@ def compress(x, logits, pos_bias, w: int, stride: int, e_begin: int = 0, e_end: 
     return out
 
 
+def compress_with_index(x, x_i, logits, pos_bias, w: int, stride: int, e_begin: int = 0, e_end: int | None = None,
+                        out=None, out_i=None):
+    """Compressed K|V entries and their indexer keys, both merged with each
+    entry's own softmax weights: x [bt][L][C], x_i [bt][L][C_i] ->
+    ([bt][N][C], [bt][N][C_i])."""
+    _need(x, "x", ndim=3)
+    dt = _fdt(x, "x")
+    _need(x_i, "x_i", x.dtype, 3)
+    bt, L, C = x.shape
+    if tuple(x_i.shape[:2]) != (bt, L):
+        raise ValueError("x_i must be [bt][L][C_i]")
+    C_i = x_i.shape[2]
+    N = (L - w) // stride + 1 if L >= w else 0
+    if logits is not None:
+        _need(logits, "logits", torch.float32, 2)
+    if pos_bias is not None:
+        _need(pos_bias, "pos_bias", torch.float32, 1)
+    if e_end is None:
+        e_end = N
+    out = torch.empty((bt, N, C), dtype=x.dtype, device=x.device) if out is None else out
+    out_i = torch.empty((bt, N, C_i), dtype=x.dtype, device=x.device) if out_i is None else out_i
+    _need(out, "out", x.dtype, 3)
+    _need(out_i, "out_i", x.dtype, 3)
+    check("hattn_compress_with_index",
+          lib().hattn_compress_with_index(dt, _ptr(x), _ptr(x_i), bt, L, C, C_i, _ptr(logits), _ptr(pos_bias), w,
+                                          stride, e_begin, e_end, _ptr(out), _ptr(out_i), _stream(x.device)))
+    return out, out_i
+
+
+def compress_channel_logits(x, logits, pos_bias, w: int, stride: int, e_begin: int = 0, e_end: int | None = None,
+                            out=None):
+    """Compression with one logit per raw token and channel: x [bt][L][C],
+    logits [bt][L][C] fp32 -> [bt][N][C]."""
+    _need(x, "x", ndim=3)
+    dt = _fdt(x, "x")
+    bt, L, C = x.shape
+    _need(logits, "logits", torch.float32, 3)
+    if tuple(logits.shape) != (bt, L, C):
+        raise ValueError("logits must be [bt][L][C]")
+    if pos_bias is not None:
+        _need(pos_bias, "pos_bias", torch.float32, 1)
+    N = (L - w) // stride + 1 if L >= w else 0
+    if e_end is None:
+        e_end = N
+    out = torch.empty((bt, N, C), dtype=x.dtype, device=x.device) if out is None else out
+    _need(out, "out", x.dtype, 3)
+    check("hattn_compress_channel_logits",
+          lib().hattn_compress_channel_logits(dt, _ptr(x), bt, L, C, _ptr(logits), _ptr(pos_bias), w, stride, e_begin,
+                                              e_end, _ptr(out), _stream(x.device)))
+    return out
+
+
 def visible_count(pos, w: int, stride: int, n_entries: int, out=None):
     """Entries visible at each raw position: int32 tensor shaped like pos."""
     _need(pos, "pos", torch.int32)

@@ -96,6 +96,39 @@ hattn_status_t hattn_compress(int dtype, const void* x, int64_t bt, int64_t L, i
                               int64_t e_begin, int64_t e_end, void* y, void* stream);
 
 /*
+ * hattn_compress_with_index -- compressed K|V entries and their indexer keys.
+ * [TRDM] section 2.1 (the indexer picks the most important compressed KV
+ * blocks: it scores the entries this call builds) and [HCA] section 怎么压
+ * (the softmax(logit + position bias) merge): each entry's indexer key is
+ * the merge of the raw indexer keys of its window with the entry's own
+ * weights, the ones that merge its K|V rows:
+ *   y[b][i]   = sum_j softmax(a)_j * x[b][i*stride + j]       (as hattn_compress)
+ *   y_i[b][i] = sum_j softmax(a)_j * x_i[b][i*stride + j]     (same a)
+ *   x   [bt][L][C]   dtype     x_i [bt][L][C_i] dtype (raw indexer keys)
+ *   y   [bt][N][C]   dtype     y_i [bt][N][C_i] dtype (the entries' K_I)
+ * Other arguments and limits as for hattn_compress (C_i a multiple of 16
+ * bytes' worth of elements).  One pass computes both outputs.
+ */
+hattn_status_t hattn_compress_with_index(int dtype, const void* x, const void* x_i, int64_t bt, int64_t L, int32_t C,
+                                         int32_t C_i, const float* logits, const float* pos_bias, int32_t w,
+                                         int32_t stride, int64_t e_begin, int64_t e_end, void* y, void* y_i,
+                                         void* stream);
+
+/*
+ * hattn_compress_channel_logits -- compression with a logit per channel.
+ * The variant of hattn_compress whose compression weight ([HCA] section
+ * 怎么压: one weight per raw entry, softmax over weight + position bias) is a
+ * vector, one value per channel, so each channel has its own softmax:
+ *   a_jc = logits[b][i*stride + j][c] + pos_bias[j]
+ *   y[b][i][c] = sum_j softmax_j(a_.c)_j * x[b][i*stride + j][c]
+ *   logits [bt][L][C] fp32 (required; 16-byte aligned), pos_bias [w] or NULL.
+ * Other arguments and limits as for hattn_compress.
+ */
+hattn_status_t hattn_compress_channel_logits(int dtype, const void* x, int64_t bt, int64_t L, int32_t C,
+                                             const float* logits, const float* pos_bias, int32_t w, int32_t stride,
+                                             int64_t e_begin, int64_t e_end, void* y, void* stream);
+
+/*
  * hattn_visible_count -- how many compressed entries each query may see.
  * Causal reading of [HYB] section 为什么长上下文需要新的 Attention (decode
  * reads only history): entry i is visible to a query at raw position p iff

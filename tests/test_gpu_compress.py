@@ -176,3 +176,66 @@ def test_decode_append(dtype, w, s, L, C, pool):
                     np.testing.assert_array_equal(reps[i, j], ref_reps[j])  # small integers / 2^k: exact
                 else:
                     assert (reps[i, j] == -3.0).all(), (i, j)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("w,s,L", [(8, 4, 1001), (128, 128, 1000), (5, 3, 77)])
+def test_compress_with_index(dtype, w, s, L):
+    # K|V entries and their indexer keys from one pass with the entries'
+    # own weights; each output against the oracle's compression of its raw
+    # rows, and the K|V output equals hattn_compress's where the two share a
+    # kernel and its per-thread arithmetic (the w = 2s and generic kernels).
+    bt, C, Ci = 2, 256, 128
+    x = synth.normal((bt, L, C), seed=31 + w, dtype=dtype)
+    xi = synth.normal((bt, L, Ci), seed=32 + w, dtype=dtype)
+    z = synth.normal((bt, L), seed=33 + w)
+    b = synth.normal((w,), seed=34 + w, std=0.1)
+    y, yi = ops.compress_with_index(x.to(DEV), xi.to(DEV), z.to(DEV), b.to(DEV), w, s)
+    y_ref_gpu = ops.compress(x.to(DEV), z.to(DEV), b.to(DEV), w, s)
+    torch.cuda.synchronize()
+    for i in range(bt):
+        r, ri = oracle.compress_with_index(f64(x[i]), f64(xi[i]), f64(z[i]), f64(b), w, s)
+        for got, ref in ((y[i], r), (yi[i], ri)):
+            if dtype == torch.float32:
+                np.testing.assert_allclose(f64(got), ref, rtol=2e-5, atol=2e-5)
+            else:
+                assert_bf16_close(f64(got), ref)
+    if w < 32:
+        assert torch.equal(y, y_ref_gpu)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("w,s,L", [(8, 4, 1001), (128, 128, 1024), (5, 3, 77), (1, 1, 9)])
+def test_compress_channel_logits(dtype, w, s, L):
+    bt, C = 2, 64
+    x = synth.normal((bt, L, C), seed=41 + w, dtype=dtype)
+    Z = synth.normal((bt, L, C), seed=42 + w)
+    b = synth.normal((w,), seed=43 + w, std=0.1)
+    y = ops.compress_channel_logits(x.to(DEV), Z.to(DEV), b.to(DEV), w, s)
+    # the same logit in every channel reproduces the per-token compression
+    z1 = synth.normal((bt, L), seed=44 + w)
+    y1 = ops.compress_channel_logits(x.to(DEV), z1[:, :, None].expand(bt, L, C).contiguous().to(DEV), b.to(DEV), w, s)
+    torch.cuda.synchronize()
+    for i in range(bt):
+        ref = oracle.compress_channel_logits(f64(x[i]), f64(Z[i]), f64(b), w, s)
+        ref1 = oracle.compress(f64(x[i]), f64(z1[i]), f64(b), w, s)
+        for got, r in ((y[i], ref), (y1[i], ref1)):
+            if dtype == torch.float32:
+                np.testing.assert_allclose(f64(got), r, rtol=2e-5, atol=2e-5)
+            else:
+                assert_bf16_close(f64(got), r)
+
+
+def test_compress_channel_logits_decode_entry_only():
+    # a decode step rewrites just the entry the new token completes
+    bt, L, C, w, s = 3, 2048, 256, 8, 4
+    N = oracle.n_entries(L, w, s)
+    x = synth.normal((bt, L, C), seed=51, dtype=torch.bfloat16)
+    Z = synth.normal((bt, L, C), seed=52)
+    y = torch.zeros((bt, N, C), dtype=torch.bfloat16, device=DEV)
+    ops.compress_channel_logits(x.to(DEV), Z.to(DEV), None, w, s, N - 1, N, out=y)
+    torch.cuda.synchronize()
+    assert (y[:, : N - 1] == 0).all()
+    for i in range(bt):
+        ref = oracle.compress_channel_logits(f64(x[i, L - w:]), f64(Z[i, L - w:]), None, w, s)
+        assert_bf16_close(f64(y[i, N - 1:]), ref)
