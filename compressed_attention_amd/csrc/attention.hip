@@ -128,6 +128,10 @@ struct AttnK {
   float* lse;
   float* part_o;
   float* part_ml;
+  // Head groups of a query row: the row has 16 * NW * hg heads and a
+  // workgroup takes one group of 16 * NW (layers that share one cache and
+  // one selection fold into the head axis: MQA heads share every key).
+  int hg = 1;
 };
 
 template <int D>
@@ -143,7 +147,8 @@ struct AttnLds {
 // its cache and plain loads keep it in L2.  (A template parameter: the
 // compiler merges a runtime choice between the two loads into a plain one.)
 template <int D, int NW, bool SPARSE, bool STREAM>
-HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D>& lds, int32_t* sidx) {
+HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D>& lds, int32_t* sidx,
+                              int hgroup = 0) {
   const uint16_t* __restrict__ q = a.q;
   const uint16_t* __restrict__ ckv = a.ckv;
   const int64_t n = a.n;
@@ -193,11 +198,12 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, r16 = lane & 15;
-  const int head = 16 * wave + r16;
+  const int HT = H * a.hg;                      // heads of the query row
+  const int head = hgroup * H + 16 * wave + r16;  // this lane's head in the row
 
   u32x4_t qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(q + (qrow * H + head) * D + 32 * ks + 8 * g);
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(q + (qrow * HT + head) * D + 32 * ks + 8 * g);
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -347,18 +353,18 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
   const float l_tot = sum_groups(l_run);
   if (nsplit == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* op = out + (qrow * H + head) * D + 4 * g;
+    float* op = out + (qrow * HT + head) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t*>(op + 16 * dt) = o[dt] * inv;
-    if (lse && g == 0) lse[qrow * H + head] = (m_run + __log2f(l_tot)) * kLn2;
+    if (lse && g == 0) lse[qrow * HT + head] = (m_run + __log2f(l_tot)) * kLn2;
   } else {
     const int64_t pr = qrow * nsplit + split;
-    float* op = part_o + (pr * H + head) * D + 4 * g;
+    float* op = part_o + (pr * HT + head) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t*>(op + 16 * dt) = o[dt];
     if (g == 0) {
-      part_ml[(pr * H + head) * 2 + 0] = m_run;
-      part_ml[(pr * H + head) * 2 + 1] = l_tot;
+      part_ml[(pr * HT + head) * 2 + 0] = m_run;
+      part_ml[(pr * HT + head) * 2 + 1] = l_tot;
     }
   }
 }
@@ -367,7 +373,7 @@ template <int D, int NW, bool SPARSE, bool STREAM>
 __global__ __launch_bounds__(64 * NW, 2) void attn_mfma_kernel(AttnK a) {
   __shared__ AttnLds<D> lds;
   __shared__ int32_t sidx[SPARSE ? kSparseChunkMax : 1];  // this chunk's compressed indices
-  attn_mfma_body<D, NW, SPARSE, STREAM>(a, blockIdx.x, blockIdx.y, lds, sidx);
+  attn_mfma_body<D, NW, SPARSE, STREAM>(a, blockIdx.x, blockIdx.y, lds, sidx, blockIdx.z);
 }
 
 // A sparse and a dense query set in one launch (e.g. the CSA and HCA
@@ -638,11 +644,15 @@ __global__ __launch_bounds__(256) void attn_merge_any_kernel(const float* __rest
 // ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
+// bf16 MFMA shapes: 16, 32 or any multiple of 64 heads (up to 1,024; 64 per
+// workgroup, head groups in grid z), d in {64, 128}.
 static bool mfma_shape(const AttnArgs& a) {
   const int64_t lim = int64_t(1) << 31;
-  return a.dtype == 1 && (a.d == 64 || a.d == 128) && (a.h == 16 || a.h == 32 || a.h == 64) &&
-         a.n * 2 * a.d < lim && a.L * 2 * a.d < lim && (a.idx ? int64_t(a.k) : a.n) + a.window < lim;
+  const bool heads = a.h == 16 || a.h == 32 || (a.h % 64 == 0 && a.h <= 1024);
+  return a.dtype == 1 && (a.d == 64 || a.d == 128) && heads && a.n * 2 * a.d < lim && a.L * 2 * a.d < lim &&
+         (a.idx ? int64_t(a.k) : a.n) + a.window < lim;
 }
+static int head_groups(const AttnArgs& a) { return a.h > 64 ? a.h / 64 : 1; }
 
 bool attn_supported(const AttnArgs& a) {
   if (mfma_shape(a)) return true;
@@ -667,7 +677,8 @@ static AttnPlan plan_attn(const AttnArgs& a) {
   // reads back (measured: 480 beat 352 and 704 at batch 32).  Never a chunk
   // under 128 keys.
   const int64_t target_wg = mfma_shape(a) ? 512 : 1024;
-  int64_t chunk = (rows * maxkeys + target_wg - 1) / target_wg;
+  const int64_t hg = mfma_shape(a) ? head_groups(a) : 1;  // workgroups per (query, chunk)
+  int64_t chunk = (rows * hg * maxkeys + target_wg - 1) / target_wg;
   chunk = std::max<int64_t>(chunk, 128);
   chunk = (chunk + tk - 1) / tk * tk;
   if (chunk >= maxkeys) chunk = (maxkeys + tk - 1) / tk * tk;
@@ -685,19 +696,20 @@ size_t attn_ws_bytes(const AttnArgs& a) { return plan_attn(a).total; }
 
 static AttnK attn_k(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml) {
   return AttnK{(const uint16_t*)a.q, (const uint16_t*)a.ckv, a.n, a.idx, a.k, a.n_vis, (const uint16_t*)a.raw_kv,
-               a.L, a.q_pos, a.window, a.scale * kLog2e, a.nq, pl.chunk, pl.nsplit, a.out, a.lse, po, pml};
+               a.L, a.q_pos, a.window, a.scale * kLog2e, a.nq, pl.chunk, pl.nsplit, a.out, a.lse, po, pml,
+               head_groups(a)};
 }
 
 template <bool SPARSE>
 static void launch_attn_mfma(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml, hipStream_t st) {
   const AttnK k = attn_k(a, pl, po, pml);
-  dim3 grid(unsigned(pl.nsplit), unsigned(a.bt * a.nq));
+  dim3 grid(unsigned(pl.nsplit), unsigned(a.bt * a.nq), unsigned(head_groups(a)));
 #define HATTN_ATTN(D, NH)                                                                     \
   do {                                                                                        \
     if (a.nq == 1) HATTN_LAUNCH((attn_mfma_kernel<D, NH, SPARSE, true>), grid, dim3(64 * NH), 0, st, k); \
     else HATTN_LAUNCH((attn_mfma_kernel<D, NH, SPARSE, false>), grid, dim3(64 * NH), 0, st, k);        \
   } while (0)
-  const int nw = a.h / 16;
+  const int nw = std::min(a.h, 64) / 16;  // waves per workgroup (16 heads each)
   if (a.d == 128) {
     switch (nw) {
       case 1: HATTN_ATTN(128, 1); break;
@@ -766,7 +778,8 @@ hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
 // other.  Results equal launch_attn on each set.
 hipError_t launch_attn_pair(const AttnArgs& s, void* ws_s, const AttnArgs& d, void* ws_d, hipStream_t st) {
   // (the paired launch streams K|V: one query per sequence, as in decode)
-  if (!(mfma_shape(s) && mfma_shape(d) && s.idx && !d.idx && s.h == d.h && s.d == d.d && s.nq == 1 && d.nq == 1)) {
+  if (!(mfma_shape(s) && mfma_shape(d) && s.idx && !d.idx && s.h == d.h && s.h <= 64 && s.d == d.d && s.nq == 1 &&
+        d.nq == 1)) {
     hipError_t e = launch_attn(s, ws_s, st);
     return e != hipSuccess ? e : launch_attn(d, ws_d, st);
   }

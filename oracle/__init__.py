@@ -38,5 +38,6 @@ from .hattn_ref import (  # noqa: F401
     attend,
     sparse_attention,
     dense_compressed_attention,
+    csa2_layer_group,
     lse_merge,
 )

@@ -375,6 +375,39 @@ def dense_compressed_attention(q, ckv, n_vis, raw_kv, q_pos, W: int, scale: floa
     return out, lse
 
 
+def csa2_layer_group(q, raw_kv, raw_ki, z, b, q_i, w_i, q_pos, k: int, W: int, w: int, s: int, scale: float):
+    """CSA2 (V4.1-Flash) for a group of layers that share one global cache.
+
+    [HCA] section V4.1 为什么不要它了: V4.1 keeps a single global branch,
+    one compression level plus cross-layer sharing, and every query sees the
+    global context only through a top-512 selection, beside the 128-token
+    sliding window.  Here (readings: the compression is ``compress`` at the
+    group's one rate, w = 2s as for CSA, or w = s = 1 for an uncompressed
+    cache; the indexer keys are compressed from raw indexer keys with the
+    entries' own weights; the group of layers shares the cache, the
+    visibility and the selected indices, and each layer has its own
+    queries):
+
+        ckv, K_I = compress_with_index(raw_kv, raw_ki, z, b, w, s)
+        idx      = flat_topk(q_i, K_I, w_i, n_vis, k)            once per group
+        out[g]   = sparse_attention(q[g], ckv, idx, raw_kv, q_pos, W, scale)
+
+    q [G][nq][H][d] (layer g's queries), raw_kv [L][2d], raw_ki [L][d_I],
+    z [L] per-token logits, q_i [nq][H_I][d_I], w_i [nq][H_I].
+    Returns (out [G][nq][H][d], lse [G][nq][H], idx [nq][k]).
+    """
+    ckv, k_i = compress_with_index(raw_kv, raw_ki, z, b, w, s)
+    N = ckv.shape[0]
+    n_vis = np.array([n_visible(int(p), w, s, N) for p in q_pos])
+    idx = flat_topk(q_i, k_i, w_i, n_vis, k)
+    outs, lses = [], []
+    for g in range(q.shape[0]):
+        o, lse = sparse_attention(q[g], ckv, idx, raw_kv, q_pos, W, scale)
+        outs.append(o)
+        lses.append(lse)
+    return np.stack(outs), np.stack(lses), idx
+
+
 def lse_merge(outs, lses):
     """Combine attention over disjoint key lists from their (o, lse) pairs.
 

@@ -160,3 +160,70 @@ def test_causality_future_tokens_do_not_matter():
             outs.append((ckv[:nv], idx, o_s, o_d))
         for a, bb in zip(*outs):
             np.testing.assert_array_equal(a, bb)
+
+
+# ---- CSA2: one compression level, a selection shared by a group of layers ---
+
+def _csa2_inputs(L=300, d=8, H=3, G=2, nq=4, DI=4, HI=2):
+    raw = rng.standard_normal((L, 2 * d))
+    raw_ki = rng.integers(-3, 4, (L, DI)).astype(float)
+    z = rng.standard_normal(L)
+    q = rng.standard_normal((G, nq, H, d))
+    q_i = rng.integers(-3, 4, (nq, HI, DI)).astype(float)
+    w_i = rng.integers(0, 4, (nq, HI)).astype(float) / 4
+    q_pos = np.sort(rng.choice(np.arange(8, L), nq, replace=False))
+    return raw, raw_ki, z, q, q_i, w_i, q_pos
+
+
+@pytest.mark.parametrize("w,s", [(4, 2), (1, 1)])
+def test_csa2_keeping_every_entry_is_library_attention(w, s):
+    # k at least the visible count: each layer attends to every visible
+    # entry (compressed from its raw rows here with explicit window slices)
+    # plus the window, in one library softmax
+    d, W = 8, 16
+    raw, raw_ki, z, q, q_i, w_i, q_pos = _csa2_inputs(d=d)
+    b = 0.1 * rng.standard_normal(w)
+    out, lse, idx = oracle.csa2_layer_group(q, raw, raw_ki, z, b, q_i, w_i, q_pos, 400, W, w, s, 1 / np.sqrt(d))
+    for j, p in enumerate(q_pos):
+        nv = (p - w + 1) // s + 1
+        assert list(idx[j][:nv]) == list(range(nv)) and (idx[j][nv:] == -1).all()
+        ents = []
+        for i in range(nv):
+            a = z[i * s:i * s + w] + b
+            al = np.exp(a - a.max())
+            al /= al.sum()
+            ents.append(al @ raw[i * s:i * s + w])
+        ents = np.array(ents)
+        lo = max(0, p - W + 1)
+        keys = np.concatenate([ents[:, :d], raw[lo:p + 1, :d]])
+        vals = np.concatenate([ents[:, d:], raw[lo:p + 1, d:]])
+        for g in range(q.shape[0]):
+            # torch's SDPA scales by 1/sqrt(d), the scale passed above
+            np.testing.assert_allclose(out[g, j], sdpa(q[g, j], keys, vals), rtol=1e-10, atol=1e-12)
+
+
+def test_csa2_uncompressed_cache_is_the_raw_rows():
+    raw, raw_ki, z, q, q_i, w_i, q_pos = _csa2_inputs()
+    ckv, k_i = oracle.compress_with_index(raw, raw_ki, z, None, 1, 1)
+    np.testing.assert_array_equal(ckv, raw)
+    np.testing.assert_array_equal(k_i, raw_ki)
+
+
+def test_csa2_layers_fold_into_heads():
+    # MQA: every head attends to the same keys, so a group's layers sharing
+    # one cache and one selection are one attention with G*H heads (the
+    # layout the GPU uses: head g*H + h is head h of layer g)
+    d = 8
+    raw, raw_ki, z, q, q_i, w_i, q_pos = _csa2_inputs(d=d)
+    G, nq, H, _ = q.shape
+    b = 0.1 * rng.standard_normal(4)
+    out, lse, idx = oracle.csa2_layer_group(q, raw, raw_ki, z, b, q_i, w_i, q_pos, 20, 16, 4, 2, 1 / np.sqrt(d))
+    ckv, _ = oracle.compress_with_index(raw, raw_ki, z, b, 4, 2)
+    folded = q.transpose(1, 0, 2, 3).reshape(nq, G * H, d)
+    of, lf = oracle.sparse_attention(folded, ckv, idx, raw, q_pos, 16, 1 / np.sqrt(d))
+    np.testing.assert_allclose(of.reshape(nq, G, H, d).transpose(1, 0, 2, 3), out, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lf.reshape(nq, G, H).transpose(1, 0, 2), lse, rtol=1e-13, atol=1e-14)
+    # the layers really share a sparse set: some query sees more entries
+    # than it selects
+    nvis = (q_pos - 4 + 1) // 2 + 1
+    assert (nvis > 20).any() and ((idx >= 0).sum(axis=1) == np.minimum(nvis, 20)).all()
