@@ -353,6 +353,47 @@ def hca_decode_b32(args):
     return dict(ms=ms, kernels=kt, step_bytes=byt, compress_ms=comp_ms, compress_bytes=comp_bytes, bt=bt)
 
 
+def csa2_decode(args):
+    """CSA2 decode step at 1M context: 8 sequences, a group of 2 layers
+    sharing one cache compressed at rate 2 (w = 4, s = 2: 524,287 entries)
+    and one flat top-512 selection (16 x 128 indexer over the compressed
+    indexer keys), each layer's 64 heads attending to the selection plus its
+    128-token window (the two layers as 128 MFMA heads).  The step compresses
+    the entry the new token completes (K|V and indexer key together), counts
+    the visible entries, selects and attends; replayed as graphs."""
+    import torch
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    bt, L, G, H, d, DI, k, w, s = 8, 1 << 20, 2, 64, 128, 128, 512, 4, 2
+    N = (L - w) // s + 1
+    names = synth.tensor_seeds(11, ["raw", "raw_ki", "z", "b", "q", "q_i", "w_i"])
+    raw = synth.normal((bt, L, 2 * d), names["raw"], dtype=torch.bfloat16, device=dev)
+    raw_ki = synth.normal((bt, L, DI), names["raw_ki"], dtype=torch.bfloat16, device=dev)
+    z = synth.normal((bt, L), names["z"], device=dev)
+    b = synth.tiled_bias(2, w, names["b"]).to(dev)
+    q = synth.normal((bt, 1, G * H, d), names["q"], dtype=torch.bfloat16, device=dev)
+    q_i = synth.normal((bt, 1, 16, DI), names["q_i"], dtype=torch.bfloat16, device=dev)
+    w_i = synth.uniform((bt, 1, 16), names["w_i"], device=dev)
+    q_pos = torch.full((bt, 1), L - 1, dtype=torch.int32, device=dev)
+    ckv, k_i = ops.compress_with_index(raw, raw_ki, z, b, w, s)
+    del raw_ki
+    torch.cuda.synchronize()
+    x_i = synth.normal((bt, L, DI), names["raw_ki"], dtype=torch.bfloat16, device=dev)
+
+    def step(_):
+        ops.compress_with_index(raw, x_i, z, b, w, s, N - 1, N, out=ckv, out_i=k_i)
+        nv = ops.visible_count(q_pos, w, s, N)
+        idx = ops.index_topk(q_i, k_i, w_i, nv, k)
+        return ops.sparse_attn(q, ckv, idx, raw, q_pos, 128)
+
+    graphs = capture(step, [None])
+    ms = timed_graphs(graphs, max(10, args.steps), 3)
+    kt = kernel_times(step, [None], max(10, args.steps // 2))
+    del graphs
+    return dict(ms=ms, kernels=kt, bt=bt, layers=G, N=N)
+
+
 def csa_prefill(args):
     """CSA prefill chunk: 1,024 query tokens at the end of a 32K sequence
     (H=64, d=128; 8,191 entries; 16 x 64 indexer; k=512 + window 128).  The
@@ -703,6 +744,12 @@ def main():
             kernels_us={kk: v[0] * 1e3 for kk, v in h["kernels"].items()})
         extras["compress_1M_hca_b32"] = dict(ms=h["compress_ms"], GBps=h["compress_bytes"] / (h["compress_ms"] * 1e-3) / 1e9,
                                              hbm_frac=h["compress_bytes"] / (h["compress_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS)
+        torch.cuda.empty_cache()
+        c2 = csa2_decode(args)
+        extras["csa2_decode_1M_b8_2layers"] = dict(
+            us_per_step=c2["ms"] * 1e3, layer_queries_per_s=c2["bt"] * c2["layers"] / (c2["ms"] * 1e-3),
+            entries=c2["N"], kernels_us={kk: v[0] * 1e3 for kk, v in c2["kernels"].items()},
+            note="rate-2 cache (w=4, s=2), flat top-512 over the compressed indexer keys, 2 layers as 128 heads")
         torch.cuda.empty_cache()
         cp = csa_prefill(args)
         ck = {kk: v[0] for kk, v in cp["kernels"].items()}

@@ -232,8 +232,12 @@ hattn_status_t hattn_block_sparse_topk(int dtype, const void* q_i, const void* k
  *   raw_kv [bt][L][2d] dtype         q_pos [bt][nq] int32, 0 <= p < L
  *   out    [bt][nq][h][d] fp32 out   lse [bt][nq][h] fp32 out or NULL
  * Requires window >= 1 and d a multiple of 8.  bf16 with d in {64, 128}
- * and h in {16, 32, 64} runs on MFMA; any other shape with h*d <= 8192 and
- * d <= 256 takes the vector path.
+ * and h in {16, 32} or a multiple of 64 up to 1,024 runs on MFMA (64 heads
+ * per workgroup); any other shape with h*d <= 8192 and d <= 256 takes the
+ * vector path.  Layers that share one cache and one index list (CSA2's
+ * cross-layer reuse, [HCA] section V4.1 为什么不要它了) are one call: with
+ * MQA every head attends to the same keys, so layer g's head j is head
+ * g*h_layer + j of q, out and lse.
  */
 hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx,
                                  int32_t k, const void* raw_kv, int64_t L, const int32_t* q_pos,

@@ -121,7 +121,7 @@ def test_attention_validation(L):
     assert f(1, p, p, 100, p, p, 1000, p, 128, -1.0, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
     assert f(1, p, p, 100, p, p, 1000, p, 128, 0.1, 1, 1, 64, 12, p, None, None, ctypes.byref(sz), None) == 1
     assert f(1, p, p, 100, None, p, 1000, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
-    assert f(1, p, p, 100, p, p, 1000, p, 128, 0.1, 1, 1, 512, 128, p, None, None, ctypes.byref(sz), None) == 2
+    assert f(1, p, p, 100, p, p, 1000, p, 128, 0.1, 1, 1, 2048, 128, p, None, None, ctypes.byref(sz), None) == 2
     # long key lists are split: the partials need a workspace
     assert f(1, p, p, 8192, p, p, 1 << 20, p, 128, 0.1, 32, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 0
     assert sz.value > 0

@@ -203,3 +203,54 @@ def test_decode_plan_indexer_widths(dtype, d_i):
     r_reps = oracle.hisa_pool(f64(t["k_i"][0]), B)
     assert np.array_equal(f64(reps[0, -1]), r_reps[-1])
     plan.close()
+
+
+@pytest.mark.parametrize("nq,w,s", [(1, 4, 2), (64, 4, 2), (1, 1, 1)])
+def test_csa2_layer_group(nq, w, s):
+    # CSA2: the K|V cache and its indexer keys compressed at the group's one
+    # rate (or left uncompressed: w = s = 1), one flat top-512 selection, and
+    # two layers' 64 query heads each attending to the shared selection plus
+    # their window: the layers fold into 128 MFMA heads (two head groups).
+    bt, L, G, H, d, DI, k = 2, 8192, 2, 64, 128, 64, 512
+    names = synth.tensor_seeds(7, ["raw", "raw_ki", "z", "b", "q", "q_i", "w_i"])
+    raw = synth.normal((bt, L, 2 * d), names["raw"], dtype=torch.bfloat16)
+    raw_ki = synth.int_grid((bt, L, DI), names["raw_ki"], -8, 8, dtype=torch.bfloat16)
+    z = synth.normal((bt, L), names["z"])
+    b = synth.tiled_bias(2, w, names["b"]) if w > 1 else torch.zeros(1)
+    q = synth.normal((bt, nq, G * H, d), names["q"], dtype=torch.bfloat16)
+    q_i = synth.int_grid((bt, nq, 16, DI), names["q_i"], -8, 8, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((bt, nq, 16), names["w_i"])
+    q_pos = torch.arange(L - nq, L, dtype=torch.int32).reshape(1, nq).repeat(bt, 1)
+    N = oracle.n_entries(L, w, s)
+    g = {n: t.to(DEV) for n, t in dict(raw=raw, raw_ki=raw_ki, z=z, b=b, q=q, q_i=q_i, w_i=w_i, q_pos=q_pos).items()}
+    if w > 1:
+        # integer-grid keys merged with softmax weights are not integers:
+        # the selection stays exact only with uniform weights, so the
+        # indexer keys get no logits; K|V use the real ones
+        ckv, _ = ops.compress_with_index(g["raw"], g["raw_ki"], g["z"], g["b"], w, s)
+        _, k_i = ops.compress_with_index(g["raw"], g["raw_ki"], None, None, w, s)
+    else:
+        ckv, k_i = ops.compress_with_index(g["raw"], g["raw_ki"], g["z"], None, w, s)
+    nv = ops.visible_count(g["q_pos"], w, s, N)
+    idx = ops.index_topk(g["q_i"], k_i, g["w_i"], nv, k)
+    out = ops.sparse_attn(g["q"], ckv, idx, g["raw"], g["q_pos"], 128)
+    torch.cuda.synchronize()
+    sc = 1 / math.sqrt(d)
+    for bb in range(bt):
+        qq = f64(q[bb]).reshape(nq, G, H, d).transpose(1, 0, 2, 3)
+        if w > 1:
+            r_o, _, r_idx = oracle.csa2_layer_group(qq, f64(raw[bb]), f64(raw_ki[bb]), f64(z[bb]), f64(b), f64(q_i[bb]),
+                                                    f64(w_i[bb]), q_pos[bb].numpy(), k, 128, w, s, sc)
+            # the reference's selection over the same uniform-weight keys
+            r_ki = oracle.compress(f64(raw_ki[bb]), None, None, w, s)
+            nvh = np.array([oracle.n_visible(int(p), w, s, N) for p in q_pos[bb]])
+            r_idx = oracle.flat_topk(f64(q_i[bb]), r_ki, f64(w_i[bb]), nvh, k)
+            ckv_r = oracle.compress(f64(raw[bb]), f64(z[bb]), f64(b), w, s)
+            r_o = np.stack([oracle.sparse_attention(qq[gg], ckv_r, r_idx, f64(raw[bb]), q_pos[bb].numpy(), 128, sc)[0]
+                            for gg in range(G)])
+        else:
+            r_o, _, r_idx = oracle.csa2_layer_group(qq, f64(raw[bb]), f64(raw_ki[bb]), f64(z[bb]), None, f64(q_i[bb]),
+                                                    f64(w_i[bb]), q_pos[bb].numpy(), k, 128, w, s, sc)
+        assert np.array_equal(idx[bb].cpu().numpy(), r_idx), bb
+        got = f64(out[bb]).reshape(nq, G, H, d).transpose(1, 0, 2, 3)
+        assert np.abs(got - r_o).max() < 1e-2, (bb, float(np.abs(got - r_o).max()))
