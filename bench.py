@@ -170,12 +170,14 @@ def flat_decode_step(args, t, caches, k):
     per cache replica; returns ms per step."""
     from compressed_attention_amd import ops
 
+    L = 1 << 20
+
     def step(c):
-        nv = ops.decode_append(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, t["q_pos"], c["ckv"])
+        nv = ops.decode_append(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, t["q_pos"], c["ckv"], L=L)
         idx = ops.index_topk(t["q_i"], c["k_i"], t["w_i"], nv, k)
-        o1 = ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128)
-        nvh = ops.decode_append(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, t["q_pos"], c["hkv"])
-        o2 = ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128)
+        o1 = ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128, L=L)
+        nvh = ops.decode_append(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, t["q_pos"], c["hkv"], L=L)
+        o2 = ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128, L=L)
         return o1, o2
 
     graphs = capture(step, caches)
@@ -204,6 +206,19 @@ def hybrid_pair(args):
     torch.cuda.synchronize()
     assert ckv.shape[1] == N and hkv.shape[1] == Nh
     nb = reps.shape[1]
+    # The decode step keeps only the newest 128 raw rows and logits of each
+    # layer, as rings (row r at slot r % 128): the full prefix only built the
+    # caches above.
+    RING = 128
+    for n in ("csa_raw_kv", "hca_raw_kv", "csa_z", "hca_z"):
+        full = t[n]
+        ring = torch.empty((bt, RING) + tuple(full.shape[2:]), dtype=full.dtype, device=dev)
+        rows = torch.arange(L - RING, L, device=dev)
+        ring[:, rows % RING] = full[:, rows]
+        t[n] = ring
+        del full
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     R = args.replicas
     caches = [dict(ckv=ckv, hkv=hkv, k_i=t["k_i"], reps=reps)]
     for _ in range(R - 1):
@@ -214,18 +229,18 @@ def hybrid_pair(args):
     def csa_select(c):
         # compressed entry + block mean + visible count of the new token, one launch
         nv = ops.decode_append(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4, t["q_pos"], c["ckv"], c["k_i"],
-                               c["reps"], B)
+                               c["reps"], B, L=L)
         return ops.hisa_topk(t["q_i"], c["k_i"], t["w_i"], nv, c["reps"], B, m, k)
 
     def csa_attend(c, idx):
-        return ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128)
+        return ops.sparse_attn(t["csa_q"], c["ckv"], idx, t["csa_raw_kv"], t["q_pos"], 128, L=L)
 
     def csa_step(c):
         return csa_attend(c, csa_select(c))
 
     def hca_step(c):
-        nvh = ops.decode_append(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, t["q_pos"], c["hkv"])
-        return ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128)
+        nvh = ops.decode_append(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128, t["q_pos"], c["hkv"], L=L)
+        return ops.dense_compressed_attn(t["hca_q"], c["hkv"], nvh, t["hca_raw_kv"], t["q_pos"], 128, L=L)
 
     def step(c):  # eager, one stream
         return csa_step(c), hca_step(c)
@@ -237,7 +252,7 @@ def hybrid_pair(args):
     plans = [ops.DecodePlan(q_pos=t["q_pos"], csa_raw_kv=t["csa_raw_kv"], csa_logits=t["csa_z"],
                             csa_pos_bias=t["csa_b"], csa_ckv=c["ckv"], k_i=c["k_i"], reps=c["reps"], q_i=t["q_i"],
                             w_i=t["w_i"], csa_q=t["csa_q"], hca_raw_kv=t["hca_raw_kv"], hca_logits=t["hca_z"],
-                            hca_pos_bias=t["hca_b"], hca_ckv=c["hkv"], hca_q=t["hca_q"], B=B, m=m, k=k)
+                            hca_pos_bias=t["hca_b"], hca_ckv=c["hkv"], hca_q=t["hca_q"], B=B, m=m, k=k, L=L)
              for c in caches]
 
     def replay(i):
@@ -377,12 +392,10 @@ def csa2_decode(args):
     w_i = synth.uniform((bt, 1, 16), names["w_i"], device=dev)
     q_pos = torch.full((bt, 1), L - 1, dtype=torch.int32, device=dev)
     ckv, k_i = ops.compress_with_index(raw, raw_ki, z, b, w, s)
-    del raw_ki
     torch.cuda.synchronize()
-    x_i = synth.normal((bt, L, DI), names["raw_ki"], dtype=torch.bfloat16, device=dev)
 
     def step(_):
-        ops.compress_with_index(raw, x_i, z, b, w, s, N - 1, N, out=ckv, out_i=k_i)
+        ops.compress_with_index(raw, raw_ki, z, b, w, s, N - 1, N, out=ckv, out_i=k_i)
         nv = ops.visible_count(q_pos, w, s, N)
         idx = ops.index_topk(q_i, k_i, w_i, nv, k)
         return ops.sparse_attn(q, ckv, idx, raw, q_pos, 128)
@@ -815,6 +828,7 @@ def main():
         "config": {"workload": "hybrid_pair_decode_1M", "batch": res["bt"], "context": res["L"], "heads": 64,
                    "head_dim": 128, "window": 128, "csa_entries": res["N"], "hca_entries": res["Nh"],
                    "indexer": "16x128", "hisa_B": 128, "hisa_m": 64, "k": res["k"], "cache_replicas": args.replicas,
+                   "raw_rows_kept": 128,
                    "launch": "native decode plan (one host call, 6 kernels per step)"},
         "step_us": {kk: round(v, 2) for kk, v in res["dist"].items() if kk != "n"} | {"n": res["dist"]["n"]},
         "step_us_plan_graph": round(res["graph_plan_ms"] * 1e3, 2),

@@ -6,7 +6,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhattn.so")
-ABI_VERSION = 2  # hattn_abi_version() of the library this binding matches
+ABI_VERSION = 3  # hattn_abi_version() of the library this binding matches
 
 _i32, _i64, _f32, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 _psz = ctypes.POINTER(ctypes.c_size_t)
@@ -23,13 +23,13 @@ SIGNATURES = {
                         _p],
     "hattn_block_sparse_topk": [_i32, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i64, _p, _i32, _i32, _p, _p, _p, _psz,
                                _p],
-    "hattn_sparse_attn": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p, _p,
-                          _psz, _p],
-    "hattn_sparse_attn_noalloc": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p,
-                                  _p, _p],
-    "hattn_dense_compressed_attn": [_i32, _p, _p, _i64, _p, _p, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p, _p,
-                                    _p, _psz, _p],
-    "hattn_decode_append": [_i32, _p, _i64, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p, _p, _i32, _i32, _p, _p],
+    "hattn_sparse_attn": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p,
+                          _p, _p, _psz, _p],
+    "hattn_sparse_attn_noalloc": [_i32, _p, _p, _i64, _p, _i32, _p, _i64, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32,
+                                  _p, _p, _p],
+    "hattn_dense_compressed_attn": [_i32, _p, _p, _i64, _p, _p, _i64, _i64, _p, _i32, _f32, _i64, _i64, _i32, _i32, _p,
+                                    _p, _p, _psz, _p],
+    "hattn_decode_append": [_i32, _p, _i64, _i64, _i64, _i32, _p, _p, _i32, _i32, _p, _p, _p, _p, _i32, _i32, _p, _p],
     "hattn_decode_desc_size": [],
     "hattn_decode_plan_ws_bytes": [_p, _psz],
     "hattn_decode_plan_create": [_p, ctypes.POINTER(_p)],
@@ -50,7 +50,7 @@ class DecodeDesc(ctypes.Structure):
     """Mirror of hattn_decode_desc (include/hattn.h), field for field."""
     _fields_ = [
         ("dtype", _i32), ("h", _i32), ("d", _i32), ("window", _i32),
-        ("bt", _i64), ("L", _i64),
+        ("bt", _i64), ("L", _i64), ("raw_rows", _i64),
         ("scale", _f32),
         ("h_i", _i32), ("d_i", _i32), ("B", _i32), ("m", _i32), ("k", _i32),
         ("csa_w", _i32), ("csa_stride", _i32), ("hca_w", _i32), ("hca_stride", _i32),

@@ -59,20 +59,25 @@ struct Vec16<uint16_t> {
 constexpr int kAppNT = 256;  // threads per workgroup of the append kernel
 constexpr int kAppUNR = 16;  // rows each thread has in flight
 
+// Row u of a window of rows: base + u*ld, or, when the rows live in a ring
+// of `wrap` rows whose row 0 sits at slot s0, base + ((s0 + u) % wrap)*ld.
+HATTN_DEV int64_t win_row(int u, int s0, int wrap) { return wrap ? (s0 + u) % wrap : u; }
+
 // Sums rows [0, n) of a [n][ld] matrix (16-byte slot cs, rows rg, rg + RG, ...)
 // with per-row weights wt(u) into acc.  The first batch of rows is already in
 // `first` (loaded before the weights were ready); later batches reuse it.
-// Loads of a batch are all issued before any is used.
+// Loads of a batch are all issued before any is used.  (s0, wrap): see
+// win_row.
 template <typename T, typename Wt>
 HATTN_DEV void append_rows(const T* __restrict__ base, int64_t ld, int n, int rg, int RG, u32x4_t (&first)[kAppUNR],
-                           Wt wt, float* acc) {
+                           Wt wt, float* acc, int s0 = 0, int wrap = 0) {
   constexpr int V = Vec16<T>::N;
   for (int u0 = rg; u0 < n; u0 += kAppUNR * RG) {
     if (u0 != rg) {
 #pragma unroll
       for (int k = 0; k < kAppUNR; ++k) {
         const int u = u0 + k * RG;
-        first[k] = u < n ? ld16_nt(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
+        first[k] = u < n ? ld16_nt(base + win_row(u, s0, wrap) * ld) : u32x4_t{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -90,20 +95,21 @@ HATTN_DEV void append_rows(const T* __restrict__ base, int64_t ld, int n, int rg
 }
 
 template <typename T>
-HATTN_DEV void append_first(const T* __restrict__ base, int64_t ld, int n, int rg, u32x4_t (&first)[kAppUNR], int RG) {
+HATTN_DEV void append_first(const T* __restrict__ base, int64_t ld, int n, int rg, u32x4_t (&first)[kAppUNR], int RG,
+                            int s0 = 0, int wrap = 0) {
 #pragma unroll
   for (int k = 0; k < kAppUNR; ++k) {
     const int u = rg + k * RG;
-    first[k] = u < n ? ld16_nt(base + int64_t(u) * ld) : u32x4_t{0u, 0u, 0u, 0u};
+    first[k] = u < n ? ld16_nt(base + win_row(u, s0, wrap) * ld) : u32x4_t{0u, 0u, 0u, 0u};
   }
 }
 
 // Per-token maintenance of one compressed layer: the launch arguments.
 struct AppendK {
-  const void* x;  // raw rows [bt][L][C]
+  const void* x;  // raw rows [bt][L][C], or a ring [bt][R][C]
   int64_t L;
   int C;
-  const float* z;
+  const float* z;  // [bt][L], or a ring [bt][R]
   const float* bias;
   int w, s;
   void* y;  // entries [bt][N][C]
@@ -112,6 +118,7 @@ struct AppendK {
   const void* k_i;  // [bt][N][d_i] or NULL
   int d_i, B;
   float* reps;  // [bt][ceil(N/B)][d_i] or NULL
+  int R = 0;    // 0: x and z hold all L rows; R > 0: row r at slot r % R
 };
 
 // The entry the token at p completes (-1 if none) and the visible count.
@@ -136,14 +143,18 @@ HATTN_DEV void append_entry_body(const AppendK& a, int64_t b, int64_t p, float* 
   const int RG = NT / slots;
   const int cs = threadIdx.x % slots, rg = threadIdx.x / slots;
   const int64_t t0 = e * a.s;
-  const T* xb = x + (b * a.L + t0) * C + cs * V;
+  // the window's rows: linear from row t0, or in the ring from slot t0 % R
+  const int R = a.R;
+  const int s0 = R ? int(t0 % R) : 0;
+  const T* xb = R ? x + (b * R) * C + cs * V : x + (b * a.L + t0) * C + cs * V;
+  const float* zb = a.z ? (R ? a.z + b * R : a.z + b * a.L + t0) : nullptr;
   // the window's first rows go out before the softmax weights are known
   u32x4_t first[kAppUNR];
-  if (rg < RG) append_first(xb, C, w, rg, first, RG);
+  if (rg < RG) append_first(xb, C, w, rg, first, RG, s0, R);
   float* wt = sm;        // [w] logits, then softmax numerators
   float* part = sm + w;  // [RG][C] row-group partial sums
   for (int u = threadIdx.x; u < w; u += NT)
-    wt[u] = (a.z ? a.z[b * a.L + t0 + u] : 0.f) + (a.bias ? a.bias[u] : 0.f);
+    wt[u] = (zb ? zb[win_row(u, s0, R)] : 0.f) + (a.bias ? a.bias[u] : 0.f);
   __syncthreads();
   if (threadIdx.x < kWave) {
     float mx = -INFINITY;
@@ -163,7 +174,7 @@ HATTN_DEV void append_entry_body(const AppendK& a, int64_t b, int64_t p, float* 
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    append_rows(xb, C, w, rg, RG, first, [&](int u) { return __expf(wt[u] - mx); }, acc);
+    append_rows(xb, C, w, rg, RG, first, [&](int u) { return __expf(wt[u] - mx); }, acc, s0, R);
 #pragma unroll
     for (int i = 0; i < V; ++i) part[rg * C + cs * V + i] = acc[i];
   }

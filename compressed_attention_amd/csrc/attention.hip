@@ -60,7 +60,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // window rows.  Returns nullptr for skipped keys (index -1 / out of range).
 template <typename T, bool SPARSE>
 HATTN_DEV const T* key_row(int64_t j, int64_t nc, const int32_t* idx_row, const T* ckv_b, int64_t n, const T* raw_b,
-                           int64_t L, int64_t p, int nw, int C) {
+                           int64_t L, int64_t p, int nw, int C, int R) {
   if (j < nc) {
     const int64_t e = SPARSE ? int64_t(idx_row[j]) : j;
     if (e < 0 || e >= n) return nullptr;
@@ -68,7 +68,7 @@ HATTN_DEV const T* key_row(int64_t j, int64_t nc, const int32_t* idx_row, const 
   }
   const int64_t r = p - nw + 1 + (j - nc);
   if (r < 0 || r >= L) return nullptr;
-  return raw_b + r * C;
+  return raw_b + (R ? r % R : r) * C;  // R > 0: the raw rows are a ring of R
 }
 
 // Source row of virtual key j (0 <= j < 2^31) for the MFMA kernel, computed
@@ -81,7 +81,7 @@ HATTN_DEV const T* key_row(int64_t j, int64_t nc, const int32_t* idx_row, const 
 template <bool SPARSE>
 HATTN_DEV const uint16_t* key_src32(int j, int j_end, int nc, const int32_t* sidx, int j_base,
                                     const uint16_t* ckv_b, int n, const uint16_t* raw_b, int L, int rbase, int C,
-                                    bool* ok) {
+                                    bool* ok, int R = 0) {
   const bool in_c = j < nc;
   int e;
   if (SPARSE) e = sidx[in_c && j < j_end ? j - j_base : 0];
@@ -91,7 +91,8 @@ HATTN_DEV const uint16_t* key_src32(int j, int j_end, int nc, const int32_t* sid
   const bool okr = !in_c && unsigned(r) < unsigned(L);
   const bool v = j < j_end && (okc || okr);
   *ok = v;
-  const unsigned off = v ? unsigned(okc ? e : r) * unsigned(C) : 0u;
+  const int slot = R && okr ? r % R : r;  // raw rows in a ring: slot r % R
+  const unsigned off = v ? unsigned(okc ? e : slot) * unsigned(C) : 0u;
   return (v && okc ? ckv_b : raw_b) + off;
 }
 
@@ -132,6 +133,9 @@ struct AttnK {
   // workgroup takes one group of 16 * NW (layers that share one cache and
   // one selection fold into the head axis: MQA heads share every key).
   int hg = 1;
+  // Raw rows held per sequence: 0 = all L (row r at r); R > 0 = a ring
+  // holding the newest R rows (row r at slot r % R).
+  int R = 0;
 };
 
 template <int D>
@@ -191,7 +195,8 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
   const int j_end = min(total, j_begin + chunk);
   const int32_t* idx_row = SPARSE ? idx + qrow * k : nullptr;
   const uint16_t* ckv_b = ckv + b * n * C;
-  const uint16_t* raw_b = raw + b * L * C;
+  const int R = a.R;
+  const uint16_t* raw_b = raw + b * (R ? int64_t(R) : L) * C;
   const int rbase = int(p) - nw + 1 - int(nc);
   const int n32 = int(n), L32 = int(L), nc32 = int(nc);
 
@@ -216,7 +221,14 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
   auto plain_base = [&](int j0) -> const uint16_t* {
     if (SPARSE || j0 + TK > j_end) return nullptr;
     if (j0 + TK <= nc32) return ckv_b + size_t(j0) * C;
-    if (j0 >= nc32) return raw_b + size_t(rbase + j0) * C;
+    if (j0 >= nc32) {
+      // window rows rbase + j0 .. + TK - 1 (>= 0): contiguous unless they
+      // wrap around the ring
+      const int r0 = rbase + j0;
+      if (!R) return raw_b + size_t(r0) * C;
+      const int s0 = r0 % R;
+      return s0 + TK <= R ? raw_b + size_t(s0) * C : nullptr;
+    }
     return nullptr;
   };
   auto fetch = [&](int j0) {
@@ -235,7 +247,7 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
         bool ok;
         // Skipped keys read raw row 0 (finite data); their logits are masked.
         const uint16_t* src = key_src32<SPARSE>(j0 + pidx / PPR, j_end, nc32, sidx, j_begin, ckv_b, n32, raw_b,
-                                                L32, rbase, C, &ok);
+                                                L32, rbase, C, &ok, R);
         pre[u] = STREAM ? ld16_nt(src + (pidx % PPR) * 8) : ld16(src + (pidx % PPR) * 8);
       }
     }
@@ -263,7 +275,7 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
 #pragma unroll
       for (int h = 0; h < TK / 64; ++h) {
         bool ok;
-        key_src32<SPARSE>(j0 + 64 * h + lane, j_end, nc32, sidx, j_begin, ckv_b, n32, raw_b, L32, rbase, C, &ok);
+        key_src32<SPARSE>(j0 + 64 * h + lane, j_end, nc32, sidx, j_begin, ckv_b, n32, raw_b, L32, rbase, C, &ok, R);
         const uint64_t mk = ballot(ok);
         if (lane == 0) vmask[h] = mk;
       }
@@ -406,7 +418,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
                                                         int64_t L, const int32_t* __restrict__ q_pos, int window,
                                                         float scale_log2, int64_t nq, int H, int D, int chunk,
                                                         int nsplit, float* __restrict__ out, float* __restrict__ lse,
-                                                        float* __restrict__ part_o, float* __restrict__ part_ml) {
+                                                        float* __restrict__ part_o, float* __restrict__ part_ml,
+                                                        int R) {
   constexpr int TK = 32;
   constexpr int MAXO = 32;  // outputs per thread: h*d <= 256*32
   extern __shared__ float sm[];
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
   const int64_t j_end = imin64(total, j_begin + chunk);
   const int32_t* idx_row = SPARSE ? idx + qrow * k : nullptr;
   const T* ckv_b = ckv + b * n * C;
-  const T* raw_b = raw + b * L * C;
+  const T* raw_b = raw + b * (R ? int64_t(R) : L) * C;
   const int tid = threadIdx.x;
 
   for (int i = tid; i < H * D; i += 256) qs[i] = to_float(q[qrow * H * D + i]);
@@ -448,7 +461,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
     for (int i = tid; i < TK * D; i += 256) {
       const int r = i / D, c = i % D;
       const int64_t j = j0 + r;
-      const T* src = j < j_end ? key_row<T, SPARSE>(j, nc, idx_row, ckv_b, n, raw_b, L, p, nw, C) : nullptr;
+      const T* src = j < j_end ? key_row<T, SPARSE>(j, nc, idx_row, ckv_b, n, raw_b, L, p, nw, C, R) : nullptr;
       kt[i] = src ? to_float(src[c]) : 0.f;
       vt[i] = src ? to_float(src[D + c]) : 0.f;
       if (c == 0) valid[r] = src != nullptr;
@@ -647,7 +660,7 @@ __global__ __launch_bounds__(256) void attn_merge_any_kernel(const float* __rest
 // bf16 MFMA shapes: 16, 32 or any multiple of 64 heads (up to 1,024; 64 per
 // workgroup, head groups in grid z), d in {64, 128}.
 static bool mfma_shape(const AttnArgs& a) {
-  const int64_t lim = int64_t(1) << 31;
+  const int64_t lim = int64_t(1) << 31;  // (a ring of raw rows is never longer than L)
   const bool heads = a.h == 16 || a.h == 32 || (a.h % 64 == 0 && a.h <= 1024);
   return a.dtype == 1 && (a.d == 64 || a.d == 128) && heads && a.n * 2 * a.d < lim && a.L * 2 * a.d < lim &&
          (a.idx ? int64_t(a.k) : a.n) + a.window < lim;
@@ -697,7 +710,7 @@ size_t attn_ws_bytes(const AttnArgs& a) { return plan_attn(a).total; }
 static AttnK attn_k(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml) {
   return AttnK{(const uint16_t*)a.q, (const uint16_t*)a.ckv, a.n, a.idx, a.k, a.n_vis, (const uint16_t*)a.raw_kv,
                a.L, a.q_pos, a.window, a.scale * kLog2e, a.nq, pl.chunk, pl.nsplit, a.out, a.lse, po, pml,
-               head_groups(a)};
+               head_groups(a), a.raw_rows};
 }
 
 template <bool SPARSE>
@@ -733,7 +746,7 @@ static void launch_attn_valu(const AttnArgs& a, const AttnPlan& pl, float* po, f
   const size_t smem = size_t(a.h) * a.d * 4 + 2 * 32 * size_t(a.d) * 4 + size_t(a.h) * 32 * 4 + 3 * size_t(a.h) * 4;
   HATTN_LAUNCH((attn_valu_kernel<T, SPARSE>), grid, dim3(256), smem, st, (const T*)a.q, (const T*)a.ckv, a.n,
                      a.idx, a.k, a.n_vis, (const T*)a.raw_kv, a.L, a.q_pos, a.window, sl2, a.nq, a.h, a.d, pl.chunk,
-                     pl.nsplit, a.out, a.lse, po, pml);
+                     pl.nsplit, a.out, a.lse, po, pml, a.raw_rows);
 }
 
 hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {

@@ -535,8 +535,8 @@ size_t append_lds_bytes(int dtype, int C, int w, int d_i, bool with_reps) {
 
 hipError_t launch_append(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
                          int w, int s, const int32_t* q_pos, void* y, int64_t N, int32_t* n_vis, const void* k_i,
-                         int d_i, int B, float* reps, hipStream_t st) {
-  const AppendK la{x, L, C, z, bias, w, s, y, N, n_vis, k_i, d_i, B, reps};
+                         int d_i, int B, float* reps, hipStream_t st, int raw_rows) {
+  const AppendK la{x, L, C, z, bias, w, s, y, N, n_vis, k_i, d_i, B, reps, raw_rows};
   return launch_append_k(dtype, la, nullptr, bt, q_pos, st);
 }
 
@@ -544,9 +544,9 @@ hipError_t launch_append_pair(int dtype, int64_t bt, const int32_t* q_pos, const
                               const float* bias1, int w1, int s1, void* y1, int64_t N1, int32_t* n_vis1,
                               const void* k_i, int d_i, int B, float* reps, const void* x2, const float* z2,
                               const float* bias2, int w2, int s2, void* y2, int64_t N2, int32_t* n_vis2, int64_t L,
-                              int C, hipStream_t st) {
-  const AppendK la{x1, L, C, z1, bias1, w1, s1, y1, N1, n_vis1, k_i, d_i, B, reps};
-  const AppendK lb{x2, L, C, z2, bias2, w2, s2, y2, N2, n_vis2, nullptr, 0, 0, nullptr};
+                              int C, hipStream_t st, int raw_rows) {
+  const AppendK la{x1, L, C, z1, bias1, w1, s1, y1, N1, n_vis1, k_i, d_i, B, reps, raw_rows};
+  const AppendK lb{x2, L, C, z2, bias2, w2, s2, y2, N2, n_vis2, nullptr, 0, 0, nullptr, raw_rows};
   return launch_append_k(dtype, la, &lb, bt, q_pos, st);
 }
 

@@ -139,7 +139,7 @@ const char* hattn_status_string(int status) {
 
 const char* hattn_last_error(void) { return g_err; }
 
-int hattn_abi_version(void) { return 2; }
+int hattn_abi_version(void) { return 3; }
 
 // Arrays that kernels access with 16-byte vector loads or stores; NULL passes.
 static bool aligned16(std::initializer_list<const void*> ps) {
@@ -317,6 +317,9 @@ static hattn_status_t attn_check(const char* fn, const hattn::AttnArgs& a, void*
   if (!dtype_ok(a.dtype)) return fail(HATTN_ERR_ARG, "%s: bad dtype %d", fn, a.dtype);
   if (a.bt < 0 || a.nq < 0 || a.n < 0 || a.L < 1 || a.window < 1)
     return fail(HATTN_ERR_ARG, "%s: bad sizes (need L >= 1, window >= 1)", fn);
+  if (a.raw_rows < 0 || (a.raw_rows > 0 && (a.raw_rows < a.window || a.raw_rows > a.L)))
+    return fail(HATTN_ERR_ARG, "%s: a ring of raw_rows=%d must hold window=%d to L=%lld rows", fn, a.raw_rows,
+                a.window, (long long)a.L);
   if (a.h < 1 || a.d < 1 || a.d % 8) return fail(HATTN_ERR_ARG, "%s: bad head shape h=%d d=%d", fn, a.h, a.d);
   if (!(a.scale > 0.f) || a.scale != a.scale) return fail(HATTN_ERR_ARG, "%s: scale must be > 0", fn);
   if (!hattn::attn_supported(a)) return fail(HATTN_ERR_UNSUPPORTED, "%s: h=%d d=%d has no kernel", fn, a.h, a.d);
@@ -337,27 +340,31 @@ static hattn_status_t attn_common(const char* fn, hattn::AttnArgs& a, void* ws, 
   return hip_status(hattn::launch_attn(a, ws, (hipStream_t)stream), fn);
 }
 
+// A ring length that does not fit in int32 is passed on as -1 so that
+// attn_check rejects it.
+static int32_t ring_arg(int64_t raw_rows) { return raw_rows > INT32_MAX ? -1 : int32_t(raw_rows); }
+
 hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx, int32_t k,
-                                 const void* raw_kv, int64_t L, const int32_t* q_pos, int32_t window, float scale,
-                                 int64_t bt, int64_t nq, int32_t h, int32_t d, float* out, float* lse, void* ws,
-                                 size_t* ws_bytes, void* stream) {
+                                 const void* raw_kv, int64_t L, int64_t raw_rows, const int32_t* q_pos,
+                                 int32_t window, float scale, int64_t bt, int64_t nq, int32_t h, int32_t d, float* out,
+                                 float* lse, void* ws, size_t* ws_bytes, void* stream) {
   if (k < 0) return fail(HATTN_ERR_ARG, "sparse_attn: k < 0");
   if (bt * nq > 0 && k > 0 && !idx) return fail(HATTN_ERR_ARG, "sparse_attn: NULL idx");
   // With k == 0 no index is ever used; the kernels still read a clamped
   // slot, so hand them a valid device int32 array (q_pos has >= 1 entry).
   hattn::AttnArgs a{dtype, q, ckv, n, k > 0 ? idx : q_pos, k, nullptr, raw_kv, L, q_pos, window, scale,
-                    bt, nq, h, d, out, lse};
+                    bt, nq, h, d, out, lse, ring_arg(raw_rows)};
   return attn_common("sparse_attn", a, ws, ws_bytes, stream);
 }
 
 hattn_status_t hattn_sparse_attn_noalloc(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx,
-                                         int32_t k, const void* raw_kv, int64_t L, const int32_t* q_pos,
-                                         int32_t window, float scale, int64_t bt, int64_t nq, int32_t h, int32_t d,
-                                         float* out, float* lse, void* stream) {
+                                         int32_t k, const void* raw_kv, int64_t L, int64_t raw_rows,
+                                         const int32_t* q_pos, int32_t window, float scale, int64_t bt, int64_t nq,
+                                         int32_t h, int32_t d, float* out, float* lse, void* stream) {
   if (k < 0) return fail(HATTN_ERR_ARG, "sparse_attn_noalloc: k < 0");
   if (bt * nq > 0 && k > 0 && !idx) return fail(HATTN_ERR_ARG, "sparse_attn_noalloc: NULL idx");
   hattn::AttnArgs a{dtype, q, ckv, n, k > 0 ? idx : q_pos, k, nullptr, raw_kv, L, q_pos, window, scale,
-                    bt, nq, h, d, out, lse};
+                    bt, nq, h, d, out, lse, ring_arg(raw_rows)};
   hattn_status_t st = attn_check("sparse_attn_noalloc", a, nullptr);
   if (st != HATTN_OK) return st;
   const int64_t rows = bt * nq;
@@ -375,21 +382,26 @@ hattn_status_t hattn_sparse_attn_noalloc(int dtype, const void* q, const void* c
 }
 
 hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* n_vis,
-                                           const void* raw_kv, int64_t L, const int32_t* q_pos, int32_t window,
-                                           float scale, int64_t bt, int64_t nq, int32_t h, int32_t d, float* out,
-                                           float* lse, void* ws, size_t* ws_bytes, void* stream) {
+                                           const void* raw_kv, int64_t L, int64_t raw_rows, const int32_t* q_pos,
+                                           int32_t window, float scale, int64_t bt, int64_t nq, int32_t h, int32_t d,
+                                           float* out, float* lse, void* ws, size_t* ws_bytes, void* stream) {
   if (bt * nq > 0 && !n_vis) return fail(HATTN_ERR_ARG, "dense_compressed_attn: NULL n_vis");
-  hattn::AttnArgs a{dtype, q, ckv, n, nullptr, 0, n_vis, raw_kv, L, q_pos, window, scale, bt, nq, h, d, out, lse};
+  hattn::AttnArgs a{dtype, q, ckv, n, nullptr, 0, n_vis, raw_kv, L, q_pos, window, scale, bt, nq, h, d, out, lse,
+                    ring_arg(raw_rows)};
   return attn_common("dense_compressed_attn", a, ws, ws_bytes, stream);
 }
 
 static hattn_status_t append_check(int dtype, const void* raw_kv, int64_t bt, int64_t L, int32_t C, int32_t w,
                                    int32_t stride, const int32_t* q_pos, const void* ckv, const int32_t* n_vis,
-                                   const void* k_i, int32_t d_i, int32_t B, const float* reps, int64_t* N) {
+                                   const void* k_i, int32_t d_i, int32_t B, const float* reps, int64_t* N,
+                                   int64_t raw_rows = 0) {
   if (!dtype_ok(dtype)) return fail(HATTN_ERR_ARG, "decode_append: bad dtype %d", dtype);
   if (bt < 0 || L < 0) return fail(HATTN_ERR_ARG, "decode_append: negative size");
   if (w < 1 || w > 4096 || stride < 1) return fail(HATTN_ERR_ARG, "decode_append: need 1 <= w <= 4096, stride >= 1");
   if (L < w) return fail(HATTN_ERR_ARG, "decode_append: L=%lld shorter than the window %d", (long long)L, w);
+  if (raw_rows < 0 || raw_rows > INT32_MAX || (raw_rows > 0 && (raw_rows < w || raw_rows > L)))
+    return fail(HATTN_ERR_ARG, "decode_append: a ring of raw_rows=%lld must hold w=%d to L=%lld rows",
+                (long long)raw_rows, w, (long long)L);
   const int vec = 16 / elem_bytes(dtype);
   if (C <= 0 || C % vec || C / vec > 256)
     return fail(HATTN_ERR_ARG, "decode_append: C=%d must be a positive multiple of %d, at most %d", C, vec, 256 * vec);
@@ -404,17 +416,17 @@ static hattn_status_t append_check(int dtype, const void* raw_kv, int64_t bt, in
   return HATTN_OK;
 }
 
-hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, int64_t L, int32_t C,
+hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, int64_t L, int64_t raw_rows, int32_t C,
                                    const float* logits, const float* pos_bias, int32_t w, int32_t stride,
                                    const int32_t* q_pos, void* ckv, int32_t* n_vis, const void* k_i, int32_t d_i,
                                    int32_t B, float* reps, void* stream) {
   int64_t N = 0;
   const hattn_status_t st =
-      append_check(dtype, raw_kv, bt, L, C, w, stride, q_pos, ckv, n_vis, k_i, d_i, B, reps, &N);
+      append_check(dtype, raw_kv, bt, L, C, w, stride, q_pos, ckv, n_vis, k_i, d_i, B, reps, &N, raw_rows);
   if (st != HATTN_OK) return st;
   if (bt == 0) return ok();
   return hip_status(hattn::launch_append(dtype, raw_kv, bt, L, C, logits, pos_bias, w, stride, q_pos, ckv, N, n_vis,
-                                         k_i, d_i, B, reps, (hipStream_t)stream),
+                                         k_i, d_i, B, reps, (hipStream_t)stream, int(raw_rows)),
                     "decode_append");
 }
 
@@ -483,6 +495,7 @@ struct hattn_decode_plan {
   int dtype = 0;
   int64_t bt = 0, L = 0;
   int C = 0;
+  int raw_rows = 0;  // 0: full raw arrays; R > 0: rings of the newest R rows
   const int32_t* q_pos = nullptr;
   // CSA branch
   const void* csa_raw_kv = nullptr;
@@ -522,12 +535,15 @@ hattn_status_t decode_layout(const hattn_decode_desc* d, size_t* total, hattn_de
   const int C = 2 * d->d;
   int64_t Nc = 0, Nh = 0;
   hattn_status_t st = append_check(d->dtype, d->csa_raw_kv, d->bt, d->L, C, d->csa_w, d->csa_stride, d->q_pos,
-                                   d->csa_ckv, d->q_pos, d->k_i, d->d_i, d->B, d->reps, &Nc);
+                                   d->csa_ckv, d->q_pos, d->k_i, d->d_i, d->B, d->reps, &Nc, d->raw_rows);
   if (st != HATTN_OK) return st;
   if (!d->k_i) return fail(HATTN_ERR_ARG, "decode_plan: the CSA branch needs k_i and reps");
   st = append_check(d->dtype, d->hca_raw_kv, d->bt, d->L, C, d->hca_w, d->hca_stride, d->q_pos, d->hca_ckv,
-                    d->q_pos, nullptr, 0, 0, nullptr, &Nh);
+                    d->q_pos, nullptr, 0, 0, nullptr, &Nh, d->raw_rows);
   if (st != HATTN_OK) return st;
+  if (d->raw_rows > 0 && d->raw_rows < d->window)
+    return fail(HATTN_ERR_ARG, "decode_plan: a ring of %lld raw rows cannot hold the %d-row window",
+                (long long)d->raw_rows, d->window);
   // Workspace: counts, selected indices, then each call's own workspace.
   const size_t o_nvc = 0;
   const size_t o_nvh = o_nvc + al256(size_t(d->bt) * 4);
@@ -543,12 +559,14 @@ hattn_status_t decode_layout(const hattn_decode_desc* d, size_t* total, hattn_de
   if (st != HATTN_OK) return st;
   const size_t o_sa = o_hisa + al256(hattn::hisa_topk_ws_bytes(ia, d->B, d->m, d->k));
   hattn::AttnArgs sa{d->dtype, d->csa_q, d->csa_ckv, Nc, idx, d->k, nullptr, d->csa_raw_kv,
-                     d->L, d->q_pos, d->window, d->scale, d->bt, 1, d->h, d->d, d->csa_out, d->csa_lse};
+                     d->L, d->q_pos, d->window, d->scale, d->bt, 1, d->h, d->d, d->csa_out, d->csa_lse,
+                     int(d->raw_rows)};
   st = attn_check("decode_plan (CSA attention)", sa, d->ws);
   if (st != HATTN_OK) return st;
   const size_t o_da = o_sa + al256(hattn::attn_ws_bytes(sa));
   hattn::AttnArgs da{d->dtype, d->hca_q, d->hca_ckv, Nh, nullptr, 0, (const int32_t*)at(o_nvh), d->hca_raw_kv,
-                     d->L, d->q_pos, d->window, d->scale, d->bt, 1, d->h, d->d, d->hca_out, d->hca_lse};
+                     d->L, d->q_pos, d->window, d->scale, d->bt, 1, d->h, d->d, d->hca_out, d->hca_lse,
+                     int(d->raw_rows)};
   st = attn_check("decode_plan (HCA attention)", da, d->ws);
   if (st != HATTN_OK) return st;
   *total = o_da + al256(hattn::attn_ws_bytes(da));
@@ -557,6 +575,7 @@ hattn_status_t decode_layout(const hattn_decode_desc* d, size_t* total, hattn_de
   p->bt = d->bt;
   p->L = d->L;
   p->C = C;
+  p->raw_rows = int(d->raw_rows);
   p->q_pos = d->q_pos;
   p->csa_raw_kv = d->csa_raw_kv;
   p->csa_logits = d->csa_logits;
@@ -640,14 +659,14 @@ hattn_status_t hattn_decode_plan_run(hattn_decode_plan_t p, void* stream) {
     e = hattn::launch_decode_front(p->ia, p->reps, p->B, p->m, p->hisa_ws, p->q_pos, p->csa_raw_kv, p->csa_logits,
                                    p->csa_pos_bias, p->csa_w, p->csa_stride, p->csa_ckv, p->nv_csa, p->hca_raw_kv,
                                    p->hca_logits, p->hca_pos_bias, p->hca_w, p->hca_stride, p->hca_ckv, p->hca_N,
-                                   p->nv_hca, p->L, p->C, st);
+                                   p->nv_hca, p->L, p->C, st, p->raw_rows);
     if (e == hipSuccess)
       e = hattn::launch_hisa_topk(p->ia, p->reps, p->B, p->m, p->k, p->idx, nullptr, p->hisa_ws, st, true);
   } else {
     e = hattn::launch_append_pair(p->dtype, p->bt, p->q_pos, p->csa_raw_kv, p->csa_logits, p->csa_pos_bias,
                                   p->csa_w, p->csa_stride, p->csa_ckv, p->csa_N, p->nv_csa, p->k_i, p->d_i, p->B,
                                   p->reps, p->hca_raw_kv, p->hca_logits, p->hca_pos_bias, p->hca_w, p->hca_stride,
-                                  p->hca_ckv, p->hca_N, p->nv_hca, p->L, p->C, st);
+                                  p->hca_ckv, p->hca_N, p->nv_hca, p->L, p->C, st, p->raw_rows);
     if (e == hipSuccess)
       e = hattn::launch_hisa_topk(p->ia, p->reps, p->B, p->m, p->k, p->idx, nullptr, p->hisa_ws, st);
   }

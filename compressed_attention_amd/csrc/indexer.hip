@@ -2030,11 +2030,12 @@ bool decode_front_ok(const IndexArgs& a, int B, int m, int max_w) {
 hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, void* ws, const int32_t* q_pos,
                                const void* x1, const float* z1, const float* bias1, int w1, int s1, void* y1,
                                int32_t* n_vis1, const void* x2, const float* z2, const float* bias2, int w2, int s2,
-                               void* y2, int64_t N2, int32_t* n_vis2, int64_t L, int C, hipStream_t st) {
+                               void* y2, int64_t N2, int32_t* n_vis2, int64_t L, int C, hipStream_t st,
+                               int raw_rows) {
   const HisaPlan p = plan_hisa(a, B, m);
   float* S1 = reinterpret_cast<float*>(ws);
-  const AppendK la{x1, L, C, z1, bias1, w1, s1, y1, a.n, n_vis1, a.k_i, a.d_i, B, reps};
-  const AppendK lb{x2, L, C, z2, bias2, w2, s2, y2, N2, n_vis2, nullptr, 0, 0, nullptr};
+  const AppendK la{x1, L, C, z1, bias1, w1, s1, y1, a.n, n_vis1, a.k_i, a.d_i, B, reps, raw_rows};
+  const AppendK lb{x2, L, C, z2, bias2, w2, s2, y2, N2, n_vis2, nullptr, 0, 0, nullptr, raw_rows};
   const int nch = int((p.nb + 63) / 64);
   const int nch_grid = int(xcd_grid(1, nch));
   const int nroles = x2 ? 2 : 1;

@@ -53,14 +53,16 @@ hipError_t launch_pool(int dtype, const void* k_i, int64_t bt, int64_t n, int d_
 size_t append_lds_bytes(int dtype, int C, int w, int d_i, bool with_reps);
 // Two layers of the same sequences in one launch: layer 1 (with block means
 // when k_i / reps are given) and layer 2 (entries only).
+// raw_rows: 0 when x and z hold all L rows; R > 0 when they are rings of the
+// newest R rows (row r at slot r % R; R >= w).
 hipError_t launch_append_pair(int dtype, int64_t bt, const int32_t* q_pos, const void* x1, const float* z1,
                               const float* bias1, int w1, int s1, void* y1, int64_t N1, int32_t* n_vis1,
                               const void* k_i, int d_i, int B, float* reps, const void* x2, const float* z2,
                               const float* bias2, int w2, int s2, void* y2, int64_t N2, int32_t* n_vis2, int64_t L,
-                              int C, hipStream_t st);
+                              int C, hipStream_t st, int raw_rows = 0);
 hipError_t launch_append(int dtype, const void* x, int64_t bt, int64_t L, int C, const float* z, const float* bias,
                          int w, int s, const int32_t* q_pos, void* y, int64_t N, int32_t* n_vis, const void* k_i,
-                         int d_i, int B, float* reps, hipStream_t st);
+                         int d_i, int B, float* reps, hipStream_t st, int raw_rows = 0);
 
 // ---- indexer ---------------------------------------------------------------
 struct IndexArgs {
@@ -96,7 +98,8 @@ bool decode_front_ok(const IndexArgs& a, int B, int m, int max_w);
 hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, void* ws, const int32_t* q_pos,
                                const void* x1, const float* z1, const float* bias1, int w1, int s1, void* y1,
                                int32_t* n_vis1, const void* x2, const float* z2, const float* bias2, int w2, int s2,
-                               void* y2, int64_t N2, int32_t* n_vis2, int64_t L, int C, hipStream_t st);
+                               void* y2, int64_t N2, int32_t* n_vis2, int64_t L, int C, hipStream_t st,
+                               int raw_rows = 0);
 
 // ---- attention -------------------------------------------------------------
 struct AttnArgs {
@@ -116,6 +119,7 @@ struct AttnArgs {
   int h, d;
   float* out;
   float* lse;
+  int raw_rows = 0;  // 0: raw_kv holds all L rows; R > 0: a ring of the newest R (row r at slot r % R)
 };
 
 size_t attn_ws_bytes(const AttnArgs& a);

@@ -161,14 +161,17 @@ def visible_count(pos, w: int, stride: int, n_entries: int, out=None):
 
 
 def decode_append(x, logits, pos_bias, w: int, stride: int, q_pos, ckv, k_i=None, reps=None, B: int = 1,
-                  n_vis=None):
+                  n_vis=None, L: int | None = None):
     """Per-token maintenance of one compressed layer for a decode step (one
     query per sequence at q_pos [bt][1]): returns n_vis [bt][1]; rewrites the
     entry of ckv that the token completes and, with k_i / reps, the mean of
-    the HISA block holding it."""
+    the HISA block holding it.  With L given and x [bt][R][C] shorter than
+    L, x and logits are rings of the newest R raw rows (row r at r % R)."""
     _need(x, "x", ndim=3)
     dt = _fdt(x, "x")
-    bt, L, C = x.shape
+    bt, rows, C = x.shape
+    L = rows if L is None else L
+    raw_rows = 0 if rows == L else rows
     _need(q_pos, "q_pos", torch.int32)
     if q_pos.numel() != bt:
         raise ValueError("q_pos must hold one position per sequence")
@@ -189,9 +192,10 @@ def decode_append(x, logits, pos_bias, w: int, stride: int, q_pos, ckv, k_i=None
             raise ValueError("k_i must be [bt][N][d_i] and reps [bt][ceil(N/B)][d_i]")
     if n_vis is None:
         n_vis = torch.empty(q_pos.shape, dtype=torch.int32, device=x.device)
-    check("hattn_decode_append", lib().hattn_decode_append(dt, _ptr(x), bt, L, C, _ptr(logits), _ptr(pos_bias), w,
-                                                           stride, _ptr(q_pos), _ptr(ckv), _ptr(n_vis), _ptr(k_i),
-                                                           d_i, B, _ptr(reps), _stream(x.device)))
+    check("hattn_decode_append", lib().hattn_decode_append(dt, _ptr(x), bt, L, raw_rows, C, _ptr(logits),
+                                                           _ptr(pos_bias), w, stride, _ptr(q_pos), _ptr(ckv),
+                                                           _ptr(n_vis), _ptr(k_i), d_i, B, _ptr(reps),
+                                                           _stream(x.device)))
     return n_vis
 
 
@@ -279,6 +283,14 @@ def block_sparse_topk(q_i, k_i, w_i, n_vis, reps, B: int, m: int, return_blocks:
     return (idx, blk) if return_blocks else idx
 
 
+def _ring_rows(raw_kv, L):
+    """(L, raw_rows) for the attention calls: raw_kv [bt][R][2d] with L given
+    and R < L is a ring of the newest R raw rows (row r at slot r % R)."""
+    rows = raw_kv.shape[1]
+    L = rows if L is None else L
+    return L, (0 if rows == L else rows)
+
+
 def _attn_common(q, ckv, raw_kv, q_pos):
     _need(q, "q", ndim=4)
     dt = _fdt(q, "q")
@@ -293,9 +305,13 @@ def _attn_common(q, ckv, raw_kv, q_pos):
     return dt, bt, nq, h, d
 
 
-def sparse_attn(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = None, return_lse: bool = False):
-    """Attention over ckv[idx] plus the raw window: out [bt][nq][h][d] fp32."""
+def sparse_attn(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = None, return_lse: bool = False,
+                L: int | None = None):
+    """Attention over ckv[idx] plus the raw window: out [bt][nq][h][d] fp32.
+    With L given and raw_kv shorter than L, raw_kv is a ring of the newest
+    raw rows (row r at slot r % R) that holds every row the queries read."""
     dt, bt, nq, h, d = _attn_common(q, ckv, raw_kv, q_pos)
+    L_raw, raw_rows = _ring_rows(raw_kv, L)
     _need(idx, "idx", torch.int32, 3)
     if idx.shape[:2] != (bt, nq):
         raise ValueError("idx must be [bt][nq][k]")
@@ -303,22 +319,24 @@ def sparse_attn(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = N
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out = torch.empty((bt, nq, h, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((bt, nq, h), dtype=torch.float32, device=q.device) if return_lse else None
-    L = lib()
+    lb = lib()
     st = _stream(q.device)
 
     def call(ws, szp):
-        return L.hattn_sparse_attn(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(idx), k, _ptr(raw_kv), raw_kv.shape[1],
-                                   _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out), _ptr(lse), ws, szp, st)
+        return lb.hattn_sparse_attn(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(idx), k, _ptr(raw_kv), L_raw, raw_rows,
+                                    _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out), _ptr(lse), ws, szp, st)
 
     _ws_call("hattn_sparse_attn", ("attn", q.device, st.value), q.device, call)
     return (out, lse) if return_lse else out
 
 
-def sparse_attn_noalloc(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = None, out=None, lse=None):
+def sparse_attn_noalloc(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = None, out=None, lse=None,
+                        L: int | None = None):
     """sparse_attn through the entry point that allocates nothing (the
     library's static scratch instead of a workspace).  Pass out (and lse) to
     keep the call free of allocations on the torch side too."""
     dt, bt, nq, h, d = _attn_common(q, ckv, raw_kv, q_pos)
+    L_raw, raw_rows = _ring_rows(raw_kv, L)
     _need(idx, "idx", torch.int32, 3)
     if idx.shape[:2] != (bt, nq):
         raise ValueError("idx must be [bt][nq][k]")
@@ -330,26 +348,28 @@ def sparse_attn_noalloc(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | 
         _need(lse, "lse", torch.float32, 3)
     check("hattn_sparse_attn_noalloc",
           lib().hattn_sparse_attn_noalloc(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(idx), idx.shape[2], _ptr(raw_kv),
-                                          raw_kv.shape[1], _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out),
+                                          L_raw, raw_rows, _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out),
                                           _ptr(lse), _stream(q.device)))
     return out
 
 
 def dense_compressed_attn(q, ckv, n_vis, raw_kv, q_pos, window: int, scale: float | None = None,
-                          return_lse: bool = False):
-    """Attention over ckv[0 .. n_vis) plus the raw window: out [bt][nq][h][d] fp32."""
+                          return_lse: bool = False, L: int | None = None):
+    """Attention over ckv[0 .. n_vis) plus the raw window: out [bt][nq][h][d]
+    fp32 (raw_kv as in sparse_attn, a ring when L is given and longer)."""
     dt, bt, nq, h, d = _attn_common(q, ckv, raw_kv, q_pos)
+    L_raw, raw_rows = _ring_rows(raw_kv, L)
     _need(n_vis, "n_vis", torch.int32, 2)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out = torch.empty((bt, nq, h, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((bt, nq, h), dtype=torch.float32, device=q.device) if return_lse else None
-    L = lib()
+    lb = lib()
     st = _stream(q.device)
 
     def call(ws, szp):
-        return L.hattn_dense_compressed_attn(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(n_vis), _ptr(raw_kv),
-                                             raw_kv.shape[1], _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out),
-                                             _ptr(lse), ws, szp, st)
+        return lb.hattn_dense_compressed_attn(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(n_vis), _ptr(raw_kv),
+                                              L_raw, raw_rows, _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out),
+                                              _ptr(lse), ws, szp, st)
 
     _ws_call("hattn_dense_compressed_attn", ("attn", q.device, st.value), q.device, call)
     return (out, lse) if return_lse else out
@@ -391,7 +411,8 @@ class DecodePlan:
     def __init__(self, *, q_pos, csa_raw_kv, csa_logits, csa_pos_bias, csa_ckv, k_i, reps, q_i, w_i, csa_q,
                  hca_raw_kv, hca_logits, hca_pos_bias, hca_ckv, hca_q, B: int, m: int, k: int, csa_w: int = 8,
                  csa_stride: int = 4, hca_w: int = 128, hca_stride: int = 128, window: int = 128,
-                 scale: float | None = None, return_lse: bool = False, return_idx: bool = False):
+                 scale: float | None = None, return_lse: bool = False, return_idx: bool = False,
+                 L: int | None = None):
         from ._lib import DecodeDesc
 
         self._plan = None
@@ -402,12 +423,16 @@ class DecodePlan:
         _need(q_pos, "q_pos", torch.int32)
         _need(reps, "reps", torch.float32, 3)
         _need(w_i, "w_i", torch.float32)
-        bt, L, C = csa_raw_kv.shape
+        bt, rows, C = csa_raw_kv.shape
+        # with L given and fewer raw rows than L, the raw arrays are rings of
+        # the newest rows (row r at slot r % rows)
+        L = rows if L is None else L
+        raw_rows = 0 if rows == L else rows
         h, d = csa_q.shape[-2], csa_q.shape[-1]
         if q_pos.numel() != bt or csa_q.numel() != bt * h * d or hca_q.numel() != bt * h * d:
             raise ValueError("one query per sequence: q_pos [bt][1], csa_q / hca_q [bt][1][h][d]")
-        if C != 2 * d or tuple(hca_raw_kv.shape) != (bt, L, C):
-            raise ValueError("raw K|V rows must be [bt][L][2d] for both branches")
+        if C != 2 * d or tuple(hca_raw_kv.shape) != (bt, rows, C):
+            raise ValueError("raw K|V rows must be [bt][rows][2d] for both branches")
         h_i, d_i = q_i.shape[-2], q_i.shape[-1]
         if q_i.numel() != bt * h_i * d_i or w_i.numel() != bt * h_i:
             raise ValueError("q_i must be [bt][1][h_i][d_i] and w_i [bt][1][h_i]")
@@ -425,7 +450,8 @@ class DecodePlan:
         self._keep = [q_pos, csa_raw_kv, csa_logits, csa_pos_bias, csa_ckv, k_i, reps, q_i, w_i, csa_q, hca_raw_kv,
                       hca_logits, hca_pos_bias, hca_ckv, hca_q]
         self.device = dev
-        desc = DecodeDesc(dtype=dt, h=h, d=d, window=window, bt=bt, L=L, scale=scale, h_i=h_i, d_i=d_i, B=B, m=m,
+        desc = DecodeDesc(dtype=dt, h=h, d=d, window=window, bt=bt, L=L, raw_rows=raw_rows, scale=scale, h_i=h_i,
+                          d_i=d_i, B=B, m=m,
                           k=k, csa_w=csa_w, csa_stride=csa_stride, hca_w=hca_w, hca_stride=hca_stride,
                           q_pos=_ptr(q_pos), csa_raw_kv=_ptr(csa_raw_kv), csa_logits=_ptr(csa_logits),
                           csa_pos_bias=_ptr(csa_pos_bias), csa_ckv=_ptr(csa_ckv), k_i=_ptr(k_i), reps=_ptr(reps),

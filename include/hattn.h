@@ -68,7 +68,8 @@ typedef enum { HATTN_F32 = 0, HATTN_BF16 = 1 } hattn_dtype_t;
 const char* hattn_status_string(int status);
 /* Detail for the calling thread's last failing call (static thread storage). */
 const char* hattn_last_error(void);
-/* Version of this ABI (bumped on incompatible changes; 2: hattn_decode_desc gained csa_idx). */
+/* Version of this ABI (bumped on incompatible changes; 2: hattn_decode_desc gained csa_idx; 3: raw_rows
+ * (raw K|V rings) in hattn_decode_desc, hattn_decode_append and the attention calls). */
 int hattn_abi_version(void);
 
 /*
@@ -230,6 +231,11 @@ hattn_status_t hattn_block_sparse_topk(int dtype, const void* q_i, const void* k
  *   q      [bt][nq][h][d] dtype      ckv [bt][n][2d] dtype (K | V per entry)
  *   idx    [bt][nq][k] int32; entries < 0 or >= n are skipped
  *   raw_kv [bt][L][2d] dtype         q_pos [bt][nq] int32, 0 <= p < L
+ *          or, with raw_rows = R > 0, a ring [bt][R][2d] of the newest
+ *          rows (row r at slot r % R; window <= R <= L): it must hold every
+ *          row a query reads, max(0, p - window + 1) .. p for each q_pos p
+ *          of the sequence (the device cannot check this).  raw_rows = 0:
+ *          all L rows.
  *   out    [bt][nq][h][d] fp32 out   lse [bt][nq][h] fp32 out or NULL
  * Requires window >= 1 and d a multiple of 8.  bf16 with d in {64, 128}
  * and h in {16, 32} or a multiple of 64 up to 1,024 runs on MFMA (64 heads
@@ -240,7 +246,7 @@ hattn_status_t hattn_block_sparse_topk(int dtype, const void* q_i, const void* k
  * g*h_layer + j of q, out and lse.
  */
 hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx,
-                                 int32_t k, const void* raw_kv, int64_t L, const int32_t* q_pos,
+                                 int32_t k, const void* raw_kv, int64_t L, int64_t raw_rows, const int32_t* q_pos,
                                  int32_t window, float scale, int64_t bt, int64_t nq, int32_t h, int32_t d,
                                  float* out, float* lse, void* ws, size_t* ws_bytes, void* stream);
 
@@ -260,9 +266,9 @@ hattn_status_t hattn_sparse_attn(int dtype, const void* q, const void* ckv, int6
  *     between calls (every partial is written before it is read).
  */
 hattn_status_t hattn_sparse_attn_noalloc(int dtype, const void* q, const void* ckv, int64_t n, const int32_t* idx,
-                                         int32_t k, const void* raw_kv, int64_t L, const int32_t* q_pos,
-                                         int32_t window, float scale, int64_t bt, int64_t nq, int32_t h, int32_t d,
-                                         float* out, float* lse, void* stream);
+                                         int32_t k, const void* raw_kv, int64_t L, int64_t raw_rows,
+                                         const int32_t* q_pos, int32_t window, float scale, int64_t bt, int64_t nq,
+                                         int32_t h, int32_t d, float* out, float* lse, void* stream);
 
 /*
  * hattn_dense_compressed_attn -- HCA attention: every visible entry plus window.
@@ -272,7 +278,7 @@ hattn_status_t hattn_sparse_attn_noalloc(int dtype, const void* q, const void* c
  * with n_vis [bt][nq] int32 (clamped to [0, n]) in place of idx and k.
  */
 hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void* ckv, int64_t n,
-                                           const int32_t* n_vis, const void* raw_kv, int64_t L,
+                                           const int32_t* n_vis, const void* raw_kv, int64_t L, int64_t raw_rows,
                                            const int32_t* q_pos, int32_t window, float scale, int64_t bt,
                                            int64_t nq, int32_t h, int32_t d, float* out, float* lse, void* ws,
                                            size_t* ws_bytes, void* stream);
@@ -290,8 +296,13 @@ hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void*
  * Sources: [HCA] section 怎么压 (each entry is a weighted merge of its run
  * of raw entries), [HISA] section 02, first stage (one pooled representative
  * per block), and the causal visibility of hattn_visible_count.
- *   raw_kv   [bt][L][C]      dtype; K|V rows as in hattn_compress
- *   logits   [bt][L] fp32 or NULL; pos_bias [w] fp32 or NULL
+ *   raw_kv   [bt][L][C]      dtype; K|V rows as in hattn_compress, or, with
+ *                            raw_rows = R > 0, a ring [bt][R][C] holding the
+ *                            newest R rows: row r at slot r % R (the caller
+ *                            writes each new token's row before the call;
+ *                            w <= R <= L).  A decode step needs only the
+ *                            rows of the newest windows, not the prefix.
+ *   logits   [bt][L] fp32 or NULL ([bt][R] with a ring); pos_bias [w] or NULL
  *   q_pos    [bt] int32      any values (positions that complete no entry
  *                            only get their visible count)
  *   ckv      [bt][N][C]      N = (L - w) / stride + 1; entry e rewritten
@@ -302,8 +313,8 @@ hattn_status_t hattn_dense_compressed_attn(int dtype, const void* q, const void*
  * at most 256 16-byte pieces per row.  Errors: HATTN_ERR_ARG for bad sizes,
  * NULL required pointers or an inconsistent k_i / reps pair.
  */
-hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, int64_t L, int32_t C,
-                                   const float* logits, const float* pos_bias, int32_t w, int32_t stride,
+hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, int64_t L, int64_t raw_rows,
+                                   int32_t C, const float* logits, const float* pos_bias, int32_t w, int32_t stride,
                                    const int32_t* q_pos, void* ckv, int32_t* n_vis, const void* k_i, int32_t d_i,
                                    int32_t B, float* reps, void* stream);
 
@@ -329,6 +340,11 @@ hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, in
  * hattn_decode_desc (all arrays as documented for the calls above; the two
  * branches share bt, L, h, d, window, scale and q_pos):
  *   dtype, bt, L, h, d, window, scale, q_pos [bt] int32
+ *   raw_rows: 0 when csa_raw_kv / hca_raw_kv ([bt][L][2d]) and the logits
+ *     ([bt][L]) hold every raw row; R > 0 when they are rings of the newest
+ *     R rows ([bt][R][2d], [bt][R]; row r at slot r % R; R >= window and
+ *     both compression windows): the caller writes the new token's rows and
+ *     logits at slot q_pos[b] % R before each step
  *   csa_raw_kv, csa_logits, csa_pos_bias, csa_w, csa_stride, csa_ckv
  *     ([bt][N][2d], N = (L - csa_w) / csa_stride + 1; rewritten in place)
  *   k_i [bt][N][d_i], reps [bt][ceil(N/B)][d_i] fp32 (rewritten in place),
@@ -360,6 +376,7 @@ typedef struct hattn_decode_desc {
   int32_t dtype;
   int32_t h, d, window;
   int64_t bt, L;
+  int64_t raw_rows;
   float scale;
   int32_t h_i, d_i, B, m, k;
   int32_t csa_w, csa_stride, hca_w, hca_stride;

@@ -58,7 +58,7 @@ def test_decode_append_validation(L):
     f = L.hattn_decode_append
     p = ctypes.c_void_p(16)
     args = lambda **kw: [kw.get(n, d) for n, d in [
-        ("dt", 1), ("x", p), ("bt", 2), ("L", 100), ("C", 256), ("z", None), ("b", None), ("w", 8), ("s", 4),
+        ("dt", 1), ("x", p), ("bt", 2), ("L", 100), ("R", 0), ("C", 256), ("z", None), ("b", None), ("w", 8), ("s", 4),
         ("qp", p), ("y", p), ("nv", p), ("ki", None), ("di", 0), ("B", 0), ("reps", None), ("st", None)]]
     assert f(*args(dt=5)) == 1
     assert f(*args(C=250)) == 1                      # not a multiple of 8 bf16 elements
@@ -73,6 +73,12 @@ def test_decode_append_validation(L):
     assert f(*args(y=None)) == 1
     assert b"NULL" in L.hattn_last_error()
     assert f(*args(bt=0, x=None, qp=None, y=None, nv=None)) == 0  # nothing to do
+    # a ring of raw rows must hold the window and no more than L rows
+    assert f(*args(R=4)) == 1
+    assert b"ring" in L.hattn_last_error()
+    assert f(*args(R=101)) == 1
+    assert f(*args(R=-1)) == 1
+    assert f(*args(R=8, bt=0, x=None, qp=None, y=None, nv=None)) == 0
 
 
 def _sz():
@@ -117,16 +123,32 @@ def test_attention_validation(L):
     p = ctypes.c_void_p(16)
     sz = _sz()
     f = L.hattn_dense_compressed_attn
-    assert f(1, p, p, 100, p, p, 1000, p, 0, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1  # window
-    assert f(1, p, p, 100, p, p, 1000, p, 128, -1.0, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
-    assert f(1, p, p, 100, p, p, 1000, p, 128, 0.1, 1, 1, 64, 12, p, None, None, ctypes.byref(sz), None) == 1
-    assert f(1, p, p, 100, None, p, 1000, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
-    assert f(1, p, p, 100, p, p, 1000, p, 128, 0.1, 1, 1, 2048, 128, p, None, None, ctypes.byref(sz), None) == 2
+    # arguments: dtype q ckv n n_vis raw_kv L raw_rows q_pos window scale bt nq h d out lse ws ws_bytes stream
+    assert f(1, p, p, 100, p, p, 1000, 0, p, 0, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1  # window
+    assert f(1, p, p, 100, p, p, 1000, 0, p, 128, -1.0, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert f(1, p, p, 100, p, p, 1000, 0, p, 128, 0.1, 1, 1, 64, 12, p, None, None, ctypes.byref(sz), None) == 1
+    assert f(1, p, p, 100, None, p, 1000, 0, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert f(1, p, p, 100, p, p, 1000, 0, p, 128, 0.1, 1, 1, 2048, 128, p, None, None, ctypes.byref(sz), None) == 2
     # long key lists are split: the partials need a workspace
-    assert f(1, p, p, 8192, p, p, 1 << 20, p, 128, 0.1, 32, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 0
+    assert f(1, p, p, 8192, p, p, 1 << 20, 0, p, 128, 0.1, 32, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 0
     assert sz.value > 0
+    # a raw ring must hold at least the window and at most L rows
+    assert f(1, p, p, 8192, p, p, 1 << 20, 127, p, 128, 0.1, 32, 1, 64, 128, p, None, None, ctypes.byref(sz),
+             None) == 1
+    assert b"ring" in L.hattn_last_error()
+    assert f(1, p, p, 100, p, p, 1000, 1001, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert f(1, p, p, 100, p, p, 1000, -1, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert f(1, p, p, 8192, p, p, 1 << 20, 1 << 40, p, 128, 0.1, 32, 1, 64, 128, p, None, None, ctypes.byref(sz),
+             None) == 1
+    assert f(1, p, p, 8192, p, p, 1 << 20, 128, p, 128, 0.1, 32, 1, 64, 128, p, None, None, ctypes.byref(sz),
+             None) == 0
     g = L.hattn_sparse_attn
-    assert g(1, p, p, 100, None, 8, p, 1000, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert g(1, p, p, 100, None, 8, p, 1000, 0, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert g(1, p, p, 100, p, 8, p, 1000, 64, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 1
+    assert g(1, p, p, 100, p, 8, p, 1000, 200, p, 128, 0.1, 1, 1, 64, 128, p, None, None, ctypes.byref(sz), None) == 0
+    n = L.hattn_sparse_attn_noalloc
+    assert n(1, p, p, 100, p, 8, p, 1000, 64, p, 128, ctypes.c_float(0.1), 1, 1, 64, 128, p, None, None) == 1
+    assert b"ring" in L.hattn_last_error()
 
 
 def test_decode_plan_validation(L):
@@ -166,11 +188,11 @@ def test_sparse_attn_noalloc_rejects_oversize(L):
     # 32 MiB static scratch: refused before any launch.
     f = L.hattn_sparse_attn_noalloc
     p = ctypes.c_void_p(256)
-    st = f(0, p, p, 4000, p, 2048, p, 9000, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p, None, None)
+    st = f(0, p, p, 4000, p, 2048, p, 9000, 0, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p, None, None)
     assert st == 3, L.hattn_last_error()
     assert b"static" in L.hattn_last_error()
     # the same call with a workspace would need more than 32 MiB
     sz = ctypes.c_size_t(0)
-    assert L.hattn_sparse_attn(0, p, p, 4000, p, 2048, p, 9000, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p,
+    assert L.hattn_sparse_attn(0, p, p, 4000, p, 2048, p, 9000, 0, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p,
                                None, None, ctypes.byref(sz), None) == 0
     assert sz.value > 32 << 20

@@ -177,3 +177,49 @@ def test_long_chunks_ragged(d):
         ro, rl = oracle.sparse_attention(f64(q[b]), f64(ckv[b]), ii, f64(raw[b]), pos[b].numpy(), 128,
                                          1 / math.sqrt(d))
         _check(out_s[b], lse_s[b], ro, rl)
+
+
+def _ring_of(raw, R, last):
+    """Rows last-R+1 .. last of raw [bt][L][C] at slots r % R (rows < 0
+    left as NaN: nothing may read them)."""
+    out = torch.full((raw.shape[0], R, raw.shape[2]), float("nan"), dtype=raw.dtype, device=raw.device)
+    rows = torch.arange(max(0, last - R + 1), last + 1, device=raw.device)
+    out[:, rows % R] = raw[:, rows]
+    return out
+
+
+@pytest.mark.parametrize("h,d,dt", [(64, 128, torch.bfloat16), (128, 64, torch.bfloat16), (24, 64, torch.bfloat16),
+                                    (16, 64, torch.float32)])
+def test_ring_window_reads_match_full(h, d, dt):
+    """Both attention calls reading the window from a ring of the newest
+    R raw rows give bit-for-bit what they give from all L rows: a chunk of
+    queries whose windows straddle the ring's wrap, and one sequence still
+    inside its first window."""
+    bt, L, N, k, R = 2, 5000, 1249, 64, 256
+    raw = synth.normal((bt, L, 2 * d), 90, dtype=dt).to(DEV)
+    ckv = synth.normal((bt, N, 2 * d), 91, dtype=dt).to(DEV)
+    q = synth.normal((bt, 13, h, d), 92, dtype=dt).to(DEV)
+    # sequence 0: positions 3000 .. 3120 (their windows reach back to 2873;
+    # slot 0 holds row 3072); sequence 1: positions 0 .. 120
+    p0 = [3000, 3001, 3010, 3071, 3072, 3073, 3090, 3100, 3110, 3117, 3118, 3119, 3120]
+    p1 = [0, 1, 2, 5, 63, 64, 100, 111, 112, 113, 118, 119, 120]
+    pos = torch.tensor([p0, p1], dtype=torch.int32, device=DEV)
+    ring = torch.stack([_ring_of(raw[b:b + 1], R, max(pp))[0] for b, pp in enumerate((p0, p1))])
+    nv = ops.visible_count(pos, 8, 4, N)
+    idx = torch.stack([synth.random_index_lists(nv.cpu()[b], k, seed=93 + b, n_pad_holes=2) for b in range(bt)])
+    idx = idx.reshape(bt, 13, k).to(DEV)
+    o_full, l_full = ops.sparse_attn(q, ckv, idx, raw, pos, 128, return_lse=True)
+    o_ring, l_ring = ops.sparse_attn(q, ckv, idx, ring, pos, 128, return_lse=True, L=L)
+    n_full = ops.sparse_attn_noalloc(q, ckv, idx, raw, pos, 128)
+    n_ring = ops.sparse_attn_noalloc(q, ckv, idx, ring, pos, 128, L=L)
+    d_full, dl_full = ops.dense_compressed_attn(q, ckv, nv, raw, pos, 128, return_lse=True)
+    d_ring, dl_ring = ops.dense_compressed_attn(q, ckv, nv, ring, pos, 128, return_lse=True, L=L)
+    torch.cuda.synchronize()
+    for a, b in ((o_full, o_ring), (l_full, l_ring), (n_full, n_ring), (d_full, d_ring), (dl_full, dl_ring)):
+        assert torch.isfinite(b).all()
+        assert torch.equal(a, b)
+    # and the full-array results are the oracle's
+    for b, pp in enumerate((p0, p1)):
+        ro, rl = oracle.sparse_attention(f64(q[b]), f64(ckv[b]), idx[b].cpu().numpy(), f64(raw[b]), np.array(pp),
+                                         128, 1 / math.sqrt(d))
+        _check(o_ring[b], l_ring[b], ro, rl)

@@ -1,10 +1,11 @@
 """GPU parity of the decode step at the size the benchmark times.
 
 Hybrid layer pair at 1M context: 8 sequences of 2^20 raw tokens, one query
-each at position L - 1; CSA 262,143 entries (HISA B = 128, m = 64, k in
-{2048, 512}) and HCA 8,192 entries; 64 heads x 128, window 128.  The native
-decode plan runs the step (cache maintenance of both layers, HISA, sparse and
-dense attention); its outputs are checked against the oracle:
+each at position L - 1, the raw rows either whole or as 128-row rings; CSA
+262,143 entries (HISA B = 128, m = 64, k in {2048, 512}) and HCA 8,192
+entries; 64 heads x 128, window 128.  The native decode plan runs the step
+(cache maintenance of both layers, HISA, sparse and dense attention); its
+outputs are checked against the oracle:
 
   - the CSA selection, bit-exact: the indexer is drawn on the integer grid
     [-4, 4] with 4-bit dyadic head weights, so every fp32 score on both sides
@@ -53,7 +54,15 @@ def full():
     return dict(t=t, ckv=ckv, hkv=hkv, reps=reps, hca_ref=None)
 
 
-def _run_plan(F, k):
+def _ring(x, R):
+    """The newest R rows of x [BT, L, ...] at slots r % R."""
+    rows = torch.arange(L - R, L, device=x.device)
+    out = torch.empty((x.shape[0], R) + tuple(x.shape[2:]), dtype=x.dtype, device=x.device)
+    out[:, rows % R] = x[:, rows]
+    return out
+
+
+def _run_plan(F, k, ring=0):
     t = F["t"]
     ckv, hkv, reps = F["ckv"], F["hkv"], F["reps"]
     # the state before the step: the entries (and block mean) that the new
@@ -61,10 +70,12 @@ def _run_plan(F, k):
     ckv[:, N - 1] = 0
     hkv[:, NH - 1] = 0
     reps[:, -1] = 0
-    plan = ops.DecodePlan(q_pos=t["q_pos"], csa_raw_kv=t["csa_raw_kv"], csa_logits=t["csa_z"],
+    raw = {n: (_ring(t[n], ring) if ring else t[n]) for n in ("csa_raw_kv", "csa_z", "hca_raw_kv", "hca_z")}
+    plan = ops.DecodePlan(q_pos=t["q_pos"], csa_raw_kv=raw["csa_raw_kv"], csa_logits=raw["csa_z"],
                           csa_pos_bias=t["csa_b"], csa_ckv=ckv, k_i=t["k_i"], reps=reps, q_i=t["q_i"], w_i=t["w_i"],
-                          csa_q=t["csa_q"], hca_raw_kv=t["hca_raw_kv"], hca_logits=t["hca_z"],
-                          hca_pos_bias=t["hca_b"], hca_ckv=hkv, hca_q=t["hca_q"], B=B, m=M, k=k, return_idx=True)
+                          csa_q=t["csa_q"], hca_raw_kv=raw["hca_raw_kv"], hca_logits=raw["hca_z"],
+                          hca_pos_bias=t["hca_b"], hca_ckv=hkv, hca_q=t["hca_q"], B=B, m=M, k=k, return_idx=True,
+                          L=L if ring else None)
     plan.run()
     torch.cuda.synchronize()
     out = (plan.csa_idx[:, 0].cpu().numpy(), f64(plan.csa_out[:, 0]), f64(plan.hca_out[:, 0]))
@@ -92,11 +103,13 @@ def _selected_entries(raw_kv_b, z_b, bias, ent):
     return oracle.compress(x, z, bias, 8, 8)
 
 
-@pytest.mark.parametrize("k", [2048, 512])
-def test_decode_plan_full_size_matches_oracle(full, k):
+@pytest.mark.parametrize("k,ring", [(2048, 0), (512, 0), (2048, 128)])
+def test_decode_plan_full_size_matches_oracle(full, k, ring):
+    """ring=128: the plan reads only the newest 128 raw rows of each layer,
+    kept at slots r % 128 (the configuration the benchmark times)."""
     t = full["t"]
-    _say(f"k={k}: running the decode plan")
-    idx, o_csa, o_hca = _run_plan(full, k)
+    _say(f"k={k} ring={ring}: running the decode plan")
+    idx, o_csa, o_hca = _run_plan(full, k, ring)
     sc = 1 / math.sqrt(128)
     p = L - 1
     assert (t["q_pos"].cpu().numpy() == p).all()

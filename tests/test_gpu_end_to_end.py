@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from compressed_attention_amd import ops, synth
-from helpers import f64
+from helpers import assert_bf16_close, f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -254,3 +254,81 @@ def test_csa2_layer_group(nq, w, s):
         assert np.array_equal(idx[bb].cpu().numpy(), r_idx), bb
         got = f64(out[bb]).reshape(nq, G, H, d).transpose(1, 0, 2, 3)
         assert np.abs(got - r_o).max() < 1e-2, (bb, float(np.abs(got - r_o).max()))
+
+
+def test_decode_plan_ring_multi_step():
+    # A decode loop of 130 steps (positions 3500 .. 3629): both layers' raw
+    # K|V rows and logits live in 128-row rings (before each step the
+    # caller writes the new token's rows at slot p % 128), and the caches
+    # grow by the plan's own appends.  The run crosses CSA-entry (every 4
+    # tokens), HCA-entry (p = 3583) and HISA-block (entry 896, p = 3591)
+    # boundaries.  Checked against the oracle on the whole raw prefix every
+    # 8 steps and at the boundaries; a second plan on the full raw arrays
+    # must give the same bits at every step.
+    bt, L, R, B, m, k = 2, 4096, 128, 128, 4, 128
+    N, Nh = oracle.n_entries(L, 8, 4), oracle.n_entries(L, 128, 128)
+    w = synth.hybrid_pair_decode(3, device="cpu", bt=bt, L=L, N_csa=N)
+    t = dict(w.tensors)
+    t["q_i"] = synth.int_grid((bt, 1, 16, 128), 351, -4, 4, dtype=torch.bfloat16)
+    t["k_i"] = synth.int_grid((bt, N, 128), 352, -4, 4, dtype=torch.bfloat16)
+    t["w_i"] = synth.dyadic_uniform((bt, 1, 16), 353, bits=4)
+    g = {k_: v.to(DEV) for k_, v in t.items()}
+    p0, T = 3500, 130
+    nv0, nvh0 = oracle.n_visible(p0 - 1, 8, 4, N), oracle.n_visible(p0 - 1, 128, 128, Nh)
+    caches = []
+    for _ in range(2):  # ring plan, full plan
+        ckv = ops.compress(g["csa_raw_kv"], g["csa_z"], g["csa_b"], 8, 4)
+        hkv = ops.compress(g["hca_raw_kv"], g["hca_z"], g["hca_b"], 128, 128)
+        ckv[:, nv0:] = 0
+        hkv[:, nvh0:] = 0
+        caches.append((ckv, hkv, ops.hisa_pool(g["k_i"], B)))
+    rings = {n: torch.zeros((bt, R) + tuple(g[n].shape[2:]), dtype=g[n].dtype, device=DEV)
+             for n in ("csa_raw_kv", "hca_raw_kv", "csa_z", "hca_z")}
+    for r in range(p0 - R, p0):
+        for n, ring in rings.items():
+            ring[:, r % R] = g[n][:, r]
+    q_pos = torch.full((bt, 1), p0, dtype=torch.int32, device=DEV)
+    common = dict(csa_pos_bias=g["csa_b"], hca_pos_bias=g["hca_b"], k_i=g["k_i"], q_i=g["q_i"], w_i=g["w_i"],
+                  csa_q=g["csa_q"], hca_q=g["hca_q"], B=B, m=m, k=k, return_idx=True, q_pos=q_pos)
+    ring_plan = ops.DecodePlan(csa_raw_kv=rings["csa_raw_kv"], csa_logits=rings["csa_z"], hca_raw_kv=rings["hca_raw_kv"],
+                               hca_logits=rings["hca_z"], csa_ckv=caches[0][0], hca_ckv=caches[0][1], reps=caches[0][2],
+                               L=L, **common)
+    full_plan = ops.DecodePlan(csa_raw_kv=g["csa_raw_kv"], csa_logits=g["csa_z"], hca_raw_kv=g["hca_raw_kv"],
+                               hca_logits=g["hca_z"], csa_ckv=caches[1][0], hca_ckv=caches[1][1], reps=caches[1][2],
+                               **common)
+    sc = 1 / math.sqrt(128)
+    r_ckv = [oracle.compress(f64(t["csa_raw_kv"][b]), f64(t["csa_z"][b]), f64(t["csa_b"]), 8, 4) for b in range(bt)]
+    r_hkv = [oracle.compress(f64(t["hca_raw_kv"][b]), f64(t["hca_z"][b]), f64(t["hca_b"]), 128, 128) for b in range(bt)]
+    checked = 0
+    for p in range(p0, p0 + T):
+        for n, ring in rings.items():
+            ring[:, p % R] = g[n][:, p]
+        q_pos.fill_(p)
+        o_r = [x.clone() for x in ring_plan.run()] + [ring_plan.csa_idx.clone()]
+        o_f = [x.clone() for x in full_plan.run()] + [full_plan.csa_idx.clone()]
+        for a, b_ in zip(o_r, o_f):
+            assert torch.equal(a, b_), p
+        if (p - p0) % 8 and p not in (3503, 3583, 3591):
+            continue
+        torch.cuda.synchronize()
+        nv, nvh = oracle.n_visible(p, 8, 4, N), oracle.n_visible(p, 128, 128, Nh)
+        for b in range(bt):
+            r_idx, _ = oracle.hisa_topk(f64(t["q_i"][b]), f64(t["k_i"][b]), f64(t["w_i"][b]), np.array([nv]), B, m, k)
+            assert np.array_equal(o_r[2][b].cpu().numpy(), r_idx), (p, b)
+            r_o1, _ = oracle.sparse_attention(f64(t["csa_q"][b]), r_ckv[b], r_idx, f64(t["csa_raw_kv"][b]),
+                                              np.array([p]), 128, sc)
+            r_o2, _ = oracle.dense_compressed_attention(f64(t["hca_q"][b]), r_hkv[b], [nvh], f64(t["hca_raw_kv"][b]),
+                                                        np.array([p]), 128, sc)
+            assert np.abs(f64(o_r[0][b]) - r_o1).max() < 1e-2, (p, b)
+            assert np.abs(f64(o_r[1][b]) - r_o2).max() < 1e-2, (p, b)
+        checked += 1
+    torch.cuda.synchronize()
+    # the entries the loop completed, appended from the rings
+    nv_end, nvh_end = oracle.n_visible(p0 + T - 1, 8, 4, N), oracle.n_visible(p0 + T - 1, 128, 128, Nh)
+    assert nvh_end == nvh0 + 1 and nv_end > nv0 + 30
+    for b in range(bt):
+        assert_bf16_close(f64(caches[0][0][b, nv0:nv_end]), r_ckv[b][nv0:nv_end])
+        assert_bf16_close(f64(caches[0][1][b, nvh0:nvh_end]), r_hkv[b][nvh0:nvh_end])
+    assert checked >= 18
+    ring_plan.close()
+    full_plan.close()
