@@ -164,6 +164,26 @@ def step_distribution(run_step, n):
                 p90=float(np.percentile(us, 90)), mean=float(us.mean()))
 
 
+RING = 128
+
+
+def keep_rings(t, L):
+    """Replaces the raw K|V and logits of both layers by rings of their
+    newest RING rows (row r at slot r % RING), as a decode loop keeps them:
+    the full prefix only builds the caches."""
+    import torch
+
+    for n in ("csa_raw_kv", "hca_raw_kv", "csa_z", "hca_z"):
+        full = t[n]
+        ring = torch.empty((full.shape[0], RING) + tuple(full.shape[2:]), dtype=full.dtype, device=full.device)
+        rows = torch.arange(L - RING, L, device=full.device)
+        ring[:, rows % RING] = full[:, rows]
+        t[n] = ring
+        del full
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def flat_decode_step(args, t, caches, k):
     """The same decode step with the flat indexer in place of HISA (scores
     every one of the 262,143 visible entries of each query), as one graph
@@ -206,19 +226,7 @@ def hybrid_pair(args):
     torch.cuda.synchronize()
     assert ckv.shape[1] == N and hkv.shape[1] == Nh
     nb = reps.shape[1]
-    # The decode step keeps only the newest 128 raw rows and logits of each
-    # layer, as rings (row r at slot r % 128): the full prefix only built the
-    # caches above.
-    RING = 128
-    for n in ("csa_raw_kv", "hca_raw_kv", "csa_z", "hca_z"):
-        full = t[n]
-        ring = torch.empty((bt, RING) + tuple(full.shape[2:]), dtype=full.dtype, device=dev)
-        rows = torch.arange(L - RING, L, device=dev)
-        ring[:, rows % RING] = full[:, rows]
-        t[n] = ring
-        del full
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
+    keep_rings(t, L)
     R = args.replicas
     caches = [dict(ckv=ckv, hkv=hkv, k_i=t["k_i"], reps=reps)]
     for _ in range(R - 1):
@@ -623,17 +631,19 @@ def probe_decode_plan(args):
     dev = "cuda:0"
     bt, L, N, B, m = 8, 1 << 20, 262143, 128, 64
     W = synth.hybrid_pair_decode(0, device=dev, bt=bt, L=L, N_csa=N)
-    t = W.tensors
+    t = dict(W.tensors)
     ckv = ops.compress(t["csa_raw_kv"], t["csa_z"], t["csa_b"], 8, 4)
     hkv = ops.compress(t["hca_raw_kv"], t["hca_z"], t["hca_b"], 128, 128)
     reps = ops.hisa_pool(t["k_i"], B)
+    keep_rings(t, L)
     plans = []
     for r in range(args.replicas):
         c = (ckv, hkv, reps) if r == 0 else (ckv.clone(), hkv.clone(), reps.clone())
         plans.append(ops.DecodePlan(q_pos=t["q_pos"], csa_raw_kv=t["csa_raw_kv"], csa_logits=t["csa_z"],
                                     csa_pos_bias=t["csa_b"], csa_ckv=c[0], k_i=t["k_i"], reps=c[2], q_i=t["q_i"],
                                     w_i=t["w_i"], csa_q=t["csa_q"], hca_raw_kv=t["hca_raw_kv"], hca_logits=t["hca_z"],
-                                    hca_pos_bias=t["hca_b"], hca_ckv=c[1], hca_q=t["hca_q"], B=B, m=m, k=args.k))
+                                    hca_pos_bias=t["hca_b"], hca_ckv=c[1], hca_q=t["hca_q"], B=B, m=m, k=args.k,
+                                    L=L))
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
