@@ -1527,11 +1527,13 @@ __global__ __launch_bounds__(kSelNT) void select_merge_kernel(const uint32_t* __
 // 64-key tile, packed (sample position i is cache key
 // (i / 64) * 64 * tstride + i % 64).  With v visible keys of which the
 // sample holds s, the threshold is the sample key of rank
-// r = max(2 k s / v, 64) (at most s): about 2k keys of the whole row are
-// expected at or above it, and at least k with overwhelming probability for
-// any row whose scores do not depend on the key's position modulo the
-// stride.  Rows with v <= k, or a sample of at most r keys, take every key
-// (threshold key 0).  Also clears the row's chunk counts.
+// r = max(2 k s / v, floor) (at most s): about max(2k, floor v / s) keys of
+// the whole row are expected at or above it.  The floor, 64 or less when
+// 64 v / s would pass half the candidate select's capacity (4,096), keeps
+// the rank's relative spread small: at least k keys pass with overwhelming
+// probability for any row whose scores do not depend on the key's position
+// modulo the stride.  Rows with v <= k, or a sample of at most r keys, take
+// every key (threshold key 0).  Also clears the row's chunk counts.
 constexpr int kThrNT = 256;
 __global__ __launch_bounds__(kThrNT) void flat_threshold_kernel(const float* __restrict__ Ssamp, int64_t lds,
                                                                 const int32_t* __restrict__ n_vis, int64_t n,
@@ -1564,7 +1566,8 @@ __global__ __launch_bounds__(kThrNT) void flat_threshold_kernel(const float* __r
       kc[it] = it < sg.iters && i < sg.p1 && e < nv ? order_key(v[it]) : 0u;
     }
   }
-  int r = int(imin64(ns, imax64(64, (2LL * k * ns + nv - 1) / imax64(1, nv))));
+  const int64_t floor_r = imax64(1, imin64(64, 4096LL * ns / imax64(1, nv)));
+  int r = int(imin64(ns, imax64(floor_r, (2LL * k * ns + nv - 1) / imax64(1, nv))));
   if (nv <= k) r = ns;  // every key
   const SelThr st = radix_threshold<kThrNT, kSelIT>(kc, sg.iters, r, sh);
   if (threadIdx.x == 0) thr[row] = nv <= k ? 0u : st.thr;
@@ -1772,8 +1775,10 @@ static FlatPlan plan_flat(const IndexArgs& a, int k) {
     // k would flag most rows and rerun them on the full path.
     p.fused = flat_mfma_ok(a) && a.d_i <= 128 && p.nch <= kCandMaxChunks && ntiles >= 64 && k <= 3072;
     if (p.fused) {
-      // 32 to 64 sample tiles (2,048 to 4,096 sample keys) spread evenly
-      p.tstride = int(ntiles / 32);
+      // 32 to 64 sample tiles spread evenly (the threshold kernel holds
+      // 4,096 sample keys), the most for small k, where the threshold rank
+      // 2ks/v is lowest.
+      p.tstride = int(std::max<int64_t>((ntiles + 63) / 64, std::min<int64_t>(ntiles / 32, std::max(k / 32, 1))));
       p.lds = (ntiles + p.tstride - 1) / p.tstride * 64;
       p.samp_bytes = align256(size_t(p.rows) * p.lds * 4);
       p.thr_bytes = align256(size_t(p.rows) * 4);
