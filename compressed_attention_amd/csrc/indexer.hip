@@ -415,6 +415,118 @@ __global__ __launch_bounds__(256, 2) void score_flat_mfma32_kernel(const uint16_
 }
 
 // ---------------------------------------------------------------------------
+// Flat score for one query per sequence (decode), bf16, 16 heads,
+// d_i = 32*KS in {32, 64, 128}: the 16-query tiles above would leave 15 of
+// every 16 MFMA rows empty here.  Each wave owns one chunk of launch keys
+// of its row and streams it 64 keys at a time, with the arithmetic of the
+// decode HISA stage 2 (score_stage2_mfma_kernel), so both give every key the
+// same score: 16x16x32 MFMA with A = the query's 16 heads and B = 16 keys,
+// lane (g, r) = (l/16, l%16) loading elements 32ks + 8g .. +7 of key r of
+// each 16-key subtile (64 contiguous bytes of 16 rows per load
+// instruction), the weighted ReLU sum of the lane's 4 heads, and one
+// transpose-sum over the 4 lane groups that leaves key 16g + r of the
+// 64 in lane l.  No LDS and no barrier; two register buffers keep the next
+// 64 keys in flight.  Modes, launch-key mapping (tstride),
+// thresholds, chunk spans and counts are those of score_flat_mfma32_kernel;
+// a chunk is a wave's, 4 per workgroup.
+// ---------------------------------------------------------------------------
+template <int KS, int MODE>
+__global__ __launch_bounds__(256) void score_flat_dec_kernel(const uint16_t* __restrict__ q_i,
+                                                             const uint16_t* __restrict__ k_i,
+                                                             const float* __restrict__ w_i,
+                                                             const int32_t* __restrict__ n_vis, int64_t n,
+                                                             int64_t ld, float* __restrict__ S, int nch, int chunk,
+                                                             int tstride, const uint32_t* __restrict__ thr,
+                                                             int32_t* __restrict__ ccnt,
+                                                             const int32_t* __restrict__ gate) {
+  constexpr int D = 32 * KS;
+  const int64_t row = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ch = blockIdx.x * 4 + wave;
+  if (ch >= nch) return;
+  const int g = lane >> 4, r16 = lane & 15;
+  int nv = int(imin64(n, imax64(0, n_vis[row])));
+  if (gate && gate[row] == 0) nv = 0;
+  const int64_t e_begin = int64_t(ch) * chunk;
+  const int64_t tiles_vis = (int64_t(nv) + 64LL * tstride - 1) / (64LL * tstride);
+  const int64_t e_end = imin64(e_begin + chunk, tiles_vis * 64);
+  if (e_begin >= e_end) return;
+
+  u32x4_t a[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) a[ks] = ld16(q_i + (row * 16 + r16) * D + 8 * g + 32 * ks);
+  const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(w_i + row * 16 + 4 * g);
+  float* srow = S + row * ld;
+  float thr_f = INFINITY;
+  bool all = true;
+  float* creg = nullptr;
+  int cap = 0, cnt = 0;
+  if (MODE == 1) {
+    const uint32_t t = thr[row];
+    all = t == 0u;  // take every key: plain scores
+    thr_f = all ? INFINITY : key_to_float(t);
+    creg = srow + e_begin;
+    cap = int(imin64(chunk, ld - e_begin)) / 2;
+  }
+  const uint16_t* kb = k_i + row * n * D + 8 * g;
+  const int n32 = int(n);
+  const int ts = MODE == 1 ? 1 : tstride;
+
+  // 64 keys per step; the next step's keys load while this one is scored.
+  // Plain loads: an instruction reads 64 bytes of each of 16 rows, half of
+  // a 128-byte line, and L2 serves the other half to the next instruction
+  // (non-temporal loads here measured 1.45x slower).
+  auto ldk = [&](int64_t e0, u32x4_t (&dst)[4][KS]) {
+    const int64_t c0 = (e0 / 64) * 64 * ts;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int key = int(imin64(c0 + 16 * nt + r16, n32 - 1));  // rows past the cache are read clamped, never stored
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) dst[nt][ks] = ld16(kb + size_t(key) * D + 32 * ks);
+    }
+  };
+  auto step = [&](int64_t e0, const u32x4_t (&bf)[4][KS]) {
+    const int64_t c0 = (e0 / 64) * 64 * ts;  // launch keys e0 .. e0 + 63 are cache keys c0 .. c0 + 63
+    float v[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(a[ks], bf[nt][ks], acc);
+      float sv = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv = fmaf(wv[i], relu_bits(acc[i]), sv);
+      v[nt] = sv;  // this lane group's 4 heads
+    }
+    const float x = sum4_transpose(v[0], v[1], v[2], v[3]);  // key 16g + r16 = lane of the 64
+    const int el = int(e0) + lane;                             // its launch position
+    const bool vis = c0 + lane < nv;                           // its cache key is visible
+    if (MODE == 0 || all) {
+      if (vis) srow[el] = x;
+    } else {
+      const bool ok = vis && x >= thr_f;
+      const uint64_t m = ballot(ok);
+      if (m != 0ull) {
+        const int slot = cnt + mbcnt(m);  // lanes in key order
+        if (ok && slot < cap) *reinterpret_cast<float2*>(creg + 2 * slot) = make_float2(x, __int_as_float(el));
+        cnt += __popcll(m);
+      }
+    }
+  };
+  u32x4_t b0[4][KS], b1[4][KS];
+  ldk(e_begin, b0);
+  for (int64_t e0 = e_begin; e0 < e_end; e0 += 128) {
+    const bool more = e0 + 64 < e_end;
+    if (more) ldk(e0 + 64, b1);
+    step(e0, b0);
+    if (!more) break;
+    if (e0 + 128 < e_end) ldk(e0 + 128, b0);
+    step(e0 + 64, b1);
+  }
+  if (MODE == 1 && lane == 0) ccnt[row * nch + ch] = cnt;
+}
+
+// ---------------------------------------------------------------------------
 // HISA stage 1 score on fp32 block representatives, 16 heads, d_i = 16*KQ.
 // A workgroup owns QPW queries (1 or 4) and one LDS tile of 64 block means;
 // its 4 waves cover the (query, 16-block subtile) pairs: with 4 queries each
@@ -1739,6 +1851,15 @@ static int flat_chunk(const IndexArgs& a, int64_t nkeys, int64_t target_wg = 102
 }
 
 
+// Flat score for one query per sequence (score_flat_dec_kernel): chunks of
+// a multiple of 64 launch keys, one per wave, about 4,096 waves per launch
+// and at most kCandMaxChunks chunks per row.
+static bool flat_dec_ok(const IndexArgs& a) { return flat_mfma_ok(a) && a.nq == 1 && a.d_i <= 128; }
+static int flat_dec_chunk(const IndexArgs& a, int64_t nkeys) {
+  int64_t c = std::max<int64_t>((a.bt * nkeys + 4095) / 4096, (nkeys + kCandMaxChunks - 1) / kCandMaxChunks);
+  return int(std::max<int64_t>(64, (c + 63) / 64 * 64));
+}
+
 struct FlatPlan {
   int64_t rows, ld;
   bool multi;
@@ -1768,7 +1889,7 @@ static FlatPlan plan_flat(const IndexArgs& a, int k) {
     p.cand_bytes = align256(l1) + align256(l2);
     p.flag_bytes = align256(size_t(p.rows) * 4);
     const int64_t ntiles = (a.n + 63) / 64;
-    p.chunk = flat_chunk(a, a.n);
+    p.chunk = flat_dec_ok(a) ? flat_dec_chunk(a, a.n) : flat_chunk(a, a.n);
     p.nch = int((a.n + p.chunk - 1) / p.chunk);
     // The threshold keeps about 2k candidates (+-12% at the smallest sample);
     // the candidate select holds kSelIT * kCandNT = 8,192 of them, so larger
@@ -1826,6 +1947,37 @@ struct FlatScoreMode {
 
 static hipError_t launch_flat_score(const IndexArgs& a, int64_t ld, float* S, const FlatScoreMode& fm,
                                     hipStream_t st) {
+  if (flat_dec_ok(a)) {
+    const int chunk = fm.chunk ? fm.chunk : flat_dec_chunk(a, fm.nkeys);
+    const int nch = int((fm.nkeys + chunk - 1) / chunk);
+    const dim3 grid(unsigned((nch + 3) / 4), unsigned(a.bt));
+    const bool collect = fm.thr != nullptr;
+    LaunchScope ls(collect             ? "score_flat_collect"
+                   : fm.tstride > 1    ? "score_flat_sample"
+                   : fm.gate != nullptr ? "score_flat_fallback"
+                                        : "score_flat_mfma",
+                   st);
+#define HATTN_FLATDEC(KS, MODE)                                                                                \
+  HATTN_LAUNCH((score_flat_dec_kernel<KS, MODE>), grid, dim3(256), 0, st, (const uint16_t*)a.q_i,            \
+               (const uint16_t*)a.k_i, a.w_i, a.n_vis, a.n, ld, S, nch, chunk, fm.tstride, fm.thr, fm.ccnt, \
+               fm.gate)
+    switch (a.d_i) {
+      case 32:
+        if (collect) HATTN_FLATDEC(1, 1);
+        else HATTN_FLATDEC(1, 0);
+        break;
+      case 64:
+        if (collect) HATTN_FLATDEC(2, 1);
+        else HATTN_FLATDEC(2, 0);
+        break;
+      default:
+        if (collect) HATTN_FLATDEC(4, 1);
+        else HATTN_FLATDEC(4, 0);
+        break;
+    }
+#undef HATTN_FLATDEC
+    return hipGetLastError();
+  }
   if (flat_mfma_ok(a)) {
     // 16 queries per workgroup.  (32, with 8 waves sharing each key tile,
     // measured slower: one resident workgroup per CU and longer barriers.)

@@ -441,3 +441,82 @@ def test_block_sparse_128k_exact_sampled_and_same_blocks_as_hisa():
     ref, ref_blk = oracle.block_sparse_topk(q[rows], kk, ww[rows], nv.cpu().numpy()[0][rows], B, m)
     assert np.array_equal(blk.cpu().numpy()[0, rows], ref_blk)
     assert np.array_equal(idx.cpu().numpy()[0, rows], ref)
+
+
+# ---- flat top-k with one query per sequence (decode) --------------------------
+
+@pytest.mark.parametrize("d,lo,hi", [(32, -8, 8), (64, -8, 8), (128, -4, 4)])
+@pytest.mark.parametrize("N", [3001, 70000])
+def test_flat_decode_exact(d, lo, hi, N):
+    # One query per sequence: the decode score kernel, on the plain path
+    # (N = 3001) and the fused sample / threshold / candidate path
+    # (N = 70,000), bit-exact on the integer grid; visible counts around k,
+    # 2k, the 64-key tile and the full row.
+    bt = 8
+    q_i = synth.int_grid((bt, 1, 16, d), 301 + d, lo, hi, dtype=torch.bfloat16)
+    k_i = synth.int_grid((bt, N, d), 302 + d, lo, hi, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((bt, 1, 16), 303 + d)
+    for k in (1, 100, 700, 2048):
+        nvl = [N, N - 1, 0, 1, min(N, k), min(N, k + 37), min(N, 2 * k + 5), 64 * (N // 128) + 13]
+        nv = torch.tensor(nvl, dtype=torch.int32).reshape(bt, 1)
+        idx, sc = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), k, return_scores=True)
+        idx, sc = idx.cpu().numpy(), f64(sc)
+        for b in range(bt):
+            ref, ref_sc = oracle.flat_topk(f64(q_i[b]), f64(k_i[b]), f64(w_i[b]), nv[b].numpy(), k,
+                                           return_scores=True)
+            assert np.array_equal(idx[b], ref), (d, N, k, b)
+            assert np.array_equal(np.where(ref >= 0, sc[b], 0), np.where(ref >= 0, ref_sc, 0)), (d, N, k, b)
+
+
+def test_flat_decode_ties_take_the_fallback_path():
+    # One query per sequence on the fused path: an all-zero query (every
+    # score 0, the sample cannot isolate k candidates) must be finished by
+    # the exact fallback; the other rows stay on the fast path.
+    N, k, bt = 40000, 1000, 4
+    q_i = synth.int_grid((bt, 1, 16, 128), 311, -4, 4, dtype=torch.bfloat16)
+    q_i[2] = 0
+    k_i = synth.int_grid((bt, N, 128), 312, -4, 4, dtype=torch.bfloat16)
+    w_i = synth.dyadic_uniform((bt, 1, 16), 313, bits=4)
+    nv = torch.tensor([[N], [N - 5], [N], [9000]], dtype=torch.int32)
+    idx = ops.index_topk(q_i.to(DEV), k_i.to(DEV), w_i.to(DEV), nv.to(DEV), k).cpu().numpy()
+    assert list(idx[2, 0]) == list(range(k))
+    for b in (0, 1, 3):
+        ref = oracle.flat_topk(f64(q_i[b]), f64(k_i[b]), f64(w_i[b]), nv[b].numpy(), k)
+        assert np.array_equal(idx[b], ref), b
+
+
+@pytest.mark.parametrize("N,B,m", [(16000, 128, 125), (5000, 64, 80)])
+def test_flat_decode_equals_hisa_keeping_every_block_float(N, B, m):
+    # At decode the flat score and HISA's second stage share their
+    # arithmetic, so on float inputs HISA keeping every block returns the
+    # flat selection bit for bit.
+    bt, k = 6, 512
+    q_i = synth.normal((bt, 1, 16, 128), 321, dtype=torch.bfloat16).to(DEV)
+    k_i = synth.normal((bt, N, 128), 322, dtype=torch.bfloat16).to(DEV)
+    w_i = synth.uniform((bt, 1, 16), 323).to(DEV)
+    nv = torch.tensor([[N], [N - 3], [N // 2], [k], [k + 1], [B * 7 + 5]], dtype=torch.int32).to(DEV)
+    reps = ops.hisa_pool(k_i, B)
+    a = ops.hisa_topk(q_i, k_i, w_i, nv, reps, B, m, k)
+    f = ops.index_topk(q_i, k_i, w_i, nv, k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, f)
+
+
+def test_flat_decode_csa2_size_exact_sampled():
+    # The CSA2 decode selection at its full size: 8 sequences of 524,287
+    # compressed entries (rate 2 at 1M), one query each, top-512, on the
+    # integer grid with 4-bit weights (exact scores); two rows against the
+    # oracle, every row's selection checked for validity.
+    bt, N, k = 8, 524287, 512
+    q_i = synth.int_grid((bt, 1, 16, 128), 331, -4, 4, dtype=torch.bfloat16, device=DEV)
+    k_i = synth.int_grid((bt, N, 128), 332, -4, 4, dtype=torch.bfloat16, device=DEV)
+    w_i = synth.dyadic_uniform((bt, 1, 16), 333, device=DEV, bits=4)
+    nv = torch.full((bt, 1), N, dtype=torch.int32, device=DEV)
+    nv[5, 0] = N - 1000
+    idx = ops.index_topk(q_i, k_i, w_i, nv, k).cpu().numpy()
+    for b in range(bt):
+        row = idx[b, 0]
+        assert (np.diff(row) > 0).all() and row[0] >= 0 and row[-1] < int(nv[b, 0])
+    for b in (0, 5):
+        ref = oracle.flat_topk(f64(q_i[b]), f64(k_i[b]), f64(w_i[b]), nv[b].cpu().numpy(), k)
+        assert np.array_equal(idx[b], ref), b
