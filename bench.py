@@ -278,6 +278,22 @@ def hybrid_pair(args):
     ms = e0.elapsed_time(e1) / args.steps
     dist = step_distribution(replay, max(30, args.steps))
 
+    # The same step as one launch: each plan's graph of its 6 kernels
+    # (hattn_decode_plan_run_graph; the first call per plan captures it).
+    def replay_graph(i):
+        plans[i % R].run_graph()
+
+    for i in range(max(args.warmup, R)):
+        replay_graph(i)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        replay_graph(i)
+    e1.record()
+    torch.cuda.synchronize()
+    native_graph_ms = e0.elapsed_time(e1) / args.steps
+    native_graph_dist = step_distribution(replay_graph, max(30, args.steps))
+
     # The same plan steps replayed from one HIP graph holding one step per
     # cache replica (a decode loop captured once): kernel boundaries inside a
     # graph cost less than stream launches, and one replay enqueues R steps.
@@ -332,7 +348,7 @@ def hybrid_pair(args):
     flat_ms = flat_decode_step(args, t, caches, k) if args.flat_compare else None
     info = dict(ms=ms, graph_ms=graph_ms, kernels=kt, kernels_calls=kt_calls, kernel_bytes=kb, step_bytes=step_bytes,
                 bt=bt, N=N, Nh=Nh, k=k, L=L, dist=dist, flat_ms=flat_ms, graph_plan_ms=graph_plan_ms,
-                graph_dist=graph_dist)
+                graph_dist=graph_dist, native_graph_ms=native_graph_ms, native_graph_dist=native_graph_dist)
     for p_ in plans:
         p_.close()
     return info
@@ -841,6 +857,8 @@ def main():
                    "raw_rows_kept": 128,
                    "launch": "native decode plan (one host call, 6 kernels per step)"},
         "step_us": {kk: round(v, 2) for kk, v in res["dist"].items() if kk != "n"} | {"n": res["dist"]["n"]},
+        "step_us_one_launch": {"timed": round(res["native_graph_ms"] * 1e3, 2),
+                               **{kk: round(v, 2) for kk, v in res["native_graph_dist"].items()}},
         "step_us_plan_graph": round(res["graph_plan_ms"] * 1e3, 2),
         "step_us_plan_graph_dist": {kk: round(v, 2) for kk, v in res["graph_dist"].items()},
         "flat_indexer_step_us": None if res["flat_ms"] is None else round(res["flat_ms"] * 1e3, 1),

@@ -34,6 +34,7 @@ SIGNATURES = {
     "hattn_decode_plan_ws_bytes": [_p, _psz],
     "hattn_decode_plan_create": [_p, ctypes.POINTER(_p)],
     "hattn_decode_plan_run": [_p, _p],
+    "hattn_decode_plan_run_graph": [_p, _p],
     "hattn_decode_plan_destroy": [_p],
     "hattn_timer_enable": [_i32],
     "hattn_timer_collect": [],

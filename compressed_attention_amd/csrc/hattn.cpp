@@ -490,7 +490,14 @@ hattn_status_t hattn_timer_names(char* buf, int64_t len) {
 }  // extern "C"
 
 struct hattn_decode_plan {
+  ~hattn_decode_plan() {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+  }
   int device = -1;
+  // the step captured once by hattn_decode_plan_run_graph
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
   bool front = false;  // stage 1 and cache maintenance in one launch
   int dtype = 0;
   int64_t bt = 0, L = 0;
@@ -645,13 +652,13 @@ hattn_status_t hattn_decode_plan_create(const hattn_decode_desc* desc, hattn_dec
   return ok();
 }
 
-hattn_status_t hattn_decode_plan_run(hattn_decode_plan_t p, void* stream) {
-  if (!p) return fail(HATTN_ERR_ARG, "decode_plan_run: NULL plan");
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_status(e, "decode_plan_run");
-  if (dev != p->device) return fail(HATTN_ERR_ARG, "decode_plan_run: plan made on device %d, current %d", p->device, dev);
-  const hipStream_t st = (hipStream_t)stream;
+}  // extern "C"
+
+namespace {
+
+// The step's launches, in order, on st.
+hipError_t plan_enqueue(hattn_decode_plan* p, hipStream_t st) {
+  hipError_t e;
   // Both branches on one stream: the HCA work rides in the CSA launches
   // (one cache-maintenance launch, one attention launch, one merge launch).
   if (p->front) {
@@ -671,7 +678,63 @@ hattn_status_t hattn_decode_plan_run(hattn_decode_plan_t p, void* stream) {
       e = hattn::launch_hisa_topk(p->ia, p->reps, p->B, p->m, p->k, p->idx, nullptr, p->hisa_ws, st);
   }
   if (e == hipSuccess) e = hattn::launch_attn_pair(p->sa, p->sa_ws, p->da, p->da_ws, st);
-  return hip_status(e, "decode_plan_run");
+  return e;
+}
+
+hattn_status_t plan_device_check(hattn_decode_plan* p, const char* fn) {
+  if (!p) return fail(HATTN_ERR_ARG, "%s: NULL plan", fn);
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev != p->device) return fail(HATTN_ERR_ARG, "%s: plan made on device %d, current %d", fn, p->device, dev);
+  return HATTN_OK;
+}
+
+// Captures the step into p->graph / p->exec on a private stream.
+hipError_t plan_capture(hattn_decode_plan* p) {
+  hipStream_t cap = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cap, hipStreamNonBlocking);
+  if (e != hipSuccess) return e;
+  e = hipStreamBeginCapture(cap, hipStreamCaptureModeThreadLocal);
+  if (e == hipSuccess) {
+    const hipError_t el = plan_enqueue(p, cap);
+    hipGraph_t g = nullptr;
+    e = hipStreamEndCapture(cap, &g);
+    if (el != hipSuccess) e = el;
+    if (e == hipSuccess) {
+      hipGraphExec_t x = nullptr;
+      e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+      if (e == hipSuccess) {
+        p->graph = g;
+        p->exec = x;
+      }
+    }
+    if (e != hipSuccess && g) (void)hipGraphDestroy(g);
+  }
+  (void)hipStreamDestroy(cap);
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+hattn_status_t hattn_decode_plan_run(hattn_decode_plan_t p, void* stream) {
+  hattn_status_t s = plan_device_check(p, "decode_plan_run");
+  if (s != HATTN_OK) return s;
+  return hip_status(plan_enqueue(p, (hipStream_t)stream), "decode_plan_run");
+}
+
+hattn_status_t hattn_decode_plan_run_graph(hattn_decode_plan_t p, void* stream) {
+  hattn_status_t s = plan_device_check(p, "decode_plan_run_graph");
+  if (s != HATTN_OK) return s;
+  if (!p->exec) {
+    if (g_timer_on)
+      return fail(HATTN_ERR_ARG, "decode_plan_run_graph: the first call captures the step; turn the timer off");
+    const hipError_t e = plan_capture(p);
+    if (e != hipSuccess) return hip_status(e, "decode_plan_run_graph (capture)");
+  }
+  return hip_status(hipGraphLaunch(p->exec, (hipStream_t)stream), "decode_plan_run_graph");
 }
 
 hattn_status_t hattn_decode_plan_destroy(hattn_decode_plan_t p) {

@@ -479,6 +479,13 @@ class DecodePlan:
             check("hattn_decode_plan_run", status)
         return self.csa_out, self.hca_out
 
+    def run_graph(self, stream=None):
+        """The same step as one launch of a HIP graph that the first call
+        captures (hattn_decode_plan_run_graph)."""
+        st = ctypes.c_void_p((stream or torch.cuda.current_stream(self.device)).cuda_stream)
+        check("hattn_decode_plan_run_graph", lib().hattn_decode_plan_run_graph(self._plan, st))
+        return self.csa_out, self.hca_out
+
     def close(self):
         if self._plan is not None:
             check("hattn_decode_plan_destroy", lib().hattn_decode_plan_destroy(self._plan))

@@ -369,8 +369,14 @@ hattn_status_t hattn_decode_append(int dtype, const void* raw_kv, int64_t bt, in
  *   hattn_decode_plan_run(plan, stream)  enqueues one step on `stream` (the
  *       current device must be the plan's).  Two runs of one plan must not
  *       overlap in time (they share the workspace).
- *   hattn_decode_plan_destroy(plan)  frees the plan (host memory only);
- *       NULL is accepted.
+ *   hattn_decode_plan_run_graph(plan, stream)  the same step as one launch:
+ *       the first call captures the step's kernels into a HIP graph held by
+ *       the plan (on a private stream; the kernel timer must be off, else
+ *       HATTN_ERR_ARG), and every call launches that graph on `stream`.
+ *       Results equal hattn_decode_plan_run's.  The graph reads the buffers
+ *       when it runs, as run does, so inputs may change between steps.
+ *   hattn_decode_plan_destroy(plan)  frees the plan and its graph; NULL is
+ *       accepted.
  */
 typedef struct hattn_decode_desc {
   int32_t dtype;
@@ -410,6 +416,7 @@ int64_t hattn_decode_desc_size(void);
 hattn_status_t hattn_decode_plan_ws_bytes(const hattn_decode_desc* desc, size_t* ws_bytes);
 hattn_status_t hattn_decode_plan_create(const hattn_decode_desc* desc, hattn_decode_plan_t* plan);
 hattn_status_t hattn_decode_plan_run(hattn_decode_plan_t plan, void* stream);
+hattn_status_t hattn_decode_plan_run_graph(hattn_decode_plan_t plan, void* stream);
 hattn_status_t hattn_decode_plan_destroy(hattn_decode_plan_t plan);
 
 /*

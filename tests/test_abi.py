@@ -180,6 +180,8 @@ def test_decode_plan_validation(L):
     d.ws, d.ws_bytes = p, 16  # too small: refused before any device work
     assert L.hattn_decode_plan_create(ctypes.byref(d), ctypes.byref(plan)) == 3
     assert L.hattn_decode_plan_destroy(None) == 0
+    assert L.hattn_decode_plan_run(None, None) == 1
+    assert L.hattn_decode_plan_run_graph(None, None) == 1
 
 
 def test_sparse_attn_noalloc_rejects_oversize(L):

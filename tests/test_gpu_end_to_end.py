@@ -256,7 +256,8 @@ def test_csa2_layer_group(nq, w, s):
         assert np.abs(got - r_o).max() < 1e-2, (bb, float(np.abs(got - r_o).max()))
 
 
-def test_decode_plan_ring_multi_step():
+@pytest.mark.parametrize("graph", [False, True])
+def test_decode_plan_ring_multi_step(graph):
     # A decode loop of 130 steps (positions 3500 .. 3629): both layers' raw
     # K|V rows and logits live in 128-row rings (before each step the
     # caller writes the new token's rows at slot p % 128), and the caches
@@ -264,7 +265,9 @@ def test_decode_plan_ring_multi_step():
     # tokens), HCA-entry (p = 3583) and HISA-block (entry 896, p = 3591)
     # boundaries.  Checked against the oracle on the whole raw prefix every
     # 8 steps and at the boundaries; a second plan on the full raw arrays
-    # must give the same bits at every step.
+    # must give the same bits at every step.  With graph=True the ring plan
+    # runs each step as one launch of its captured graph (replayed 130 times,
+    # with eager writes and copies between the replays).
     bt, L, R, B, m, k = 2, 4096, 128, 128, 4, 128
     N, Nh = oracle.n_entries(L, 8, 4), oracle.n_entries(L, 128, 128)
     w = synth.hybrid_pair_decode(3, device="cpu", bt=bt, L=L, N_csa=N)
@@ -304,7 +307,7 @@ def test_decode_plan_ring_multi_step():
         for n, ring in rings.items():
             ring[:, p % R] = g[n][:, p]
         q_pos.fill_(p)
-        o_r = [x.clone() for x in ring_plan.run()] + [ring_plan.csa_idx.clone()]
+        o_r = [x.clone() for x in (ring_plan.run_graph() if graph else ring_plan.run())] + [ring_plan.csa_idx.clone()]
         o_f = [x.clone() for x in full_plan.run()] + [full_plan.csa_idx.clone()]
         for a, b_ in zip(o_r, o_f):
             assert torch.equal(a, b_), p
