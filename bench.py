@@ -400,6 +400,7 @@ def csa2_decode(args):
     128-token window (the two layers as 128 MFMA heads).  The step compresses
     the entry the new token completes (K|V and indexer key together), counts
     the visible entries, selects and attends; replayed as graphs."""
+    import numpy as np
     import torch
     from compressed_attention_amd import ops, synth
 
@@ -428,7 +429,31 @@ def csa2_decode(args):
     ms = timed_graphs(graphs, max(10, args.steps), 3)
     kt = kernel_times(step, [None], max(10, args.steps // 2))
     del graphs
-    return dict(ms=ms, kernels=kt, bt=bt, layers=G, N=N)
+
+    # The same step with HISA in place of the flat indexer (B = 128, m = 16:
+    # 2,048 candidates for the top-512, the pages' m*B = 4k); the step also
+    # refreshes the mean of the block holding the new entry.
+    B, m = 128, 16
+    reps = ops.hisa_pool(k_i, B)
+    nb = reps.shape[1]
+
+    def step_hisa(_):
+        ops.compress_with_index(raw, raw_ki, z, b, w, s, N - 1, N, out=ckv, out_i=k_i)
+        ops.hisa_pool(k_i, B, nb - 1, nb, out=reps)
+        nv = ops.visible_count(q_pos, w, s, N)
+        idx = ops.hisa_topk(q_i, k_i, w_i, nv, reps, B, m, k)
+        return ops.sparse_attn(q, ckv, idx, raw, q_pos, 128), idx
+
+    graphs = capture(lambda c: step_hisa(c)[0], [None])
+    ms_h = timed_graphs(graphs, max(10, args.steps), 3)
+    kt_h = kernel_times(lambda c: step_hisa(c)[0], [None], max(10, args.steps // 2))
+    del graphs
+    nv = ops.visible_count(q_pos, w, s, N)
+    i_flat = ops.index_topk(q_i, k_i, w_i, nv, k).cpu().numpy()
+    i_hisa = step_hisa(None)[1].cpu().numpy()
+    iou = float(np.mean([len(np.intersect1d(i_flat[r, 0], i_hisa[r, 0])) /
+                         len(np.union1d(i_flat[r, 0], i_hisa[r, 0])) for r in range(bt)]))
+    return dict(ms=ms, kernels=kt, bt=bt, layers=G, N=N, ms_hisa=ms_h, kernels_hisa=kt_h, iou=iou)
 
 
 def csa_prefill(args):
@@ -788,7 +813,12 @@ def main():
         extras["csa2_decode_1M_b8_2layers"] = dict(
             us_per_step=c2["ms"] * 1e3, layer_queries_per_s=c2["bt"] * c2["layers"] / (c2["ms"] * 1e-3),
             entries=c2["N"], kernels_us={kk: v[0] * 1e3 for kk, v in c2["kernels"].items()},
-            note="rate-2 cache (w=4, s=2), flat top-512 over the compressed indexer keys, 2 layers as 128 heads")
+            hisa_us_per_step=c2["ms_hisa"] * 1e3,
+            hisa_layer_queries_per_s=c2["bt"] * c2["layers"] / (c2["ms_hisa"] * 1e-3),
+            hisa_kernels_us={kk: v[0] * 1e3 for kk, v in c2["kernels_hisa"].items()},
+            hisa_vs_flat_iou_mean=c2["iou"],
+            note="rate-2 cache (w=4, s=2), flat top-512 over the compressed indexer keys, 2 layers as 128 heads; "
+                 "hisa_*: the same step with HISA (B=128, m=16) selecting the top-512")
         torch.cuda.empty_cache()
         cp = csa_prefill(args)
         ck = {kk: v[0] for kk, v in cp["kernels"].items()}

@@ -224,6 +224,7 @@ def test_hisa_float_inputs_vs_oracle():
 
 
 @pytest.mark.parametrize("N,B,m,k", [(20000, 128, 64, 2048), (262143, 128, 64, 512), (5000, 64, 8, 300),
+                                     (524287, 128, 16, 512),  # CSA2's rate-2 cache at 1M, 4,096 blocks
                                      (20000, 8, 1100, 2048),  # more chosen blocks than LDS slots
                                      (20000, 2, 64, 100)])  # over 8,192 blocks a row: the 1,024-thread block select
 def test_hisa_decode_shape_exact(N, B, m, k):
