@@ -127,8 +127,8 @@ struct AttnK {
   int chunk, nsplit;
   float* out;
   float* lse;
-  float* part_o;
-  float* part_ml;
+  _Float16* part_o;  // split-K partials: O / l of the split, fp16
+  float* part_ml;    // (max, sum) of the split, fp32
   // Head groups of a query row: the row has 16 * NW * hg heads and a
   // workgroup takes one group of 16 * NW (layers that share one cache and
   // one selection fold into the head axis: MQA heads share every key).
@@ -168,7 +168,7 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
   const int chunk = a.chunk, nsplit = a.nsplit;
   float* __restrict__ out = a.out;
   float* __restrict__ lse = a.lse;
-  float* __restrict__ part_o = a.part_o;
+  _Float16* __restrict__ part_o = a.part_o;
   float* __restrict__ part_ml = a.part_ml;
   constexpr int H = 16 * NW;
   constexpr int C = 2 * D;
@@ -370,10 +370,17 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t*>(op + 16 * dt) = o[dt] * inv;
     if (lse && g == 0) lse[qrow * HT + head] = (m_run + __log2f(l_tot)) * kLn2;
   } else {
+    // the split's output normalised by its own sum (|O / l| <= max |V|),
+    // stored in fp16; the merge weights it by 2^(m - M) l
     const int64_t pr = qrow * nsplit + split;
-    float* op = part_o + (pr * HT + head) * D + 4 * g;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    _Float16* op = part_o + (pr * HT + head) * D + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t*>(op + 16 * dt) = o[dt];
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4_t v = o[dt] * inv;
+      *reinterpret_cast<f16x4_t*>(op + 16 * dt) =
+          f16x4_t{_Float16(v[0]), _Float16(v[1]), _Float16(v[2]), _Float16(v[3])};
+    }
     if (g == 0) {
       part_ml[(pr * HT + head) * 2 + 0] = m_run;
       part_ml[(pr * HT + head) * 2 + 1] = l_tot;
@@ -507,12 +514,10 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
     const int i = tid + 256 * u;
     if (i < H * D) {
       const int h = i / D;
-      if (nsplit == 1) {
-        const float l = lrun[h];
-        out[qrow * H * D + i] = l > 0.f ? acc[u] / l : 0.f;
-      } else {
-        part_o[(qrow * nsplit + split) * H * D + i] = acc[u];
-      }
+      const float l = lrun[h];
+      const float v = l > 0.f ? acc[u] / l : 0.f;
+      if (nsplit == 1) out[qrow * H * D + i] = v;
+      else part_o[(qrow * nsplit + split) * H * D + i] = v;  // normalised, as the MFMA kernel's (fp32 here)
     }
   }
   for (int h = tid; h < H; h += 256) {
@@ -525,15 +530,18 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
   }
 }
 
-// Combines per-chunk partials: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,
-// with weights w_s = 2^(m_s - M) / sum_t 2^(m_t - M) l_t.  Needs
-// nsplit <= 4 * kMergeRegs and a head shape merge_fast() accepts.
+// Combines per-chunk partials, each stored as its normalised output
+// u_s = O_s / l_s (PT: fp16 from the bf16 MFMA kernels, fp32 from the
+// vector kernel) with its (m_s, l_s): o = sum_s w_s u_s with weights
+// w_s = 2^(m_s - M) l_s / sum_t 2^(m_t - M) l_t.  Needs nsplit <= 4 *
+// kMergeRegs and a head shape merge_fast() accepts.
 constexpr int kMergeRegs = 16;
 constexpr int kMergeMaxSplit = 4 * kMergeRegs;
 
 // Arguments of one merge (one query set's partials).
+template <typename PT>
 struct MergeK {
-  const float* part_o;
+  const PT* part_o;
   const float* part_ml;
   int nsplit;
   float* out;
@@ -554,22 +562,34 @@ struct MergeLds {
 // holds outputs e0 + 4l .. 4l + 3 (one head), and wave g sums splits
 // g, g + 4, ...: all partial loads and, in wave 0, the heads' (m_s, l_s)
 // loads are issued before anything waits, so the merge is one memory round
-// trip.  Wave 0 turns (m_s, l_s) into per-split weights (exp2(m_s - M) / den
-// with M the heads' largest m_s), the waves weight their partials, and the
-// four group sums are added through LDS in group order.
-HATTN_DEV void attn_merge_body(const MergeK& mk, int H, int D, int64_t qrow, int e0, MergeLds& sm) {
+// trip.  Wave 0 turns (m_s, l_s) into per-split weights (exp2(m_s - M) l_s /
+// den with M the heads' largest m_s), the waves weight their partials, and
+// the four group sums are added through LDS in group order.
+// 4 consecutive partial values as loaded (Vec4<PT>::type) and as fp32.  The
+// merge keeps the loaded vectors until every load is issued: converting
+// each one as it arrives lets the compiler reuse one register pair and wait
+// for every load in turn.
+template <typename PT> struct Vec4;
+template <> struct Vec4<float> { typedef f32x4_t type; };
+template <> struct Vec4<_Float16> { typedef f16x4_t type; };
+HATTN_DEV f32x4_t to_f32x4(f32x4_t v) { return v; }
+HATTN_DEV f32x4_t to_f32x4(f16x4_t h) { return f32x4_t{float(h[0]), float(h[1]), float(h[2]), float(h[3])}; }
+
+template <typename PT>
+HATTN_DEV void attn_merge_body(const MergeK<PT>& mk, int H, int D, int64_t qrow, int e0, MergeLds& sm) {
   const int nsplit = mk.nsplit;
   const int tid = threadIdx.x, lane = tid & 63, sg = tid >> 6;
   const int hpg = 256 / D;            // heads in the group
   const int h0 = e0 / D;
   const int hl = (4 * lane) / D;      // this lane's head within the group
   const int64_t pos = int64_t(H) * D;
-  const float* __restrict__ po = mk.part_o + qrow * nsplit * pos + e0 + 4 * lane;
-  f32x4_t ov[kMergeRegs];
+  typedef typename Vec4<PT>::type V4;
+  const PT* __restrict__ po = mk.part_o + qrow * nsplit * pos + e0 + 4 * lane;
+  V4 ov[kMergeRegs];
 #pragma unroll
   for (int i = 0; i < kMergeRegs; ++i) {
     const int s = sg + 4 * i;
-    ov[i] = s < nsplit ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(po + s * pos)) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    ov[i] = s < nsplit ? __builtin_nontemporal_load(reinterpret_cast<const V4*>(po + s * pos)) : V4{0, 0, 0, 0};
   }
   if (sg == 0) {
     const float* __restrict__ ml = mk.part_ml + (qrow * nsplit * H + h0) * 2;
@@ -586,7 +606,7 @@ HATTN_DEV void attn_merge_body(const MergeK& mk, int H, int D, int64_t qrow, int
         float den = v[hh].x != -INFINITY ? exp2f(v[hh].x - M) * v[hh].y : 0.f;
         den = wave_sum(den);
         const float inv = den > 0.f ? 1.f / den : 0.f;
-        if (lane < nsplit) sm.w[hh][lane] = v[hh].x == -INFINITY ? 0.f : exp2f(v[hh].x - M) * inv;
+        if (lane < nsplit) sm.w[hh][lane] = v[hh].x == -INFINITY ? 0.f : exp2f(v[hh].x - M) * v[hh].y * inv;
         if (lane == 0 && mk.lse) mk.lse[qrow * H + h0 + hh] = (M + __log2f(den)) * kLn2;
       }
     }
@@ -598,8 +618,9 @@ HATTN_DEV void attn_merge_body(const MergeK& mk, int H, int D, int64_t qrow, int
     const int s = sg + 4 * i;
     if (s < nsplit) {
       const float w = sm.w[hl][s];
+      const f32x4_t v = to_f32x4(ov[i]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) num[c] = fmaf(w, ov[i][c], num[c]);
+      for (int c = 0; c < 4; ++c) num[c] = fmaf(w, v[c], num[c]);
     }
   }
   sm.red[sg][lane] = num;
@@ -612,14 +633,17 @@ HATTN_DEV void attn_merge_body(const MergeK& mk, int H, int D, int64_t qrow, int
   }
 }
 
-__global__ __launch_bounds__(256) void attn_merge_kernel(MergeK mk, int H, int D) {
+template <typename PT>
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeK<PT> mk, int H, int D) {
   __shared__ MergeLds sm;
   attn_merge_body(mk, H, D, blockIdx.y, blockIdx.x * 256, sm);
 }
 
 // Two query sets' merges in one launch: rows [0, rows_a) of grid y are set
 // a, the rest set b (same head count and size).
-__global__ __launch_bounds__(256) void attn_merge_pair_kernel(MergeK a, int64_t rows_a, MergeK b, int H, int D) {
+template <typename PT>
+__global__ __launch_bounds__(256) void attn_merge_pair_kernel(MergeK<PT> a, int64_t rows_a, MergeK<PT> b, int H,
+                                                              int D) {
   __shared__ MergeLds sm;
   const int64_t y = blockIdx.y;
   if (y < rows_a) attn_merge_body(a, H, D, y, blockIdx.x * 256, sm);
@@ -628,7 +652,8 @@ __global__ __launch_bounds__(256) void attn_merge_pair_kernel(MergeK a, int64_t 
 
 // Same combination for any head size or split count: one thread per output,
 // each looping over all splits.
-__global__ __launch_bounds__(256) void attn_merge_any_kernel(const float* __restrict__ part_o,
+template <typename PT>
+__global__ __launch_bounds__(256) void attn_merge_any_kernel(const PT* __restrict__ part_o,
                                                              const float* __restrict__ part_ml, int nsplit, int H,
                                                              int D, float* __restrict__ out, float* __restrict__ lse) {
   const int64_t qrow = blockIdx.y;
@@ -641,14 +666,14 @@ __global__ __launch_bounds__(256) void attn_merge_any_kernel(const float* __rest
 #pragma unroll 8
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[s * mls]);
   float num = 0.f, den = 0.f;
-  const float* po = part_o + qrow * nsplit * H * D + e;
+  const PT* po = part_o + qrow * nsplit * H * D + e;
   const int64_t pos = int64_t(H) * D;
 #pragma unroll 8
   for (int s = 0; s < nsplit; ++s) {
     const float ms = ml[s * mls];
-    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    den = fmaf(w, ml[s * mls + 1], den);
-    num = fmaf(w, po[s * pos], num);
+    const float w = ms == -INFINITY ? 0.f : exp2f(ms - M) * ml[s * mls + 1];
+    den += w;
+    num = fmaf(w, float(po[s * pos]), num);
   }
   out[qrow * H * D + e] = den > 0.f ? num / den : 0.f;
   if (c == 0 && lse) lse[qrow * H + h] = (M + __log2f(den)) * kLn2;
@@ -699,7 +724,7 @@ static AttnPlan plan_attn(const AttnArgs& a) {
   p.chunk = int(chunk);
   p.nsplit = int((maxkeys + chunk - 1) / chunk);
   if (p.nsplit > 1) {
-    p.po_bytes = align256(size_t(rows) * p.nsplit * a.h * a.d * 4);
+    p.po_bytes = align256(size_t(rows) * p.nsplit * a.h * a.d * (mfma_shape(a) ? 2 : 4));  // fp16 from MFMA
     p.total = p.po_bytes + align256(size_t(rows) * p.nsplit * a.h * 2 * 4);
   }
   return p;
@@ -707,14 +732,14 @@ static AttnPlan plan_attn(const AttnArgs& a) {
 
 size_t attn_ws_bytes(const AttnArgs& a) { return plan_attn(a).total; }
 
-static AttnK attn_k(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml) {
+static AttnK attn_k(const AttnArgs& a, const AttnPlan& pl, _Float16* po, float* pml) {
   return AttnK{(const uint16_t*)a.q, (const uint16_t*)a.ckv, a.n, a.idx, a.k, a.n_vis, (const uint16_t*)a.raw_kv,
                a.L, a.q_pos, a.window, a.scale * kLog2e, a.nq, pl.chunk, pl.nsplit, a.out, a.lse, po, pml,
                head_groups(a), a.raw_rows};
 }
 
 template <bool SPARSE>
-static void launch_attn_mfma(const AttnArgs& a, const AttnPlan& pl, float* po, float* pml, hipStream_t st) {
+static void launch_attn_mfma(const AttnArgs& a, const AttnPlan& pl, _Float16* po, float* pml, hipStream_t st) {
   const AttnK k = attn_k(a, pl, po, pml);
   dim3 grid(unsigned(pl.nsplit), unsigned(a.bt * a.nq), unsigned(head_groups(a)));
 #define HATTN_ATTN(D, NH)                                                                     \
@@ -749,39 +774,49 @@ static void launch_attn_valu(const AttnArgs& a, const AttnPlan& pl, float* po, f
                      pl.nsplit, a.out, a.lse, po, pml, a.raw_rows);
 }
 
+// The merge of one query set whose partials (type PT) are at po / pml.
+template <typename PT>
+static void launch_merge(const AttnArgs& a, const AttnPlan& pl, PT* po, float* pml, hipStream_t st) {
+  if (merge_fast(a.h, a.d, pl.nsplit))
+    HATTN_LAUNCH((attn_merge_kernel<PT>), dim3(unsigned(a.h * a.d / 256), unsigned(a.bt * a.nq)), dim3(256), 0, st,
+                 MergeK<PT>{po, pml, pl.nsplit, a.out, a.lse}, a.h, a.d);
+  else
+    HATTN_LAUNCH((attn_merge_any_kernel<PT>), dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)),
+                 dim3(256), 0, st, po, pml, pl.nsplit, a.h, a.d, a.out, a.lse);
+}
+
 hipError_t launch_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   const AttnPlan pl = plan_attn(a);
-  float* po = nullptr;
+  void* po = nullptr;  // fp16 partials from the MFMA kernels, fp32 from the vector kernel
   float* pml = nullptr;
   if (pl.nsplit > 1) {
-    po = reinterpret_cast<float*>(ws);
+    po = ws;
     pml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + pl.po_bytes);
   }
   const bool sparse = a.idx != nullptr;
+  const bool mfma = mfma_shape(a);
   {
-    LaunchScope ls(mfma_shape(a) ? (sparse ? "attn_sparse_mfma" : "attn_dense_mfma")
-                                 : (sparse ? "attn_sparse_valu" : "attn_dense_valu"),
+    LaunchScope ls(mfma ? (sparse ? "attn_sparse_mfma" : "attn_dense_mfma")
+                        : (sparse ? "attn_sparse_valu" : "attn_dense_valu"),
                    st);
-    if (mfma_shape(a)) {
-      if (sparse) launch_attn_mfma<true>(a, pl, po, pml, st);
-      else launch_attn_mfma<false>(a, pl, po, pml, st);
+    _Float16* poh = static_cast<_Float16*>(po);
+    float* pof = static_cast<float*>(po);
+    if (mfma) {
+      if (sparse) launch_attn_mfma<true>(a, pl, poh, pml, st);
+      else launch_attn_mfma<false>(a, pl, poh, pml, st);
     } else if (a.dtype == 0) {
-      if (sparse) launch_attn_valu<float, true>(a, pl, po, pml, st);
-      else launch_attn_valu<float, false>(a, pl, po, pml, st);
+      if (sparse) launch_attn_valu<float, true>(a, pl, pof, pml, st);
+      else launch_attn_valu<float, false>(a, pl, pof, pml, st);
     } else {
-      if (sparse) launch_attn_valu<uint16_t, true>(a, pl, po, pml, st);
-      else launch_attn_valu<uint16_t, false>(a, pl, po, pml, st);
+      if (sparse) launch_attn_valu<uint16_t, true>(a, pl, pof, pml, st);
+      else launch_attn_valu<uint16_t, false>(a, pl, pof, pml, st);
     }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   LaunchScope ls("attn_merge", st);
-  if (merge_fast(a.h, a.d, pl.nsplit))
-    HATTN_LAUNCH(attn_merge_kernel, dim3(unsigned(a.h * a.d / 256), unsigned(a.bt * a.nq)), dim3(256), 0, st,
-                 MergeK{po, pml, pl.nsplit, a.out, a.lse}, a.h, a.d);
-  else
-    HATTN_LAUNCH(attn_merge_any_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256), 0,
-                 st, po, pml, pl.nsplit, a.h, a.d, a.out, a.lse);
+  if (mfma) launch_merge(a, pl, static_cast<_Float16*>(po), pml, st);
+  else launch_merge(a, pl, static_cast<float*>(po), pml, st);
   return hipGetLastError();
 }
 
@@ -797,15 +832,16 @@ hipError_t launch_attn_pair(const AttnArgs& s, void* ws_s, const AttnArgs& d, vo
     return e != hipSuccess ? e : launch_attn(d, ws_d, st);
   }
   const AttnPlan ps = plan_attn(s), pd = plan_attn(d);
-  auto parts = [](const AttnPlan& pl, void* ws, float** po, float** pml) {
+  auto parts = [](const AttnPlan& pl, void* ws, _Float16** po, float** pml) {
     *po = nullptr;
     *pml = nullptr;
     if (pl.nsplit > 1) {
-      *po = reinterpret_cast<float*>(ws);
+      *po = reinterpret_cast<_Float16*>(ws);
       *pml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + pl.po_bytes);
     }
   };
-  float *po_s, *pml_s, *po_d, *pml_d;
+  _Float16 *po_s, *po_d;
+  float *pml_s, *pml_d;
   parts(ps, ws_s, &po_s, &pml_s);
   parts(pd, ws_d, &po_d, &pml_d);
   const AttnK ks = attn_k(s, ps, po_s, pml_s), kd = attn_k(d, pd, po_d, pml_d);
@@ -835,26 +871,17 @@ hipError_t launch_attn_pair(const AttnArgs& s, void* ws_s, const AttnArgs& d, vo
   const bool ms = ps.nsplit > 1, md = pd.nsplit > 1;
   const bool fast = merge_fast(s.h, s.d, ps.nsplit) && merge_fast(d.h, d.d, pd.nsplit);
   LaunchScope ls("attn_merge", st);
-  const MergeK mks{po_s, pml_s, ps.nsplit, s.out, s.lse}, mkd{po_d, pml_d, pd.nsplit, d.out, d.lse};
+  const MergeK<_Float16> mks{po_s, pml_s, ps.nsplit, s.out, s.lse}, mkd{po_d, pml_d, pd.nsplit, d.out, d.lse};
   const unsigned gx = unsigned(s.h * s.d / 256);
   if (ms && md && fast) {
-    HATTN_LAUNCH(attn_merge_pair_kernel, dim3(gx, unsigned(rows_s + rows_d)), dim3(256), 0, st, mks, rows_s, mkd,
-                 s.h, s.d);
+    HATTN_LAUNCH((attn_merge_pair_kernel<_Float16>), dim3(gx, unsigned(rows_s + rows_d)), dim3(256), 0, st, mks,
+                 rows_s, mkd, s.h, s.d);
     return hipGetLastError();
   }
   for (int r = 0; r < 2; ++r) {
     const bool need = r == 0 ? ms : md;
     if (!need) continue;
-    const AttnPlan& pl = r == 0 ? ps : pd;
-    const AttnArgs& a = r == 0 ? s : d;
-    float* po = r == 0 ? po_s : po_d;
-    float* pml = r == 0 ? pml_s : pml_d;
-    if (merge_fast(a.h, a.d, pl.nsplit))
-      HATTN_LAUNCH(attn_merge_kernel, dim3(unsigned(a.h * a.d / 256), unsigned(a.bt * a.nq)), dim3(256), 0, st,
-                   MergeK{po, pml, pl.nsplit, a.out, a.lse}, a.h, a.d);
-    else
-      HATTN_LAUNCH(attn_merge_any_kernel, dim3(unsigned((a.h * a.d + 255) / 256), unsigned(a.bt * a.nq)), dim3(256),
-                   0, st, po, pml, pl.nsplit, a.h, a.d, a.out, a.lse);
+    launch_merge(r == 0 ? s : d, r == 0 ? ps : pd, r == 0 ? po_s : po_d, r == 0 ? pml_s : pml_d, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -240,7 +240,11 @@ hattn_status_t hattn_block_sparse_topk(int dtype, const void* q_i, const void* k
  * Requires window >= 1 and d a multiple of 8.  bf16 with d in {64, 128}
  * and h in {16, 32} or a multiple of 64 up to 1,024 runs on MFMA (64 heads
  * per workgroup); any other shape with h*d <= 8192 and d <= 256 takes the
- * vector path.  Layers that share one cache and one index list (CSA2's
+ * vector path.  Arithmetic: fp32 accumulation; on the MFMA path the
+ * softmax weights enter the PV product in bf16 and, when a query's key
+ * list is split over several workgroups, each split's normalised output
+ * O/l is kept in fp16 in the workspace (with its max and sum in fp32)
+ * until the merge; the fp32 vector path keeps fp32 throughout.  Layers that share one cache and one index list (CSA2's
  * cross-layer reuse, [HCA] section V4.1 为什么不要它了) are one call: with
  * MQA every head attends to the same keys, so layer g's head j is head
  * g*h_layer + j of q, out and lse.

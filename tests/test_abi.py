@@ -185,16 +185,16 @@ def test_decode_plan_validation(L):
 
 
 def test_sparse_attn_noalloc_rejects_oversize(L):
-    # 600 fp32 queries with 2,048 + 128 keys split in two chunks need
-    # 600 * 2 * 64 * 128 * 4 bytes (39.3 MB) of partials, more than the
-    # 32 MiB static scratch: refused before any launch.
+    # 600 bf16 queries with 30,000 + 128 keys split in 15 chunks of 2,048
+    # need 600 * 15 * 64 * 128 * 2 bytes (147 MB) of fp16 partials, more than
+    # the 32 MiB static scratch: refused before any launch.
     f = L.hattn_sparse_attn_noalloc
     p = ctypes.c_void_p(256)
-    st = f(0, p, p, 4000, p, 2048, p, 9000, 0, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p, None, None)
+    st = f(1, p, p, 4000, p, 30000, p, 9000, 0, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p, None, None)
     assert st == 3, L.hattn_last_error()
     assert b"static" in L.hattn_last_error()
     # the same call with a workspace would need more than 32 MiB
     sz = ctypes.c_size_t(0)
-    assert L.hattn_sparse_attn(0, p, p, 4000, p, 2048, p, 9000, 0, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128, p,
-                               None, None, ctypes.byref(sz), None) == 0
+    assert L.hattn_sparse_attn(1, p, p, 4000, p, 30000, p, 9000, 0, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128,
+                               p, None, None, ctypes.byref(sz), None) == 0
     assert sz.value > 32 << 20
