@@ -223,3 +223,33 @@ def test_ring_window_reads_match_full(h, d, dt):
         ro, rl = oracle.sparse_attention(f64(q[b]), f64(ckv[b]), idx[b].cpu().numpy(), f64(raw[b]), np.array(pp),
                                          128, 1 / math.sqrt(d))
         _check(o_ring[b], l_ring[b], ro, rl)
+
+
+@pytest.mark.parametrize("vscale,qscale", [(1000.0, 1.0), (1.0, 6.0)])
+def test_split_partials_large_values(vscale, qscale):
+    # Long key lists split over several workgroups, whose partial outputs are
+    # kept as fp16 O/l: V rows of magnitude ~1,000 (O/l is a convex
+    # combination of them, far below fp16's 65,504) and sharp logits (q x 6,
+    # the lazy rescale moving often).  The error must stay within the bound
+    # of the arithmetic: |err| <= (2^-9 for the bf16 weights + 2^-11 for the
+    # fp16 partial) * max |V|, with a factor 4 for accumulation.
+    bt, nq, N, L, h, d = 2, 3, 8000, 9000, 64, 128
+    dt = torch.bfloat16
+    raw = synth.normal((bt, L, 2 * d), 120, dtype=dt)
+    ckv = synth.normal((bt, N, 2 * d), 121, dtype=dt)
+    raw[..., d:] = (raw[..., d:].float() * vscale).to(dt)
+    ckv[..., d:] = (ckv[..., d:].float() * vscale).to(dt)
+    q = (synth.normal((bt, nq, h, d), 122) * qscale).to(dt)
+    pos = torch.tensor([[8999, 5000, 300]] * bt, dtype=torch.int32)
+    nv = torch.tensor([[N, 1200, 9], [N - 1, 4000, 50]], dtype=torch.int32)
+    out, lse = ops.dense_compressed_attn(q.to(DEV), ckv.to(DEV), nv.to(DEV), raw.to(DEV), pos.to(DEV), 128,
+                                         return_lse=True)
+    torch.cuda.synchronize()
+    vmax = float(max(raw[..., d:].float().abs().max(), ckv[..., d:].float().abs().max()))
+    bound = 4 * (2.0**-9 + 2.0**-11) * vmax
+    for b in range(bt):
+        ro, rl = oracle.dense_compressed_attention(f64(q[b]), f64(ckv[b]), nv[b].numpy(), f64(raw[b]),
+                                                   pos[b].numpy(), 128, 1 / math.sqrt(d))
+        err = float(np.abs(f64(out[b]) - ro).max())
+        assert err <= bound, (vscale, qscale, b, err, bound)
+        assert float(np.abs(f64(lse[b]) - rl).max()) <= 1e-2
