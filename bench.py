@@ -619,6 +619,106 @@ def _oracle_decode_rate(k, seconds):
     return done, el
 
 
+def _median_s(fn, reps=3):
+    import numpy as np
+
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_configs():
+    """The fp64 oracle on the host for the other configurations, in the GPU's
+    units, each bounded to a few seconds: the tiny layer in full (median of
+    3); the CSA prefill chunk with its compression in full and the indexer
+    and attention on 64 of its 1,024 queries; HCA decode: one query's
+    attention, and the compression of 1/16 of a 2^20-token sequence; the 128K
+    indexer chunk: pooling in full, flat and HISA selection on 16 of its
+    1,024 queries.  Sampled parts are scaled to the whole and say so."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from compressed_attention_amd import synth
+
+    f = lambda x: x.double().numpy()  # noqa: E731
+    out = {}
+    # tiny hybrid layer (fp32), whole layer
+    t, P = (lambda w: (w.tensors, w.params))(synth.tiny_hybrid_layer(0))
+    raw, z, pos = f(t["raw_kv"][0]), f(t["z"][0]), t["q_pos"][0].numpy()
+
+    def tiny():
+        ckv = oracle.compress(raw, z, f(t["b_csa"]), 8, 4)
+        nv = np.array([oracle.n_visible(int(p), 8, 4, ckv.shape[0]) for p in pos])
+        idx = oracle.flat_topk(f(t["q_i"][0]), f(t["k_i"][0]), f(t["w_i"][0]), nv, P["k"])
+        oracle.sparse_attention(f(t["q"][0]), ckv, idx, raw, pos, 128, 1 / 8)
+        hkv = oracle.compress(raw, z, f(t["b_hca"]), 128, 128)
+        nvh = np.array([oracle.n_visible(int(p), 128, 128, hkv.shape[0]) for p in pos])
+        oracle.dense_compressed_attention(f(t["q"][0]), hkv, nvh, raw, pos, 128, 1 / 8)
+
+    out["tiny_layer_fp32"] = dict(ms=round(_median_s(tiny) * 1e3, 2), sample="whole layer, median of 3")
+    # CSA prefill chunk
+    t = synth.csa_prefill_chunk(0).tensors
+    raw, z, b = f(t["raw_kv"][0]), f(t["z"][0]), f(t["b"])
+    t0 = time.perf_counter()
+    ckv = oracle.compress(raw, z, b, 8, 4)
+    comp_s = time.perf_counter() - t0
+    rows = np.arange(0, 1024, 16)
+    pos = t["q_pos"][0].numpy()[rows]
+    nv = np.array([oracle.n_visible(int(p), 8, 4, ckv.shape[0]) for p in pos])
+    t0 = time.perf_counter()
+    idx = oracle.flat_topk(f(t["q_i"][0, rows]), f(t["k_i"][0]), f(t["w_i"][0, rows]), nv, 512)
+    idx_s = (time.perf_counter() - t0) * 1024 / len(rows)
+    t0 = time.perf_counter()
+    oracle.sparse_attention(f(t["q"][0, rows]), ckv, idx, raw, pos, 128, 1 / math.sqrt(128))
+    attn_s = (time.perf_counter() - t0) * 1024 / len(rows)
+    chunk_s = comp_s + idx_s + attn_s
+    out["csa_prefill_32k_chunk1024"] = dict(
+        ms=round(chunk_s * 1e3, 1), tokens_per_s=round(1024 / chunk_s, 1),
+        stage_ms=dict(compress=round(comp_s * 1e3, 1), index=round(idx_s * 1e3, 1), attention=round(attn_s * 1e3, 1)),
+        sample="compression in full; indexer and attention on 64 of the 1,024 queries, scaled by 16")
+    del t, raw, ckv
+    # HCA decode: one query's attention over 8,192 entries + window; the
+    # compression of a sequence from 1/16 of it
+    hkv = synth.normal((8192, 256), 911, dtype=torch.bfloat16).double().numpy()
+    tail = synth.normal((128, 256), 912, dtype=torch.bfloat16).double().numpy()
+    q = synth.normal((1, 64, 128), 913, dtype=torch.bfloat16).double().numpy()
+    att_s = _median_s(lambda: oracle.dense_compressed_attention(q, hkv, [8192], tail, np.array([127]), 128,
+                                                               1 / math.sqrt(128)))
+    seg = synth.normal((65536, 256), 914, dtype=torch.bfloat16).double().numpy()
+    zs = synth.normal((65536,), 915).double().numpy()
+    bs = synth.tiled_bias(128, 128, 916).double().numpy()
+    t0 = time.perf_counter()
+    oracle.compress(seg, zs, bs, 128, 128)
+    comp_s = (time.perf_counter() - t0) * 16
+    out["hca_decode"] = dict(
+        queries_per_s=round(1 / att_s, 1), compress_1M_tokens_s=round(comp_s, 2),
+        sample="one query's attention (median of 3); compression of 65,536 tokens scaled by 16 to one sequence")
+    del hkv, seg
+    # 128K indexer chunk
+    t = synth.indexer_128k(0).tensors
+    k_i = f(t["k_i"][0])
+    rows = np.arange(0, 1024, 64)
+    nv = t["entry_pos"][0].numpy()[rows] + 1
+    q_i, w_i = f(t["q_i"][0, rows]), f(t["w_i"][0, rows])
+    t0 = time.perf_counter()
+    reps = oracle.hisa_pool(k_i, 128)
+    pool_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.flat_topk(q_i, k_i, w_i, nv, 2048)
+    flat_s = (time.perf_counter() - t0) * 1024 / len(rows)
+    t0 = time.perf_counter()
+    oracle.hisa_topk(q_i, k_i, w_i, nv, 128, 64, 2048, reps=reps)
+    hisa_s = (time.perf_counter() - t0) * 1024 / len(rows) + pool_s
+    out["indexer_128k"] = dict(
+        flat_ms=round(flat_s * 1e3, 1), hisa_ms=round(hisa_s * 1e3, 1), hisa_pool_ms=round(pool_s * 1e3, 1),
+        sample="pooling in full; flat and HISA selection on 16 of the 1,024 queries, scaled by 64")
+    return out
+
+
 def cpu_baseline(args, k):
     """The oracle timed twice on the host: with the BLAS pool as the process
     starts it (all of the host share) and limited to one thread."""
@@ -902,6 +1002,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, main_k)
+        line["cpu_baseline"]["other_configs"] = cpu_configs()
     print(json.dumps(line), flush=True)
 
 
