@@ -186,35 +186,52 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
   uint16_t* vt = lds.vt;
   uint64_t* vmask = lds.vmask;
 
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int HT = H * a.hg;                        // heads of the query row
+  const int head = hgroup * H + 16 * wave + r16;  // this lane's head in the row
+  // Loads that need no other load go first: the query fragments and the
+  // speculative first tile below.
+  u32x4_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(q + (qrow * HT + head) * D + 32 * ks + 8 * g);
   const int64_t b = idiv(qrow, nq);
-  const int64_t p = q_pos[qrow];
-  const int nw = int(imax64(0, imin64(window, p + 1)));
-  const int64_t nc = SPARSE ? int64_t(k) : imin64(n, imax64(0, n_vis[qrow]));
-  const int total = int(nc) + nw;
   const int j_begin = split * chunk;
+  const uint16_t* ckv_b = ckv + b * n * C;
+  // Dense chunks whose first tile lies inside the cache (rows j_begin ..
+  // j_begin + TK - 1 < n) issue that tile's loads before the query's
+  // position and visible count arrive, so the first tile costs one memory
+  // round trip instead of two.  The data is kept when the tile is a plain
+  // run of compressed rows (exactly the rows fetch() reads then), and
+  // fetched again otherwise.
+  const bool spec = !SPARSE && int64_t(j_begin) + TK <= n;
+  u32x4_t pre[PIECES];
+  if (spec) {
+#pragma unroll
+    for (int u = 0; u < PIECES; ++u) {
+      const int pidx = tid + NT * u;
+      const uint16_t* src = ckv_b + size_t(j_begin) * C + (pidx / PPR) * C + (pidx % PPR) * 8;
+      pre[u] = STREAM ? ld16_nt(src) : ld16(src);
+    }
+  }
+  const int64_t p = q_pos[qrow];
+  const int64_t nv_raw = SPARSE ? 0 : n_vis[qrow];
+  const int nw = int(imax64(0, imin64(window, p + 1)));
+  const int64_t nc = SPARSE ? int64_t(k) : imin64(n, imax64(0, nv_raw));
+  const int total = int(nc) + nw;
   const int j_end = min(total, j_begin + chunk);
   const int32_t* idx_row = SPARSE ? idx + qrow * k : nullptr;
-  const uint16_t* ckv_b = ckv + b * n * C;
   const int R = a.R;
   const uint16_t* raw_b = raw + b * (R ? int64_t(R) : L) * C;
   const int rbase = int(p) - nw + 1 - int(nc);
   const int n32 = int(n), L32 = int(L), nc32 = int(nc);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, r16 = lane & 15;
-  const int HT = H * a.hg;                      // heads of the query row
-  const int head = hgroup * H + 16 * wave + r16;  // this lane's head in the row
-
-  u32x4_t qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = ld16(q + (qrow * HT + head) * D + 32 * ks + 8 * g);
   f32x4_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  u32x4_t pre[PIECES];
   // A tile is "plain" when all its TK keys exist and sit in one contiguous
   // run of rows (dense entries, or window rows): then row r is base + r*C
   // and every key is valid.  Other tiles take the general per-row path.
@@ -261,7 +278,10 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
     for (int t = tid; j_begin + t < cend; t += NT) sidx[t] = idx_row[j_begin + t];
     __syncthreads();
   }
-  if (j_begin < j_end) fetch(j_begin);
+  // the speculative tile is the one fetch() would load iff plain_base(j_begin)
+  // is ckv_b + j_begin * C
+  const bool spec_ok = spec && j_begin + TK <= j_end && j_begin + TK <= nc32;
+  if (j_begin < j_end && !spec_ok) fetch(j_begin);
   for (int j0 = j_begin; j0 < j_end; j0 += TK) {
 #pragma unroll
     for (int u = 0; u < PIECES; ++u) {
