@@ -97,6 +97,29 @@ def test_shapes_and_edges_dense(h, d):
         _check(out[b], lse[b], ro, rl)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_dense_decode_ragged_visible_counts(d):
+    """One query per sequence (the decode launch: streamed K|V, chunks of
+    128 keys over 3,000 entries) with visible counts from 0 to all entries:
+    a chunk's first tile is loaded before its query's visible count is
+    known, and must be dropped and fetched again wherever the tile is not
+    a full run of visible entries (chunks past the count, the window's
+    chunk, empty chunks)."""
+    bt, L, N, h = 8, 4000, 3000, 64
+    dt = torch.bfloat16
+    raw = synth.normal((bt, L, 2 * d), 110 + d, dtype=dt).to(DEV)
+    ckv = synth.normal((bt, N, 2 * d), 111 + d, dtype=dt).to(DEV)
+    q = synth.normal((bt, 1, h, d), 112 + d, dtype=dt).to(DEV)
+    pos = torch.tensor([[0], [5], [300], [1000], [1999], [2500], [3998], [3999]], dtype=torch.int32)
+    nv = torch.tensor([[0], [1], [63], [64], [65], [1500], [2999], [3000]], dtype=torch.int32)
+    out, lse = ops.dense_compressed_attn(q, ckv, nv.to(DEV), raw, pos.to(DEV), 128, return_lse=True)
+    torch.cuda.synchronize()
+    for b in range(bt):
+        ro, rl = oracle.dense_compressed_attention(f64(q[b]), f64(ckv[b]), nv[b].numpy(), f64(raw[b]),
+                                                   pos[b].numpy(), 128, 1 / math.sqrt(d))
+        _check(out[b], lse[b], ro, rl)
+
+
 def test_sparse_edges_and_all_entries_equal_dense():
     bt, nq, L, N, d, h = 2, 6, 700, 300, 128, 64
     dt = torch.bfloat16
