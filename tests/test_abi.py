@@ -177,6 +177,16 @@ def test_decode_plan_validation(L):
     assert L.hattn_decode_plan_ws_bytes(ctypes.byref(d), ctypes.byref(sz)) == 1
     assert b"aligned" in L.hattn_last_error()
     d.csa_q = p
+    # raw rings: at least the window and both compression windows, at most L rows
+    for rows, ok in ((128, True), (4096, True), (64, False), (127, False), (4097, False), (-1, False)):
+        d.raw_rows = rows
+        st = L.hattn_decode_plan_ws_bytes(ctypes.byref(d), ctypes.byref(sz))
+        assert (st == 0) == ok, (rows, st, L.hattn_last_error())
+        if not ok:
+            assert b"raw_rows" in L.hattn_last_error() or b"ring" in L.hattn_last_error()
+    d.hca_w, d.hca_stride, d.raw_rows = 256, 256, 128  # the HCA window does not fit the ring
+    assert L.hattn_decode_plan_ws_bytes(ctypes.byref(d), ctypes.byref(sz)) == 1
+    d.hca_w, d.hca_stride, d.raw_rows = 128, 128, 0
     d.ws, d.ws_bytes = p, 16  # too small: refused before any device work
     assert L.hattn_decode_plan_create(ctypes.byref(d), ctypes.byref(plan)) == 3
     assert L.hattn_decode_plan_destroy(None) == 0
