@@ -1400,7 +1400,7 @@ __global__ __launch_bounds__(kSampNT, 4) void select_sampled_kernel(const float*
   uint32_t* samp = rkey;
   __shared__ SelectShared<kSampNT> sh;
   __shared__ int wcnt[NW];
-  __shared__ int verdict;
+  __shared__ int bracket;
   // One row per trip (a gated launch uses a small grid and loops over the
   // rows; each row's work ends with a return from the lambda).
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
@@ -1507,10 +1507,10 @@ __global__ __launch_bounds__(kSampNT, 4) void select_sampled_kernel(const float*
             tot += wcnt[w];
             ovf |= wcnt[w] > kRegion;
           }
-          verdict = ovf ? 1 : (tot < k ? 2 : 0);  // 1: tau too low, 2: tau too high
+          bracket = ovf ? 1 : (tot < k ? 2 : 0);  // 1: tau too low, 2: tau too high
         }
         __syncthreads();
-        const int vd = verdict;
+        const int vd = bracket;
         if (vd == 0) {
           for (int t = min(cnt, kRegion) + lane; t < kRegion; t += 64) rk[t] = 0u;
           done = true;
