@@ -850,6 +850,27 @@ def roofline_entry(kern_ms, nbytes):
     return gbs
 
 
+def measured_copy_GBps(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """HBM bandwidth of a plain device-to-device copy of nbytes (read +
+    written bytes per second), reported beside the 8 TB/s spec peak."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbps = 2.0 * nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -968,6 +989,10 @@ def main():
     if dom_bytes:
         a = dom_bytes / (dom_ms * 1e-3) / 1e9
         roof.update(achieved=round(a, 1), frac=round(a / HBM_PEAK_GBS, 4), algorithmic_bytes=dom_bytes)
+    copy_gbps = measured_copy_GBps()
+    roof["measured_copy_GBps"] = round(copy_gbps, 1)
+    if dom_bytes:
+        roof["frac_of_measured_copy"] = round(roof["achieved"] / copy_gbps, 4)
     line = {
         "metric": "decode queries/s at 1M context (CSA+HCA hybrid layer pair, HISA top-k)",
         "value": round(res["bt"] / (ms * 1e-3), 1),
