@@ -489,6 +489,32 @@ def csa_prefill(args):
                 compress_bytes=32768 * 512 + 32768 * 4 + N * 512)
 
 
+def tiny_layer(args):
+    """The tiny fp32 hybrid layer (64 queries at 4K; the parity workload),
+    timed for information: both branches (compression, visible counts, flat
+    top-64, sparse attention; compression, dense attention), one graph."""
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    w = synth.tiny_hybrid_layer(0, device=dev)
+    t, P = w.tensors, w.params
+
+    def step(_):
+        ckv = ops.compress(t["raw_kv"], t["z"], t["b_csa"], 8, 4)
+        nv = ops.visible_count(t["q_pos"], 8, 4, ckv.shape[1])
+        idx = ops.index_topk(t["q_i"], t["k_i"], t["w_i"], nv, P["k"])
+        o1 = ops.sparse_attn(t["q"], ckv, idx, t["raw_kv"], t["q_pos"], P["window"])
+        hkv = ops.compress(t["raw_kv"], t["z"], t["b_hca"], 128, 128)
+        nvh = ops.visible_count(t["q_pos"], 128, 128, hkv.shape[1])
+        o2 = ops.dense_compressed_attn(t["q"], hkv, nvh, t["raw_kv"], t["q_pos"], P["window"])
+        return o1, o2
+
+    graphs = capture(step, [None])
+    ms = timed_graphs(graphs, 30, 3)
+    del graphs
+    return dict(ms=ms, nq=P["nq"])
+
+
 def indexer_128k(args):
     import numpy as np
     import torch
@@ -941,6 +967,10 @@ def main():
             note="rate-2 cache (w=4, s=2), flat top-512 over the compressed indexer keys, 2 layers as 128 heads; "
                  "hisa_*: the same step with HISA (B=128, m=16) selecting the top-512")
         torch.cuda.empty_cache()
+        tl = tiny_layer(args)
+        extras["tiny_layer_fp32"] = dict(ms=tl["ms"], queries_per_s=tl["nq"] / (tl["ms"] * 1e-3),
+                                         note="parity workload (64 queries, both branches, fp32), one graph "
+                                              "replay; for information")
         cp = csa_prefill(args)
         ck = {kk: v[0] for kk, v in cp["kernels"].items()}
         sk = ck.get("score_flat_mfma", float("nan"))
