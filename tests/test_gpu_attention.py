@@ -80,7 +80,7 @@ def test_hca_decode_full_size_sampled():
         _check(out[b], lse[b], ro, rl)
 
 
-@pytest.mark.parametrize("h,d", [(64, 128), (32, 128), (16, 128), (16, 64), (64, 64), (8, 128), (24, 64)])
+@pytest.mark.parametrize("h,d", [(64, 128), (32, 128), (16, 128), (16, 64), (32, 64), (64, 64), (8, 128), (24, 64)])
 def test_shapes_and_edges_dense(h, d):
     bt, nq, L, N = 2, 9, 900, 200
     dt = torch.bfloat16
