@@ -156,6 +156,69 @@ def test_decode_plan_matches_separate_calls_and_oracle():
     plan.close()
 
 
+@pytest.mark.parametrize("h,d", [(16, 128), (32, 64), (64, 64)])
+def test_decode_plan_head_shapes(h, d):
+    """The decode plan's paired attention launch for other head counts and
+    sizes (16 or 32 heads per query, d = 64): bit-exact against the separate
+    calls, and within 1e-2 of the oracle (integer-grid indexer, so that both
+    select the same entries)."""
+    bt, L = 2, 8192
+    N = oracle.n_entries(L, 8, 4)
+    Nh = oracle.n_entries(L, 128, 128)
+    bf = torch.bfloat16
+    t = {
+        "csa_raw_kv": synth.normal((bt, L, 2 * d), 401, dtype=bf),
+        "csa_z": synth.normal((bt, L), 402),
+        "csa_b": synth.tiled_bias(4, 8, 403),
+        "csa_q": synth.normal((bt, 1, h, d), 404, dtype=bf),
+        "q_i": synth.int_grid((bt, 1, 16, 128), 405, -4, 4, dtype=bf),
+        "k_i": synth.int_grid((bt, N, 128), 406, -4, 4, dtype=bf),
+        "w_i": synth.dyadic_uniform((bt, 1, 16), 407, bits=4),
+        "hca_raw_kv": synth.normal((bt, L, 2 * d), 408, dtype=bf),
+        "hca_z": synth.normal((bt, L), 409),
+        "hca_b": synth.tiled_bias(128, 128, 410),
+        "hca_q": synth.normal((bt, 1, h, d), 411, dtype=bf),
+        "q_pos": torch.tensor([[L - 1], [L - 3]], dtype=torch.int32),
+    }
+    g = {k_: v.to(DEV) for k_, v in t.items()}
+    B, m, k = 128, 4, 128
+    ckv = ops.compress(g["csa_raw_kv"], g["csa_z"], g["csa_b"], 8, 4)
+    hkv = ops.compress(g["hca_raw_kv"], g["hca_z"], g["hca_b"], 128, 128)
+    ckv[:, N - 1] = 0  # completed by the step
+    hkv[:, Nh - 1] = 0
+    reps = ops.hisa_pool(g["k_i"], B)
+    ckv2, hkv2, reps2 = ckv.clone(), hkv.clone(), reps.clone()
+    plan = ops.DecodePlan(q_pos=g["q_pos"], csa_raw_kv=g["csa_raw_kv"], csa_logits=g["csa_z"], csa_pos_bias=g["csa_b"],
+                          csa_ckv=ckv, k_i=g["k_i"], reps=reps, q_i=g["q_i"], w_i=g["w_i"], csa_q=g["csa_q"],
+                          hca_raw_kv=g["hca_raw_kv"], hca_logits=g["hca_z"], hca_pos_bias=g["hca_b"], hca_ckv=hkv,
+                          hca_q=g["hca_q"], B=B, m=m, k=k, return_lse=True)
+    o1, o2 = plan.run()
+    nv = ops.decode_append(g["csa_raw_kv"], g["csa_z"], g["csa_b"], 8, 4, g["q_pos"], ckv2, g["k_i"], reps2, B)
+    idx = ops.hisa_topk(g["q_i"], g["k_i"], g["w_i"], nv, reps2, B, m, k)
+    s1, l1 = ops.sparse_attn(g["csa_q"], ckv2, idx, g["csa_raw_kv"], g["q_pos"], 128, return_lse=True)
+    nvh = ops.decode_append(g["hca_raw_kv"], g["hca_z"], g["hca_b"], 128, 128, g["q_pos"], hkv2)
+    s2, l2 = ops.dense_compressed_attn(g["hca_q"], hkv2, nvh, g["hca_raw_kv"], g["q_pos"], 128, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ckv, ckv2) and torch.equal(hkv, hkv2) and torch.equal(reps, reps2)
+    assert torch.equal(o1, s1) and torch.equal(o2, s2)
+    assert torch.equal(plan.csa_lse, l1) and torch.equal(plan.hca_lse, l2)
+    sc = 1 / math.sqrt(d)
+    for b in range(bt):
+        raw_c, raw_h = f64(t["csa_raw_kv"][b]), f64(t["hca_raw_kv"][b])
+        p = int(t["q_pos"][b, 0])
+        r_ckv = oracle.compress(raw_c, f64(t["csa_z"][b]), f64(t["csa_b"]), 8, 4)
+        r_hkv = oracle.compress(raw_h, f64(t["hca_z"][b]), f64(t["hca_b"]), 128, 128)
+        nv_c = oracle.n_visible(p, 8, 4, N)
+        nv_h = oracle.n_visible(p, 128, 128, Nh)
+        r_idx, _ = oracle.hisa_topk(f64(t["q_i"][b]), f64(t["k_i"][b]), f64(t["w_i"][b]), np.array([nv_c]), B, m, k)
+        assert np.array_equal(idx[b].cpu().numpy(), r_idx)
+        r_o1, _ = oracle.sparse_attention(f64(t["csa_q"][b]), r_ckv, r_idx, raw_c, np.array([p]), 128, sc)
+        r_o2, _ = oracle.dense_compressed_attention(f64(t["hca_q"][b]), r_hkv, [nv_h], raw_h, np.array([p]), 128, sc)
+        assert np.abs(f64(o1[b]) - r_o1).max() < 1e-2
+        assert np.abs(f64(o2[b]) - r_o2).max() < 1e-2
+    plan.close()
+
+
 @pytest.mark.parametrize("dtype,d_i", [(torch.bfloat16, 48), (torch.float32, 48), (torch.bfloat16, 16),
                                        (torch.bfloat16, 32), (torch.float32, 128)])
 def test_decode_plan_indexer_widths(dtype, d_i):
