@@ -156,7 +156,7 @@ def test_decode_plan_matches_separate_calls_and_oracle():
     plan.close()
 
 
-@pytest.mark.parametrize("h,d", [(16, 128), (32, 64), (64, 64)])
+@pytest.mark.parametrize("h,d", [(16, 64), (16, 128), (32, 64), (32, 128), (64, 64)])
 def test_decode_plan_head_shapes(h, d):
     """The decode plan's paired attention launch for other head counts and
     sizes (16 or 32 heads per query, d = 64): bit-exact against the separate
@@ -220,12 +220,14 @@ def test_decode_plan_head_shapes(h, d):
 
 
 @pytest.mark.parametrize("dtype,d_i", [(torch.bfloat16, 48), (torch.float32, 48), (torch.bfloat16, 16),
-                                       (torch.bfloat16, 32), (torch.float32, 128)])
+                                       (torch.bfloat16, 32), (torch.bfloat16, 64), (torch.bfloat16, 256),
+                                       (torch.float32, 128)])
 def test_decode_plan_indexer_widths(dtype, d_i):
     # The decode plan at indexer widths that take each stage-1 path: 48 has no
     # MFMA instantiation (vector kernels), 16 has one but its LDS tile is too
-    # small for the fused front kernel's cache-maintenance scratch, 32 runs
-    # the fused front kernel; fp32 runs every step on the vector kernels.
+    # small for the fused front kernel's cache-maintenance scratch, 32, 64 and
+    # 256 run the fused front kernel; fp32 runs every step on the vector
+    # kernels.
     # Integer-grid indexer with 4-bit weights: the selection is exact.
     bt, L = 2, 16384
     N, Nh = oracle.n_entries(L, 8, 4), oracle.n_entries(L, 128, 128)
