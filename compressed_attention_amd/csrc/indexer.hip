@@ -2209,8 +2209,9 @@ hipError_t launch_decode_front(const IndexArgs& a, float* reps, int B, int m, vo
 #define HATTN_FRONT(KQ)                                                                                      \
   HATTN_LAUNCH(decode_front_kernel<KQ>, grid, dim3(256), 0, st, (const uint16_t*)a.q_i, reps, a.w_i, q_pos, B, \
                p.nb, p.ld1, S1, nch, nch_grid, la, lb, nroles)
+  // (d_i = 16 never gets here: its LDS tile cannot hold the append roles'
+  // scratch, so decode_front_ok sends it to the separate kernels)
   switch (a.d_i) {
-    case 16: HATTN_FRONT(1); break;
     case 32: HATTN_FRONT(2); break;
     case 64: HATTN_FRONT(4); break;
     case 128: HATTN_FRONT(8); break;

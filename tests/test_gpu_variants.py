@@ -107,6 +107,29 @@ def test_decode_shape_attention_every_mfma_shape(h, d):
         assert np.abs(f64(o_d[b]) - ro).max() < 1e-2 and np.abs(f64(l_d[b]) - rl).max() < 1e-2, b
 
 
+@pytest.mark.parametrize("h,d", [(16, 64), (32, 64), (32, 128)])
+def test_sparse_multi_query_shapes(h, d):
+    # Several queries per sequence (K|V through L2) in sparse attention at the
+    # smaller MFMA head shapes; holes, out-of-range indices, partial windows.
+    bt, nq, L, N, k = 2, 6, 1500, 900, 200
+    dt = torch.bfloat16
+    raw = synth.normal((bt, L, 2 * d), 561 + d, dtype=dt).to(DEV)
+    ckv = synth.normal((bt, N, 2 * d), 562 + d, dtype=dt).to(DEV)
+    q = synth.normal((bt, nq, h, d), 563 + h, dtype=dt).to(DEV)
+    pos = torch.tensor([[0, 5, 127, 128, 900, 1499]] * bt, dtype=torch.int32)
+    nv = torch.tensor([[0, 1, 30, 31, 224, 373], [900, 17, 0, 400, 2, 899]], dtype=torch.int32)
+    idx = synth.random_index_lists(nv.reshape(-1), k, seed=564 + h, n_pad_holes=4).reshape(bt, nq, k)
+    idx[1, 3, 10] = N + 5  # out of range: skipped
+    out, lse = ops.sparse_attn(q, ckv, idx.to(DEV), raw, pos.to(DEV), 128, return_lse=True)
+    torch.cuda.synchronize()
+    for b in range(bt):
+        ii = idx[b].numpy().copy()
+        ii[ii >= N] = -1
+        ro, rl = oracle.sparse_attention(f64(q[b]), f64(ckv[b]), ii, f64(raw[b]), pos[b].numpy(), 128,
+                                         1 / math.sqrt(d))
+        assert np.abs(f64(out[b]) - ro).max() < 1e-2 and np.abs(f64(lse[b]) - rl).max() < 1e-2, b
+
+
 def test_merge_of_many_splits():
     # One query over 20,000 entries: 158 splits of 128 keys, more than the
     # fast merge holds (64), so the general merge combines them.
