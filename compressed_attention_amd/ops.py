@@ -39,6 +39,18 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be shaped {list(shape)}, got {list(t.shape)}")
+
+
+def _on(dev, *named) -> None:
+    """Every given tensor must sit on the device the call runs on."""
+    for name, t in named:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}; the call runs on {dev}")
+
+
 def _fdt(t: torch.Tensor, name: str) -> int:
     if t.dtype not in _DT:
         raise TypeError(f"{name} must be float32 or bfloat16")
@@ -93,6 +105,7 @@ def compress(x, logits, pos_bias, w: int, stride: int, e_begin: int = 0, e_end: 
         _need(out, "out", x.dtype, 3)
         if tuple(out.shape) != (bt, N, C):
             raise ValueError(f"out must be [{bt}][{N}][{C}]")
+    _on(x.device, ("logits", logits), ("pos_bias", pos_bias), ("out", out))
     check("hattn_compress", lib().hattn_compress(dt, _ptr(x), bt, L, C, _ptr(logits), _ptr(pos_bias), w, stride,
                                                  e_begin, e_end, _ptr(out), _stream(x.device)))
     return out
@@ -113,14 +126,19 @@ def compress_with_index(x, x_i, logits, pos_bias, w: int, stride: int, e_begin: 
     N = (L - w) // stride + 1 if L >= w else 0
     if logits is not None:
         _need(logits, "logits", torch.float32, 2)
+        _shape(logits, "logits", (bt, L))
     if pos_bias is not None:
         _need(pos_bias, "pos_bias", torch.float32, 1)
+        _shape(pos_bias, "pos_bias", (w,))
     if e_end is None:
         e_end = N
     out = torch.empty((bt, N, C), dtype=x.dtype, device=x.device) if out is None else out
     out_i = torch.empty((bt, N, C_i), dtype=x.dtype, device=x.device) if out_i is None else out_i
     _need(out, "out", x.dtype, 3)
     _need(out_i, "out_i", x.dtype, 3)
+    _shape(out, "out", (bt, N, C))
+    _shape(out_i, "out_i", (bt, N, C_i))
+    _on(x.device, ("x_i", x_i), ("logits", logits), ("pos_bias", pos_bias), ("out", out), ("out_i", out_i))
     check("hattn_compress_with_index",
           lib().hattn_compress_with_index(dt, _ptr(x), _ptr(x_i), bt, L, C, C_i, _ptr(logits), _ptr(pos_bias), w,
                                           stride, e_begin, e_end, _ptr(out), _ptr(out_i), _stream(x.device)))
@@ -139,11 +157,14 @@ def compress_channel_logits(x, logits, pos_bias, w: int, stride: int, e_begin: i
         raise ValueError("logits must be [bt][L][C]")
     if pos_bias is not None:
         _need(pos_bias, "pos_bias", torch.float32, 1)
+        _shape(pos_bias, "pos_bias", (w,))
     N = (L - w) // stride + 1 if L >= w else 0
     if e_end is None:
         e_end = N
     out = torch.empty((bt, N, C), dtype=x.dtype, device=x.device) if out is None else out
     _need(out, "out", x.dtype, 3)
+    _shape(out, "out", (bt, N, C))
+    _on(x.device, ("logits", logits), ("pos_bias", pos_bias), ("out", out))
     check("hattn_compress_channel_logits",
           lib().hattn_compress_channel_logits(dt, _ptr(x), bt, L, C, _ptr(logits), _ptr(pos_bias), w, stride, e_begin,
                                               e_end, _ptr(out), _stream(x.device)))
@@ -155,6 +176,9 @@ def visible_count(pos, w: int, stride: int, n_entries: int, out=None):
     _need(pos, "pos", torch.int32)
     if out is None:
         out = torch.empty_like(pos)
+    _need(out, "out", torch.int32)
+    _shape(out, "out", pos.shape)
+    _on(pos.device, ("out", out))
     check("hattn_visible_count", lib().hattn_visible_count(_ptr(pos), pos.numel(), w, stride, n_entries, _ptr(out),
                                                            _stream(pos.device)))
     return out
@@ -181,8 +205,10 @@ def decode_append(x, logits, pos_bias, w: int, stride: int, q_pos, ckv, k_i=None
         raise ValueError(f"ckv must be [{bt}][{N}][{C}]")
     if logits is not None:
         _need(logits, "logits", torch.float32)
+        _shape(logits, "logits", (bt, rows))
     if pos_bias is not None:
         _need(pos_bias, "pos_bias", torch.float32)
+        _shape(pos_bias, "pos_bias", (w,))
     d_i = 0
     if k_i is not None or reps is not None:
         _need(k_i, "k_i", x.dtype, 3)
@@ -192,6 +218,10 @@ def decode_append(x, logits, pos_bias, w: int, stride: int, q_pos, ckv, k_i=None
             raise ValueError("k_i must be [bt][N][d_i] and reps [bt][ceil(N/B)][d_i]")
     if n_vis is None:
         n_vis = torch.empty(q_pos.shape, dtype=torch.int32, device=x.device)
+    _need(n_vis, "n_vis", torch.int32)
+    _shape(n_vis, "n_vis", q_pos.shape)
+    _on(x.device, ("logits", logits), ("pos_bias", pos_bias), ("q_pos", q_pos), ("ckv", ckv), ("k_i", k_i),
+        ("reps", reps), ("n_vis", n_vis))
     check("hattn_decode_append", lib().hattn_decode_append(dt, _ptr(x), bt, L, raw_rows, C, _ptr(logits),
                                                            _ptr(pos_bias), w, stride, _ptr(q_pos), _ptr(ckv),
                                                            _ptr(n_vis), _ptr(k_i), d_i, B, _ptr(reps),
@@ -208,6 +238,7 @@ def _index_common(q_i, k_i, w_i, n_vis):
     bt, nq, h_i, d_i = q_i.shape
     if k_i.shape[0] != bt or k_i.shape[2] != d_i or tuple(w_i.shape) != (bt, nq, h_i) or tuple(n_vis.shape) != (bt, nq):
         raise ValueError("indexer shapes disagree")
+    _on(q_i.device, ("k_i", k_i), ("w_i", w_i), ("n_vis", n_vis))
     return dt, bt, nq, h_i, d_i, k_i.shape[1]
 
 
@@ -239,6 +270,8 @@ def hisa_pool(k_i, B: int, j_begin: int = 0, j_end: int | None = None, out=None)
         out = torch.empty((bt, nb, d_i), dtype=torch.float32, device=k_i.device)
     else:
         _need(out, "out", torch.float32, 3)
+        _shape(out, "out", (bt, nb, d_i))
+        _on(k_i.device, ("out", out))
     check("hattn_hisa_pool", lib().hattn_hisa_pool(dt, _ptr(k_i), bt, n, d_i, B, j_begin, j_end, _ptr(out),
                                                    _stream(k_i.device)))
     return out
@@ -250,6 +283,7 @@ def hisa_topk(q_i, k_i, w_i, n_vis, reps, B: int, m: int, k: int, return_blocks:
     _need(reps, "reps", torch.float32, 3)
     if tuple(reps.shape) != (bt, -(-n // B), d_i):
         raise ValueError("reps must be [bt][ceil(n/B)][d_i]")
+    _on(q_i.device, ("reps", reps))
     idx = torch.empty((bt, nq, k), dtype=torch.int32, device=q_i.device)
     blk = torch.empty((bt, nq, m), dtype=torch.int32, device=q_i.device) if return_blocks else None
     L = lib()
@@ -270,6 +304,7 @@ def block_sparse_topk(q_i, k_i, w_i, n_vis, reps, B: int, m: int, return_blocks:
     _need(reps, "reps", torch.float32, 3)
     if tuple(reps.shape) != (bt, -(-n // B), d_i):
         raise ValueError("reps must be [bt][ceil(n/B)][d_i]")
+    _on(q_i.device, ("reps", reps))
     idx = torch.empty((bt, nq, m * B), dtype=torch.int32, device=q_i.device)
     blk = torch.empty((bt, nq, m), dtype=torch.int32, device=q_i.device) if return_blocks else None
     L = lib()
@@ -302,6 +337,7 @@ def _attn_common(q, ckv, raw_kv, q_pos):
         raise ValueError("K|V rows must be [.., 2*d]")
     if tuple(q_pos.shape) != (bt, nq):
         raise ValueError("q_pos must be [bt][nq]")
+    _on(q.device, ("ckv", ckv), ("raw_kv", raw_kv), ("q_pos", q_pos))
     return dt, bt, nq, h, d
 
 
@@ -315,6 +351,7 @@ def sparse_attn(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | None = N
     _need(idx, "idx", torch.int32, 3)
     if idx.shape[:2] != (bt, nq):
         raise ValueError("idx must be [bt][nq][k]")
+    _on(q.device, ("idx", idx))
     k = idx.shape[2]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out = torch.empty((bt, nq, h, d), dtype=torch.float32, device=q.device)
@@ -340,12 +377,16 @@ def sparse_attn_noalloc(q, ckv, idx, raw_kv, q_pos, window: int, scale: float | 
     _need(idx, "idx", torch.int32, 3)
     if idx.shape[:2] != (bt, nq):
         raise ValueError("idx must be [bt][nq][k]")
+    _on(q.device, ("idx", idx))
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if out is None:
         out = torch.empty((bt, nq, h, d), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, 4)
+    _shape(out, "out", (bt, nq, h, d))
     if lse is not None:
         _need(lse, "lse", torch.float32, 3)
+        _shape(lse, "lse", (bt, nq, h))
+    _on(q.device, ("out", out), ("lse", lse))
     check("hattn_sparse_attn_noalloc",
           lib().hattn_sparse_attn_noalloc(dt, _ptr(q), _ptr(ckv), ckv.shape[1], _ptr(idx), idx.shape[2], _ptr(raw_kv),
                                           L_raw, raw_rows, _ptr(q_pos), window, scale, bt, nq, h, d, _ptr(out),
@@ -360,6 +401,8 @@ def dense_compressed_attn(q, ckv, n_vis, raw_kv, q_pos, window: int, scale: floa
     dt, bt, nq, h, d = _attn_common(q, ckv, raw_kv, q_pos)
     L_raw, raw_rows = _ring_rows(raw_kv, L)
     _need(n_vis, "n_vis", torch.int32, 2)
+    _shape(n_vis, "n_vis", (bt, nq))
+    _on(q.device, ("n_vis", n_vis))
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out = torch.empty((bt, nq, h, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((bt, nq, h), dtype=torch.float32, device=q.device) if return_lse else None
@@ -440,8 +483,27 @@ class DecodePlan:
                         ("hca_pos_bias", hca_pos_bias)]:
             if t is not None:
                 _need(t, name, torch.float32)
-        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        # the caches the plan rewrites and reads, shaped as the layer
+        # geometry implies (the library sees only their addresses)
+        for name, t in [("csa_ckv", csa_ckv), ("hca_ckv", hca_ckv), ("hca_raw_kv", hca_raw_kv), ("csa_q", csa_q),
+                        ("hca_q", hca_q), ("k_i", k_i), ("q_i", q_i)]:
+            if t.dtype != csa_raw_kv.dtype:
+                raise TypeError(f"{name} must be {csa_raw_kv.dtype}, got {t.dtype}")
+        n_csa = (L - csa_w) // csa_stride + 1 if L >= csa_w else 0
+        n_hca = (L - hca_w) // hca_stride + 1 if L >= hca_w else 0
+        _shape(csa_ckv, "csa_ckv", (bt, n_csa, C))
+        _shape(hca_ckv, "hca_ckv", (bt, n_hca, C))
+        _shape(k_i, "k_i", (bt, n_csa, d_i))
+        _shape(reps, "reps", (bt, -(-n_csa // B) if B > 0 else 0, d_i))
+        for name, t, w in [("csa_logits", csa_logits, None), ("hca_logits", hca_logits, None),
+                           ("csa_pos_bias", csa_pos_bias, csa_w), ("hca_pos_bias", hca_pos_bias, hca_w)]:
+            if t is not None:
+                _shape(t, name, (bt, rows) if w is None else (w,))
         dev = csa_raw_kv.device
+        _on(dev, ("q_pos", q_pos), ("csa_logits", csa_logits), ("csa_pos_bias", csa_pos_bias), ("csa_ckv", csa_ckv),
+            ("k_i", k_i), ("reps", reps), ("q_i", q_i), ("w_i", w_i), ("csa_q", csa_q), ("hca_raw_kv", hca_raw_kv),
+            ("hca_logits", hca_logits), ("hca_pos_bias", hca_pos_bias), ("hca_ckv", hca_ckv), ("hca_q", hca_q))
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
         self.csa_out = torch.empty((bt, 1, h, d), dtype=torch.float32, device=dev)
         self.hca_out = torch.empty((bt, 1, h, d), dtype=torch.float32, device=dev)
         self.csa_lse = torch.empty((bt, 1, h), dtype=torch.float32, device=dev) if return_lse else None

@@ -208,3 +208,32 @@ def test_sparse_attn_noalloc_rejects_oversize(L):
     assert L.hattn_sparse_attn(1, p, p, 4000, p, 30000, p, 9000, 0, p, 128, ctypes.c_float(0.088), 1, 600, 64, 128,
                                p, None, None, ctypes.byref(sz), None) == 0
     assert sz.value > 32 << 20
+
+
+def test_empty_shapes_launch_nothing(L):
+    # With no rows (bt * nq == 0) every compute call asks for no workspace,
+    # accepts NULL buffers and returns HATTN_OK without touching a device.
+    f32 = ctypes.c_float(0.088)
+    sz = ctypes.c_size_t(123)
+    assert L.hattn_index_topk(1, None, None, None, None, 0, 4, 16, 128, 1000, 8, None, None, None,
+                              ctypes.byref(sz), None) == 0 and sz.value == 0
+    assert L.hattn_index_topk(1, None, None, None, None, 2, 0, 16, 128, 1000, 8, None, None, None, None, None) == 0
+    sz.value = 123
+    assert L.hattn_hisa_topk(1, None, None, None, None, 2, 0, 16, 128, 4096, None, 128, 8, 64, None, None, None,
+                             ctypes.byref(sz), None) == 0 and sz.value == 0
+    sz.value = 123
+    assert L.hattn_block_sparse_topk(1, None, None, None, None, 0, 4, 16, 128, 4096, None, 128, 8, None, None, None,
+                                     ctypes.byref(sz), None) == 0 and sz.value == 0
+    assert L.hattn_hisa_pool(1, None, 0, 100, 16, 16, 0, 7, None, None) == 0
+    assert L.hattn_hisa_pool(1, None, 2, 100, 16, 16, 3, 3, None, None) == 0  # empty block range
+    assert L.hattn_visible_count(None, 0, 8, 4, 1023, None, None) == 0
+    for bt, nq in ((0, 1), (3, 0)):
+        sz.value = 123
+        assert L.hattn_sparse_attn(1, None, None, 100, None, 8, None, 1000, 0, None, 128, f32, bt, nq, 64, 128,
+                                   None, None, None, ctypes.byref(sz), None) == 0 and sz.value == 0
+        sz.value = 123
+        assert L.hattn_dense_compressed_attn(1, None, None, 100, None, None, 1000, 0, None, 128, f32, bt, nq, 64, 128,
+                                             None, None, None, ctypes.byref(sz), None) == 0 and sz.value == 0
+        assert L.hattn_sparse_attn_noalloc(1, None, None, 100, None, 8, None, 1000, 0, None, 128, f32, bt, nq, 64,
+                                           128, None, None, None) == 0
+    assert L.hattn_last_error() == b""
