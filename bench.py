@@ -851,6 +851,35 @@ def probe_indexer_128k(args):
     log("[probe] done")
 
 
+def probe_hca_b32(args):
+    """Compresses 32 sequences of 1M tokens (HCA, w = s = 128) once, runs
+    ``args.steps`` HCA dense decode steps at batch 32 over rotating cache
+    replicas, then copies a 256 MiB buffer 3 times.  Run under rocprofv3
+    --pmc for the compression and attention kernels' HBM traffic."""
+    import torch
+    from compressed_attention_amd import ops, synth
+
+    dev = "cuda:0"
+    bt, L, Nh = 32, 1 << 20, 8192
+    W = synth.hca_decode(0, device=dev, bt=bt, L=L)
+    t = W.tensors
+    hkv = ops.compress(t["raw_kv"], t["z"], t["b"], 128, 128)
+    nvh = ops.visible_count(t["q_pos"], 128, 128, Nh)
+    reps = [hkv] + [hkv.clone() for _ in range(3)]
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    log(f"[probe] sources {attn_sources_sha()}: {args.steps} HCA decode steps at batch 32, "
+        f"then 3 copies of {COPY_BYTES} B")
+    for i in range(args.steps):
+        ops.dense_compressed_attn(t["q"], reps[i % len(reps)], nvh, t["raw_kv"], t["q_pos"], 128)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log("[probe] done")
+
+
 def load_traffic(kernel):
     """Calibrated HBM bytes per launch of the dominant kernel (its timer
     name), from the committed counter summary; None when it is missing,
@@ -909,8 +938,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flat-compare", dest="flat_compare", action="store_false",
                     help="skip timing the decode step with the flat indexer in place of HISA")
-    ap.add_argument("--probe", choices=["decode_plan", "indexer_128k"], default=None,
-                    help="run only the decode step and a calibration copy, or only the 128K indexer chunk "
+    ap.add_argument("--probe", choices=["decode_plan", "indexer_128k", "hca_b32"], default=None,
+                    help="run only the decode step and a calibration copy, only the 128K indexer chunk, or "
+                         "only the batch-32 HCA compression and decode with a calibration copy "
                          "(for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -929,6 +959,9 @@ def main():
         return
     if args.probe == "indexer_128k":
         probe_indexer_128k(args)
+        return
+    if args.probe == "hca_b32":
+        probe_hca_b32(args)
         return
 
     main_k = args.k
