@@ -949,7 +949,7 @@ def main():
                          "(for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(decode batches shard by sequence with no communication).", file=sys.stderr)
         sys.exit(2)
 
