@@ -127,8 +127,8 @@ struct AttnK {
   int chunk, nsplit;
   float* out;
   float* lse;
-  _Float16* part_o;  // split-K partials: O / l of the split, fp16
-  float* part_ml;    // (max, sum) of the split, fp32
+  _Float16* part_o;  // split-K partials: O / l of the split (scaled), fp16
+  float* part_ml;    // per head: (max, sum, multiplier of part_o, 0), fp32
   // Head groups of a query row: the row has 16 * NW * hg heads and a
   // workgroup takes one group of 16 * NW (layers that share one cache and
   // one selection fold into the head axis: MQA heads share every key).
@@ -390,21 +390,34 @@ HATTN_DEV void attn_mfma_body(const AttnK& a, int split, int64_t qrow, AttnLds<D
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t*>(op + 16 * dt) = o[dt] * inv;
     if (lse && g == 0) lse[qrow * HT + head] = (m_run + __log2f(l_tot)) * kLn2;
   } else {
-    // the split's output normalised by its own sum (|O / l| <= max |V|),
-    // stored in fp16; the merge weights it by 2^(m - M) l
+    // The split's output normalised by its own sum (|O / l| <= max |V|),
+    // stored in fp16 after a power-of-two scaling 2^-sh that keeps the
+    // head's largest value below 2^15 (sh = 0, no scaling, unless |V|
+    // exceeds fp16's range).  The record holds the multiplier 2^sh; the
+    // merge weights the split by 2^(m - M) l and that multiplier.
     const int64_t pr = qrow * nsplit + split;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] *= inv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(o[dt][i]));
+    }
+    amax = max_groups(amax);  // the head's values sit in its four lane groups
+    const int ex = int((__float_as_uint(amax) >> 23) & 0xffu) - 127;  // amax in [2^ex, 2^(ex+1))
+    const int sh = max(0, ex - 14);                                   // <= 113 for finite values
+    const float down = __uint_as_float(uint32_t(127 - sh) << 23);     // 2^-sh
     _Float16* op = part_o + (pr * HT + head) * D + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const f32x4_t v = o[dt] * inv;
+      const f32x4_t v = o[dt] * down;
       *reinterpret_cast<f16x4_t*>(op + 16 * dt) =
           f16x4_t{_Float16(v[0]), _Float16(v[1]), _Float16(v[2]), _Float16(v[3])};
     }
-    if (g == 0) {
-      part_ml[(pr * HT + head) * 2 + 0] = m_run;
-      part_ml[(pr * HT + head) * 2 + 1] = l_tot;
-    }
+    if (g == 0)
+      *reinterpret_cast<f32x4_t*>(part_ml + (pr * HT + head) * 4) =
+          f32x4_t{m_run, l_tot, __uint_as_float(uint32_t(127 + sh) << 23), 0.f};
   }
 }
 
@@ -544,15 +557,19 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(const T* __restrict__ q,
     if (nsplit == 1) {
       if (lse) lse[qrow * H + h] = (mrun[h] + __log2f(lrun[h])) * kLn2;
     } else {
-      part_ml[((qrow * nsplit + split) * H + h) * 2 + 0] = mrun[h];
-      part_ml[((qrow * nsplit + split) * H + h) * 2 + 1] = lrun[h];
+      float* rec = part_ml + ((qrow * nsplit + split) * H + h) * 4;  // (max, sum, multiplier 1, 0)
+      rec[0] = mrun[h];
+      rec[1] = lrun[h];
+      rec[2] = 1.f;
+      rec[3] = 0.f;
     }
   }
 }
 
 // Combines per-chunk partials, each stored as its normalised output
-// u_s = O_s / l_s (PT: fp16 from the bf16 MFMA kernels, fp32 from the
-// vector kernel) with its (m_s, l_s): o = sum_s w_s u_s with weights
+// u_s = O_s / l_s divided by a power-of-two multiplier c_s (PT: fp16 from
+// the bf16 MFMA kernels, fp32 with c_s = 1 from the vector kernel) with a
+// record (m_s, l_s, c_s, 0): o = sum_s w_s c_s (u_s / c_s) with weights
 // w_s = 2^(m_s - M) l_s / sum_t 2^(m_t - M) l_t.  Needs nsplit <= 4 *
 // kMergeRegs and a head shape merge_fast() accepts.
 constexpr int kMergeRegs = 16;
@@ -612,21 +629,22 @@ HATTN_DEV void attn_merge_body(const MergeK<PT>& mk, int H, int D, int64_t qrow,
     ov[i] = s < nsplit ? __builtin_nontemporal_load(reinterpret_cast<const V4*>(po + s * pos)) : V4{0, 0, 0, 0};
   }
   if (sg == 0) {
-    const float* __restrict__ ml = mk.part_ml + (qrow * nsplit * H + h0) * 2;
-    const int64_t mls = int64_t(H) * 2;
-    float2 v[4];
+    const float* __restrict__ ml = mk.part_ml + (qrow * nsplit * H + h0) * 4;
+    const int64_t mls = int64_t(H) * 4;
+    f32x4_t v[4];
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh)
-      v[hh] = hh < hpg && lane < nsplit ? *reinterpret_cast<const float2*>(ml + lane * mls + 2 * hh)
-                                        : make_float2(-INFINITY, 0.f);
+      v[hh] = hh < hpg && lane < nsplit ? *reinterpret_cast<const f32x4_t*>(ml + lane * mls + 4 * hh)
+                                        : f32x4_t{-INFINITY, 0.f, 1.f, 0.f};
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
       if (hh < hpg) {
-        const float M = wave_max(v[hh].x);
-        float den = v[hh].x != -INFINITY ? exp2f(v[hh].x - M) * v[hh].y : 0.f;
+        const float M = wave_max(v[hh][0]);
+        float den = v[hh][0] != -INFINITY ? exp2f(v[hh][0] - M) * v[hh][1] : 0.f;
         den = wave_sum(den);
         const float inv = den > 0.f ? 1.f / den : 0.f;
-        if (lane < nsplit) sm.w[hh][lane] = v[hh].x == -INFINITY ? 0.f : exp2f(v[hh].x - M) * v[hh].y * inv;
+        if (lane < nsplit)
+          sm.w[hh][lane] = v[hh][0] == -INFINITY ? 0.f : exp2f(v[hh][0] - M) * v[hh][1] * inv * v[hh][2];
         if (lane == 0 && mk.lse) mk.lse[qrow * H + h0 + hh] = (M + __log2f(den)) * kLn2;
       }
     }
@@ -680,8 +698,8 @@ __global__ __launch_bounds__(256) void attn_merge_any_kernel(const PT* __restric
   const int e = blockIdx.x * 256 + threadIdx.x;
   if (e >= H * D) return;
   const int h = e / D, c = e % D;
-  const float* ml = part_ml + (qrow * nsplit * H + h) * 2;
-  const int64_t mls = int64_t(H) * 2;
+  const float* ml = part_ml + (qrow * nsplit * H + h) * 4;
+  const int64_t mls = int64_t(H) * 4;
   float M = -INFINITY;
 #pragma unroll 8
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[s * mls]);
@@ -693,7 +711,7 @@ __global__ __launch_bounds__(256) void attn_merge_any_kernel(const PT* __restric
     const float ms = ml[s * mls];
     const float w = ms == -INFINITY ? 0.f : exp2f(ms - M) * ml[s * mls + 1];
     den += w;
-    num = fmaf(w, float(po[s * pos]), num);
+    num = fmaf(w * ml[s * mls + 2], float(po[s * pos]), num);
   }
   out[qrow * H * D + e] = den > 0.f ? num / den : 0.f;
   if (c == 0 && lse) lse[qrow * H + h] = (M + __log2f(den)) * kLn2;
@@ -745,7 +763,7 @@ static AttnPlan plan_attn(const AttnArgs& a) {
   p.nsplit = int((maxkeys + chunk - 1) / chunk);
   if (p.nsplit > 1) {
     p.po_bytes = align256(size_t(rows) * p.nsplit * a.h * a.d * (mfma_shape(a) ? 2 : 4));  // fp16 from MFMA
-    p.total = p.po_bytes + align256(size_t(rows) * p.nsplit * a.h * 2 * 4);
+    p.total = p.po_bytes + align256(size_t(rows) * p.nsplit * a.h * 4 * 4);  // 16-byte (m, l, c, 0) records
   }
   return p;
 }

@@ -243,8 +243,10 @@ hattn_status_t hattn_block_sparse_topk(int dtype, const void* q_i, const void* k
  * vector path.  Arithmetic: fp32 accumulation; on the MFMA path the
  * softmax weights enter the PV product in bf16 and, when a query's key
  * list is split over several workgroups, each split's normalised output
- * O/l is kept in fp16 in the workspace (with its max and sum in fp32)
- * until the merge; the fp32 vector path keeps fp32 throughout.  Layers that share one cache and one index list (CSA2's
+ * O/l is kept in fp16 in the workspace until the merge, scaled down by a
+ * power of two when its largest value reaches 2^15 (values beyond fp16's
+ * range), with its max, sum and scale in fp32; the fp32 vector path keeps
+ * fp32 throughout.  Layers that share one cache and one index list (CSA2's
  * cross-layer reuse, [HCA] section V4.1 为什么不要它了) are one call: with
  * MQA every head attends to the same keys, so layer g's head j is head
  * g*h_layer + j of q, out and lse.

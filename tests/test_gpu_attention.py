@@ -249,14 +249,16 @@ def test_ring_window_reads_match_full(h, d, dt):
         _check(o_ring[b], l_ring[b], ro, rl)
 
 
-@pytest.mark.parametrize("vscale,qscale", [(1000.0, 1.0), (1.0, 6.0)])
+@pytest.mark.parametrize("vscale,qscale", [(1000.0, 1.0), (1.0, 6.0), (1e6, 1.0), (1e30, 6.0)])
 def test_split_partials_large_values(vscale, qscale):
     # Long key lists split over several workgroups, whose partial outputs are
     # kept as fp16 O/l: V rows of magnitude ~1,000 (O/l is a convex
-    # combination of them, far below fp16's 65,504) and sharp logits (q x 6,
-    # the lazy rescale moving often).  The error must stay within the bound
-    # of the arithmetic: |err| <= (2^-9 for the bf16 weights + 2^-11 for the
-    # fp16 partial) * max |V|, with a factor 4 for accumulation.
+    # combination of them, below fp16's 65,504), of magnitude ~1e6 and ~1e30
+    # (beyond fp16's range: each split's O/l is scaled by a power of two
+    # before it is stored), and sharp logits (q x 6, the lazy rescale moving
+    # often).  The error must stay within the bound of the arithmetic:
+    # |err| <= (2^-9 for the bf16 weights + 2^-11 for the fp16 partial) *
+    # max |V|, with a factor 4 for accumulation.
     bt, nq, N, L, h, d = 2, 3, 8000, 9000, 64, 128
     dt = torch.bfloat16
     raw = synth.normal((bt, L, 2 * d), 120, dtype=dt)
@@ -274,6 +276,8 @@ def test_split_partials_large_values(vscale, qscale):
     for b in range(bt):
         ro, rl = oracle.dense_compressed_attention(f64(q[b]), f64(ckv[b]), nv[b].numpy(), f64(raw[b]),
                                                    pos[b].numpy(), 128, 1 / math.sqrt(d))
-        err = float(np.abs(f64(out[b]) - ro).max())
+        got = f64(out[b])
+        assert np.isfinite(got).all(), (vscale, qscale, b)
+        err = float(np.abs(got - ro).max())
         assert err <= bound, (vscale, qscale, b, err, bound)
         assert float(np.abs(f64(lse[b]) - rl).max()) <= 1e-2
