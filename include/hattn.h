@@ -32,7 +32,10 @@
  *     Faults inside kernels surface at the caller's next synchronisation.
  *   - Floating inputs are either all fp32 (HATTN_F32) or bf16 (HATTN_BF16,
  *     stored as raw 16-bit patterns) as stated per argument; accumulation is
- *     always fp32.  Non-finite inputs are not supported.
+ *     always fp32.  Non-finite inputs are not supported, nor are finite
+ *     ones whose fp32 intermediates overflow (an indexer score or a scaled
+ *     attention logit beyond about 3.4e38).  Finite V of any magnitude is
+ *     handled (split-K partials are range-scaled).
  *   - Workspaces (device scratch for intermediate scores and partial
  *     results; contents need no initialisation and are meaningless after
  *     the call): with ws == NULL and ws_bytes != NULL the call stores the
