@@ -82,8 +82,6 @@ HATTN_DEV float wave_max(float v) {
   return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
-HATTN_DEV int lane_id() { return __lane_id(); }
-
 // a / b for 0 <= a and 0 < b: a 32-bit division when both fit (a row index
 // over a per-sequence count), the 64-bit expansion only otherwise.
 HATTN_DEV int64_t idiv(int64_t a, int64_t b) {
