@@ -432,15 +432,16 @@ def csa2_decode(args):
 
     # The same step with HISA in place of the flat indexer (B = 128, m = 16:
     # 2,048 candidates for the top-512, the pages' m*B = 4k); the step also
-    # refreshes the mean of the block holding the new entry.
+    # refreshes the mean of the block holding the new entry.  After the
+    # entry and its indexer key are compressed, one decode-append launch
+    # gives the visible count and that block mean (it writes the K|V entry
+    # again, the same 4-row merge).
     B, m = 128, 16
     reps = ops.hisa_pool(k_i, B)
-    nb = reps.shape[1]
 
     def step_hisa(_):
         ops.compress_with_index(raw, raw_ki, z, b, w, s, N - 1, N, out=ckv, out_i=k_i)
-        ops.hisa_pool(k_i, B, nb - 1, nb, out=reps)
-        nv = ops.visible_count(q_pos, w, s, N)
+        nv = ops.decode_append(raw, z, b, w, s, q_pos, ckv, k_i=k_i, reps=reps, B=B)
         idx = ops.hisa_topk(q_i, k_i, w_i, nv, reps, B, m, k)
         return ops.sparse_attn(q, ckv, idx, raw, q_pos, 128), idx
 
